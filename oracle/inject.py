@@ -1,0 +1,113 @@
+"""Write side of the paged cache: inject and append (oracle; test infra).
+
+[InferScale] §3 (connector flow): blocks are first reserved for the memory
+tokens without computing them, then the composed K/V is scatter-copied into
+those blocks through the slot mapping; §3.3 and §5.1: the stored pre-rotation
+key of each token is rotated to the position it lands on.  [InferScale] §2
+and [KV essay] "The fix": decoding appends one K/V entry per generated token.
+
+Readings taken where the pages are silent:
+
+* a run is (seq, n, dst_pos, src_token): source tokens src_token ..
+  src_token+n-1 land at positions dst_pos .. dst_pos+n-1 of ``seq``;
+* every destination must lie inside the sequence's reserved blocks and below
+  the rotary table length; two tokens of one call may not share a slot
+  (rejected as 'OVERLAP'); positions written by an earlier call may be
+  overwritten;
+* after the call the sequence's length is max(old length, dst_pos + n);
+* the key is rotated to its destination position (rope.rotate_f32) and
+  rounded to the cache format; the value is copied bit for bit;
+* append writes T tokens per sequence at positions len-T .. len-1 of the
+  already-extended lengths, rotated the same way (mode "none" stores keys as
+  given).
+
+The source store is [layer][token][kv head][d], with element strides
+``layer_stride`` and ``token_stride`` and the d elements of a head
+contiguous.
+"""
+
+import numpy as np
+
+from .layout import BLOCK_TOKENS, PoolSpec, k_element_offsets, v_element_offsets, slot
+from .numerics import from_f32, to_f32
+from .rope import rotate_f32
+
+
+class InjectError(Exception):
+    def __init__(self, code: str, msg: str):
+        super().__init__("%s: %s" % (code, msg))
+        self.code = code
+
+
+def validate_runs(tables, lens, runs, max_pos: int):
+    """Check every run; return the list of (seq, position, src_token) writes."""
+    writes = []
+    seen = set()
+    for (seq, n, p0, src) in runs:
+        if not (0 <= seq < len(tables)):
+            raise InjectError("INVALID", "unknown sequence %d" % seq)
+        if n < 0 or p0 < 0 or src < 0:
+            raise InjectError("INVALID", "negative run field")
+        cap = sum(1 for b in tables[seq] if b >= 0) * BLOCK_TOKENS
+        if p0 + n > cap:
+            raise InjectError("RANGE", "run past reserved capacity")
+        if p0 + n > max_pos:
+            raise InjectError("RANGE", "run past the rotary table")
+        for t in range(n):
+            s = slot(tables[seq], p0 + t)
+            if s in seen:
+                raise InjectError("OVERLAP", "two tokens target slot %d" % s)
+            seen.add(s)
+            writes.append((seq, p0 + t, src + t))
+    return writes
+
+
+def write_token(k_pool, v_pool, spec: PoolSpec, layer: int, table_row, pos: int,
+                k_raw, v_raw, mode: str, cos_t, sin_t):
+    """Store one token (all KV heads) of one layer at position ``pos``.
+
+    k_raw, v_raw: [n_kv_heads][d] in the cache's storage format.
+    """
+    s = slot(table_row, pos)
+    blk, t = divmod(s, BLOCK_TOKENS)
+    k32 = to_f32(k_raw, spec.dtype)
+    k_rot = rotate_f32(k32, np.full(k32.shape[:-1], pos), cos_t, sin_t, mode)
+    k_store = from_f32(k_rot, spec.dtype)
+    for h in range(spec.n_kv_heads):
+        k_pool[k_element_offsets(spec, layer, blk, h, t)] = k_store[h]
+        v_pool[v_element_offsets(spec, layer, blk, h, t)] = v_raw[h]
+
+
+def inject(k_pool, v_pool, spec: PoolSpec, tables, lens, runs, src_k, src_v,
+           src_layer_stride: int, src_token_stride: int, layer_begin: int, layer_end: int,
+           mode: str, cos_t, sin_t):
+    """Scatter runs of stored, unrotated K/V into the pool; returns new lens."""
+    max_pos = cos_t.shape[0]
+    if not (0 <= layer_begin <= layer_end <= spec.n_layers):
+        raise InjectError("INVALID", "bad layer range")
+    writes = validate_runs(tables, lens, runs, max_pos)
+    hd = spec.n_kv_heads * spec.head_dim
+    for layer in range(layer_begin, layer_end):
+        for (seq, pos, src) in writes:
+            base = layer * src_layer_stride + src * src_token_stride
+            k_raw = src_k[base:base + hd].reshape(spec.n_kv_heads, spec.head_dim)
+            v_raw = src_v[base:base + hd].reshape(spec.n_kv_heads, spec.head_dim)
+            write_token(k_pool, v_pool, spec, layer, tables[seq], pos, k_raw, v_raw,
+                        mode, cos_t, sin_t)
+    new_lens = list(lens)
+    for (seq, n, p0, _src) in runs:
+        new_lens[seq] = max(new_lens[seq], p0 + n)
+    return new_lens
+
+
+def append(k_pool, v_pool, spec: PoolSpec, layer: int, tables, lens_after, seqs, n_new: int,
+           k_new, v_new, mode: str, cos_t, sin_t):
+    """Write n_new tokens per sequence at its last n_new positions.
+
+    k_new, v_new: raw arrays [len(seqs)][n_new][n_kv_heads][d].
+    """
+    for i, seq in enumerate(seqs):
+        first = lens_after[seq] - n_new
+        for t in range(n_new):
+            write_token(k_pool, v_pool, spec, layer, tables[seq], first + t,
+                        k_new[i, t], v_new[i, t], mode, cos_t, sin_t)
