@@ -13,12 +13,15 @@ The pages name RoFormer (Su et al.) and nothing more precise.  Readings taken:
   block-diagonal form) or, as a flag, (i, i + d/2) ("halves"); block i turns
   by the angle p * theta_i with theta_i = base ** (-2i/d);
 * the rotary table is computed in float64 and rounded once to float32:
-  cos_table[p][i] = f32(cos(p * theta_i)), sin_table[p][i] = f32(sin(...));
+  cos_table[p][i] = f32(cos(p * theta_i)), sin_table[p][i] = f32(sin(...)),
+  with theta_i from the C library's pow;
 * a key is rotated in float32 with no fused multiply-add:
   y0 = f32(f32(x0*c) - f32(x1*s)),  y1 = f32(f32(x0*s) + f32(x1*c)),
   and then stored with round-to-nearest-even (see numerics);
 * values are never rotated.
 """
+
+import math
 
 import numpy as np
 
@@ -26,11 +29,17 @@ MODES = ("pairs", "halves", "none")
 
 
 def thetas(head_dim: int, base: float) -> np.ndarray:
-    """theta_i = base ** (-2i/d), i = 0 .. d/2 - 1, in float64."""
+    """theta_i = base ** (-2i/d), i = 0 .. d/2 - 1, in float64.
+
+    Each power is the C library's double-precision pow (Python's math.pow).
+    numpy's vectorised power can differ from it in the last bit for some i;
+    the reading fixes one float64 function so that the float32 table is a
+    single, reproducible rounding of the definition.
+    """
     if head_dim % 2:
         raise ValueError("head_dim must be even")
-    i = np.arange(head_dim // 2, dtype=np.float64)
-    return np.float64(base) ** (-2.0 * i / head_dim)
+    return np.array([math.pow(float(base), -2.0 * i / head_dim) for i in range(head_dim // 2)],
+                    dtype=np.float64)
 
 
 def rope_table(head_dim: int, base: float, max_pos: int):
