@@ -1,0 +1,299 @@
+"""Benchmark of the paged KV cache hot path on one MI355X.
+
+One step = one decode pass over all 80 layers of the Llama-3-70B-shaped
+workload (batch 32 x 8,192 tokens, 64 query / 8 KV heads of 128, bf16, 16-token
+blocks under a shuffled table): the per-step split plan is uploaded, then
+paged decode attention runs layer after layer.  The reported value is the
+whole step's algorithmic HBM bytes (every cached K/V byte, q, out, lse and the
+block-table entries) divided by its time, in GB/s.
+
+The injection workload runs after it: top-8 memory chunks of 64..256 tokens
+from a 10,000-chunk store of unrotated bf16 K/V (32 layers x 8 KV heads x 128)
+injected for 64 requests at non-consecutive positions, in one call per
+repetition; reported as injected tokens/s and GB/s.
+
+Each dominant kernel is also timed per launch with HIP events on the stream
+it runs on.  The CPU oracle is timed on a bounded sample of the decode
+workload.  One JSON line is printed on stdout; progress goes to stderr.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def device_pool(n_layers, num_blocks, n_kv_heads, head_dim, dtype, seed):
+    """[layer][block][K planes | V planes] buffer filled with N(0,1) per layer."""
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    from workloads.configs import device_normal
+    plane = 16 * head_dim
+    block_stride = 2 * n_kv_heads * plane
+    layer_stride = num_blocks * block_stride
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    buf = torch.empty(n_layers * layer_stride, dtype=tdt, device="cuda")
+    if seed is not None:
+        for layer in range(n_layers):
+            buf[layer * layer_stride:(layer + 1) * layer_stride] = device_normal(
+                layer_stride, dtype, seed * 1000 + layer)
+    e = buf.element_size()
+    desc = pkv.pkv_pool(n_layers, num_blocks, n_kv_heads, head_dim, pkv.DTYPE_CODES[dtype], 0,
+                        buf.data_ptr(), buf.data_ptr() + n_kv_heads * plane * e, layer_stride,
+                        block_stride, plane)
+    return buf, desc
+
+
+def decode_bytes(lens, n_kv_heads, head_dim, n_q_heads, elem):
+    """Algorithmic bytes of one decode launch (one layer)."""
+    kv = int(np.sum(lens)) * n_kv_heads * head_dim * elem * 2
+    q = len(lens) * n_q_heads * head_dim * elem
+    out = len(lens) * n_q_heads * head_dim * 4 + len(lens) * n_q_heads * 4
+    tables = int(sum(-(-int(x) // 16) for x in lens)) * 4
+    return kv + q + out + tables
+
+
+def bw_probe(n_bytes=8 << 30, reps=5):
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    src = torch.ones(n_bytes // 2, dtype=torch.bfloat16, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    pkv.pkv_bw_probe(src, sink)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        pkv.pkv_bw_probe(src, sink)
+    e.record()
+    torch.cuda.synchronize()
+    gbps = n_bytes * reps / (s.elapsed_time(e) * 1e-3) / 1e9
+    del src
+    return gbps
+
+
+def run_decode(steps, warmup):
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    from workloads.configs import CONFIGS, llama70b_structure, host_normal
+    cfg = CONFIGS[3]
+    st = llama70b_structure(cfg)
+    lens = st["lens"]
+    log("decode: allocating and filling %d layers x %d blocks" % (cfg.n_layers, st["num_blocks"]))
+    buf, pool = device_pool(cfg.n_layers, st["num_blocks"], cfg.n_kv_heads, cfg.head_dim,
+                            cfg.dtype, cfg.seed)
+    q_host = host_normal(st["rng"], (cfg.batch, cfg.n_q_heads, cfg.head_dim), cfg.dtype)
+    q = torch.from_numpy(q_host.view(np.int16)).cuda().view(torch.bfloat16)
+    tables = torch.from_numpy(st["tables"]).cuda()
+    out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, device="cuda")
+    lse = torch.empty(cfg.batch, cfg.n_q_heads, device="cuda")
+    part = int(os.environ.get("PKV_BENCH_PART", "0"))
+    plan = pkv.pkv_decode_plan_create(lens, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, part)
+    ws = torch.empty(pkv.pkv_decode_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
+    n_items = pkv.pkv_decode_plan_items(plan)
+    part_tokens = pkv.pkv_decode_plan_part_tokens(plan)
+
+    def step(events=None):
+        pkv.pkv_decode_plan_upload(plan, ws)
+        for layer in range(cfg.n_layers):
+            if events is not None:
+                events[layer][0].record()
+            pkv.pkv_decode_attention(plan, pool, layer, q, tables, out, lse, ws)
+            if events is not None:
+                events[layer][1].record()
+
+    log("decode: %d warmup steps" % warmup)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(cfg.n_layers)]
+          for _ in range(steps)]
+    t_s, t_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log("decode: %d timed steps" % steps)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_s.record()
+    for k in range(steps):
+        step(ev[k])
+    t_e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t_s.elapsed_time(t_e)
+    launch_ms = [ev[k][l][0].elapsed_time(ev[k][l][1]) for k in range(steps)
+                 for l in range(cfg.n_layers)]
+    per_launch = decode_bytes(lens, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads, 2)
+    ms_step = total_ms / steps
+    res = dict(ms_per_step=ms_step, wall_ms_per_step=wall * 1e3 / steps,
+               bytes_per_step=per_launch * cfg.n_layers, bytes_per_launch=per_launch,
+               launch_ms_avg=float(np.mean(launch_ms)), launch_ms_p50=float(np.median(launch_ms)),
+               n_items=n_items, part_tokens=part_tokens, workload=cfg.workload,
+               batch=cfg.batch, context=int(lens[0]), layers=cfg.n_layers)
+    res["value"] = res["bytes_per_step"] / (ms_step * 1e-3) / 1e9
+    res["launch_gbps"] = per_launch / (res["launch_ms_avg"] * 1e-3) / 1e9
+    log("decode: %.3f ms/step, %.1f GB/s; per launch %.1f us -> %.1f GB/s"
+        % (ms_step, res["value"], res["launch_ms_avg"] * 1e3, res["launch_gbps"]))
+    pkv.pkv_decode_plan_destroy(plan)
+    del buf, ws, q, tables, out, lse
+    torch.cuda.empty_cache()
+    return res, st
+
+
+def run_inject(reps):
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    from workloads.configs import CONFIGS, inject_structure, device_normal
+    cfg = CONFIGS[4]
+    st = inject_structure(cfg)
+    L, H, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+    n_src = st["n_src"]
+    row = H * d
+    log("inject: store of %d tokens x %d layers (%.1f GB)" %
+        (n_src, L, 2 * n_src * L * row * 2 / 1e9))
+    store_k = torch.empty(L * n_src * row, dtype=torch.bfloat16, device="cuda")
+    store_v = torch.empty(L * n_src * row, dtype=torch.bfloat16, device="cuda")
+    for layer in range(L):
+        a, b = layer * n_src * row, (layer + 1) * n_src * row
+        store_k[a:b] = device_normal(b - a, "bf16", cfg.seed * 1000 + 2 * layer)
+        store_v[a:b] = device_normal(b - a, "bf16", cfg.seed * 1000 + 2 * layer + 1)
+    buf, pool = device_pool(L, st["num_blocks"], H, d, "bf16", None)
+    cache = pkv.pkv_cache_create(st["num_blocks"], cfg.batch, st["max_blocks"],
+                                 st["free_list_seed"])
+    for b, m in enumerate(st["mem_lens"]):
+        pkv.pkv_alloc_blocks(cache, b, int(m))
+    max_pos = 4096
+    cos, sin = pkv.pkv_rope_table(d, cfg.rope_base, max_pos)
+    dcos, dsin = torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda()
+    src = pkv.make_src(store_k, store_v, n_src * row, row, n_src)
+    runs = pkv.make_runs(st["runs"])
+    ws = torch.empty(pkv.pkv_inject_workspace_bytes(runs), dtype=torch.uint8, device="cuda")
+    n_tok = int(sum(r[1] for r in st["runs"]))
+
+    def once():
+        pkv.pkv_inject(cache, pool, src, runs, 0, L, "pairs", dcos, dsin, max_pos, ws)
+
+    once()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        once()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    bytes_call = n_tok * L * row * 2 * 2 * 2     # K and V, read and written
+    res = dict(ms_per_call=ms, tokens=n_tok, tokens_per_s=n_tok / (ms * 1e-3),
+               token_layers_per_s=n_tok * L / (ms * 1e-3), gbps=bytes_call / (ms * 1e-3) / 1e9,
+               bytes_per_call=bytes_call, requests=cfg.batch, layers=L)
+    log("inject: %.3f ms/call, %.3g tok/s, %.1f GB/s" % (ms, res["tokens_per_s"], res["gbps"]))
+    pkv.pkv_cache_destroy(cache)
+    del store_k, store_v, buf, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(budget_s=15.0):
+    """The oracle's decode on whole sequences of the decode workload (layer 0,
+    all 64 query heads), one thread, until the budget is spent."""
+    import torch
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as o_att
+    from oracle.layout import PoolSpec
+    from workloads.configs import CONFIGS, llama70b_structure, host_normal, device_normal
+    cfg = CONFIGS[3]
+    st = llama70b_structure(cfg)
+    nb = st["num_blocks"]
+    plane = 16 * cfg.head_dim
+    bs = 2 * cfg.n_kv_heads * plane
+    q = host_normal(st["rng"], (cfg.batch, cfg.n_q_heads, cfg.head_dim), cfg.dtype)
+    layer0 = device_normal(nb * bs, "bf16", cfg.seed * 1000).view(torch.int16).cpu().numpy()
+    flat = layer0.view(np.uint16)
+    spec = PoolSpec(1, nb, cfg.n_kv_heads, cfg.head_dim, "bf16", nb * bs, bs, plane)
+    kp, vp = flat, flat[cfg.n_kv_heads * plane:]
+    rows = [list(r) for r in st["tables"]]
+    done, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t0 < budget_s and done < cfg.batch:
+            o_att.decode_paged(q, kp, vp, spec, 0, rows, st["lens"], cfg.n_q_heads,
+                               seqs=[done], by_plane=True)
+            done += 1
+    dt = time.perf_counter() - t0
+    by = decode_bytes(st["lens"][:done], cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads, 2)
+    return dict(value=by / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
+                sample="layer 0, %d of 32 sequences x 8192 tokens, all 64 query heads, "
+                       "float64 numpy, %.1f s" % (done, dt))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--inject-reps", type=int, default=10)
+    ap.add_argument("--no-inject", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the hot path here runs on a single MI355X; "
+              "multi-GPU sharding is design-only. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    pkv.load_library()
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log("device:", props.name, getattr(props, "gcnArchName", "?"), "%d CUs" % props.multi_processor_count)
+    probe = bw_probe()
+    log("bw probe: %.1f GB/s" % probe)
+    dec, _ = run_decode(args.steps, args.warmup)
+    inj = None if args.no_inject else run_inject(args.inject_reps)
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    line = {
+        "metric": "paged decode attention achieved HBM GB/s (% of peak) + injected tokens/s",
+        "value": round(dec["value"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_peak": round(100 * dec["value"] / PEAK_HBM_GBPS, 2),
+        "config": {"workload": dec["workload"], "batch": dec["batch"], "context": dec["context"],
+                   "layers": dec["layers"], "part_tokens": dec["part_tokens"],
+                   "work_items": dec["n_items"]},
+        "roofline": {"bound": "hbm", "achieved": round(dec["launch_gbps"], 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(dec["launch_gbps"] / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "pkv_decode_attention (one layer)",
+                     "bytes_per_launch": dec["bytes_per_launch"],
+                     "launch_us_avg": round(dec["launch_ms_avg"] * 1e3, 2)},
+        "bw_probe_gbps": round(probe, 1),
+        "cpu_baseline": cpu,
+    }
+    if inj is not None:
+        line["inject"] = {"tokens_per_s": round(inj["tokens_per_s"], 1), "unit": "tokens/s",
+                          "token_layers_per_s": round(inj["token_layers_per_s"], 1),
+                          "gbps": round(inj["gbps"], 1), "ms_per_call": round(inj["ms_per_call"], 4),
+                          "tokens_per_call": inj["tokens"], "requests": inj["requests"],
+                          "layers": inj["layers"],
+                          "workload": "top-8 of 10k chunks (64..256 tokens), 32 layers x 8 x 128 "
+                                      "bf16, 64 requests, gaps of 1..15 positions"}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,304 @@
+/*
+ * pkv.h -- C ABI of libpkv: a paged KV cache for MI355X (gfx950) whose write
+ * side injects precomputed, unrotated K/V into fixed 16-token blocks (rotating
+ * each key to its destination position as it is written) and whose read side
+ * runs grouped-query decode attention through per-sequence block tables.
+ *
+ * Sources, cited by page title and section:
+ *   [InferScale]     "InferScale: GPU-Native KV Injection for Personalized LLM
+ *                    Serving"
+ *   [KV essay]       "LLM Inference: KV Caching"
+ *   [Inside engines] "Inside LLM Inference Engines: KV Caching,
+ *                    PagedAttention, and Continuous Batching"
+ *   [KV management]  "Latency Optimization > KV Cache Management"
+ *
+ * Conventions for every entry point:
+ *   - Returns a pkv_status (0 = PKV_OK, negative = error) unless noted.
+ *   - All argument checks run on the host before anything is enqueued; on an
+ *     error nothing is enqueued, no host state changes, and pkv_last_error()
+ *     describes the problem.
+ *   - "device" pointers are HIP device memory owned by the caller; the library
+ *     never allocates, frees or retains them beyond the enqueued work, which
+ *     must complete before the caller frees them.  "host" pointers are read or
+ *     written before the call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued on it asynchronously; no call synchronises the
+ *     device except where stated.
+ *   - Element strides and offsets are in elements of the stated dtype.
+ *   - Index data that lives on the device (block tables, positions) is
+ *     range-checked inside the kernels: an out-of-range block id or position
+ *     is never dereferenced; the element it would have produced is skipped.
+ *   - A pkv_cache or pkv_plan is not thread-safe: one host thread at a time.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+/* Tokens per physical block ([InferScale] §2; [KV essay] "Paged attention"). */
+#define PKV_BLOCK_TOKENS 16
+
+typedef int32_t pkv_status;
+#define PKV_OK             0
+#define PKV_E_INVALID     -1  /* bad argument, unknown sequence, bad state   */
+#define PKV_E_OOM         -2  /* the free list cannot cover a reservation    */
+#define PKV_E_RANGE       -3  /* position/length beyond capacity or table    */
+#define PKV_E_OVERLAP     -4  /* two tokens of one inject call, one slot     */
+#define PKV_E_WORKSPACE   -5  /* device workspace missing or too small       */
+#define PKV_E_HIP         -6  /* a HIP runtime call or launch failed         */
+#define PKV_E_UNSUPPORTED -7  /* shape/dtype combination not implemented     */
+
+/* Element formats of the cache, of injected/appended K/V and of q. */
+#define PKV_F32  0
+#define PKV_BF16 1
+#define PKV_F16  2
+
+/* RoPE pairings ([InferScale] §2: R_p is block-diagonal with 2x2 rotations).
+ * PAIRS rotates dimensions (2i, 2i+1); HALVES rotates (i, i+d/2); NONE stores
+ * keys as given (already rotated by the caller). */
+#define PKV_ROPE_PAIRS  0
+#define PKV_ROPE_HALVES 1
+#define PKV_ROPE_NONE   2
+
+typedef struct pkv_cache pkv_cache; /* host allocator state (opaque)      */
+typedef struct pkv_plan pkv_plan;   /* host decode split plan (opaque)    */
+
+/* ---------------------------------------------------------------------------
+ * Data descriptors
+ * ------------------------------------------------------------------------- */
+
+/* The paged pool of one model ([KV essay] "Paged attention": a shared pool of
+ * fixed blocks).  For every (layer, physical block, KV head) there is one K
+ * plane and one V plane of 16*head_dim elements each:
+ *   K plane base = k + layer*layer_stride + block*block_stride + head*head_stride
+ *   V plane base = v + (same offset)
+ * Inside a K plane, element (token t in block, dim j) is at
+ *   ((j / X) * 16 + t) * X + (j % X),   X = 16 bytes / element size,
+ * i.e. d/X chunks of X consecutive dims for all 16 tokens.  Inside a V plane,
+ * element (t, j) is at j * 16 + t (dimension-major).  Planes must be 16-byte
+ * aligned (base pointers and every stride times the element size a multiple
+ * of 16).  dtype is PKV_F32, PKV_BF16 or PKV_F16; head_dim is 64 or 128. */
+typedef struct {
+  int32_t n_layers;
+  int32_t num_blocks;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+  int32_t _reserved;
+  void* k;              /* device */
+  void* v;              /* device */
+  int64_t layer_stride; /* elements */
+  int64_t block_stride; /* elements */
+  int64_t head_stride;  /* elements */
+} pkv_pool;
+
+/* The store of precomputed, unrotated K/V ([InferScale] §3: keys captured
+ * before the rotary embedding, kept with their values, per layer).  Element
+ * (layer, token, kv head, dim) is at layer*layer_stride + token*token_stride +
+ * head*head_dim + dim, for K at k and V at v.  Same dtype, n_kv_heads and
+ * head_dim as the pool; 16-byte aligned rows. */
+typedef struct {
+  const void* k;        /* device */
+  const void* v;        /* device */
+  int64_t layer_stride; /* elements */
+  int64_t token_stride; /* elements */
+  int64_t n_tokens;     /* tokens per layer (for range checks) */
+} pkv_src;
+
+/* One injected run: source tokens src_token .. src_token+n_tokens-1 land at
+ * positions dst_pos .. dst_pos+n_tokens-1 of sequence seq. */
+typedef struct {
+  int32_t seq;
+  int32_t n_tokens;
+  int32_t dst_pos;
+  int32_t _reserved;
+  int64_t src_token;
+} pkv_run;
+
+/* Host allocator configuration. free_list_seed 0 = ascending initial order;
+ * otherwise the Fisher-Yates shuffle (i from N-1 down to 1, j = next() mod
+ * (i+1)) driven by splitmix64 seeded with free_list_seed. */
+typedef struct {
+  int32_t num_blocks;
+  int32_t max_seqs;
+  int32_t max_blocks_per_seq;
+  int32_t _reserved;
+  uint64_t free_list_seed;
+} pkv_cache_config;
+
+/* ---------------------------------------------------------------------------
+ * Library
+ * ------------------------------------------------------------------------- */
+
+/* PKV_ABI_VERSION of the built library. */
+int32_t pkv_abi_version(void);
+
+/* Message of the last error on this thread ("" if none).  Valid until the next
+ * pkv_* call on the same thread. */
+const char* pkv_last_error(void);
+
+/* Bytes of K plus V for n_tokens tokens: 2 * n_layers * n_kv_heads * head_dim
+ * * elem_bytes * n_tokens ([Inside engines] "The KV Cache: Mathematical
+ * Formulation & Memory Footprint"; [KV essay] "What the cache costs";
+ * [InferScale] §3, per-fact storage).  Returns 0 for a negative argument. */
+uint64_t pkv_kv_bytes(int32_t n_layers, int32_t n_kv_heads, int32_t head_dim,
+                      int32_t elem_bytes, int64_t n_tokens);
+
+/* ---------------------------------------------------------------------------
+ * Host block allocator ([KV essay] "Paged attention": free list, per-sequence
+ * block table, a new block handed out when a sequence reaches it;
+ * [Inside engines] "PagedAttention", "Continuous Batching": blocks return to
+ * the pool when a sequence ends).  Blocks are taken from the head of a FIFO
+ * free list and returned to its tail in table order.
+ * ------------------------------------------------------------------------- */
+
+/* Create an allocator. *out receives the handle. Errors: INVALID. */
+pkv_status pkv_cache_create(const pkv_cache_config* cfg, pkv_cache** out);
+
+/* Destroy an allocator (NULL is ignored). */
+void pkv_cache_destroy(pkv_cache* cache);
+
+/* Grow seq's blocks until it can hold n_tokens positions (its length is
+ * unchanged).  All-or-nothing.  Errors: INVALID (seq, n_tokens < 0),
+ * RANGE (more than max_blocks_per_seq blocks), OOM. */
+pkv_status pkv_alloc_blocks(pkv_cache* cache, int32_t seq, int64_t n_tokens);
+
+/* Give an empty sequence an explicit table (host ids[n_ids], each currently
+ * free, no repeats) and length len <= 16*n_ids.  The ids leave the free list,
+ * whose remaining order is kept.  Errors: INVALID, RANGE. */
+pkv_status pkv_set_blocks(pkv_cache* cache, int32_t seq, const int32_t* ids,
+                          int32_t n_ids, int64_t len);
+
+/* Append n_new positions to each of seqs[n_seqs] (host, distinct), reserving
+ * a block whenever a sequence crosses a 16-token boundary.  All-or-nothing
+ * over the whole list.  first_pos_out (host, may be NULL) receives each
+ * sequence's first new position (its old length).  Errors: INVALID, RANGE,
+ * OOM. */
+pkv_status pkv_extend(pkv_cache* cache, const int32_t* seqs, int32_t n_seqs,
+                      int32_t n_new, int64_t* first_pos_out);
+
+/* Return seq's blocks to the tail of the free list; its length becomes 0. */
+pkv_status pkv_free_seq(pkv_cache* cache, int32_t seq);
+
+/* Export block tables: table_out (host, n_seqs x max_blocks_per_seq int32,
+ * padded with -1) and lens_out (host, n_seqs int64; may be NULL). */
+pkv_status pkv_block_table(const pkv_cache* cache, const int32_t* seqs, int32_t n_seqs,
+                           int32_t* table_out, int64_t* lens_out);
+
+/* Number of free blocks. Returns -1 for a NULL cache. */
+int32_t pkv_num_free_blocks(const pkv_cache* cache);
+
+/* Copy the free list, head first, into out (host, capacity cap).  Returns the
+ * number of entries copied, or a negative status. */
+int32_t pkv_free_list(const pkv_cache* cache, int32_t* out, int32_t cap);
+
+/* ---------------------------------------------------------------------------
+ * Rotary table ([InferScale] §2 and §3.3: keys are rotated with the model's
+ * own rotary tables).  theta_i = base^(-2i/d); cos_out[p][i] and sin_out[p][i]
+ * (host, max_pos x d/2 float each) are cos and sin of p*theta_i evaluated in
+ * double precision and rounded once to float.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_rope_table(int32_t head_dim, double base, int32_t max_pos,
+                          float* cos_out, float* sin_out);
+
+/* ---------------------------------------------------------------------------
+ * Inject ([InferScale] §3, connector steps 2-3 and the worker-side scatter
+ * copy through the slot mapping; §3.3 and §5.1, chunked RoPE): for every run
+ * token and every layer in [layer_begin, layer_end):
+ *   K[slot(seq, p)] = round(R_p * k_src),  V[slot(seq, p)] = v_src  (bit copy)
+ * with slot(seq, p) = table[seq][p / 16] * 16 + p % 16 taken from the host
+ * allocator, R_p the rotation by the rotary table (cos, sin: device, max_pos
+ * x d/2 float) applied in float32 without fused multiply-add, and round the
+ * round-to-nearest-even store into the pool dtype.  Each run must lie within
+ * its sequence's reserved blocks and below max_pos; two tokens of one call
+ * may not share a slot (PKV_E_OVERLAP).  Afterwards each sequence's length is
+ * max(length, dst_pos + n_tokens).  Runs are host memory.  The device
+ * workspace (d_ws, ws_bytes >= pkv_inject_workspace_bytes(runs, n_runs)) holds
+ * the per-block write plan; it must not be reused by other work until this
+ * call's kernels finish (stream order suffices).
+ * ------------------------------------------------------------------------- */
+size_t pkv_inject_workspace_bytes(const pkv_run* runs, int32_t n_runs);
+
+pkv_status pkv_inject(pkv_cache* cache, const pkv_pool* pool, const pkv_src* src,
+                      const pkv_run* runs, int32_t n_runs, int32_t layer_begin,
+                      int32_t layer_end, int32_t rope_mode, const float* d_cos,
+                      const float* d_sin, int32_t max_pos, void* d_ws, size_t ws_bytes,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Append ([InferScale] §2 and [KV essay] "The fix": decoding appends one K/V
+ * entry per generated token): for b < n_seqs and t < n_new, token t of
+ * sequence b lands at position p = d_first_pos[b] + t through row b of the
+ * device block table (d_tables, int32, row stride table_stride):
+ *   K[slot] = round(R_p * k_new[b][t]),  V[slot] = v_new[b][t]
+ * k_new, v_new: device, [n_seqs][n_new][n_kv_heads][head_dim] in pool dtype.
+ * d_first_pos: device int32[n_seqs] (the first_pos_out of pkv_extend).
+ * Rows of tokens at positions >= max_pos or beyond the table are skipped.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* d_tables,
+                         int32_t table_stride, const int32_t* d_first_pos, int32_t n_seqs,
+                         int32_t n_new, const void* d_k_new, const void* d_v_new,
+                         int32_t rope_mode, const float* d_cos, const float* d_sin,
+                         int32_t max_pos, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode attention ([KV essay] "First, what K and V are": softmax(q K^T /
+ * sqrt(d)) V for one query row per head; "Paged attention": K/V read through
+ * the block table; "What the cache costs" and [KV management]: query head h
+ * reads KV head h / (n_q_heads / n_kv_heads)).  Sequence b attends to its
+ * lens[b] cached tokens (positions 0 .. lens[b]-1, no mask).
+ *
+ * A plan fixes the lengths (host, int64 lens[n_seqs]) and splits every
+ * sequence into 16-aligned token ranges of part_tokens tokens (0 = chosen
+ * from the total work), which run on separate workgroups; their softmax
+ * states (running max, sum, unnormalised output) are merged by log-sum-exp in
+ * ascending range order.  Upload the plan into a device workspace once, then
+ * call pkv_decode_attention for every layer that shares the lengths.
+ *
+ * Outputs: d_out (device float [n_seqs][n_q_heads][head_dim]) and, if not
+ * NULL, d_lse (device float [n_seqs][n_q_heads], ln of the sum of exp of the
+ * scaled scores).  A sequence of length 0 gets out = 0, lse = -inf.
+ * q: device [n_seqs][n_q_heads][head_dim] in the pool dtype, already rotated
+ * to its own position.  scale <= 0 selects 1/sqrt(head_dim).
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_decode_plan_create(const int64_t* lens, int32_t n_seqs, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim, int32_t part_tokens,
+                                  pkv_plan** out);
+
+void pkv_decode_plan_destroy(pkv_plan* plan);
+
+/* Number of work items (sequence token ranges) of a plan; -1 for NULL. */
+int32_t pkv_decode_plan_items(const pkv_plan* plan);
+
+/* Token range length the plan chose; -1 for NULL. */
+int32_t pkv_decode_plan_part_tokens(const pkv_plan* plan);
+
+/* Device workspace a plan needs (work list + float partials). */
+size_t pkv_decode_workspace_bytes(const pkv_plan* plan);
+
+/* Copy the plan's work list into the workspace (asynchronous on stream; the
+ * host copy is kept in library-owned pinned memory until it has landed). */
+pkv_status pkv_decode_plan_upload(pkv_plan* plan, void* d_ws, size_t ws_bytes, void* stream);
+
+pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int32_t layer,
+                                const void* d_q, float scale, const int32_t* d_tables,
+                                int32_t table_stride, float* d_out, float* d_lse, void* d_ws,
+                                size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Measurement helper: a streaming 16-byte-per-lane read of n_bytes (a
+ * multiple of 16) from d_src, reduced into d_sink (device, >= 16 bytes), to
+ * measure the achievable HBM read rate in the same process.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_bw_probe(const void* d_src, size_t n_bytes, void* d_sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

@@ -131,3 +131,38 @@ def gather_sequence(k_pool, v_pool, spec: PoolSpec, layer: int, table_row, lengt
             k[p, i] = k_pool[k_element_offsets(spec, layer, blk, h, t)]
             v[p, i] = v_pool[v_element_offsets(spec, layer, blk, h, t)]
     return k, v
+
+
+def plane_tokens_k(plane, spec: PoolSpec) -> np.ndarray:
+    """A whole K plane (16*d raw elements) as [16 tokens][d].
+
+    The plane is d/X chunks of [16 tokens][X dims]: reshape to
+    (d/X, 16, X), bring the token axis first, merge the chunk and dim axes.
+    """
+    x = chunk_elems(spec.dtype)
+    return plane.reshape(spec.head_dim // x, BLOCK_TOKENS, x).transpose(1, 0, 2).reshape(
+        BLOCK_TOKENS, spec.head_dim)
+
+
+def plane_tokens_v(plane, spec: PoolSpec) -> np.ndarray:
+    """A whole V plane (16*d raw elements, dimension-major) as [16 tokens][d]."""
+    return plane.reshape(spec.head_dim, BLOCK_TOKENS).T
+
+
+def gather_sequence_planes(k_pool, v_pool, spec: PoolSpec, layer: int, table_row, length: int,
+                           heads=None):
+    """Same result as gather_sequence, one whole plane at a time."""
+    heads = list(range(spec.n_kv_heads)) if heads is None else list(heads)
+    n_blocks = -(-length // BLOCK_TOKENS)
+    plane = BLOCK_TOKENS * spec.head_dim
+    k = np.empty((n_blocks * BLOCK_TOKENS, len(heads), spec.head_dim), spec.storage_dtype())
+    v = np.empty_like(k)
+    for i in range(n_blocks):
+        blk = int(table_row[i])
+        if blk < 0:
+            raise IndexError("logical block %d has no physical block" % i)
+        for hi, h in enumerate(heads):
+            base = spec.plane_base(layer, blk, h)
+            k[i * BLOCK_TOKENS:(i + 1) * BLOCK_TOKENS, hi] = plane_tokens_k(k_pool[base:base + plane], spec)
+            v[i * BLOCK_TOKENS:(i + 1) * BLOCK_TOKENS, hi] = plane_tokens_v(v_pool[base:base + plane], spec)
+    return k[:length], v[:length]

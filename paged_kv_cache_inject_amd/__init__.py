@@ -1,0 +1,332 @@
+"""Python binding of libpkv (include/pkv.h): argument marshalling only.
+
+Every function here has the name of the C entry point it calls and forwards
+its arguments: torch tensors become device or host pointers, the current
+torch stream becomes the HIP stream, and a negative status raises PkvError
+with the library's message.  No step of the hot path runs in Python.
+
+Loading fails loudly when the built library is missing: there is no
+fallback.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PKV_OK = 0
+PKV_E_INVALID = -1
+PKV_E_OOM = -2
+PKV_E_RANGE = -3
+PKV_E_OVERLAP = -4
+PKV_E_WORKSPACE = -5
+PKV_E_HIP = -6
+PKV_E_UNSUPPORTED = -7
+STATUS_NAMES = {0: "OK", -1: "INVALID", -2: "OOM", -3: "RANGE", -4: "OVERLAP",
+                -5: "WORKSPACE", -6: "HIP", -7: "UNSUPPORTED"}
+
+PKV_F32, PKV_BF16, PKV_F16 = 0, 1, 2
+DTYPE_CODES = {"f32": PKV_F32, "bf16": PKV_BF16, "f16": PKV_F16}
+PKV_ROPE_PAIRS, PKV_ROPE_HALVES, PKV_ROPE_NONE = 0, 1, 2
+ROPE_CODES = {"pairs": PKV_ROPE_PAIRS, "halves": PKV_ROPE_HALVES, "none": PKV_ROPE_NONE}
+BLOCK_TOKENS = 16
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s (%d): %s" % (STATUS_NAMES.get(status, "?"), status, msg))
+        self.status = status
+        self.code = STATUS_NAMES.get(status, "?")
+
+
+class pkv_pool(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("_reserved", ctypes.c_int32),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("layer_stride", ctypes.c_int64), ("block_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64)]
+
+
+class pkv_src(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("layer_stride", ctypes.c_int64), ("token_stride", ctypes.c_int64),
+                ("n_tokens", ctypes.c_int64)]
+
+
+class pkv_run(ctypes.Structure):
+    _fields_ = [("seq", ctypes.c_int32), ("n_tokens", ctypes.c_int32),
+                ("dst_pos", ctypes.c_int32), ("_reserved", ctypes.c_int32),
+                ("src_token", ctypes.c_int64)]
+
+
+class pkv_cache_config(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("max_seqs", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("_reserved", ctypes.c_int32),
+                ("free_list_seed", ctypes.c_uint64)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "pkv_abi_version": (_I32, []),
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_kv_bytes": (ctypes.c_uint64, [_I32, _I32, _I32, _I32, _I64]),
+    "pkv_cache_create": (_I32, [ctypes.POINTER(pkv_cache_config), ctypes.POINTER(_P)]),
+    "pkv_cache_destroy": (None, [_P]),
+    "pkv_alloc_blocks": (_I32, [_P, _I32, _I64]),
+    "pkv_set_blocks": (_I32, [_P, _I32, _P, _I32, _I64]),
+    "pkv_extend": (_I32, [_P, _P, _I32, _I32, _P]),
+    "pkv_free_seq": (_I32, [_P, _I32]),
+    "pkv_block_table": (_I32, [_P, _P, _I32, _P, _P]),
+    "pkv_num_free_blocks": (_I32, [_P]),
+    "pkv_free_list": (_I32, [_P, _P, _I32]),
+    "pkv_rope_table": (_I32, [_I32, ctypes.c_double, _I32, _P, _P]),
+    "pkv_inject_workspace_bytes": (_SZ, [_P, _I32]),
+    "pkv_inject": (_I32, [_P, ctypes.POINTER(pkv_pool), ctypes.POINTER(pkv_src), _P, _I32,
+                          _I32, _I32, _I32, _P, _P, _I32, _P, _SZ, _P]),
+    "pkv_append_kv": (_I32, [ctypes.POINTER(pkv_pool), _I32, _P, _I32, _P, _I32, _I32, _P, _P,
+                             _I32, _P, _P, _I32, _P]),
+    "pkv_decode_plan_create": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_P)]),
+    "pkv_decode_plan_destroy": (None, [_P]),
+    "pkv_decode_plan_items": (_I32, [_P]),
+    "pkv_decode_plan_part_tokens": (_I32, [_P]),
+    "pkv_decode_workspace_bytes": (_SZ, [_P]),
+    "pkv_decode_plan_upload": (_I32, [_P, _P, _SZ, _P]),
+    "pkv_decode_attention": (_I32, [_P, ctypes.POINTER(pkv_pool), _I32, _P, ctypes.c_float, _P,
+                                    _I32, _P, _P, _P, _SZ, _P]),
+    "pkv_bw_probe": (_I32, [_P, _SZ, _P, _P]),
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpkv.so; raises if it is missing or lacks a declared symbol."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError("libpkv.so is not built (%s); run paged_kv_cache_inject_amd/build.py"
+                          % path)
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status < 0:
+        raise PkvError(status, _lib.pkv_last_error().decode())
+    return status
+
+
+def _ptr(t):
+    """Device or host address of a torch tensor or numpy array (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if hasattr(t, "data_ptr"):
+        return t.data_ptr()
+    return t.ctypes.data
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# Library
+# ---------------------------------------------------------------------------
+def pkv_abi_version() -> int:
+    return load_library().pkv_abi_version()
+
+
+def pkv_last_error() -> str:
+    return load_library().pkv_last_error().decode()
+
+
+def pkv_kv_bytes(n_layers, n_kv_heads, head_dim, elem_bytes, n_tokens) -> int:
+    return load_library().pkv_kv_bytes(n_layers, n_kv_heads, head_dim, elem_bytes, n_tokens)
+
+
+# ---------------------------------------------------------------------------
+# Allocator
+# ---------------------------------------------------------------------------
+def pkv_cache_create(num_blocks, max_seqs, max_blocks_per_seq, free_list_seed=0):
+    lib = load_library()
+    cfg = pkv_cache_config(num_blocks, max_seqs, max_blocks_per_seq, 0, free_list_seed)
+    h = ctypes.c_void_p()
+    _check(lib.pkv_cache_create(ctypes.byref(cfg), ctypes.byref(h)))
+    return h
+
+
+def pkv_cache_destroy(cache):
+    load_library().pkv_cache_destroy(cache)
+
+
+def pkv_alloc_blocks(cache, seq, n_tokens):
+    _check(load_library().pkv_alloc_blocks(cache, seq, n_tokens))
+
+
+def pkv_set_blocks(cache, seq, ids, length):
+    import numpy as np
+    a = np.ascontiguousarray(ids, dtype=np.int32)
+    _check(load_library().pkv_set_blocks(cache, seq, a.ctypes.data, len(a), length))
+
+
+def pkv_extend(cache, seqs, n_new):
+    """Returns the int64 array of first new positions."""
+    import numpy as np
+    s = np.ascontiguousarray(seqs, dtype=np.int32)
+    first = np.zeros(len(s), dtype=np.int64)
+    _check(load_library().pkv_extend(cache, s.ctypes.data, len(s), n_new, first.ctypes.data))
+    return first
+
+
+def pkv_free_seq(cache, seq):
+    _check(load_library().pkv_free_seq(cache, seq))
+
+
+def pkv_block_table(cache, seqs, max_blocks_per_seq):
+    """Returns (int32 table [n][max_blocks_per_seq], int64 lens [n])."""
+    import numpy as np
+    s = np.ascontiguousarray(seqs, dtype=np.int32)
+    table = np.empty((len(s), max_blocks_per_seq), dtype=np.int32)
+    lens = np.empty(len(s), dtype=np.int64)
+    _check(load_library().pkv_block_table(cache, s.ctypes.data, len(s), table.ctypes.data,
+                                          lens.ctypes.data))
+    return table, lens
+
+
+def pkv_num_free_blocks(cache) -> int:
+    return load_library().pkv_num_free_blocks(cache)
+
+
+def pkv_free_list(cache):
+    import numpy as np
+    n = pkv_num_free_blocks(cache)
+    out = np.empty(max(n, 1), dtype=np.int32)
+    got = _check(load_library().pkv_free_list(cache, out.ctypes.data, n))
+    return out[:got].tolist()
+
+
+# ---------------------------------------------------------------------------
+# Rotary table
+# ---------------------------------------------------------------------------
+def pkv_rope_table(head_dim, base, max_pos):
+    """Returns (cos, sin) as float32 numpy arrays [max_pos][head_dim/2]."""
+    import numpy as np
+    cos = np.empty((max_pos, head_dim // 2), dtype=np.float32)
+    sin = np.empty((max_pos, head_dim // 2), dtype=np.float32)
+    _check(load_library().pkv_rope_table(head_dim, base, max_pos, cos.ctypes.data,
+                                         sin.ctypes.data))
+    return cos, sin
+
+
+# ---------------------------------------------------------------------------
+# Descriptors
+# ---------------------------------------------------------------------------
+def make_pool(k, v, n_layers, num_blocks, n_kv_heads, head_dim, dtype,
+              layer_stride, block_stride, head_stride) -> pkv_pool:
+    return pkv_pool(n_layers, num_blocks, n_kv_heads, head_dim, DTYPE_CODES[dtype], 0,
+                    _ptr(k), _ptr(v), layer_stride, block_stride, head_stride)
+
+
+def make_src(k, v, layer_stride, token_stride, n_tokens) -> pkv_src:
+    return pkv_src(_ptr(k), _ptr(v), layer_stride, token_stride, n_tokens)
+
+
+def make_runs(runs):
+    arr = (pkv_run * max(1, len(runs)))()
+    for i, (seq, n, pos, src) in enumerate(runs):
+        arr[i] = pkv_run(int(seq), int(n), int(pos), 0, int(src))
+    return arr
+
+
+# ---------------------------------------------------------------------------
+# Inject / append
+# ---------------------------------------------------------------------------
+def pkv_inject_workspace_bytes(runs) -> int:
+    arr = runs if isinstance(runs, ctypes.Array) else make_runs(runs)
+    return load_library().pkv_inject_workspace_bytes(arr, len(arr))
+
+
+def pkv_inject(cache, pool: pkv_pool, src: pkv_src, runs, layer_begin, layer_end, rope_mode,
+               cos, sin, max_pos, workspace, stream=None):
+    arr = runs if isinstance(runs, ctypes.Array) else make_runs(runs)
+    n = len(arr) if not isinstance(runs, (list, tuple)) else len(runs)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().pkv_inject(cache, ctypes.byref(pool), ctypes.byref(src), arr, n,
+                                     layer_begin, layer_end, ROPE_CODES.get(rope_mode, rope_mode),
+                                     _ptr(cos), _ptr(sin), max_pos, _ptr(workspace), ws_bytes,
+                                     _stream(stream)))
+
+
+def pkv_append_kv(pool: pkv_pool, layer, tables, first_pos, n_new, k_new, v_new, rope_mode,
+                  cos, sin, max_pos, stream=None):
+    _check(load_library().pkv_append_kv(ctypes.byref(pool), layer, _ptr(tables),
+                                        tables.shape[1], _ptr(first_pos), first_pos.shape[0],
+                                        n_new, _ptr(k_new), _ptr(v_new),
+                                        ROPE_CODES.get(rope_mode, rope_mode), _ptr(cos), _ptr(sin),
+                                        max_pos, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Decode
+# ---------------------------------------------------------------------------
+def pkv_decode_plan_create(lens, n_q_heads, n_kv_heads, head_dim, part_tokens=0):
+    import numpy as np
+    a = np.ascontiguousarray(lens, dtype=np.int64)
+    h = ctypes.c_void_p()
+    _check(load_library().pkv_decode_plan_create(a.ctypes.data, len(a), n_q_heads, n_kv_heads,
+                                                 head_dim, part_tokens, ctypes.byref(h)))
+    return h
+
+
+def pkv_decode_plan_destroy(plan):
+    load_library().pkv_decode_plan_destroy(plan)
+
+
+def pkv_decode_plan_items(plan) -> int:
+    return load_library().pkv_decode_plan_items(plan)
+
+
+def pkv_decode_plan_part_tokens(plan) -> int:
+    return load_library().pkv_decode_plan_part_tokens(plan)
+
+
+def pkv_decode_workspace_bytes(plan) -> int:
+    return load_library().pkv_decode_workspace_bytes(plan)
+
+
+def pkv_decode_plan_upload(plan, workspace, stream=None):
+    _check(load_library().pkv_decode_plan_upload(plan, _ptr(workspace),
+                                                 workspace.numel() * workspace.element_size(),
+                                                 _stream(stream)))
+
+
+def pkv_decode_attention(plan, pool: pkv_pool, layer, q, tables, out, lse, workspace,
+                         scale=0.0, stream=None):
+    _check(load_library().pkv_decode_attention(plan, ctypes.byref(pool), layer, _ptr(q),
+                                               float(scale), _ptr(tables), tables.shape[1],
+                                               _ptr(out), _ptr(lse), _ptr(workspace),
+                                               workspace.numel() * workspace.element_size(),
+                                               _stream(stream)))
+
+
+def pkv_bw_probe(src, sink, stream=None):
+    _check(load_library().pkv_bw_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                       _stream(stream)))

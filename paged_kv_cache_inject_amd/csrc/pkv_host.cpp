@@ -1,0 +1,667 @@
+// Host runtime of libpkv: block allocator, inject write planner, decode split
+// planner, rotary table, argument validation and the C ABI (include/pkv.h).
+//
+// The allocator follows "LLM Inference: KV Caching" ("Paged attention": free
+// list, per-sequence block table, a block handed out when the sequence
+// reaches it) and "Inside LLM Inference Engines" ("PagedAttention",
+// "Continuous Batching": blocks return to the pool when a sequence ends),
+// with a FIFO free list so that the resulting tables are reproducible.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <deque>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "pkv_internal.h"
+
+using pkv::DecodeItem;
+using pkv::InjectDesc;
+using pkv::MergeSeq;
+using pkv::kBlock;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pkv_status ok() {
+  g_last_error.clear();
+  return PKV_OK;
+}
+
+pkv_status hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t blocks_for(int64_t n_tokens) { return (n_tokens + kBlock - 1) / kBlock; }
+
+int elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_BF16: return 2;
+    case PKV_F16: return 2;
+    default: return 0;
+  }
+}
+
+// splitmix64 (S. Vigna's published definition): one 64-bit output per call.
+struct SplitMix64 {
+  uint64_t state;
+  uint64_t next() {
+    uint64_t z = (state += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  }
+};
+
+// Pinned host staging for a small H2D upload, reusable once the previous copy
+// out of it has landed (tracked with an event on the copying stream).
+struct Staging {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+
+  ~Staging() {
+    if (pending && done) (void)hipEventSynchronize(done);
+    if (host) (void)hipHostFree(host);
+    if (done) (void)hipEventDestroy(done);
+  }
+
+  // Returns a host buffer of >= bytes that no in-flight copy reads.
+  pkv_status acquire(size_t bytes, void** out) {
+    if (!done) {
+      hipError_t e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+    }
+    if (pending) {
+      hipError_t e = hipEventSynchronize(done);
+      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+      pending = false;
+    }
+    if (bytes > cap) {
+      if (host) (void)hipHostFree(host);
+      host = nullptr;
+      cap = 0;
+      size_t want = std::max<size_t>(bytes, 4096);
+      hipError_t e = hipHostMalloc(&host, want, hipHostMallocDefault);
+      if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
+      cap = want;
+    }
+    *out = host;
+    return PKV_OK;
+  }
+
+  pkv_status upload(void* dst, size_t bytes, hipStream_t stream) {
+    hipError_t e = hipMemcpyAsync(dst, host, bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    e = hipEventRecord(done, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    pending = true;
+    return PKV_OK;
+  }
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+struct pkv_cache {
+  int32_t num_blocks = 0;
+  int32_t max_seqs = 0;
+  int32_t max_blocks_per_seq = 0;
+  std::deque<int32_t> free_list;
+  std::vector<std::vector<int32_t>> tables;
+  std::vector<int64_t> lens;
+  std::vector<int32_t> desc_of_block;  // inject planner scratch, -1 when idle
+  Staging staging;
+};
+
+struct pkv_plan {
+  int32_t n_seqs = 0, n_q_heads = 0, n_kv_heads = 0, head_dim = 0, part_tokens = 0;
+  int32_t n_slots = 0;
+  std::vector<DecodeItem> items;
+  std::vector<MergeSeq> merges;
+  size_t off_items = 0, off_merges = 0, off_part_o = 0, off_part_ml = 0, ws_bytes = 0;
+  Staging staging;
+};
+
+namespace {
+
+pkv_status check_seq(const pkv_cache* c, int32_t seq) {
+  if (!c) return fail(PKV_E_INVALID, "null cache");
+  if (seq < 0 || seq >= c->max_seqs)
+    return fail(PKV_E_INVALID, "sequence %d out of range [0, %d)", seq, c->max_seqs);
+  return PKV_OK;
+}
+
+// Validates a pool descriptor: shapes, dtype, alignment.
+pkv_status check_pool(const pkv_pool* p) {
+  if (!p) return fail(PKV_E_INVALID, "null pool");
+  const int eb = elem_bytes(p->dtype);
+  if (!eb) return fail(PKV_E_INVALID, "unknown pool dtype %d", p->dtype);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(PKV_E_UNSUPPORTED, "head_dim %d (supported: 64, 128)", p->head_dim);
+  if (p->n_layers <= 0 || p->num_blocks <= 0 || p->n_kv_heads <= 0)
+    return fail(PKV_E_INVALID, "pool sizes must be positive");
+  if (!p->k || !p->v) return fail(PKV_E_INVALID, "null pool pointer");
+  if ((reinterpret_cast<uintptr_t>(p->k) | reinterpret_cast<uintptr_t>(p->v)) & 15)
+    return fail(PKV_E_INVALID, "pool base pointers must be 16-byte aligned");
+  const int64_t plane = int64_t(kBlock) * p->head_dim;
+  if (p->layer_stride < 0 || p->block_stride < 0 || p->head_stride < 0)
+    return fail(PKV_E_INVALID, "negative pool stride");
+  if (((p->layer_stride | p->block_stride | p->head_stride) * eb) % 16)
+    return fail(PKV_E_INVALID, "pool strides must be multiples of 16 bytes");
+  if (p->n_kv_heads > 1 && p->head_stride < plane)
+    return fail(PKV_E_INVALID, "head_stride smaller than a plane");
+  if (p->num_blocks > 1 && p->block_stride < plane)
+    return fail(PKV_E_INVALID, "block_stride smaller than a plane");
+  return PKV_OK;
+}
+
+pkv_status check_rope(int32_t mode, const float* cos, const float* sin, int32_t max_pos) {
+  if (mode != PKV_ROPE_PAIRS && mode != PKV_ROPE_HALVES && mode != PKV_ROPE_NONE)
+    return fail(PKV_E_INVALID, "unknown rope mode %d", mode);
+  if (mode != PKV_ROPE_NONE && (!cos || !sin))
+    return fail(PKV_E_INVALID, "rotary table pointers are null");
+  if (max_pos < 0) return fail(PKV_E_INVALID, "negative max_pos");
+  return PKV_OK;
+}
+
+// Upper bound of destination blocks touched by a list of runs.
+int64_t inject_desc_bound(const pkv_run* runs, int32_t n_runs) {
+  int64_t n = 0;
+  for (int32_t i = 0; i < n_runs; ++i)
+    if (runs[i].n_tokens > 0) n += blocks_for(runs[i].n_tokens) + 1;
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+uint64_t pkv_kv_bytes(int32_t n_layers, int32_t n_kv_heads, int32_t head_dim, int32_t elem_b,
+                      int64_t n_tokens) {
+  if (n_layers < 0 || n_kv_heads < 0 || head_dim < 0 || elem_b < 0 || n_tokens < 0) return 0;
+  return 2ull * uint64_t(n_layers) * uint64_t(n_kv_heads) * uint64_t(head_dim) *
+         uint64_t(elem_b) * uint64_t(n_tokens);
+}
+
+// ---------------------------------------------------------------------------
+// Allocator
+// ---------------------------------------------------------------------------
+pkv_status pkv_cache_create(const pkv_cache_config* cfg, pkv_cache** out) {
+  if (!cfg || !out) return fail(PKV_E_INVALID, "null argument");
+  if (cfg->num_blocks <= 0 || cfg->max_seqs <= 0 || cfg->max_blocks_per_seq <= 0)
+    return fail(PKV_E_INVALID, "cache sizes must be positive");
+  pkv_cache* c = new (std::nothrow) pkv_cache();
+  if (!c) return fail(PKV_E_INVALID, "out of host memory");
+  c->num_blocks = cfg->num_blocks;
+  c->max_seqs = cfg->max_seqs;
+  c->max_blocks_per_seq = cfg->max_blocks_per_seq;
+  std::vector<int32_t> order(cfg->num_blocks);
+  for (int32_t i = 0; i < cfg->num_blocks; ++i) order[i] = i;
+  if (cfg->free_list_seed != 0) {
+    SplitMix64 g{cfg->free_list_seed};
+    for (int64_t i = int64_t(cfg->num_blocks) - 1; i > 0; --i) {
+      uint64_t j = g.next() % uint64_t(i + 1);
+      std::swap(order[i], order[j]);
+    }
+  }
+  c->free_list.assign(order.begin(), order.end());
+  c->tables.resize(cfg->max_seqs);
+  c->lens.assign(cfg->max_seqs, 0);
+  *out = c;
+  return ok();
+}
+
+void pkv_cache_destroy(pkv_cache* cache) { delete cache; }
+
+pkv_status pkv_alloc_blocks(pkv_cache* c, int32_t seq, int64_t n_tokens) {
+  if (pkv_status st = check_seq(c, seq)) return st;
+  if (n_tokens < 0) return fail(PKV_E_INVALID, "negative token count");
+  const int64_t want = blocks_for(n_tokens);
+  if (want > c->max_blocks_per_seq)
+    return fail(PKV_E_RANGE, "%lld blocks exceed max_blocks_per_seq %d", (long long)want,
+                c->max_blocks_per_seq);
+  auto& t = c->tables[seq];
+  const int64_t need = std::max<int64_t>(0, want - int64_t(t.size()));
+  if (need > int64_t(c->free_list.size()))
+    return fail(PKV_E_OOM, "need %lld blocks, %zu free", (long long)need, c->free_list.size());
+  for (int64_t i = 0; i < need; ++i) {
+    t.push_back(c->free_list.front());
+    c->free_list.pop_front();
+  }
+  return ok();
+}
+
+pkv_status pkv_set_blocks(pkv_cache* c, int32_t seq, const int32_t* ids, int32_t n_ids,
+                          int64_t len) {
+  if (pkv_status st = check_seq(c, seq)) return st;
+  if (n_ids < 0 || (n_ids > 0 && !ids)) return fail(PKV_E_INVALID, "bad id list");
+  if (!c->tables[seq].empty()) return fail(PKV_E_INVALID, "sequence %d already owns blocks", seq);
+  if (n_ids > c->max_blocks_per_seq)
+    return fail(PKV_E_RANGE, "%d blocks exceed max_blocks_per_seq %d", n_ids,
+                c->max_blocks_per_seq);
+  if (len < 0 || len > int64_t(n_ids) * kBlock)
+    return fail(PKV_E_RANGE, "length %lld does not fit %d blocks", (long long)len, n_ids);
+  std::vector<uint8_t> is_free(c->num_blocks, 0), taken(c->num_blocks, 0);
+  for (int32_t b : c->free_list) is_free[b] = 1;
+  for (int32_t i = 0; i < n_ids; ++i) {
+    const int32_t b = ids[i];
+    if (b < 0 || b >= c->num_blocks) return fail(PKV_E_INVALID, "block id %d out of range", b);
+    if (!is_free[b]) return fail(PKV_E_INVALID, "block id %d is not free", b);
+    if (taken[b]) return fail(PKV_E_INVALID, "block id %d repeated", b);
+    taken[b] = 1;
+  }
+  std::deque<int32_t> rest;
+  for (int32_t b : c->free_list)
+    if (!taken[b]) rest.push_back(b);
+  c->free_list.swap(rest);
+  c->tables[seq].assign(ids, ids + n_ids);
+  c->lens[seq] = len;
+  return ok();
+}
+
+pkv_status pkv_extend(pkv_cache* c, const int32_t* seqs, int32_t n_seqs, int32_t n_new,
+                      int64_t* first_pos_out) {
+  if (!c) return fail(PKV_E_INVALID, "null cache");
+  if (n_seqs < 0 || (n_seqs > 0 && !seqs) || n_new < 0)
+    return fail(PKV_E_INVALID, "bad sequence list or count");
+  std::vector<uint8_t> seen(c->max_seqs, 0);
+  int64_t total = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    if (pkv_status st = check_seq(c, seqs[i])) return st;
+    if (seen[seqs[i]]) return fail(PKV_E_INVALID, "sequence %d repeated", seqs[i]);
+    seen[seqs[i]] = 1;
+    const int64_t want = blocks_for(c->lens[seqs[i]] + n_new);
+    if (want > c->max_blocks_per_seq)
+      return fail(PKV_E_RANGE, "sequence %d would need %lld blocks", seqs[i], (long long)want);
+    total += std::max<int64_t>(0, want - int64_t(c->tables[seqs[i]].size()));
+  }
+  if (total > int64_t(c->free_list.size()))
+    return fail(PKV_E_OOM, "need %lld blocks, %zu free", (long long)total, c->free_list.size());
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int32_t s = seqs[i];
+    pkv_alloc_blocks(c, s, c->lens[s] + n_new);
+    if (first_pos_out) first_pos_out[i] = c->lens[s];
+    c->lens[s] += n_new;
+  }
+  return ok();
+}
+
+pkv_status pkv_free_seq(pkv_cache* c, int32_t seq) {
+  if (pkv_status st = check_seq(c, seq)) return st;
+  for (int32_t b : c->tables[seq]) c->free_list.push_back(b);
+  c->tables[seq].clear();
+  c->lens[seq] = 0;
+  return ok();
+}
+
+pkv_status pkv_block_table(const pkv_cache* c, const int32_t* seqs, int32_t n_seqs,
+                           int32_t* table_out, int64_t* lens_out) {
+  if (!c) return fail(PKV_E_INVALID, "null cache");
+  if (n_seqs < 0 || (n_seqs > 0 && (!seqs || !table_out)))
+    return fail(PKV_E_INVALID, "bad arguments");
+  for (int32_t i = 0; i < n_seqs; ++i)
+    if (pkv_status st = check_seq(c, seqs[i])) return st;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const auto& t = c->tables[seqs[i]];
+    int32_t* row = table_out + int64_t(i) * c->max_blocks_per_seq;
+    for (int32_t j = 0; j < c->max_blocks_per_seq; ++j)
+      row[j] = j < int32_t(t.size()) ? t[j] : -1;
+    if (lens_out) lens_out[i] = c->lens[seqs[i]];
+  }
+  return ok();
+}
+
+int32_t pkv_num_free_blocks(const pkv_cache* c) {
+  return c ? int32_t(c->free_list.size()) : -1;
+}
+
+int32_t pkv_free_list(const pkv_cache* c, int32_t* out, int32_t cap) {
+  if (!c || (cap > 0 && !out) || cap < 0) return fail(PKV_E_INVALID, "bad arguments");
+  int32_t n = 0;
+  for (int32_t b : c->free_list) {
+    if (n >= cap) break;
+    out[n++] = b;
+  }
+  ok();
+  return n;
+}
+
+// ---------------------------------------------------------------------------
+// Rotary table
+// ---------------------------------------------------------------------------
+pkv_status pkv_rope_table(int32_t head_dim, double base, int32_t max_pos, float* cos_out,
+                          float* sin_out) {
+  if (head_dim <= 0 || head_dim % 2 || max_pos < 0 || !(base > 0.0))
+    return fail(PKV_E_INVALID, "bad rotary table shape or base");
+  if (max_pos > 0 && (!cos_out || !sin_out)) return fail(PKV_E_INVALID, "null output");
+  const int32_t half = head_dim / 2;
+  std::vector<double> theta(half);
+  for (int32_t i = 0; i < half; ++i) theta[i] = std::pow(base, -2.0 * double(i) / head_dim);
+  for (int64_t p = 0; p < max_pos; ++p) {
+    for (int32_t i = 0; i < half; ++i) {
+      const double a = double(p) * theta[i];
+      cos_out[p * half + i] = float(std::cos(a));
+      sin_out[p * half + i] = float(std::sin(a));
+    }
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Inject
+// ---------------------------------------------------------------------------
+size_t pkv_inject_workspace_bytes(const pkv_run* runs, int32_t n_runs) {
+  if (n_runs <= 0 || !runs) return 256;
+  return align_up(size_t(inject_desc_bound(runs, n_runs)) * sizeof(InjectDesc), 256);
+}
+
+pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
+                      const pkv_run* runs, int32_t n_runs, int32_t layer_begin,
+                      int32_t layer_end, int32_t rope_mode, const float* d_cos,
+                      const float* d_sin, int32_t max_pos, void* d_ws, size_t ws_bytes,
+                      void* stream) {
+  if (!c) return fail(PKV_E_INVALID, "null cache");
+  if (pkv_status st = check_pool(pool)) return st;
+  if (pkv_status st = check_rope(rope_mode, d_cos, d_sin, max_pos)) return st;
+  if (!src || !src->k || !src->v) return fail(PKV_E_INVALID, "null source");
+  const int eb = elem_bytes(pool->dtype);
+  if ((reinterpret_cast<uintptr_t>(src->k) | reinterpret_cast<uintptr_t>(src->v)) & 15)
+    return fail(PKV_E_INVALID, "source pointers must be 16-byte aligned");
+  if (((src->layer_stride | src->token_stride) * eb) % 16 || src->layer_stride < 0 ||
+      src->token_stride < int64_t(pool->n_kv_heads) * pool->head_dim)
+    return fail(PKV_E_INVALID, "bad source strides");
+  if (n_runs < 0 || (n_runs > 0 && !runs)) return fail(PKV_E_INVALID, "bad run list");
+  if (layer_begin < 0 || layer_end > pool->n_layers || layer_begin > layer_end)
+    return fail(PKV_E_INVALID, "layer range [%d, %d) outside [0, %d)", layer_begin, layer_end,
+                pool->n_layers);
+
+  // Resolve every run token to (physical block, slot in block); build one
+  // write descriptor per destination block.
+  std::vector<InjectDesc> descs;
+  if (int64_t(c->desc_of_block.size()) < int64_t(pool->num_blocks))
+    c->desc_of_block.assign(pool->num_blocks, -1);
+  std::vector<int32_t>& desc_of_block = c->desc_of_block;
+  auto reset_scratch = [&]() {
+    for (const InjectDesc& d : descs) desc_of_block[d.phys_block] = -1;
+  };
+  for (int32_t r = 0; r < n_runs; ++r) {
+    const pkv_run& run = runs[r];
+    pkv_status st = check_seq(c, run.seq);
+    if (!st && (run.n_tokens < 0 || run.dst_pos < 0 || run.src_token < 0))
+      st = fail(PKV_E_INVALID, "run %d has a negative field", r);
+    if (st) {
+      reset_scratch();
+      return st;
+    }
+    if (run.n_tokens == 0) continue;
+    const auto& table = c->tables[run.seq];
+    const int64_t end = int64_t(run.dst_pos) + run.n_tokens;
+    if (end > int64_t(table.size()) * kBlock)
+      st = fail(PKV_E_RANGE, "run %d ends at %lld past the %zu reserved slots of seq %d", r,
+                (long long)end, table.size() * kBlock, run.seq);
+    else if (end > max_pos)
+      st = fail(PKV_E_RANGE, "run %d ends at %lld past the rotary table (%d)", r, (long long)end,
+                max_pos);
+    else if (run.src_token + run.n_tokens > src->n_tokens ||
+             run.src_token + run.n_tokens > INT32_MAX)
+      st = fail(PKV_E_RANGE, "run %d reads past the source store", r);
+    if (st) {
+      reset_scratch();
+      return st;
+    }
+    for (int32_t t = 0; t < run.n_tokens; ++t) {
+      const int32_t p = run.dst_pos + t;
+      const int32_t blk = table[p / kBlock];
+      if (blk >= pool->num_blocks) {
+        reset_scratch();
+        return fail(PKV_E_RANGE, "block %d outside the pool", blk);
+      }
+      int32_t di = desc_of_block[blk];
+      if (di < 0) {
+        di = int32_t(descs.size());
+        desc_of_block[blk] = di;
+        InjectDesc d;
+        d.phys_block = blk;
+        d.pos_base = p - p % kBlock;
+        for (int k = 0; k < kBlock; ++k) d.src[k] = -1;
+        descs.push_back(d);
+      }
+      int32_t& slot_src = descs[di].src[p % kBlock];
+      if (slot_src >= 0) {
+        reset_scratch();
+        return fail(PKV_E_OVERLAP, "two tokens of this call target slot %lld (seq %d pos %d)",
+                    (long long)blk * kBlock + p % kBlock, run.seq, p);
+      }
+      slot_src = int32_t(run.src_token + t);
+    }
+  }
+  reset_scratch();
+  const size_t bytes = descs.size() * sizeof(InjectDesc);
+  if (!descs.empty() && layer_end > layer_begin) {
+    if (!d_ws || ws_bytes < bytes)
+      return fail(PKV_E_WORKSPACE, "inject workspace %zu bytes, need %zu", ws_bytes, bytes);
+    if (reinterpret_cast<uintptr_t>(d_ws) & 15)
+      return fail(PKV_E_WORKSPACE, "workspace must be 16-byte aligned");
+    void* host = nullptr;
+    if (pkv_status st = c->staging.acquire(bytes, &host)) return st;
+    std::memcpy(host, descs.data(), bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (pkv_status st = c->staging.upload(d_ws, bytes, s)) return st;
+    hipError_t e = pkv::launch_inject(*pool, *src, static_cast<const InjectDesc*>(d_ws),
+                                      int(descs.size()), layer_begin, layer_end, rope_mode,
+                                      d_cos, d_sin, s);
+    if (e != hipSuccess) return hip_fail(e, "inject launch");
+  }
+  for (int32_t r = 0; r < n_runs; ++r) {
+    const int64_t end = int64_t(runs[r].dst_pos) + runs[r].n_tokens;
+    if (runs[r].n_tokens > 0) c->lens[runs[r].seq] = std::max(c->lens[runs[r].seq], end);
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Append
+// ---------------------------------------------------------------------------
+pkv_status pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* d_tables,
+                         int32_t table_stride, const int32_t* d_first_pos, int32_t n_seqs,
+                         int32_t n_new, const void* d_k_new, const void* d_v_new,
+                         int32_t rope_mode, const float* d_cos, const float* d_sin,
+                         int32_t max_pos, void* stream) {
+  if (pkv_status st = check_pool(pool)) return st;
+  if (pkv_status st = check_rope(rope_mode, d_cos, d_sin, max_pos)) return st;
+  if (layer < 0 || layer >= pool->n_layers) return fail(PKV_E_INVALID, "layer %d", layer);
+  if (n_seqs < 0 || n_new < 0) return fail(PKV_E_INVALID, "negative count");
+  if (n_seqs == 0 || n_new == 0) return ok();
+  if (!d_tables || !d_first_pos || !d_k_new || !d_v_new || table_stride <= 0)
+    return fail(PKV_E_INVALID, "null device argument or bad table stride");
+  if ((reinterpret_cast<uintptr_t>(d_k_new) | reinterpret_cast<uintptr_t>(d_v_new)) & 15)
+    return fail(PKV_E_INVALID, "k_new / v_new must be 16-byte aligned");
+  hipError_t e = pkv::launch_append(*pool, layer, d_tables, table_stride, d_first_pos, n_seqs,
+                                    n_new, d_k_new, d_v_new, rope_mode, d_cos, d_sin, max_pos,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Decode plan and attention
+// ---------------------------------------------------------------------------
+pkv_status pkv_decode_plan_create(const int64_t* lens, int32_t n_seqs, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim, int32_t part_tokens,
+                                  pkv_plan** out) {
+  if (!out || n_seqs < 0 || (n_seqs > 0 && !lens)) return fail(PKV_E_INVALID, "bad arguments");
+  if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads)
+    return fail(PKV_E_INVALID, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_E_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+  if (part_tokens < 0 || part_tokens % kBlock)
+    return fail(PKV_E_INVALID, "part_tokens must be a non-negative multiple of 16");
+  int64_t total = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    if (lens[b] < 0 || lens[b] > (int64_t(1) << 30))
+      return fail(PKV_E_RANGE, "length %lld of sequence %d", (long long)lens[b], b);
+    total += lens[b];
+  }
+  int32_t part = part_tokens;
+  if (part == 0) {
+    if (const char* env = std::getenv("PKV_PART_TOKENS")) part = std::atoi(env);
+    if (part <= 0 || part % kBlock) {
+      // Aim at ~2048 workgroups (8 per CU) of (token range, KV head); keep
+      // ranges between 256 and 4096 tokens.
+      const int64_t per = (total * n_kv_heads + 2047) / 2048;
+      int64_t p = (per + kBlock - 1) / kBlock * kBlock;
+      part = int32_t(std::min<int64_t>(4096, std::max<int64_t>(256, p)));
+    }
+  }
+  pkv_plan* plan = new (std::nothrow) pkv_plan();
+  if (!plan) return fail(PKV_E_INVALID, "out of host memory");
+  plan->n_seqs = n_seqs;
+  plan->n_q_heads = n_q_heads;
+  plan->n_kv_heads = n_kv_heads;
+  plan->head_dim = head_dim;
+  plan->part_tokens = part;
+  int32_t slots = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int64_t n_items = (lens[b] + part - 1) / part;
+    if (n_items == 0) {
+      plan->merges.push_back(MergeSeq{b, 0, 0, 0});  // empty: out 0, lse -inf
+    } else if (n_items == 1) {
+      plan->items.push_back(DecodeItem{b, 0, int32_t(lens[b]), -1});
+    } else {
+      MergeSeq m{b, slots, int32_t(n_items), 0};
+      for (int64_t i = 0; i < n_items; ++i) {
+        const int64_t t0 = i * part;
+        const int64_t n = std::min<int64_t>(part, lens[b] - t0);
+        plan->items.push_back(DecodeItem{b, int32_t(t0), int32_t(n), slots++});
+      }
+      plan->merges.push_back(m);
+    }
+  }
+  plan->n_slots = slots;
+  size_t off = 0;
+  plan->off_items = off;
+  off = align_up(off + plan->items.size() * sizeof(DecodeItem), 256);
+  plan->off_merges = off;
+  off = align_up(off + plan->merges.size() * sizeof(MergeSeq), 256);
+  plan->off_part_o = off;
+  off = align_up(off + size_t(slots) * n_q_heads * head_dim * sizeof(float), 256);
+  plan->off_part_ml = off;
+  off = align_up(off + size_t(slots) * n_q_heads * 2 * sizeof(float), 256);
+  plan->ws_bytes = std::max<size_t>(off, 256);
+  *out = plan;
+  return ok();
+}
+
+void pkv_decode_plan_destroy(pkv_plan* plan) { delete plan; }
+
+int32_t pkv_decode_plan_items(const pkv_plan* plan) {
+  return plan ? int32_t(plan->items.size()) : -1;
+}
+
+int32_t pkv_decode_plan_part_tokens(const pkv_plan* plan) {
+  return plan ? plan->part_tokens : -1;
+}
+
+size_t pkv_decode_workspace_bytes(const pkv_plan* plan) { return plan ? plan->ws_bytes : 0; }
+
+pkv_status pkv_decode_plan_upload(pkv_plan* plan, void* d_ws, size_t ws_bytes, void* stream) {
+  if (!plan) return fail(PKV_E_INVALID, "null plan");
+  if (!d_ws || ws_bytes < plan->ws_bytes)
+    return fail(PKV_E_WORKSPACE, "decode workspace %zu bytes, need %zu", ws_bytes,
+                plan->ws_bytes);
+  if (reinterpret_cast<uintptr_t>(d_ws) & 255)
+    return fail(PKV_E_WORKSPACE, "workspace must be 256-byte aligned");
+  const size_t bytes = plan->off_part_o;
+  if (bytes == 0) return ok();
+  void* host = nullptr;
+  if (pkv_status st = plan->staging.acquire(bytes, &host)) return st;
+  std::memset(host, 0, bytes);
+  std::memcpy(static_cast<char*>(host) + plan->off_items, plan->items.data(),
+              plan->items.size() * sizeof(DecodeItem));
+  std::memcpy(static_cast<char*>(host) + plan->off_merges, plan->merges.data(),
+              plan->merges.size() * sizeof(MergeSeq));
+  if (pkv_status st = plan->staging.upload(d_ws, bytes, static_cast<hipStream_t>(stream)))
+    return st;
+  return ok();
+}
+
+pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int32_t layer,
+                                const void* d_q, float scale, const int32_t* d_tables,
+                                int32_t table_stride, float* d_out, float* d_lse, void* d_ws,
+                                size_t ws_bytes, void* stream) {
+  if (!plan) return fail(PKV_E_INVALID, "null plan");
+  if (pkv_status st = check_pool(pool)) return st;
+  if (layer < 0 || layer >= pool->n_layers) return fail(PKV_E_INVALID, "layer %d", layer);
+  if (pool->n_kv_heads != plan->n_kv_heads || pool->head_dim != plan->head_dim)
+    return fail(PKV_E_INVALID, "plan and pool disagree on KV heads or head_dim");
+  if (plan->n_seqs == 0) return ok();
+  if (!d_q || !d_out || !d_tables) return fail(PKV_E_INVALID, "null device argument");
+  if (reinterpret_cast<uintptr_t>(d_q) & 15) return fail(PKV_E_INVALID, "q must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(d_out) & 15)
+    return fail(PKV_E_INVALID, "out must be 16-byte aligned");
+  int64_t max_blocks = 0;
+  for (const DecodeItem& it : plan->items)
+    max_blocks = std::max<int64_t>(max_blocks, blocks_for(int64_t(it.t_begin) + it.n_tokens));
+  if (table_stride <= 0 || max_blocks > table_stride)
+    return fail(PKV_E_RANGE, "table_stride %d smaller than %lld blocks", table_stride,
+                (long long)max_blocks);
+  if (!d_ws || ws_bytes < plan->ws_bytes)
+    return fail(PKV_E_WORKSPACE, "decode workspace %zu bytes, need %zu", ws_bytes,
+                plan->ws_bytes);
+  char* ws = static_cast<char*>(d_ws);
+  pkv::DecodeArgs a;
+  a.q = d_q;
+  a.n_q_heads = plan->n_q_heads;
+  a.scale = scale > 0.f ? scale : float(1.0 / std::sqrt(double(plan->head_dim)));
+  a.tables = d_tables;
+  a.table_stride = table_stride;
+  a.items = reinterpret_cast<const DecodeItem*>(ws + plan->off_items);
+  a.n_items = int(plan->items.size());
+  a.merges = reinterpret_cast<const MergeSeq*>(ws + plan->off_merges);
+  a.n_merges = int(plan->merges.size());
+  a.part_o = reinterpret_cast<float*>(ws + plan->off_part_o);
+  a.part_ml = reinterpret_cast<float*>(ws + plan->off_part_ml);
+  a.out = d_out;
+  a.lse = d_lse;
+  int variant = 0;
+  if (const char* env = std::getenv("PKV_DECODE_KERNEL")) variant = std::atoi(env);
+  hipError_t e = pkv::launch_decode(*pool, layer, a, variant, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+pkv_status pkv_bw_probe(const void* d_src, size_t n_bytes, void* d_sink, void* stream) {
+  if (!d_src || !d_sink || n_bytes % 16 || (reinterpret_cast<uintptr_t>(d_src) & 15))
+    return fail(PKV_E_INVALID, "bad probe arguments");
+  hipError_t e = pkv::launch_bw_probe(d_src, n_bytes, d_sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal interface between the host runtime (pkv_host.cpp) and the HIP
+// kernels (pkv_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pkv.h"
+
+namespace pkv {
+
+constexpr int kBlock = PKV_BLOCK_TOKENS;
+
+// Write plan of one destination block for an inject call: the physical block,
+// the logical position of its first slot, and for each of its 16 slots the
+// source token to write there (-1: leave the slot as it is).
+struct InjectDesc {
+  int32_t phys_block;
+  int32_t pos_base;
+  int32_t src[kBlock];
+};
+static_assert(sizeof(InjectDesc) == 72, "descriptor layout");
+
+// One decode work item: tokens [t_begin, t_begin + n_tokens) of sequence seq
+// (t_begin a multiple of 16).  `slot` is where its partial softmax state is
+// stored; slot < 0 means the item covers the whole sequence and writes the
+// final output directly.
+struct DecodeItem {
+  int32_t seq;
+  int32_t t_begin;
+  int32_t n_tokens;
+  int32_t slot;
+};
+
+// Merge work: sequence seq owns partial slots [first, first + count); count 0
+// marks an empty sequence (output 0, lse -inf).
+struct MergeSeq {
+  int32_t seq;
+  int32_t first;
+  int32_t count;
+  int32_t _pad;
+};
+
+hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, const InjectDesc* d_desc,
+                         int n_desc, int layer_begin, int layer_end, int rope_mode,
+                         const float* d_cos, const float* d_sin, hipStream_t stream);
+
+hipError_t launch_append(const pkv_pool& pool, int layer, const int32_t* d_tables,
+                         int table_stride, const int32_t* d_first_pos, int n_seqs, int n_new,
+                         const void* d_k, const void* d_v, int rope_mode, const float* d_cos,
+                         const float* d_sin, int max_pos, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  int n_q_heads;
+  float scale;
+  const int32_t* tables;
+  int table_stride;
+  const DecodeItem* items;
+  int n_items;
+  const MergeSeq* merges;
+  int n_merges;
+  float* part_o;   // [n_slots][n_q_heads][head_dim]
+  float* part_ml;  // [n_slots][n_q_heads][2]
+  float* out;
+  float* lse;      // may be null
+};
+
+// kernel_variant: 0 = automatic, 1 = force the generic VALU kernel.
+hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
+                         int kernel_variant, hipStream_t stream);
+
+hipError_t launch_bw_probe(const void* src, size_t n_bytes, void* sink, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,824 @@
+// HIP kernels of libpkv for MI355X (gfx950, CDNA4, wave64).
+//
+//   inject_rope_kernel     write side: one workgroup per (destination block,
+//                          layer); rotates stored pre-RoPE keys to their
+//                          destination positions and scatters K/V into the
+//                          block's planes ("InferScale" §3 scatter copy through
+//                          the slot mapping, §3.3 and §5.1 chunked RoPE).
+//   append_kv_kernel       one workgroup per new token (the per-step append of
+//                          "InferScale" §2 / "LLM Inference: KV Caching",
+//                          "The fix").
+//   decode_mfma_kernel     read side: one wave per (token range, KV head);
+//                          QK^T and PV of the whole GQA group on MFMA tiles,
+//                          online softmax in registers.
+//   decode_valu_kernel     generic read side for any dtype / group size.
+//   decode_merge_kernel    log-sum-exp merge of the token-range partials.
+//   bw_probe_kernel        streaming read for the same-run HBM ceiling.
+//
+// Pool plane layouts (see include/pkv.h): K plane = d/X chunks x 16 tokens x X
+// dims (X = 16 bytes / element), V plane = d dims x 16 tokens.
+//
+// This file is compiled with -ffp-contract=off: the key rotation is two
+// float32 products and one float32 add/subtract, never fused, so the stored
+// keys are reproducible bit for bit.  Where a fused multiply-add is wanted it
+// is written as fmaf().
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Element formats
+// ---------------------------------------------------------------------------
+template <int DT> struct Fmt;
+template <> struct Fmt<PKV_F32> {
+  typedef float T;
+  static constexpr int kBytes = 4;
+  __device__ static float to_f32(float x) { return x; }
+  __device__ static float from_f32(float x) { return x; }
+};
+template <> struct Fmt<PKV_BF16> {
+  typedef uint16_t T;
+  static constexpr int kBytes = 2;
+  __device__ static float to_f32(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+  // Round to nearest, ties to even; NaN stays a (quiet) NaN.
+  __device__ static uint16_t from_f32(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+  }
+};
+template <> struct Fmt<PKV_F16> {
+  typedef uint16_t T;
+  static constexpr int kBytes = 2;
+  __device__ static float to_f32(uint16_t x) { return float(__builtin_bit_cast(_Float16, x)); }
+  // Hardware conversion under the default round-to-nearest-even mode.
+  __device__ static uint16_t from_f32(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+  }
+};
+
+// 16-byte global access helpers.
+__device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ inline void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Rotate the X elements of one 16-byte chunk.  PAIRS: element e pairs with
+// e^1 inside the chunk (pair index = (first_dim + e) / 2).  HALVES: element e
+// of chunk `a` (first half) pairs with element e of chunk `b` (second half),
+// pair index first_dim + e.  y0 = x0*c - x1*s, y1 = x0*s + x1*c in float32.
+template <int DT>
+__device__ inline void rotate_pairs(uint4& chunk, int first_dim, const float* cos_row,
+                                    const float* sin_row) {
+  typedef typename Fmt<DT>::T T;
+  constexpr int X = 16 / Fmt<DT>::kBytes;
+  T v[X];
+  *reinterpret_cast<uint4*>(v) = chunk;
+#pragma unroll
+  for (int e = 0; e < X; e += 2) {
+    const int i = (first_dim + e) >> 1;
+    const float c = cos_row[i], s = sin_row[i];
+    const float x0 = Fmt<DT>::to_f32(v[e]), x1 = Fmt<DT>::to_f32(v[e + 1]);
+    const float y0 = x0 * c - x1 * s;
+    const float y1 = x0 * s + x1 * c;
+    v[e] = Fmt<DT>::from_f32(y0);
+    v[e + 1] = Fmt<DT>::from_f32(y1);
+  }
+  chunk = *reinterpret_cast<uint4*>(v);
+}
+
+template <int DT>
+__device__ inline void rotate_halves(uint4& a, uint4& b, int first_dim, const float* cos_row,
+                                     const float* sin_row) {
+  typedef typename Fmt<DT>::T T;
+  constexpr int X = 16 / Fmt<DT>::kBytes;
+  T va[X], vb[X];
+  *reinterpret_cast<uint4*>(va) = a;
+  *reinterpret_cast<uint4*>(vb) = b;
+#pragma unroll
+  for (int e = 0; e < X; ++e) {
+    const int i = first_dim + e;
+    const float c = cos_row[i], s = sin_row[i];
+    const float x0 = Fmt<DT>::to_f32(va[e]), x1 = Fmt<DT>::to_f32(vb[e]);
+    const float y0 = x0 * c - x1 * s;
+    const float y1 = x0 * s + x1 * c;
+    va[e] = Fmt<DT>::from_f32(y0);
+    vb[e] = Fmt<DT>::from_f32(y1);
+  }
+  a = *reinterpret_cast<uint4*>(va);
+  b = *reinterpret_cast<uint4*>(vb);
+}
+
+// Rotates the chunk pair (c0, c0 + C/2) of one token at position pos.
+template <int DT, int D>
+__device__ inline void rotate_chunk_pair(uint4& lo, uint4& hi, int c0, int pos, int mode,
+                                         const float* cos_t, const float* sin_t) {
+  constexpr int X = 16 / Fmt<DT>::kBytes;
+  constexpr int C = D / X;
+  if (mode == PKV_ROPE_NONE) return;
+  const float* cr = cos_t + size_t(pos) * (D / 2);
+  const float* sr = sin_t + size_t(pos) * (D / 2);
+  if (mode == PKV_ROPE_PAIRS) {
+    rotate_pairs<DT>(lo, c0 * X, cr, sr);
+    rotate_pairs<DT>(hi, (c0 + C / 2) * X, cr, sr);
+  } else {
+    rotate_halves<DT>(lo, hi, c0 * X, cr, sr);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Inject: one workgroup per (destination block descriptor, layer)
+// ---------------------------------------------------------------------------
+struct InjectParams {
+  char* pool_k;
+  char* pool_v;
+  int64_t p_layer, p_block, p_head;  // bytes
+  int n_kv_heads;
+  const char* src_k;
+  const char* src_v;
+  int64_t s_layer, s_token;          // bytes
+  const InjectDesc* descs;
+  int layer_begin;
+  int rope_mode;
+  const float* cos_t;
+  const float* sin_t;
+};
+
+constexpr int kInjectThreads = 256;
+// Heads staged per pass: V tiles of up to 32 KiB of LDS.
+constexpr int inject_heads_per_pass(int d, int e) { return 2048 / (d * e) < 8 ? 2048 / (d * e) : 8; }
+
+template <int DT, int D>
+__global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParams p) {
+  typedef typename Fmt<DT>::T T;
+  constexpr int E = Fmt<DT>::kBytes;
+  constexpr int X = 16 / E;          // elements per 16-byte chunk
+  constexpr int C = D / X;           // chunks per token row
+  constexpr int UNITS = kBlock * (C / 2);   // (token, chunk pair) units per head
+  constexpr int VPIECES = D * (kBlock / X); // 16-byte pieces of a V plane
+  constexpr int HG = inject_heads_per_pass(D, E);
+  __shared__ T vtile[HG][kBlock][D];
+  __shared__ InjectDesc desc;
+
+  const int layer = p.layer_begin + blockIdx.y;
+  if (threadIdx.x < sizeof(InjectDesc) / 4)
+    reinterpret_cast<int32_t*>(&desc)[threadIdx.x] =
+        reinterpret_cast<const int32_t*>(&p.descs[blockIdx.x])[threadIdx.x];
+  __syncthreads();
+  bool full = true;
+#pragma unroll
+  for (int t = 0; t < kBlock; ++t) full &= desc.src[t] >= 0;
+
+  char* kplane0 = p.pool_k + layer * p.p_layer + int64_t(desc.phys_block) * p.p_block;
+  char* vplane0 = p.pool_v + layer * p.p_layer + int64_t(desc.phys_block) * p.p_block;
+  const char* sk = p.src_k + layer * p.s_layer;
+  const char* sv = p.src_v + layer * p.s_layer;
+
+  for (int h0 = 0; h0 < p.n_kv_heads; h0 += HG) {
+    const int nh = min(HG, p.n_kv_heads - h0);
+    // Phase A: read each token's chunk pair, rotate K and store it; stage V.
+    for (int w = threadIdx.x; w < nh * UNITS; w += kInjectThreads) {
+      const int hl = w / UNITS;
+      const int r = w - hl * UNITS;
+      const int t = r % kBlock;
+      const int c0 = r / kBlock;
+      const int src = desc.src[t];
+      if (src < 0) continue;
+      const int h = h0 + hl;
+      const int64_t row = int64_t(src) * p.s_token + int64_t(h) * D * E;
+      uint4 k0 = ld16(sk + row + c0 * 16);
+      uint4 k1 = ld16(sk + row + (c0 + C / 2) * 16);
+      const uint4 v0 = ld16(sv + row + c0 * 16);
+      const uint4 v1 = ld16(sv + row + (c0 + C / 2) * 16);
+      rotate_chunk_pair<DT, D>(k0, k1, c0, desc.pos_base + t, p.rope_mode, p.cos_t, p.sin_t);
+      char* kplane = kplane0 + int64_t(h) * p.p_head;
+      st16(kplane + (c0 * kBlock + t) * 16, k0);
+      st16(kplane + ((c0 + C / 2) * kBlock + t) * 16, k1);
+      *reinterpret_cast<uint4*>(&vtile[hl][t][c0 * X]) = v0;
+      *reinterpret_cast<uint4*>(&vtile[hl][t][(c0 + C / 2) * X]) = v1;
+    }
+    __syncthreads();
+    // Phase B: write V planes dimension-major, X tokens per 16-byte piece.
+    for (int w = threadIdx.x; w < nh * VPIECES; w += kInjectThreads) {
+      const int hl = w / VPIECES;
+      const int r = w - hl * VPIECES;
+      const int j = r / (kBlock / X);
+      const int t0 = (r % (kBlock / X)) * X;
+      char* dst = vplane0 + int64_t(h0 + hl) * p.p_head + (int64_t(j) * kBlock + t0) * E;
+      T out[X];
+      bool need_old = false;
+      if (!full) {
+#pragma unroll
+        for (int e = 0; e < X; ++e) need_old |= desc.src[t0 + e] < 0;
+      }
+      if (need_old) *reinterpret_cast<uint4*>(out) = ld16(dst);
+#pragma unroll
+      for (int e = 0; e < X; ++e)
+        if (desc.src[t0 + e] >= 0) out[e] = vtile[hl][t0 + e][j];
+      st16(dst, *reinterpret_cast<uint4*>(out));
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Append: one workgroup per (sequence, new token)
+// ---------------------------------------------------------------------------
+struct AppendParams {
+  char* pool_k;
+  char* pool_v;
+  int64_t p_layer, p_block, p_head;  // bytes
+  int n_kv_heads;
+  int num_blocks;
+  int layer;
+  const int32_t* tables;
+  int table_stride;
+  const int32_t* first_pos;
+  int n_new;
+  const char* k_new;
+  const char* v_new;
+  int rope_mode;
+  const float* cos_t;
+  const float* sin_t;
+  int max_pos;
+};
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) void append_kv_kernel(AppendParams p) {
+  typedef typename Fmt<DT>::T T;
+  constexpr int E = Fmt<DT>::kBytes;
+  constexpr int X = 16 / E;
+  constexpr int C = D / X;
+  const int b = blockIdx.x / p.n_new;
+  const int t = blockIdx.x - b * p.n_new;
+  const int pos = p.first_pos[b] + t;
+  if (pos < 0) return;
+  if (p.rope_mode != PKV_ROPE_NONE && pos >= p.max_pos) return;
+  const int lb = pos / kBlock;
+  if (lb >= p.table_stride) return;
+  const int blk = p.tables[int64_t(b) * p.table_stride + lb];
+  if (blk < 0 || blk >= p.num_blocks) return;
+  const int tin = pos % kBlock;
+  char* kplane0 = p.pool_k + p.layer * p.p_layer + int64_t(blk) * p.p_block;
+  char* vplane0 = p.pool_v + p.layer * p.p_layer + int64_t(blk) * p.p_block;
+  const int64_t row0 = (int64_t(b) * p.n_new + t) * p.n_kv_heads * D * E;
+  const char* kin = p.k_new + row0;
+  const char* vin = p.v_new + row0;
+  for (int w = threadIdx.x; w < p.n_kv_heads * (C / 2); w += blockDim.x) {
+    const int h = w / (C / 2);
+    const int c0 = w - h * (C / 2);
+    uint4 k0 = ld16(kin + int64_t(h) * D * E + c0 * 16);
+    uint4 k1 = ld16(kin + int64_t(h) * D * E + (c0 + C / 2) * 16);
+    rotate_chunk_pair<DT, D>(k0, k1, c0, pos, p.rope_mode, p.cos_t, p.sin_t);
+    char* kplane = kplane0 + int64_t(h) * p.p_head;
+    st16(kplane + (c0 * kBlock + tin) * 16, k0);
+    st16(kplane + ((c0 + C / 2) * kBlock + tin) * 16, k1);
+  }
+  for (int w = threadIdx.x; w < p.n_kv_heads * D; w += blockDim.x) {
+    const int h = w / D;
+    const int j = w - h * D;
+    const T v = reinterpret_cast<const T*>(vin + int64_t(h) * D * E)[j];
+    reinterpret_cast<T*>(vplane0 + int64_t(h) * p.p_head)[j * kBlock + tin] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode: common parameters
+// ---------------------------------------------------------------------------
+struct DecodeParams {
+  const char* pool_k;
+  const char* pool_v;
+  int64_t p_layer, p_block, p_head;  // bytes
+  int num_blocks;
+  int n_kv_heads;
+  int n_q_heads;
+  int group;                         // n_q_heads / n_kv_heads
+  const char* q;
+  float scale_log2;                  // scale * log2(e)
+  const int32_t* tables;
+  int table_stride;
+  const DecodeItem* items;
+  float* part_o;
+  float* part_ml;
+  float* out;
+  float* lse;
+};
+
+// Stores one head's result: final (single-range sequence) or partial state.
+// m is in the log2-scaled domain; l is the sum of 2^(s - m).
+__device__ inline void store_head_result(const DecodeParams& p, const DecodeItem& it, int hq,
+                                         int dim, float o, float m, float l, bool write_ml,
+                                         int D) {
+  if (it.slot < 0) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    p.out[(int64_t(it.seq) * p.n_q_heads + hq) * D + dim] = o * inv;
+    if (write_ml && p.lse)
+      p.lse[int64_t(it.seq) * p.n_q_heads + hq] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+  } else {
+    p.part_o[(int64_t(it.slot) * p.n_q_heads + hq) * D + dim] = o;
+    if (write_ml) {
+      p.part_ml[(int64_t(it.slot) * p.n_q_heads + hq) * 2 + 0] = m;
+      p.part_ml[(int64_t(it.slot) * p.n_q_heads + hq) * 2 + 1] = l;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode, MFMA: one wave per (work item, KV head), G <= 16 query heads.
+//
+// Per 16-token block:
+//   S^T[t][h] = sum_j K[t][j] q_h[j]   v_mfma_f32_16x16x32 (bf16/f16), D/32 steps
+//     A = K plane: lane l loads 16 bytes at (64*s + l)*16 of the plane, i.e.
+//         token l%16, chunk 4s + l/16 -- the k-slots of row l%16;
+//     B = q: lane l holds head (l%16)'s dims of the same chunk (0 for l%16 >= G).
+//   Result: lane l holds scores of tokens 4*(l/16)+r (r<4) for head l%16.
+//   Online softmax per head across the 4 lanes sharing l%16 (xor 16, 32).
+//   out^T[j][h] += sum_t V^T[j][t] P^T[t][h]   v_mfma_f32_16x16x16, D/16 tiles
+//     A = V plane rows 16n + l%16, tokens 4*(l/16)..+3 (8 bytes);
+//     B = P^T: exactly the score registers of this lane, converted to
+//         16-bit as a hi part plus a lo residual (two MFMAs) so that the
+//         probabilities keep ~16 significant bits.
+// Accumulators: lane l holds out[head l%16][dims 16n + 4*(l/16) + r].
+// ---------------------------------------------------------------------------
+template <int DT> struct Mfma;
+template <> struct Mfma<PKV_BF16> {
+  typedef bf16x8_t V8;
+  typedef bf16x4_t V4;
+  __device__ static f32x4_t qk(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(V8, a),
+                                                    __builtin_bit_cast(V8, b), c, 0, 0, 0);
+  }
+  __device__ static f32x4_t pv(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(V4, a),
+                                                      __builtin_bit_cast(V4, b), c, 0, 0, 0);
+  }
+  // Split p into hi + lo 16-bit parts (hi by truncation, lo = rest truncated).
+  __device__ static void split(float p, uint16_t& hi, uint16_t& lo) {
+    const uint32_t u = __float_as_uint(p) & 0xffff0000u;
+    hi = uint16_t(u >> 16);
+    lo = uint16_t(__float_as_uint(p - __uint_as_float(u)) >> 16);
+  }
+};
+template <> struct Mfma<PKV_F16> {
+  typedef f16x8_t V8;
+  typedef f16x4_t V4;
+  __device__ static f32x4_t qk(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(V8, a),
+                                                   __builtin_bit_cast(V8, b), c, 0, 0, 0);
+  }
+  __device__ static f32x4_t pv(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(V4, a),
+                                                  __builtin_bit_cast(V4, b), c, 0, 0, 0);
+  }
+  __device__ static void split(float p, uint16_t& hi, uint16_t& lo) {
+    const _Float16 h = static_cast<_Float16>(p);
+    const _Float16 l = static_cast<_Float16>(p - float(h));
+    hi = __builtin_bit_cast(uint16_t, h);
+    lo = __builtin_bit_cast(uint16_t, l);
+  }
+};
+
+template <int DT, int D, int DEPTH>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeParams p) {
+  constexpr int S = D / 32;   // QK MFMA steps (4 chunks of 8 dims each)
+  constexpr int NT = D / 16;  // PV MFMA tiles of 16 dims
+  const int lane = threadIdx.x;
+  const int row = lane & 15;
+  const int grp = lane >> 4;
+  const DecodeItem it = p.items[blockIdx.x];
+  const int g = blockIdx.y;
+  const int hq = g * p.group + row;
+  const bool head_ok = row < p.group;
+
+  // q operand (B of QK): head `row`, chunk 4s + grp of each step.
+  uint4 qreg[S];
+  {
+    const char* qh = p.q + (int64_t(it.seq) * p.n_q_heads + (head_ok ? hq : g * p.group)) * D * 2;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      qreg[s] = ld16(qh + (4 * s + grp) * 16);
+      if (!head_ok) qreg[s] = make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  const int32_t* tab = p.tables + int64_t(it.seq) * p.table_stride + it.t_begin / kBlock;
+  const char* kbase = p.pool_k + int64_t(g) * p.p_head;
+  const char* vbase = p.pool_v + int64_t(g) * p.p_head;
+  const int nblk = (it.n_tokens + kBlock - 1) / kBlock;
+
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;  // running max (log2 domain), uniform over the head's lanes
+  float l = 0.f;        // this lane's share of the running sum
+
+  uint4 kbuf[DEPTH][S];
+  uint2 vbuf[DEPTH][NT];
+  bool okbuf[DEPTH];
+
+  auto issue = [&](int i, int d) {
+    int blk = tab[i];
+    const bool ok = unsigned(blk) < unsigned(p.num_blocks);
+    okbuf[d] = ok;
+    blk = ok ? blk : 0;
+    const char* kp = kbase + int64_t(blk) * p.p_block;
+    const char* vp = vbase + int64_t(blk) * p.p_block;
+#pragma unroll
+    for (int s = 0; s < S; ++s) kbuf[d][s] = ld16(kp + (64 * s + lane) * 16);
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      vbuf[d][n] = *reinterpret_cast<const uint2*>(vp + (16 * n + row) * 32 + grp * 8);
+  };
+
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < nblk) issue(d, d);
+
+  for (int i0 = 0; i0 < nblk; i0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int i = i0 + d;
+      if (i < nblk) {
+        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < S; ++s) sc = Mfma<DT>::qk(kbuf[d][s], qreg[s], sc);
+        uint2 vcur[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) vcur[n] = vbuf[d][n];
+        const bool blk_ok = okbuf[d];
+        if (i + DEPTH < nblk) issue(i + DEPTH, d);
+
+        const int valid = it.n_tokens - i * kBlock;  // tokens of this block in range
+        float s4[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool live = blk_ok && (4 * grp + r) < valid;
+          s4[r] = live ? sc[r] * p.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, s4[r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);
+        float pr[4];
+        if (m_new == -INFINITY) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pr[r] = 0.f;
+        } else {
+          const float alpha = exp2f(m - m_new);  // 0 when m was -inf
+          l *= alpha;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pr[r] = exp2f(s4[r] - m_new);
+            l += pr[r];
+          }
+          m = m_new;
+        }
+        uint16_t ph[4], pl[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Mfma<DT>::split(pr[r], ph[r], pl[r]);
+        const uint2 bh = make_uint2(uint32_t(ph[0]) | (uint32_t(ph[1]) << 16),
+                                    uint32_t(ph[2]) | (uint32_t(ph[3]) << 16));
+        const uint2 bl = make_uint2(uint32_t(pl[0]) | (uint32_t(pl[1]) << 16),
+                                    uint32_t(pl[2]) | (uint32_t(pl[3]) << 16));
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          acc[n] = Mfma<DT>::pv(vcur[n], bh, acc[n]);
+          acc[n] = Mfma<DT>::pv(vcur[n], bl, acc[n]);
+        }
+      }
+    }
+  }
+
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!head_ok) return;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      store_head_result(p, it, hq, 16 * n + 4 * grp + r, acc[n][r], m, l,
+                        n == 0 && r == 0 && grp == 0, D);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode, generic VALU: one wave per (work item, KV head); any dtype, any
+// group size (query heads in passes of up to 4).
+//   scores: lane l takes token l%16 and a quarter l/16 of the dimensions;
+//           quarters are summed with xor-16/32 shuffles;
+//   PV:     lane l owns dims l (+64); probabilities go through LDS.
+// ---------------------------------------------------------------------------
+constexpr int kValuHeads = 4;
+
+template <int DT, int D>
+__global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
+  typedef typename Fmt<DT>::T T;
+  constexpr int E = Fmt<DT>::kBytes;
+  constexpr int X = 16 / E;
+  constexpr int C = D / X;
+  constexpr int QC = C / 4;     // chunks per dimension quarter
+  constexpr int DL = D / 64;    // dims per lane in PV
+  __shared__ float ps[kValuHeads][kBlock];
+  const int lane = threadIdx.x;
+  const int tok = lane & 15;
+  const int quarter = lane >> 4;
+  const DecodeItem it = p.items[blockIdx.x];
+  const int g = blockIdx.y;
+  const int32_t* tab = p.tables + int64_t(it.seq) * p.table_stride + it.t_begin / kBlock;
+  const char* kbase = p.pool_k + int64_t(g) * p.p_head;
+  const char* vbase = p.pool_v + int64_t(g) * p.p_head;
+  const int nblk = (it.n_tokens + kBlock - 1) / kBlock;
+
+  for (int h0 = 0; h0 < p.group; h0 += kValuHeads) {
+    const int nh = min(kValuHeads, p.group - h0);
+    float qv[kValuHeads][QC * X];
+    for (int i = 0; i < kValuHeads; ++i) {
+      const int hq = g * p.group + h0 + min(i, nh - 1);
+      const T* qh = reinterpret_cast<const T*>(p.q + (int64_t(it.seq) * p.n_q_heads + hq) * D * E);
+#pragma unroll
+      for (int c = 0; c < QC; ++c)
+#pragma unroll
+        for (int e = 0; e < X; ++e) qv[i][c * X + e] = Fmt<DT>::to_f32(qh[(quarter * QC + c) * X + e]);
+    }
+    float m[kValuHeads], l[kValuHeads], acc[kValuHeads][DL];
+    for (int i = 0; i < kValuHeads; ++i) {
+      m[i] = -INFINITY;
+      l[i] = 0.f;
+#pragma unroll
+      for (int k = 0; k < DL; ++k) acc[i][k] = 0.f;
+    }
+    for (int bi = 0; bi < nblk; ++bi) {
+      const int blk = tab[bi];
+      const bool ok = unsigned(blk) < unsigned(p.num_blocks);
+      const bool live = ok && (bi * kBlock + tok) < it.n_tokens;
+      const char* kp = kbase + int64_t(ok ? blk : 0) * p.p_block;
+      const char* vp = vbase + int64_t(ok ? blk : 0) * p.p_block;
+      float kv[QC * X];
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+        const T* chunk = reinterpret_cast<const T*>(kp + ((quarter * QC + c) * kBlock + tok) * 16);
+#pragma unroll
+        for (int e = 0; e < X; ++e) kv[c * X + e] = Fmt<DT>::to_f32(chunk[e]);
+      }
+      for (int i = 0; i < nh; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < QC * X; ++e) s = fmaf(qv[i][e], kv[e], s);
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        s = live ? s * p.scale_log2 : -INFINITY;
+        float mx = s;
+        mx = fmaxf(mx, __shfl_xor(mx, 1));
+        mx = fmaxf(mx, __shfl_xor(mx, 2));
+        mx = fmaxf(mx, __shfl_xor(mx, 4));
+        mx = fmaxf(mx, __shfl_xor(mx, 8));
+        const float m_new = fmaxf(m[i], mx);
+        float pr = 0.f;
+        if (m_new != -INFINITY) {
+          const float alpha = exp2f(m[i] - m_new);
+          pr = exp2f(s - m_new);
+          float bsum = pr;
+          bsum += __shfl_xor(bsum, 1);
+          bsum += __shfl_xor(bsum, 2);
+          bsum += __shfl_xor(bsum, 4);
+          bsum += __shfl_xor(bsum, 8);
+          l[i] = l[i] * alpha + bsum;
+#pragma unroll
+          for (int k = 0; k < DL; ++k) acc[i][k] *= alpha;
+          m[i] = m_new;
+        }
+        if (lane < kBlock) ps[i][lane] = pr;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < DL; ++k) {
+        const int j = lane + 64 * k;
+        const T* vrow = reinterpret_cast<const T*>(vp + int64_t(j) * kBlock * E);
+        float vv[kBlock];
+#pragma unroll
+        for (int t = 0; t < kBlock; ++t) vv[t] = Fmt<DT>::to_f32(vrow[t]);
+        for (int i = 0; i < nh; ++i) {
+          float a = acc[i][k];
+#pragma unroll
+          for (int t = 0; t < kBlock; ++t) a = fmaf(ps[i][t], vv[t], a);
+          acc[i][k] = a;
+        }
+      }
+      __syncthreads();
+    }
+    for (int i = 0; i < nh; ++i) {
+      const int hq = g * p.group + h0 + i;
+#pragma unroll
+      for (int k = 0; k < DL; ++k)
+        store_head_result(p, it, hq, lane + 64 * k, acc[i][k], m[i], l[i], lane == 0 && k == 0, D);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge: one wave per (sequence with several ranges, query head); partial
+// states combined in ascending range order:
+//   M = max m_i, L = sum 2^(m_i - M) l_i, out = sum 2^(m_i - M) o_i / L,
+//   lse = (M + log2 L) * ln 2.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(const MergeSeq* merges,
+                                                          const float* part_o,
+                                                          const float* part_ml, float* out,
+                                                          float* lse, int n_q_heads) {
+  constexpr int DL = D / 64;
+  const MergeSeq ms = merges[blockIdx.x];
+  const int hq = blockIdx.y;
+  const int lane = threadIdx.x;
+  float big_m = -INFINITY;
+  for (int i = 0; i < ms.count; ++i)
+    big_m = fmaxf(big_m, part_ml[(int64_t(ms.first + i) * n_q_heads + hq) * 2]);
+  float L = 0.f, o[DL];
+#pragma unroll
+  for (int k = 0; k < DL; ++k) o[k] = 0.f;
+  for (int i = 0; i < ms.count; ++i) {
+    const int64_t slot = int64_t(ms.first + i) * n_q_heads + hq;
+    const float mi = part_ml[slot * 2];
+    const float w = mi == -INFINITY ? 0.f : exp2f(mi - big_m);
+    L = fmaf(w, part_ml[slot * 2 + 1], L);
+#pragma unroll
+    for (int k = 0; k < DL; ++k) o[k] = fmaf(w, part_o[slot * D + lane + 64 * k], o[k]);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int k = 0; k < DL; ++k)
+    out[(int64_t(ms.seq) * n_q_heads + hq) * D + lane + 64 * k] = o[k] * inv;
+  if (lane == 0 && lse)
+    lse[int64_t(ms.seq) * n_q_heads + hq] = L > 0.f ? (big_m + __log2f(L)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// Bandwidth probe
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+
+__global__ __launch_bounds__(256) void bw_probe_kernel(const u32x4_t* src, size_t n16,
+                                                       u32x4_t* sink) {
+  u32x4_t a = {0u, 0u, 0u, 0u};
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+    a ^= __builtin_nontemporal_load(src + i);
+  if (a.x == 0x12345678u && a.y == 0x9abcdef0u) sink[0] = a;
+}
+
+template <typename K, typename P>
+hipError_t launch(K kernel, dim3 grid, dim3 block, hipStream_t stream, const P& params) {
+  hipLaunchKernelGGL(kernel, grid, block, 0, stream, params);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, const InjectDesc* d_desc,
+                         int n_desc, int layer_begin, int layer_end, int rope_mode,
+                         const float* d_cos, const float* d_sin, hipStream_t stream) {
+  const int eb = pool.dtype == PKV_F32 ? 4 : 2;
+  InjectParams p;
+  p.pool_k = static_cast<char*>(pool.k);
+  p.pool_v = static_cast<char*>(pool.v);
+  p.p_layer = pool.layer_stride * eb;
+  p.p_block = pool.block_stride * eb;
+  p.p_head = pool.head_stride * eb;
+  p.n_kv_heads = pool.n_kv_heads;
+  p.src_k = static_cast<const char*>(src.k);
+  p.src_v = static_cast<const char*>(src.v);
+  p.s_layer = src.layer_stride * eb;
+  p.s_token = src.token_stride * eb;
+  p.descs = d_desc;
+  p.layer_begin = layer_begin;
+  p.rope_mode = rope_mode;
+  p.cos_t = d_cos;
+  p.sin_t = d_sin;
+  dim3 grid(n_desc, layer_end - layer_begin);
+  dim3 block(kInjectThreads);
+#define PKV_INJ(DT, DD) \
+  if (pool.dtype == DT && pool.head_dim == DD) return launch(inject_rope_kernel<DT, DD>, grid, block, stream, p);
+  PKV_INJ(PKV_F32, 64) PKV_INJ(PKV_F32, 128) PKV_INJ(PKV_BF16, 64) PKV_INJ(PKV_BF16, 128)
+  PKV_INJ(PKV_F16, 64) PKV_INJ(PKV_F16, 128)
+#undef PKV_INJ
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_append(const pkv_pool& pool, int layer, const int32_t* d_tables,
+                         int table_stride, const int32_t* d_first_pos, int n_seqs, int n_new,
+                         const void* d_k, const void* d_v, int rope_mode, const float* d_cos,
+                         const float* d_sin, int max_pos, hipStream_t stream) {
+  const int eb = pool.dtype == PKV_F32 ? 4 : 2;
+  AppendParams p;
+  p.pool_k = static_cast<char*>(pool.k);
+  p.pool_v = static_cast<char*>(pool.v);
+  p.p_layer = pool.layer_stride * eb;
+  p.p_block = pool.block_stride * eb;
+  p.p_head = pool.head_stride * eb;
+  p.n_kv_heads = pool.n_kv_heads;
+  p.num_blocks = pool.num_blocks;
+  p.layer = layer;
+  p.tables = d_tables;
+  p.table_stride = table_stride;
+  p.first_pos = d_first_pos;
+  p.n_new = n_new;
+  p.k_new = static_cast<const char*>(d_k);
+  p.v_new = static_cast<const char*>(d_v);
+  p.rope_mode = rope_mode;
+  p.cos_t = d_cos;
+  p.sin_t = d_sin;
+  p.max_pos = max_pos;
+  dim3 grid(int64_t(n_seqs) * n_new);
+  dim3 block(256);
+#define PKV_APP(DT, DD) \
+  if (pool.dtype == DT && pool.head_dim == DD) return launch(append_kv_kernel<DT, DD>, grid, block, stream, p);
+  PKV_APP(PKV_F32, 64) PKV_APP(PKV_F32, 128) PKV_APP(PKV_BF16, 64) PKV_APP(PKV_BF16, 128)
+  PKV_APP(PKV_F16, 64) PKV_APP(PKV_F16, 128)
+#undef PKV_APP
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
+                         int kernel_variant, hipStream_t stream) {
+  const int eb = pool.dtype == PKV_F32 ? 4 : 2;
+  DecodeParams p;
+  p.pool_k = static_cast<const char*>(pool.k) + int64_t(layer) * pool.layer_stride * eb;
+  p.pool_v = static_cast<const char*>(pool.v) + int64_t(layer) * pool.layer_stride * eb;
+  p.p_layer = pool.layer_stride * eb;
+  p.p_block = pool.block_stride * eb;
+  p.p_head = pool.head_stride * eb;
+  p.num_blocks = pool.num_blocks;
+  p.n_kv_heads = pool.n_kv_heads;
+  p.n_q_heads = a.n_q_heads;
+  p.group = a.n_q_heads / pool.n_kv_heads;
+  p.q = static_cast<const char*>(a.q);
+  p.scale_log2 = a.scale * kLog2e;
+  p.tables = a.tables;
+  p.table_stride = a.table_stride;
+  p.items = a.items;
+  p.part_o = a.part_o;
+  p.part_ml = a.part_ml;
+  p.out = a.out;
+  p.lse = a.lse;
+  hipError_t e = hipSuccess;
+  if (a.n_items > 0) {
+    dim3 grid(a.n_items, pool.n_kv_heads);
+    dim3 block(64);
+    const bool mfma = kernel_variant != 1 && pool.dtype != PKV_F32 && p.group <= 16;
+    bool launched = false;
+#define PKV_DEC_MFMA(DT, DD) \
+    if (!launched && mfma && pool.dtype == DT && pool.head_dim == DD) { e = launch(decode_mfma_kernel<DT, DD, 2>, grid, block, stream, p); launched = true; }
+#define PKV_DEC_VALU(DT, DD) \
+    if (!launched && pool.dtype == DT && pool.head_dim == DD) { e = launch(decode_valu_kernel<DT, DD>, grid, block, stream, p); launched = true; }
+    PKV_DEC_MFMA(PKV_BF16, 64) PKV_DEC_MFMA(PKV_BF16, 128) PKV_DEC_MFMA(PKV_F16, 64)
+    PKV_DEC_MFMA(PKV_F16, 128)
+    PKV_DEC_VALU(PKV_F32, 64) PKV_DEC_VALU(PKV_F32, 128) PKV_DEC_VALU(PKV_BF16, 64)
+    PKV_DEC_VALU(PKV_BF16, 128) PKV_DEC_VALU(PKV_F16, 64) PKV_DEC_VALU(PKV_F16, 128)
+#undef PKV_DEC_MFMA
+#undef PKV_DEC_VALU
+    if (!launched) return hipErrorInvalidValue;
+    if (e != hipSuccess) return e;
+  }
+  if (a.n_merges > 0) {
+    dim3 grid(a.n_merges, a.n_q_heads);
+    dim3 block(64);
+    if (pool.head_dim == 64)
+      hipLaunchKernelGGL(decode_merge_kernel<64>, grid, block, 0, stream, a.merges, a.part_o,
+                         a.part_ml, a.out, a.lse, a.n_q_heads);
+    else
+      hipLaunchKernelGGL(decode_merge_kernel<128>, grid, block, 0, stream, a.merges, a.part_o,
+                         a.part_ml, a.out, a.lse, a.n_q_heads);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_bw_probe(const void* src, size_t n_bytes, void* sink, hipStream_t stream) {
+  const size_t n16 = n_bytes / 16;
+  const int blocks = 256 * 16;
+  hipLaunchKernelGGL(bw_probe_kernel, dim3(blocks), dim3(256), 0, stream,
+                     static_cast<const u32x4_t*>(src), n16, static_cast<u32x4_t*>(sink));
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,145 @@
+"""Write side on the GPU against the oracle, byte for byte: inject (aligned
+and unaligned runs, partial blocks, overwrites, every dtype and rotary
+mode) and append (T = 1, 17, 32, crossing block boundaries)."""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+CANARY = {"f32": 0x7FC0DEAD, "bf16": 0x7FAB, "f16": 0x7DAB}
+
+
+def canary_buffer(dp, dtype):
+    if dtype == "f32":
+        return np.full(dp.total, np.uint32(CANARY[dtype]).view(np.float32), dtype=np.float32)
+    return np.full(dp.total, CANARY[dtype], dtype=np.uint16)
+
+
+@pytest.mark.parametrize("dtype,d,mode", [
+    ("bf16", 128, "pairs"), ("bf16", 128, "halves"), ("bf16", 128, "none"),
+    ("f16", 128, "pairs"), ("f16", 64, "halves"), ("bf16", 64, "pairs"),
+    ("f32", 128, "pairs"), ("f32", 64, "halves"),
+])
+def test_inject_matches_oracle(dtype, d, mode):
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    from oracle import inject as o_inject
+    from oracle.allocator import AllocatorModel
+    from oracle.rope import rope_table
+    from tests import gpu_util as gu
+    from workloads.configs import host_normal
+
+    gu.say("inject", dtype, d, mode)
+    rng = np.random.default_rng(hash((dtype, d, mode)) % 2 ** 32)
+    L, H, NB, max_pos = 3, 4, 48, 300
+    dp = gu.DevicePool(L, NB, H, d, dtype, fill_bits=CANARY[dtype])
+    cache = pkv.pkv_cache_create(NB, 4, 16, free_list_seed=77)
+    model = AllocatorModel(NB, 4, 16, seed=77)
+    for s, n in enumerate((100, 37, 250, 16)):
+        pkv.pkv_alloc_blocks(cache, s, n)
+        model.alloc_blocks(s, n)
+    t, _ = pkv.pkv_block_table(cache, range(4), 16)
+    assert [list(r[r >= 0]) for r in t] == model.tables
+    n_src = 400
+    src_k = host_normal(rng, (L, n_src, H, d), dtype)
+    src_v = host_normal(rng, (L, n_src, H, d), dtype)
+    calls = [
+        [(0, 100, 0, 0), (1, 37, 0, 100), (3, 16, 0, 137)],                 # aligned prefill
+        [(2, 5, 3, 200), (2, 40, 9, 153), (2, 1, 250 - 1, 399),             # unaligned, partial
+         (2, 100, 60, 210), (0, 24, 40, 300), (1, 2, 35, 330)],              # overwrites
+        [(2, 0, 0, 0), (1, 1, 0, 398)],                                      # empty run, one token
+    ]
+    o_cos, o_sin = rope_table(d, 10000.0, max_pos)
+    cos, sin, dcos, dsin = gu.rope_tables(d, max_pos)
+    assert np.array_equal(cos, o_cos) and np.array_equal(sin, o_sin)
+    dk = gu.to_device_raw(src_k.reshape(-1), dtype)
+    dv = gu.to_device_raw(src_v.reshape(-1), dtype)
+    src = pkv.make_src(dk, dv, n_src * H * d, H * d, n_src)
+    ref = canary_buffer(dp, dtype)
+    kp, vp = dp.oracle_arrays(ref)
+    lens = [0] * 4
+    for i, runs in enumerate(calls):
+        lb, le = (0, L) if i != 1 else (1, L)        # one call on a layer range
+        ws = gu.workspace(pkv.pkv_inject_workspace_bytes(runs))
+        pkv.pkv_inject(cache, dp.desc(), src, runs, lb, le, mode, dcos, dsin, max_pos, ws)
+        torch.cuda.synchronize()
+        lens = o_inject.inject(kp, vp, dp.spec(), model.tables, lens, runs, src_k.reshape(-1),
+                               src_v.reshape(-1), n_src * H * d, H * d, lb, le, mode, o_cos, o_sin)
+        gu.assert_bytes_equal(dp.host_copy(), ref, "pool after inject call %d" % i)
+    _, glens = pkv.pkv_block_table(cache, range(4), 16)
+    assert list(glens) == lens
+
+
+def test_inject_rejects_overlap_and_range_without_enqueueing():
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    from tests import gpu_util as gu
+
+    dp = gu.DevicePool(1, 8, 2, 64, "bf16", fill_bits=0x1234)
+    cache = pkv.pkv_cache_create(8, 2, 4)
+    pkv.pkv_alloc_blocks(cache, 0, 40)
+    src_t = torch.zeros(64 * 2 * 64, dtype=torch.bfloat16, device="cuda")
+    src = pkv.make_src(src_t, src_t, 0, 128, 64)
+    cos, sin, dcos, dsin = gu.rope_tables(64, 100)
+    ws = gu.workspace(1 << 16)
+    before = dp.host_copy()
+    for runs, code in [([(0, 4, 0, 0), (0, 4, 2, 10)], "OVERLAP"),
+                       ([(0, 10, 40, 0)], "RANGE"),
+                       ([(0, 10, 95, 0)], "RANGE"),
+                       ([(0, 10, 0, 60)], "RANGE"),
+                       ([(1, 1, 0, 0)], "RANGE"),
+                       ([(5, 1, 0, 0)], "INVALID")]:
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_inject(cache, dp.desc(), src, runs, 0, 1, "pairs", dcos, dsin, 100, ws)
+        assert e.value.code == code, (runs, e.value)
+    torch.cuda.synchronize()
+    gu.assert_bytes_equal(dp.host_copy(), before, "pool after rejected calls")
+    _, lens = pkv.pkv_block_table(cache, [0, 1], 4)
+    assert list(lens) == [0, 0]
+
+
+@pytest.mark.parametrize("dtype,d,mode,n_new", [
+    ("bf16", 128, "pairs", 1), ("bf16", 128, "pairs", 32), ("bf16", 128, "halves", 17),
+    ("bf16", 128, "none", 1), ("f16", 128, "pairs", 32), ("f32", 64, "pairs", 3),
+])
+def test_append_matches_oracle(dtype, d, mode, n_new):
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    from oracle import inject as o_inject
+    from oracle.allocator import AllocatorModel
+    from oracle.rope import rope_table
+    from tests import gpu_util as gu
+    from workloads.configs import host_normal
+
+    gu.say("append", dtype, d, mode, n_new)
+    rng = np.random.default_rng(n_new * 7 + d)
+    L, H, NB, B, max_pos = 2, 8, 64, 6, 512
+    dp = gu.DevicePool(L, NB, H, d, dtype, fill_bits=CANARY[dtype])
+    cache = pkv.pkv_cache_create(NB, B, 32, free_list_seed=5)
+    model = AllocatorModel(NB, B, 32, seed=5)
+    start = [0, 15, 16, 31, 100, 47]
+    for s, n in enumerate(start):
+        pkv.pkv_extend(cache, [s], n)
+        model.extend([s], n)
+    seqs = list(range(B))
+    first = pkv.pkv_extend(cache, seqs, n_new)
+    assert list(first) == model.extend(seqs, n_new)
+    table, lens = pkv.pkv_block_table(cache, seqs, 32)
+    assert [list(r[r >= 0]) for r in table] == model.tables and list(lens) == model.lens
+    o_cos, o_sin = rope_table(d, 10000.0, max_pos)
+    _, _, dcos, dsin = gu.rope_tables(d, max_pos)
+    ref = canary_buffer(dp, dtype)
+    kp, vp = dp.oracle_arrays(ref)
+    tables_dev = torch.from_numpy(table).cuda()
+    first_dev = torch.from_numpy(first.astype(np.int32)).cuda()
+    for layer in range(L):
+        k_new = host_normal(rng, (B, n_new, H, d), dtype)
+        v_new = host_normal(rng, (B, n_new, H, d), dtype)
+        pkv.pkv_append_kv(dp.desc(), layer, tables_dev, first_dev, n_new,
+                          gu.to_device_raw(k_new.reshape(-1), dtype),
+                          gu.to_device_raw(v_new.reshape(-1), dtype), mode, dcos, dsin, max_pos)
+        o_inject.append(kp, vp, dp.spec(), layer, model.tables, model.lens, seqs, n_new,
+                        k_new, v_new, mode, o_cos, o_sin)
+    torch.cuda.synchronize()
+    gu.assert_bytes_equal(dp.host_copy(), ref, "pool after append")

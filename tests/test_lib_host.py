@@ -1,0 +1,187 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and its host logic (allocator, rotary table, size formula, decode
+split planner, argument checks) matches the oracle bit for bit.  No call
+here touches a GPU."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_inject_amd as pkv
+from oracle.allocator import AllocatorModel, AllocError
+from oracle.kv_size import kv_bytes
+from oracle.rope import rope_table
+from tests.conftest import ROOT
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = pkv.load_library()
+    names = header_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(pkv.SIGNATURES), set(names) ^ set(pkv.SIGNATURES)
+    assert pkv.pkv_abi_version() == 1
+
+
+def test_kv_bytes_matches_closed_form():
+    for args in [(80, 8, 128, 2, 8192), (32, 8, 128, 2, 1024), (12, 12, 64, 4, 1), (0, 1, 1, 1, 1)]:
+        assert pkv.pkv_kv_bytes(*args) == kv_bytes(*args)
+    assert pkv.pkv_kv_bytes(1, 1, 1, 1, -1) == 0
+
+
+@pytest.mark.parametrize("d,max_pos", [(64, 128), (128, 4096), (128, 32768 + 64)])
+def test_rope_table_bitwise_equal_to_oracle(d, max_pos):
+    c, s = pkv.pkv_rope_table(d, 10000.0, max_pos)
+    oc, os_ = rope_table(d, 10000.0, max_pos)
+    assert np.array_equal(c.view(np.uint32), oc.view(np.uint32))
+    assert np.array_equal(s.view(np.uint32), os_.view(np.uint32))
+
+
+def test_worked_example_through_the_abi():
+    c = pkv.pkv_cache_create(12, 2, 8)
+    pkv.pkv_set_blocks(c, 0, [3, 7, 1], 40)
+    pkv.pkv_set_blocks(c, 1, [2, 9], 20)
+    assert pkv.pkv_free_list(c) == [0, 4, 5, 6, 8, 10, 11]
+    first = pkv.pkv_extend(c, [1], 13)
+    t, lens = pkv.pkv_block_table(c, [0, 1], 8)
+    assert list(first) == [20] and list(lens) == [40, 33]
+    assert list(t[1][:3]) == [2, 9, 0]
+    pkv.pkv_cache_destroy(c)
+
+
+def _state(c, model, max_b):
+    t, lens = pkv.pkv_block_table(c, list(range(model.max_seqs)), max_b)
+    return ([list(r[r >= 0]) for r in t], list(lens), pkv.pkv_free_list(c))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 12345])
+def test_allocator_matches_oracle_on_random_operations(seed):
+    rng = np.random.default_rng(seed + 7)
+    nb, ns, mb = 40, 5, 12
+    c = pkv.pkv_cache_create(nb, ns, mb, free_list_seed=seed)
+    m = AllocatorModel(nb, ns, mb, seed=seed)
+    assert pkv.pkv_free_list(c) == list(m.free)
+    for step in range(400):
+        op = rng.integers(0, 4)
+        s = int(rng.integers(0, ns))
+        err_c = err_m = None
+        try:
+            if op == 0:
+                n = int(rng.integers(0, 120))
+                try:
+                    pkv.pkv_alloc_blocks(c, s, n)
+                except pkv.PkvError as e:
+                    err_c = e.code
+                try:
+                    m.alloc_blocks(s, n)
+                except AllocError as e:
+                    err_m = e.code
+            elif op == 1:
+                seqs = sorted(set(rng.integers(0, ns, size=int(rng.integers(1, 4))).tolist()))
+                n = int(rng.integers(0, 40))
+                try:
+                    first = list(pkv.pkv_extend(c, seqs, n))
+                except pkv.PkvError as e:
+                    err_c, first = e.code, None
+                try:
+                    mfirst = m.extend(seqs, n)
+                except AllocError as e:
+                    err_m, mfirst = e.code, None
+                assert first == mfirst
+            elif op == 2:
+                pkv.pkv_free_seq(c, s)
+                m.free_seq(s)
+            else:
+                ids = list(m.free)[:int(rng.integers(0, 4))]
+                ids = [int(x) for x in rng.permutation(ids)] if ids else []
+                ln = int(rng.integers(0, 16 * len(ids) + 1))
+                try:
+                    pkv.pkv_set_blocks(c, s, ids, ln)
+                except pkv.PkvError as e:
+                    err_c = e.code
+                try:
+                    m.set_blocks(s, ids, ln)
+                except AllocError as e:
+                    err_m = e.code
+        finally:
+            pass
+        assert err_c == err_m, (step, op, err_c, err_m)
+        tables, lens, free = _state(c, m, mb)
+        assert tables == m.tables and lens == m.lens and free == list(m.free), step
+        m.check_invariants()
+    pkv.pkv_cache_destroy(c)
+
+
+def test_seeded_free_list_matches_oracle_at_workload_size():
+    from workloads.configs import inject_structure
+    st = inject_structure(n_chunks=50)
+    c = pkv.pkv_cache_create(st["num_blocks"], 64, st["max_blocks"], st["free_list_seed"])
+    m = AllocatorModel(st["num_blocks"], 64, st["max_blocks"], seed=st["free_list_seed"])
+    assert pkv.pkv_free_list(c) == list(m.free)
+    for b, ml in enumerate(st["mem_lens"]):
+        pkv.pkv_alloc_blocks(c, b, int(ml))
+        m.alloc_blocks(b, int(ml))
+    tables, _, free = _state(c, m, st["max_blocks"])
+    assert tables == m.tables and free == list(m.free)
+
+
+def test_decode_plan_splits():
+    lens = [37, 100, 0, 5000, 16, 17]
+    plan = pkv.pkv_decode_plan_create(lens, 4, 2, 64, 32)
+    # ceil(len / 32) ranges per sequence
+    assert pkv.pkv_decode_plan_items(plan) == sum(-(-x // 32) for x in lens)
+    assert pkv.pkv_decode_plan_part_tokens(plan) == 32
+    assert pkv.pkv_decode_workspace_bytes(plan) % 256 == 0
+    pkv.pkv_decode_plan_destroy(plan)
+    plan = pkv.pkv_decode_plan_create([8192] * 32, 64, 8, 128, 0)
+    assert pkv.pkv_decode_plan_part_tokens(plan) == 1024       # ~2048 workgroups
+    assert pkv.pkv_decode_plan_items(plan) == 32 * 8
+    pkv.pkv_decode_plan_destroy(plan)
+    for bad in [dict(part=8), dict(hq=6, hkv=4), dict(d=96)]:
+        with pytest.raises(pkv.PkvError):
+            pkv.pkv_decode_plan_create([10], bad.get("hq", 4), bad.get("hkv", 2),
+                                       bad.get("d", 64), bad.get("part", 0))
+
+
+def test_inject_host_validation_errors():
+    """Argument errors are found on the host before any device work (the
+    fake device pointers below are never dereferenced)."""
+    fake = 1 << 20
+    pool = pkv.pkv_pool(1, 8, 2, 64, pkv.PKV_BF16, 0, fake, fake + 4096, 8 * 4096, 4096, 1024)
+    src = pkv.pkv_src(fake, fake, 0, 128, 64)
+    c = pkv.pkv_cache_create(8, 2, 4)
+    pkv.pkv_alloc_blocks(c, 0, 40)
+    cases = [([(0, 4, 0, 0), (0, 4, 2, 10)], "OVERLAP"), ([(0, 10, 40, 0)], "RANGE"),
+             ([(0, 10, 0, 60)], "RANGE"), ([(1, 1, 0, 0)], "RANGE"), ([(5, 1, 0, 0)], "INVALID"),
+             ([(0, -1, 0, 0)], "INVALID")]
+    for runs, code in cases:
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_inject(c, pool, src, runs, 0, 1, "pairs", fake, fake, 100, None, stream=0)
+        assert e.value.code == code
+    bad_pool = pkv.pkv_pool(1, 8, 2, 96, pkv.PKV_BF16, 0, fake, fake, 0, 0, 0)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_inject(c, bad_pool, src, [(0, 1, 0, 0)], 0, 1, "pairs", fake, fake, 100, None,
+                       stream=0)
+    assert e.value.code == "UNSUPPORTED"
+    misaligned = pkv.pkv_pool(1, 8, 2, 64, pkv.PKV_BF16, 0, fake + 2, fake, 0, 4096, 1024)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_inject(c, misaligned, src, [(0, 1, 0, 0)], 0, 1, "pairs", fake, fake, 100, None,
+                       stream=0)
+    assert e.value.code == "INVALID"
+    with pytest.raises(pkv.PkvError) as e:      # needs a workspace
+        pkv.pkv_inject(c, pool, src, [(0, 1, 0, 0)], 0, 1, "pairs", fake, fake, 100, None,
+                       stream=0)
+    assert e.value.code == "WORKSPACE"
+    _, lens = pkv.pkv_block_table(c, [0], 4)
+    assert list(lens) == [0]
+    pkv.pkv_cache_destroy(c)

@@ -170,3 +170,20 @@ def test_interleaved_strides():
                     block_stride=2 * 2 * 1024, head_stride=1024)
     assert spec.plane_base(0, 3, 1) == 3 * 4096 + 1024
     assert spec.elements() == 3 * 4096 + 1024 + 1024
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("f16", 64)])
+def test_plane_gather_equals_element_gather(dtype, d):
+    from oracle.layout import gather_sequence_planes
+    spec = PoolSpec(2, 9, 3, d, dtype, layer_stride=9 * 2 * 3 * 16 * d,
+                    block_stride=2 * 3 * 16 * d, head_stride=16 * d)
+    rng = np.random.default_rng(11)
+    sdt = spec.storage_dtype()
+    buf = (rng.integers(0, 2 ** 16, size=spec.elements() + 3 * 16 * d).astype(sdt)
+           if sdt == np.uint16 else rng.standard_normal(spec.elements() + 3 * 16 * d).astype(sdt))
+    kp, vp = buf, buf[3 * 16 * d:]
+    row = [4, 0, 7, 2, -1]
+    for n in (1, 16, 17, 50, 64):
+        a = gather_sequence(kp, vp, spec, 1, row, n, heads=[2, 0])
+        b = gather_sequence_planes(kp, vp, spec, 1, row, n, heads=[2, 0])
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
