@@ -463,6 +463,21 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeParams p) {
         if (i + DEPTH < nblk) issue(i + DEPTH, d);
 
         const int valid = it.n_tokens - i * kBlock;  // tokens of this block in range
+        if (valid < kBlock || !blk_ok) {
+          // Slots past the sequence end (or of a rejected block id) may hold
+          // anything, NaN included: zero their V so that 0-weight * V stays 0.
+          // Lane holds tokens 4*grp + e, e = 0..3, as 16-bit halves of x, y.
+          const int lim = blk_ok ? valid : 0;
+          const uint32_t mx0 = (4 * grp + 0 < lim ? 0x0000ffffu : 0u) |
+                               (4 * grp + 1 < lim ? 0xffff0000u : 0u);
+          const uint32_t mx1 = (4 * grp + 2 < lim ? 0x0000ffffu : 0u) |
+                               (4 * grp + 3 < lim ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            vcur[n].x &= mx0;
+            vcur[n].y &= mx1;
+          }
+        }
         float s4[4];
         float mx = -INFINITY;
 #pragma unroll
@@ -612,8 +627,9 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
         const int j = lane + 64 * k;
         const T* vrow = reinterpret_cast<const T*>(vp + int64_t(j) * kBlock * E);
         float vv[kBlock];
+        const int lim = ok ? it.n_tokens - bi * kBlock : 0;  // live tokens of the block
 #pragma unroll
-        for (int t = 0; t < kBlock; ++t) vv[t] = Fmt<DT>::to_f32(vrow[t]);
+        for (int t = 0; t < kBlock; ++t) vv[t] = t < lim ? Fmt<DT>::to_f32(vrow[t]) : 0.f;
         for (int i = 0; i < nh; ++i) {
           float a = acc[i][k];
 #pragma unroll

@@ -227,3 +227,30 @@ def test_llama70b_full_size_sampled():
                          seqs=seqs)
     del dp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 64, 8, 128), ("f16", 8, 8, 128),
+                                             ("f32", 4, 2, 64), ("bf16", 4, 2, 64)])
+def test_nan_in_unused_slots_does_not_leak(dtype, hq, hkv, d):
+    """Slots past a sequence's end hold NaN; the output must not see them."""
+    import torch
+    from oracle.layout import k_element_offsets, v_element_offsets
+    from tests import gpu_util as gu
+    from workloads.configs import host_normal, deal_tables
+    rng = np.random.default_rng(41)
+    lens = np.array([1, 17, 30, 100, 250], dtype=np.int64)
+    need = int(sum(-(-x // 16) for x in lens))
+    table = deal_tables(rng.permutation(need).astype(np.int32), lens, 16)
+    dp = gu.DevicePool(1, need, hkv, d, dtype)
+    host = host_normal(rng, (dp.total,), dtype)
+    nan = np.float32(np.nan) if dtype == "f32" else np.uint16(0x7FC1 if dtype == "bf16" else 0x7E01)
+    kp, vp = dp.oracle_arrays(host)
+    for b, n in enumerate(lens):
+        blk = table[b][(n - 1) // 16]
+        for t in range(int(n) % 16 or 16, 16):
+            for h in range(hkv):
+                kp[k_element_offsets(dp.spec(), 0, blk, h, t)] = nan
+                vp[v_element_offsets(dp.spec(), 0, blk, h, t)] = nan
+    dp.buf.copy_(gu.to_device_raw(host, dtype))
+    q = host_normal(rng, (len(lens), hq, d), dtype)
+    check_decode_all(dp, 0, q, table, lens, hq, parts=(0, 16, 64), variants=("auto", "valu"))
