@@ -35,14 +35,22 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def device_pool(n_layers, num_blocks, n_kv_heads, head_dim, dtype, seed):
-    """[layer][block][K planes | V planes] buffer filled with N(0,1) per layer."""
+POOL_LAYOUT = os.environ.get("PKV_BENCH_LAYOUT", "block")
+
+
+def device_pool(n_layers, num_blocks, n_kv_heads, head_dim, dtype, seed, layout=None):
+    """Pool buffer filled with N(0,1) per layer.  layout "head":
+    [layer][block][head][K plane | V plane] (one (block, head) = K and V
+    adjacent); layout "block": [layer][block][K planes | V planes]."""
     import torch
     import paged_kv_cache_inject_amd as pkv
     from workloads.configs import device_normal
+    layout = layout or POOL_LAYOUT
     plane = 16 * head_dim
     block_stride = 2 * n_kv_heads * plane
     layer_stride = num_blocks * block_stride
+    head_stride = 2 * plane if layout == "head" else plane
+    v_off = plane if layout == "head" else n_kv_heads * plane
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
     buf = torch.empty(n_layers * layer_stride, dtype=tdt, device="cuda")
     if seed is not None:
@@ -51,8 +59,8 @@ def device_pool(n_layers, num_blocks, n_kv_heads, head_dim, dtype, seed):
                 layer_stride, dtype, seed * 1000 + layer)
     e = buf.element_size()
     desc = pkv.pkv_pool(n_layers, num_blocks, n_kv_heads, head_dim, pkv.DTYPE_CODES[dtype], 0,
-                        buf.data_ptr(), buf.data_ptr() + n_kv_heads * plane * e, layer_stride,
-                        block_stride, plane)
+                        buf.data_ptr(), buf.data_ptr() + v_off * e, layer_stride, block_stride,
+                        head_stride)
     return buf, desc
 
 
@@ -83,18 +91,30 @@ def bw_probe(n_bytes=8 << 30, reps=5):
     return gbps
 
 
-def run_decode(steps, warmup):
+def decode_workload(name):
+    from workloads.configs import (CONFIGS, llama70b_structure, llama8b_structure,
+                                   ragged_mha_structure)
+    if name == "70b":
+        return CONFIGS[3], llama70b_structure(CONFIGS[3])
+    if name == "8b":
+        return CONFIGS[2], llama8b_structure(CONFIGS[2])
+    if name == "ragged":
+        return CONFIGS[5], ragged_mha_structure(CONFIGS[5])
+    raise ValueError(name)
+
+
+def run_decode(steps, warmup, workload="70b"):
     import torch
     import paged_kv_cache_inject_amd as pkv
-    from workloads.configs import CONFIGS, llama70b_structure, host_normal
-    cfg = CONFIGS[3]
-    st = llama70b_structure(cfg)
+    from workloads.configs import host_normal
+    cfg, st = decode_workload(workload)
     lens = st["lens"]
     log("decode: allocating and filling %d layers x %d blocks" % (cfg.n_layers, st["num_blocks"]))
     buf, pool = device_pool(cfg.n_layers, st["num_blocks"], cfg.n_kv_heads, cfg.head_dim,
                             cfg.dtype, cfg.seed)
     q_host = host_normal(st["rng"], (cfg.batch, cfg.n_q_heads, cfg.head_dim), cfg.dtype)
-    q = torch.from_numpy(q_host.view(np.int16)).cuda().view(torch.bfloat16)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[cfg.dtype]
+    q = torch.from_numpy(q_host.view(np.int16)).cuda().view(tdt)
     tables = torch.from_numpy(st["tables"]).cuda()
     out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, device="cuda")
     lse = torch.empty(cfg.batch, cfg.n_q_heads, device="cuda")
@@ -103,6 +123,7 @@ def run_decode(steps, warmup):
     ws = torch.empty(pkv.pkv_decode_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
     n_items = pkv.pkv_decode_plan_items(plan)
     part_tokens = pkv.pkv_decode_plan_part_tokens(plan)
+    waves = pkv.pkv_decode_plan_waves(plan)
 
     def step(events=None):
         pkv.pkv_decode_plan_upload(plan, ws)
@@ -137,8 +158,8 @@ def run_decode(steps, warmup):
     res = dict(ms_per_step=ms_step, wall_ms_per_step=wall * 1e3 / steps,
                bytes_per_step=per_launch * cfg.n_layers, bytes_per_launch=per_launch,
                launch_ms_avg=float(np.mean(launch_ms)), launch_ms_p50=float(np.median(launch_ms)),
-               n_items=n_items, part_tokens=part_tokens, workload=cfg.workload,
-               batch=cfg.batch, context=int(lens[0]), layers=cfg.n_layers)
+               n_items=n_items, part_tokens=part_tokens, waves=waves, workload=cfg.workload,
+               batch=cfg.batch, context=int(lens.max()), layers=cfg.n_layers)
     res["value"] = res["bytes_per_step"] / (ms_step * 1e-3) / 1e9
     res["launch_gbps"] = per_launch / (res["launch_ms_avg"] * 1e-3) / 1e9
     log("decode: %.3f ms/step, %.1f GB/s; per launch %.1f us -> %.1f GB/s"
@@ -202,9 +223,10 @@ def run_inject(reps):
     return res
 
 
-def cpu_baseline(budget_s=15.0):
-    """The oracle's decode on whole sequences of the decode workload (layer 0,
-    all 64 query heads), one thread, until the budget is spent."""
+def cpu_baseline(budget_s=12.0):
+    """The oracle's decode on whole sequences of the decode workload (all 64
+    query heads per sequence, layer after layer), one thread, until the
+    budget is spent."""
     import torch
     from threadpoolctl import threadpool_limits
     from oracle import attention as o_att
@@ -216,22 +238,28 @@ def cpu_baseline(budget_s=15.0):
     plane = 16 * cfg.head_dim
     bs = 2 * cfg.n_kv_heads * plane
     q = host_normal(st["rng"], (cfg.batch, cfg.n_q_heads, cfg.head_dim), cfg.dtype)
-    layer0 = device_normal(nb * bs, "bf16", cfg.seed * 1000).view(torch.int16).cpu().numpy()
-    flat = layer0.view(np.uint16)
     spec = PoolSpec(1, nb, cfg.n_kv_heads, cfg.head_dim, "bf16", nb * bs, bs, plane)
-    kp, vp = flat, flat[cfg.n_kv_heads * plane:]
     rows = [list(r) for r in st["tables"]]
-    done, t0 = 0, time.perf_counter()
-    with threadpool_limits(limits=1):
-        while time.perf_counter() - t0 < budget_s and done < cfg.batch:
-            o_att.decode_paged(q, kp, vp, spec, 0, rows, st["lens"], cfg.n_q_heads,
-                               seqs=[done], by_plane=True)
-            done += 1
-    dt = time.perf_counter() - t0
-    by = decode_bytes(st["lens"][:done], cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads, 2)
+    seqs_done, layers, dt = 0, 0, 0.0
+    while dt < budget_s and layers < cfg.n_layers:
+        layer = device_normal(nb * bs, "bf16", cfg.seed * 1000 + layers)
+        flat = layer.view(torch.int16).cpu().numpy().view(np.uint16)
+        del layer
+        kp, vp = flat, flat[cfg.n_kv_heads * plane:]
+        t0 = time.perf_counter()
+        with threadpool_limits(limits=1):
+            for b in range(cfg.batch):
+                o_att.decode_paged(q, kp, vp, spec, 0, rows, st["lens"], cfg.n_q_heads,
+                                   seqs=[b], by_plane=True)
+                seqs_done += 1
+                if dt + time.perf_counter() - t0 > budget_s:
+                    break
+        dt += time.perf_counter() - t0
+        layers += 1
+    by = seqs_done * decode_bytes(st["lens"][:1], cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads, 2)
     return dict(value=by / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample="layer 0, %d of 32 sequences x 8192 tokens, all 64 query heads, "
-                       "float64 numpy, %.1f s" % (done, dt))
+                sample="%d (sequence, layer) pairs of the decode workload: 8192 tokens, all 64 "
+                       "query heads each; float64 numpy, one thread, %.1f s" % (seqs_done, dt))
 
 
 def main():
@@ -242,6 +270,8 @@ def main():
     ap.add_argument("--inject-reps", type=int, default=10)
     ap.add_argument("--no-inject", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-workload", default="70b", choices=["70b", "8b", "ragged"],
+                    help="decode workload timed (the reported line uses 70b)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the hot path here runs on a single MI355X; "
@@ -255,7 +285,7 @@ def main():
     log("device:", props.name, getattr(props, "gcnArchName", "?"), "%d CUs" % props.multi_processor_count)
     probe = bw_probe()
     log("bw probe: %.1f GB/s" % probe)
-    dec, _ = run_decode(args.steps, args.warmup)
+    dec, _ = run_decode(args.steps, args.warmup, args.decode_workload)
     inj = None if args.no_inject else run_inject(args.inject_reps)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     line = {
@@ -274,11 +304,12 @@ def main():
         "pct_of_peak": round(100 * dec["value"] / PEAK_HBM_GBPS, 2),
         "config": {"workload": dec["workload"], "batch": dec["batch"], "context": dec["context"],
                    "layers": dec["layers"], "part_tokens": dec["part_tokens"],
-                   "work_items": dec["n_items"]},
+                   "work_items": dec["n_items"], "waves_per_workgroup": dec["waves"],
+                   "pool_layout": POOL_LAYOUT},
         "roofline": {"bound": "hbm", "achieved": round(dec["launch_gbps"], 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(dec["launch_gbps"] / PEAK_HBM_GBPS, 4), "traffic": None,
-                     "kernel": "pkv_decode_attention (one layer)",
+                     "kernel": "decode_mfma_kernel (pkv_decode_attention, one layer)",
                      "bytes_per_launch": dec["bytes_per_launch"],
                      "launch_us_avg": round(dec["launch_ms_avg"] * 1e3, 2)},
         "bw_probe_gbps": round(probe, 1),

@@ -255,10 +255,10 @@ pkv_status pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* d_t
  * lens[b] cached tokens (positions 0 .. lens[b]-1, no mask).
  *
  * A plan fixes the lengths (host, int64 lens[n_seqs]) and splits every
- * sequence into 16-aligned token ranges of part_tokens tokens (0 = chosen
- * from the total work), which run on separate workgroups; their softmax
- * states (running max, sum, unnormalised output) are merged by log-sum-exp in
- * ascending range order.  Upload the plan into a device workspace once, then
+ * sequence longer than part_tokens (a multiple of 16; 0 = chosen from the
+ * total work) into ranges of part_tokens tokens, which run on separate
+ * workgroups; their softmax states (running max, sum, unnormalised output)
+ * are merged by log-sum-exp in ascending range order.  Upload the plan into a device workspace once, then
  * call pkv_decode_attention for every layer that shares the lengths.
  *
  * Outputs: d_out (device float [n_seqs][n_q_heads][head_dim]) and, if not
@@ -278,6 +278,11 @@ int32_t pkv_decode_plan_items(const pkv_plan* plan);
 
 /* Token range length the plan chose; -1 for NULL. */
 int32_t pkv_decode_plan_part_tokens(const pkv_plan* plan);
+
+/* Waves per workgroup the plan chose (1, 2, 4 or 8): the waves of one
+ * workgroup take turns over the blocks of one token range and merge their
+ * softmax states in LDS; -1 for NULL. */
+int32_t pkv_decode_plan_waves(const pkv_plan* plan);
 
 /* Device workspace a plan needs (work list + float partials). */
 size_t pkv_decode_workspace_bytes(const pkv_plan* plan);

@@ -96,6 +96,7 @@ SIGNATURES = {
     "pkv_decode_plan_destroy": (None, [_P]),
     "pkv_decode_plan_items": (_I32, [_P]),
     "pkv_decode_plan_part_tokens": (_I32, [_P]),
+    "pkv_decode_plan_waves": (_I32, [_P]),
     "pkv_decode_workspace_bytes": (_SZ, [_P]),
     "pkv_decode_plan_upload": (_I32, [_P, _P, _SZ, _P]),
     "pkv_decode_attention": (_I32, [_P, ctypes.POINTER(pkv_pool), _I32, _P, ctypes.c_float, _P,
@@ -306,6 +307,10 @@ def pkv_decode_plan_items(plan) -> int:
 
 def pkv_decode_plan_part_tokens(plan) -> int:
     return load_library().pkv_decode_plan_part_tokens(plan)
+
+
+def pkv_decode_plan_waves(plan) -> int:
+    return load_library().pkv_decode_plan_waves(plan)
 
 
 def pkv_decode_workspace_bytes(plan) -> int:

@@ -137,7 +137,7 @@ struct pkv_cache {
 
 struct pkv_plan {
   int32_t n_seqs = 0, n_q_heads = 0, n_kv_heads = 0, head_dim = 0, part_tokens = 0;
-  int32_t n_slots = 0;
+  int32_t n_slots = 0, waves = 1;
   std::vector<DecodeItem> items;
   std::vector<MergeSeq> merges;
   size_t off_items = 0, off_merges = 0, off_part_o = 0, off_part_ml = 0, ws_bytes = 0;
@@ -522,21 +522,33 @@ pkv_status pkv_decode_plan_create(const int64_t* lens, int32_t n_seqs, int32_t n
     return fail(PKV_E_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
   if (part_tokens < 0 || part_tokens % kBlock)
     return fail(PKV_E_INVALID, "part_tokens must be a non-negative multiple of 16");
-  int64_t total = 0;
+  int64_t total = 0, total_blocks = 0, n_nonempty = 0;
   for (int32_t b = 0; b < n_seqs; ++b) {
     if (lens[b] < 0 || lens[b] > (int64_t(1) << 30))
       return fail(PKV_E_RANGE, "length %lld of sequence %d", (long long)lens[b], b);
     total += lens[b];
+    total_blocks += blocks_for(lens[b]);
+    n_nonempty += lens[b] > 0;
+  }
+  // Waves per workgroup: the waves of one workgroup share a token range,
+  // taking its blocks in turn, so give each wave at least ~4 blocks.
+  int32_t waves = 8;
+  const int64_t avg_blocks = n_nonempty ? total_blocks / n_nonempty : 0;
+  while (waves > 1 && avg_blocks < 4 * waves) waves /= 2;
+  if (const char* env = std::getenv("PKV_DECODE_WAVES")) {
+    const int w = std::atoi(env);
+    if (w == 1 || w == 2 || w == 4 || w == 8) waves = w;
   }
   int32_t part = part_tokens;
   if (part == 0) {
     if (const char* env = std::getenv("PKV_PART_TOKENS")) part = std::atoi(env);
     if (part <= 0 || part % kBlock) {
-      // Aim at ~2048 workgroups (8 per CU) of (token range, KV head); keep
-      // ranges between 256 and 4096 tokens.
-      const int64_t per = (total * n_kv_heads + 2047) / 2048;
-      int64_t p = (per + kBlock - 1) / kBlock * kBlock;
-      part = int32_t(std::min<int64_t>(4096, std::max<int64_t>(256, p)));
+      // Spread the work over ~2048 waves (8 per CU of 256): a sequence longer
+      // than its share is split into several ranges merged afterwards.
+      const int64_t wgs = std::max<int64_t>(1, 2048 / waves);
+      const int64_t per = (total * n_kv_heads + wgs - 1) / wgs;
+      const int64_t p = (per + kBlock - 1) / kBlock * kBlock;
+      part = int32_t(std::min<int64_t>(1 << 30, std::max<int64_t>(int64_t(64) * waves, p)));
     }
   }
   pkv_plan* plan = new (std::nothrow) pkv_plan();
@@ -546,23 +558,26 @@ pkv_status pkv_decode_plan_create(const int64_t* lens, int32_t n_seqs, int32_t n
   plan->n_kv_heads = n_kv_heads;
   plan->head_dim = head_dim;
   plan->part_tokens = part;
+  plan->waves = waves;
   int32_t slots = 0;
   for (int32_t b = 0; b < n_seqs; ++b) {
     const int64_t n_items = (lens[b] + part - 1) / part;
-    if (n_items == 0) {
-      plan->merges.push_back(MergeSeq{b, 0, 0, 0});  // empty: out 0, lse -inf
-    } else if (n_items == 1) {
+    if (n_items <= 1) {
+      // whole sequence in one item (an empty one included): final output
       plan->items.push_back(DecodeItem{b, 0, int32_t(lens[b]), -1});
     } else {
-      MergeSeq m{b, slots, int32_t(n_items), 0};
+      plan->merges.push_back(MergeSeq{b, slots, int32_t(n_items), 0});
       for (int64_t i = 0; i < n_items; ++i) {
         const int64_t t0 = i * part;
         const int64_t n = std::min<int64_t>(part, lens[b] - t0);
         plan->items.push_back(DecodeItem{b, int32_t(t0), int32_t(n), slots++});
       }
-      plan->merges.push_back(m);
     }
   }
+  // Longest items first: the dispatcher starts workgroups in grid order, so
+  // this approximates longest-processing-time-first scheduling.
+  std::stable_sort(plan->items.begin(), plan->items.end(),
+                   [](const DecodeItem& x, const DecodeItem& y) { return x.n_tokens > y.n_tokens; });
   plan->n_slots = slots;
   size_t off = 0;
   plan->off_items = off;
@@ -587,6 +602,8 @@ int32_t pkv_decode_plan_items(const pkv_plan* plan) {
 int32_t pkv_decode_plan_part_tokens(const pkv_plan* plan) {
   return plan ? plan->part_tokens : -1;
 }
+
+int32_t pkv_decode_plan_waves(const pkv_plan* plan) { return plan ? plan->waves : -1; }
 
 size_t pkv_decode_workspace_bytes(const pkv_plan* plan) { return plan ? plan->ws_bytes : 0; }
 
@@ -645,6 +662,7 @@ pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int3
   a.n_items = int(plan->items.size());
   a.merges = reinterpret_cast<const MergeSeq*>(ws + plan->off_merges);
   a.n_merges = int(plan->merges.size());
+  a.waves = plan->waves;
   a.part_o = reinterpret_cast<float*>(ws + plan->off_part_o);
   a.part_ml = reinterpret_cast<float*>(ws + plan->off_part_ml);
   a.out = d_out;

@@ -22,9 +22,9 @@ struct InjectDesc {
 static_assert(sizeof(InjectDesc) == 72, "descriptor layout");
 
 // One decode work item: tokens [t_begin, t_begin + n_tokens) of sequence seq
-// (t_begin a multiple of 16).  `slot` is where its partial softmax state is
-// stored; slot < 0 means the item covers the whole sequence and writes the
-// final output directly.
+// (t_begin a multiple of 16).  slot < 0: the item covers the whole sequence
+// (an empty one included) and writes the final output; otherwise it stores
+// its partial softmax state in partial slot `slot`, merged afterwards.
 struct DecodeItem {
   int32_t seq;
   int32_t t_begin;
@@ -32,8 +32,7 @@ struct DecodeItem {
   int32_t slot;
 };
 
-// Merge work: sequence seq owns partial slots [first, first + count); count 0
-// marks an empty sequence (output 0, lse -inf).
+// Merge work: sequence seq owns partial slots [first, first + count).
 struct MergeSeq {
   int32_t seq;
   int32_t first;
@@ -60,6 +59,7 @@ struct DecodeArgs {
   int n_items;
   const MergeSeq* merges;
   int n_merges;
+  int waves;       // waves per workgroup sharing one item (1, 2, 4 or 8)
   float* part_o;   // [n_slots][n_q_heads][head_dim]
   float* part_ml;  // [n_slots][n_q_heads][2]
   float* out;

@@ -8,11 +8,13 @@
 //   append_kv_kernel       one workgroup per new token (the per-step append of
 //                          "InferScale" §2 / "LLM Inference: KV Caching",
 //                          "The fix").
-//   decode_mfma_kernel     read side: one wave per (token range, KV head);
-//                          QK^T and PV of the whole GQA group on MFMA tiles,
-//                          online softmax in registers.
+//   decode_mfma_kernel     read side: one workgroup per (token range, KV head),
+//                          its waves taking interleaved blocks; QK^T and PV of
+//                          the whole GQA group on MFMA tiles, online softmax
+//                          in registers, the waves' states merged in LDS.
 //   decode_valu_kernel     generic read side for any dtype / group size.
-//   decode_merge_kernel    log-sum-exp merge of the token-range partials.
+//   decode_merge_kernel    log-sum-exp merge of ranges of one sequence that
+//                          ran on different workgroups.
 //   bw_probe_kernel        streaming read for the same-run HBM ceiling.
 //
 // Pool plane layouts (see include/pkv.h): K plane = d/X chunks x 16 tokens x X
@@ -76,6 +78,19 @@ template <> struct Fmt<PKV_F16> {
 // 16-byte global access helpers.
 __device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ inline void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Streaming (non-temporal) loads for data read exactly once: the cached K/V
+// of a decode step.  The hint keeps them from displacing reusable lines.
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+__device__ inline uint4 ld16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline uint2 ld8_stream(const void* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
 
 // Rotate the X elements of one 16-byte chunk.  PAIRS: element e pairs with
 // e^1 inside the chunk (pair index = (first_dim + e) / 2).  HALVES: element e
@@ -392,11 +407,12 @@ template <> struct Mfma<PKV_F16> {
   }
 };
 
-template <int DT, int D, int DEPTH>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeParams p) {
+template <int DT, int D, int DEPTH, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   constexpr int S = D / 32;   // QK MFMA steps (4 chunks of 8 dims each)
   constexpr int NT = D / 16;  // PV MFMA tiles of 16 dims
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int row = lane & 15;
   const int grp = lane >> 4;
   const DecodeItem it = p.items[blockIdx.x];
@@ -419,6 +435,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeParams p) {
   const char* kbase = p.pool_k + int64_t(g) * p.p_head;
   const char* vbase = p.pool_v + int64_t(g) * p.p_head;
   const int nblk = (it.n_tokens + kBlock - 1) / kBlock;
+  // This wave takes blocks wave, wave + NW, wave + 2 NW, ...
+  const int nj = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;
 
   f32x4_t acc[NT];
 #pragma unroll
@@ -430,29 +448,28 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeParams p) {
   uint2 vbuf[DEPTH][NT];
   bool okbuf[DEPTH];
 
-  auto issue = [&](int i, int d) {
-    int blk = tab[i];
+  auto issue = [&](int j, int d) {
+    int blk = tab[wave + j * NW];
     const bool ok = unsigned(blk) < unsigned(p.num_blocks);
     okbuf[d] = ok;
     blk = ok ? blk : 0;
     const char* kp = kbase + int64_t(blk) * p.p_block;
     const char* vp = vbase + int64_t(blk) * p.p_block;
 #pragma unroll
-    for (int s = 0; s < S; ++s) kbuf[d][s] = ld16(kp + (64 * s + lane) * 16);
+    for (int s = 0; s < S; ++s) kbuf[d][s] = ld16_stream(kp + (64 * s + lane) * 16);
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      vbuf[d][n] = *reinterpret_cast<const uint2*>(vp + (16 * n + row) * 32 + grp * 8);
+    for (int n = 0; n < NT; ++n) vbuf[d][n] = ld8_stream(vp + (16 * n + row) * 32 + grp * 8);
   };
 
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d)
-    if (d < nblk) issue(d, d);
+    if (d < nj) issue(d, d);
 
-  for (int i0 = 0; i0 < nblk; i0 += DEPTH) {
+  for (int j0 = 0; j0 < nj; j0 += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
-      const int i = i0 + d;
-      if (i < nblk) {
+      const int j = j0 + d;
+      if (j < nj) {
         f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < S; ++s) sc = Mfma<DT>::qk(kbuf[d][s], qreg[s], sc);
@@ -460,9 +477,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) vcur[n] = vbuf[d][n];
         const bool blk_ok = okbuf[d];
-        if (i + DEPTH < nblk) issue(i + DEPTH, d);
+        if (j + DEPTH < nj) issue(j + DEPTH, d);
 
-        const int valid = it.n_tokens - i * kBlock;  // tokens of this block in range
+        const int valid = it.n_tokens - (wave + j * NW) * kBlock;  // tokens in range
         if (valid < kBlock || !blk_ok) {
           // Slots past the sequence end (or of a rejected block id) may hold
           // anything, NaN included: zero their V so that 0-weight * V stays 0.
@@ -523,6 +540,45 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeParams p) {
 
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+
+  if constexpr (NW > 1) {
+    // Merge the waves' softmax states (fixed order: wave 0, 1, ..., NW-1).
+    __shared__ float sm_m[NW][16], sm_l[NW][16];
+    __shared__ float sm_o[NW - 1][16][D + 4];
+    if (grp == 0) {
+      sm_m[wave][row] = m;
+      sm_l[wave][row] = l;
+    }
+    __syncthreads();
+    float big_m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) big_m = fmaxf(big_m, sm_m[w][row]);
+    float big_l = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = sm_m[w][row];
+      big_l += (mw == -INFINITY ? 0.f : exp2f(mw - big_m)) * sm_l[w][row];
+    }
+    const float own = m == -INFINITY ? 0.f : exp2f(m - big_m);
+    if (wave > 0) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        *reinterpret_cast<f32x4_t*>(&sm_o[wave - 1][row][16 * n + 4 * grp]) = acc[n] * own;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      f32x4_t a = acc[n] * own;
+#pragma unroll
+      for (int w = 1; w < NW; ++w)
+        a += *reinterpret_cast<const f32x4_t*>(&sm_o[w - 1][row][16 * n + 4 * grp]);
+      acc[n] = a;
+    }
+    m = big_m;
+    l = big_l;
+  }
+
   if (!head_ok) return;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -649,8 +705,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge: one wave per (sequence with several ranges, query head); partial
-// states combined in ascending range order:
+// Merge: one wave per (sequence split over several workgroups, query head);
+// partial states combined in ascending range order:
 //   M = max m_i, L = sum 2^(m_i - M) l_i, out = sum 2^(m_i - M) o_i / L,
 //   lse = (M + log2 L) * ln 2.
 // ---------------------------------------------------------------------------
@@ -688,14 +744,20 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const MergeSeq* merges
 // ---------------------------------------------------------------------------
 // Bandwidth probe
 // ---------------------------------------------------------------------------
-typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
-
 __global__ __launch_bounds__(256) void bw_probe_kernel(const u32x4_t* src, size_t n16,
                                                        u32x4_t* sink) {
   u32x4_t a = {0u, 0u, 0u, 0u};
   const size_t stride = size_t(gridDim.x) * blockDim.x;
-  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
-    a ^= __builtin_nontemporal_load(src + i);
+  size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  // four independent 16-byte loads in flight per lane
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4_t v0 = __builtin_nontemporal_load(src + i);
+    const u32x4_t v1 = __builtin_nontemporal_load(src + i + stride);
+    const u32x4_t v2 = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u32x4_t v3 = __builtin_nontemporal_load(src + i + 3 * stride);
+    a ^= (v0 ^ v1) ^ (v2 ^ v3);
+  }
+  for (; i < n16; i += stride) a ^= __builtin_nontemporal_load(src + i);
   if (a.x == 0x12345678u && a.y == 0x9abcdef0u) sink[0] = a;
 }
 
@@ -799,31 +861,49 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
   hipError_t e = hipSuccess;
   if (a.n_items > 0) {
     dim3 grid(a.n_items, pool.n_kv_heads);
-    dim3 block(64);
+    // variant: 0 automatic, 1 generic VALU kernel, 10 + k MFMA kernel with a
+    // prefetch depth of k blocks (k = 1..4).
     const bool mfma = kernel_variant != 1 && pool.dtype != PKV_F32 && p.group <= 16;
+    // One block in flight per wave measured fastest with 8 waves per workgroup.
+    const int depth = kernel_variant >= 11 && kernel_variant <= 14 ? kernel_variant - 10 : 1;
+    const int nw = a.waves;
     bool launched = false;
-#define PKV_DEC_MFMA(DT, DD) \
-    if (!launched && mfma && pool.dtype == DT && pool.head_dim == DD) { e = launch(decode_mfma_kernel<DT, DD, 2>, grid, block, stream, p); launched = true; }
-#define PKV_DEC_VALU(DT, DD) \
-    if (!launched && pool.dtype == DT && pool.head_dim == DD) { e = launch(decode_valu_kernel<DT, DD>, grid, block, stream, p); launched = true; }
-    PKV_DEC_MFMA(PKV_BF16, 64) PKV_DEC_MFMA(PKV_BF16, 128) PKV_DEC_MFMA(PKV_F16, 64)
-    PKV_DEC_MFMA(PKV_F16, 128)
+#define PKV_DEC_MFMA(DT, DD, DEP, W)                                                         \
+    if (!launched && mfma && pool.dtype == DT && pool.head_dim == DD && depth == DEP &&      \
+        nw == W) {                                                                           \
+      e = launch(decode_mfma_kernel<DT, DD, DEP, W>, grid, dim3(64 * W), stream, p);         \
+      launched = true;                                                                       \
+    }
+#define PKV_DEC_MFMA_W(DT, DD, DEP) \
+    PKV_DEC_MFMA(DT, DD, DEP, 1) PKV_DEC_MFMA(DT, DD, DEP, 2) PKV_DEC_MFMA(DT, DD, DEP, 4) \
+    PKV_DEC_MFMA(DT, DD, DEP, 8)
+#define PKV_DEC_MFMA_ALL(DT, DD) \
+    PKV_DEC_MFMA_W(DT, DD, 1) PKV_DEC_MFMA_W(DT, DD, 2) PKV_DEC_MFMA_W(DT, DD, 3) \
+    PKV_DEC_MFMA_W(DT, DD, 4)
+#define PKV_DEC_VALU(DT, DD)                                                                 \
+    if (!launched && pool.dtype == DT && pool.head_dim == DD) {                              \
+      e = launch(decode_valu_kernel<DT, DD>, grid, dim3(64), stream, p);                     \
+      launched = true;                                                                       \
+    }
+    PKV_DEC_MFMA_ALL(PKV_BF16, 64) PKV_DEC_MFMA_ALL(PKV_BF16, 128)
+    PKV_DEC_MFMA_ALL(PKV_F16, 64) PKV_DEC_MFMA_ALL(PKV_F16, 128)
     PKV_DEC_VALU(PKV_F32, 64) PKV_DEC_VALU(PKV_F32, 128) PKV_DEC_VALU(PKV_BF16, 64)
     PKV_DEC_VALU(PKV_BF16, 128) PKV_DEC_VALU(PKV_F16, 64) PKV_DEC_VALU(PKV_F16, 128)
 #undef PKV_DEC_MFMA
+#undef PKV_DEC_MFMA_W
+#undef PKV_DEC_MFMA_ALL
 #undef PKV_DEC_VALU
     if (!launched) return hipErrorInvalidValue;
     if (e != hipSuccess) return e;
   }
   if (a.n_merges > 0) {
     dim3 grid(a.n_merges, a.n_q_heads);
-    dim3 block(64);
     if (pool.head_dim == 64)
-      hipLaunchKernelGGL(decode_merge_kernel<64>, grid, block, 0, stream, a.merges, a.part_o,
+      hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(64), 0, stream, a.merges, a.part_o,
                          a.part_ml, a.out, a.lse, a.n_q_heads);
     else
-      hipLaunchKernelGGL(decode_merge_kernel<128>, grid, block, 0, stream, a.merges, a.part_o,
-                         a.part_ml, a.out, a.lse, a.n_q_heads);
+      hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(64), 0, stream, a.merges,
+                         a.part_o, a.part_ml, a.out, a.lse, a.n_q_heads);
     e = hipGetLastError();
   }
   return e;
@@ -831,7 +911,7 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
 
 hipError_t launch_bw_probe(const void* src, size_t n_bytes, void* sink, hipStream_t stream) {
   const size_t n16 = n_bytes / 16;
-  const int blocks = 256 * 16;
+  const int blocks = 256 * 8;
   hipLaunchKernelGGL(bw_probe_kernel, dim3(blocks), dim3(256), 0, stream,
                      static_cast<const u32x4_t*>(src), n16, static_cast<u32x4_t*>(sink));
   return hipGetLastError();

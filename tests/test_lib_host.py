@@ -138,14 +138,16 @@ def test_seeded_free_list_matches_oracle_at_workload_size():
 def test_decode_plan_splits():
     lens = [37, 100, 0, 5000, 16, 17]
     plan = pkv.pkv_decode_plan_create(lens, 4, 2, 64, 32)
-    # ceil(len / 32) ranges per sequence
-    assert pkv.pkv_decode_plan_items(plan) == sum(-(-x // 32) for x in lens)
+    # ceil(len / 32) ranges per sequence; an empty sequence is one empty item
+    assert pkv.pkv_decode_plan_items(plan) == sum(max(1, -(-x // 32)) for x in lens)
+    assert pkv.pkv_decode_plan_waves(plan) in (1, 2, 4, 8)
     assert pkv.pkv_decode_plan_part_tokens(plan) == 32
     assert pkv.pkv_decode_workspace_bytes(plan) % 256 == 0
     pkv.pkv_decode_plan_destroy(plan)
     plan = pkv.pkv_decode_plan_create([8192] * 32, 64, 8, 128, 0)
-    assert pkv.pkv_decode_plan_part_tokens(plan) == 1024       # ~2048 workgroups
-    assert pkv.pkv_decode_plan_items(plan) == 32 * 8
+    # 32 x 8 (sequence, KV head) pairs of 512 blocks: one 8-wave workgroup each
+    assert pkv.pkv_decode_plan_waves(plan) == 8
+    assert pkv.pkv_decode_plan_items(plan) == 32
     pkv.pkv_decode_plan_destroy(plan)
     for bad in [dict(part=8), dict(hq=6, hkv=4), dict(d=96)]:
         with pytest.raises(pkv.PkvError):
