@@ -269,6 +269,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--inject-reps", type=int, default=10)
     ap.add_argument("--no-inject", action="store_true")
+    ap.add_argument("--inject-only", action="store_true",
+                    help="time only the injection workload (no JSON line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-workload", default="70b", choices=["70b", "8b", "ragged"],
                     help="decode workload timed (the reported line uses 70b)")
@@ -283,6 +285,9 @@ def main():
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
     log("device:", props.name, getattr(props, "gcnArchName", "?"), "%d CUs" % props.multi_processor_count)
+    if args.inject_only:
+        run_inject(args.inject_reps)
+        return
     probe = bw_probe()
     log("bw probe: %.1f GB/s" % probe)
     dec, _ = run_decode(args.steps, args.warmup, args.decode_workload)

@@ -28,6 +28,9 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+
+#include <algorithm>
 
 #include "pkv_internal.h"
 
@@ -90,6 +93,11 @@ __device__ inline uint4 ld16_stream(const void* p) {
 __device__ inline uint2 ld8_stream(const void* p) {
   const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
   return make_uint2(v.x, v.y);
+}
+// Streaming store for data written once and not read back soon.
+__device__ inline void st16_stream(void* p, uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
 }
 
 // Rotate the X elements of one 16-byte chunk.  PAIRS: element e pairs with
@@ -168,85 +176,135 @@ struct InjectParams {
   int64_t s_layer, s_token;          // bytes
   const InjectDesc* descs;
   int layer_begin;
+  int layer_end;
+  int layers_per_wg;
   int rope_mode;
   const float* cos_t;
   const float* sin_t;
 };
 
 constexpr int kInjectThreads = 256;
-// Heads staged per pass: V tiles of up to 32 KiB of LDS.
-constexpr int inject_heads_per_pass(int d, int e) { return 2048 / (d * e) < 8 ? 2048 / (d * e) : 8; }
 
+// Rotation of one chunk pair using cos/sin rows staged in LDS (row t of the
+// block: cs[t][0..D/2) = cos, cs[t][D/2..D) = sin).
 template <int DT, int D>
+__device__ inline void rotate_chunk_pair_lds(uint4& lo, uint4& hi, int c0, int mode,
+                                             const float* row) {
+  constexpr int X = 16 / Fmt<DT>::kBytes;
+  constexpr int C = D / X;
+  if (mode == PKV_ROPE_NONE) return;
+  if (mode == PKV_ROPE_PAIRS) {
+    rotate_pairs<DT>(lo, c0 * X, row, row + D / 2);
+    rotate_pairs<DT>(hi, (c0 + C / 2) * X, row, row + D / 2);
+  } else {
+    rotate_halves<DT>(lo, hi, c0 * X, row, row + D / 2);
+  }
+}
+
+// One workgroup per (destination block, group of layers).  The block's 16
+// rotary rows are staged in LDS once; then for every layer and group of HG
+// KV heads: each (token, chunk pair) unit reads its two 16-byte K and V
+// chunks of the source row, rotates K and stores it into the K plane; V goes
+// through LDS to be written dimension-major.
+template <int DT, int D, int HG>
 __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParams p) {
   typedef typename Fmt<DT>::T T;
   constexpr int E = Fmt<DT>::kBytes;
-  constexpr int X = 16 / E;          // elements per 16-byte chunk
-  constexpr int C = D / X;           // chunks per token row
-  constexpr int UNITS = kBlock * (C / 2);   // (token, chunk pair) units per head
-  constexpr int VPIECES = D * (kBlock / X); // 16-byte pieces of a V plane
-  constexpr int HG = inject_heads_per_pass(D, E);
+  constexpr int X = 16 / E;
+  constexpr int C = D / X;
+  constexpr int UNITS = kBlock * (C / 2);
+  constexpr int VPIECES = D * (kBlock / X);
+  constexpr int UPT = (HG * UNITS + kInjectThreads - 1) / kInjectThreads;
+  constexpr int VPT = (HG * VPIECES + kInjectThreads - 1) / kInjectThreads;
   __shared__ T vtile[HG][kBlock][D];
+  __shared__ float cs[kBlock][D];
   __shared__ InjectDesc desc;
 
-  const int layer = p.layer_begin + blockIdx.y;
   if (threadIdx.x < sizeof(InjectDesc) / 4)
     reinterpret_cast<int32_t*>(&desc)[threadIdx.x] =
         reinterpret_cast<const int32_t*>(&p.descs[blockIdx.x])[threadIdx.x];
   __syncthreads();
+  if (p.rope_mode != PKV_ROPE_NONE) {
+    for (int w = threadIdx.x; w < kBlock * (D / 2); w += kInjectThreads) {
+      const int t = w / (D / 2), i = w - t * (D / 2);
+      if (desc.src[t] < 0) continue;
+      const size_t at = size_t(desc.pos_base + t) * (D / 2) + i;
+      cs[t][i] = p.cos_t[at];
+      cs[t][D / 2 + i] = p.sin_t[at];
+    }
+  }
   bool full = true;
 #pragma unroll
   for (int t = 0; t < kBlock; ++t) full &= desc.src[t] >= 0;
+  __syncthreads();
 
-  char* kplane0 = p.pool_k + layer * p.p_layer + int64_t(desc.phys_block) * p.p_block;
-  char* vplane0 = p.pool_v + layer * p.p_layer + int64_t(desc.phys_block) * p.p_block;
-  const char* sk = p.src_k + layer * p.s_layer;
-  const char* sv = p.src_v + layer * p.s_layer;
-
-  for (int h0 = 0; h0 < p.n_kv_heads; h0 += HG) {
-    const int nh = min(HG, p.n_kv_heads - h0);
-    // Phase A: read each token's chunk pair, rotate K and store it; stage V.
-    for (int w = threadIdx.x; w < nh * UNITS; w += kInjectThreads) {
-      const int hl = w / UNITS;
-      const int r = w - hl * UNITS;
-      const int t = r % kBlock;
-      const int c0 = r / kBlock;
-      const int src = desc.src[t];
-      if (src < 0) continue;
-      const int h = h0 + hl;
-      const int64_t row = int64_t(src) * p.s_token + int64_t(h) * D * E;
-      uint4 k0 = ld16(sk + row + c0 * 16);
-      uint4 k1 = ld16(sk + row + (c0 + C / 2) * 16);
-      const uint4 v0 = ld16(sv + row + c0 * 16);
-      const uint4 v1 = ld16(sv + row + (c0 + C / 2) * 16);
-      rotate_chunk_pair<DT, D>(k0, k1, c0, desc.pos_base + t, p.rope_mode, p.cos_t, p.sin_t);
-      char* kplane = kplane0 + int64_t(h) * p.p_head;
-      st16(kplane + (c0 * kBlock + t) * 16, k0);
-      st16(kplane + ((c0 + C / 2) * kBlock + t) * 16, k1);
-      *reinterpret_cast<uint4*>(&vtile[hl][t][c0 * X]) = v0;
-      *reinterpret_cast<uint4*>(&vtile[hl][t][(c0 + C / 2) * X]) = v1;
-    }
-    __syncthreads();
-    // Phase B: write V planes dimension-major, X tokens per 16-byte piece.
-    for (int w = threadIdx.x; w < nh * VPIECES; w += kInjectThreads) {
-      const int hl = w / VPIECES;
-      const int r = w - hl * VPIECES;
-      const int j = r / (kBlock / X);
-      const int t0 = (r % (kBlock / X)) * X;
-      char* dst = vplane0 + int64_t(h0 + hl) * p.p_head + (int64_t(j) * kBlock + t0) * E;
-      T out[X];
-      bool need_old = false;
-      if (!full) {
+  const int l0 = p.layer_begin + blockIdx.y * p.layers_per_wg;
+  const int l1 = min(l0 + p.layers_per_wg, p.layer_end);
+  for (int layer = l0; layer < l1; ++layer) {
+    char* kplane0 = p.pool_k + layer * p.p_layer + int64_t(desc.phys_block) * p.p_block;
+    char* vplane0 = p.pool_v + layer * p.p_layer + int64_t(desc.phys_block) * p.p_block;
+    const char* sk = p.src_k + layer * p.s_layer;
+    const char* sv = p.src_v + layer * p.s_layer;
+    for (int h0 = 0; h0 < p.n_kv_heads; h0 += HG) {
+      const int nh = min(HG, p.n_kv_heads - h0);
+      uint4 k0[UPT], k1[UPT], v0[UPT], v1[UPT];
 #pragma unroll
-        for (int e = 0; e < X; ++e) need_old |= desc.src[t0 + e] < 0;
+      for (int u = 0; u < UPT; ++u) {
+        const int w = threadIdx.x + u * kInjectThreads;
+        const int hl = w / UNITS;
+        const int r = w - hl * UNITS;
+        const int t = r % kBlock;
+        const int c0 = r / kBlock;
+        const int src = (w < nh * UNITS) ? desc.src[t] : -1;
+        if (src >= 0) {
+          const int64_t row = int64_t(src) * p.s_token + int64_t(h0 + hl) * D * E;
+          k0[u] = ld16_stream(sk + row + c0 * 16);
+          k1[u] = ld16_stream(sk + row + (c0 + C / 2) * 16);
+          v0[u] = ld16_stream(sv + row + c0 * 16);
+          v1[u] = ld16_stream(sv + row + (c0 + C / 2) * 16);
+        }
       }
-      if (need_old) *reinterpret_cast<uint4*>(out) = ld16(dst);
 #pragma unroll
-      for (int e = 0; e < X; ++e)
-        if (desc.src[t0 + e] >= 0) out[e] = vtile[hl][t0 + e][j];
-      st16(dst, *reinterpret_cast<uint4*>(out));
+      for (int u = 0; u < UPT; ++u) {
+        const int w = threadIdx.x + u * kInjectThreads;
+        const int hl = w / UNITS;
+        const int r = w - hl * UNITS;
+        const int t = r % kBlock;
+        const int c0 = r / kBlock;
+        if (w >= nh * UNITS || desc.src[t] < 0) continue;
+        rotate_chunk_pair_lds<DT, D>(k0[u], k1[u], c0, p.rope_mode, cs[t]);
+        char* kplane = kplane0 + int64_t(h0 + hl) * p.p_head;
+        st16_stream(kplane + (c0 * kBlock + t) * 16, k0[u]);
+        st16_stream(kplane + ((c0 + C / 2) * kBlock + t) * 16, k1[u]);
+        *reinterpret_cast<uint4*>(&vtile[hl][t][c0 * X]) = v0[u];
+        *reinterpret_cast<uint4*>(&vtile[hl][t][(c0 + C / 2) * X]) = v1[u];
+      }
+      __syncthreads();
+      // V planes dimension-major, X tokens per 16-byte piece; a piece with
+      // slots this call does not write keeps their old contents.
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        const int w = threadIdx.x + u * kInjectThreads;
+        if (w >= nh * VPIECES) break;
+        const int hl = w / VPIECES;
+        const int r = w - hl * VPIECES;
+        const int j = r / (kBlock / X);
+        const int t0 = (r % (kBlock / X)) * X;
+        char* dst = vplane0 + int64_t(h0 + hl) * p.p_head + (int64_t(j) * kBlock + t0) * E;
+        T out[X];
+        bool need_old = false;
+        if (!full) {
+#pragma unroll
+          for (int e = 0; e < X; ++e) need_old |= desc.src[t0 + e] < 0;
+        }
+        if (need_old) *reinterpret_cast<uint4*>(out) = ld16(dst);
+#pragma unroll
+        for (int e = 0; e < X; ++e)
+          if (desc.src[t0 + e] >= 0) out[e] = vtile[hl][t0 + e][j];
+        st16_stream(dst, *reinterpret_cast<uint4*>(out));
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
@@ -749,14 +807,6 @@ __global__ __launch_bounds__(256) void bw_probe_kernel(const u32x4_t* src, size_
   u32x4_t a = {0u, 0u, 0u, 0u};
   const size_t stride = size_t(gridDim.x) * blockDim.x;
   size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  // four independent 16-byte loads in flight per lane
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4_t v0 = __builtin_nontemporal_load(src + i);
-    const u32x4_t v1 = __builtin_nontemporal_load(src + i + stride);
-    const u32x4_t v2 = __builtin_nontemporal_load(src + i + 2 * stride);
-    const u32x4_t v3 = __builtin_nontemporal_load(src + i + 3 * stride);
-    a ^= (v0 ^ v1) ^ (v2 ^ v3);
-  }
   for (; i < n16; i += stride) a ^= __builtin_nontemporal_load(src + i);
   if (a.x == 0x12345678u && a.y == 0x9abcdef0u) sink[0] = a;
 }
@@ -789,16 +839,32 @@ hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, const InjectD
   p.s_token = src.token_stride * eb;
   p.descs = d_desc;
   p.layer_begin = layer_begin;
+  p.layer_end = layer_end;
   p.rope_mode = rope_mode;
   p.cos_t = d_cos;
   p.sin_t = d_sin;
-  dim3 grid(n_desc, layer_end - layer_begin);
+  // Each workgroup walks a few layers of one block, reusing its staged
+  // rotary rows; ~50k workgroups measured best on the top-8 injection.
+  const int n_layers = layer_end - layer_begin;
+  int lpw = int(std::min<int64_t>(n_layers, std::max<int64_t>(1, int64_t(n_layers) * n_desc / 49152)));
+  if (const char* env = std::getenv("PKV_INJECT_LAYERS_PER_WG")) {
+    const int v = std::atoi(env);
+    if (v > 0) lpw = std::min(v, n_layers);
+  }
+  p.layers_per_wg = lpw;
+  dim3 grid(n_desc, (n_layers + lpw - 1) / lpw);
   dim3 block(kInjectThreads);
-#define PKV_INJ(DT, DD) \
-  if (pool.dtype == DT && pool.head_dim == DD) return launch(inject_rope_kernel<DT, DD>, grid, block, stream, p);
-  PKV_INJ(PKV_F32, 64) PKV_INJ(PKV_F32, 128) PKV_INJ(PKV_BF16, 64) PKV_INJ(PKV_BF16, 128)
-  PKV_INJ(PKV_F16, 64) PKV_INJ(PKV_F16, 128)
+  // KV heads per pass: V tiles of 16 KiB (4 heads of d=128 bf16) by default.
+  int hg = 4;
+  if (const char* env = std::getenv("PKV_INJECT_HEADS")) hg = std::atoi(env) == 8 ? 8 : 4;
+#define PKV_INJ(DT, DD, H) \
+  if (pool.dtype == DT && pool.head_dim == DD && hg == H) \
+    return launch(inject_rope_kernel<DT, DD, H>, grid, block, stream, p);
+#define PKV_INJ_H(DT, DD) PKV_INJ(DT, DD, 4) PKV_INJ(DT, DD, 8)
+  PKV_INJ_H(PKV_F32, 64) PKV_INJ_H(PKV_F32, 128) PKV_INJ_H(PKV_BF16, 64)
+  PKV_INJ_H(PKV_BF16, 128) PKV_INJ_H(PKV_F16, 64) PKV_INJ_H(PKV_F16, 128)
 #undef PKV_INJ
+#undef PKV_INJ_H
   return hipErrorInvalidValue;
 }
 
@@ -911,7 +977,7 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
 
 hipError_t launch_bw_probe(const void* src, size_t n_bytes, void* sink, hipStream_t stream) {
   const size_t n16 = n_bytes / 16;
-  const int blocks = 256 * 8;
+  const int blocks = 2048;  // measured best for a streaming read on 256 CUs
   hipLaunchKernelGGL(bw_probe_kernel, dim3(blocks), dim3(256), 0, stream,
                      static_cast<const u32x4_t*>(src), n16, static_cast<u32x4_t*>(sink));
   return hipGetLastError();
