@@ -35,6 +35,23 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def recorded_traffic(kernel="decode_mfma_kernel"):
+    """HBM bytes per launch of `kernel` from the rocprofv3 counter summary in
+    profiles/, if it was taken on the current kernel sources (else None)."""
+    import glob
+    import hashlib
+    src = os.path.join(ROOT, "paged_kv_cache_inject_amd", "csrc", "pkv_kernels.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            if not line.startswith("traffic-record:"):
+                continue
+            fields = dict(kv.split("=", 1) for kv in line.split()[1:])
+            if fields.get("kernel") == kernel and fields.get("sources_sha256") == sha:
+                return int(fields["bytes_per_launch"])
+    return None
+
+
 POOL_LAYOUT = os.environ.get("PKV_BENCH_LAYOUT", "block")
 
 
@@ -313,7 +330,8 @@ def main():
                    "pool_layout": POOL_LAYOUT},
         "roofline": {"bound": "hbm", "achieved": round(dec["launch_gbps"], 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(dec["launch_gbps"] / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(dec["launch_gbps"] / PEAK_HBM_GBPS, 4),
+                     "traffic": recorded_traffic(),
                      "kernel": "decode_mfma_kernel (pkv_decode_attention, one layer)",
                      "bytes_per_launch": dec["bytes_per_launch"],
                      "launch_us_avg": round(dec["launch_ms_avg"] * 1e3, 2)},
