@@ -120,12 +120,13 @@ def decode_workload(name):
     raise ValueError(name)
 
 
-def run_decode(steps, warmup, workload="70b"):
+def run_decode(steps, warmup, workload="70b", launch_steps=None):
     import torch
     import paged_kv_cache_inject_amd as pkv
     from workloads.configs import host_normal
     cfg, st = decode_workload(workload)
     lens = st["lens"]
+    launch_steps = steps if launch_steps is None else launch_steps
     log("decode: allocating and filling %d layers x %d blocks" % (cfg.n_layers, st["num_blocks"]))
     buf, pool = device_pool(cfg.n_layers, st["num_blocks"], cfg.n_kv_heads, cfg.head_dim,
                             cfg.dtype, cfg.seed)
@@ -155,26 +156,39 @@ def run_decode(steps, warmup, workload="70b"):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(cfg.n_layers)]
-          for _ in range(steps)]
     t_s, t_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Timed region: exactly `steps` steps, no markers between the launches.
     log("decode: %d timed steps" % steps)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_s.record()
-    for k in range(steps):
-        step(ev[k])
+    for _ in range(steps):
+        step()
     t_e.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total_ms = t_s.elapsed_time(t_e)
-    launch_ms = [ev[k][l][0].elapsed_time(ev[k][l][1]) for k in range(steps)
+    # Instrumented pass: the same number of steps again, with a HIP event
+    # pair around every launch on the stream the kernels run on, for the
+    # per-launch kernel duration (the markers themselves add a few us per
+    # launch, which is why they stay out of the timed region).
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(cfg.n_layers)]
+          for _ in range(launch_steps)]
+    i_s, i_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    i_s.record()
+    for k in range(launch_steps):
+        step(ev[k])
+    i_e.record()
+    torch.cuda.synchronize()
+    launch_ms = [ev[k][l][0].elapsed_time(ev[k][l][1]) for k in range(launch_steps)
                  for l in range(cfg.n_layers)]
     per_launch = decode_bytes(lens, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads, 2)
     ms_step = total_ms / steps
     res = dict(ms_per_step=ms_step, wall_ms_per_step=wall * 1e3 / steps,
+               instrumented_ms_per_step=i_s.elapsed_time(i_e) / max(1, launch_steps),
                bytes_per_step=per_launch * cfg.n_layers, bytes_per_launch=per_launch,
                launch_ms_avg=float(np.mean(launch_ms)), launch_ms_p50=float(np.median(launch_ms)),
+               launches_timed=len(launch_ms),
                n_items=n_items, part_tokens=part_tokens, waves=waves, workload=cfg.workload,
                batch=cfg.batch, context=int(lens.max()), layers=cfg.n_layers)
     res["value"] = res["bytes_per_step"] / (ms_step * 1e-3) / 1e9
@@ -334,7 +348,11 @@ def main():
                      "traffic": recorded_traffic(),
                      "kernel": "decode_mfma_kernel (pkv_decode_attention, one layer)",
                      "bytes_per_launch": dec["bytes_per_launch"],
-                     "launch_us_avg": round(dec["launch_ms_avg"] * 1e3, 2)},
+                     "launch_us_avg": round(dec["launch_ms_avg"] * 1e3, 2),
+                     "launch_timing": "HIP events around each of %d launches in an instrumented "
+                                      "pass of %d steps after the timed steps (%.3f ms/step)"
+                                      % (dec["launches_timed"], dec["launches_timed"] // dec["layers"],
+                                         dec["instrumented_ms_per_step"])},
         "bw_probe_gbps": round(probe, 1),
         "cpu_baseline": cpu,
     }
