@@ -16,6 +16,8 @@ Readings taken:
   rotated to its own position;
 * scale = 1/sqrt(d); everything is evaluated in float64 from the exactly
   widened stored values;
+* an fp8 cache holds codes whose values are e4m3(code) times the float32
+  scale of their (layer, KV head); the query then comes in a 16-bit format;
 * besides ``out`` the log-sum-exp ``lse = m + ln(sum exp(s - m))`` of the
   scaled scores is returned; a sequence of length 0 gives out = 0 and
   lse = -inf.
@@ -70,14 +72,15 @@ def decode_contiguous(q, k_seqs, v_seqs, dtype: str, n_q_heads: int, scale=None)
 
 
 def decode_paged(q, k_pool, v_pool, spec: PoolSpec, layer: int, tables, lens,
-                 n_q_heads: int, scale=None, seqs=None, heads=None, by_plane=False):
+                 n_q_heads: int, scale=None, seqs=None, heads=None, by_plane=False,
+                 q_dtype=None, k_scale=None, v_scale=None):
     """Decode attention reading K/V through the block tables.
 
     ``seqs`` / ``heads`` restrict which (sequence, query head) outputs are
     computed (sampling at large sizes); the rest stay 0 / -inf.  ``by_plane``
     gathers a whole plane at a time (same values, faster).
     """
-    q64 = to_f64(q, spec.dtype)
+    q64 = to_f64(q, spec.dtype if q_dtype is None else q_dtype)
     b_n, hq, d = q64.shape
     g = hq // spec.n_kv_heads
     sc = 1.0 / math.sqrt(d) if scale is None else scale
@@ -91,6 +94,11 @@ def decode_paged(q, k_pool, v_pool, spec: PoolSpec, layer: int, tables, lens,
         k_raw, v_raw = gather(k_pool, v_pool, spec, layer, tables[b], int(lens[b]), heads=kv_heads)
         k64 = to_f64(k_raw, spec.dtype)
         v64 = to_f64(v_raw, spec.dtype)
+        if spec.dtype == "fp8":
+            ks = np.array([float(k_scale[layer][h]) for h in kv_heads])
+            vs = np.array([float(v_scale[layer][h]) for h in kv_heads])
+            k64 = k64 * ks[None, :, None]
+            v64 = v64 * vs[None, :, None]
         for h in qh:
             i = kv_heads.index(h // g)
             if lens[b] == 0:

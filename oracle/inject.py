@@ -16,7 +16,11 @@ Readings taken where the pages are silent:
   overwritten;
 * after the call the sequence's length is max(old length, dst_pos + n);
 * the key is rotated to its destination position (rope.rotate_f32) and
-  rounded to the cache format; the value is copied bit for bit;
+  rounded to the cache format; the value is copied bit for bit when the
+  source and the cache share a format;
+* a quantised (fp8) cache stores code = e4m3(f32(x / scale)) with one
+  float32 scale per (layer, KV head) for K and one for V (the key after its
+  rotation, the value as given), the division a single float32 division;
 * append writes T tokens per sequence at positions len-T .. len-1 of the
   already-extended lengths, rotated the same way (mode "none" stores keys as
   given).
@@ -29,7 +33,7 @@ contiguous.
 import numpy as np
 
 from .layout import BLOCK_TOKENS, PoolSpec, k_element_offsets, v_element_offsets, slot
-from .numerics import from_f32, to_f32
+from .numerics import from_f32, to_f32, f32_to_e4m3_rne_sat
 from .rope import rotate_f32
 
 
@@ -62,25 +66,40 @@ def validate_runs(tables, lens, runs, max_pos: int):
     return writes
 
 
+def _store(x32, dtype, scale):
+    """float32 values -> stored codes of the cache format (fp8: x / scale)."""
+    if dtype == "fp8":
+        return f32_to_e4m3_rne_sat(np.divide(x32, np.float32(scale), dtype=np.float32))
+    return from_f32(x32, dtype)
+
+
 def write_token(k_pool, v_pool, spec: PoolSpec, layer: int, table_row, pos: int,
-                k_raw, v_raw, mode: str, cos_t, sin_t):
+                k_raw, v_raw, mode: str, cos_t, sin_t, src_dtype=None, k_scale=None,
+                v_scale=None):
     """Store one token (all KV heads) of one layer at position ``pos``.
 
-    k_raw, v_raw: [n_kv_heads][d] in the cache's storage format.
+    k_raw, v_raw: [n_kv_heads][d] in ``src_dtype`` (default: the cache's).
+    k_scale, v_scale: [n_layers][n_kv_heads] float32 (fp8 caches only).
     """
+    src_dtype = spec.dtype if src_dtype is None else src_dtype
     s = slot(table_row, pos)
     blk, t = divmod(s, BLOCK_TOKENS)
-    k32 = to_f32(k_raw, spec.dtype)
+    k32 = to_f32(k_raw, src_dtype)
     k_rot = rotate_f32(k32, np.full(k32.shape[:-1], pos), cos_t, sin_t, mode)
-    k_store = from_f32(k_rot, spec.dtype)
     for h in range(spec.n_kv_heads):
-        k_pool[k_element_offsets(spec, layer, blk, h, t)] = k_store[h]
-        v_pool[v_element_offsets(spec, layer, blk, h, t)] = v_raw[h]
+        ks = None if k_scale is None else k_scale[layer][h]
+        vs = None if v_scale is None else v_scale[layer][h]
+        k_pool[k_element_offsets(spec, layer, blk, h, t)] = _store(k_rot[h], spec.dtype, ks)
+        if src_dtype == spec.dtype:
+            v_pool[v_element_offsets(spec, layer, blk, h, t)] = v_raw[h]
+        else:
+            v_pool[v_element_offsets(spec, layer, blk, h, t)] = _store(
+                to_f32(v_raw[h], src_dtype), spec.dtype, vs)
 
 
 def inject(k_pool, v_pool, spec: PoolSpec, tables, lens, runs, src_k, src_v,
            src_layer_stride: int, src_token_stride: int, layer_begin: int, layer_end: int,
-           mode: str, cos_t, sin_t):
+           mode: str, cos_t, sin_t, src_dtype=None, k_scale=None, v_scale=None):
     """Scatter runs of stored, unrotated K/V into the pool; returns new lens."""
     max_pos = cos_t.shape[0]
     if not (0 <= layer_begin <= layer_end <= spec.n_layers):
@@ -93,7 +112,7 @@ def inject(k_pool, v_pool, spec: PoolSpec, tables, lens, runs, src_k, src_v,
             k_raw = src_k[base:base + hd].reshape(spec.n_kv_heads, spec.head_dim)
             v_raw = src_v[base:base + hd].reshape(spec.n_kv_heads, spec.head_dim)
             write_token(k_pool, v_pool, spec, layer, tables[seq], pos, k_raw, v_raw,
-                        mode, cos_t, sin_t)
+                        mode, cos_t, sin_t, src_dtype, k_scale, v_scale)
     new_lens = list(lens)
     for (seq, n, p0, _src) in runs:
         new_lens[seq] = max(new_lens[seq], p0 + n)
@@ -101,7 +120,7 @@ def inject(k_pool, v_pool, spec: PoolSpec, tables, lens, runs, src_k, src_v,
 
 
 def append(k_pool, v_pool, spec: PoolSpec, layer: int, tables, lens_after, seqs, n_new: int,
-           k_new, v_new, mode: str, cos_t, sin_t):
+           k_new, v_new, mode: str, cos_t, sin_t, src_dtype=None, k_scale=None, v_scale=None):
     """Write n_new tokens per sequence at its last n_new positions.
 
     k_new, v_new: raw arrays [len(seqs)][n_new][n_kv_heads][d].
@@ -110,4 +129,5 @@ def append(k_pool, v_pool, spec: PoolSpec, layer: int, tables, lens_after, seqs,
         first = lens_after[seq] - n_new
         for t in range(n_new):
             write_token(k_pool, v_pool, spec, layer, tables[seq], first + t,
-                        k_new[i, t], v_new[i, t], mode, cos_t, sin_t)
+                        k_new[i, t], v_new[i, t], mode, cos_t, sin_t, src_dtype, k_scale,
+                        v_scale)

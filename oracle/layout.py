@@ -89,7 +89,7 @@ class PoolSpec:
         return last + BLOCK_TOKENS * self.head_dim
 
     def storage_dtype(self):
-        return np.float32 if self.dtype == "f32" else np.uint16
+        return {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16, "fp8": np.uint8}[self.dtype]
 
 
 def k_element_offsets(spec: PoolSpec, layer: int, block: int, head: int, t: int) -> np.ndarray:

@@ -12,8 +12,8 @@ float32 as float32.  Widening to float64 is exact for all three.
 
 import numpy as np
 
-DTYPES = ("f32", "bf16", "f16")
-ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
+DTYPES = ("f32", "bf16", "f16", "fp8")
+ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1}
 
 
 def bf16_bits_to_f64(bits) -> np.ndarray:
@@ -28,7 +28,9 @@ def f16_bits_to_f64(bits) -> np.ndarray:
 
 
 def to_f64(raw, dtype: str) -> np.ndarray:
-    """Widen stored elements of ``dtype`` to float64 (exact)."""
+    """Widen stored elements of ``dtype`` to float64 (exact; fp8 unscaled)."""
+    if dtype == "fp8":
+        return e4m3_to_f64(raw)
     if dtype == "f32":
         return np.asarray(raw, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
@@ -101,3 +103,55 @@ def from_f32(x, dtype: str) -> np.ndarray:
     if dtype == "f16":
         return f32_to_f16_rne(x)
     raise ValueError(dtype)
+
+
+# -- fp8: OCP E4M3 (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits) --------
+# Used by the quantised cache (the int8/int4 paragraph of "Latency Optimization ›
+# KV Cache Management" motivates storing K/V in fewer bits).  Finite values
+# go up to 448; the all-ones exponent with all-ones mantissa is NaN; there
+# are no infinities.  Codes 0..0x7E are the non-negative finite values.
+
+def e4m3_to_f64(bits) -> np.ndarray:
+    """Exact value of E4M3 codes (uint8) as float64, from the field definition."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = b & 0x7
+    normal = np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    sub = np.ldexp(m / 8.0, -6)
+    val = np.where(e == 0, sub, normal)
+    nan = (e == 0xF) & (m == 0x7)
+    return np.where(nan, np.nan, sign * val)
+
+
+_E4M3_POS = None
+
+
+def _e4m3_table():
+    global _E4M3_POS
+    if _E4M3_POS is None:
+        codes = np.arange(0, 0x7F, dtype=np.uint8)        # 0 .. 0x7E: +0 .. 448
+        _E4M3_POS = (codes, e4m3_to_f64(codes))
+    return _E4M3_POS
+
+
+def f32_to_e4m3_rne_sat(x) -> np.ndarray:
+    """Round float32 values to E4M3: the nearest finite code, ties to the even
+    code, magnitudes beyond 448 saturate to 448 (reading: the saturating
+    conversion); NaN -> 0x7F with the sign.  Brute force over the 127
+    non-negative codes."""
+    x = np.asarray(x, dtype=np.float32)
+    codes, vals = _e4m3_table()
+    a = np.abs(x.astype(np.float64)).ravel()
+    i = np.clip(np.searchsorted(vals, a), 1, len(vals) - 1)
+    lo, hi = i - 1, i
+    d_lo = a - vals[lo]
+    d_hi = vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((codes[hi] & 1) == 0))
+    c = np.where(pick_hi, codes[hi], codes[lo])
+    c = np.where(a >= vals[-1], codes[-1], c)               # saturate at 448
+    c = np.where(a == 0, 0, c)
+    neg = (x.ravel() < 0) | ((x.ravel() == 0) & np.signbit(x.ravel()))
+    out = (c.astype(np.uint8) | np.where(neg, 0x80, 0).astype(np.uint8)).astype(np.uint8)
+    out = np.where(np.isnan(x.ravel()), np.where(np.signbit(x.ravel()), 0xFF, 0x7F), out)
+    return out.astype(np.uint8).reshape(x.shape)
