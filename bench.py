@@ -55,6 +55,31 @@ def recorded_traffic(kernel="decode_mfma_kernel"):
 POOL_LAYOUT = os.environ.get("PKV_BENCH_LAYOUT", "block")
 
 
+def device_pool_fp8(n_layers, num_blocks, n_kv_heads, head_dim, seed, scale=0.01):
+    """fp8 (E4M3) pool of random finite codes, [layer][block][K | V planes],
+    with one K and one V scale per (layer, KV head)."""
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    plane = 16 * head_dim
+    block_stride = 2 * n_kv_heads * plane
+    layer_stride = num_blocks * block_stride
+    buf = torch.empty(n_layers * layer_stride, dtype=torch.uint8, device="cuda")
+    g = torch.Generator(device="cuda")
+    for layer in range(n_layers):
+        g.manual_seed(seed * 1000 + layer)
+        part = buf[layer * layer_stride:(layer + 1) * layer_stride]
+        part.copy_(torch.randint(0, 0x7F, (layer_stride,), dtype=torch.uint8, device="cuda",
+                                 generator=g))
+        part |= torch.randint(0, 2, (layer_stride,), dtype=torch.uint8, device="cuda",
+                              generator=g) << 7
+    ks = torch.full((n_layers, n_kv_heads), scale, dtype=torch.float32, device="cuda")
+    vs = torch.full((n_layers, n_kv_heads), scale, dtype=torch.float32, device="cuda")
+    desc = pkv.pkv_pool(n_layers, num_blocks, n_kv_heads, head_dim, pkv.PKV_FP8E4M3, 0,
+                        buf.data_ptr(), buf.data_ptr() + n_kv_heads * plane, layer_stride,
+                        block_stride, plane, ks.data_ptr(), vs.data_ptr())
+    return (buf, ks, vs), desc
+
+
 def device_pool(n_layers, num_blocks, n_kv_heads, head_dim, dtype, seed, layout=None):
     """Pool buffer filled with N(0,1) per layer.  layout "head":
     [layer][block][head][K plane | V plane] (one (block, head) = K and V
@@ -81,9 +106,14 @@ def device_pool(n_layers, num_blocks, n_kv_heads, head_dim, dtype, seed, layout=
     return buf, desc
 
 
-def decode_bytes(lens, n_kv_heads, head_dim, n_q_heads, elem):
-    """Algorithmic bytes of one decode launch (one layer)."""
-    kv = int(np.sum(lens)) * n_kv_heads * head_dim * elem * 2
+def decode_bytes(lens, n_kv_heads, head_dim, n_q_heads, elem, kv_elem=None):
+    """Algorithmic bytes of one decode launch (one layer): every cached K/V
+    byte (kv_elem bytes per element, default elem), q, out, lse, the table
+    entries (and the two scales per KV head of a quantised pool)."""
+    kv_elem = elem if kv_elem is None else kv_elem
+    kv = int(np.sum(lens)) * n_kv_heads * head_dim * kv_elem * 2
+    if kv_elem == 1:
+        kv += 2 * n_kv_heads * 4
     q = len(lens) * n_q_heads * head_dim * elem
     out = len(lens) * n_q_heads * head_dim * 4 + len(lens) * n_q_heads * 4
     tables = int(sum(-(-int(x) // 16) for x in lens)) * 4
@@ -111,7 +141,7 @@ def bw_probe(n_bytes=8 << 30, reps=5):
 def decode_workload(name):
     from workloads.configs import (CONFIGS, llama70b_structure, llama8b_structure,
                                    ragged_mha_structure)
-    if name == "70b":
+    if name in ("70b", "70b-fp8"):
         return CONFIGS[3], llama70b_structure(CONFIGS[3])
     if name == "8b":
         return CONFIGS[2], llama8b_structure(CONFIGS[2])
@@ -127,9 +157,15 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None):
     cfg, st = decode_workload(workload)
     lens = st["lens"]
     launch_steps = steps if launch_steps is None else launch_steps
-    log("decode: allocating and filling %d layers x %d blocks" % (cfg.n_layers, st["num_blocks"]))
-    buf, pool = device_pool(cfg.n_layers, st["num_blocks"], cfg.n_kv_heads, cfg.head_dim,
-                            cfg.dtype, cfg.seed)
+    fp8 = workload.endswith("-fp8")
+    log("decode: allocating and filling %d layers x %d blocks%s"
+        % (cfg.n_layers, st["num_blocks"], " (fp8)" if fp8 else ""))
+    if fp8:
+        buf, pool = device_pool_fp8(cfg.n_layers, st["num_blocks"], cfg.n_kv_heads,
+                                    cfg.head_dim, cfg.seed)
+    else:
+        buf, pool = device_pool(cfg.n_layers, st["num_blocks"], cfg.n_kv_heads, cfg.head_dim,
+                                cfg.dtype, cfg.seed)
     q_host = host_normal(st["rng"], (cfg.batch, cfg.n_q_heads, cfg.head_dim), cfg.dtype)
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[cfg.dtype]
     q = torch.from_numpy(q_host.view(np.int16)).cuda().view(tdt)
@@ -182,7 +218,8 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None):
     torch.cuda.synchronize()
     launch_ms = [ev[k][l][0].elapsed_time(ev[k][l][1]) for k in range(launch_steps)
                  for l in range(cfg.n_layers)]
-    per_launch = decode_bytes(lens, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads, 2)
+    per_launch = decode_bytes(lens, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads, 2,
+                              kv_elem=1 if fp8 else 2)
     ms_step = total_ms / steps
     res = dict(ms_per_step=ms_step, wall_ms_per_step=wall * 1e3 / steps,
                instrumented_ms_per_step=i_s.elapsed_time(i_e) / max(1, launch_steps),
@@ -303,7 +340,8 @@ def main():
     ap.add_argument("--inject-only", action="store_true",
                     help="time only the injection workload (no JSON line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--decode-workload", default="70b", choices=["70b", "8b", "ragged"],
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache decode figure")
+    ap.add_argument("--decode-workload", default="70b", choices=["70b", "8b", "ragged", "70b-fp8"],
                     help="decode workload timed (the reported line uses 70b)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -322,6 +360,9 @@ def main():
     probe = bw_probe()
     log("bw probe: %.1f GB/s" % probe)
     dec, _ = run_decode(args.steps, args.warmup, args.decode_workload)
+    fp8 = None
+    if not args.no_fp8 and args.decode_workload == "70b":
+        fp8, _ = run_decode(args.steps, args.warmup, "70b-fp8")
     inj = None if args.no_inject else run_inject(args.inject_reps)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     line = {
@@ -356,6 +397,14 @@ def main():
         "bw_probe_gbps": round(probe, 1),
         "cpu_baseline": cpu,
     }
+    if fp8 is not None:
+        line["decode_fp8"] = {
+            "workload": "the same decode workload with an fp8 (E4M3) cache, per-(layer, KV head) "
+                        "scales, bf16 queries",
+            "ms_per_step": round(fp8["ms_per_step"], 4), "gbps": round(fp8["value"], 1),
+            "pct_of_peak": round(100 * fp8["value"] / PEAK_HBM_GBPS, 2),
+            "launch_us_avg": round(fp8["launch_ms_avg"] * 1e3, 2),
+            "step_speedup_vs_bf16": round(dec["ms_per_step"] / fp8["ms_per_step"], 3)}
     if inj is not None:
         line["inject"] = {"tokens_per_s": round(inj["tokens_per_s"], 1), "unit": "tokens/s",
                           "token_layers_per_s": round(inj["token_layers_per_s"], 1),

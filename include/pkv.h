@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 /* Tokens per physical block ([InferScale] §2; [KV essay] "Paged attention"). */
 #define PKV_BLOCK_TOKENS 16
 
@@ -54,10 +54,15 @@ typedef int32_t pkv_status;
 #define PKV_E_HIP         -6  /* a HIP runtime call or launch failed         */
 #define PKV_E_UNSUPPORTED -7  /* shape/dtype combination not implemented     */
 
-/* Element formats of the cache, of injected/appended K/V and of q. */
-#define PKV_F32  0
-#define PKV_BF16 1
-#define PKV_F16  2
+/* Element formats.  A pool holds F32, BF16, F16 or FP8E4M3; injected and
+ * appended K/V and q are F32, BF16 or F16.  FP8E4M3 is the OCP 8-bit E4M3
+ * format (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest
+ * finite value 448, no infinities): a quantised cache, which the int8/int4
+ * paragraph of [KV management] motivates, halving decode bytes. */
+#define PKV_F32     0
+#define PKV_BF16    1
+#define PKV_F16     2
+#define PKV_FP8E4M3 3
 
 /* RoPE pairings ([InferScale] §2: R_p is block-diagonal with 2x2 rotations).
  * PAIRS rotates dimensions (2i, 2i+1); HALVES rotates (i, i+d/2); NONE stores
@@ -83,7 +88,11 @@ typedef struct pkv_plan pkv_plan;   /* host decode split plan (opaque)    */
  * i.e. d/X chunks of X consecutive dims for all 16 tokens.  Inside a V plane,
  * element (t, j) is at j * 16 + t (dimension-major).  Planes must be 16-byte
  * aligned (base pointers and every stride times the element size a multiple
- * of 16).  dtype is PKV_F32, PKV_BF16 or PKV_F16; head_dim is 64 or 128. */
+ * of 16).  dtype is PKV_F32, PKV_BF16, PKV_F16 or PKV_FP8E4M3; head_dim is 64
+ * or 128.  An FP8E4M3 pool stores code = e4m3(x / scale) (round to nearest
+ * even, saturating at 448) with one float scale per (layer, KV head) for K
+ * and one for V: k_scale, v_scale are device float [n_layers][n_kv_heads]
+ * (NULL for the other formats). */
 typedef struct {
   int32_t n_layers;
   int32_t num_blocks;
@@ -96,19 +105,24 @@ typedef struct {
   int64_t layer_stride; /* elements */
   int64_t block_stride; /* elements */
   int64_t head_stride;  /* elements */
+  const float* k_scale; /* device, FP8E4M3 pools only */
+  const float* v_scale; /* device, FP8E4M3 pools only */
 } pkv_pool;
 
 /* The store of precomputed, unrotated K/V ([InferScale] §3: keys captured
  * before the rotary embedding, kept with their values, per layer).  Element
  * (layer, token, kv head, dim) is at layer*layer_stride + token*token_stride +
- * head*head_dim + dim, for K at k and V at v.  Same dtype, n_kv_heads and
- * head_dim as the pool; 16-byte aligned rows. */
+ * head*head_dim + dim, for K at k and V at v.  Same n_kv_heads and head_dim
+ * as the pool; 16-byte aligned rows.  dtype is the pool's, or PKV_BF16 /
+ * PKV_F16 for an FP8E4M3 pool. */
 typedef struct {
   const void* k;        /* device */
   const void* v;        /* device */
   int64_t layer_stride; /* elements */
   int64_t token_stride; /* elements */
   int64_t n_tokens;     /* tokens per layer (for range checks) */
+  int32_t dtype;        /* format of the stored K/V */
+  int32_t _reserved;
 } pkv_src;
 
 /* One injected run: source tokens src_token .. src_token+n_tokens-1 land at
@@ -237,15 +251,16 @@ pkv_status pkv_inject(pkv_cache* cache, const pkv_pool* pool, const pkv_src* src
  * sequence b lands at position p = d_first_pos[b] + t through row b of the
  * device block table (d_tables, int32, row stride table_stride):
  *   K[slot] = round(R_p * k_new[b][t]),  V[slot] = v_new[b][t]
- * k_new, v_new: device, [n_seqs][n_new][n_kv_heads][head_dim] in pool dtype.
+ * k_new, v_new: device, [n_seqs][n_new][n_kv_heads][head_dim] in new_dtype
+ * (the pool's, or PKV_BF16 / PKV_F16 for an FP8E4M3 pool).
  * d_first_pos: device int32[n_seqs] (the first_pos_out of pkv_extend).
  * Rows of tokens at positions >= max_pos or beyond the table are skipped.
  * ------------------------------------------------------------------------- */
 pkv_status pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* d_tables,
                          int32_t table_stride, const int32_t* d_first_pos, int32_t n_seqs,
                          int32_t n_new, const void* d_k_new, const void* d_v_new,
-                         int32_t rope_mode, const float* d_cos, const float* d_sin,
-                         int32_t max_pos, void* stream);
+                         int32_t new_dtype, int32_t rope_mode, const float* d_cos,
+                         const float* d_sin, int32_t max_pos, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Decode attention ([KV essay] "First, what K and V are": softmax(q K^T /
@@ -264,8 +279,9 @@ pkv_status pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* d_t
  * Outputs: d_out (device float [n_seqs][n_q_heads][head_dim]) and, if not
  * NULL, d_lse (device float [n_seqs][n_q_heads], ln of the sum of exp of the
  * scaled scores).  A sequence of length 0 gets out = 0, lse = -inf.
- * q: device [n_seqs][n_q_heads][head_dim] in the pool dtype, already rotated
- * to its own position.  scale <= 0 selects 1/sqrt(head_dim).
+ * q: device [n_seqs][n_q_heads][head_dim] in q_dtype (the pool's; PKV_BF16 or
+ * PKV_F16 for an FP8E4M3 pool), already rotated to its own position.
+ * scale <= 0 selects 1/sqrt(head_dim).
  * ------------------------------------------------------------------------- */
 pkv_status pkv_decode_plan_create(const int64_t* lens, int32_t n_seqs, int32_t n_q_heads,
                                   int32_t n_kv_heads, int32_t head_dim, int32_t part_tokens,
@@ -292,7 +308,8 @@ size_t pkv_decode_workspace_bytes(const pkv_plan* plan);
 pkv_status pkv_decode_plan_upload(pkv_plan* plan, void* d_ws, size_t ws_bytes, void* stream);
 
 pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int32_t layer,
-                                const void* d_q, float scale, const int32_t* d_tables,
+                                const void* d_q, int32_t q_dtype, float scale,
+                                const int32_t* d_tables,
                                 int32_t table_stride, float* d_out, float* d_lse, void* d_ws,
                                 size_t ws_bytes, void* stream);
 

@@ -26,8 +26,8 @@ PKV_E_UNSUPPORTED = -7
 STATUS_NAMES = {0: "OK", -1: "INVALID", -2: "OOM", -3: "RANGE", -4: "OVERLAP",
                 -5: "WORKSPACE", -6: "HIP", -7: "UNSUPPORTED"}
 
-PKV_F32, PKV_BF16, PKV_F16 = 0, 1, 2
-DTYPE_CODES = {"f32": PKV_F32, "bf16": PKV_BF16, "f16": PKV_F16}
+PKV_F32, PKV_BF16, PKV_F16, PKV_FP8E4M3 = 0, 1, 2, 3
+DTYPE_CODES = {"f32": PKV_F32, "bf16": PKV_BF16, "f16": PKV_F16, "fp8": PKV_FP8E4M3}
 PKV_ROPE_PAIRS, PKV_ROPE_HALVES, PKV_ROPE_NONE = 0, 1, 2
 ROPE_CODES = {"pairs": PKV_ROPE_PAIRS, "halves": PKV_ROPE_HALVES, "none": PKV_ROPE_NONE}
 BLOCK_TOKENS = 16
@@ -46,13 +46,15 @@ class pkv_pool(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("_reserved", ctypes.c_int32),
                 ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("layer_stride", ctypes.c_int64), ("block_stride", ctypes.c_int64),
-                ("head_stride", ctypes.c_int64)]
+                ("head_stride", ctypes.c_int64), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p)]
 
 
 class pkv_src(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("layer_stride", ctypes.c_int64), ("token_stride", ctypes.c_int64),
-                ("n_tokens", ctypes.c_int64)]
+                ("n_tokens", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("_reserved", ctypes.c_int32)]
 
 
 class pkv_run(ctypes.Structure):
@@ -91,7 +93,7 @@ SIGNATURES = {
     "pkv_inject": (_I32, [_P, ctypes.POINTER(pkv_pool), ctypes.POINTER(pkv_src), _P, _I32,
                           _I32, _I32, _I32, _P, _P, _I32, _P, _SZ, _P]),
     "pkv_append_kv": (_I32, [ctypes.POINTER(pkv_pool), _I32, _P, _I32, _P, _I32, _I32, _P, _P,
-                             _I32, _P, _P, _I32, _P]),
+                             _I32, _I32, _P, _P, _I32, _P]),
     "pkv_decode_plan_create": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_P)]),
     "pkv_decode_plan_destroy": (None, [_P]),
     "pkv_decode_plan_items": (_I32, [_P]),
@@ -99,8 +101,8 @@ SIGNATURES = {
     "pkv_decode_plan_waves": (_I32, [_P]),
     "pkv_decode_workspace_bytes": (_SZ, [_P]),
     "pkv_decode_plan_upload": (_I32, [_P, _P, _SZ, _P]),
-    "pkv_decode_attention": (_I32, [_P, ctypes.POINTER(pkv_pool), _I32, _P, ctypes.c_float, _P,
-                                    _I32, _P, _P, _P, _SZ, _P]),
+    "pkv_decode_attention": (_I32, [_P, ctypes.POINTER(pkv_pool), _I32, _P, _I32,
+                                    ctypes.c_float, _P, _I32, _P, _P, _P, _SZ, _P]),
     "pkv_bw_probe": (_I32, [_P, _SZ, _P, _P]),
 }
 
@@ -241,13 +243,25 @@ def pkv_rope_table(head_dim, base, max_pos):
 # Descriptors
 # ---------------------------------------------------------------------------
 def make_pool(k, v, n_layers, num_blocks, n_kv_heads, head_dim, dtype,
-              layer_stride, block_stride, head_stride) -> pkv_pool:
+              layer_stride, block_stride, head_stride, k_scale=None, v_scale=None) -> pkv_pool:
     return pkv_pool(n_layers, num_blocks, n_kv_heads, head_dim, DTYPE_CODES[dtype], 0,
-                    _ptr(k), _ptr(v), layer_stride, block_stride, head_stride)
+                    _ptr(k), _ptr(v), layer_stride, block_stride, head_stride, _ptr(k_scale),
+                    _ptr(v_scale))
 
 
-def make_src(k, v, layer_stride, token_stride, n_tokens) -> pkv_src:
-    return pkv_src(_ptr(k), _ptr(v), layer_stride, token_stride, n_tokens)
+def make_src(k, v, layer_stride, token_stride, n_tokens, dtype=None) -> pkv_src:
+    """dtype defaults to the torch dtype of k ("f32", "bf16", "f16")."""
+    if dtype is None:
+        dtype = {"torch.float32": "f32", "torch.bfloat16": "bf16",
+                 "torch.float16": "f16"}[str(k.dtype)]
+    return pkv_src(_ptr(k), _ptr(v), layer_stride, token_stride, n_tokens, DTYPE_CODES[dtype], 0)
+
+
+def _dtype_of(t, default):
+    if t is None or not hasattr(t, "dtype"):
+        return default
+    return {"torch.float32": PKV_F32, "torch.bfloat16": PKV_BF16,
+            "torch.float16": PKV_F16}.get(str(t.dtype), default)
 
 
 def make_runs(runs):
@@ -277,10 +291,12 @@ def pkv_inject(cache, pool: pkv_pool, src: pkv_src, runs, layer_begin, layer_end
 
 
 def pkv_append_kv(pool: pkv_pool, layer, tables, first_pos, n_new, k_new, v_new, rope_mode,
-                  cos, sin, max_pos, stream=None):
+                  cos, sin, max_pos, stream=None, new_dtype=None):
+    """new_dtype defaults to the torch dtype of k_new."""
+    nd = DTYPE_CODES[new_dtype] if isinstance(new_dtype, str) else _dtype_of(k_new, pool.dtype)
     _check(load_library().pkv_append_kv(ctypes.byref(pool), layer, _ptr(tables),
                                         tables.shape[1], _ptr(first_pos), first_pos.shape[0],
-                                        n_new, _ptr(k_new), _ptr(v_new),
+                                        n_new, _ptr(k_new), _ptr(v_new), nd,
                                         ROPE_CODES.get(rope_mode, rope_mode), _ptr(cos), _ptr(sin),
                                         max_pos, _stream(stream)))
 
@@ -324,8 +340,10 @@ def pkv_decode_plan_upload(plan, workspace, stream=None):
 
 
 def pkv_decode_attention(plan, pool: pkv_pool, layer, q, tables, out, lse, workspace,
-                         scale=0.0, stream=None):
-    _check(load_library().pkv_decode_attention(plan, ctypes.byref(pool), layer, _ptr(q),
+                         scale=0.0, stream=None, q_dtype=None):
+    """q_dtype defaults to the torch dtype of q."""
+    qd = DTYPE_CODES[q_dtype] if isinstance(q_dtype, str) else _dtype_of(q, pool.dtype)
+    _check(load_library().pkv_decode_attention(plan, ctypes.byref(pool), layer, _ptr(q), qd,
                                                float(scale), _ptr(tables), tables.shape[1],
                                                _ptr(out), _ptr(lse), _ptr(workspace),
                                                workspace.numel() * workspace.element_size(),

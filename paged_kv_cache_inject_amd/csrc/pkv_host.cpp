@@ -57,6 +57,7 @@ int elem_bytes(int32_t dtype) {
     case PKV_F32: return 4;
     case PKV_BF16: return 2;
     case PKV_F16: return 2;
+    case PKV_FP8E4M3: return 1;
     default: return 0;
   }
 }
@@ -174,6 +175,22 @@ pkv_status check_pool(const pkv_pool* p) {
     return fail(PKV_E_INVALID, "head_stride smaller than a plane");
   if (p->num_blocks > 1 && p->block_stride < plane)
     return fail(PKV_E_INVALID, "block_stride smaller than a plane");
+  if (p->dtype == PKV_FP8E4M3 && (!p->k_scale || !p->v_scale))
+    return fail(PKV_E_INVALID, "an FP8E4M3 pool needs k_scale and v_scale");
+  return PKV_OK;
+}
+
+// Format of incoming K/V or q for a pool: the pool's own, or a 16-bit float
+// for a quantised (FP8E4M3) pool.
+pkv_status check_input_dtype(const pkv_pool* p, int32_t dtype, const char* what) {
+  if (p->dtype == PKV_FP8E4M3) {
+    if (dtype == PKV_BF16 || dtype == PKV_F16) return PKV_OK;
+    return fail(PKV_E_UNSUPPORTED, "%s dtype %d for an FP8E4M3 pool (supported: BF16, F16)",
+                what, dtype);
+  }
+  if (dtype != p->dtype)
+    return fail(PKV_E_UNSUPPORTED, "%s dtype %d differs from the pool's %d", what, dtype,
+                p->dtype);
   return PKV_OK;
 }
 
@@ -390,7 +407,8 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
   if (pkv_status st = check_pool(pool)) return st;
   if (pkv_status st = check_rope(rope_mode, d_cos, d_sin, max_pos)) return st;
   if (!src || !src->k || !src->v) return fail(PKV_E_INVALID, "null source");
-  const int eb = elem_bytes(pool->dtype);
+  if (pkv_status st = check_input_dtype(pool, src->dtype, "source")) return st;
+  const int eb = elem_bytes(src->dtype);
   if ((reinterpret_cast<uintptr_t>(src->k) | reinterpret_cast<uintptr_t>(src->v)) & 15)
     return fail(PKV_E_INVALID, "source pointers must be 16-byte aligned");
   if (((src->layer_stride | src->token_stride) * eb) % 16 || src->layer_stride < 0 ||
@@ -491,9 +509,10 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
 pkv_status pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* d_tables,
                          int32_t table_stride, const int32_t* d_first_pos, int32_t n_seqs,
                          int32_t n_new, const void* d_k_new, const void* d_v_new,
-                         int32_t rope_mode, const float* d_cos, const float* d_sin,
-                         int32_t max_pos, void* stream) {
+                         int32_t new_dtype, int32_t rope_mode, const float* d_cos,
+                         const float* d_sin, int32_t max_pos, void* stream) {
   if (pkv_status st = check_pool(pool)) return st;
+  if (pkv_status st = check_input_dtype(pool, new_dtype, "new K/V")) return st;
   if (pkv_status st = check_rope(rope_mode, d_cos, d_sin, max_pos)) return st;
   if (layer < 0 || layer >= pool->n_layers) return fail(PKV_E_INVALID, "layer %d", layer);
   if (n_seqs < 0 || n_new < 0) return fail(PKV_E_INVALID, "negative count");
@@ -503,8 +522,8 @@ pkv_status pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* d_t
   if ((reinterpret_cast<uintptr_t>(d_k_new) | reinterpret_cast<uintptr_t>(d_v_new)) & 15)
     return fail(PKV_E_INVALID, "k_new / v_new must be 16-byte aligned");
   hipError_t e = pkv::launch_append(*pool, layer, d_tables, table_stride, d_first_pos, n_seqs,
-                                    n_new, d_k_new, d_v_new, rope_mode, d_cos, d_sin, max_pos,
-                                    static_cast<hipStream_t>(stream));
+                                    n_new, d_k_new, d_v_new, new_dtype, rope_mode, d_cos, d_sin,
+                                    max_pos, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");
   return ok();
 }
@@ -629,14 +648,17 @@ pkv_status pkv_decode_plan_upload(pkv_plan* plan, void* d_ws, size_t ws_bytes, v
 }
 
 pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int32_t layer,
-                                const void* d_q, float scale, const int32_t* d_tables,
-                                int32_t table_stride, float* d_out, float* d_lse, void* d_ws,
-                                size_t ws_bytes, void* stream) {
+                                const void* d_q, int32_t q_dtype, float scale,
+                                const int32_t* d_tables, int32_t table_stride, float* d_out,
+                                float* d_lse, void* d_ws, size_t ws_bytes, void* stream) {
   if (!plan) return fail(PKV_E_INVALID, "null plan");
   if (pkv_status st = check_pool(pool)) return st;
+  if (pkv_status st = check_input_dtype(pool, q_dtype, "q")) return st;
   if (layer < 0 || layer >= pool->n_layers) return fail(PKV_E_INVALID, "layer %d", layer);
   if (pool->n_kv_heads != plan->n_kv_heads || pool->head_dim != plan->head_dim)
     return fail(PKV_E_INVALID, "plan and pool disagree on KV heads or head_dim");
+  if (pool->dtype == PKV_FP8E4M3 && plan->n_q_heads / plan->n_kv_heads > 16)
+    return fail(PKV_E_UNSUPPORTED, "FP8E4M3 decode supports up to 16 query heads per KV head");
   if (plan->n_seqs == 0) return ok();
   if (!d_q || !d_out || !d_tables) return fail(PKV_E_INVALID, "null device argument");
   if (reinterpret_cast<uintptr_t>(d_q) & 15) return fail(PKV_E_INVALID, "q must be 16-byte aligned");
@@ -654,6 +676,7 @@ pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int3
   char* ws = static_cast<char*>(d_ws);
   pkv::DecodeArgs a;
   a.q = d_q;
+  a.q_dtype = q_dtype;
   a.n_q_heads = plan->n_q_heads;
   a.scale = scale > 0.f ? scale : float(1.0 / std::sqrt(double(plan->head_dim)));
   a.tables = d_tables;

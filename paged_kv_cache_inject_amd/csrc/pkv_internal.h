@@ -46,11 +46,13 @@ hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, const InjectD
 
 hipError_t launch_append(const pkv_pool& pool, int layer, const int32_t* d_tables,
                          int table_stride, const int32_t* d_first_pos, int n_seqs, int n_new,
-                         const void* d_k, const void* d_v, int rope_mode, const float* d_cos,
-                         const float* d_sin, int max_pos, hipStream_t stream);
+                         const void* d_k, const void* d_v, int new_dtype, int rope_mode,
+                         const float* d_cos, const float* d_sin, int max_pos,
+                         hipStream_t stream);
 
 struct DecodeArgs {
   const void* q;
+  int q_dtype;
   int n_q_heads;
   float scale;
   const int32_t* tables;

@@ -78,6 +78,38 @@ template <> struct Fmt<PKV_F16> {
   }
 };
 
+// OCP E4M3: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; largest
+// finite value 448 (0x7E), 0x7F/0xFF are NaN, no infinities.
+template <> struct Fmt<PKV_FP8E4M3> {
+  typedef uint8_t T;
+  static constexpr int kBytes = 1;
+  __device__ static float to_f32(uint8_t b) {
+    const uint32_t e = (b >> 3) & 0xF, m = b & 7;
+    float v = e == 0 ? float(m) * 0.001953125f  // m * 2^-9
+                     : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    if ((b & 0x7F) == 0x7F) v = __uint_as_float(0x7fc00000u);
+    return (b & 0x80) ? -v : v;
+  }
+  // Round to nearest, ties to even; magnitudes that would round beyond 448
+  // saturate to 448; NaN stays NaN.
+  __device__ static uint8_t from_f32(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return uint8_t(sign | 0x7Fu);
+    if (a >= 0x43e00000u) return uint8_t(sign | 0x7Eu);          // >= 448
+    if (a < 0x3c800000u) {                                         // < 2^-6: step 2^-9
+      const uint32_t q = uint32_t(rintf(__uint_as_float(a) * 512.0f));
+      return uint8_t(sign | q);                                    // q = 8 is 2^-6
+    }
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);                  // keep 3 mantissa bits
+    r &= 0xFFF00000u;
+    uint32_t code = ((((r >> 23) & 0xFFu) - 120u) << 3) | ((r >> 20) & 7u);
+    if (code > 0x7Eu) code = 0x7Eu;
+    return uint8_t(sign | code);
+  }
+};
+
 // 16-byte global access helpers.
 __device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ inline void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
@@ -98,6 +130,72 @@ __device__ inline uint2 ld8_stream(const void* p) {
 __device__ inline void st16_stream(void* p, uint4 v) {
   const u32x4_t w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ inline void st8_stream(void* p, uint2 v) {
+  const u32x2_t w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
+}
+__device__ inline uint32_t ld4_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+// The X elements of a 16-byte chunk as float32.
+template <int DT>
+__device__ inline void unpack16(const uint4& c, float* f) {
+  typedef typename Fmt<DT>::T T;
+  constexpr int X = 16 / Fmt<DT>::kBytes;
+  T v[X];
+  *reinterpret_cast<uint4*>(v) = c;
+#pragma unroll
+  for (int e = 0; e < X; ++e) f[e] = Fmt<DT>::to_f32(v[e]);
+}
+
+// Rotation of float32 values, two products and one add/subtract each, never
+// fused (y0 = x0*c - x1*s, y1 = x0*s + x1*c).  PAIRS: element e pairs with
+// e+1 inside the run (pair index (first_dim + e) / 2); HALVES: element e of
+// `a` pairs with element e of `b` (pair index first_dim + e).
+template <int N>
+__device__ inline void rot_pairs_f(float* f, int first_dim, const float* cr, const float* sr) {
+#pragma unroll
+  for (int e = 0; e < N; e += 2) {
+    const int i = (first_dim + e) >> 1;
+    const float c = cr[i], s = sr[i];
+    const float x0 = f[e], x1 = f[e + 1];
+    f[e] = x0 * c - x1 * s;
+    f[e + 1] = x0 * s + x1 * c;
+  }
+}
+template <int N>
+__device__ inline void rot_halves_f(float* a, float* b, int first_dim, const float* cr,
+                                    const float* sr) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const int i = first_dim + e;
+    const float c = cr[i], s = sr[i];
+    const float x0 = a[e], x1 = b[e];
+    a[e] = x0 * c - x1 * s;
+    b[e] = x0 * s + x1 * c;
+  }
+}
+
+// N float32 values stored in the pool format PDT; a quantised (fp8) pool
+// stores e4m3(x / scale), the division correctly rounded in float32.
+template <int PDT, int N>
+struct Packed {
+  typedef typename Fmt<PDT>::T T;
+  T v[N];
+  __device__ void set(const float* f, float scale) {
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+      v[e] = Fmt<PDT>::from_f32(PDT == PKV_FP8E4M3 ? f[e] / scale : f[e]);
+  }
+};
+template <int PDT, int N>
+__device__ inline void store_packed(void* dst, const Packed<PDT, N>& pk) {
+  constexpr int B = N * Fmt<PDT>::kBytes;
+  static_assert(B == 16 || B == 8, "16- or 8-byte pieces");
+  if constexpr (B == 16) st16_stream(dst, *reinterpret_cast<const uint4*>(pk.v));
+  else st8_stream(dst, *reinterpret_cast<const uint2*>(pk.v));
 }
 
 // Rotate the X elements of one 16-byte chunk.  PAIRS: element e pairs with
@@ -171,6 +269,8 @@ struct InjectParams {
   char* pool_v;
   int64_t p_layer, p_block, p_head;  // bytes
   int n_kv_heads;
+  const float* k_scale;              // [layers][heads], quantised pools only
+  const float* v_scale;
   const char* src_k;
   const char* src_v;
   int64_t s_layer, s_token;          // bytes
@@ -185,38 +285,26 @@ struct InjectParams {
 
 constexpr int kInjectThreads = 256;
 
-// Rotation of one chunk pair using cos/sin rows staged in LDS (row t of the
-// block: cs[t][0..D/2) = cos, cs[t][D/2..D) = sin).
-template <int DT, int D>
-__device__ inline void rotate_chunk_pair_lds(uint4& lo, uint4& hi, int c0, int mode,
-                                             const float* row) {
-  constexpr int X = 16 / Fmt<DT>::kBytes;
-  constexpr int C = D / X;
-  if (mode == PKV_ROPE_NONE) return;
-  if (mode == PKV_ROPE_PAIRS) {
-    rotate_pairs<DT>(lo, c0 * X, row, row + D / 2);
-    rotate_pairs<DT>(hi, (c0 + C / 2) * X, row, row + D / 2);
-  } else {
-    rotate_halves<DT>(lo, hi, c0 * X, row, row + D / 2);
-  }
-}
-
 // One workgroup per (destination block, group of layers).  The block's 16
 // rotary rows are staged in LDS once; then for every layer and group of HG
-// KV heads: each (token, chunk pair) unit reads its two 16-byte K and V
-// chunks of the source row, rotates K and stores it into the K plane; V goes
-// through LDS to be written dimension-major.
-template <int DT, int D, int HG>
+// KV heads: each (token, source chunk pair) unit reads its two 16-byte K and
+// V chunks of the source row (format SDT), rotates K in float32 and stores it
+// into the K plane in the pool format PDT; V goes through LDS (already in
+// PDT) to be written dimension-major.  Source chunk pairs are (c0, c0 + C/2)
+// so that the halves pairing finds both partners in one unit.
+template <int SDT, int PDT, int D, int HG>
 __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParams p) {
-  typedef typename Fmt<DT>::T T;
-  constexpr int E = Fmt<DT>::kBytes;
-  constexpr int X = 16 / E;
-  constexpr int C = D / X;
-  constexpr int UNITS = kBlock * (C / 2);
-  constexpr int VPIECES = D * (kBlock / X);
+  typedef typename Fmt<PDT>::T TP;
+  constexpr int ES = Fmt<SDT>::kBytes, EP = Fmt<PDT>::kBytes;
+  constexpr int XS = 16 / ES;                 // source elements per 16-byte chunk
+  constexpr int XP = 16 / EP;                 // pool elements per 16-byte chunk
+  constexpr int CS = D / XS;                  // source chunks per row
+  constexpr int UNITS = kBlock * (CS / 2);    // (token, chunk pair) units per head
+  constexpr int VPIECES = D * (kBlock / XP);  // 16-byte pieces of a V plane
   constexpr int UPT = (HG * UNITS + kInjectThreads - 1) / kInjectThreads;
   constexpr int VPT = (HG * VPIECES + kInjectThreads - 1) / kInjectThreads;
-  __shared__ T vtile[HG][kBlock][D];
+  static_assert(XP % XS == 0, "a source chunk lands inside one pool chunk");
+  __shared__ TP vtile[HG][kBlock][D];
   __shared__ float cs[kBlock][D];
   __shared__ InjectDesc desc;
 
@@ -257,11 +345,11 @@ __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParam
         const int c0 = r / kBlock;
         const int src = (w < nh * UNITS) ? desc.src[t] : -1;
         if (src >= 0) {
-          const int64_t row = int64_t(src) * p.s_token + int64_t(h0 + hl) * D * E;
+          const int64_t row = int64_t(src) * p.s_token + int64_t(h0 + hl) * D * ES;
           k0[u] = ld16_stream(sk + row + c0 * 16);
-          k1[u] = ld16_stream(sk + row + (c0 + C / 2) * 16);
+          k1[u] = ld16_stream(sk + row + (c0 + CS / 2) * 16);
           v0[u] = ld16_stream(sv + row + c0 * 16);
-          v1[u] = ld16_stream(sv + row + (c0 + C / 2) * 16);
+          v1[u] = ld16_stream(sv + row + (c0 + CS / 2) * 16);
         }
       }
 #pragma unroll
@@ -272,15 +360,41 @@ __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParam
         const int t = r % kBlock;
         const int c0 = r / kBlock;
         if (w >= nh * UNITS || desc.src[t] < 0) continue;
-        rotate_chunk_pair_lds<DT, D>(k0[u], k1[u], c0, p.rope_mode, cs[t]);
-        char* kplane = kplane0 + int64_t(h0 + hl) * p.p_head;
-        st16_stream(kplane + (c0 * kBlock + t) * 16, k0[u]);
-        st16_stream(kplane + ((c0 + C / 2) * kBlock + t) * 16, k1[u]);
-        *reinterpret_cast<uint4*>(&vtile[hl][t][c0 * X]) = v0[u];
-        *reinterpret_cast<uint4*>(&vtile[hl][t][(c0 + C / 2) * X]) = v1[u];
+        const int h = h0 + hl;
+        const int j0 = c0 * XS, j1 = (c0 + CS / 2) * XS;  // first dims of the two chunks
+        float kl[XS], kh[XS];
+        unpack16<SDT>(k0[u], kl);
+        unpack16<SDT>(k1[u], kh);
+        if (p.rope_mode == PKV_ROPE_PAIRS) {
+          rot_pairs_f<XS>(kl, j0, cs[t], cs[t] + D / 2);
+          rot_pairs_f<XS>(kh, j1, cs[t], cs[t] + D / 2);
+        } else if (p.rope_mode == PKV_ROPE_HALVES) {
+          rot_halves_f<XS>(kl, kh, j0, cs[t], cs[t] + D / 2);
+        }
+        const float ksc = PDT == PKV_FP8E4M3 ? p.k_scale[layer * p.n_kv_heads + h] : 1.f;
+        Packed<PDT, XS> pk;
+        char* kplane = kplane0 + int64_t(h) * p.p_head;
+        pk.set(kl, ksc);
+        store_packed(kplane + (((j0 / XP) * kBlock + t) * XP + j0 % XP) * EP, pk);
+        pk.set(kh, ksc);
+        store_packed(kplane + (((j1 / XP) * kBlock + t) * XP + j1 % XP) * EP, pk);
+        if constexpr (SDT == PDT) {
+          *reinterpret_cast<uint4*>(&vtile[hl][t][j0]) = v0[u];
+          *reinterpret_cast<uint4*>(&vtile[hl][t][j1]) = v1[u];
+        } else {
+          const float vsc = p.v_scale[layer * p.n_kv_heads + h];
+          float vf[XS];
+          Packed<PDT, XS> pv;
+          unpack16<SDT>(v0[u], vf);
+          pv.set(vf, vsc);
+          *reinterpret_cast<uint2*>(&vtile[hl][t][j0]) = *reinterpret_cast<const uint2*>(pv.v);
+          unpack16<SDT>(v1[u], vf);
+          pv.set(vf, vsc);
+          *reinterpret_cast<uint2*>(&vtile[hl][t][j1]) = *reinterpret_cast<const uint2*>(pv.v);
+        }
       }
       __syncthreads();
-      // V planes dimension-major, X tokens per 16-byte piece; a piece with
+      // V planes dimension-major, XP tokens per 16-byte piece; a piece with
       // slots this call does not write keeps their old contents.
 #pragma unroll
       for (int u = 0; u < VPT; ++u) {
@@ -288,18 +402,18 @@ __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParam
         if (w >= nh * VPIECES) break;
         const int hl = w / VPIECES;
         const int r = w - hl * VPIECES;
-        const int j = r / (kBlock / X);
-        const int t0 = (r % (kBlock / X)) * X;
-        char* dst = vplane0 + int64_t(h0 + hl) * p.p_head + (int64_t(j) * kBlock + t0) * E;
-        T out[X];
+        const int j = r / (kBlock / XP);
+        const int t0 = (r % (kBlock / XP)) * XP;
+        char* dst = vplane0 + int64_t(h0 + hl) * p.p_head + (int64_t(j) * kBlock + t0) * EP;
+        TP out[XP];
         bool need_old = false;
         if (!full) {
 #pragma unroll
-          for (int e = 0; e < X; ++e) need_old |= desc.src[t0 + e] < 0;
+          for (int e = 0; e < XP; ++e) need_old |= desc.src[t0 + e] < 0;
         }
         if (need_old) *reinterpret_cast<uint4*>(out) = ld16(dst);
 #pragma unroll
-        for (int e = 0; e < X; ++e)
+        for (int e = 0; e < XP; ++e)
           if (desc.src[t0 + e] >= 0) out[e] = vtile[hl][t0 + e][j];
         st16_stream(dst, *reinterpret_cast<uint4*>(out));
       }
@@ -316,6 +430,8 @@ struct AppendParams {
   char* pool_v;
   int64_t p_layer, p_block, p_head;  // bytes
   int n_kv_heads;
+  const float* k_scale;              // [layers][heads], quantised pools only
+  const float* v_scale;
   int num_blocks;
   int layer;
   const int32_t* tables;
@@ -330,12 +446,13 @@ struct AppendParams {
   int max_pos;
 };
 
-template <int DT, int D>
+template <int SDT, int PDT, int D>
 __global__ __launch_bounds__(256) void append_kv_kernel(AppendParams p) {
-  typedef typename Fmt<DT>::T T;
-  constexpr int E = Fmt<DT>::kBytes;
-  constexpr int X = 16 / E;
-  constexpr int C = D / X;
+  typedef typename Fmt<SDT>::T TS;
+  typedef typename Fmt<PDT>::T TP;
+  constexpr int ES = Fmt<SDT>::kBytes, EP = Fmt<PDT>::kBytes;
+  constexpr int XS = 16 / ES, XP = 16 / EP;
+  constexpr int CS = D / XS;
   const int b = blockIdx.x / p.n_new;
   const int t = blockIdx.x - b * p.n_new;
   const int pos = p.first_pos[b] + t;
@@ -348,24 +465,43 @@ __global__ __launch_bounds__(256) void append_kv_kernel(AppendParams p) {
   const int tin = pos % kBlock;
   char* kplane0 = p.pool_k + p.layer * p.p_layer + int64_t(blk) * p.p_block;
   char* vplane0 = p.pool_v + p.layer * p.p_layer + int64_t(blk) * p.p_block;
-  const int64_t row0 = (int64_t(b) * p.n_new + t) * p.n_kv_heads * D * E;
+  const int64_t row0 = (int64_t(b) * p.n_new + t) * p.n_kv_heads * D * ES;
   const char* kin = p.k_new + row0;
   const char* vin = p.v_new + row0;
-  for (int w = threadIdx.x; w < p.n_kv_heads * (C / 2); w += blockDim.x) {
-    const int h = w / (C / 2);
-    const int c0 = w - h * (C / 2);
-    uint4 k0 = ld16(kin + int64_t(h) * D * E + c0 * 16);
-    uint4 k1 = ld16(kin + int64_t(h) * D * E + (c0 + C / 2) * 16);
-    rotate_chunk_pair<DT, D>(k0, k1, c0, pos, p.rope_mode, p.cos_t, p.sin_t);
+  const float* cr = p.cos_t + size_t(pos) * (D / 2);
+  const float* sr = p.sin_t + size_t(pos) * (D / 2);
+  for (int w = threadIdx.x; w < p.n_kv_heads * (CS / 2); w += blockDim.x) {
+    const int h = w / (CS / 2);
+    const int c0 = w - h * (CS / 2);
+    const int j0 = c0 * XS, j1 = (c0 + CS / 2) * XS;
+    float kl[XS], kh[XS];
+    unpack16<SDT>(ld16(kin + int64_t(h) * D * ES + j0 * ES), kl);
+    unpack16<SDT>(ld16(kin + int64_t(h) * D * ES + j1 * ES), kh);
+    if (p.rope_mode == PKV_ROPE_PAIRS) {
+      rot_pairs_f<XS>(kl, j0, cr, sr);
+      rot_pairs_f<XS>(kh, j1, cr, sr);
+    } else if (p.rope_mode == PKV_ROPE_HALVES) {
+      rot_halves_f<XS>(kl, kh, j0, cr, sr);
+    }
+    const float ksc = PDT == PKV_FP8E4M3 ? p.k_scale[p.layer * p.n_kv_heads + h] : 1.f;
     char* kplane = kplane0 + int64_t(h) * p.p_head;
-    st16(kplane + (c0 * kBlock + tin) * 16, k0);
-    st16(kplane + ((c0 + C / 2) * kBlock + tin) * 16, k1);
+    Packed<PDT, XS> pk;
+    pk.set(kl, ksc);
+    store_packed(kplane + (((j0 / XP) * kBlock + tin) * XP + j0 % XP) * EP, pk);
+    pk.set(kh, ksc);
+    store_packed(kplane + (((j1 / XP) * kBlock + tin) * XP + j1 % XP) * EP, pk);
   }
   for (int w = threadIdx.x; w < p.n_kv_heads * D; w += blockDim.x) {
     const int h = w / D;
     const int j = w - h * D;
-    const T v = reinterpret_cast<const T*>(vin + int64_t(h) * D * E)[j];
-    reinterpret_cast<T*>(vplane0 + int64_t(h) * p.p_head)[j * kBlock + tin] = v;
+    const TS v = reinterpret_cast<const TS*>(vin + int64_t(h) * D * ES)[j];
+    TP out;
+    if constexpr (SDT == PDT) {
+      out = v;
+    } else {
+      out = Fmt<PDT>::from_f32(Fmt<SDT>::to_f32(v) / p.v_scale[p.layer * p.n_kv_heads + h]);
+    }
+    reinterpret_cast<TP*>(vplane0 + int64_t(h) * p.p_head)[j * kBlock + tin] = out;
   }
 }
 
@@ -389,6 +525,8 @@ struct DecodeParams {
   float* part_ml;
   float* out;
   float* lse;
+  const float* k_scale;              // this layer's [heads] scales, quantised pools only
+  const float* v_scale;
 };
 
 // Stores one head's result: final (single-range sequence) or partial state.
@@ -465,12 +603,35 @@ template <> struct Mfma<PKV_F16> {
   }
 };
 
-template <int DT, int D, int DEPTH, int NW>
+// fp8 (E4M3) codes as float16 bit patterns worth exactly 2^-8 of their value:
+// the sign moves to bit 15 and the 7 exponent+mantissa bits to bits 13..7,
+// which rebases the exponent from bias 7 to bias 15 (subnormals included).
+// Two codes (low bytes of `t`, one per 16-bit half) per call.
+__device__ inline uint32_t e4m3x2_to_f16x2_div256(uint32_t t) {
+  return ((t & 0x007F007Fu) << 7) | ((t & 0x00800080u) << 8);
+}
+// Four codes in a dword -> four float16 values (x: codes 0,1; y: codes 2,3).
+__device__ inline uint2 e4m3x4_to_f16x4_div256(uint32_t w) {
+  const uint32_t lo = (w & 0xFFu) | ((w & 0xFF00u) << 8);
+  const uint32_t hi = ((w >> 16) & 0xFFu) | ((w >> 8) & 0xFF0000u);
+  return make_uint2(e4m3x2_to_f16x2_div256(lo), e4m3x2_to_f16x2_div256(hi));
+}
+
+// Decode kernel template parameters: KVDT the pool format, QDT the query
+// format (equal to KVDT, or BF16/F16 for an fp8 pool whose MFMA operands are
+// float16), head dim D, prefetch depth, waves per workgroup NW.
+template <int KVDT, int QDT, int D, int DEPTH, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
-  constexpr int S = D / 32;   // QK MFMA steps (4 chunks of 8 dims each)
+  constexpr bool FP8 = KVDT == PKV_FP8E4M3;
+  constexpr int OT = FP8 ? PKV_F16 : KVDT;  // MFMA operand format
+  constexpr int S = D / 32;   // QK MFMA steps of 32 dims
+  constexpr int SL = FP8 ? S / 2 : S;  // 16-byte K loads per lane and block
   constexpr int NT = D / 16;  // PV MFMA tiles of 16 dims
+  constexpr int VB = FP8 ? 4 : 8;      // V bytes per lane and tile
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // Wave-uniform (scalar register): block-table reads below then become
+  // scalar loads, whose waits do not stall on the K/V loads in flight.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane & 15;
   const int grp = lane >> 4;
   const DecodeItem it = p.items[blockIdx.x];
@@ -478,16 +639,35 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   const int hq = g * p.group + row;
   const bool head_ok = row < p.group;
 
-  // q operand (B of QK): head `row`, chunk 4s + grp of each step.
+  // q operand (B of QK) for head `row`: the dims whose K this lane loads in
+  // the same step (16-bit pools: chunk 4s + grp of 8 dims; fp8 pools: half
+  // `st % 2` of chunk 4(st/2) + grp of 16 dims).
   uint4 qreg[S];
   {
-    const char* qh = p.q + (int64_t(it.seq) * p.n_q_heads + (head_ok ? hq : g * p.group)) * D * 2;
+    typedef typename Fmt<QDT>::T TQ;
+    const TQ* qh = reinterpret_cast<const TQ*>(p.q) +
+                   (int64_t(it.seq) * p.n_q_heads + (head_ok ? hq : g * p.group)) * D;
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      qreg[s] = ld16(qh + (4 * s + grp) * 16);
-      if (!head_ok) qreg[s] = make_uint4(0, 0, 0, 0);
+    for (int st = 0; st < S; ++st) {
+      const int dim0 = FP8 ? (4 * (st / 2) + grp) * 16 + 8 * (st % 2) : (4 * st + grp) * 8;
+      uint4 raw = ld16(qh + dim0);
+      if constexpr (FP8 && QDT != PKV_F16) {
+        float f[8];
+        unpack16<QDT>(raw, f);
+        _Float16 hv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[e] = static_cast<_Float16>(f[e]);
+        raw = *reinterpret_cast<const uint4*>(hv);
+      }
+      qreg[st] = head_ok ? raw : make_uint4(0, 0, 0, 0);
     }
   }
+  float kmul = 1.f, vmul = 1.f;
+  if constexpr (FP8) {
+    kmul = 256.f * p.k_scale[g];
+    vmul = 256.f * p.v_scale[g];
+  }
+  const float score_mul = p.scale_log2 * kmul;
 
   const int32_t* tab = p.tables + int64_t(it.seq) * p.table_stride + it.t_begin / kBlock;
   const char* kbase = p.pool_k + int64_t(g) * p.p_head;
@@ -502,8 +682,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   float m = -INFINITY;  // running max (log2 domain), uniform over the head's lanes
   float l = 0.f;        // this lane's share of the running sum
 
-  uint4 kbuf[DEPTH][S];
-  uint2 vbuf[DEPTH][NT];
+  uint4 kbuf[DEPTH][SL];
+  uint2 vbuf[DEPTH][NT];   // fp8: only .x holds the 4 codes
   bool okbuf[DEPTH];
 
   auto issue = [&](int j, int d) {
@@ -514,9 +694,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
     const char* kp = kbase + int64_t(blk) * p.p_block;
     const char* vp = vbase + int64_t(blk) * p.p_block;
 #pragma unroll
-    for (int s = 0; s < S; ++s) kbuf[d][s] = ld16_stream(kp + (64 * s + lane) * 16);
+    for (int s = 0; s < SL; ++s) kbuf[d][s] = ld16_stream(kp + (64 * s + lane) * 16);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) vbuf[d][n] = ld8_stream(vp + (16 * n + row) * 32 + grp * 8);
+    for (int n = 0; n < NT; ++n) {
+      if constexpr (FP8) vbuf[d][n].x = ld4_stream(vp + (16 * n + row) * 16 + grp * 4);
+      else vbuf[d][n] = ld8_stream(vp + (16 * n + row) * 32 + grp * 8);
+    }
   };
 
 #pragma unroll
@@ -529,11 +712,23 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
       const int j = j0 + d;
       if (j < nj) {
         f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (FP8) {
 #pragma unroll
-        for (int s = 0; s < S; ++s) sc = Mfma<DT>::qk(kbuf[d][s], qreg[s], sc);
+          for (int s = 0; s < SL; ++s) {
+            const uint4 w = kbuf[d][s];
+            const uint2 a0 = e4m3x4_to_f16x4_div256(w.x), a1 = e4m3x4_to_f16x4_div256(w.y);
+            const uint2 a2 = e4m3x4_to_f16x4_div256(w.z), a3 = e4m3x4_to_f16x4_div256(w.w);
+            sc = Mfma<OT>::qk(make_uint4(a0.x, a0.y, a1.x, a1.y), qreg[2 * s], sc);
+            sc = Mfma<OT>::qk(make_uint4(a2.x, a2.y, a3.x, a3.y), qreg[2 * s + 1], sc);
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < S; ++s) sc = Mfma<OT>::qk(kbuf[d][s], qreg[s], sc);
+        }
         uint2 vcur[NT];
 #pragma unroll
-        for (int n = 0; n < NT; ++n) vcur[n] = vbuf[d][n];
+        for (int n = 0; n < NT; ++n)
+          vcur[n] = FP8 ? e4m3x4_to_f16x4_div256(vbuf[d][n].x) : vbuf[d][n];
         const bool blk_ok = okbuf[d];
         if (j + DEPTH < nj) issue(j + DEPTH, d);
 
@@ -558,7 +753,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const bool live = blk_ok && (4 * grp + r) < valid;
-          s4[r] = live ? sc[r] * p.scale_log2 : -INFINITY;
+          s4[r] = live ? sc[r] * score_mul : -INFINITY;
           mx = fmaxf(mx, s4[r]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -582,15 +777,15 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
         }
         uint16_t ph[4], pl[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Mfma<DT>::split(pr[r], ph[r], pl[r]);
+        for (int r = 0; r < 4; ++r) Mfma<OT>::split(pr[r], ph[r], pl[r]);
         const uint2 bh = make_uint2(uint32_t(ph[0]) | (uint32_t(ph[1]) << 16),
                                     uint32_t(ph[2]) | (uint32_t(ph[3]) << 16));
         const uint2 bl = make_uint2(uint32_t(pl[0]) | (uint32_t(pl[1]) << 16),
                                     uint32_t(pl[2]) | (uint32_t(pl[3]) << 16));
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          acc[n] = Mfma<DT>::pv(vcur[n], bh, acc[n]);
-          acc[n] = Mfma<DT>::pv(vcur[n], bl, acc[n]);
+          acc[n] = Mfma<OT>::pv(vcur[n], bh, acc[n]);
+          acc[n] = Mfma<OT>::pv(vcur[n], bl, acc[n]);
         }
       }
     }
@@ -642,7 +837,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   for (int n = 0; n < NT; ++n) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      store_head_result(p, it, hq, 16 * n + 4 * grp + r, acc[n][r], m, l,
+      store_head_result(p, it, hq, 16 * n + 4 * grp + r, acc[n][r] * vmul, m, l,
                         n == 0 && r == 0 && grp == 0, D);
   }
 }
@@ -811,6 +1006,10 @@ __global__ __launch_bounds__(256) void bw_probe_kernel(const u32x4_t* src, size_
   if (a.x == 0x12345678u && a.y == 0x9abcdef0u) sink[0] = a;
 }
 
+int elem_size(int dtype) {
+  return dtype == PKV_F32 ? 4 : dtype == PKV_FP8E4M3 ? 1 : 2;
+}
+
 template <typename K, typename P>
 hipError_t launch(K kernel, dim3 grid, dim3 block, hipStream_t stream, const P& params) {
   hipLaunchKernelGGL(kernel, grid, block, 0, stream, params);
@@ -825,7 +1024,8 @@ hipError_t launch(K kernel, dim3 grid, dim3 block, hipStream_t stream, const P& 
 hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, const InjectDesc* d_desc,
                          int n_desc, int layer_begin, int layer_end, int rope_mode,
                          const float* d_cos, const float* d_sin, hipStream_t stream) {
-  const int eb = pool.dtype == PKV_F32 ? 4 : 2;
+  const int eb = elem_size(pool.dtype);
+  const int sb = elem_size(src.dtype);
   InjectParams p;
   p.pool_k = static_cast<char*>(pool.k);
   p.pool_v = static_cast<char*>(pool.v);
@@ -833,10 +1033,12 @@ hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, const InjectD
   p.p_block = pool.block_stride * eb;
   p.p_head = pool.head_stride * eb;
   p.n_kv_heads = pool.n_kv_heads;
+  p.k_scale = pool.k_scale;
+  p.v_scale = pool.v_scale;
   p.src_k = static_cast<const char*>(src.k);
   p.src_v = static_cast<const char*>(src.v);
-  p.s_layer = src.layer_stride * eb;
-  p.s_token = src.token_stride * eb;
+  p.s_layer = src.layer_stride * sb;
+  p.s_token = src.token_stride * sb;
   p.descs = d_desc;
   p.layer_begin = layer_begin;
   p.layer_end = layer_end;
@@ -857,22 +1059,25 @@ hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, const InjectD
   // KV heads per pass: V tiles of 16 KiB (4 heads of d=128 bf16) by default.
   int hg = 4;
   if (const char* env = std::getenv("PKV_INJECT_HEADS")) hg = std::atoi(env) == 8 ? 8 : 4;
-#define PKV_INJ(DT, DD, H) \
-  if (pool.dtype == DT && pool.head_dim == DD && hg == H) \
-    return launch(inject_rope_kernel<DT, DD, H>, grid, block, stream, p);
-#define PKV_INJ_H(DT, DD) PKV_INJ(DT, DD, 4) PKV_INJ(DT, DD, 8)
-  PKV_INJ_H(PKV_F32, 64) PKV_INJ_H(PKV_F32, 128) PKV_INJ_H(PKV_BF16, 64)
-  PKV_INJ_H(PKV_BF16, 128) PKV_INJ_H(PKV_F16, 64) PKV_INJ_H(PKV_F16, 128)
+#define PKV_INJ(SDT, PDT, DD, H) \
+  if (src.dtype == SDT && pool.dtype == PDT && pool.head_dim == DD && hg == H) \
+    return launch(inject_rope_kernel<SDT, PDT, DD, H>, grid, block, stream, p);
+#define PKV_INJ_H(SDT, PDT, DD) PKV_INJ(SDT, PDT, DD, 4) PKV_INJ(SDT, PDT, DD, 8)
+#define PKV_INJ_D(SDT, PDT) PKV_INJ_H(SDT, PDT, 64) PKV_INJ_H(SDT, PDT, 128)
+  PKV_INJ_D(PKV_F32, PKV_F32) PKV_INJ_D(PKV_BF16, PKV_BF16) PKV_INJ_D(PKV_F16, PKV_F16)
+  PKV_INJ_D(PKV_BF16, PKV_FP8E4M3) PKV_INJ_D(PKV_F16, PKV_FP8E4M3)
 #undef PKV_INJ
 #undef PKV_INJ_H
+#undef PKV_INJ_D
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_append(const pkv_pool& pool, int layer, const int32_t* d_tables,
                          int table_stride, const int32_t* d_first_pos, int n_seqs, int n_new,
-                         const void* d_k, const void* d_v, int rope_mode, const float* d_cos,
-                         const float* d_sin, int max_pos, hipStream_t stream) {
-  const int eb = pool.dtype == PKV_F32 ? 4 : 2;
+                         const void* d_k, const void* d_v, int new_dtype, int rope_mode,
+                         const float* d_cos, const float* d_sin, int max_pos,
+                         hipStream_t stream) {
+  const int eb = elem_size(pool.dtype);
   AppendParams p;
   p.pool_k = static_cast<char*>(pool.k);
   p.pool_v = static_cast<char*>(pool.v);
@@ -880,6 +1085,8 @@ hipError_t launch_append(const pkv_pool& pool, int layer, const int32_t* d_table
   p.p_block = pool.block_stride * eb;
   p.p_head = pool.head_stride * eb;
   p.n_kv_heads = pool.n_kv_heads;
+  p.k_scale = pool.k_scale;
+  p.v_scale = pool.v_scale;
   p.num_blocks = pool.num_blocks;
   p.layer = layer;
   p.tables = d_tables;
@@ -894,17 +1101,20 @@ hipError_t launch_append(const pkv_pool& pool, int layer, const int32_t* d_table
   p.max_pos = max_pos;
   dim3 grid(int64_t(n_seqs) * n_new);
   dim3 block(256);
-#define PKV_APP(DT, DD) \
-  if (pool.dtype == DT && pool.head_dim == DD) return launch(append_kv_kernel<DT, DD>, grid, block, stream, p);
-  PKV_APP(PKV_F32, 64) PKV_APP(PKV_F32, 128) PKV_APP(PKV_BF16, 64) PKV_APP(PKV_BF16, 128)
-  PKV_APP(PKV_F16, 64) PKV_APP(PKV_F16, 128)
+#define PKV_APP(SDT, PDT, DD) \
+  if (new_dtype == SDT && pool.dtype == PDT && pool.head_dim == DD) \
+    return launch(append_kv_kernel<SDT, PDT, DD>, grid, block, stream, p);
+#define PKV_APP_D(SDT, PDT) PKV_APP(SDT, PDT, 64) PKV_APP(SDT, PDT, 128)
+  PKV_APP_D(PKV_F32, PKV_F32) PKV_APP_D(PKV_BF16, PKV_BF16) PKV_APP_D(PKV_F16, PKV_F16)
+  PKV_APP_D(PKV_BF16, PKV_FP8E4M3) PKV_APP_D(PKV_F16, PKV_FP8E4M3)
 #undef PKV_APP
+#undef PKV_APP_D
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
                          int kernel_variant, hipStream_t stream) {
-  const int eb = pool.dtype == PKV_F32 ? 4 : 2;
+  const int eb = elem_size(pool.dtype);
   DecodeParams p;
   p.pool_k = static_cast<const char*>(pool.k) + int64_t(layer) * pool.layer_stride * eb;
   p.pool_v = static_cast<const char*>(pool.v) + int64_t(layer) * pool.layer_stride * eb;
@@ -924,35 +1134,38 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
   p.part_ml = a.part_ml;
   p.out = a.out;
   p.lse = a.lse;
+  p.k_scale = pool.k_scale ? pool.k_scale + int64_t(layer) * pool.n_kv_heads : nullptr;
+  p.v_scale = pool.v_scale ? pool.v_scale + int64_t(layer) * pool.n_kv_heads : nullptr;
   hipError_t e = hipSuccess;
   if (a.n_items > 0) {
     dim3 grid(a.n_items, pool.n_kv_heads);
-    // variant: 0 automatic, 1 generic VALU kernel, 10 + k MFMA kernel with a
-    // prefetch depth of k blocks (k = 1..4).
-    const bool mfma = kernel_variant != 1 && pool.dtype != PKV_F32 && p.group <= 16;
+    // variant: 0 automatic, 1 generic VALU kernel (not for fp8 pools), 10 + k
+    // MFMA kernel with a prefetch depth of k blocks (k = 1, 2).
+    const bool mfma = (kernel_variant != 1 || pool.dtype == PKV_FP8E4M3) &&
+                      pool.dtype != PKV_F32 && p.group <= 16;
     // One block in flight per wave measured fastest with 8 waves per workgroup.
-    const int depth = kernel_variant >= 11 && kernel_variant <= 14 ? kernel_variant - 10 : 1;
+    const int depth = kernel_variant == 12 ? 2 : 1;
     const int nw = a.waves;
     bool launched = false;
-#define PKV_DEC_MFMA(DT, DD, DEP, W)                                                         \
-    if (!launched && mfma && pool.dtype == DT && pool.head_dim == DD && depth == DEP &&      \
-        nw == W) {                                                                           \
-      e = launch(decode_mfma_kernel<DT, DD, DEP, W>, grid, dim3(64 * W), stream, p);         \
+#define PKV_DEC_MFMA(KV, Q, DD, DEP, W)                                                      \
+    if (!launched && mfma && pool.dtype == KV && a.q_dtype == Q && pool.head_dim == DD &&    \
+        depth == DEP && nw == W) {                                                           \
+      e = launch(decode_mfma_kernel<KV, Q, DD, DEP, W>, grid, dim3(64 * W), stream, p);      \
       launched = true;                                                                       \
     }
-#define PKV_DEC_MFMA_W(DT, DD, DEP) \
-    PKV_DEC_MFMA(DT, DD, DEP, 1) PKV_DEC_MFMA(DT, DD, DEP, 2) PKV_DEC_MFMA(DT, DD, DEP, 4) \
-    PKV_DEC_MFMA(DT, DD, DEP, 8)
-#define PKV_DEC_MFMA_ALL(DT, DD) \
-    PKV_DEC_MFMA_W(DT, DD, 1) PKV_DEC_MFMA_W(DT, DD, 2) PKV_DEC_MFMA_W(DT, DD, 3) \
-    PKV_DEC_MFMA_W(DT, DD, 4)
+#define PKV_DEC_MFMA_W(KV, Q, DD, DEP) \
+    PKV_DEC_MFMA(KV, Q, DD, DEP, 1) PKV_DEC_MFMA(KV, Q, DD, DEP, 2) \
+    PKV_DEC_MFMA(KV, Q, DD, DEP, 4) PKV_DEC_MFMA(KV, Q, DD, DEP, 8)
+#define PKV_DEC_MFMA_ALL(KV, Q) \
+    PKV_DEC_MFMA_W(KV, Q, 64, 1) PKV_DEC_MFMA_W(KV, Q, 64, 2) \
+    PKV_DEC_MFMA_W(KV, Q, 128, 1) PKV_DEC_MFMA_W(KV, Q, 128, 2)
 #define PKV_DEC_VALU(DT, DD)                                                                 \
     if (!launched && pool.dtype == DT && pool.head_dim == DD) {                              \
       e = launch(decode_valu_kernel<DT, DD>, grid, dim3(64), stream, p);                     \
       launched = true;                                                                       \
     }
-    PKV_DEC_MFMA_ALL(PKV_BF16, 64) PKV_DEC_MFMA_ALL(PKV_BF16, 128)
-    PKV_DEC_MFMA_ALL(PKV_F16, 64) PKV_DEC_MFMA_ALL(PKV_F16, 128)
+    PKV_DEC_MFMA_ALL(PKV_BF16, PKV_BF16) PKV_DEC_MFMA_ALL(PKV_F16, PKV_F16)
+    PKV_DEC_MFMA_ALL(PKV_FP8E4M3, PKV_BF16) PKV_DEC_MFMA_ALL(PKV_FP8E4M3, PKV_F16)
     PKV_DEC_VALU(PKV_F32, 64) PKV_DEC_VALU(PKV_F32, 128) PKV_DEC_VALU(PKV_BF16, 64)
     PKV_DEC_VALU(PKV_BF16, 128) PKV_DEC_VALU(PKV_F16, 64) PKV_DEC_VALU(PKV_F16, 128)
 #undef PKV_DEC_MFMA

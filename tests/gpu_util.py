@@ -10,7 +10,7 @@ from oracle.layout import PoolSpec
 
 ATOL = 1e-3
 RTOL = 2e-3
-ELEM = {"f32": 4, "bf16": 2, "f16": 2}
+ELEM = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1}
 
 
 def say(*a):
@@ -20,13 +20,15 @@ def say(*a):
 
 def torch_dtype(dtype):
     import torch
-    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
+            "fp8": torch.uint8}[dtype]
 
 
 def raw_view(t):
-    """numpy raw view of a CPU tensor: float32, or uint16 bits for 16-bit types."""
+    """numpy raw view of a CPU tensor: float32, uint16 bits for 16-bit types,
+    uint8 codes for fp8."""
     import torch
-    if t.dtype == torch.float32:
+    if t.dtype in (torch.float32, torch.uint8):
         return t.numpy()
     return t.view(torch.int16).numpy().view(np.uint16)
 
@@ -37,6 +39,8 @@ def to_device_raw(arr, dtype, device="cuda"):
     a = np.ascontiguousarray(arr)
     if dtype == "f32":
         return torch.from_numpy(a.astype(np.float32)).to(device)
+    if dtype == "fp8":
+        return torch.from_numpy(a.astype(np.uint8)).to(device)
     t = torch.from_numpy(a.view(np.int16)).to(device)
     return t.view(torch_dtype(dtype))
 
@@ -57,8 +61,11 @@ class DevicePool:
         self.v_off = n_kv_heads * plane
         self.total = n_layers * self.layer_stride
         self.buf = torch.empty(self.total, dtype=torch_dtype(dtype), device=device)
+        self.k_scale = self.v_scale = None        # float32 [layers][heads] (fp8 pools)
         if fill_bits is not None:
-            if dtype == "f32":
+            if dtype == "fp8":
+                self.buf.fill_(int(fill_bits) & 0xFF)
+            elif dtype == "f32":
                 self.buf.view(torch.int32).fill_(int(np.int32(np.uint32(fill_bits))))
             else:
                 self.buf.view(torch.int16).fill_(int(np.int16(np.uint16(fill_bits))))
@@ -69,7 +76,9 @@ class DevicePool:
         return pkv.pkv_pool(self.n_layers - layer_offset, self.num_blocks, self.n_kv_heads,
                             self.head_dim, pkv.DTYPE_CODES[self.dtype], 0, base,
                             base + self.v_off * e, self.layer_stride, self.block_stride,
-                            self.head_stride)
+                            self.head_stride,
+                            None if self.k_scale is None else self.k_scale.data_ptr(),
+                            None if self.v_scale is None else self.v_scale.data_ptr())
 
     def spec(self):
         return PoolSpec(self.n_layers, self.num_blocks, self.n_kv_heads, self.head_dim,
@@ -78,6 +87,12 @@ class DevicePool:
     def host_copy(self):
         """Raw numpy copy of the whole buffer."""
         return raw_view(self.buf.cpu()).copy()
+
+    def set_scales(self, k_scale, v_scale):
+        """Per-(layer, KV head) float32 scales of an fp8 pool (host arrays)."""
+        import torch
+        self.k_scale = torch.from_numpy(np.ascontiguousarray(k_scale, np.float32)).cuda()
+        self.v_scale = torch.from_numpy(np.ascontiguousarray(v_scale, np.float32)).cuda()
 
     def oracle_arrays(self, flat):
         """(k_pool, v_pool) views of one flat buffer, as the oracle indexes them."""
@@ -99,7 +114,7 @@ def host_planes_for(dp: DevicePool, layer, tables, seqs, heads):
     from per-block device slices, so huge pools can be sampled cheaply.
     """
     import torch
-    flat = np.zeros(dp.total, dtype=np.float32 if dp.dtype == "f32" else np.uint16)
+    flat = np.zeros(dp.total, dtype={"f32": np.float32, "fp8": np.uint8}.get(dp.dtype, np.uint16))
     blocks = sorted({int(b) for s in seqs for b in tables[s] if b >= 0})
     idx = torch.tensor(blocks, dtype=torch.long, device=dp.buf.device)
     view = dp.buf[layer * dp.layer_stride:(layer + 1) * dp.layer_stride].view(
@@ -148,7 +163,7 @@ def workspace(n_bytes):
 
 
 def decode(dp: DevicePool, layer, q_dev, tables_dev, lens, n_q_heads, part_tokens=0,
-           with_lse=True):
+           with_lse=True, q_dtype=None):
     """Plan + upload + decode one layer; returns (out, lse) device tensors."""
     import torch
     plan = pkv.pkv_decode_plan_create(lens, n_q_heads, dp.n_kv_heads, dp.head_dim, part_tokens)
@@ -158,7 +173,8 @@ def decode(dp: DevicePool, layer, q_dev, tables_dev, lens, n_q_heads, part_token
         b = len(lens)
         out = torch.full((b, n_q_heads, dp.head_dim), float("nan"), device="cuda")
         lse = torch.full((b, n_q_heads), float("nan"), device="cuda") if with_lse else None
-        pkv.pkv_decode_attention(plan, dp.desc(), layer, q_dev, tables_dev, out, lse, ws)
+        pkv.pkv_decode_attention(plan, dp.desc(), layer, q_dev, tables_dev, out, lse, ws,
+                                 q_dtype=q_dtype)
         torch.cuda.synchronize()
     finally:
         pkv.pkv_decode_plan_destroy(plan)

@@ -30,7 +30,9 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(pkv.SIGNATURES), set(names) ^ set(pkv.SIGNATURES)
-    assert pkv.pkv_abi_version() == 1
+    header = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    version = int(re.search(r"#define PKV_ABI_VERSION (\d+)", header).group(1))
+    assert pkv.pkv_abi_version() == version
 
 
 def test_kv_bytes_matches_closed_form():
@@ -160,7 +162,7 @@ def test_inject_host_validation_errors():
     fake device pointers below are never dereferenced)."""
     fake = 1 << 20
     pool = pkv.pkv_pool(1, 8, 2, 64, pkv.PKV_BF16, 0, fake, fake + 4096, 8 * 4096, 4096, 1024)
-    src = pkv.pkv_src(fake, fake, 0, 128, 64)
+    src = pkv.pkv_src(fake, fake, 0, 128, 64, pkv.PKV_BF16)
     c = pkv.pkv_cache_create(8, 2, 4)
     pkv.pkv_alloc_blocks(c, 0, 40)
     cases = [([(0, 4, 0, 0), (0, 4, 2, 10)], "OVERLAP"), ([(0, 10, 40, 0)], "RANGE"),
@@ -173,6 +175,22 @@ def test_inject_host_validation_errors():
     bad_pool = pkv.pkv_pool(1, 8, 2, 96, pkv.PKV_BF16, 0, fake, fake, 0, 0, 0)
     with pytest.raises(pkv.PkvError) as e:
         pkv.pkv_inject(c, bad_pool, src, [(0, 1, 0, 0)], 0, 1, "pairs", fake, fake, 100, None,
+                       stream=0)
+    assert e.value.code == "UNSUPPORTED"
+    no_scales = pkv.pkv_pool(1, 8, 2, 64, pkv.PKV_FP8E4M3, 0, fake, fake, 0, 2048, 1024)
+    with pytest.raises(pkv.PkvError) as e:       # an fp8 pool needs its scales
+        pkv.pkv_inject(c, no_scales, src, [(0, 1, 0, 0)], 0, 1, "pairs", fake, fake, 100, None,
+                       stream=0)
+    assert e.value.code == "INVALID"
+    fp8_pool = pkv.pkv_pool(1, 8, 2, 64, pkv.PKV_FP8E4M3, 0, fake, fake, 0, 2048, 1024, fake, fake)
+    f32_src = pkv.pkv_src(fake, fake, 0, 128, 64, pkv.PKV_F32)
+    with pytest.raises(pkv.PkvError) as e:       # f32 sources are not quantised
+        pkv.pkv_inject(c, fp8_pool, f32_src, [(0, 1, 0, 0)], 0, 1, "pairs", fake, fake, 100,
+                       None, stream=0)
+    assert e.value.code == "UNSUPPORTED"
+    f16_src = pkv.pkv_src(fake, fake, 0, 128, 64, pkv.PKV_F16)
+    with pytest.raises(pkv.PkvError) as e:       # a bf16 pool takes bf16 sources only
+        pkv.pkv_inject(c, pool, f16_src, [(0, 1, 0, 0)], 0, 1, "pairs", fake, fake, 100, None,
                        stream=0)
     assert e.value.code == "UNSUPPORTED"
     misaligned = pkv.pkv_pool(1, 8, 2, 64, pkv.PKV_BF16, 0, fake + 2, fake, 0, 4096, 1024)
