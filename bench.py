@@ -226,7 +226,9 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None):
                bytes_per_step=per_launch * cfg.n_layers, bytes_per_launch=per_launch,
                launch_ms_avg=float(np.mean(launch_ms)), launch_ms_p50=float(np.median(launch_ms)),
                launches_timed=len(launch_ms),
-               n_items=n_items, part_tokens=part_tokens, waves=waves, workload=cfg.workload,
+               n_items=n_items, part_tokens=part_tokens, waves=waves,
+               workload=cfg.workload + (" (fp8 E4M3 cache)" if fp8 else ""),
+               dtype="fp8e4m3" if fp8 else cfg.dtype,
                batch=cfg.batch, context=int(lens.max()), layers=cfg.n_layers)
     res["value"] = res["bytes_per_step"] / (ms_step * 1e-3) / 1e9
     res["launch_gbps"] = per_launch / (res["launch_ms_avg"] * 1e-3) / 1e9
@@ -376,7 +378,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": dec["dtype"],
         "data": "synthetic",
         "pct_of_peak": round(100 * dec["value"] / PEAK_HBM_GBPS, 2),
         "config": {"workload": dec["workload"], "batch": dec["batch"], "context": dec["context"],

@@ -603,18 +603,16 @@ template <> struct Mfma<PKV_F16> {
   }
 };
 
-// fp8 (E4M3) codes as float16 bit patterns worth exactly 2^-8 of their value:
-// the sign moves to bit 15 and the 7 exponent+mantissa bits to bits 13..7,
-// which rebases the exponent from bias 7 to bias 15 (subnormals included).
-// Two codes (low bytes of `t`, one per 16-bit half) per call.
-__device__ inline uint32_t e4m3x2_to_f16x2_div256(uint32_t t) {
-  return ((t & 0x007F007Fu) << 7) | ((t & 0x00800080u) << 8);
-}
-// Four codes in a dword -> four float16 values (x: codes 0,1; y: codes 2,3).
-__device__ inline uint2 e4m3x4_to_f16x4_div256(uint32_t w) {
-  const uint32_t lo = (w & 0xFFu) | ((w & 0xFF00u) << 8);
-  const uint32_t hi = ((w >> 16) & 0xFFu) | ((w >> 8) & 0xFF0000u);
-  return make_uint2(e4m3x2_to_f16x2_div256(lo), e4m3x2_to_f16x2_div256(hi));
+// Four fp8 (OCP E4M3) codes of a dword -> their exact float16 values
+// (x: codes 0, 1; y: codes 2, 3).  CDNA4's packed conversion with a unit
+// scale is exact for every code (E4M3 values are a subset of float16's),
+// NaN included; the per-(layer, head) scales are applied to the scores and
+// the output instead.
+__device__ inline uint2 e4m3x4_to_f16x4(uint32_t w) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  const f16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
 // Decode kernel template parameters: KVDT the pool format, QDT the query
@@ -664,8 +662,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   }
   float kmul = 1.f, vmul = 1.f;
   if constexpr (FP8) {
-    kmul = 256.f * p.k_scale[g];
-    vmul = 256.f * p.v_scale[g];
+    kmul = p.k_scale[g];
+    vmul = p.v_scale[g];
   }
   const float score_mul = p.scale_log2 * kmul;
 
@@ -716,8 +714,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
           for (int s = 0; s < SL; ++s) {
             const uint4 w = kbuf[d][s];
-            const uint2 a0 = e4m3x4_to_f16x4_div256(w.x), a1 = e4m3x4_to_f16x4_div256(w.y);
-            const uint2 a2 = e4m3x4_to_f16x4_div256(w.z), a3 = e4m3x4_to_f16x4_div256(w.w);
+            const uint2 a0 = e4m3x4_to_f16x4(w.x), a1 = e4m3x4_to_f16x4(w.y);
+            const uint2 a2 = e4m3x4_to_f16x4(w.z), a3 = e4m3x4_to_f16x4(w.w);
             sc = Mfma<OT>::qk(make_uint4(a0.x, a0.y, a1.x, a1.y), qreg[2 * s], sc);
             sc = Mfma<OT>::qk(make_uint4(a2.x, a2.y, a3.x, a3.y), qreg[2 * s + 1], sc);
           }
@@ -728,7 +726,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
         uint2 vcur[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n)
-          vcur[n] = FP8 ? e4m3x4_to_f16x4_div256(vbuf[d][n].x) : vbuf[d][n];
+          vcur[n] = FP8 ? e4m3x4_to_f16x4(vbuf[d][n].x) : vbuf[d][n];
         const bool blk_ok = okbuf[d];
         if (j + DEPTH < nj) issue(j + DEPTH, d);
 

@@ -176,3 +176,46 @@ def test_fp8_inject_then_decode_tracks_bf16_path():
         pkv.pkv_cache_destroy(cache)
     err = np.abs(outs[0] - outs[1])
     assert np.max(err) < 0.05 and np.mean(err) < 0.01, (np.max(err), np.mean(err))
+
+
+def test_fp8_nan_codes_in_unused_slots_do_not_leak():
+    """Slots past each sequence's end and blocks no table names hold the NaN
+    code; the decode output depends only on the live slots."""
+    import torch
+    from oracle import attention as o_att
+    from oracle.layout import k_element_offsets, v_element_offsets
+    from tests import gpu_util as gu
+    from workloads.configs import host_normal, deal_tables
+
+    rng = np.random.default_rng(4242)
+    hq, hkv, d = 32, 8, 128
+    lens = np.array([1, 15, 17, 31, 300, 0, 129], dtype=np.int64)
+    need = int(sum(-(-x // 16) for x in lens))
+    nb = need + 3
+    table = deal_tables(rng.permutation(nb)[:need].astype(np.int32), lens, 32)
+    dp = gu.DevicePool(1, nb, hkv, d, "fp8")
+    ks, vs = scales(rng, 1, hkv)
+    dp.set_scales(ks, vs)
+    codes = rng.integers(0, 0x60, size=dp.total, dtype=np.uint8)
+    codes |= (rng.integers(0, 2, size=dp.total, dtype=np.uint8) << 7).astype(np.uint8)
+    live = np.zeros(dp.total, dtype=bool)
+    kp, vp = dp.oracle_arrays(codes)
+    spec = dp.spec()
+    for b, n in enumerate(lens):
+        for p in range(int(n)):
+            blk = int(table[b][p // 16])
+            for h in range(hkv):
+                live[k_element_offsets(spec, 0, blk, h, p % 16)] = True
+                live[dp.v_off + v_element_offsets(spec, 0, blk, h, p % 16)] = True
+    codes[~live] = np.where(rng.integers(0, 2, size=int((~live).sum())) == 1, 0xFF, 0x7F)
+    dp.buf.copy_(gu.to_device_raw(codes, "fp8"))
+    q = host_normal(rng, (len(lens), hq, d), "bf16")
+    ref, ref_lse = o_att.decode_paged(q, kp, vp, spec, 0, [list(r) for r in table], lens, hq,
+                                      by_plane=True, q_dtype="bf16", k_scale=ks, v_scale=vs)
+    assert np.all(np.isfinite(ref))
+    q_dev = gu.to_device_raw(q.reshape(-1), "bf16").view(q.shape)
+    tdev = torch.from_numpy(table).cuda()
+    for part in (0, 16, 64):
+        out, lse = gu.decode(dp, 0, q_dev, tdev, lens, hq, part, q_dtype="bf16")
+        gu.assert_close(out.cpu().numpy(), ref, "fp8 NaN-canary out part=%d" % part)
+        gu.assert_close(lse.cpu().numpy(), ref_lse, "fp8 NaN-canary lse part=%d" % part)
