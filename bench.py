@@ -55,14 +55,17 @@ def recorded_traffic(kernel="decode_mfma_kernel"):
 POOL_LAYOUT = os.environ.get("PKV_BENCH_LAYOUT", "block")
 
 
-def device_pool_fp8(n_layers, num_blocks, n_kv_heads, head_dim, seed, scale=0.01):
-    """fp8 (E4M3) pool of random finite codes, [layer][block][K | V planes],
-    with one K and one V scale per (layer, KV head)."""
+def device_pool_fp8(n_layers, num_blocks, n_kv_heads, head_dim, seed, scale=0.01, layout=None):
+    """fp8 (E4M3) pool of random finite codes with one K and one V scale per
+    (layer, KV head); layouts as in device_pool."""
     import torch
     import paged_kv_cache_inject_amd as pkv
+    layout = layout or POOL_LAYOUT
     plane = 16 * head_dim
     block_stride = 2 * n_kv_heads * plane
     layer_stride = num_blocks * block_stride
+    head_stride = 2 * plane if layout == "head" else plane
+    v_off = plane if layout == "head" else n_kv_heads * plane
     buf = torch.empty(n_layers * layer_stride, dtype=torch.uint8, device="cuda")
     g = torch.Generator(device="cuda")
     for layer in range(n_layers):
@@ -75,8 +78,8 @@ def device_pool_fp8(n_layers, num_blocks, n_kv_heads, head_dim, seed, scale=0.01
     ks = torch.full((n_layers, n_kv_heads), scale, dtype=torch.float32, device="cuda")
     vs = torch.full((n_layers, n_kv_heads), scale, dtype=torch.float32, device="cuda")
     desc = pkv.pkv_pool(n_layers, num_blocks, n_kv_heads, head_dim, pkv.PKV_FP8E4M3, 0,
-                        buf.data_ptr(), buf.data_ptr() + n_kv_heads * plane, layer_stride,
-                        block_stride, plane, ks.data_ptr(), vs.data_ptr())
+                        buf.data_ptr(), buf.data_ptr() + v_off, layer_stride,
+                        block_stride, head_stride, ks.data_ptr(), vs.data_ptr())
     return (buf, ks, vs), desc
 
 

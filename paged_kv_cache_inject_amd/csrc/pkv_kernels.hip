@@ -756,22 +756,25 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m, mx);
-        float pr[4];
-        if (m_new == -INFINITY) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pr[r] = 0.f;
-        } else {
-          const float alpha = exp2f(m - m_new);  // 0 when m was -inf
+        // Rescale the running state only when some head's maximum grows (a
+        // wave-uniform test): otherwise the factor would be exactly 1, and
+        // after the first blocks of a long range it rarely grows.
+        const bool grow = mx > m;  // false while both are -inf
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float alpha = grow ? exp2f(m - mx) : 1.f;  // 0 when m was -inf
           l *= alpha;
 #pragma unroll
           for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+          m = fmaxf(m, mx);
+        }
+        // m is -inf only while every score seen so far is masked; then every
+        // s4 is -inf too and its weight must be 0.
+        const float m_ref = m == -INFINITY ? 0.f : m;
+        float pr[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            pr[r] = exp2f(s4[r] - m_new);
-            l += pr[r];
-          }
-          m = m_new;
+        for (int r = 0; r < 4; ++r) {
+          pr[r] = exp2f(s4[r] - m_ref);
+          l += pr[r];
         }
         uint16_t ph[4], pl[4];
 #pragma unroll
