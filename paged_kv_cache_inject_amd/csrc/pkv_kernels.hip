@@ -796,9 +796,11 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   l += __shfl_xor(l, 32);
 
   if constexpr (NW > 1) {
-    // Merge the waves' softmax states (fixed order: wave 0, 1, ..., NW-1).
+    // Merge the waves' softmax states.  Every wave scales its partial output
+    // to the common maximum and parks it in LDS; wave w then sums output
+    // tiles w, w + NW, ... over all waves in fixed order (wave 0, 1, ...).
     __shared__ float sm_m[NW][16], sm_l[NW][16];
-    __shared__ float sm_o[NW - 1][16][D + 4];
+    __shared__ float sm_o[NW][16][D + 4];
     if (grp == 0) {
       sm_m[wave][row] = m;
       sm_l[wave][row] = l;
@@ -814,23 +816,22 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
       big_l += (mw == -INFINITY ? 0.f : exp2f(mw - big_m)) * sm_l[w][row];
     }
     const float own = m == -INFINITY ? 0.f : exp2f(m - big_m);
-    if (wave > 0) {
 #pragma unroll
-      for (int n = 0; n < NT; ++n)
-        *reinterpret_cast<f32x4_t*>(&sm_o[wave - 1][row][16 * n + 4 * grp]) = acc[n] * own;
-    }
+    for (int n = 0; n < NT; ++n)
+      *reinterpret_cast<f32x4_t*>(&sm_o[wave][row][16 * n + 4 * grp]) = acc[n] * own;
     __syncthreads();
-    if (wave > 0) return;
+    if (!head_ok) return;
+    for (int n = wave; n < NT; n += NW) {
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      f32x4_t a = acc[n] * own;
+      for (int w = 0; w < NW; ++w)
+        a += *reinterpret_cast<const f32x4_t*>(&sm_o[w][row][16 * n + 4 * grp]);
 #pragma unroll
-      for (int w = 1; w < NW; ++w)
-        a += *reinterpret_cast<const f32x4_t*>(&sm_o[w - 1][row][16 * n + 4 * grp]);
-      acc[n] = a;
+      for (int r = 0; r < 4; ++r)
+        store_head_result(p, it, hq, 16 * n + 4 * grp + r, a[r] * vmul, big_m, big_l,
+                          n == 0 && r == 0 && grp == 0, D);
     }
-    m = big_m;
-    l = big_l;
+    return;
   }
 
   if (!head_ok) return;
