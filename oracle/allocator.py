@@ -18,6 +18,35 @@ reading taken, which makes the expected table unique:
   that seed;
 * a reservation is all-or-nothing: when the pool cannot cover it, nothing
   changes.
+
+Shared blocks ([KV essay] "Paged attention" and "Prefix caching"; [KV
+management] on beam search, parallel sampling and prefix caching; [Inside
+engines] "Zero-Copy Page Sharing"): a block is an object that several
+sequences may name; it is duplicated only when one of them writes into it,
+and the engine hashes prefixes to find blocks it can reuse, which requires an
+exact match from position 0.  Readings taken:
+
+* every block has a reference count, the number of table entries naming it;
+  it is on the free list exactly when the count is 0; freeing a sequence
+  decrements its blocks in table order and appends those reaching 0 to the
+  free list's tail;
+* ``fork(src, dst)`` gives an empty sequence the table and length of another
+  (every block's count + 1), as beams and parallel samples share a prompt;
+* copy-on-write: before positions of a block whose count exceeds 1 are
+  written (by ``extend`` for the new positions, or by an inject), the writer
+  takes a fresh block from the free list's head, the pair (old, new) is
+  queued, the writer's table entry is replaced and the old block's count
+  drops by one; queued copies take effect, in queue order, before any write;
+  within one call the blocks are handled in order of first touch;
+* prefix cache: the caller names what each position holds by a 64-bit key
+  (a token id for a prompt, the store row for injected memory); a full block
+  is registered under (the block registered for the preceding block or -1,
+  its 16 keys), compared exactly; ``prefix_match`` shares, for an empty
+  sequence, the longest chain of registered blocks from position 0 (taking a
+  block back off the free list when its count was 0); ``prefix_commit``
+  registers a sequence's full blocks; an entry lasts until its block is
+  handed out again by the free list or written in place, and then goes
+  together with every entry registered under it.
 """
 
 from collections import deque
@@ -74,6 +103,11 @@ class AllocatorModel:
         self.free = deque(initial_free_order(num_blocks, seed))
         self.tables = [[] for _ in range(max_seqs)]
         self.lens = [0] * max_seqs
+        self.ref = [0] * num_blocks
+        self.pending = []          # queued copies (src, dst), in order
+        self.entries = {}          # (parent block or -1, 16 keys) -> block
+        self.entry_of = {}         # block -> its (parent, keys)
+        self.children = {}         # block -> blocks registered under it
 
     # -- queries -------------------------------------------------------------
     def _check_seq(self, seq: int):
@@ -107,7 +141,7 @@ class AllocatorModel:
         if need > len(self.free):
             raise AllocError("OOM", "pool exhausted")
         for _ in range(need):
-            self.tables[seq].append(self.free.popleft())
+            self.tables[seq].append(self._pop())
 
     def set_blocks(self, seq: int, ids, length: int):
         """Give an empty sequence an explicit table (ids must all be free)."""
@@ -126,6 +160,9 @@ class AllocatorModel:
             raise AllocError("RANGE", "length exceeds the given blocks")
         taken = set(ids)
         self.free = deque(b for b in self.free if b not in taken)
+        for b in ids:
+            self._forget(b)
+            self.ref[b] = 1
         self.tables[seq] = ids
         self.lens[seq] = int(length)
 
@@ -145,14 +182,24 @@ class AllocatorModel:
             if want > self.max_blocks_per_seq:
                 raise AllocError("RANGE", "more blocks than a table row holds")
             total += max(0, want - len(self.tables[s]))
+            total += 1 if self._partial_shared(s, n_new) else 0
         if total > len(self.free):
             raise AllocError("OOM", "pool exhausted")
         first = []
         for s in seqs:
+            if self._partial_shared(s, n_new):
+                self._cow(s, self.lens[s] // BLOCK_TOKENS)
             self.alloc_blocks(s, self.lens[s] + n_new)
             first.append(self.lens[s])
             self.lens[s] += n_new
         return first
+
+    def _partial_shared(self, s: int, n_new: int) -> bool:
+        """Will appending to ``s`` write into a block other sequences share?"""
+        ln = self.lens[s]
+        if n_new <= 0 or ln % BLOCK_TOKENS == 0:
+            return False
+        return self.ref[self.tables[s][ln // BLOCK_TOKENS]] > 1
 
     def set_len(self, seq: int, length: int):
         self._check_seq(seq)
@@ -161,17 +208,156 @@ class AllocatorModel:
         self.lens[seq] = int(length)
 
     def free_seq(self, seq: int):
-        """Return a sequence's blocks to the tail of the free list, in order."""
+        """Drop a sequence's references; blocks no longer named by any table
+        go to the tail of the free list, in table order."""
         self._check_seq(seq)
-        self.free.extend(self.tables[seq])
+        for b in self.tables[seq]:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
         self.tables[seq] = []
         self.lens[seq] = 0
 
+    # -- sharing ---------------------------------------------------------------
+    def _pop(self) -> int:
+        """Hand out the free list's head (forgetting what it cached)."""
+        b = self.free.popleft()
+        self._forget(b)
+        self.ref[b] = 1
+        return b
+
+    def _forget(self, b: int):
+        """Drop the prefix entry of ``b`` and every entry registered under it."""
+        stack = [b]
+        while stack:
+            x = stack.pop()
+            key = self.entry_of.pop(x, None)
+            if key is not None:
+                del self.entries[key]
+                if key[0] >= 0:
+                    self.children.get(key[0], set()).discard(x)
+            stack.extend(sorted(self.children.pop(x, ())))
+
+    def _cow(self, seq: int, idx: int):
+        """Give ``seq`` a private copy of its ``idx``-th block."""
+        old = self.tables[seq][idx]
+        new = self._pop()
+        self.pending.append((old, new))
+        self.tables[seq][idx] = new
+        self.ref[old] -= 1
+
+    def fork(self, src: int, dst: int):
+        """``dst`` (empty) shares every block of ``src``, with its length."""
+        self._check_seq(src)
+        self._check_seq(dst)
+        if src == dst or self.tables[dst] or self.lens[dst]:
+            raise AllocError("INVALID", "fork needs a distinct, empty destination")
+        for b in self.tables[src]:
+            self.ref[b] += 1
+        self.tables[dst] = list(self.tables[src])
+        self.lens[dst] = self.lens[src]
+
+    def prepare_inject(self, runs):
+        """Copy-on-write for the destination blocks of an inject call.
+
+        ``runs`` are (seq, n, dst_pos, src_token); every destination must lie
+        inside the sequence's blocks (checked by the inject itself).  Blocks
+        are handled in order of first touch (runs in order, positions
+        ascending): a shared block is copied, a cached private block loses its
+        prefix entry.  All-or-nothing on OOM.
+        """
+        order, seen = [], set()
+        for (seq, n, p0, _) in runs:
+            self._check_seq(seq)
+            for p in range(int(p0), int(p0) + int(n)):
+                key = (int(seq), p // BLOCK_TOKENS)
+                if key not in seen:
+                    seen.add(key)
+                    order.append(key)
+        for (seq, idx) in order:
+            if idx >= len(self.tables[seq]):
+                raise AllocError("RANGE", "destination beyond the reserved blocks")
+        need = sum(1 for (seq, idx) in order if self.ref[self.tables[seq][idx]] > 1)
+        if need > len(self.free):
+            raise AllocError("OOM", "pool exhausted")
+        for (seq, idx) in order:
+            b = self.tables[seq][idx]
+            if self.ref[b] > 1:
+                self._cow(seq, idx)
+            else:
+                self._forget(b)
+
+    def take_pending(self):
+        """The queued copies, in order; the queue is emptied."""
+        out, self.pending = self.pending, []
+        return out
+
+    # -- prefix cache ------------------------------------------------------------
+    @staticmethod
+    def _block_keys(keys, i):
+        return tuple(int(k) & _MASK for k in keys[i * BLOCK_TOKENS:(i + 1) * BLOCK_TOKENS])
+
+    def prefix_match(self, seq: int, keys) -> int:
+        """Share the longest registered chain matching ``keys`` from position 0
+        with the empty sequence ``seq``; returns the matched token count."""
+        self._check_seq(seq)
+        if self.tables[seq] or self.lens[seq]:
+            raise AllocError("INVALID", "prefix match needs an empty sequence")
+        full = min(len(keys) // BLOCK_TOKENS, self.max_blocks_per_seq)
+        parent = -1
+        for i in range(full):
+            b = self.entries.get((parent, self._block_keys(keys, i)))
+            if b is None:
+                break
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+            self.tables[seq].append(b)
+            parent = b
+        self.lens[seq] = len(self.tables[seq]) * BLOCK_TOKENS
+        return self.lens[seq]
+
+    def prefix_commit(self, seq: int, keys):
+        """Register the full blocks of ``seq`` covered by ``keys``."""
+        self._check_seq(seq)
+        if len(keys) > self.lens[seq]:
+            raise AllocError("RANGE", "more keys than the sequence holds")
+        full = len(keys) // BLOCK_TOKENS
+        plan, parent = [], -1
+        for i in range(full):
+            b = self.tables[seq][i]
+            key = (parent, self._block_keys(keys, i))
+            have = self.entries.get(key)
+            if have is not None:
+                parent = have
+                continue
+            if b in self.entry_of:
+                raise AllocError("INVALID", "block %d already caches other content" % b)
+            plan.append((key, b))
+            parent = b
+        for key, b in plan:
+            self.entries[key] = b
+            self.entry_of[b] = key
+            if key[0] >= 0:
+                self.children.setdefault(key[0], set()).add(b)
+
     # -- invariants ------------------------------------------------------------
     def check_invariants(self):
-        owned = [b for t in self.tables for b in t]
-        assert len(owned) == len(set(owned)), "a block is owned twice"
-        assert not (set(owned) & set(self.free)), "an owned block is also free"
-        assert len(owned) + len(self.free) == self.num_blocks, "blocks lost"
+        count = [0] * self.num_blocks
+        for t in self.tables:
+            assert len(t) == len(set(t)), "a table names a block twice"
+            for b in t:
+                count[b] += 1
+        assert count == self.ref, "reference counts disagree with the tables"
+        free = list(self.free)
+        assert len(free) == len(set(free)), "a block is free twice"
+        assert set(free) == {b for b in range(self.num_blocks) if self.ref[b] == 0}, \
+            "free list differs from the unreferenced blocks"
         for s, t in enumerate(self.tables):
             assert self.lens[s] <= len(t) * BLOCK_TOKENS
+        assert len(self.entries) == len(self.entry_of)
+        for key, b in self.entries.items():
+            assert self.entry_of[b] == key
+            if key[0] >= 0:
+                assert b in self.children.get(key[0], set())
+                assert key[0] in self.entry_of, "an entry's parent is not registered"

@@ -131,3 +131,18 @@ def append(k_pool, v_pool, spec: PoolSpec, layer: int, tables, lens_after, seqs,
             write_token(k_pool, v_pool, spec, layer, tables[seq], first + t,
                         k_new[i, t], v_new[i, t], mode, cos_t, sin_t, src_dtype, k_scale,
                         v_scale)
+
+
+def copy_blocks(k_pool, v_pool, spec: PoolSpec, pairs):
+    """Carry out queued copy-on-write copies, one after another in order:
+    for each (src, dst) every layer's and KV head's K and V plane of block
+    ``src`` is copied into block ``dst`` (a block holds all layers, since one
+    table serves every layer)."""
+    plane = BLOCK_TOKENS * spec.head_dim
+    for src, dst in pairs:
+        for layer in range(spec.n_layers):
+            for h in range(spec.n_kv_heads):
+                a = spec.plane_base(layer, int(src), h)
+                b = spec.plane_base(layer, int(dst), h)
+                k_pool[b:b + plane] = k_pool[a:a + plane].copy()
+                v_pool[b:b + plane] = v_pool[a:a + plane].copy()
