@@ -277,7 +277,13 @@ class AllocatorModel:
         for (seq, idx) in order:
             if idx >= len(self.tables[seq]):
                 raise AllocError("RANGE", "destination beyond the reserved blocks")
-        need = sum(1 for (seq, idx) in order if self.ref[self.tables[seq][idx]] > 1)
+        need, refs = 0, {}
+        for (seq, idx) in order:          # counts as they will be when each block is reached
+            b = self.tables[seq][idx]
+            r = refs.get(b, self.ref[b])
+            if r > 1:
+                need += 1
+                refs[b] = r - 1
         if need > len(self.free):
             raise AllocError("OOM", "pool exhausted")
         for (seq, idx) in order:

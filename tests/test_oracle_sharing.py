@@ -229,6 +229,25 @@ def test_inject_into_shared_blocks_copies_each_touched_block_once():
     sh.check()
 
 
+def test_inject_by_all_sharers_needs_one_copy_fewer():
+    """Two sequences share a block and both write it in one call: the first
+    writer takes a copy, the second then owns the block alone and writes in
+    place, so one free block covers the call."""
+    m = AllocatorModel(3, 2, 4)
+    sh = Shadow(m)
+    sh.extend([0], [keys_of(1, 20)])                   # blocks a, b; one block left
+    sh.fork(0, 1)
+    a = list(m.tables[0])
+    m.prepare_inject([(0, 2, 3, 0), (1, 2, 5, 0)])
+    assert m.pending == [(a[0], m.tables[0][0])] and m.tables[1][0] == a[0]
+    sh.flush()
+    for p in (3, 4):
+        sh.write(0, p, 0xA0 + p)
+    for p in (5, 6):
+        sh.write(1, p, 0xB0 + p)
+    sh.check()
+
+
 def test_errors_leave_the_state_unchanged():
     m = AllocatorModel(4, 3, 4)
     m.extend([0], 40)
