@@ -176,13 +176,18 @@ class AllocatorModel:
             self._check_seq(s)
         if len(set(seqs)) != len(seqs) or n_new < 0:
             raise AllocError("INVALID", "repeated sequence or negative count")
-        total = 0
+        total, refs = 0, {}
         for s in seqs:
             want = blocks_for(self.lens[s] + n_new)
             if want > self.max_blocks_per_seq:
                 raise AllocError("RANGE", "more blocks than a table row holds")
             total += max(0, want - len(self.tables[s]))
-            total += 1 if self._partial_shared(s, n_new) else 0
+            if n_new > 0 and self.lens[s] % BLOCK_TOKENS:
+                b = self.tables[s][self.lens[s] // BLOCK_TOKENS]
+                r = refs.get(b, self.ref[b])     # count as it will be when s is reached
+                if r > 1:
+                    total += 1
+                    refs[b] = r - 1
         if total > len(self.free):
             raise AllocError("OOM", "pool exhausted")
         first = []

@@ -248,6 +248,16 @@ def test_inject_by_all_sharers_needs_one_copy_fewer():
     sh.check()
 
 
+def test_extend_by_all_sharers_needs_one_copy_fewer():
+    m = AllocatorModel(3, 2, 4)
+    sh = Shadow(m)
+    sh.extend([0], [keys_of(1, 20)])                   # blocks a, b; one block left
+    sh.fork(0, 1)
+    sh.extend([0, 1], [keys_of(2, 1), keys_of(3, 1)])  # seq 0 copies b, seq 1 keeps it
+    assert sh.copies == 1 and not m.free
+    sh.check()
+
+
 def test_errors_leave_the_state_unchanged():
     m = AllocatorModel(4, 3, 4)
     m.extend([0], 40)
