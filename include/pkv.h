@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 /* Tokens per physical block ([InferScale] §2; [KV essay] "Paged attention"). */
 #define PKV_BLOCK_TOKENS 16
 
@@ -170,6 +170,19 @@ uint64_t pkv_kv_bytes(int32_t n_layers, int32_t n_kv_heads, int32_t head_dim,
  * [Inside engines] "PagedAttention", "Continuous Batching": blocks return to
  * the pool when a sequence ends).  Blocks are taken from the head of a FIFO
  * free list and returned to its tail in table order.
+ *
+ * Blocks may be shared ([KV essay] "Paged attention", "Prefix caching";
+ * [KV management] on beam search, parallel sampling and prefix caching;
+ * [Inside engines] "Zero-Copy Page Sharing"): every block has a reference
+ * count, the number of table entries naming it, and is on the free list
+ * exactly when that count is 0 (a block leaves the free list when handed out
+ * or taken back by pkv_prefix_match, and rejoins its tail when its count
+ * drops to 0).  Before a sequence writes into a block whose count exceeds 1,
+ * it takes a fresh block from the free list's head (copy-on-write): the pair
+ * (old, new) is queued, the sequence's table entry becomes the new block and
+ * the old block's count drops by one.  Queued copies must be carried out,
+ * in queue order, before the written positions are used: pkv_inject does so
+ * itself; after pkv_extend call pkv_copy_blocks before appending.
  * ------------------------------------------------------------------------- */
 
 /* Create an allocator. *out receives the handle. Errors: INVALID. */
@@ -190,14 +203,17 @@ pkv_status pkv_set_blocks(pkv_cache* cache, int32_t seq, const int32_t* ids,
                           int32_t n_ids, int64_t len);
 
 /* Append n_new positions to each of seqs[n_seqs] (host, distinct), reserving
- * a block whenever a sequence crosses a 16-token boundary.  All-or-nothing
- * over the whole list.  first_pos_out (host, may be NULL) receives each
- * sequence's first new position (its old length).  Errors: INVALID, RANGE,
- * OOM. */
+ * a block whenever a sequence crosses a 16-token boundary.  When the new
+ * positions start inside a block the sequence shares, that block is copied
+ * first (queued; see pkv_copy_blocks), sequences handled in list order.
+ * All-or-nothing over the whole list (the copies count as reservations).
+ * first_pos_out (host, may be NULL) receives each sequence's first new
+ * position (its old length).  Errors: INVALID, RANGE, OOM. */
 pkv_status pkv_extend(pkv_cache* cache, const int32_t* seqs, int32_t n_seqs,
                       int32_t n_new, int64_t* first_pos_out);
 
-/* Return seq's blocks to the tail of the free list; its length becomes 0. */
+/* Drop seq's reference to each of its blocks in table order; blocks whose
+ * count reaches 0 join the tail of the free list.  Its length becomes 0. */
 pkv_status pkv_free_seq(pkv_cache* cache, int32_t seq);
 
 /* Export block tables: table_out (host, n_seqs x max_blocks_per_seq int32,
@@ -211,6 +227,57 @@ int32_t pkv_num_free_blocks(const pkv_cache* cache);
 /* Copy the free list, head first, into out (host, capacity cap).  Returns the
  * number of entries copied, or a negative status. */
 int32_t pkv_free_list(const pkv_cache* cache, int32_t* out, int32_t cap);
+
+/* Give the empty sequence dst_seq the table and length of src_seq (every
+ * block's count + 1), as beams or parallel samples share their prompt
+ * ([KV management]).  No device work.  Errors: INVALID (bad or equal ids,
+ * dst_seq not empty). */
+pkv_status pkv_fork(pkv_cache* cache, int32_t src_seq, int32_t dst_seq);
+
+/* Reference count of a block (>= 0), or a negative status. */
+int32_t pkv_block_refcount(const pkv_cache* cache, int32_t block);
+
+/* Copy the queued copy-on-write pairs (src, dst), oldest first, into
+ * pairs_out (host, cap pairs of two int32).  Returns the number queued (which
+ * may exceed cap), or a negative status. */
+int32_t pkv_pending_copies(const pkv_cache* cache, int32_t* pairs_out, int32_t cap);
+
+/* Carry out the queued copies on `stream` and empty the queue: for each pair,
+ * every layer's K and V planes (all KV heads) of block src are copied into
+ * block dst.  The result equals doing them one after another in queue order.
+ * The pool's blocks must include every queued id.  Device work only; the
+ * pool must not be written by other work until the copies finish (stream
+ * order suffices).  Errors: INVALID, RANGE (an id outside the pool), HIP. */
+pkv_status pkv_copy_blocks(pkv_cache* cache, const pkv_pool* pool, void* stream);
+
+/* Prefix cache ([KV essay] "Prefix caching"; [KV management]: serving systems
+ * hash the prefix to find matching entries, and a match must be exact from
+ * position 0).  The caller names what each position holds by a 64-bit key
+ * (a token id of a prompt, or the store row of injected memory).  A full
+ * block is registered under (the block registered for the preceding 16
+ * positions, or -1 at position 0; its 16 keys), compared exactly.  An entry
+ * lasts until its block is handed out again by the free list, given out by
+ * pkv_set_blocks, or written in place by pkv_inject; it then goes together
+ * with every entry registered under it. */
+
+/* For an empty sequence: share the longest chain of registered blocks that
+ * matches keys[0 .. n_keys) (host) block by block from position 0 (a block
+ * with count 0 is taken back off the free list); the sequence's length
+ * becomes the matched token count, written to *matched_out (host, may be
+ * NULL), a multiple of 16.  Errors: INVALID (sequence not empty, bad keys). */
+pkv_status pkv_prefix_match(pkv_cache* cache, int32_t seq, const uint64_t* keys,
+                            int64_t n_keys, int64_t* matched_out);
+
+/* Register the full blocks of seq covered by keys[0 .. n_keys) (host,
+ * n_keys <= length): a block whose (predecessor, keys) is already registered
+ * is skipped (later blocks chain off the registered one).  Errors: INVALID
+ * (a block already registered under other keys; nothing is registered),
+ * RANGE (n_keys beyond the length). */
+pkv_status pkv_prefix_commit(pkv_cache* cache, int32_t seq, const uint64_t* keys,
+                             int64_t n_keys);
+
+/* Number of registered blocks, or -1 for a NULL cache. */
+int32_t pkv_prefix_cached_blocks(const pkv_cache* cache);
 
 /* ---------------------------------------------------------------------------
  * Rotary table ([InferScale] §2 and §3.3: keys are rotated with the model's
@@ -231,8 +298,12 @@ pkv_status pkv_rope_table(int32_t head_dim, double base, int32_t max_pos,
  * x d/2 float) applied in float32 without fused multiply-add, and round the
  * round-to-nearest-even store into the pool dtype.  Each run must lie within
  * its sequence's reserved blocks and below max_pos; two tokens of one call
- * may not share a slot (PKV_E_OVERLAP).  Afterwards each sequence's length is
- * max(length, dst_pos + n_tokens).  Runs are host memory.  The device
+ * may not target one position of one sequence (PKV_E_OVERLAP).  Destination
+ * blocks shared with other sequences are copied first (copy-on-write, blocks
+ * in order of first touch: runs in order, positions ascending; OOM when the
+ * free list cannot cover the copies), a written block loses its prefix-cache
+ * entry, and every queued copy is carried out on `stream` before the write.
+ * Afterwards each sequence's length is max(length, dst_pos + n_tokens).  Runs are host memory.  The device
  * workspace (d_ws, ws_bytes >= pkv_inject_workspace_bytes(runs, n_runs)) holds
  * the per-block write plan; it must not be reused by other work until this
  * call's kernels finish (stream order suffices).

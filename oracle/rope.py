@@ -42,12 +42,17 @@ def thetas(head_dim: int, base: float) -> np.ndarray:
                     dtype=np.float64)
 
 
-def rope_table(head_dim: int, base: float, max_pos: int):
-    """float32 cos and sin tables, shape [max_pos][d/2]."""
+def rope_rows(head_dim: int, base: float, positions):
+    """float32 cos and sin rows of the given positions, shape [n][d/2]."""
     th = thetas(head_dim, base)
-    p = np.arange(max_pos, dtype=np.float64)[:, None]
+    p = np.asarray(positions, dtype=np.float64)[:, None]
     ang = p * th[None, :]
     return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def rope_table(head_dim: int, base: float, max_pos: int):
+    """float32 cos and sin tables, shape [max_pos][d/2]."""
+    return rope_rows(head_dim, base, np.arange(max_pos))
 
 
 def pair_index(head_dim: int, mode: str):

@@ -88,6 +88,13 @@ SIGNATURES = {
     "pkv_block_table": (_I32, [_P, _P, _I32, _P, _P]),
     "pkv_num_free_blocks": (_I32, [_P]),
     "pkv_free_list": (_I32, [_P, _P, _I32]),
+    "pkv_fork": (_I32, [_P, _I32, _I32]),
+    "pkv_block_refcount": (_I32, [_P, _I32]),
+    "pkv_pending_copies": (_I32, [_P, _P, _I32]),
+    "pkv_copy_blocks": (_I32, [_P, ctypes.POINTER(pkv_pool), _P]),
+    "pkv_prefix_match": (_I32, [_P, _I32, _P, _I64, _P]),
+    "pkv_prefix_commit": (_I32, [_P, _I32, _P, _I64]),
+    "pkv_prefix_cached_blocks": (_I32, [_P]),
     "pkv_rope_table": (_I32, [_I32, ctypes.c_double, _I32, _P, _P]),
     "pkv_inject_workspace_bytes": (_SZ, [_P, _I32]),
     "pkv_inject": (_I32, [_P, ctypes.POINTER(pkv_pool), ctypes.POINTER(pkv_src), _P, _I32,
@@ -224,6 +231,55 @@ def pkv_free_list(cache):
     out = np.empty(max(n, 1), dtype=np.int32)
     got = _check(load_library().pkv_free_list(cache, out.ctypes.data, n))
     return out[:got].tolist()
+
+
+# ---------------------------------------------------------------------------
+# Sharing: fork, copy-on-write copies, prefix cache
+# ---------------------------------------------------------------------------
+def pkv_fork(cache, src_seq, dst_seq):
+    _check(load_library().pkv_fork(cache, src_seq, dst_seq))
+
+
+def pkv_block_refcount(cache, block) -> int:
+    return _check(load_library().pkv_block_refcount(cache, block))
+
+
+def pkv_pending_copies(cache):
+    """Queued copy-on-write pairs as a list of (src, dst), oldest first."""
+    import numpy as np
+    lib = load_library()
+    n = _check(lib.pkv_pending_copies(cache, None, 0))
+    out = np.empty((max(n, 1), 2), dtype=np.int32)
+    _check(lib.pkv_pending_copies(cache, out.ctypes.data, n))
+    return [tuple(int(x) for x in r) for r in out[:n]]
+
+
+def pkv_copy_blocks(cache, pool, stream=None):
+    _check(load_library().pkv_copy_blocks(cache, ctypes.byref(pool), _stream(stream)))
+
+
+def _keys(keys):
+    import numpy as np
+    return np.ascontiguousarray(np.asarray(keys, dtype=np.uint64).reshape(-1))
+
+
+def pkv_prefix_match(cache, seq, keys) -> int:
+    """Share the longest cached chain matching ``keys``; returns matched tokens."""
+    k = _keys(keys)
+    out = ctypes.c_int64(0)
+    _check(load_library().pkv_prefix_match(cache, seq, k.ctypes.data if len(k) else None,
+                                           len(k), ctypes.byref(out)))
+    return int(out.value)
+
+
+def pkv_prefix_commit(cache, seq, keys):
+    k = _keys(keys)
+    _check(load_library().pkv_prefix_commit(cache, seq, k.ctypes.data if len(k) else None,
+                                            len(k)))
+
+
+def pkv_prefix_cached_blocks(cache) -> int:
+    return load_library().pkv_prefix_cached_blocks(cache)
 
 
 # ---------------------------------------------------------------------------

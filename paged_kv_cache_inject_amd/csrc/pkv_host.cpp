@@ -6,6 +6,18 @@
 // reaches it) and "Inside LLM Inference Engines" ("PagedAttention",
 // "Continuous Batching": blocks return to the pool when a sequence ends),
 // with a FIFO free list so that the resulting tables are reproducible.
+//
+// Blocks are shared objects ("LLM Inference: KV Caching", "Paged attention"
+// and "Prefix caching"; "Latency Optimization > KV Cache Management" on
+// beams and prefix caching): each carries a reference count (the table
+// entries naming it) and sits on the free list exactly when the count is 0.
+// A sequence about to write into a block other sequences also name first
+// takes a private copy (copy-on-write; the copies are queued and carried out
+// on the GPU, in order, before any write).  Full blocks can be registered in
+// a prefix cache keyed by (the preceding block's entry, the 16 positions'
+// 64-bit keys) and compared exactly, so that a new sequence shares the
+// longest cached chain from position 0; an entry lasts until its block is
+// handed out again or written in place.
 
 #include <hip/hip_runtime.h>
 
@@ -15,9 +27,10 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <deque>
 #include <new>
 #include <string>
+#include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "pkv_internal.h"
@@ -123,17 +136,104 @@ struct Staging {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Prefix-cache key of one full block: the block registered for the
+// preceding 16 positions (-1 at position 0) and this block's 16 keys.
+struct PrefixKey {
+  int32_t parent = -1;
+  uint64_t keys[kBlock] = {};
+  bool operator==(const PrefixKey& o) const {
+    return parent == o.parent && std::memcmp(keys, o.keys, sizeof(keys)) == 0;
+  }
+};
+struct PrefixKeyHash {
+  size_t operator()(const PrefixKey& k) const {
+    uint64_t h = 0x9E3779B97F4A7C15ull ^ uint64_t(uint32_t(k.parent));
+    for (uint64_t x : k.keys) {
+      h = (h ^ x) * 0xBF58476D1CE4E5B9ull;
+      h ^= h >> 31;
+    }
+    return size_t(h);
+  }
+};
+
 }  // namespace
 
 struct pkv_cache {
   int32_t num_blocks = 0;
   int32_t max_seqs = 0;
   int32_t max_blocks_per_seq = 0;
-  std::deque<int32_t> free_list;
+  // FIFO free list, doubly linked through block ids (head = next handed out),
+  // so that a cached block can be taken back from anywhere in O(1).
+  std::vector<int32_t> fl_prev, fl_next;
+  int32_t fl_head = -1, fl_tail = -1, fl_size = 0;
+  std::vector<int32_t> ref;                               // table entries per block
+  std::vector<std::pair<int32_t, int32_t>> pending;       // queued copies (src, dst)
+  std::unordered_map<PrefixKey, int32_t, PrefixKeyHash> entries;
+  std::vector<PrefixKey> entry_key;                       // valid where cached[b]
+  std::vector<uint8_t> cached;
+  std::vector<std::vector<int32_t>> children;             // entries registered under b
   std::vector<std::vector<int32_t>> tables;
   std::vector<int64_t> lens;
   std::vector<int32_t> desc_of_block;  // inject planner scratch, -1 when idle
   Staging staging;
+
+  void fl_push_back(int32_t b) {
+    fl_prev[b] = fl_tail;
+    fl_next[b] = -1;
+    if (fl_tail >= 0) fl_next[fl_tail] = b; else fl_head = b;
+    fl_tail = b;
+    ++fl_size;
+  }
+  void fl_remove(int32_t b) {
+    if (fl_prev[b] >= 0) fl_next[fl_prev[b]] = fl_next[b]; else fl_head = fl_next[b];
+    if (fl_next[b] >= 0) fl_prev[fl_next[b]] = fl_prev[b]; else fl_tail = fl_prev[b];
+    fl_prev[b] = fl_next[b] = -1;
+    --fl_size;
+  }
+  // Drops b's prefix entry and every entry registered under it.
+  void forget(int32_t b) {
+    std::vector<int32_t> stack{b};
+    while (!stack.empty()) {
+      const int32_t x = stack.back();
+      stack.pop_back();
+      if (cached[x]) {
+        cached[x] = 0;
+        const PrefixKey& key = entry_key[x];
+        entries.erase(key);
+        if (key.parent >= 0) {
+          auto& ch = children[key.parent];
+          auto it = std::find(ch.begin(), ch.end(), x);
+          if (it != ch.end()) {
+            *it = ch.back();
+            ch.pop_back();
+          }
+        }
+      }
+      for (int32_t y : children[x]) stack.push_back(y);
+      children[x].clear();
+    }
+  }
+  // Hands out the free list's head (forgetting what it cached).
+  int32_t pop_block() {
+    const int32_t b = fl_head;
+    fl_remove(b);
+    forget(b);
+    ref[b] = 1;
+    return b;
+  }
+  // Gives sequence `seq` a private copy of its idx-th block.
+  void cow(int32_t seq, int64_t idx) {
+    const int32_t old = tables[seq][idx];
+    const int32_t fresh = pop_block();
+    pending.emplace_back(old, fresh);
+    tables[seq][idx] = fresh;
+    --ref[old];
+  }
+  // Drops one reference to each block of a table, in table order.
+  void release(const std::vector<int32_t>& t) {
+    for (int32_t b : t)
+      if (--ref[b] == 0) fl_push_back(b);
+  }
 };
 
 struct pkv_plan {
@@ -203,6 +303,55 @@ pkv_status check_rope(int32_t mode, const float* cos, const float* sin, int32_t 
   return PKV_OK;
 }
 
+// Carries out the queued copy-on-write copies on `stream`.  The queue's
+// meaning is sequential; copies go out in levels so that no launch holds two
+// copies touching a common block as destination, or as the source of one and
+// the destination of the other: a copy's level is one above the highest
+// level of an earlier copy it depends on.
+pkv_status flush_copies(pkv_cache* c, const pkv_pool& pool, hipStream_t stream) {
+  for (const auto& pr : c->pending)
+    if (pr.first >= pool.num_blocks || pr.second >= pool.num_blocks)
+      return fail(PKV_E_RANGE, "copy %d -> %d outside the pool's %d blocks", pr.first,
+                  pr.second, pool.num_blocks);
+  std::unordered_map<int32_t, int32_t> read_at, written_at;  // highest level per block
+  std::vector<int32_t> level(c->pending.size());
+  int32_t n_levels = 0;
+  for (size_t i = 0; i < c->pending.size(); ++i) {
+    const int32_t s = c->pending[i].first, d = c->pending[i].second;
+    int32_t lv = 0;
+    auto bump = [&](const std::unordered_map<int32_t, int32_t>& m, int32_t b) {
+      auto it = m.find(b);
+      if (it != m.end()) lv = std::max(lv, it->second + 1);
+    };
+    bump(written_at, s);  // reads what an earlier copy writes
+    bump(read_at, d);     // overwrites what an earlier copy reads
+    bump(written_at, d);  // overwrites what an earlier copy writes
+    level[i] = lv;
+    read_at[s] = std::max(read_at.count(s) ? read_at[s] : 0, lv);
+    written_at[d] = std::max(written_at.count(d) ? written_at[d] : 0, lv);
+    n_levels = std::max(n_levels, lv + 1);
+  }
+  pkv::CopyBatch batch;
+  for (int32_t lv = 0; lv < n_levels; ++lv) {
+    batch.n = 0;
+    for (size_t i = 0; i <= c->pending.size(); ++i) {
+      const bool last = i == c->pending.size();
+      if (!last && level[i] == lv) {
+        batch.src[batch.n] = c->pending[i].first;
+        batch.dst[batch.n] = c->pending[i].second;
+        ++batch.n;
+      }
+      if (batch.n == pkv::kCopyBatch || (last && batch.n > 0)) {
+        hipError_t e = pkv::launch_copy_blocks(pool, batch, stream);
+        if (e != hipSuccess) return hip_fail(e, "block copy launch");
+        batch.n = 0;
+      }
+    }
+  }
+  c->pending.clear();
+  return PKV_OK;
+}
+
 // Upper bound of destination blocks touched by a list of runs.
 int64_t inject_desc_bound(const pkv_run* runs, int32_t n_runs) {
   int64_t n = 0;
@@ -247,7 +396,13 @@ pkv_status pkv_cache_create(const pkv_cache_config* cfg, pkv_cache** out) {
       std::swap(order[i], order[j]);
     }
   }
-  c->free_list.assign(order.begin(), order.end());
+  c->fl_prev.assign(cfg->num_blocks, -1);
+  c->fl_next.assign(cfg->num_blocks, -1);
+  for (int32_t b : order) c->fl_push_back(b);
+  c->ref.assign(cfg->num_blocks, 0);
+  c->entry_key.resize(cfg->num_blocks);
+  c->cached.assign(cfg->num_blocks, 0);
+  c->children.resize(cfg->num_blocks);
   c->tables.resize(cfg->max_seqs);
   c->lens.assign(cfg->max_seqs, 0);
   *out = c;
@@ -265,12 +420,9 @@ pkv_status pkv_alloc_blocks(pkv_cache* c, int32_t seq, int64_t n_tokens) {
                 c->max_blocks_per_seq);
   auto& t = c->tables[seq];
   const int64_t need = std::max<int64_t>(0, want - int64_t(t.size()));
-  if (need > int64_t(c->free_list.size()))
-    return fail(PKV_E_OOM, "need %lld blocks, %zu free", (long long)need, c->free_list.size());
-  for (int64_t i = 0; i < need; ++i) {
-    t.push_back(c->free_list.front());
-    c->free_list.pop_front();
-  }
+  if (need > c->fl_size)
+    return fail(PKV_E_OOM, "need %lld blocks, %d free", (long long)need, c->fl_size);
+  for (int64_t i = 0; i < need; ++i) t.push_back(c->pop_block());
   return ok();
 }
 
@@ -284,19 +436,19 @@ pkv_status pkv_set_blocks(pkv_cache* c, int32_t seq, const int32_t* ids, int32_t
                 c->max_blocks_per_seq);
   if (len < 0 || len > int64_t(n_ids) * kBlock)
     return fail(PKV_E_RANGE, "length %lld does not fit %d blocks", (long long)len, n_ids);
-  std::vector<uint8_t> is_free(c->num_blocks, 0), taken(c->num_blocks, 0);
-  for (int32_t b : c->free_list) is_free[b] = 1;
+  std::vector<uint8_t> taken(c->num_blocks, 0);
   for (int32_t i = 0; i < n_ids; ++i) {
     const int32_t b = ids[i];
     if (b < 0 || b >= c->num_blocks) return fail(PKV_E_INVALID, "block id %d out of range", b);
-    if (!is_free[b]) return fail(PKV_E_INVALID, "block id %d is not free", b);
+    if (c->ref[b] != 0) return fail(PKV_E_INVALID, "block id %d is not free", b);
     if (taken[b]) return fail(PKV_E_INVALID, "block id %d repeated", b);
     taken[b] = 1;
   }
-  std::deque<int32_t> rest;
-  for (int32_t b : c->free_list)
-    if (!taken[b]) rest.push_back(b);
-  c->free_list.swap(rest);
+  for (int32_t i = 0; i < n_ids; ++i) {
+    c->fl_remove(ids[i]);
+    c->forget(ids[i]);
+    c->ref[ids[i]] = 1;
+  }
   c->tables[seq].assign(ids, ids + n_ids);
   c->lens[seq] = len;
   return ok();
@@ -308,20 +460,34 @@ pkv_status pkv_extend(pkv_cache* c, const int32_t* seqs, int32_t n_seqs, int32_t
   if (n_seqs < 0 || (n_seqs > 0 && !seqs) || n_new < 0)
     return fail(PKV_E_INVALID, "bad sequence list or count");
   std::vector<uint8_t> seen(c->max_seqs, 0);
+  std::unordered_map<int32_t, int32_t> refs_then;  // counts as they will be when reached
   int64_t total = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
     if (pkv_status st = check_seq(c, seqs[i])) return st;
     if (seen[seqs[i]]) return fail(PKV_E_INVALID, "sequence %d repeated", seqs[i]);
     seen[seqs[i]] = 1;
-    const int64_t want = blocks_for(c->lens[seqs[i]] + n_new);
+    const int32_t s = seqs[i];
+    const int64_t want = blocks_for(c->lens[s] + n_new);
     if (want > c->max_blocks_per_seq)
-      return fail(PKV_E_RANGE, "sequence %d would need %lld blocks", seqs[i], (long long)want);
-    total += std::max<int64_t>(0, want - int64_t(c->tables[seqs[i]].size()));
+      return fail(PKV_E_RANGE, "sequence %d would need %lld blocks", s, (long long)want);
+    total += std::max<int64_t>(0, want - int64_t(c->tables[s].size()));
+    if (n_new > 0 && c->lens[s] % kBlock) {
+      const int32_t b = c->tables[s][c->lens[s] / kBlock];
+      auto it = refs_then.find(b);
+      const int32_t r = it == refs_then.end() ? c->ref[b] : it->second;
+      if (r > 1) {
+        ++total;
+        refs_then[b] = r - 1;
+      }
+    }
   }
-  if (total > int64_t(c->free_list.size()))
-    return fail(PKV_E_OOM, "need %lld blocks, %zu free", (long long)total, c->free_list.size());
+  if (total > c->fl_size)
+    return fail(PKV_E_OOM, "need %lld blocks, %d free", (long long)total, c->fl_size);
   for (int32_t i = 0; i < n_seqs; ++i) {
     const int32_t s = seqs[i];
+    // The new positions start inside a block other sequences share: copy it.
+    if (n_new > 0 && c->lens[s] % kBlock && c->ref[c->tables[s][c->lens[s] / kBlock]] > 1)
+      c->cow(s, c->lens[s] / kBlock);
     pkv_alloc_blocks(c, s, c->lens[s] + n_new);
     if (first_pos_out) first_pos_out[i] = c->lens[s];
     c->lens[s] += n_new;
@@ -331,7 +497,7 @@ pkv_status pkv_extend(pkv_cache* c, const int32_t* seqs, int32_t n_seqs, int32_t
 
 pkv_status pkv_free_seq(pkv_cache* c, int32_t seq) {
   if (pkv_status st = check_seq(c, seq)) return st;
-  for (int32_t b : c->tables[seq]) c->free_list.push_back(b);
+  c->release(c->tables[seq]);
   c->tables[seq].clear();
   c->lens[seq] = 0;
   return ok();
@@ -355,18 +521,113 @@ pkv_status pkv_block_table(const pkv_cache* c, const int32_t* seqs, int32_t n_se
 }
 
 int32_t pkv_num_free_blocks(const pkv_cache* c) {
-  return c ? int32_t(c->free_list.size()) : -1;
+  return c ? c->fl_size : -1;
 }
 
 int32_t pkv_free_list(const pkv_cache* c, int32_t* out, int32_t cap) {
   if (!c || (cap > 0 && !out) || cap < 0) return fail(PKV_E_INVALID, "bad arguments");
   int32_t n = 0;
-  for (int32_t b : c->free_list) {
-    if (n >= cap) break;
-    out[n++] = b;
+  for (int32_t b = c->fl_head; b >= 0 && n < cap; b = c->fl_next[b]) out[n++] = b;
+  ok();
+  return n;
+}
+
+// ---------------------------------------------------------------------------
+// Sharing: fork, copy-on-write copies, prefix cache
+// ---------------------------------------------------------------------------
+pkv_status pkv_fork(pkv_cache* c, int32_t src_seq, int32_t dst_seq) {
+  if (pkv_status st = check_seq(c, src_seq)) return st;
+  if (pkv_status st = check_seq(c, dst_seq)) return st;
+  if (src_seq == dst_seq || !c->tables[dst_seq].empty() || c->lens[dst_seq] != 0)
+    return fail(PKV_E_INVALID, "fork needs a distinct, empty destination sequence");
+  for (int32_t b : c->tables[src_seq]) ++c->ref[b];
+  c->tables[dst_seq] = c->tables[src_seq];
+  c->lens[dst_seq] = c->lens[src_seq];
+  return ok();
+}
+
+int32_t pkv_block_refcount(const pkv_cache* c, int32_t block) {
+  if (!c || block < 0 || block >= c->num_blocks) return fail(PKV_E_INVALID, "bad block id");
+  ok();
+  return c->ref[block];
+}
+
+int32_t pkv_pending_copies(const pkv_cache* c, int32_t* pairs_out, int32_t cap) {
+  if (!c || cap < 0 || (cap > 0 && !pairs_out)) return fail(PKV_E_INVALID, "bad arguments");
+  const int32_t n = int32_t(c->pending.size());
+  for (int32_t i = 0; i < n && i < cap; ++i) {
+    pairs_out[2 * i] = c->pending[i].first;
+    pairs_out[2 * i + 1] = c->pending[i].second;
   }
   ok();
   return n;
+}
+
+pkv_status pkv_copy_blocks(pkv_cache* c, const pkv_pool* pool, void* stream) {
+  if (!c) return fail(PKV_E_INVALID, "null cache");
+  if (c->pending.empty()) return ok();
+  if (pkv_status st = check_pool(pool)) return st;
+  return flush_copies(c, *pool, static_cast<hipStream_t>(stream));
+}
+
+pkv_status pkv_prefix_match(pkv_cache* c, int32_t seq, const uint64_t* keys, int64_t n_keys,
+                            int64_t* matched_out) {
+  if (pkv_status st = check_seq(c, seq)) return st;
+  if (n_keys < 0 || (n_keys > 0 && !keys)) return fail(PKV_E_INVALID, "bad key list");
+  if (!c->tables[seq].empty() || c->lens[seq] != 0)
+    return fail(PKV_E_INVALID, "prefix match needs an empty sequence");
+  const int64_t full = std::min<int64_t>(n_keys / kBlock, c->max_blocks_per_seq);
+  PrefixKey key;
+  auto& t = c->tables[seq];
+  for (int64_t i = 0; i < full; ++i) {
+    std::memcpy(key.keys, keys + i * kBlock, sizeof(key.keys));
+    auto it = c->entries.find(key);
+    if (it == c->entries.end()) break;
+    const int32_t b = it->second;
+    if (c->ref[b] == 0) c->fl_remove(b);
+    ++c->ref[b];
+    t.push_back(b);
+    key.parent = b;
+  }
+  c->lens[seq] = int64_t(t.size()) * kBlock;
+  if (matched_out) *matched_out = c->lens[seq];
+  return ok();
+}
+
+pkv_status pkv_prefix_commit(pkv_cache* c, int32_t seq, const uint64_t* keys, int64_t n_keys) {
+  if (pkv_status st = check_seq(c, seq)) return st;
+  if (n_keys < 0 || (n_keys > 0 && !keys)) return fail(PKV_E_INVALID, "bad key list");
+  if (n_keys > c->lens[seq])
+    return fail(PKV_E_RANGE, "%lld keys for a sequence of %lld tokens", (long long)n_keys,
+                (long long)c->lens[seq]);
+  const int64_t full = n_keys / kBlock;
+  std::vector<std::pair<PrefixKey, int32_t>> plan;
+  PrefixKey key;
+  for (int64_t i = 0; i < full; ++i) {
+    const int32_t b = c->tables[seq][i];
+    std::memcpy(key.keys, keys + i * kBlock, sizeof(key.keys));
+    auto it = c->entries.find(key);
+    if (it != c->entries.end()) {
+      key.parent = it->second;
+      continue;
+    }
+    if (c->cached[b])
+      return fail(PKV_E_INVALID, "block %d already caches other content", b);
+    plan.emplace_back(key, b);
+    key.parent = b;
+  }
+  for (const auto& pb : plan) {
+    const int32_t b = pb.second;
+    c->entries.emplace(pb.first, b);
+    c->entry_key[b] = pb.first;
+    c->cached[b] = 1;
+    if (pb.first.parent >= 0) c->children[pb.first.parent].push_back(b);
+  }
+  return ok();
+}
+
+int32_t pkv_prefix_cached_blocks(const pkv_cache* c) {
+  return c ? int32_t(c->entries.size()) : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -419,14 +680,18 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
     return fail(PKV_E_INVALID, "layer range [%d, %d) outside [0, %d)", layer_begin, layer_end,
                 pool->n_layers);
 
-  // Resolve every run token to (physical block, slot in block); build one
-  // write descriptor per destination block.
+  // Resolve every run token to (sequence, logical block, slot); build one
+  // write descriptor per destination block, in order of first touch.  A
+  // block several sequences share gets one descriptor per writing sequence
+  // (copy-on-write below gives all but the last writer a private copy), so
+  // descriptors hang off the block's current id in a short chain.
   std::vector<InjectDesc> descs;
-  if (int64_t(c->desc_of_block.size()) < int64_t(pool->num_blocks))
-    c->desc_of_block.assign(pool->num_blocks, -1);
+  std::vector<int32_t> dseq, dblk, dnext;  // writer, block id before copy-on-write, chain
+  if (int64_t(c->desc_of_block.size()) < int64_t(c->num_blocks))
+    c->desc_of_block.assign(c->num_blocks, -1);
   std::vector<int32_t>& desc_of_block = c->desc_of_block;
   auto reset_scratch = [&]() {
-    for (const InjectDesc& d : descs) desc_of_block[d.phys_block] = -1;
+    for (int32_t b : dblk) desc_of_block[b] = -1;
   };
   for (int32_t r = 0; r < n_runs; ++r) {
     const pkv_run& run = runs[r];
@@ -461,35 +726,73 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
         return fail(PKV_E_RANGE, "block %d outside the pool", blk);
       }
       int32_t di = desc_of_block[blk];
+      while (di >= 0 && dseq[di] != run.seq) di = dnext[di];
       if (di < 0) {
         di = int32_t(descs.size());
-        desc_of_block[blk] = di;
         InjectDesc d;
         d.phys_block = blk;
         d.pos_base = p - p % kBlock;
         for (int k = 0; k < kBlock; ++k) d.src[k] = -1;
         descs.push_back(d);
+        dseq.push_back(run.seq);
+        dblk.push_back(blk);
+        dnext.push_back(desc_of_block[blk]);
+        desc_of_block[blk] = di;
       }
       int32_t& slot_src = descs[di].src[p % kBlock];
       if (slot_src >= 0) {
         reset_scratch();
-        return fail(PKV_E_OVERLAP, "two tokens of this call target slot %lld (seq %d pos %d)",
-                    (long long)blk * kBlock + p % kBlock, run.seq, p);
+        return fail(PKV_E_OVERLAP, "two tokens of this call target seq %d position %d",
+                    run.seq, p);
       }
       slot_src = int32_t(run.src_token + t);
     }
   }
   reset_scratch();
   const size_t bytes = descs.size() * sizeof(InjectDesc);
-  if (!descs.empty() && layer_end > layer_begin) {
+  const bool launch = !descs.empty() && layer_end > layer_begin;
+  if (launch) {
     if (!d_ws || ws_bytes < bytes)
       return fail(PKV_E_WORKSPACE, "inject workspace %zu bytes, need %zu", ws_bytes, bytes);
     if (reinterpret_cast<uintptr_t>(d_ws) & 15)
       return fail(PKV_E_WORKSPACE, "workspace must be 16-byte aligned");
+  }
+  // Copy-on-write, all-or-nothing: count the copies with the reference
+  // counts as they will be when each block is reached.
+  {
+    std::unordered_map<int32_t, int32_t> refs_then;
+    int64_t need = 0;
+    for (size_t i = 0; i < descs.size(); ++i) {
+      const int32_t b = dblk[i];
+      auto it = refs_then.find(b);
+      const int32_t rc = it == refs_then.end() ? c->ref[b] : it->second;
+      if (rc > 1) {
+        ++need;
+        refs_then[b] = rc - 1;
+      }
+    }
+    if (need > c->fl_size)
+      return fail(PKV_E_OOM, "copy-on-write needs %lld blocks, %d free", (long long)need,
+                  c->fl_size);
+    if ((need > 0 || !c->pending.empty()) && c->num_blocks > pool->num_blocks)
+      return fail(PKV_E_INVALID, "block copies need every block of the cache (%d) inside the "
+                  "pool (%d)", c->num_blocks, pool->num_blocks);
+    for (size_t i = 0; i < descs.size(); ++i) {
+      const int32_t seq = dseq[i];
+      const int64_t idx = descs[i].pos_base / kBlock;
+      const int32_t b = c->tables[seq][idx];
+      if (c->ref[b] > 1) c->cow(seq, idx);
+      else c->forget(b);  // written in place: no longer holds what its entry says
+      descs[i].phys_block = c->tables[seq][idx];
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!c->pending.empty())
+    if (pkv_status st = flush_copies(c, *pool, s)) return st;
+  if (launch) {
     void* host = nullptr;
     if (pkv_status st = c->staging.acquire(bytes, &host)) return st;
     std::memcpy(host, descs.data(), bytes);
-    hipStream_t s = static_cast<hipStream_t>(stream);
     if (pkv_status st = c->staging.upload(d_ws, bytes, s)) return st;
     hipError_t e = pkv::launch_inject(*pool, *src, static_cast<const InjectDesc*>(d_ws),
                                       int(descs.size()), layer_begin, layer_end, rope_mode,

@@ -74,4 +74,16 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
 
 hipError_t launch_bw_probe(const void* src, size_t n_bytes, void* sink, hipStream_t stream);
 
+// Copy-on-write copies handed to one launch (a kernel argument, no device
+// staging): pairs i < n copy every layer's K and V planes of block src[i]
+// into block dst[i].  No two pairs of a batch may touch a common block as
+// destination, or as source of one and destination of another.
+constexpr int kCopyBatch = 256;
+struct CopyBatch {
+  int32_t n;
+  int32_t src[kCopyBatch];
+  int32_t dst[kCopyBatch];
+};
+hipError_t launch_copy_blocks(const pkv_pool& pool, const CopyBatch& batch, hipStream_t stream);
+
 }  // namespace pkv

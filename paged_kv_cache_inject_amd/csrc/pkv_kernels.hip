@@ -15,6 +15,11 @@
 //   decode_valu_kernel     generic read side for any dtype / group size.
 //   decode_merge_kernel    log-sum-exp merge of ranges of one sequence that
 //                          ran on different workgroups.
+//   copy_blocks_kernel     copy-on-write: duplicates whole blocks (every layer,
+//                          K and V) before a sequence writes into a block it
+//                          shares ("LLM Inference: KV Caching", "Paged
+//                          attention"; "Latency Optimization > KV Cache
+//                          Management", copy-on-write for beams).
 //   bw_probe_kernel        streaming read for the same-run HBM ceiling.
 //
 // Pool plane layouts (see include/pkv.h): K plane = d/X chunks x 16 tokens x X
@@ -1008,6 +1013,33 @@ __global__ __launch_bounds__(256) void bw_probe_kernel(const u32x4_t* src, size_
   if (a.x == 0x12345678u && a.y == 0x9abcdef0u) sink[0] = a;
 }
 
+// ---------------------------------------------------------------------------
+// Block copy (copy-on-write).  One workgroup per (pair, layer, K or V): the
+// n_kv_heads planes of one layer of the source block, 16 bytes per lane and
+// step, streaming loads and stores (each byte is read once and written once).
+// ---------------------------------------------------------------------------
+struct CopyParams {
+  const char* k;      // K base (bytes)
+  const char* v;      // V base (bytes)
+  int64_t p_layer, p_block, p_head;  // byte strides
+  int n_kv_heads;
+  int plane_units;    // 16-byte units per plane
+};
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p, CopyBatch b) {
+  const int pair = blockIdx.x;
+  const int64_t layer_off = int64_t(blockIdx.y) * p.p_layer;
+  const char* base = (blockIdx.z == 0 ? p.k : p.v) + layer_off;
+  const char* src = base + int64_t(b.src[pair]) * p.p_block;
+  char* dst = const_cast<char*>(base) + int64_t(b.dst[pair]) * p.p_block;
+  const int units = p.n_kv_heads * p.plane_units;
+  for (int u = threadIdx.x; u < units; u += blockDim.x) {
+    const int h = u / p.plane_units;
+    const int64_t off = int64_t(h) * p.p_head + int64_t(u - h * p.plane_units) * 16;
+    st16_stream(dst + off, ld16_stream(src + off));
+  }
+}
+
 int elem_size(int dtype) {
   return dtype == PKV_F32 ? 4 : dtype == PKV_FP8E4M3 ? 1 : 2;
 }
@@ -1188,6 +1220,22 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
     e = hipGetLastError();
   }
   return e;
+}
+
+hipError_t launch_copy_blocks(const pkv_pool& pool, const CopyBatch& batch, hipStream_t stream) {
+  if (batch.n <= 0) return hipSuccess;
+  const int eb = elem_size(pool.dtype);
+  CopyParams p;
+  p.k = static_cast<const char*>(pool.k);
+  p.v = static_cast<const char*>(pool.v);
+  p.p_layer = pool.layer_stride * eb;
+  p.p_block = pool.block_stride * eb;
+  p.p_head = pool.head_stride * eb;
+  p.n_kv_heads = pool.n_kv_heads;
+  p.plane_units = kBlock * pool.head_dim * eb / 16;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(batch.n, pool.n_layers, 2), dim3(256), 0, stream,
+                     p, batch);
+  return hipGetLastError();
 }
 
 hipError_t launch_bw_probe(const void* src, size_t n_bytes, void* sink, hipStream_t stream) {

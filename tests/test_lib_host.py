@@ -13,7 +13,7 @@ import pytest
 import paged_kv_cache_inject_amd as pkv
 from oracle.allocator import AllocatorModel, AllocError
 from oracle.kv_size import kv_bytes
-from oracle.rope import rope_table
+from oracle.rope import rope_rows, rope_table
 from tests.conftest import ROOT
 
 
@@ -43,10 +43,16 @@ def test_kv_bytes_matches_closed_form():
 
 @pytest.mark.parametrize("d,max_pos", [(64, 128), (128, 4096), (128, 32768 + 64)])
 def test_rope_table_bitwise_equal_to_oracle(d, max_pos):
+    """Every row up to 4096, then every 13th row and the last 512 rows (the
+    whole table at 32k positions costs minutes of float64 cos/sin on a slow
+    host)."""
     c, s = pkv.pkv_rope_table(d, 10000.0, max_pos)
-    oc, os_ = rope_table(d, 10000.0, max_pos)
-    assert np.array_equal(c.view(np.uint32), oc.view(np.uint32))
-    assert np.array_equal(s.view(np.uint32), os_.view(np.uint32))
+    rows = np.arange(max_pos)
+    if max_pos > 4096:
+        rows = np.unique(np.concatenate([rows[:4096], rows[4096::13], rows[-512:]]))
+    oc, os_ = rope_rows(d, 10000.0, rows)
+    assert np.array_equal(c[rows].view(np.uint32), oc.view(np.uint32))
+    assert np.array_equal(s[rows].view(np.uint32), os_.view(np.uint32))
 
 
 def test_worked_example_through_the_abi():
@@ -121,6 +127,111 @@ def test_allocator_matches_oracle_on_random_operations(seed):
         tables, lens, free = _state(c, m, mb)
         assert tables == m.tables and lens == m.lens and free == list(m.free), step
         m.check_invariants()
+    pkv.pkv_cache_destroy(c)
+
+
+def _both(fc, fm):
+    """Run the same operation on the library and on the model; return the
+    two error codes (None when it succeeded) and the two results."""
+    rc = rm = ec = em = None
+    try:
+        rc = fc()
+    except pkv.PkvError as e:
+        ec = e.code
+    try:
+        rm = fm()
+    except AllocError as e:
+        em = e.code
+    return ec, em, rc, rm
+
+
+@pytest.mark.parametrize("seed", [0, 3, 77])
+def test_sharing_and_prefix_cache_match_oracle_on_random_operations(seed):
+    """Fork, copy-on-write on extend, free, prefix match and commit through
+    the C ABI against the oracle model: tables, lengths, free list, reference
+    counts, the copy queue and the cache size agree after every step (the
+    queue is compared, never carried out, so nothing runs on a GPU)."""
+    rng = np.random.default_rng(seed + 11)
+    nb, ns, mb = 48, 6, 10
+    c = pkv.pkv_cache_create(nb, ns, mb, free_list_seed=seed)
+    m = AllocatorModel(nb, ns, mb, seed=seed)
+    history = []                                   # key lists committed so far
+    counts = dict(fork=0, cow=0, hit=0)
+    for step in range(600):
+        op = int(rng.integers(0, 6))
+        s = int(rng.integers(0, ns))
+        if op == 0:
+            seqs = sorted(set(rng.integers(0, ns, size=int(rng.integers(1, 3))).tolist()))
+            n = int(rng.choice([1, 5, 16, 23]))
+            ec, em, rc, rm = _both(lambda: list(pkv.pkv_extend(c, seqs, n)),
+                                   lambda: m.extend(seqs, n))
+            assert rc == rm
+        elif op == 1:
+            empty = [x for x in range(ns) if not m.tables[x] and x != s]
+            d = int(rng.choice(empty)) if empty and rng.random() < 0.9 else int(rng.integers(0, ns))
+            ec, em, _, _ = _both(lambda: pkv.pkv_fork(c, s, d), lambda: m.fork(s, d))
+            counts["fork"] += ec is None
+        elif op == 2:
+            ec, em, _, _ = _both(lambda: pkv.pkv_free_seq(c, s), lambda: m.free_seq(s))
+        elif op == 3:
+            ln = m.lens[s]
+            keys = [int(x) for x in rng.integers(0, 50, size=ln)] if ln else []
+            if history and rng.random() < 0.7:
+                base = history[int(rng.integers(0, len(history)))]
+                keys = list(base[:ln]) + keys[len(base):]
+            if len(keys) > ln:
+                keys = keys[:ln]
+            n_keys = int(rng.integers(0, ln + 1)) if ln else 0
+            ec, em, _, _ = _both(lambda: pkv.pkv_prefix_commit(c, s, keys[:n_keys]),
+                                 lambda: m.prefix_commit(s, keys[:n_keys]))
+            if ec is None and n_keys >= 16:
+                history.append(keys[:n_keys])
+        else:
+            if history and rng.random() < 0.8:
+                keys = list(history[int(rng.integers(0, len(history)))])
+                if rng.random() < 0.3 and keys:
+                    keys[int(rng.integers(0, len(keys)))] ^= 1 << 40
+            else:
+                keys = [int(x) for x in rng.integers(0, 50, size=int(rng.integers(0, 60)))]
+            keys = keys + [int(x) for x in rng.integers(0, 2 ** 63, size=int(rng.integers(0, 20)))]
+            ec, em, rc, rm = _both(lambda: pkv.pkv_prefix_match(c, s, keys),
+                                   lambda: m.prefix_match(s, keys))
+            assert rc == rm
+            counts["hit"] += bool(rc)
+        assert ec == em, (step, op, ec, em)
+        tables, lens, free = _state(c, m, mb)
+        assert tables == m.tables and lens == m.lens and free == list(m.free), step
+        assert [pkv.pkv_block_refcount(c, b) for b in range(nb)] == m.ref, step
+        assert pkv.pkv_pending_copies(c) == m.pending, step
+        assert pkv.pkv_prefix_cached_blocks(c) == len(m.entries), step
+        m.check_invariants()
+    counts["cow"] = len(m.pending)
+    assert counts["fork"] > 30 and counts["hit"] > 10 and counts["cow"] > 8, counts
+    pkv.pkv_cache_destroy(c)
+
+
+def test_sharing_errors_through_the_abi():
+    c = pkv.pkv_cache_create(4, 3, 4)
+    pkv.pkv_extend(c, [0], 40)
+    for args in [(0, 0), (0, 7), (-1, 1)]:
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_fork(c, *args)
+        assert e.value.code == "INVALID"
+    pkv.pkv_fork(c, 0, 1)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_prefix_match(c, 1, list(range(16)))    # not empty
+    assert e.value.code == "INVALID"
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_prefix_commit(c, 0, list(range(41)))   # more keys than tokens
+    assert e.value.code == "RANGE"
+    pkv.pkv_fork(c, 0, 2)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_extend(c, [1, 2], 1)                   # two copies, one free block
+    assert e.value.code == "OOM"
+    assert pkv.pkv_pending_copies(c) == [] and pkv.pkv_num_free_blocks(c) == 1
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_block_refcount(c, 4)
+    assert e.value.code == "INVALID"
     pkv.pkv_cache_destroy(c)
 
 
