@@ -296,6 +296,53 @@ def run_inject(reps):
     return res
 
 
+def run_cow(reps):
+    """Copy-on-write for beam search on the 70B-shaped cache (80 layers, 8 KV
+    heads, d=128, bf16): 32 prompts of 200 tokens (12 full blocks and 8
+    tokens), each forked into 4 beams; the first new token of beams 1-3
+    copies the shared, partly filled last block (every layer, K and V), 96
+    block copies per round.  Only pkv_copy_blocks is timed; fork, extend and
+    free between rounds are host work."""
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    L, H, d = 80, 8, 128
+    prompts, beams, plen = 32, 4, 200
+    per_prompt = -(-plen // 16)
+    nb = prompts * (per_prompt + beams) + 64
+    buf, pool = device_pool(L, nb, H, d, "bf16", None)
+    cache = pkv.pkv_cache_create(nb, prompts * beams, 16)
+    for p_ in range(prompts):
+        pkv.pkv_extend(cache, [p_], plen)
+    beam_seqs = [prompts + p_ * (beams - 1) + b for p_ in range(prompts) for b in range(beams - 1)]
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times, pairs = [], 0
+    for r in range(reps + 1):
+        for p_ in range(prompts):
+            for b in range(beams - 1):
+                pkv.pkv_fork(cache, p_, prompts + p_ * (beams - 1) + b)
+        pkv.pkv_extend(cache, beam_seqs, 1)
+        pairs = len(pkv.pkv_pending_copies(cache))
+        s.record()
+        pkv.pkv_copy_blocks(cache, pool)
+        e.record()
+        torch.cuda.synchronize()
+        if r > 0:
+            times.append(s.elapsed_time(e))
+        for x in beam_seqs:
+            pkv.pkv_free_seq(cache, x)
+    ms = float(np.median(times))
+    moved = pairs * L * 2 * H * 16 * d * 2 * 2        # K and V planes, read and written
+    res = dict(pairs=pairs, layers=L, bytes_moved=moved, us_per_round=ms * 1e3,
+               gbps=moved / (ms * 1e-3) / 1e9,
+               workload="beam search, 70B-shaped cache: 32 prompts x 200 tokens, 4 beams each; "
+                        "the first new token of beams 1-3 copies the shared partial block")
+    log("cow: %d block copies in %.1f us, %.1f GB/s (read + write)" % (pairs, ms * 1e3, res["gbps"]))
+    pkv.pkv_cache_destroy(cache)
+    del buf
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle's decode on whole sequences of the decode workload (all 64
     query heads per sequence, layer after layer), one thread, until the
@@ -346,6 +393,8 @@ def main():
                     help="time only the injection workload (no JSON line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache decode figure")
+    ap.add_argument("--no-cow", action="store_true", help="skip the copy-on-write figure")
+    ap.add_argument("--cow-reps", type=int, default=10)
     ap.add_argument("--decode-workload", default="70b", choices=["70b", "8b", "ragged", "70b-fp8"],
                     help="decode workload timed (the reported line uses 70b)")
     args = ap.parse_args()
@@ -369,6 +418,7 @@ def main():
     if not args.no_fp8 and args.decode_workload == "70b":
         fp8, _ = run_decode(args.steps, args.warmup, "70b-fp8")
     inj = None if args.no_inject else run_inject(args.inject_reps)
+    cow = None if args.no_cow else run_cow(args.cow_reps)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     line = {
         "metric": "paged decode attention achieved HBM GB/s (% of peak) + injected tokens/s",
@@ -418,6 +468,12 @@ def main():
                           "layers": inj["layers"],
                           "workload": "top-8 of 10k chunks (64..256 tokens), 32 layers x 8 x 128 "
                                       "bf16, 64 requests, gaps of 1..15 positions"}
+    if cow is not None:
+        line["cow"] = {"workload": cow["workload"], "block_copies": cow["pairs"],
+                       "layers": cow["layers"], "bytes_moved": cow["bytes_moved"],
+                       "us": round(cow["us_per_round"], 1), "gbps": round(cow["gbps"], 1),
+                       "pct_of_peak": round(100 * cow["gbps"] / PEAK_HBM_GBPS, 2),
+                       "kernel": "copy_blocks_kernel (pkv_copy_blocks)"}
     print(json.dumps(line), flush=True)
 
 
