@@ -296,6 +296,82 @@ def run_inject(reps):
     return res
 
 
+def run_inject_host(reps, n_chunks=250, batch=16):
+    """The injection workload with the chunk store in pinned host memory
+    ([InferScale] §6): 16 requests compose the prefix and top-8 of 250 chunks;
+    the inject kernel reads only the runs' rows, over PCIe, while it writes the
+    pool.  Reported against the same run's host-to-device DMA ceiling."""
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    from workloads.configs import CONFIGS, inject_structure, device_normal
+    cfg = CONFIGS[4]
+    st = inject_structure(cfg, n_chunks=n_chunks, batch=batch)
+    L, H, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+    n_src, row = st["n_src"], H * d
+    nbytes = L * n_src * row * 2
+    log("inject (host store): %d tokens x %d layers in pinned host memory (%.1f GB)"
+        % (n_src, L, 2 * nbytes / 1e9))
+    hk, hv = pkv.pkv_host_alloc(nbytes), pkv.pkv_host_alloc(nbytes)
+    try:
+        for base, salt in ((hk, 0), (hv, 1)):
+            view = pkv.host_view(base, nbytes)
+            for layer in range(L):
+                a, b = layer * n_src * row * 2, (layer + 1) * n_src * row * 2
+                t = device_normal(n_src * row, "bf16", cfg.seed * 1000 + 2 * layer + salt)
+                torch.from_numpy(view[a:b]).copy_(t.view(torch.uint8))
+                del t
+        # DMA ceiling: 1 GiB pinned -> device
+        pin = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+        dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dma = []
+        for _ in range(4):
+            s.record()
+            dst.copy_(pin, non_blocking=True)
+            e.record()
+            torch.cuda.synchronize()
+            dma.append((1 << 30) / (s.elapsed_time(e) * 1e-3) / 1e9)
+        dma_gbps = float(np.median(dma[1:]))
+        del pin, dst
+        buf, pool = device_pool(L, st["num_blocks"], H, d, "bf16", None)
+        cache = pkv.pkv_cache_create(st["num_blocks"], batch, st["max_blocks"], st["free_list_seed"])
+        for b_, m in enumerate(st["mem_lens"]):
+            pkv.pkv_alloc_blocks(cache, b_, int(m))
+        max_pos = 4096
+        cos, sin = pkv.pkv_rope_table(d, cfg.rope_base, max_pos)
+        dcos, dsin = torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda()
+        src = pkv.make_src(hk, hv, n_src * row, row, n_src, dtype="bf16")
+        runs = pkv.make_runs(st["runs"])
+        ws = torch.empty(pkv.pkv_inject_workspace_bytes(runs), dtype=torch.uint8, device="cuda")
+        n_tok = int(sum(r[1] for r in st["runs"]))
+
+        def once():
+            pkv.pkv_inject(cache, pool, src, runs, 0, L, "pairs", dcos, dsin, max_pos, ws)
+
+        once()
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            once()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        src_bytes = n_tok * L * row * 2 * 2            # K and V rows read over PCIe
+        res = dict(ms_per_call=ms, tokens=n_tok, requests=batch, layers=L,
+                   tokens_per_s=n_tok / (ms * 1e-3), pcie_gbps=src_bytes / (ms * 1e-3) / 1e9,
+                   dma_gbps=dma_gbps, src_bytes=src_bytes, store_gb=2 * nbytes / 1e9)
+        log("inject (host store): %.3f ms/call, %.3g tok/s, %.1f GB/s over PCIe (DMA ceiling %.1f)"
+            % (ms, res["tokens_per_s"], res["pcie_gbps"], dma_gbps))
+        pkv.pkv_cache_destroy(cache)
+        del buf, ws
+    finally:
+        torch.cuda.synchronize()
+        pkv.pkv_host_free(hk)
+        pkv.pkv_host_free(hv)
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_cow(reps):
     """Copy-on-write for beam search on the 70B-shaped cache (80 layers, 8 KV
     heads, d=128, bf16): 32 prompts of 200 tokens (12 full blocks and 8
@@ -394,6 +470,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache decode figure")
     ap.add_argument("--no-cow", action="store_true", help="skip the copy-on-write figure")
+    ap.add_argument("--no-host-store", action="store_true",
+                    help="skip the pinned-host-store inject figure")
+    ap.add_argument("--host-store-only", action="store_true",
+                    help="time only the pinned-host-store inject (no JSON line)")
     ap.add_argument("--cow-reps", type=int, default=10)
     ap.add_argument("--decode-workload", default="70b", choices=["70b", "8b", "ragged", "70b-fp8"],
                     help="decode workload timed (the reported line uses 70b)")
@@ -411,6 +491,9 @@ def main():
     if args.inject_only:
         run_inject(args.inject_reps)
         return
+    if args.host_store_only:
+        run_inject_host(max(2, args.inject_reps // 3))
+        return
     probe = bw_probe()
     log("bw probe: %.1f GB/s" % probe)
     dec, _ = run_decode(args.steps, args.warmup, args.decode_workload)
@@ -419,6 +502,7 @@ def main():
         fp8, _ = run_decode(args.steps, args.warmup, "70b-fp8")
     inj = None if args.no_inject else run_inject(args.inject_reps)
     cow = None if args.no_cow else run_cow(args.cow_reps)
+    inj_host = None if args.no_host_store else run_inject_host(max(2, args.inject_reps // 3))
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     line = {
         "metric": "paged decode attention achieved HBM GB/s (% of peak) + injected tokens/s",
@@ -468,6 +552,18 @@ def main():
                           "layers": inj["layers"],
                           "workload": "top-8 of 10k chunks (64..256 tokens), 32 layers x 8 x 128 "
                                       "bf16, 64 requests, gaps of 1..15 positions"}
+    if inj_host is not None:
+        line["inject_host_store"] = {
+            "workload": "top-8 of 250 chunks (64..256 tokens) + prefix, 16 requests, 32 layers x "
+                        "8 x 128 bf16; store in pinned host memory, rows read over PCIe by the "
+                        "inject kernel",
+            "tokens_per_s": round(inj_host["tokens_per_s"], 1), "unit": "tokens/s",
+            "ms_per_call": round(inj_host["ms_per_call"], 3),
+            "tokens_per_call": inj_host["tokens"], "requests": inj_host["requests"],
+            "pcie_gbps": round(inj_host["pcie_gbps"], 2),
+            "dma_h2d_ceiling_gbps": round(inj_host["dma_gbps"], 2),
+            "frac_of_dma_ceiling": round(inj_host["pcie_gbps"] / inj_host["dma_gbps"], 3),
+            "store_gb": round(inj_host["store_gb"], 2)}
     if cow is not None:
         line["cow"] = {"workload": cow["workload"], "block_copies": cow["pairs"],
                        "layers": cow["layers"], "bytes_moved": cow["bytes_moved"],

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 /* Tokens per physical block ([InferScale] §2; [KV essay] "Paged attention"). */
 #define PKV_BLOCK_TOKENS 16
 
@@ -114,10 +114,20 @@ typedef struct {
  * (layer, token, kv head, dim) is at layer*layer_stride + token*token_stride +
  * head*head_dim + dim, for K at k and V at v.  Same n_kv_heads and head_dim
  * as the pool; 16-byte aligned rows.  dtype is the pool's, or PKV_BF16 /
- * PKV_F16 for an FP8E4M3 pool. */
+ * PKV_F16 for an FP8E4M3 pool.
+ *
+ * The store may live in device memory or in pinned host memory (allocated
+ * with hipHostMalloc, or a torch tensor with pin_memory=True): [InferScale]
+ * §6 keeps the pre-RoPE store in pinned host DRAM and streams only the
+ * retrieved facts over PCIe.  The inject kernel then reads exactly the rows
+ * its runs name straight from host memory over PCIe while it writes the
+ * pool, so transfer and scatter overlap in one pass.  Any other host pointer
+ * (pageable memory) is rejected with PKV_E_INVALID before work is enqueued;
+ * pinned memory must stay allocated and unchanged until the call's kernels
+ * finish. */
 typedef struct {
-  const void* k;        /* device */
-  const void* v;        /* device */
+  const void* k;        /* device, or pinned host */
+  const void* v;        /* device, or pinned host */
   int64_t layer_stride; /* elements */
   int64_t token_stride; /* elements */
   int64_t n_tokens;     /* tokens per layer (for range checks) */
@@ -309,6 +319,17 @@ pkv_status pkv_rope_table(int32_t head_dim, double base, int32_t max_pos,
  * call's kernels finish (stream order suffices).
  * ------------------------------------------------------------------------- */
 size_t pkv_inject_workspace_bytes(const pkv_run* runs, int32_t n_runs);
+
+/* Page-locked host memory for a host-resident source store ([InferScale] §6:
+ * the pre-RoPE store kept in pinned host DRAM, only the retrieved rows read
+ * over PCIe).  *out receives n_bytes (> 0) of pinned host memory that
+ * pkv_inject can read directly; the caller fills it and releases it with
+ * pkv_host_free.  Errors: INVALID, HIP (the allocation failed). */
+pkv_status pkv_host_alloc(size_t n_bytes, void** out);
+
+/* Release memory from pkv_host_alloc (NULL is ignored).  No enqueued kernel
+ * may still read it.  Errors: HIP. */
+pkv_status pkv_host_free(void* p);
 
 pkv_status pkv_inject(pkv_cache* cache, const pkv_pool* pool, const pkv_src* src,
                       const pkv_run* runs, int32_t n_runs, int32_t layer_begin,

@@ -97,6 +97,8 @@ SIGNATURES = {
     "pkv_prefix_cached_blocks": (_I32, [_P]),
     "pkv_rope_table": (_I32, [_I32, ctypes.c_double, _I32, _P, _P]),
     "pkv_inject_workspace_bytes": (_SZ, [_P, _I32]),
+    "pkv_host_alloc": (_I32, [_SZ, ctypes.POINTER(_P)]),
+    "pkv_host_free": (_I32, [_P]),
     "pkv_inject": (_I32, [_P, ctypes.POINTER(pkv_pool), ctypes.POINTER(pkv_src), _P, _I32,
                           _I32, _I32, _I32, _P, _P, _I32, _P, _SZ, _P]),
     "pkv_append_kv": (_I32, [ctypes.POINTER(pkv_pool), _I32, _P, _I32, _P, _I32, _I32, _P, _P,
@@ -333,6 +335,23 @@ def make_runs(runs):
 def pkv_inject_workspace_bytes(runs) -> int:
     arr = runs if isinstance(runs, ctypes.Array) else make_runs(runs)
     return load_library().pkv_inject_workspace_bytes(arr, len(arr))
+
+
+def pkv_host_alloc(n_bytes) -> int:
+    """Pinned host memory of exactly n_bytes; returns its address."""
+    out = _P()
+    _check(load_library().pkv_host_alloc(int(n_bytes), ctypes.byref(out)))
+    return int(out.value)
+
+
+def pkv_host_free(addr):
+    _check(load_library().pkv_host_free(addr))
+
+
+def host_view(addr, n_bytes):
+    """uint8 numpy view of n_bytes of host memory at addr (no copy)."""
+    import numpy as np
+    return np.ctypeslib.as_array((ctypes.c_uint8 * int(n_bytes)).from_address(int(addr)))
 
 
 def pkv_inject(cache, pool: pkv_pool, src: pkv_src, runs, layer_begin, layer_end, rope_mode,

@@ -352,6 +352,33 @@ pkv_status flush_copies(pkv_cache* c, const pkv_pool& pool, hipStream_t stream) 
   return PKV_OK;
 }
 
+// Device-visible address of an inject source: device (or managed) memory as
+// is; pinned host memory (hipHostMalloc, torch's pin_memory) through the
+// address the GPU reads it by over PCIe.  Anything else -- pageable host
+// memory in particular, which the GPU cannot read -- is rejected before any
+// work is enqueued.
+pkv_status resolve_source(const void* p, const char* what, const void** dev, bool* in_host) {
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  const hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PKV_E_INVALID, "%s %p is neither device memory nor pinned host memory", what, p);
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) {
+    *dev = p;
+    *in_host = false;
+    return PKV_OK;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer) {
+    *in_host = true;
+    const char* base_h = static_cast<const char*>(attr.hostPointer ? attr.hostPointer : p);
+    *dev = static_cast<const char*>(attr.devicePointer) + (static_cast<const char*>(p) - base_h);
+    return PKV_OK;
+  }
+  return fail(PKV_E_INVALID, "%s %p is neither device memory nor pinned host memory", what, p);
+}
+
 // Upper bound of destination blocks touched by a list of runs.
 int64_t inject_desc_bound(const pkv_run* runs, int32_t n_runs) {
   int64_t n = 0;
@@ -659,6 +686,24 @@ size_t pkv_inject_workspace_bytes(const pkv_run* runs, int32_t n_runs) {
   return align_up(size_t(inject_desc_bound(runs, n_runs)) * sizeof(InjectDesc), 256);
 }
 
+pkv_status pkv_host_alloc(size_t n_bytes, void** out) {
+  if (!out || n_bytes == 0) return fail(PKV_E_INVALID, "bad arguments");
+  *out = nullptr;
+  hipError_t e = hipHostMalloc(out, n_bytes, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    *out = nullptr;
+    return hip_fail(e, "pinned host allocation");
+  }
+  return ok();
+}
+
+pkv_status pkv_host_free(void* p) {
+  if (!p) return ok();
+  hipError_t e = hipHostFree(p);
+  if (e != hipSuccess) return hip_fail(e, "pinned host release");
+  return ok();
+}
+
 pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
                       const pkv_run* runs, int32_t n_runs, int32_t layer_begin,
                       int32_t layer_end, int32_t rope_mode, const float* d_cos,
@@ -757,6 +802,12 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
     if (reinterpret_cast<uintptr_t>(d_ws) & 15)
       return fail(PKV_E_WORKSPACE, "workspace must be 16-byte aligned");
   }
+  pkv_src src_dev = *src;
+  bool k_host = false, v_host = false;
+  if (launch) {
+    if (pkv_status st = resolve_source(src->k, "source K", &src_dev.k, &k_host)) return st;
+    if (pkv_status st = resolve_source(src->v, "source V", &src_dev.v, &v_host)) return st;
+  }
   // Copy-on-write, all-or-nothing: count the copies with the reference
   // counts as they will be when each block is reached.
   {
@@ -794,7 +845,8 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
     if (pkv_status st = c->staging.acquire(bytes, &host)) return st;
     std::memcpy(host, descs.data(), bytes);
     if (pkv_status st = c->staging.upload(d_ws, bytes, s)) return st;
-    hipError_t e = pkv::launch_inject(*pool, *src, static_cast<const InjectDesc*>(d_ws),
+    hipError_t e = pkv::launch_inject(*pool, src_dev, k_host || v_host,
+                                      static_cast<const InjectDesc*>(d_ws),
                                       int(descs.size()), layer_begin, layer_end, rope_mode,
                                       d_cos, d_sin, s);
     if (e != hipSuccess) return hip_fail(e, "inject launch");

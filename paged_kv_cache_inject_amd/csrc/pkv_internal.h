@@ -40,9 +40,10 @@ struct MergeSeq {
   int32_t _pad;
 };
 
-hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, const InjectDesc* d_desc,
-                         int n_desc, int layer_begin, int layer_end, int rope_mode,
-                         const float* d_cos, const float* d_sin, hipStream_t stream);
+hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, bool src_in_host_memory,
+                         const InjectDesc* d_desc, int n_desc, int layer_begin, int layer_end,
+                         int rope_mode, const float* d_cos, const float* d_sin,
+                         hipStream_t stream);
 
 hipError_t launch_append(const pkv_pool& pool, int layer, const int32_t* d_tables,
                          int table_stride, const int32_t* d_first_pos, int n_seqs, int n_new,

@@ -297,7 +297,12 @@ constexpr int kInjectThreads = 256;
 // into the K plane in the pool format PDT; V goes through LDS (already in
 // PDT) to be written dimension-major.  Source chunk pairs are (c0, c0 + C/2)
 // so that the halves pairing finds both partners in one unit.
-template <int SDT, int PDT, int D, int HG>
+// ROW picks the lanes' walk over a head's (token, chunk pair) units: token
+// fastest (each load instruction takes 64 bytes of 16 token rows; the K
+// stores of a chunk are contiguous) for sources in HBM, or chunk fastest
+// (each load instruction takes 128-byte pieces of 8 token rows) for sources
+// in pinned host memory, whose PCIe reads want whole, aligned lines.
+template <int SDT, int PDT, int D, int HG, bool ROW>
 __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParams p) {
   typedef typename Fmt<PDT>::T TP;
   constexpr int ES = Fmt<SDT>::kBytes, EP = Fmt<PDT>::kBytes;
@@ -346,8 +351,8 @@ __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParam
         const int w = threadIdx.x + u * kInjectThreads;
         const int hl = w / UNITS;
         const int r = w - hl * UNITS;
-        const int t = r % kBlock;
-        const int c0 = r / kBlock;
+        const int t = ROW ? r / (CS / 2) : r % kBlock;
+        const int c0 = ROW ? r % (CS / 2) : r / kBlock;
         const int src = (w < nh * UNITS) ? desc.src[t] : -1;
         if (src >= 0) {
           const int64_t row = int64_t(src) * p.s_token + int64_t(h0 + hl) * D * ES;
@@ -362,8 +367,8 @@ __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParam
         const int w = threadIdx.x + u * kInjectThreads;
         const int hl = w / UNITS;
         const int r = w - hl * UNITS;
-        const int t = r % kBlock;
-        const int c0 = r / kBlock;
+        const int t = ROW ? r / (CS / 2) : r % kBlock;
+        const int c0 = ROW ? r % (CS / 2) : r / kBlock;
         if (w >= nh * UNITS || desc.src[t] < 0) continue;
         const int h = h0 + hl;
         const int j0 = c0 * XS, j1 = (c0 + CS / 2) * XS;  // first dims of the two chunks
@@ -1055,9 +1060,10 @@ hipError_t launch(K kernel, dim3 grid, dim3 block, hipStream_t stream, const P& 
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, const InjectDesc* d_desc,
-                         int n_desc, int layer_begin, int layer_end, int rope_mode,
-                         const float* d_cos, const float* d_sin, hipStream_t stream) {
+hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, bool src_in_host_memory,
+                         const InjectDesc* d_desc, int n_desc, int layer_begin, int layer_end,
+                         int rope_mode, const float* d_cos, const float* d_sin,
+                         hipStream_t stream) {
   const int eb = elem_size(pool.dtype);
   const int sb = elem_size(src.dtype);
   InjectParams p;
@@ -1093,10 +1099,13 @@ hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, const InjectD
   // KV heads per pass: V tiles of 16 KiB (4 heads of d=128 bf16) by default.
   int hg = 4;
   if (const char* env = std::getenv("PKV_INJECT_HEADS")) hg = std::atoi(env) == 8 ? 8 : 4;
-#define PKV_INJ(SDT, PDT, DD, H) \
-  if (src.dtype == SDT && pool.dtype == PDT && pool.head_dim == DD && hg == H) \
-    return launch(inject_rope_kernel<SDT, PDT, DD, H>, grid, block, stream, p);
-#define PKV_INJ_H(SDT, PDT, DD) PKV_INJ(SDT, PDT, DD, 4) PKV_INJ(SDT, PDT, DD, 8)
+  const bool row = src_in_host_memory;
+  if (row) hg = 4;
+#define PKV_INJ(SDT, PDT, DD, H, R) \
+  if (src.dtype == SDT && pool.dtype == PDT && pool.head_dim == DD && hg == H && row == R) \
+    return launch(inject_rope_kernel<SDT, PDT, DD, H, R>, grid, block, stream, p);
+#define PKV_INJ_H(SDT, PDT, DD) \
+  PKV_INJ(SDT, PDT, DD, 4, false) PKV_INJ(SDT, PDT, DD, 8, false) PKV_INJ(SDT, PDT, DD, 4, true)
 #define PKV_INJ_D(SDT, PDT) PKV_INJ_H(SDT, PDT, 64) PKV_INJ_H(SDT, PDT, 128)
   PKV_INJ_D(PKV_F32, PKV_F32) PKV_INJ_D(PKV_BF16, PKV_BF16) PKV_INJ_D(PKV_F16, PKV_F16)
   PKV_INJ_D(PKV_BF16, PKV_FP8E4M3) PKV_INJ_D(PKV_F16, PKV_FP8E4M3)

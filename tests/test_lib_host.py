@@ -293,6 +293,17 @@ def test_inject_host_validation_errors():
         pkv.pkv_inject(c, no_scales, src, [(0, 1, 0, 0)], 0, 1, "pairs", fake, fake, 100, None,
                        stream=0)
     assert e.value.code == "INVALID"
+    # a source in pageable host memory is refused before anything is enqueued
+    import torch
+    host = np.zeros(64 * 128, dtype=np.uint16)
+    pageable = pkv.pkv_src(host.ctypes.data, host.ctypes.data, 0, 128, 64, pkv.PKV_BF16)
+    ws = torch.empty(pkv.pkv_inject_workspace_bytes([(0, 4, 0, 0)]), dtype=torch.uint8)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_inject(c, pool, pageable, [(0, 4, 0, 0)], 0, 1, "pairs", fake, fake, 100, ws,
+                       stream=0)
+    assert e.value.code == "INVALID" and "pinned" in str(e.value)
+    _, lens = pkv.pkv_block_table(c, [0], 4)
+    assert list(lens) == [0]
     fp8_pool = pkv.pkv_pool(1, 8, 2, 64, pkv.PKV_FP8E4M3, 0, fake, fake, 0, 2048, 1024, fake, fake)
     f32_src = pkv.pkv_src(fake, fake, 0, 128, 64, pkv.PKV_F32)
     with pytest.raises(pkv.PkvError) as e:       # f32 sources are not quantised
