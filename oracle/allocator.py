@@ -47,6 +47,13 @@ exact match from position 0.  Readings taken:
   registers a sequence's full blocks; an entry lasts until its block is
   handed out again by the free list or written in place, and then goes
   together with every entry registered under it.
+
+Sliding window ([KV essay] "Capping the window instead of shrinking the
+rows": a token attends only to the last W tokens, older entries fall out of
+the cache, which stops growing once the window fills): ``trim_window``
+drops a sequence's references to the blocks that lie wholly before its last
+W positions (table order), leaving -1 in their table entries; positions and
+capacity keep counting from 0.
 """
 
 from collections import deque
@@ -217,11 +224,36 @@ class AllocatorModel:
         go to the tail of the free list, in table order."""
         self._check_seq(seq)
         for b in self.tables[seq]:
+            if b < 0:                  # dropped by a window trim
+                continue
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.free.append(b)
         self.tables[seq] = []
         self.lens[seq] = 0
+
+    def trim_window(self, seqs, window: int):
+        """Release, for each sequence, the blocks wholly before its last
+        ``window`` positions; returns the number of table entries dropped."""
+        seqs = list(seqs)
+        for s in seqs:
+            self._check_seq(s)
+        if window <= 0:
+            raise AllocError("INVALID", "window must be positive")
+        dropped = 0
+        for s in seqs:
+            keep_from = max(0, self.lens[s] - window) // BLOCK_TOKENS
+            t = self.tables[s]
+            for i in range(min(keep_from, len(t))):
+                b = t[i]
+                if b < 0:
+                    continue
+                self.ref[b] -= 1
+                if self.ref[b] == 0:
+                    self.free.append(b)
+                t[i] = -1
+                dropped += 1
+        return dropped
 
     # -- sharing ---------------------------------------------------------------
     def _pop(self) -> int:
@@ -258,7 +290,8 @@ class AllocatorModel:
         if src == dst or self.tables[dst] or self.lens[dst]:
             raise AllocError("INVALID", "fork needs a distinct, empty destination")
         for b in self.tables[src]:
-            self.ref[b] += 1
+            if b >= 0:
+                self.ref[b] += 1
         self.tables[dst] = list(self.tables[src])
         self.lens[dst] = self.lens[src]
 
@@ -280,7 +313,7 @@ class AllocatorModel:
                     seen.add(key)
                     order.append(key)
         for (seq, idx) in order:
-            if idx >= len(self.tables[seq]):
+            if idx >= len(self.tables[seq]) or self.tables[seq][idx] < 0:
                 raise AllocError("RANGE", "destination beyond the reserved blocks")
         need, refs = 0, {}
         for (seq, idx) in order:          # counts as they will be when each block is reached
@@ -334,6 +367,8 @@ class AllocatorModel:
         if len(keys) > self.lens[seq]:
             raise AllocError("RANGE", "more keys than the sequence holds")
         full = len(keys) // BLOCK_TOKENS
+        if any(b < 0 for b in self.tables[seq][:full]):
+            raise AllocError("RANGE", "keys cover positions the sequence no longer holds")
         plan, parent = [], -1
         for i in range(full):
             b = self.tables[seq][i]
@@ -356,8 +391,9 @@ class AllocatorModel:
     def check_invariants(self):
         count = [0] * self.num_blocks
         for t in self.tables:
-            assert len(t) == len(set(t)), "a table names a block twice"
-            for b in t:
+            live = [b for b in t if b >= 0]
+            assert len(live) == len(set(live)), "a table names a block twice"
+            for b in live:
                 count[b] += 1
         assert count == self.ref, "reference counts disagree with the tables"
         free = list(self.free)

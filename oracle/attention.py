@@ -18,6 +18,9 @@ Readings taken:
   widened stored values;
 * an fp8 cache holds codes whose values are e4m3(code) times the float32
   scale of their (layer, KV head); the query then comes in a 16-bit format;
+* with a sliding window W ([KV essay] "Capping the window": a token
+  attends only to the last W tokens), the query of a sequence of length n
+  attends to positions max(0, n - W) .. n-1 only;
 * besides ``out`` the log-sum-exp ``lse = m + ln(sum exp(s - m))`` of the
   scaled scores is returned; a sequence of length 0 gives out = 0 and
   lse = -inf.
@@ -73,12 +76,13 @@ def decode_contiguous(q, k_seqs, v_seqs, dtype: str, n_q_heads: int, scale=None)
 
 def decode_paged(q, k_pool, v_pool, spec: PoolSpec, layer: int, tables, lens,
                  n_q_heads: int, scale=None, seqs=None, heads=None, by_plane=False,
-                 q_dtype=None, k_scale=None, v_scale=None):
+                 q_dtype=None, k_scale=None, v_scale=None, window=None):
     """Decode attention reading K/V through the block tables.
 
     ``seqs`` / ``heads`` restrict which (sequence, query head) outputs are
     computed (sampling at large sizes); the rest stay 0 / -inf.  ``by_plane``
-    gathers a whole plane at a time (same values, faster).
+    gathers a whole plane at a time (same values, faster).  ``window`` (a
+    positive int) limits each query to the last ``window`` positions.
     """
     q64 = to_f64(q, spec.dtype if q_dtype is None else q_dtype)
     b_n, hq, d = q64.shape
@@ -91,7 +95,9 @@ def decode_paged(q, k_pool, v_pool, spec: PoolSpec, layer: int, tables, lens,
         qh = range(hq) if heads is None else heads
         kv_heads = sorted({h // g for h in qh})
         gather = gather_sequence_planes if by_plane else gather_sequence
-        k_raw, v_raw = gather(k_pool, v_pool, spec, layer, tables[b], int(lens[b]), heads=kv_heads)
+        start = max(0, int(lens[b]) - int(window)) if window else 0
+        k_raw, v_raw = gather(k_pool, v_pool, spec, layer, tables[b], int(lens[b]), heads=kv_heads,
+                              start=start)
         k64 = to_f64(k_raw, spec.dtype)
         v64 = to_f64(v_raw, spec.dtype)
         if spec.dtype == "fp8":

@@ -52,11 +52,13 @@ def validate_runs(tables, lens, runs, max_pos: int):
             raise InjectError("INVALID", "unknown sequence %d" % seq)
         if n < 0 or p0 < 0 or src < 0:
             raise InjectError("INVALID", "negative run field")
-        cap = sum(1 for b in tables[seq] if b >= 0) * BLOCK_TOKENS
-        if p0 + n > cap:
+        row = tables[seq]
+        if p0 + n > len(row) * BLOCK_TOKENS:
             raise InjectError("RANGE", "run past reserved capacity")
         if p0 + n > max_pos:
             raise InjectError("RANGE", "run past the rotary table")
+        if any(row[p // BLOCK_TOKENS] < 0 for p in range(p0, p0 + n)):
+            raise InjectError("RANGE", "run writes positions without a block")
         for t in range(n):
             s = slot(tables[seq], p0 + t)
             if s in seen:

@@ -114,22 +114,24 @@ def read_token(k_pool, v_pool, spec: PoolSpec, layer: int, block: int, t: int):
 
 
 def gather_sequence(k_pool, v_pool, spec: PoolSpec, layer: int, table_row, length: int,
-                    heads=None):
-    """Raw K, V of positions 0..length-1 of one sequence: [length][H][d] each.
+                    heads=None, start: int = 0):
+    """Raw K, V of positions start..length-1 of one sequence:
+    [length - start][H][d] each.
 
     Walks the block table one position at a time (the definition of paged
     reading); ``heads`` restricts the KV heads returned.
     """
     heads = list(range(spec.n_kv_heads)) if heads is None else list(heads)
     sdt = spec.storage_dtype()
-    k = np.empty((length, len(heads), spec.head_dim), dtype=sdt)
-    v = np.empty((length, len(heads), spec.head_dim), dtype=sdt)
-    for p in range(length):
+    n = max(0, length - start)
+    k = np.empty((n, len(heads), spec.head_dim), dtype=sdt)
+    v = np.empty((n, len(heads), spec.head_dim), dtype=sdt)
+    for i_p, p in enumerate(range(start, length)):
         s = slot(table_row, p)
         blk, t = divmod(s, BLOCK_TOKENS)
         for i, h in enumerate(heads):
-            k[p, i] = k_pool[k_element_offsets(spec, layer, blk, h, t)]
-            v[p, i] = v_pool[v_element_offsets(spec, layer, blk, h, t)]
+            k[i_p, i] = k_pool[k_element_offsets(spec, layer, blk, h, t)]
+            v[i_p, i] = v_pool[v_element_offsets(spec, layer, blk, h, t)]
     return k, v
 
 
@@ -150,14 +152,15 @@ def plane_tokens_v(plane, spec: PoolSpec) -> np.ndarray:
 
 
 def gather_sequence_planes(k_pool, v_pool, spec: PoolSpec, layer: int, table_row, length: int,
-                           heads=None):
+                           heads=None, start: int = 0):
     """Same result as gather_sequence, one whole plane at a time."""
     heads = list(range(spec.n_kv_heads)) if heads is None else list(heads)
     n_blocks = -(-length // BLOCK_TOKENS)
+    first = start // BLOCK_TOKENS
     plane = BLOCK_TOKENS * spec.head_dim
     k = np.empty((n_blocks * BLOCK_TOKENS, len(heads), spec.head_dim), spec.storage_dtype())
     v = np.empty_like(k)
-    for i in range(n_blocks):
+    for i in range(first, n_blocks):
         blk = int(table_row[i])
         if blk < 0:
             raise IndexError("logical block %d has no physical block" % i)
@@ -165,4 +168,4 @@ def gather_sequence_planes(k_pool, v_pool, spec: PoolSpec, layer: int, table_row
             base = spec.plane_base(layer, blk, h)
             k[i * BLOCK_TOKENS:(i + 1) * BLOCK_TOKENS, hi] = plane_tokens_k(k_pool[base:base + plane], spec)
             v[i * BLOCK_TOKENS:(i + 1) * BLOCK_TOKENS, hi] = plane_tokens_v(v_pool[base:base + plane], spec)
-    return k[:length], v[:length]
+    return k[start:length], v[start:length]
