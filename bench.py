@@ -142,8 +142,10 @@ def bw_probe(n_bytes=8 << 30, reps=5):
 
 
 def decode_workload(name):
-    from workloads.configs import (CONFIGS, llama70b_structure, llama8b_structure,
-                                   ragged_mha_structure)
+    from workloads.configs import (CONFIGS, EXTRA, llama70b_structure, llama8b_structure,
+                                   ragged_mha_structure, window_structure)
+    if name == "mistral-window":
+        return EXTRA["mistral-window"], window_structure()
     if name in ("70b", "70b-fp8"):
         return CONFIGS[3], llama70b_structure(CONFIGS[3])
     if name == "8b":
@@ -176,7 +178,9 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None):
     out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, device="cuda")
     lse = torch.empty(cfg.batch, cfg.n_q_heads, device="cuda")
     part = int(os.environ.get("PKV_BENCH_PART", "0"))
-    plan = pkv.pkv_decode_plan_create(lens, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, part)
+    window = int(st.get("window", 0))
+    plan = pkv.pkv_decode_plan_create(lens, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, part,
+                                      window=window)
     ws = torch.empty(pkv.pkv_decode_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
     n_items = pkv.pkv_decode_plan_items(plan)
     part_tokens = pkv.pkv_decode_plan_part_tokens(plan)
@@ -221,7 +225,9 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None):
     torch.cuda.synchronize()
     launch_ms = [ev[k][l][0].elapsed_time(ev[k][l][1]) for k in range(launch_steps)
                  for l in range(cfg.n_layers)]
-    per_launch = decode_bytes(lens, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads, 2,
+    # attended tokens: the last `window` positions under a sliding window
+    attended = np.minimum(lens, window) if window > 0 else lens
+    per_launch = decode_bytes(attended, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads, 2,
                               kv_elem=1 if fp8 else 2)
     ms_step = total_ms / steps
     res = dict(ms_per_step=ms_step, wall_ms_per_step=wall * 1e3 / steps,
@@ -470,12 +476,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache decode figure")
     ap.add_argument("--no-cow", action="store_true", help="skip the copy-on-write figure")
+    ap.add_argument("--no-window", action="store_true",
+                    help="skip the sliding-window decode figure")
     ap.add_argument("--no-host-store", action="store_true",
                     help="skip the pinned-host-store inject figure")
     ap.add_argument("--host-store-only", action="store_true",
                     help="time only the pinned-host-store inject (no JSON line)")
     ap.add_argument("--cow-reps", type=int, default=10)
-    ap.add_argument("--decode-workload", default="70b", choices=["70b", "8b", "ragged", "70b-fp8"],
+    ap.add_argument("--decode-workload", default="70b",
+                    choices=["70b", "8b", "ragged", "70b-fp8", "mistral-window"],
                     help="decode workload timed (the reported line uses 70b)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -500,6 +509,9 @@ def main():
     fp8 = None
     if not args.no_fp8 and args.decode_workload == "70b":
         fp8, _ = run_decode(args.steps, args.warmup, "70b-fp8")
+    win = None
+    if not args.no_window and args.decode_workload == "70b":
+        win, _ = run_decode(args.steps, args.warmup, "mistral-window")
     inj = None if args.no_inject else run_inject(args.inject_reps)
     cow = None if args.no_cow else run_cow(args.cow_reps)
     inj_host = None if args.no_host_store else run_inject_host(max(2, args.inject_reps // 3))
@@ -544,6 +556,13 @@ def main():
             "pct_of_peak": round(100 * fp8["value"] / PEAK_HBM_GBPS, 2),
             "launch_us_avg": round(fp8["launch_ms_avg"] * 1e3, 2),
             "step_speedup_vs_bf16": round(dec["ms_per_step"] / fp8["ms_per_step"], 3)}
+    if win is not None:
+        line["decode_window"] = {
+            "workload": win["workload"], "ms_per_step": round(win["ms_per_step"], 4),
+            "gbps": round(win["value"], 1), "pct_of_peak": round(100 * win["value"] / PEAK_HBM_GBPS, 2),
+            "launch_us_avg": round(win["launch_ms_avg"] * 1e3, 2),
+            "launch_gbps": round(win["launch_gbps"], 1), "layers": win["layers"],
+            "bytes_per_launch": win["bytes_per_launch"]}
     if inj is not None:
         line["inject"] = {"tokens_per_s": round(inj["tokens_per_s"], 1), "unit": "tokens/s",
                           "token_layers_per_s": round(inj["token_layers_per_s"], 1),

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 4
+#define PKV_ABI_VERSION 5
 /* Tokens per physical block ([InferScale] §2; [KV essay] "Paged attention"). */
 #define PKV_BLOCK_TOKENS 16
 
@@ -289,6 +289,17 @@ pkv_status pkv_prefix_commit(pkv_cache* cache, int32_t seq, const uint64_t* keys
 /* Number of registered blocks, or -1 for a NULL cache. */
 int32_t pkv_prefix_cached_blocks(const pkv_cache* cache);
 
+/* Sliding window ([KV essay] "Capping the window instead of shrinking the
+ * rows": older entries fall out of the cache, which stops growing once the
+ * window fills).  For each of seqs[n_seqs] (host), drop the references to
+ * the blocks lying wholly before its last `window` positions, in table order
+ * (blocks reaching count 0 join the free list's tail); their table entries
+ * become -1.  Lengths and positions are unchanged; writing a dropped position
+ * later is refused (RANGE).  *dropped_out (host, may be NULL) receives the
+ * number of entries dropped.  Errors: INVALID (bad ids, window <= 0). */
+pkv_status pkv_trim_window(pkv_cache* cache, const int32_t* seqs, int32_t n_seqs,
+                           int32_t window, int64_t* dropped_out);
+
 /* ---------------------------------------------------------------------------
  * Rotary table ([InferScale] §2 and §3.3: keys are rotated with the model's
  * own rotary tables).  theta_i = base^(-2i/d); cos_out[p][i] and sin_out[p][i]
@@ -359,7 +370,12 @@ pkv_status pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* d_t
  * sqrt(d)) V for one query row per head; "Paged attention": K/V read through
  * the block table; "What the cache costs" and [KV management]: query head h
  * reads KV head h / (n_q_heads / n_kv_heads)).  Sequence b attends to its
- * lens[b] cached tokens (positions 0 .. lens[b]-1, no mask).
+ * lens[b] cached tokens (positions 0 .. lens[b]-1, no mask), or, under a
+ * sliding window (window > 0; [KV essay] "Capping the window instead of
+ * shrinking the rows": a token attends only to the last W tokens), to
+ * positions max(0, lens[b] - window) .. lens[b]-1; blocks before those
+ * positions are never read, so a table trimmed by pkv_trim_window with a
+ * window >= this one decodes the same.
  *
  * A plan fixes the lengths (host, int64 lens[n_seqs]) and splits every
  * sequence longer than part_tokens (a multiple of 16; 0 = chosen from the
@@ -377,7 +393,7 @@ pkv_status pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* d_t
  * ------------------------------------------------------------------------- */
 pkv_status pkv_decode_plan_create(const int64_t* lens, int32_t n_seqs, int32_t n_q_heads,
                                   int32_t n_kv_heads, int32_t head_dim, int32_t part_tokens,
-                                  pkv_plan** out);
+                                  int32_t window, pkv_plan** out);
 
 void pkv_decode_plan_destroy(pkv_plan* plan);
 

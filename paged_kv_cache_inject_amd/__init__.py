@@ -95,6 +95,7 @@ SIGNATURES = {
     "pkv_prefix_match": (_I32, [_P, _I32, _P, _I64, _P]),
     "pkv_prefix_commit": (_I32, [_P, _I32, _P, _I64]),
     "pkv_prefix_cached_blocks": (_I32, [_P]),
+    "pkv_trim_window": (_I32, [_P, _P, _I32, _I32, _P]),
     "pkv_rope_table": (_I32, [_I32, ctypes.c_double, _I32, _P, _P]),
     "pkv_inject_workspace_bytes": (_SZ, [_P, _I32]),
     "pkv_host_alloc": (_I32, [_SZ, ctypes.POINTER(_P)]),
@@ -103,7 +104,8 @@ SIGNATURES = {
                           _I32, _I32, _I32, _P, _P, _I32, _P, _SZ, _P]),
     "pkv_append_kv": (_I32, [ctypes.POINTER(pkv_pool), _I32, _P, _I32, _P, _I32, _I32, _P, _P,
                              _I32, _I32, _P, _P, _I32, _P]),
-    "pkv_decode_plan_create": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_P)]),
+    "pkv_decode_plan_create": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                      ctypes.POINTER(_P)]),
     "pkv_decode_plan_destroy": (None, [_P]),
     "pkv_decode_plan_items": (_I32, [_P]),
     "pkv_decode_plan_part_tokens": (_I32, [_P]),
@@ -284,6 +286,17 @@ def pkv_prefix_cached_blocks(cache) -> int:
     return load_library().pkv_prefix_cached_blocks(cache)
 
 
+def pkv_trim_window(cache, seqs, window) -> int:
+    """Drop blocks wholly before each sequence's last ``window`` positions;
+    returns the number of table entries dropped."""
+    import numpy as np
+    s = np.ascontiguousarray(seqs, dtype=np.int32)
+    out = ctypes.c_int64(0)
+    _check(load_library().pkv_trim_window(cache, s.ctypes.data if len(s) else None, len(s),
+                                          window, ctypes.byref(out)))
+    return int(out.value)
+
+
 # ---------------------------------------------------------------------------
 # Rotary table
 # ---------------------------------------------------------------------------
@@ -379,12 +392,13 @@ def pkv_append_kv(pool: pkv_pool, layer, tables, first_pos, n_new, k_new, v_new,
 # ---------------------------------------------------------------------------
 # Decode
 # ---------------------------------------------------------------------------
-def pkv_decode_plan_create(lens, n_q_heads, n_kv_heads, head_dim, part_tokens=0):
+def pkv_decode_plan_create(lens, n_q_heads, n_kv_heads, head_dim, part_tokens=0, window=0):
+    """window > 0: each sequence attends to its last ``window`` positions."""
     import numpy as np
     a = np.ascontiguousarray(lens, dtype=np.int64)
     h = ctypes.c_void_p()
     _check(load_library().pkv_decode_plan_create(a.ctypes.data, len(a), n_q_heads, n_kv_heads,
-                                                 head_dim, part_tokens, ctypes.byref(h)))
+                                                 head_dim, part_tokens, window, ctypes.byref(h)))
     return h
 
 

@@ -232,7 +232,7 @@ struct pkv_cache {
   // Drops one reference to each block of a table, in table order.
   void release(const std::vector<int32_t>& t) {
     for (int32_t b : t)
-      if (--ref[b] == 0) fl_push_back(b);
+      if (b >= 0 && --ref[b] == 0) fl_push_back(b);  // -1: dropped by a window trim
   }
 };
 
@@ -567,7 +567,8 @@ pkv_status pkv_fork(pkv_cache* c, int32_t src_seq, int32_t dst_seq) {
   if (pkv_status st = check_seq(c, dst_seq)) return st;
   if (src_seq == dst_seq || !c->tables[dst_seq].empty() || c->lens[dst_seq] != 0)
     return fail(PKV_E_INVALID, "fork needs a distinct, empty destination sequence");
-  for (int32_t b : c->tables[src_seq]) ++c->ref[b];
+  for (int32_t b : c->tables[src_seq])
+    if (b >= 0) ++c->ref[b];
   c->tables[dst_seq] = c->tables[src_seq];
   c->lens[dst_seq] = c->lens[src_seq];
   return ok();
@@ -628,6 +629,9 @@ pkv_status pkv_prefix_commit(pkv_cache* c, int32_t seq, const uint64_t* keys, in
     return fail(PKV_E_RANGE, "%lld keys for a sequence of %lld tokens", (long long)n_keys,
                 (long long)c->lens[seq]);
   const int64_t full = n_keys / kBlock;
+  for (int64_t i = 0; i < full; ++i)
+    if (c->tables[seq][i] < 0)
+      return fail(PKV_E_RANGE, "keys cover positions the sequence no longer holds");
   std::vector<std::pair<PrefixKey, int32_t>> plan;
   PrefixKey key;
   for (int64_t i = 0; i < full; ++i) {
@@ -655,6 +659,29 @@ pkv_status pkv_prefix_commit(pkv_cache* c, int32_t seq, const uint64_t* keys, in
 
 int32_t pkv_prefix_cached_blocks(const pkv_cache* c) {
   return c ? int32_t(c->entries.size()) : -1;
+}
+
+pkv_status pkv_trim_window(pkv_cache* c, const int32_t* seqs, int32_t n_seqs, int32_t window,
+                           int64_t* dropped_out) {
+  if (!c) return fail(PKV_E_INVALID, "null cache");
+  if (n_seqs < 0 || (n_seqs > 0 && !seqs)) return fail(PKV_E_INVALID, "bad sequence list");
+  if (window <= 0) return fail(PKV_E_INVALID, "window must be positive");
+  for (int32_t i = 0; i < n_seqs; ++i)
+    if (pkv_status st = check_seq(c, seqs[i])) return st;
+  int64_t dropped = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    auto& t = c->tables[seqs[i]];
+    const int64_t keep_from = std::max<int64_t>(0, c->lens[seqs[i]] - window) / kBlock;
+    for (int64_t j = 0; j < std::min<int64_t>(keep_from, int64_t(t.size())); ++j) {
+      const int32_t b = t[j];
+      if (b < 0) continue;
+      if (--c->ref[b] == 0) c->fl_push_back(b);
+      t[j] = -1;
+      ++dropped;
+    }
+  }
+  if (dropped_out) *dropped_out = dropped;
+  return ok();
 }
 
 // ---------------------------------------------------------------------------
@@ -766,6 +793,11 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
     for (int32_t t = 0; t < run.n_tokens; ++t) {
       const int32_t p = run.dst_pos + t;
       const int32_t blk = table[p / kBlock];
+      if (blk < 0) {
+        reset_scratch();
+        return fail(PKV_E_RANGE, "seq %d position %d lies in a block a window trim dropped",
+                    run.seq, p);
+      }
       if (blk >= pool->num_blocks) {
         reset_scratch();
         return fail(PKV_E_RANGE, "block %d outside the pool", blk);
@@ -888,7 +920,7 @@ pkv_status pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* d_t
 // ---------------------------------------------------------------------------
 pkv_status pkv_decode_plan_create(const int64_t* lens, int32_t n_seqs, int32_t n_q_heads,
                                   int32_t n_kv_heads, int32_t head_dim, int32_t part_tokens,
-                                  pkv_plan** out) {
+                                  int32_t window, pkv_plan** out) {
   if (!out || n_seqs < 0 || (n_seqs > 0 && !lens)) return fail(PKV_E_INVALID, "bad arguments");
   if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads)
     return fail(PKV_E_INVALID, "n_q_heads must be a positive multiple of n_kv_heads");
@@ -896,12 +928,19 @@ pkv_status pkv_decode_plan_create(const int64_t* lens, int32_t n_seqs, int32_t n
     return fail(PKV_E_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
   if (part_tokens < 0 || part_tokens % kBlock)
     return fail(PKV_E_INVALID, "part_tokens must be a non-negative multiple of 16");
+  if (window < 0) return fail(PKV_E_INVALID, "negative window");
+  // Each sequence attends to positions [lo, len): lo = len - window under a
+  // sliding window, else 0.  Its ranges start at lo rounded down to a block.
+  auto first_pos = [&](int64_t len) {
+    return window > 0 ? std::max<int64_t>(0, len - window) : 0;
+  };
   int64_t total = 0, total_blocks = 0, n_nonempty = 0;
   for (int32_t b = 0; b < n_seqs; ++b) {
     if (lens[b] < 0 || lens[b] > (int64_t(1) << 30))
       return fail(PKV_E_RANGE, "length %lld of sequence %d", (long long)lens[b], b);
-    total += lens[b];
-    total_blocks += blocks_for(lens[b]);
+    const int64_t span = lens[b] - first_pos(lens[b]) / kBlock * kBlock;
+    total += span;
+    total_blocks += blocks_for(span);
     n_nonempty += lens[b] > 0;
   }
   // Waves per workgroup: the waves of one workgroup share a token range,
@@ -935,16 +974,19 @@ pkv_status pkv_decode_plan_create(const int64_t* lens, int32_t n_seqs, int32_t n
   plan->waves = waves;
   int32_t slots = 0;
   for (int32_t b = 0; b < n_seqs; ++b) {
-    const int64_t n_items = (lens[b] + part - 1) / part;
+    const int64_t lo = first_pos(lens[b]);
+    const int64_t start = lo / kBlock * kBlock;
+    const int64_t n_items = (lens[b] - start + part - 1) / part;
     if (n_items <= 1) {
-      // whole sequence in one item (an empty one included): final output
-      plan->items.push_back(DecodeItem{b, 0, int32_t(lens[b]), -1});
+      // whole range in one item (an empty one included): final output
+      plan->items.push_back(
+          DecodeItem{b, int32_t(start), int32_t(lens[b] - start), -1, int32_t(lo)});
     } else {
       plan->merges.push_back(MergeSeq{b, slots, int32_t(n_items), 0});
       for (int64_t i = 0; i < n_items; ++i) {
-        const int64_t t0 = i * part;
+        const int64_t t0 = start + i * part;
         const int64_t n = std::min<int64_t>(part, lens[b] - t0);
-        plan->items.push_back(DecodeItem{b, int32_t(t0), int32_t(n), slots++});
+        plan->items.push_back(DecodeItem{b, int32_t(t0), int32_t(n), slots++, int32_t(lo)});
       }
     }
   }

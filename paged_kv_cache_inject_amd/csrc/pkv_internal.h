@@ -27,9 +27,10 @@ static_assert(sizeof(InjectDesc) == 72, "descriptor layout");
 // its partial softmax state in partial slot `slot`, merged afterwards.
 struct DecodeItem {
   int32_t seq;
-  int32_t t_begin;
-  int32_t n_tokens;
-  int32_t slot;
+  int32_t t_begin;   // first position of the range (a multiple of 16)
+  int32_t n_tokens;  // positions t_begin .. t_begin + n_tokens - 1
+  int32_t slot;      // partial-result slot, or -1 for a final result
+  int32_t lo;        // first position attended (a sliding window's start)
 };
 
 // Merge work: sequence seq owns partial slots [first, first + count).

@@ -65,10 +65,11 @@ template <> struct Fmt<PKV_BF16> {
   typedef uint16_t T;
   static constexpr int kBytes = 2;
   __device__ static float to_f32(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
-  // Round to nearest, ties to even; NaN stays a (quiet) NaN.
+  // Round to nearest, ties to even; a NaN becomes the quiet NaN of its sign
+  // (0x7FC0 / 0xFFC0), whatever its payload.
   __device__ static uint16_t from_f32(float f) {
     uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t(((u >> 16) & 0x8000u) | 0x7FC0u);
     u += 0x7fffu + ((u >> 16) & 1u);
     return uint16_t(u >> 16);
   }
@@ -741,15 +742,19 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
         if (j + DEPTH < nj) issue(j + DEPTH, d);
 
         const int valid = it.n_tokens - (wave + j * NW) * kBlock;  // tokens in range
-        if (valid < kBlock || !blk_ok) {
-          // Slots past the sequence end (or of a rejected block id) may hold
+        // Slots of this block before a sliding window's start (positive only
+        // in the window's first block).
+        const int skip = it.lo - (it.t_begin + (wave + j * NW) * kBlock);
+        if (valid < kBlock || skip > 0 || !blk_ok) {
+          // Slots outside [lo, end) (or of a rejected block id) may hold
           // anything, NaN included: zero their V so that 0-weight * V stays 0.
           // Lane holds tokens 4*grp + e, e = 0..3, as 16-bit halves of x, y.
           const int lim = blk_ok ? valid : 0;
-          const uint32_t mx0 = (4 * grp + 0 < lim ? 0x0000ffffu : 0u) |
-                               (4 * grp + 1 < lim ? 0xffff0000u : 0u);
-          const uint32_t mx1 = (4 * grp + 2 < lim ? 0x0000ffffu : 0u) |
-                               (4 * grp + 3 < lim ? 0xffff0000u : 0u);
+          auto in = [&](int e) { return e < lim && e >= skip; };
+          const uint32_t mx0 = (in(4 * grp + 0) ? 0x0000ffffu : 0u) |
+                               (in(4 * grp + 1) ? 0xffff0000u : 0u);
+          const uint32_t mx1 = (in(4 * grp + 2) ? 0x0000ffffu : 0u) |
+                               (in(4 * grp + 3) ? 0xffff0000u : 0u);
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
             vcur[n].x &= mx0;
@@ -760,7 +765,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const bool live = blk_ok && (4 * grp + r) < valid;
+          const bool live = blk_ok && (4 * grp + r) < valid && (4 * grp + r) >= skip;
           s4[r] = live ? sc[r] * score_mul : -INFINITY;
           mx = fmaxf(mx, s4[r]);
         }
@@ -903,7 +908,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     for (int bi = 0; bi < nblk; ++bi) {
       const int blk = tab[bi];
       const bool ok = unsigned(blk) < unsigned(p.num_blocks);
-      const bool live = ok && (bi * kBlock + tok) < it.n_tokens;
+      const bool live = ok && (bi * kBlock + tok) < it.n_tokens &&
+                        it.t_begin + bi * kBlock + tok >= it.lo;
       const char* kp = kbase + int64_t(ok ? blk : 0) * p.p_block;
       const char* vp = vbase + int64_t(ok ? blk : 0) * p.p_block;
       float kv[QC * X];
@@ -949,8 +955,10 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
         const T* vrow = reinterpret_cast<const T*>(vp + int64_t(j) * kBlock * E);
         float vv[kBlock];
         const int lim = ok ? it.n_tokens - bi * kBlock : 0;  // live tokens of the block
+        const int skip = it.lo - (it.t_begin + bi * kBlock);  // before a window's start
 #pragma unroll
-        for (int t = 0; t < kBlock; ++t) vv[t] = t < lim ? Fmt<DT>::to_f32(vrow[t]) : 0.f;
+        for (int t = 0; t < kBlock; ++t)
+          vv[t] = t < lim && t >= skip ? Fmt<DT>::to_f32(vrow[t]) : 0.f;
         for (int i = 0; i < nh; ++i) {
           float a = acc[i][k];
 #pragma unroll

@@ -163,10 +163,11 @@ def workspace(n_bytes):
 
 
 def decode(dp: DevicePool, layer, q_dev, tables_dev, lens, n_q_heads, part_tokens=0,
-           with_lse=True, q_dtype=None):
+           with_lse=True, q_dtype=None, window=0):
     """Plan + upload + decode one layer; returns (out, lse) device tensors."""
     import torch
-    plan = pkv.pkv_decode_plan_create(lens, n_q_heads, dp.n_kv_heads, dp.head_dim, part_tokens)
+    plan = pkv.pkv_decode_plan_create(lens, n_q_heads, dp.n_kv_heads, dp.head_dim, part_tokens,
+                                      window=window)
     try:
         ws = workspace(pkv.pkv_decode_workspace_bytes(plan))
         pkv.pkv_decode_plan_upload(plan, ws)

@@ -67,9 +67,18 @@ def test_worked_example_through_the_abi():
     pkv.pkv_cache_destroy(c)
 
 
+def _unpad(row):
+    """A table row without its trailing -1 padding (holes a window trim left
+    at the front stay)."""
+    row = [int(x) for x in row]
+    while row and row[-1] < 0:
+        row.pop()
+    return row
+
+
 def _state(c, model, max_b):
     t, lens = pkv.pkv_block_table(c, list(range(model.max_seqs)), max_b)
-    return ([list(r[r >= 0]) for r in t], list(lens), pkv.pkv_free_list(c))
+    return ([_unpad(r) for r in t], list(lens), pkv.pkv_free_list(c))
 
 
 @pytest.mark.parametrize("seed", [0, 1, 12345])
@@ -158,9 +167,15 @@ def test_sharing_and_prefix_cache_match_oracle_on_random_operations(seed):
     history = []                                   # key lists committed so far
     counts = dict(fork=0, cow=0, hit=0)
     for step in range(600):
-        op = int(rng.integers(0, 6))
+        op = int(rng.integers(0, 7))
         s = int(rng.integers(0, ns))
-        if op == 0:
+        if op == 6:
+            w = int(rng.choice([1, 10, 40]))
+            ec, em, rc, rm = _both(lambda: pkv.pkv_trim_window(c, [s], w),
+                                   lambda: m.trim_window([s], w))
+            assert rc == rm
+            counts["trim"] = counts.get("trim", 0) + (rc or 0)
+        elif op == 0:
             seqs = sorted(set(rng.integers(0, ns, size=int(rng.integers(1, 3))).tolist()))
             n = int(rng.choice([1, 5, 16, 23]))
             ec, em, rc, rm = _both(lambda: list(pkv.pkv_extend(c, seqs, n)),
@@ -206,7 +221,29 @@ def test_sharing_and_prefix_cache_match_oracle_on_random_operations(seed):
         assert pkv.pkv_prefix_cached_blocks(c) == len(m.entries), step
         m.check_invariants()
     counts["cow"] = len(m.pending)
-    assert counts["fork"] > 30 and counts["hit"] > 10 and counts["cow"] > 8, counts
+    assert counts["fork"] > 30 and counts["hit"] > 4 and counts["cow"] > 8, counts
+    assert counts.get("trim", 0) > 10, counts
+    pkv.pkv_cache_destroy(c)
+
+
+def test_window_trim_through_the_abi():
+    c = pkv.pkv_cache_create(32, 2, 16)
+    m = AllocatorModel(32, 2, 16)
+    pkv.pkv_extend(c, [0], 100)
+    m.extend([0], 100)
+    assert pkv.pkv_trim_window(c, [0], 20) == m.trim_window([0], 20) == 5
+    t, lens = pkv.pkv_block_table(c, [0], 16)
+    assert list(t[0][:5]) == [-1] * 5 and list(t[0]) == m.tables[0] + [-1] * (16 - 7)
+    assert pkv.pkv_free_list(c) == list(m.free)
+    for bad in (0, -3):
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_trim_window(c, [0], bad)
+        assert e.value.code == "INVALID"
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_prefix_commit(c, 0, list(range(32)))   # keys over dropped blocks
+    assert e.value.code == "RANGE"
+    pkv.pkv_free_seq(c, 0)
+    assert pkv.pkv_num_free_blocks(c) == 32
     pkv.pkv_cache_destroy(c)
 
 

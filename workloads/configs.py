@@ -62,6 +62,16 @@ CONFIGS = {
 }
 
 
+# Workloads of the extensions beyond the five configurations above.
+EXTRA = {
+    "mistral-window": Config(
+        "mistral-7b-window", "Mistral-7B-shaped sliding-window decode: 32 layers, Hq=32 Hkv=8 "
+        "d=128 bf16, B=32 at position 32768 with a 4096-token window; tables hold the "
+        "window's blocks only",
+        1006, 32, 32, 32, 8, 128, "bf16", extra=dict(length=32768, window=4096)),
+}
+
+
 def get_config(n: int) -> Config:
     return CONFIGS[n]
 
@@ -212,3 +222,20 @@ def inject_structure(cfg: Config = None, n_chunks=None, batch=None):
     return dict(chunk_lens=chunk_lens, chunk_starts=starts[:nc], n_src=n_src, runs=runs,
                 mem_lens=np.array(mem_lens, dtype=np.int64), picks=picks, num_blocks=pool,
                 max_blocks=max_blocks, free_list_seed=cfg.seed, rng=rng)
+
+
+def window_structure(cfg: Config = None):
+    """Sliding-window decode: every sequence at the same position, its table
+    holding only the blocks of the last ``window`` positions (the rest -1, as
+    a window trim leaves them); block ids shuffled."""
+    cfg = cfg or EXTRA["mistral-window"]
+    rng = np.random.default_rng(cfg.seed)
+    n, w = cfg.extra["length"], cfg.extra["window"]
+    per = blocks_for(n)
+    keep_from = max(0, n - w) // BLOCK
+    held = per - keep_from
+    nb = cfg.batch * held
+    tables = np.full((cfg.batch, per), -1, dtype=np.int32)
+    tables[:, keep_from:] = rng.permutation(nb).astype(np.int32).reshape(cfg.batch, held)
+    lens = np.full(cfg.batch, n, dtype=np.int64)
+    return dict(lens=lens, num_blocks=nb, tables=tables, max_blocks=per, window=w, rng=rng)
