@@ -41,7 +41,7 @@ exact match from position 0.  Readings taken:
 * prefix cache: the caller names what each position holds by a 64-bit key
   (a token id for a prompt, the store row for injected memory); a full block
   is registered under (the block registered for the preceding block or -1,
-  its 16 keys), compared exactly; ``prefix_match`` shares, for an empty
+  its keys, one per position), compared exactly; ``prefix_match`` shares, for an empty
   sequence, the longest chain of registered blocks from position 0 (taking a
   block back off the free list when its count was 0); ``prefix_commit``
   registers a sequence's full blocks; an entry lasts until its block is
@@ -54,6 +54,13 @@ the cache, which stops growing once the window fills): ``trim_window``
 drops a sequence's references to the blocks that lie wholly before its last
 W positions (table order), leaving -1 in their table entries; positions and
 capacity keep counting from 0.
+
+Block size ([Inside engines] "PagedAttention": blocks of e.g. 16 or 32
+tokens): the model takes 16 or 32 tokens per block.  Reading: a 32-token
+block b is the pair of adjacent 16-token planes 2b and 2b+1 of the pool;
+allocation, sharing, copy-on-write, prefix entries and trimming work in
+32-token blocks, and ``expand_table`` gives the table of 16-token planes that
+readers and writers go through.
 """
 
 from collections import deque
@@ -93,17 +100,35 @@ def initial_free_order(num_blocks: int, seed: int) -> list:
     return order
 
 
-def blocks_for(n_tokens: int) -> int:
+def blocks_for(n_tokens: int, block_tokens: int = BLOCK_TOKENS) -> int:
     """Blocks needed to hold ``n_tokens`` positions."""
-    return -(-int(n_tokens) // BLOCK_TOKENS)
+    return -(-int(n_tokens) // block_tokens)
+
+
+def expand_table(row, block_tokens: int = BLOCK_TOKENS):
+    """A table row of ``block_tokens``-token blocks as the row of 16-token
+    planes: block b covers planes b*k .. b*k + k-1, k = block_tokens / 16
+    (-1 entries stay -1)."""
+    k = block_tokens // BLOCK_TOKENS
+    return [int(b) * k + i if b >= 0 else -1 for b in row for i in range(k)]
+
+
+def expand_pairs(pairs, block_tokens: int = BLOCK_TOKENS):
+    """Queued block copies as copies of 16-token planes, in order."""
+    k = block_tokens // BLOCK_TOKENS
+    return [(s * k + i, d * k + i) for (s, d) in pairs for i in range(k)]
 
 
 class AllocatorModel:
     """Free list, per-sequence block lists and lengths."""
 
-    def __init__(self, num_blocks: int, max_seqs: int, max_blocks_per_seq: int, seed: int = 0):
+    def __init__(self, num_blocks: int, max_seqs: int, max_blocks_per_seq: int, seed: int = 0,
+                 block_tokens: int = BLOCK_TOKENS):
         if num_blocks <= 0 or max_seqs <= 0 or max_blocks_per_seq <= 0:
             raise AllocError("INVALID", "sizes must be positive")
+        if block_tokens not in (16, 32):
+            raise AllocError("INVALID", "block size must be 16 or 32 tokens")
+        self.bt = block_tokens
         self.num_blocks = num_blocks
         self.max_seqs = max_seqs
         self.max_blocks_per_seq = max_blocks_per_seq
@@ -112,7 +137,7 @@ class AllocatorModel:
         self.lens = [0] * max_seqs
         self.ref = [0] * num_blocks
         self.pending = []          # queued copies (src, dst), in order
-        self.entries = {}          # (parent block or -1, 16 keys) -> block
+        self.entries = {}          # (parent block or -1, a block's keys) -> block
         self.entry_of = {}         # block -> its (parent, keys)
         self.children = {}         # block -> blocks registered under it
 
@@ -123,7 +148,7 @@ class AllocatorModel:
 
     def capacity(self, seq: int) -> int:
         self._check_seq(seq)
-        return len(self.tables[seq]) * BLOCK_TOKENS
+        return len(self.tables[seq]) * self.bt
 
     def block_table(self, seqs):
         """Rows padded with -1 to ``max_blocks_per_seq``, and the lengths."""
@@ -141,7 +166,7 @@ class AllocatorModel:
         self._check_seq(seq)
         if n_tokens < 0:
             raise AllocError("INVALID", "negative token count")
-        want = blocks_for(n_tokens)
+        want = blocks_for(n_tokens, self.bt)
         if want > self.max_blocks_per_seq:
             raise AllocError("RANGE", "more blocks than a table row holds")
         need = max(0, want - len(self.tables[seq]))
@@ -163,7 +188,7 @@ class AllocatorModel:
         free_set = set(self.free)
         if any(i not in free_set for i in ids):
             raise AllocError("INVALID", "block id not free")
-        if not (0 <= length <= len(ids) * BLOCK_TOKENS):
+        if not (0 <= length <= len(ids) * self.bt):
             raise AllocError("RANGE", "length exceeds the given blocks")
         taken = set(ids)
         self.free = deque(b for b in self.free if b not in taken)
@@ -185,12 +210,12 @@ class AllocatorModel:
             raise AllocError("INVALID", "repeated sequence or negative count")
         total, refs = 0, {}
         for s in seqs:
-            want = blocks_for(self.lens[s] + n_new)
+            want = blocks_for(self.lens[s] + n_new, self.bt)
             if want > self.max_blocks_per_seq:
                 raise AllocError("RANGE", "more blocks than a table row holds")
             total += max(0, want - len(self.tables[s]))
-            if n_new > 0 and self.lens[s] % BLOCK_TOKENS:
-                b = self.tables[s][self.lens[s] // BLOCK_TOKENS]
+            if n_new > 0 and self.lens[s] % self.bt:
+                b = self.tables[s][self.lens[s] // self.bt]
                 r = refs.get(b, self.ref[b])     # count as it will be when s is reached
                 if r > 1:
                     total += 1
@@ -200,7 +225,7 @@ class AllocatorModel:
         first = []
         for s in seqs:
             if self._partial_shared(s, n_new):
-                self._cow(s, self.lens[s] // BLOCK_TOKENS)
+                self._cow(s, self.lens[s] // self.bt)
             self.alloc_blocks(s, self.lens[s] + n_new)
             first.append(self.lens[s])
             self.lens[s] += n_new
@@ -209,9 +234,9 @@ class AllocatorModel:
     def _partial_shared(self, s: int, n_new: int) -> bool:
         """Will appending to ``s`` write into a block other sequences share?"""
         ln = self.lens[s]
-        if n_new <= 0 or ln % BLOCK_TOKENS == 0:
+        if n_new <= 0 or ln % self.bt == 0:
             return False
-        return self.ref[self.tables[s][ln // BLOCK_TOKENS]] > 1
+        return self.ref[self.tables[s][ln // self.bt]] > 1
 
     def set_len(self, seq: int, length: int):
         self._check_seq(seq)
@@ -242,7 +267,7 @@ class AllocatorModel:
             raise AllocError("INVALID", "window must be positive")
         dropped = 0
         for s in seqs:
-            keep_from = max(0, self.lens[s] - window) // BLOCK_TOKENS
+            keep_from = max(0, self.lens[s] - window) // self.bt
             t = self.tables[s]
             for i in range(min(keep_from, len(t))):
                 b = t[i]
@@ -308,7 +333,7 @@ class AllocatorModel:
         for (seq, n, p0, _) in runs:
             self._check_seq(seq)
             for p in range(int(p0), int(p0) + int(n)):
-                key = (int(seq), p // BLOCK_TOKENS)
+                key = (int(seq), p // self.bt)
                 if key not in seen:
                     seen.add(key)
                     order.append(key)
@@ -337,9 +362,8 @@ class AllocatorModel:
         return out
 
     # -- prefix cache ------------------------------------------------------------
-    @staticmethod
-    def _block_keys(keys, i):
-        return tuple(int(k) & _MASK for k in keys[i * BLOCK_TOKENS:(i + 1) * BLOCK_TOKENS])
+    def _block_keys(self, keys, i):
+        return tuple(int(k) & _MASK for k in keys[i * self.bt:(i + 1) * self.bt])
 
     def prefix_match(self, seq: int, keys) -> int:
         """Share the longest registered chain matching ``keys`` from position 0
@@ -347,7 +371,7 @@ class AllocatorModel:
         self._check_seq(seq)
         if self.tables[seq] or self.lens[seq]:
             raise AllocError("INVALID", "prefix match needs an empty sequence")
-        full = min(len(keys) // BLOCK_TOKENS, self.max_blocks_per_seq)
+        full = min(len(keys) // self.bt, self.max_blocks_per_seq)
         parent = -1
         for i in range(full):
             b = self.entries.get((parent, self._block_keys(keys, i)))
@@ -358,7 +382,7 @@ class AllocatorModel:
             self.ref[b] += 1
             self.tables[seq].append(b)
             parent = b
-        self.lens[seq] = len(self.tables[seq]) * BLOCK_TOKENS
+        self.lens[seq] = len(self.tables[seq]) * self.bt
         return self.lens[seq]
 
     def prefix_commit(self, seq: int, keys):
@@ -366,7 +390,7 @@ class AllocatorModel:
         self._check_seq(seq)
         if len(keys) > self.lens[seq]:
             raise AllocError("RANGE", "more keys than the sequence holds")
-        full = len(keys) // BLOCK_TOKENS
+        full = len(keys) // self.bt
         if any(b < 0 for b in self.tables[seq][:full]):
             raise AllocError("RANGE", "keys cover positions the sequence no longer holds")
         plan, parent = [], -1
@@ -401,7 +425,7 @@ class AllocatorModel:
         assert set(free) == {b for b in range(self.num_blocks) if self.ref[b] == 0}, \
             "free list differs from the unreferenced blocks"
         for s, t in enumerate(self.tables):
-            assert self.lens[s] <= len(t) * BLOCK_TOKENS
+            assert self.lens[s] <= len(t) * self.bt
         assert len(self.entries) == len(self.entry_of)
         for key, b in self.entries.items():
             assert self.entry_of[b] == key

@@ -31,7 +31,7 @@ class Shadow:
 
     def __init__(self, model: AllocatorModel):
         self.m = model
-        self.slots = [[None] * BLOCK_TOKENS for _ in range(model.num_blocks)]
+        self.slots = [[None] * model.bt for _ in range(model.num_blocks)]
         self.intended = [[] for _ in range(model.max_seqs)]
         self.copies = 0
 
@@ -41,8 +41,8 @@ class Shadow:
             self.copies += 1
 
     def write(self, seq, pos, key):
-        b = self.m.tables[seq][pos // BLOCK_TOKENS]
-        self.slots[b][pos % BLOCK_TOKENS] = key
+        b = self.m.tables[seq][pos // self.m.bt]
+        self.slots[b][pos % self.m.bt] = key
         it = self.intended[seq]
         while len(it) <= pos:
             it.append(None)
@@ -53,7 +53,7 @@ class Shadow:
         for s in range(self.m.max_seqs):
             n = self.m.lens[s]
             assert n == len(self.intended[s]), (s, n, len(self.intended[s]))
-            got = [self.slots[self.m.tables[s][p // BLOCK_TOKENS]][p % BLOCK_TOKENS]
+            got = [self.slots[self.m.tables[s][p // self.m.bt]][p % self.m.bt]
                    for p in range(n)]
             assert got == self.intended[s], "sequence %d reads what it did not write" % s
 
@@ -334,12 +334,13 @@ def test_queued_copies_act_one_after_another():
     assert np.array_equal(block(k, 4), k0[4]) and np.array_equal(block(k, 3), k0[3])
 
 
-def test_brute_force_random_operations_against_slot_contents():
-    rng = random.Random(2024)
+@pytest.mark.parametrize("bt", [16, 32])
+def test_brute_force_random_operations_against_slot_contents(bt):
+    rng = random.Random(2024 + bt)
     hits = copies = 0
     for trial in range(600):
         nb, ns = rng.choice([(6, 3), (10, 4), (24, 5)])
-        m = AllocatorModel(nb, ns, 6, seed=rng.choice([0, 7, 99]))
+        m = AllocatorModel(nb, ns, 6, seed=rng.choice([0, 7, 99]), block_tokens=bt)
         sh = Shadow(m)
         committed = []                                # key lists registered so far
         tag = 0
@@ -351,7 +352,7 @@ def test_brute_force_random_operations_against_slot_contents():
             try:
                 if op == "extend":
                     seqs = rng.sample(range(ns), rng.randint(1, 2))
-                    n = rng.choice([1, 3, 16, 17])
+                    n = rng.choice([1, 3, 16, 17, 32, 33])
                     sh.extend(seqs, [keys_of(tag * 8 + i, n) for i in range(len(seqs))])
                 elif op == "fork":
                     sh.fork(s, rng.randrange(ns))
@@ -369,7 +370,7 @@ def test_brute_force_random_operations_against_slot_contents():
                     hits += sh.match(s, keys + keys_of(tag, rng.randint(0, 20))) > 0
                     assert len(m.pending) == before
                 elif op == "commit" and m.lens[s] > 0:
-                    n = rng.randint(16, max(16, m.lens[s])) if m.lens[s] >= 16 else m.lens[s]
+                    n = rng.randint(bt, max(bt, m.lens[s])) if m.lens[s] >= bt else m.lens[s]
                     sh.commit(s, n)
                     committed.append(list(sh.intended[s][:n]))
             except AllocError:
