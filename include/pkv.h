@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 5
+#define PKV_ABI_VERSION 6
 /* Tokens per physical block ([InferScale] §2; [KV essay] "Paged attention"). */
 #define PKV_BLOCK_TOKENS 16
 
@@ -147,12 +147,19 @@ typedef struct {
 
 /* Host allocator configuration. free_list_seed 0 = ascending initial order;
  * otherwise the Fisher-Yates shuffle (i from N-1 down to 1, j = next() mod
- * (i+1)) driven by splitmix64 seeded with free_list_seed. */
+ * (i+1)) driven by splitmix64 seeded with free_list_seed.
+ *
+ * block_tokens: tokens per allocation block, 16 (or 0) or 32 ([Inside
+ * engines] "PagedAttention": blocks of e.g. 16 or 32 tokens).  A 32-token
+ * block b is the pair of 16-token planes 2b and 2b+1 of the pool (which then
+ * holds 2 * num_blocks planes); allocation, sharing, copy-on-write, prefix
+ * entries and window trimming work in blocks of block_tokens, while
+ * pkv_block_table exports the table of 16-token planes every kernel reads. */
 typedef struct {
   int32_t num_blocks;
   int32_t max_seqs;
   int32_t max_blocks_per_seq;
-  int32_t _reserved;
+  int32_t block_tokens;
   uint64_t free_list_seed;
 } pkv_cache_config;
 
@@ -226,10 +233,15 @@ pkv_status pkv_extend(pkv_cache* cache, const int32_t* seqs, int32_t n_seqs,
  * count reaches 0 join the tail of the free list.  Its length becomes 0. */
 pkv_status pkv_free_seq(pkv_cache* cache, int32_t seq);
 
-/* Export block tables: table_out (host, n_seqs x max_blocks_per_seq int32,
- * padded with -1) and lens_out (host, n_seqs int64; may be NULL). */
+/* Export block tables of 16-token planes: table_out (host, n_seqs rows of
+ * pkv_table_width(cache) int32, padded with -1; a 32-token block b appears
+ * as planes 2b, 2b+1) and lens_out (host, n_seqs int64; may be NULL). */
 pkv_status pkv_block_table(const pkv_cache* cache, const int32_t* seqs, int32_t n_seqs,
                            int32_t* table_out, int64_t* lens_out);
+
+/* Entries per exported table row: max_blocks_per_seq * block_tokens / 16;
+ * -1 for a NULL cache. */
+int32_t pkv_table_width(const pkv_cache* cache);
 
 /* Number of free blocks. Returns -1 for a NULL cache. */
 int32_t pkv_num_free_blocks(const pkv_cache* cache);

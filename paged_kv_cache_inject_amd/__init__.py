@@ -65,7 +65,7 @@ class pkv_run(ctypes.Structure):
 
 class pkv_cache_config(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("max_seqs", ctypes.c_int32),
-                ("max_blocks_per_seq", ctypes.c_int32), ("_reserved", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("block_tokens", ctypes.c_int32),
                 ("free_list_seed", ctypes.c_uint64)]
 
 
@@ -86,6 +86,7 @@ SIGNATURES = {
     "pkv_extend": (_I32, [_P, _P, _I32, _I32, _P]),
     "pkv_free_seq": (_I32, [_P, _I32]),
     "pkv_block_table": (_I32, [_P, _P, _I32, _P, _P]),
+    "pkv_table_width": (_I32, [_P]),
     "pkv_num_free_blocks": (_I32, [_P]),
     "pkv_free_list": (_I32, [_P, _P, _I32]),
     "pkv_fork": (_I32, [_P, _I32, _I32]),
@@ -179,9 +180,9 @@ def pkv_kv_bytes(n_layers, n_kv_heads, head_dim, elem_bytes, n_tokens) -> int:
 # ---------------------------------------------------------------------------
 # Allocator
 # ---------------------------------------------------------------------------
-def pkv_cache_create(num_blocks, max_seqs, max_blocks_per_seq, free_list_seed=0):
+def pkv_cache_create(num_blocks, max_seqs, max_blocks_per_seq, free_list_seed=0, block_tokens=16):
     lib = load_library()
-    cfg = pkv_cache_config(num_blocks, max_seqs, max_blocks_per_seq, 0, free_list_seed)
+    cfg = pkv_cache_config(num_blocks, max_seqs, max_blocks_per_seq, block_tokens, free_list_seed)
     h = ctypes.c_void_p()
     _check(lib.pkv_cache_create(ctypes.byref(cfg), ctypes.byref(h)))
     return h
@@ -214,11 +215,19 @@ def pkv_free_seq(cache, seq):
     _check(load_library().pkv_free_seq(cache, seq))
 
 
-def pkv_block_table(cache, seqs, max_blocks_per_seq):
-    """Returns (int32 table [n][max_blocks_per_seq], int64 lens [n])."""
+def pkv_table_width(cache) -> int:
+    return load_library().pkv_table_width(cache)
+
+
+def pkv_block_table(cache, seqs, max_blocks_per_seq=None):
+    """Returns (int32 table of 16-token planes [n][pkv_table_width], int64
+    lens [n]); max_blocks_per_seq, if given, must match the cache's width."""
     import numpy as np
     s = np.ascontiguousarray(seqs, dtype=np.int32)
-    table = np.empty((len(s), max_blocks_per_seq), dtype=np.int32)
+    width = pkv_table_width(cache)
+    if max_blocks_per_seq is not None and max_blocks_per_seq != width:
+        raise ValueError("table width is %d, not %d" % (width, max_blocks_per_seq))
+    table = np.empty((len(s), width), dtype=np.int32)
     lens = np.empty(len(s), dtype=np.int64)
     _check(load_library().pkv_block_table(cache, s.ctypes.data, len(s), table.ctypes.data,
                                           lens.ctypes.data))

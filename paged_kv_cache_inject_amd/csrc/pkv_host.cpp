@@ -140,7 +140,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // preceding 16 positions (-1 at position 0) and this block's 16 keys.
 struct PrefixKey {
   int32_t parent = -1;
-  uint64_t keys[kBlock] = {};
+  uint64_t keys[32] = {};  // one per position of a block (16 or 32 used)
   bool operator==(const PrefixKey& o) const {
     return parent == o.parent && std::memcmp(keys, o.keys, sizeof(keys)) == 0;
   }
@@ -162,6 +162,9 @@ struct pkv_cache {
   int32_t num_blocks = 0;
   int32_t max_seqs = 0;
   int32_t max_blocks_per_seq = 0;
+  int32_t bt = kBlock;   // tokens per allocation block (16 or 32)
+  int32_t sub = 1;       // 16-token planes per block
+  int64_t blocks_for(int64_t n_tokens) const { return (n_tokens + bt - 1) / bt; }
   // FIFO free list, doubly linked through block ids (head = next handed out),
   // so that a cached block can be taken back from anywhere in O(1).
   std::vector<int32_t> fl_prev, fl_next;
@@ -310,8 +313,9 @@ pkv_status check_rope(int32_t mode, const float* cos, const float* sin, int32_t 
 // level of an earlier copy it depends on.
 pkv_status flush_copies(pkv_cache* c, const pkv_pool& pool, hipStream_t stream) {
   for (const auto& pr : c->pending)
-    if (pr.first >= pool.num_blocks || pr.second >= pool.num_blocks)
-      return fail(PKV_E_RANGE, "copy %d -> %d outside the pool's %d blocks", pr.first,
+    if ((int64_t(pr.first) + 1) * c->sub > pool.num_blocks ||
+        (int64_t(pr.second) + 1) * c->sub > pool.num_blocks)
+      return fail(PKV_E_RANGE, "copy %d -> %d outside the pool's %d planes", pr.first,
                   pr.second, pool.num_blocks);
   std::unordered_map<int32_t, int32_t> read_at, written_at;  // highest level per block
   std::vector<int32_t> level(c->pending.size());
@@ -337,11 +341,13 @@ pkv_status flush_copies(pkv_cache* c, const pkv_pool& pool, hipStream_t stream) 
     for (size_t i = 0; i <= c->pending.size(); ++i) {
       const bool last = i == c->pending.size();
       if (!last && level[i] == lv) {
-        batch.src[batch.n] = c->pending[i].first;
-        batch.dst[batch.n] = c->pending[i].second;
-        ++batch.n;
+        for (int32_t k = 0; k < c->sub; ++k) {  // the block's 16-token planes
+          batch.src[batch.n] = c->pending[i].first * c->sub + k;
+          batch.dst[batch.n] = c->pending[i].second * c->sub + k;
+          ++batch.n;
+        }
       }
-      if (batch.n == pkv::kCopyBatch || (last && batch.n > 0)) {
+      if (batch.n + c->sub > pkv::kCopyBatch || (last && batch.n > 0)) {
         hipError_t e = pkv::launch_copy_blocks(pool, batch, stream);
         if (e != hipSuccess) return hip_fail(e, "block copy launch");
         batch.n = 0;
@@ -409,9 +415,15 @@ pkv_status pkv_cache_create(const pkv_cache_config* cfg, pkv_cache** out) {
   if (!cfg || !out) return fail(PKV_E_INVALID, "null argument");
   if (cfg->num_blocks <= 0 || cfg->max_seqs <= 0 || cfg->max_blocks_per_seq <= 0)
     return fail(PKV_E_INVALID, "cache sizes must be positive");
+  const int32_t bt = cfg->block_tokens == 0 ? kBlock : cfg->block_tokens;
+  if (bt != 16 && bt != 32) return fail(PKV_E_INVALID, "block_tokens must be 16 or 32");
+  if (int64_t(cfg->num_blocks) * (bt / kBlock) > INT32_MAX)
+    return fail(PKV_E_INVALID, "too many blocks");
   pkv_cache* c = new (std::nothrow) pkv_cache();
   if (!c) return fail(PKV_E_INVALID, "out of host memory");
   c->num_blocks = cfg->num_blocks;
+  c->bt = bt;
+  c->sub = bt / kBlock;
   c->max_seqs = cfg->max_seqs;
   c->max_blocks_per_seq = cfg->max_blocks_per_seq;
   std::vector<int32_t> order(cfg->num_blocks);
@@ -441,7 +453,7 @@ void pkv_cache_destroy(pkv_cache* cache) { delete cache; }
 pkv_status pkv_alloc_blocks(pkv_cache* c, int32_t seq, int64_t n_tokens) {
   if (pkv_status st = check_seq(c, seq)) return st;
   if (n_tokens < 0) return fail(PKV_E_INVALID, "negative token count");
-  const int64_t want = blocks_for(n_tokens);
+  const int64_t want = c->blocks_for(n_tokens);
   if (want > c->max_blocks_per_seq)
     return fail(PKV_E_RANGE, "%lld blocks exceed max_blocks_per_seq %d", (long long)want,
                 c->max_blocks_per_seq);
@@ -461,7 +473,7 @@ pkv_status pkv_set_blocks(pkv_cache* c, int32_t seq, const int32_t* ids, int32_t
   if (n_ids > c->max_blocks_per_seq)
     return fail(PKV_E_RANGE, "%d blocks exceed max_blocks_per_seq %d", n_ids,
                 c->max_blocks_per_seq);
-  if (len < 0 || len > int64_t(n_ids) * kBlock)
+  if (len < 0 || len > int64_t(n_ids) * c->bt)
     return fail(PKV_E_RANGE, "length %lld does not fit %d blocks", (long long)len, n_ids);
   std::vector<uint8_t> taken(c->num_blocks, 0);
   for (int32_t i = 0; i < n_ids; ++i) {
@@ -494,12 +506,12 @@ pkv_status pkv_extend(pkv_cache* c, const int32_t* seqs, int32_t n_seqs, int32_t
     if (seen[seqs[i]]) return fail(PKV_E_INVALID, "sequence %d repeated", seqs[i]);
     seen[seqs[i]] = 1;
     const int32_t s = seqs[i];
-    const int64_t want = blocks_for(c->lens[s] + n_new);
+    const int64_t want = c->blocks_for(c->lens[s] + n_new);
     if (want > c->max_blocks_per_seq)
       return fail(PKV_E_RANGE, "sequence %d would need %lld blocks", s, (long long)want);
     total += std::max<int64_t>(0, want - int64_t(c->tables[s].size()));
-    if (n_new > 0 && c->lens[s] % kBlock) {
-      const int32_t b = c->tables[s][c->lens[s] / kBlock];
+    if (n_new > 0 && c->lens[s] % c->bt) {
+      const int32_t b = c->tables[s][c->lens[s] / c->bt];
       auto it = refs_then.find(b);
       const int32_t r = it == refs_then.end() ? c->ref[b] : it->second;
       if (r > 1) {
@@ -513,8 +525,8 @@ pkv_status pkv_extend(pkv_cache* c, const int32_t* seqs, int32_t n_seqs, int32_t
   for (int32_t i = 0; i < n_seqs; ++i) {
     const int32_t s = seqs[i];
     // The new positions start inside a block other sequences share: copy it.
-    if (n_new > 0 && c->lens[s] % kBlock && c->ref[c->tables[s][c->lens[s] / kBlock]] > 1)
-      c->cow(s, c->lens[s] / kBlock);
+    if (n_new > 0 && c->lens[s] % c->bt && c->ref[c->tables[s][c->lens[s] / c->bt]] > 1)
+      c->cow(s, c->lens[s] / c->bt);
     pkv_alloc_blocks(c, s, c->lens[s] + n_new);
     if (first_pos_out) first_pos_out[i] = c->lens[s];
     c->lens[s] += n_new;
@@ -537,14 +549,21 @@ pkv_status pkv_block_table(const pkv_cache* c, const int32_t* seqs, int32_t n_se
     return fail(PKV_E_INVALID, "bad arguments");
   for (int32_t i = 0; i < n_seqs; ++i)
     if (pkv_status st = check_seq(c, seqs[i])) return st;
+  const int64_t width = int64_t(c->max_blocks_per_seq) * c->sub;
   for (int32_t i = 0; i < n_seqs; ++i) {
     const auto& t = c->tables[seqs[i]];
-    int32_t* row = table_out + int64_t(i) * c->max_blocks_per_seq;
-    for (int32_t j = 0; j < c->max_blocks_per_seq; ++j)
-      row[j] = j < int32_t(t.size()) ? t[j] : -1;
+    int32_t* row = table_out + int64_t(i) * width;
+    for (int64_t j = 0; j < width; ++j) {
+      const int64_t blk = j / c->sub;
+      row[j] = blk < int64_t(t.size()) && t[blk] >= 0 ? t[blk] * c->sub + int32_t(j % c->sub) : -1;
+    }
     if (lens_out) lens_out[i] = c->lens[seqs[i]];
   }
   return ok();
+}
+
+int32_t pkv_table_width(const pkv_cache* c) {
+  return c ? c->max_blocks_per_seq * c->sub : -1;
 }
 
 int32_t pkv_num_free_blocks(const pkv_cache* c) {
@@ -604,11 +623,11 @@ pkv_status pkv_prefix_match(pkv_cache* c, int32_t seq, const uint64_t* keys, int
   if (n_keys < 0 || (n_keys > 0 && !keys)) return fail(PKV_E_INVALID, "bad key list");
   if (!c->tables[seq].empty() || c->lens[seq] != 0)
     return fail(PKV_E_INVALID, "prefix match needs an empty sequence");
-  const int64_t full = std::min<int64_t>(n_keys / kBlock, c->max_blocks_per_seq);
+  const int64_t full = std::min<int64_t>(n_keys / c->bt, c->max_blocks_per_seq);
   PrefixKey key;
   auto& t = c->tables[seq];
   for (int64_t i = 0; i < full; ++i) {
-    std::memcpy(key.keys, keys + i * kBlock, sizeof(key.keys));
+    std::memcpy(key.keys, keys + i * c->bt, sizeof(uint64_t) * c->bt);
     auto it = c->entries.find(key);
     if (it == c->entries.end()) break;
     const int32_t b = it->second;
@@ -617,7 +636,7 @@ pkv_status pkv_prefix_match(pkv_cache* c, int32_t seq, const uint64_t* keys, int
     t.push_back(b);
     key.parent = b;
   }
-  c->lens[seq] = int64_t(t.size()) * kBlock;
+  c->lens[seq] = int64_t(t.size()) * c->bt;
   if (matched_out) *matched_out = c->lens[seq];
   return ok();
 }
@@ -628,7 +647,7 @@ pkv_status pkv_prefix_commit(pkv_cache* c, int32_t seq, const uint64_t* keys, in
   if (n_keys > c->lens[seq])
     return fail(PKV_E_RANGE, "%lld keys for a sequence of %lld tokens", (long long)n_keys,
                 (long long)c->lens[seq]);
-  const int64_t full = n_keys / kBlock;
+  const int64_t full = n_keys / c->bt;
   for (int64_t i = 0; i < full; ++i)
     if (c->tables[seq][i] < 0)
       return fail(PKV_E_RANGE, "keys cover positions the sequence no longer holds");
@@ -636,7 +655,7 @@ pkv_status pkv_prefix_commit(pkv_cache* c, int32_t seq, const uint64_t* keys, in
   PrefixKey key;
   for (int64_t i = 0; i < full; ++i) {
     const int32_t b = c->tables[seq][i];
-    std::memcpy(key.keys, keys + i * kBlock, sizeof(key.keys));
+    std::memcpy(key.keys, keys + i * c->bt, sizeof(uint64_t) * c->bt);
     auto it = c->entries.find(key);
     if (it != c->entries.end()) {
       key.parent = it->second;
@@ -671,7 +690,7 @@ pkv_status pkv_trim_window(pkv_cache* c, const int32_t* seqs, int32_t n_seqs, in
   int64_t dropped = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
     auto& t = c->tables[seqs[i]];
-    const int64_t keep_from = std::max<int64_t>(0, c->lens[seqs[i]] - window) / kBlock;
+    const int64_t keep_from = std::max<int64_t>(0, c->lens[seqs[i]] - window) / c->bt;
     for (int64_t j = 0; j < std::min<int64_t>(keep_from, int64_t(t.size())); ++j) {
       const int32_t b = t[j];
       if (b < 0) continue;
@@ -757,10 +776,12 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
   // block several sequences share gets one descriptor per writing sequence
   // (copy-on-write below gives all but the last writer a private copy), so
   // descriptors hang off the block's current id in a short chain.
+  // Descriptors are per 16-token plane; copy-on-write is per allocation
+  // block (a 32-token block is planes 2b, 2b+1).
   std::vector<InjectDesc> descs;
-  std::vector<int32_t> dseq, dblk, dnext;  // writer, block id before copy-on-write, chain
-  if (int64_t(c->desc_of_block.size()) < int64_t(c->num_blocks))
-    c->desc_of_block.assign(c->num_blocks, -1);
+  std::vector<int32_t> dseq, dblk, dnext;  // writer, plane id before copy-on-write, chain
+  if (int64_t(c->desc_of_block.size()) < int64_t(c->num_blocks) * c->sub)
+    c->desc_of_block.assign(int64_t(c->num_blocks) * c->sub, -1);
   std::vector<int32_t>& desc_of_block = c->desc_of_block;
   auto reset_scratch = [&]() {
     for (int32_t b : dblk) desc_of_block[b] = -1;
@@ -777,9 +798,9 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
     if (run.n_tokens == 0) continue;
     const auto& table = c->tables[run.seq];
     const int64_t end = int64_t(run.dst_pos) + run.n_tokens;
-    if (end > int64_t(table.size()) * kBlock)
-      st = fail(PKV_E_RANGE, "run %d ends at %lld past the %zu reserved slots of seq %d", r,
-                (long long)end, table.size() * kBlock, run.seq);
+    if (end > int64_t(table.size()) * c->bt)
+      st = fail(PKV_E_RANGE, "run %d ends at %lld past the %lld reserved slots of seq %d", r,
+                (long long)end, (long long)(int64_t(table.size()) * c->bt), run.seq);
     else if (end > max_pos)
       st = fail(PKV_E_RANGE, "run %d ends at %lld past the rotary table (%d)", r, (long long)end,
                 max_pos);
@@ -792,16 +813,18 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
     }
     for (int32_t t = 0; t < run.n_tokens; ++t) {
       const int32_t p = run.dst_pos + t;
-      const int32_t blk = table[p / kBlock];
-      if (blk < 0) {
+      const int32_t cb = table[p / c->bt];
+      if (cb < 0) {
         reset_scratch();
         return fail(PKV_E_RANGE, "seq %d position %d lies in a block a window trim dropped",
                     run.seq, p);
       }
-      if (blk >= pool->num_blocks) {
+      const int64_t plane = int64_t(cb) * c->sub + (p % c->bt) / kBlock;
+      if (plane >= pool->num_blocks) {
         reset_scratch();
-        return fail(PKV_E_RANGE, "block %d outside the pool", blk);
+        return fail(PKV_E_RANGE, "block %d outside the pool", cb);
       }
+      const int32_t blk = int32_t(plane);
       int32_t di = desc_of_block[blk];
       while (di >= 0 && dseq[di] != run.seq) di = dnext[di];
       if (di < 0) {
@@ -840,13 +863,23 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
     if (pkv_status st = resolve_source(src->k, "source K", &src_dev.k, &k_host)) return st;
     if (pkv_status st = resolve_source(src->v, "source V", &src_dev.v, &v_host)) return st;
   }
-  // Copy-on-write, all-or-nothing: count the copies with the reference
-  // counts as they will be when each block is reached.
+  // Copy-on-write, all-or-nothing: the written allocation blocks in order of
+  // first touch, copies counted with the reference counts as they will be
+  // when each block is reached.
   {
+    std::vector<std::pair<int32_t, int64_t>> touched;  // (seq, block index)
+    {
+      std::unordered_map<int64_t, char> seen;
+      for (size_t i = 0; i < descs.size(); ++i) {
+        const int64_t idx = descs[i].pos_base / c->bt;
+        if (seen.emplace(int64_t(dseq[i]) * c->max_blocks_per_seq + idx, 1).second)
+          touched.emplace_back(dseq[i], idx);
+      }
+    }
     std::unordered_map<int32_t, int32_t> refs_then;
     int64_t need = 0;
-    for (size_t i = 0; i < descs.size(); ++i) {
-      const int32_t b = dblk[i];
+    for (const auto& si : touched) {
+      const int32_t b = c->tables[si.first][si.second];
       auto it = refs_then.find(b);
       const int32_t rc = it == refs_then.end() ? c->ref[b] : it->second;
       if (rc > 1) {
@@ -857,16 +890,18 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
     if (need > c->fl_size)
       return fail(PKV_E_OOM, "copy-on-write needs %lld blocks, %d free", (long long)need,
                   c->fl_size);
-    if ((need > 0 || !c->pending.empty()) && c->num_blocks > pool->num_blocks)
+    if ((need > 0 || !c->pending.empty()) &&
+        int64_t(c->num_blocks) * c->sub > pool->num_blocks)
       return fail(PKV_E_INVALID, "block copies need every block of the cache (%d) inside the "
-                  "pool (%d)", c->num_blocks, pool->num_blocks);
-    for (size_t i = 0; i < descs.size(); ++i) {
-      const int32_t seq = dseq[i];
-      const int64_t idx = descs[i].pos_base / kBlock;
-      const int32_t b = c->tables[seq][idx];
-      if (c->ref[b] > 1) c->cow(seq, idx);
+                  "pool (%d planes)", c->num_blocks, pool->num_blocks);
+    for (const auto& si : touched) {
+      const int32_t b = c->tables[si.first][si.second];
+      if (c->ref[b] > 1) c->cow(si.first, si.second);
       else c->forget(b);  // written in place: no longer holds what its entry says
-      descs[i].phys_block = c->tables[seq][idx];
+    }
+    for (size_t i = 0; i < descs.size(); ++i) {
+      const int64_t idx = descs[i].pos_base / c->bt;
+      descs[i].phys_block = c->tables[dseq[i]][idx] * c->sub + (descs[i].pos_base % c->bt) / kBlock;
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -16,7 +16,7 @@ class Pair:
     """The library (device pool, allocator) and the oracle (host pool,
     allocator model) driven through the same operations."""
 
-    def __init__(self, dtype, L=2, H=2, d=64, NB=32, S=5, MB=8, max_pos=256, seed=0):
+    def __init__(self, dtype, L=2, H=2, d=64, NB=32, S=5, MB=8, max_pos=256, seed=0, bt=16):
         import paged_kv_cache_inject_amd as pkv
         from oracle.allocator import AllocatorModel
         from oracle.rope import rope_table
@@ -25,11 +25,12 @@ class Pair:
         self.pkv, self.gu = pkv, gu
         self.rng = np.random.default_rng(seed)
         self.L, self.H, self.d, self.NB, self.S, self.MB = L, H, d, NB, S, MB
+        self.bt, self.sub = bt, bt // 16                  # tokens per block, planes per block
         self.max_pos = max_pos
         self.dtype = dtype
         self.sdt = "bf16"
         fill = 0x5A if dtype == "fp8" else 0x7FAB
-        self.dp = gu.DevicePool(L, NB, H, d, dtype, fill_bits=fill)
+        self.dp = gu.DevicePool(L, NB * self.sub, H, d, dtype, fill_bits=fill)
         self.ks = self.vs = None
         if dtype == "fp8":
             self.ks = self.rng.uniform(0.004, 0.03, size=(L, H)).astype(np.float32)
@@ -37,8 +38,8 @@ class Pair:
             self.dp.set_scales(self.ks, self.vs)
         self.ref = np.full(self.dp.total, fill, dtype=np.uint8 if dtype == "fp8" else np.uint16)
         self.kp, self.vp = self.dp.oracle_arrays(self.ref)
-        self.cache = pkv.pkv_cache_create(NB, S, MB, free_list_seed=seed + 1)
-        self.m = AllocatorModel(NB, S, MB, seed=seed + 1)
+        self.cache = pkv.pkv_cache_create(NB, S, MB, free_list_seed=seed + 1, block_tokens=bt)
+        self.m = AllocatorModel(NB, S, MB, seed=seed + 1, block_tokens=bt)
         self.o_cos, self.o_sin = rope_table(d, 10000.0, max_pos)
         _, _, self.dcos, self.dsin = gu.rope_tables(d, max_pos)
         self.n_src = 200
@@ -51,11 +52,18 @@ class Pair:
         self.keep = []
         self.copies = 0                          # block copies carried out so far
 
+    def planes(self):
+        """The model's tables as rows of 16-token planes."""
+        from oracle.allocator import expand_table
+        return [expand_table(t, self.bt) for t in self.m.tables]
+
     # -- checks ----------------------------------------------------------------
     def check_host(self, what):
         pkv = self.pkv
-        t, lens = pkv.pkv_block_table(self.cache, list(range(self.S)), self.MB)
-        assert [list(r[r >= 0]) for r in t] == self.m.tables, what
+        t, lens = pkv.pkv_block_table(self.cache, list(range(self.S)))
+        got = [[int(x) for x in r] for r in t]
+        want = [p + [-1] * (t.shape[1] - len(p)) for p in self.planes()]
+        assert got == want, what
         assert list(lens) == self.m.lens, what
         assert pkv.pkv_free_list(self.cache) == list(self.m.free), what
         assert [pkv.pkv_block_refcount(self.cache, b) for b in range(self.NB)] == self.m.ref
@@ -70,10 +78,11 @@ class Pair:
     # -- operations --------------------------------------------------------------
     def flush(self):
         from oracle import inject as o_inject
+        from oracle.allocator import expand_pairs
         self.pkv.pkv_copy_blocks(self.cache, self.dp.desc())
         pairs = self.m.take_pending()
         self.copies += len(pairs)
-        o_inject.copy_blocks(self.kp, self.vp, self.dp.spec(), pairs)
+        o_inject.copy_blocks(self.kp, self.vp, self.dp.spec(), expand_pairs(pairs, self.bt))
 
     def extend_append(self, seqs, n):
         import torch
@@ -84,7 +93,7 @@ class Pair:
         assert first == self.m.extend(seqs, n)
         self.check_host("after extend")
         self.flush()
-        table, _ = pkv.pkv_block_table(self.cache, seqs, self.MB)
+        table, _ = pkv.pkv_block_table(self.cache, seqs)
         tdev = torch.from_numpy(table).cuda()
         fdev = torch.from_numpy(np.asarray(first, np.int32)).cuda()
         for layer in range(self.L):
@@ -95,7 +104,7 @@ class Pair:
             self.keep.append((kd, vd, tdev, fdev))
             pkv.pkv_append_kv(self.dp.desc(), layer, tdev, fdev, n, kd, vd, "pairs", self.dcos,
                               self.dsin, self.max_pos, new_dtype=self.sdt)
-            o_inject.append(self.kp, self.vp, self.dp.spec(), layer, self.m.tables, self.m.lens,
+            o_inject.append(self.kp, self.vp, self.dp.spec(), layer, self.planes(), self.m.lens,
                             seqs, n, k_new, v_new, "pairs", self.o_cos, self.o_sin,
                             src_dtype=self.sdt, k_scale=self.ks, v_scale=self.vs)
 
@@ -106,11 +115,12 @@ class Pair:
         self.keep.append(ws)
         pkv.pkv_inject(self.cache, self.dp.desc(), self.src, runs, 0, self.L, "pairs", self.dcos,
                        self.dsin, self.max_pos, ws)
+        from oracle.allocator import expand_pairs
         self.m.prepare_inject(runs)
         pairs = self.m.take_pending()
         self.copies += len(pairs)
-        o_inject.copy_blocks(self.kp, self.vp, self.dp.spec(), pairs)
-        lens = o_inject.inject(self.kp, self.vp, self.dp.spec(), self.m.tables, self.m.lens, runs,
+        o_inject.copy_blocks(self.kp, self.vp, self.dp.spec(), expand_pairs(pairs, self.bt))
+        lens = o_inject.inject(self.kp, self.vp, self.dp.spec(), self.planes(), self.m.lens, runs,
                                self.src_k.reshape(-1), self.src_v.reshape(-1),
                                self.n_src * self.H * self.d, self.H * self.d, 0, self.L, "pairs",
                                self.o_cos, self.o_sin, src_dtype=self.sdt, k_scale=self.ks,
@@ -124,13 +134,13 @@ class Pair:
         from workloads.configs import host_normal
         pkv, gu = self.pkv, self.gu
         seqs = list(range(self.S))
-        table, lens = pkv.pkv_block_table(self.cache, seqs, self.MB)
+        table, lens = pkv.pkv_block_table(self.cache, seqs)
         q = host_normal(self.rng, (self.S, hq, self.d), "bf16")
         q_dev = gu.to_device_raw(q.reshape(-1), "bf16").view(q.shape)
         tdev = torch.from_numpy(table).cuda()
         for layer in range(self.L):
             ref, ref_lse = o_att.decode_paged(q, self.kp, self.vp, self.dp.spec(), layer,
-                                              self.m.tables, self.m.lens, hq, by_plane=True,
+                                              self.planes(), self.m.lens, hq, by_plane=True,
                                               q_dtype="bf16", k_scale=self.ks, v_scale=self.vs)
             out, lse = gu.decode(self.dp, layer, q_dev, tdev, lens, hq, 0, q_dtype="bf16")
             gu.assert_close(out.cpu().numpy(), ref, "decode out layer %d" % layer)
@@ -140,13 +150,14 @@ class Pair:
 STEPS = 120
 
 
-@pytest.mark.parametrize("dtype,seed", [("bf16", 1), ("bf16", 2), ("fp8", 3)])
-def test_random_sharing_operations_pool_matches_oracle(dtype, seed):
+@pytest.mark.parametrize("dtype,seed,bt", [("bf16", 1, 16), ("bf16", 2, 16), ("fp8", 3, 16),
+                                           ("bf16", 7, 32), ("fp8", 13, 32)])
+def test_random_sharing_operations_pool_matches_oracle(dtype, seed, bt):
     from oracle.allocator import AllocError
-    P = Pair(dtype, seed=seed)
+    P = Pair(dtype, seed=seed, bt=bt)
     pkv, gu, m = P.pkv, P.gu, P.m
     rng = np.random.default_rng(1000 + seed)     # operation choices (data comes from P.rng)
-    gu.say("sharing random ops", dtype, seed)
+    gu.say("sharing random ops", dtype, seed, "block", bt)
     history = []
     forks = hits = injects = 0
     for step in range(STEPS):
@@ -157,9 +168,9 @@ def test_random_sharing_operations_pool_matches_oracle(dtype, seed):
             if op == "extend":
                 seqs = sorted(set(rng.integers(0, P.S, size=int(rng.integers(1, 3))).tolist()))
                 n = int(rng.choice([1, 5, 16]))
-                if any(m.lens[x] + n > P.MB * 16 for x in seqs):
+                if any(m.lens[x] + n > P.MB * P.bt for x in seqs):
                     continue
-                if sum(-(-(m.lens[x] + n) // 16) - len(m.tables[x]) + 1 for x in seqs) > len(m.free):
+                if sum(-(-(m.lens[x] + n) // P.bt) - len(m.tables[x]) + 1 for x in seqs) > len(m.free):
                     continue
                 P.extend_append(seqs, n)
             elif op == "fork":
@@ -179,7 +190,7 @@ def test_random_sharing_operations_pool_matches_oracle(dtype, seed):
                 p0 = int(rng.integers(0, m.lens[s]))
                 n = int(rng.integers(1, m.lens[s] - p0 + 1))
                 src = int(rng.integers(0, P.n_src - n + 1))
-                shared = sum(1 for i in range(p0 // 16, (p0 + n - 1) // 16 + 1)
+                shared = sum(1 for i in range(p0 // P.bt, (p0 + n - 1) // P.bt + 1)
                              if m.ref[m.tables[s][i]] > 1)
                 if shared > len(m.free):
                     continue
@@ -193,9 +204,9 @@ def test_random_sharing_operations_pool_matches_oracle(dtype, seed):
                 assert pkv.pkv_prefix_match(P.cache, s, keys) == want
                 hits += want > 0
             else:
-                if m.lens[s] < 16:
+                if m.lens[s] < P.bt:
                     continue
-                n_keys = int(rng.integers(16, m.lens[s] + 1))
+                n_keys = int(rng.integers(P.bt, m.lens[s] + 1))
                 keys = [int(x) for x in rng.integers(0, 1 << 62, size=n_keys)]
                 em = ec = None
                 try:
