@@ -148,6 +148,8 @@ def decode_workload(name):
         return EXTRA["mistral-window"], window_structure()
     if name in ("70b", "70b-fp8"):
         return CONFIGS[3], llama70b_structure(CONFIGS[3])
+    if name == "70b-block32":
+        return CONFIGS[3], llama70b_structure(CONFIGS[3], block_tokens=32)
     if name == "8b":
         return CONFIGS[2], llama8b_structure(CONFIGS[2])
     if name == "ragged":
@@ -484,7 +486,7 @@ def main():
                     help="time only the pinned-host-store inject (no JSON line)")
     ap.add_argument("--cow-reps", type=int, default=10)
     ap.add_argument("--decode-workload", default="70b",
-                    choices=["70b", "8b", "ragged", "70b-fp8", "mistral-window"],
+                    choices=["70b", "8b", "ragged", "70b-fp8", "mistral-window", "70b-block32"],
                     help="decode workload timed (the reported line uses 70b)")
     args = ap.parse_args()
     if args.gpus != 1:

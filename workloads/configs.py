@@ -152,13 +152,18 @@ def llama8b_structure(cfg: Config = None, batch=None):
                 max_blocks=max_blocks, rng=rng)
 
 
-def llama70b_structure(cfg: Config = None):
-    """Config 3: all lengths 8192; one shuffled table shared by all layers."""
+def llama70b_structure(cfg: Config = None, block_tokens: int = BLOCK):
+    """Config 3: all lengths 8192; one shuffled table shared by all layers.
+    With 32-token blocks the shuffle is over block pairs of 16-token planes
+    (2b, 2b+1), the table listing planes."""
     cfg = cfg or CONFIGS[3]
     rng = np.random.default_rng(cfg.seed)
     nb = cfg.extra["num_blocks"]
     per = cfg.extra["length"] // BLOCK
-    tables = rng.permutation(nb).astype(np.int32).reshape(cfg.batch, per)
+    k = block_tokens // BLOCK
+    blocks = rng.permutation(nb // k).astype(np.int32)
+    planes = (blocks[:, None] * k + np.arange(k, dtype=np.int32)[None, :]).reshape(-1)
+    tables = planes.reshape(cfg.batch, per)
     lens = np.full(cfg.batch, cfg.extra["length"], dtype=np.int64)
     return dict(lens=lens, num_blocks=nb, tables=tables, max_blocks=per, rng=rng)
 
