@@ -1105,6 +1105,9 @@ pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int3
   if (!d_ws || ws_bytes < plan->ws_bytes)
     return fail(PKV_E_WORKSPACE, "decode workspace %zu bytes, need %zu", ws_bytes,
                 plan->ws_bytes);
+  if (int64_t(plan->items.size()) * pool->n_kv_heads > INT32_MAX)
+    return fail(PKV_E_UNSUPPORTED, "%zu work items x %d KV heads exceed one launch",
+                plan->items.size(), pool->n_kv_heads);
   char* ws = static_cast<char*>(d_ws);
   pkv::DecodeArgs a;
   a.q = d_q;
