@@ -243,6 +243,24 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None):
                batch=cfg.batch, context=int(lens.max()), layers=cfg.n_layers)
     res["value"] = res["bytes_per_step"] / (ms_step * 1e-3) / 1e9
     res["launch_gbps"] = per_launch / (res["launch_ms_avg"] * 1e-3) / 1e9
+    if cfg.n_layers == 1:
+        # A single layer re-reads the same bytes every step, part of which the
+        # 256 MB last-level cache can hold: also time each step after writing
+        # a 1 GiB scratch buffer (outside the events), median of the steps.
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cold = []
+        for k in range(steps):
+            scratch.fill_(k & 0xFF)
+            c_s, c_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c_s.record()
+            step()
+            c_e.record()
+            torch.cuda.synchronize()
+            cold.append(c_s.elapsed_time(c_e))
+        del scratch
+        res["cold_ms_per_step"] = float(np.median(cold))
+        res["cold_gbps"] = res["bytes_per_step"] / (res["cold_ms_per_step"] * 1e-3) / 1e9
+        log("decode: cold caches %.4f ms/step, %.1f GB/s" % (res["cold_ms_per_step"], res["cold_gbps"]))
     log("decode: %.3f ms/step, %.1f GB/s; per launch %.1f us -> %.1f GB/s"
         % (ms_step, res["value"], res["launch_ms_avg"] * 1e3, res["launch_gbps"]))
     pkv.pkv_decode_plan_destroy(plan)
