@@ -236,6 +236,10 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None):
                instrumented_ms_per_step=i_s.elapsed_time(i_e) / max(1, launch_steps),
                bytes_per_step=per_launch * cfg.n_layers, bytes_per_launch=per_launch,
                launch_ms_avg=float(np.mean(launch_ms)), launch_ms_p50=float(np.median(launch_ms)),
+               launch_ms_p10=float(np.percentile(launch_ms, 10)),
+               launch_ms_p90=float(np.percentile(launch_ms, 90)),
+               seed=cfg.seed,
+               tables_sha256=hashlib.sha256(np.ascontiguousarray(st["tables"]).tobytes()).hexdigest(),
                launches_timed=len(launch_ms),
                n_items=n_items, part_tokens=part_tokens, waves=waves,
                workload=cfg.workload + (" (fp8 E4M3 cache)" if fp8 else ""),
@@ -561,11 +565,18 @@ def main():
                      "kernel": "decode_mfma_kernel (pkv_decode_attention, one layer)",
                      "bytes_per_launch": dec["bytes_per_launch"],
                      "launch_us_avg": round(dec["launch_ms_avg"] * 1e3, 2),
+                     "launch_us_p10_p50_p90": [round(dec["launch_ms_p10"] * 1e3, 2),
+                                               round(dec["launch_ms_p50"] * 1e3, 2),
+                                               round(dec["launch_ms_p90"] * 1e3, 2)],
+                     "frac_of_bw_probe": round(dec["launch_gbps"] / probe, 4),
                      "launch_timing": "HIP events around each of %d launches in an instrumented "
                                       "pass of %d steps after the timed steps (%.3f ms/step)"
                                       % (dec["launches_timed"], dec["launches_timed"] // dec["layers"],
                                          dec["instrumented_ms_per_step"])},
         "bw_probe_gbps": round(probe, 1),
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", "?"),
+                   "compute_units": props.multi_processor_count},
+        "inputs": {"seed": dec["seed"], "tables_sha256": dec["tables_sha256"]},
         "cpu_baseline": cpu,
     }
     if fp8 is not None:

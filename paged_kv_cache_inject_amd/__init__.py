@@ -451,3 +451,89 @@ def pkv_decode_attention(plan, pool: pkv_pool, layer, q, tables, out, lse, works
 def pkv_bw_probe(src, sink, stream=None):
     _check(load_library().pkv_bw_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
                                        _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Object facade over the allocator handle (marshalling only; every method is
+# the C entry point of the same name without the "pkv_" prefix).
+# ---------------------------------------------------------------------------
+class Cache:
+    """A ``pkv_cache`` handle: host allocator, tables, sharing, prefix cache.
+
+    ``Cache(num_blocks, max_seqs, max_blocks_per_seq, free_list_seed=0,
+    block_tokens=16)``; release with ``close()`` (or use it in ``with``)."""
+
+    def __init__(self, num_blocks, max_seqs, max_blocks_per_seq, free_list_seed=0,
+                 block_tokens=16):
+        self.handle = pkv_cache_create(num_blocks, max_seqs, max_blocks_per_seq, free_list_seed,
+                                       block_tokens)
+
+    def close(self):
+        if self.handle is not None:
+            pkv_cache_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc_blocks(self, seq, n_tokens):
+        pkv_alloc_blocks(self.handle, seq, n_tokens)
+
+    def set_blocks(self, seq, ids, length):
+        pkv_set_blocks(self.handle, seq, ids, length)
+
+    def extend(self, seqs, n_new):
+        return pkv_extend(self.handle, seqs, n_new)
+
+    def free_seq(self, seq):
+        pkv_free_seq(self.handle, seq)
+
+    def block_table(self, seqs):
+        return pkv_block_table(self.handle, seqs)
+
+    def table_width(self):
+        return pkv_table_width(self.handle)
+
+    def num_free_blocks(self):
+        return pkv_num_free_blocks(self.handle)
+
+    def free_list(self):
+        return pkv_free_list(self.handle)
+
+    def fork(self, src_seq, dst_seq):
+        pkv_fork(self.handle, src_seq, dst_seq)
+
+    def block_refcount(self, block):
+        return pkv_block_refcount(self.handle, block)
+
+    def pending_copies(self):
+        return pkv_pending_copies(self.handle)
+
+    def copy_blocks(self, pool, stream=None):
+        pkv_copy_blocks(self.handle, pool, stream)
+
+    def prefix_match(self, seq, keys):
+        return pkv_prefix_match(self.handle, seq, keys)
+
+    def prefix_commit(self, seq, keys):
+        pkv_prefix_commit(self.handle, seq, keys)
+
+    def prefix_cached_blocks(self):
+        return pkv_prefix_cached_blocks(self.handle)
+
+    def trim_window(self, seqs, window):
+        return pkv_trim_window(self.handle, seqs, window)
+
+    def inject(self, pool, src, runs, layer_begin, layer_end, rope_mode, cos, sin, max_pos,
+               workspace, stream=None):
+        pkv_inject(self.handle, pool, src, runs, layer_begin, layer_end, rope_mode, cos, sin,
+                   max_pos, workspace, stream)

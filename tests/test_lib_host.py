@@ -368,3 +368,24 @@ def test_inject_host_validation_errors():
     _, lens = pkv.pkv_block_table(c, [0], 4)
     assert list(lens) == [0]
     pkv.pkv_cache_destroy(c)
+
+
+def test_cache_facade_is_the_handle_calls():
+    with pkv.Cache(16, 3, 8, free_list_seed=3) as c:
+        m = AllocatorModel(16, 3, 8, seed=3)
+        assert c.extend([0], 40).tolist() == m.extend([0], 40)
+        c.fork(0, 1)
+        m.fork(0, 1)
+        c.extend([1], 1)
+        m.extend([1], 1)
+        assert c.pending_copies() == m.pending
+        assert c.free_list() == list(m.free) and c.num_free_blocks() == len(m.free)
+        t, lens = c.block_table([0, 1])
+        assert [_unpad(r) for r in t] == m.tables[:2] and list(lens) == m.lens[:2]
+        c.prefix_commit(0, list(range(32)))
+        m.prefix_commit(0, list(range(32)))
+        assert c.prefix_cached_blocks() == len(m.entries) == 2
+        assert c.trim_window([0], 10) == m.trim_window([0], 10)
+        assert [c.block_refcount(b) for b in range(16)] == m.ref
+        assert c.table_width() == 8
+    assert c.handle is None
