@@ -18,6 +18,7 @@ workload.  One JSON line is printed on stdout; progress goes to stderr.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
