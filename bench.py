@@ -143,18 +143,19 @@ def bw_probe(n_bytes=8 << 30, reps=5):
 
 
 def decode_workload(name):
-    from workloads.configs import (CONFIGS, EXTRA, llama70b_structure, llama8b_structure,
-                                   ragged_mha_structure, window_structure)
+    from workloads.configs import (LLAMA8B_1LAYER, LLAMA70B_80LAYER, MISTRAL_WINDOW, RAGGED_MHA,
+                                   llama70b_structure, llama8b_structure, ragged_mha_structure,
+                                   window_structure)
     if name == "mistral-window":
-        return EXTRA["mistral-window"], window_structure()
+        return MISTRAL_WINDOW, window_structure()
     if name in ("70b", "70b-fp8"):
-        return CONFIGS[3], llama70b_structure(CONFIGS[3])
+        return LLAMA70B_80LAYER, llama70b_structure(LLAMA70B_80LAYER)
     if name == "70b-block32":
-        return CONFIGS[3], llama70b_structure(CONFIGS[3], block_tokens=32)
+        return LLAMA70B_80LAYER, llama70b_structure(LLAMA70B_80LAYER, block_tokens=32)
     if name == "8b":
-        return CONFIGS[2], llama8b_structure(CONFIGS[2])
+        return LLAMA8B_1LAYER, llama8b_structure(LLAMA8B_1LAYER)
     if name == "ragged":
-        return CONFIGS[5], ragged_mha_structure(CONFIGS[5])
+        return RAGGED_MHA, ragged_mha_structure(RAGGED_MHA)
     raise ValueError(name)
 
 
@@ -277,8 +278,8 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None):
 def run_inject(reps):
     import torch
     import paged_kv_cache_inject_amd as pkv
-    from workloads.configs import CONFIGS, inject_structure, device_normal
-    cfg = CONFIGS[4]
+    from workloads.configs import INJECT_TOP8, inject_structure, device_normal
+    cfg = INJECT_TOP8
     st = inject_structure(cfg)
     L, H, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
     n_src = st["n_src"]
@@ -334,8 +335,8 @@ def run_inject_host(reps, n_chunks=250, batch=16):
     pool.  Reported against the same run's host-to-device DMA ceiling."""
     import torch
     import paged_kv_cache_inject_amd as pkv
-    from workloads.configs import CONFIGS, inject_structure, device_normal
-    cfg = CONFIGS[4]
+    from workloads.configs import INJECT_TOP8, inject_structure, device_normal
+    cfg = INJECT_TOP8
     st = inject_structure(cfg, n_chunks=n_chunks, batch=batch)
     L, H, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
     n_src, row = st["n_src"], H * d
@@ -458,8 +459,8 @@ def cpu_baseline(budget_s=12.0):
     from threadpoolctl import threadpool_limits
     from oracle import attention as o_att
     from oracle.layout import PoolSpec
-    from workloads.configs import CONFIGS, llama70b_structure, host_normal, device_normal
-    cfg = CONFIGS[3]
+    from workloads.configs import LLAMA70B_80LAYER, llama70b_structure, host_normal, device_normal
+    cfg = LLAMA70B_80LAYER
     st = llama70b_structure(cfg)
     nb = st["num_blocks"]
     plane = 16 * cfg.head_dim

@@ -18,9 +18,9 @@ def test_inject_and_decode_with_32_token_blocks():
     from oracle.allocator import AllocatorModel, expand_table
     from oracle.rope import rope_table
     from tests import gpu_util as gu
-    from workloads.configs import CONFIGS, inject_structure, host_normal
+    from workloads.configs import INJECT_TOP8, inject_structure, host_normal
 
-    cfg = CONFIGS[4]
+    cfg = INJECT_TOP8
     st = inject_structure(cfg, n_chunks=40, batch=6)
     L, H, d, HQ = 2, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads
     n_src, row = st["n_src"], H * d

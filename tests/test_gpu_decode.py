@@ -49,8 +49,8 @@ def check_decode_all(dp, layer, q_raw, table, lens, hq, parts=(0,), variants=("a
 
 def test_llama8b_layer_full():
     from tests import gpu_util as gu
-    from workloads.configs import CONFIGS, llama8b_structure, host_normal
-    cfg = CONFIGS[2]
+    from workloads.configs import LLAMA8B_1LAYER, llama8b_structure, host_normal
+    cfg = LLAMA8B_1LAYER
     st = llama8b_structure(cfg)
     gu.say("llama8b decode: pool", st["num_blocks"], "blocks, sum len", int(st["lens"].sum()))
     dp = gu.DevicePool(1, st["num_blocks"], cfg.n_kv_heads, cfg.head_dim, cfg.dtype)
@@ -197,8 +197,8 @@ def test_theorem1_inject_equals_relative_form():
 def test_ragged_mha_full_size_sampled():
     import torch
     from tests import gpu_util as gu
-    from workloads.configs import CONFIGS, ragged_mha_structure, host_normal
-    cfg = CONFIGS[5]
+    from workloads.configs import RAGGED_MHA, ragged_mha_structure, host_normal
+    cfg = RAGGED_MHA
     st = ragged_mha_structure(cfg)
     lens = st["lens"]
     gu.say("ragged MHA: pool", st["num_blocks"], "blocks, max len", int(lens.max()))
@@ -214,8 +214,8 @@ def test_ragged_mha_full_size_sampled():
 def test_llama70b_full_size_sampled():
     import torch
     from tests import gpu_util as gu
-    from workloads.configs import CONFIGS, llama70b_structure, host_normal
-    cfg = CONFIGS[3]
+    from workloads.configs import LLAMA70B_80LAYER, llama70b_structure, host_normal
+    cfg = LLAMA70B_80LAYER
     st = llama70b_structure(cfg)
     gu.say("llama70b: 80 layers x", st["num_blocks"], "blocks")
     dp = gu.DevicePool(cfg.n_layers, st["num_blocks"], cfg.n_kv_heads, cfg.head_dim, cfg.dtype)

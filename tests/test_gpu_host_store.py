@@ -85,9 +85,9 @@ def test_reduced_workload_host_store_equals_device_store():
     import torch
     import paged_kv_cache_inject_amd as pkv
     from tests import gpu_util as gu
-    from workloads.configs import CONFIGS, inject_structure, device_normal
+    from workloads.configs import INJECT_TOP8, inject_structure, device_normal
 
-    cfg = CONFIGS[4]
+    cfg = INJECT_TOP8
     st = inject_structure(cfg, n_chunks=120, batch=8)
     L, H, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
     n_src, row = st["n_src"], H * d

@@ -21,9 +21,9 @@ def run_inject_workload(n_chunks, batch=None, check_layers=(0, 31), decode_seqs=
     from oracle.layout import PoolSpec
     from oracle.rope import rope_table
     from tests import gpu_util as gu
-    from workloads.configs import CONFIGS, inject_structure, device_normal, host_normal
+    from workloads.configs import INJECT_TOP8, inject_structure, device_normal, host_normal
 
-    cfg = CONFIGS[4]
+    cfg = INJECT_TOP8
     st = inject_structure(cfg, n_chunks=n_chunks, batch=batch)
     L, H, d, HQ = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads
     B = len(st["mem_lens"])

@@ -15,9 +15,9 @@ def run_tiny(part_tokens_list=(0, 16, 32, 48)):
     from oracle.allocator import AllocatorModel
     from oracle.rope import rope_table
     from tests import gpu_util as gu
-    from workloads.configs import CONFIGS, tiny_inputs
+    from workloads.configs import TINY, tiny_inputs
 
-    cfg = CONFIGS[1]
+    cfg = TINY
     w = tiny_inputs(cfg)
     L, H, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
     max_pos = 128

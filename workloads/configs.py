@@ -1,4 +1,4 @@
-"""The five workload shapes and their seeded input recipes.
+"""The workload shapes and their seeded input recipes.
 
 Shapes follow the pages' examples: the Llama-3.1-8B grouped-query shape
 (32 layers, 8 KV heads of 128, bf16) used for the per-fact storage cost in
@@ -38,42 +38,42 @@ class Config:
     extra: dict = field(default_factory=dict)
 
 
-CONFIGS = {
-    1: Config("tiny", "tiny fp32 reference: L=1 B=2 Hq=4 Hkv=2 d=64, lens 37/100, "
-              "16-block pool, 24-token chunk injected at 40..63 of seq 1",
-              1001, 1, 2, 4, 2, 64, "f32",
-              extra=dict(lens=(37, 100), num_blocks=16, chunk_len=24, chunk_pos=40)),
-    2: Config("llama3-8b-1layer", "Llama-3-8B-shaped single-layer decode: Hq=32 Hkv=8 d=128 "
-              "bf16, B=64, lens U[512,4096], pool 1.2x need",
-              1002, 1, 64, 32, 8, 128, "bf16", extra=dict(len_lo=512, len_hi=4096)),
-    3: Config("llama3-70b-80layer", "Llama-3-70B-shaped decode: 80 layers, Hq=64 Hkv=8 d=128 "
-              "bf16, B=32 x 8192 tokens, shuffled tables",
-              1003, 80, 32, 64, 8, 128, "bf16", extra=dict(length=8192, num_blocks=16384)),
-    4: Config("inject-top8", "KV injection + decode: top-8 of 10k chunks (64..256 tokens) of "
-              "unrotated bf16 K/V (32 layers x 8 x 128), B=64, then 32-token suffix and "
-              "one decode step",
-              1004, 32, 64, 32, 8, 128, "bf16",
-              extra=dict(n_chunks=10000, chunk_lo=64, chunk_hi=256, top_k=8,
-                         prefix_len=32, sep_len=15, suffix=32)),
-    5: Config("ragged-mha", "ragged MHA decode: Hq=Hkv=64 d=128 fp16, B=256, lens "
-              "lognormal(median 1024, sigma 1) clipped to [16,32768], random tables",
-              1005, 1, 256, 64, 64, 128, "f16",
-              extra=dict(median=1024, sigma=1.0, len_lo=16, len_hi=32768)),
-}
+TINY = Config(
+    "tiny", "tiny fp32 reference: L=1 B=2 Hq=4 Hkv=2 d=64, lens 37/100, 16-block pool, "
+    "24-token chunk injected at 40..63 of seq 1",
+    1001, 1, 2, 4, 2, 64, "f32",
+    extra=dict(lens=(37, 100), num_blocks=16, chunk_len=24, chunk_pos=40))
+LLAMA8B_1LAYER = Config(
+    "llama3-8b-1layer", "Llama-3-8B-shaped single-layer decode: Hq=32 Hkv=8 d=128 bf16, B=64, "
+    "lens U[512,4096], pool 1.2x need",
+    1002, 1, 64, 32, 8, 128, "bf16", extra=dict(len_lo=512, len_hi=4096))
+LLAMA70B_80LAYER = Config(
+    "llama3-70b-80layer", "Llama-3-70B-shaped decode: 80 layers, Hq=64 Hkv=8 d=128 bf16, "
+    "B=32 x 8192 tokens, shuffled tables",
+    1003, 80, 32, 64, 8, 128, "bf16", extra=dict(length=8192, num_blocks=16384))
+INJECT_TOP8 = Config(
+    "inject-top8", "KV injection + decode: top-8 of 10k chunks (64..256 tokens) of unrotated "
+    "bf16 K/V (32 layers x 8 x 128), B=64, then 32-token suffix and one decode step",
+    1004, 32, 64, 32, 8, 128, "bf16",
+    extra=dict(n_chunks=10000, chunk_lo=64, chunk_hi=256, top_k=8, prefix_len=32, sep_len=15,
+               suffix=32))
+RAGGED_MHA = Config(
+    "ragged-mha", "ragged MHA decode: Hq=Hkv=64 d=128 fp16, B=256, lens lognormal(median 1024, "
+    "sigma 1) clipped to [16,32768], random tables",
+    1005, 1, 256, 64, 64, 128, "f16",
+    extra=dict(median=1024, sigma=1.0, len_lo=16, len_hi=32768))
+MISTRAL_WINDOW = Config(
+    "mistral-7b-window", "Mistral-7B-shaped sliding-window decode: 32 layers, Hq=32 Hkv=8 "
+    "d=128 bf16, B=32 at position 32768 with a 4096-token window; tables hold the window's "
+    "blocks only",
+    1006, 32, 32, 32, 8, 128, "bf16", extra=dict(length=32768, window=4096))
+
+CONFIGS = {c.name: c for c in (TINY, LLAMA8B_1LAYER, LLAMA70B_80LAYER, INJECT_TOP8, RAGGED_MHA,
+                                MISTRAL_WINDOW)}
 
 
-# Workloads of the extensions beyond the five configurations above.
-EXTRA = {
-    "mistral-window": Config(
-        "mistral-7b-window", "Mistral-7B-shaped sliding-window decode: 32 layers, Hq=32 Hkv=8 "
-        "d=128 bf16, B=32 at position 32768 with a 4096-token window; tables hold the "
-        "window's blocks only",
-        1006, 32, 32, 32, 8, 128, "bf16", extra=dict(length=32768, window=4096)),
-}
-
-
-def get_config(n: int) -> Config:
-    return CONFIGS[n]
+def get_config(name: str) -> Config:
+    return CONFIGS[name]
 
 
 def blocks_for(n: int) -> int:
@@ -115,12 +115,12 @@ def deal_tables(ids: np.ndarray, lens, max_blocks: int) -> np.ndarray:
 
 
 def tiny_inputs(cfg: Config = None):
-    """Config 1: host arrays for a two-run prefill and one injected chunk.
+    """Tiny workload: host arrays for a two-run prefill and one injected chunk.
 
     The source store holds seq 0's 37 tokens, seq 1's 100 tokens and the
     24-token chunk, all unrotated: [L][137 + 24][Hkv][d] fp32.
     """
-    cfg = cfg or CONFIGS[1]
+    cfg = cfg or TINY
     rng = np.random.default_rng(cfg.seed)
     lens = list(cfg.extra["lens"])
     nb = cfg.extra["num_blocks"]
@@ -139,8 +139,8 @@ def tiny_inputs(cfg: Config = None):
 
 
 def llama8b_structure(cfg: Config = None, batch=None):
-    """Config 2: lengths, pool size (1.2x need) and dealt random tables."""
-    cfg = cfg or CONFIGS[2]
+    """Llama-3-8B single layer: lengths, pool size (1.2x need) and dealt random tables."""
+    cfg = cfg or LLAMA8B_1LAYER
     rng = np.random.default_rng(cfg.seed)
     b = cfg.batch if batch is None else batch
     lens = rng.integers(cfg.extra["len_lo"], cfg.extra["len_hi"] + 1, size=b).astype(np.int64)
@@ -153,10 +153,10 @@ def llama8b_structure(cfg: Config = None, batch=None):
 
 
 def llama70b_structure(cfg: Config = None, block_tokens: int = BLOCK):
-    """Config 3: all lengths 8192; one shuffled table shared by all layers.
+    """Llama-3-70B, 80 layers: all lengths 8192; one shuffled table shared by all layers.
     With 32-token blocks the shuffle is over block pairs of 16-token planes
     (2b, 2b+1), the table listing planes."""
-    cfg = cfg or CONFIGS[3]
+    cfg = cfg or LLAMA70B_80LAYER
     rng = np.random.default_rng(cfg.seed)
     nb = cfg.extra["num_blocks"]
     per = cfg.extra["length"] // BLOCK
@@ -169,8 +169,8 @@ def llama70b_structure(cfg: Config = None, block_tokens: int = BLOCK):
 
 
 def ragged_mha_structure(cfg: Config = None, batch=None):
-    """Config 5: lognormal lengths, pool = exact need, permuted tables."""
-    cfg = cfg or CONFIGS[5]
+    """Ragged MHA: lognormal lengths, pool = exact need, permuted tables."""
+    cfg = cfg or RAGGED_MHA
     rng = np.random.default_rng(cfg.seed)
     b = cfg.batch if batch is None else batch
     raw = np.exp(rng.normal(np.log(cfg.extra["median"]), cfg.extra["sigma"], size=b))
@@ -183,7 +183,7 @@ def ragged_mha_structure(cfg: Config = None, batch=None):
 
 
 def inject_structure(cfg: Config = None, n_chunks=None, batch=None):
-    """Config 4: chunk store index, per-request composition and run list.
+    """Top-8 injection: chunk store index, per-request composition and run list.
 
     Store entries: chunk c (64..256 tokens), then a 32-token instruction
     prefix and a 15-token separator.  Each request lays out the prefix at
@@ -192,7 +192,7 @@ def inject_structure(cfg: Config = None, n_chunks=None, batch=None):
     chunk.  Runs are (seq, n, dst_pos, src_token); the whole list is
     shuffled.
     """
-    cfg = cfg or CONFIGS[4]
+    cfg = cfg or INJECT_TOP8
     e = cfg.extra
     rng = np.random.default_rng(cfg.seed)
     nc = e["n_chunks"] if n_chunks is None else n_chunks
@@ -233,7 +233,7 @@ def window_structure(cfg: Config = None):
     """Sliding-window decode: every sequence at the same position, its table
     holding only the blocks of the last ``window`` positions (the rest -1, as
     a window trim leaves them); block ids shuffled."""
-    cfg = cfg or EXTRA["mistral-window"]
+    cfg = cfg or MISTRAL_WINDOW
     rng = np.random.default_rng(cfg.seed)
     n, w = cfg.extra["length"], cfg.extra["window"]
     per = blocks_for(n)
