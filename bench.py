@@ -124,6 +124,15 @@ def decode_bytes(lens, n_kv_heads, head_dim, n_q_heads, elem, kv_elem=None):
     return kv + q + out + tables
 
 
+def append_bytes(n_seqs, n_kv_heads, head_dim, elem, kv_elem=None):
+    """Algorithmic bytes of one single-token append (one layer): the new K
+    and V rows read and stored, the cos/sin row of each position, the
+    position and the table entry of each sequence."""
+    kv_elem = elem if kv_elem is None else kv_elem
+    rows = n_seqs * n_kv_heads * head_dim
+    return rows * 2 * (elem + kv_elem) + n_seqs * head_dim * 4 + n_seqs * 8
+
+
 def bw_probe(n_bytes=8 << 30, reps=5):
     import torch
     import paged_kv_cache_inject_amd as pkv
@@ -159,10 +168,10 @@ def decode_workload(name):
     raise ValueError(name)
 
 
-def run_decode(steps, warmup, workload="70b", launch_steps=None):
+def run_decode(steps, warmup, workload="70b", launch_steps=None, two_calls=True):
     import torch
     import paged_kv_cache_inject_amd as pkv
-    from workloads.configs import host_normal
+    from workloads.configs import host_normal, device_normal
     cfg, st = decode_workload(workload)
     lens = st["lens"]
     launch_steps = steps if launch_steps is None else launch_steps
@@ -189,15 +198,38 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None):
     n_items = pkv.pkv_decode_plan_items(plan)
     part_tokens = pkv.pkv_decode_plan_part_tokens(plan)
     waves = pkv.pkv_decode_plan_waves(plan)
+    # The step's own token: its K and V (per layer, unrotated) are appended
+    # at position len - 1 with RoPE before the layer's decode reads the
+    # cache, so the query attends to itself.  Every step rewrites that slot,
+    # which keeps the context at the workload's length from step to step.
+    first = torch.from_numpy((np.asarray(lens) - 1).astype(np.int32)).cuda()
+    new_dt = "bf16" if fp8 else cfg.dtype
+    n_new = cfg.batch * cfg.n_kv_heads * cfg.head_dim
+    k_new = [device_normal(n_new, new_dt, cfg.seed * 7919 + 2 * layer)
+             for layer in range(cfg.n_layers)]
+    v_new = [device_normal(n_new, new_dt, cfg.seed * 7919 + 2 * layer + 1)
+             for layer in range(cfg.n_layers)]
+    max_pos = int(np.max(lens))
+    cos_h, sin_h = pkv.pkv_rope_table(cfg.head_dim, cfg.rope_base, max_pos)
+    dcos, dsin = torch.from_numpy(cos_h).cuda(), torch.from_numpy(sin_h).cuda()
 
     def step(events=None):
         pkv.pkv_decode_plan_upload(plan, ws)
         for layer in range(cfg.n_layers):
             if events is not None:
                 events[layer][0].record()
-            pkv.pkv_decode_attention(plan, pool, layer, q, tables, out, lse, ws)
+            pkv.pkv_append_decode_attention(plan, pool, layer, q, tables, k_new[layer],
+                                            v_new[layer], "pairs", dcos, dsin, max_pos, out, lse,
+                                            ws, q_dtype=new_dt)
             if events is not None:
                 events[layer][1].record()
+
+    def step_two_calls():
+        pkv.pkv_decode_plan_upload(plan, ws)
+        for layer in range(cfg.n_layers):
+            pkv.pkv_append_kv(pool, layer, tables, first, 1, k_new[layer], v_new[layer], "pairs",
+                              dcos, dsin, max_pos)
+            pkv.pkv_decode_attention(plan, pool, layer, q, tables, out, lse, ws)
 
     log("decode: %d warmup steps" % warmup)
     for _ in range(warmup):
@@ -215,6 +247,18 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total_ms = t_s.elapsed_time(t_e)
+    # The same step as two launches per layer (pkv_append_kv, then
+    # pkv_decode_attention), for comparison.
+    two_calls_ms = None
+    if two_calls:
+        u_s, u_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        step_two_calls()
+        u_s.record()
+        for _ in range(steps):
+            step_two_calls()
+        u_e.record()
+        torch.cuda.synchronize()
+        two_calls_ms = u_s.elapsed_time(u_e) / steps
     # Instrumented pass: the same number of steps again, with a HIP event
     # pair around every launch on the stream the kernels run on, for the
     # per-launch kernel duration (the markers themselves add a few us per
@@ -231,12 +275,17 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None):
                  for l in range(cfg.n_layers)]
     # attended tokens: the last `window` positions under a sliding window
     attended = np.minimum(lens, window) if window > 0 else lens
-    per_launch = decode_bytes(attended, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads, 2,
+    per_decode = decode_bytes(attended, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads, 2,
                               kv_elem=1 if fp8 else 2)
+    per_append = append_bytes(cfg.batch, cfg.n_kv_heads, cfg.head_dim, 2,
+                              kv_elem=1 if fp8 else 2)
+    per_launch = per_decode + per_append
     ms_step = total_ms / steps
     res = dict(ms_per_step=ms_step, wall_ms_per_step=wall * 1e3 / steps,
                instrumented_ms_per_step=i_s.elapsed_time(i_e) / max(1, launch_steps),
-               bytes_per_step=per_launch * cfg.n_layers, bytes_per_launch=per_launch,
+               bytes_per_step=per_launch * cfg.n_layers,
+               bytes_per_launch=per_launch, append_bytes_per_launch=per_append,
+               two_calls_ms_per_step=two_calls_ms,
                launch_ms_avg=float(np.mean(launch_ms)), launch_ms_p50=float(np.median(launch_ms)),
                launch_ms_p10=float(np.percentile(launch_ms, 10)),
                launch_ms_p90=float(np.percentile(launch_ms, 90)),
@@ -267,10 +316,12 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None):
         res["cold_ms_per_step"] = float(np.median(cold))
         res["cold_gbps"] = res["bytes_per_step"] / (res["cold_ms_per_step"] * 1e-3) / 1e9
         log("decode: cold caches %.4f ms/step, %.1f GB/s" % (res["cold_ms_per_step"], res["cold_gbps"]))
-    log("decode: %.3f ms/step, %.1f GB/s; per launch %.1f us -> %.1f GB/s"
-        % (ms_step, res["value"], res["launch_ms_avg"] * 1e3, res["launch_gbps"]))
+    log("decode: %.3f ms/step, %.1f GB/s; per launch %.1f us -> %.1f GB/s; as two calls "
+        "per layer %s ms/step" % (ms_step, res["value"], res["launch_ms_avg"] * 1e3,
+                                  res["launch_gbps"],
+                                  "-" if two_calls_ms is None else "%.3f" % two_calls_ms))
     pkv.pkv_decode_plan_destroy(plan)
-    del buf, ws, q, tables, out, lse
+    del buf, ws, q, tables, out, lse, k_new, v_new, first, dcos, dsin
     torch.cuda.empty_cache()
     return res, st
 
@@ -490,6 +541,10 @@ def cpu_baseline(budget_s=12.0):
                        "query heads each; float64 numpy, one thread, %.1f s" % (seqs_done, dt))
 
 
+def _r4(x):
+    return None if x is None else round(x, 4)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -509,6 +564,8 @@ def main():
     ap.add_argument("--host-store-only", action="store_true",
                     help="time only the pinned-host-store inject (no JSON line)")
     ap.add_argument("--cow-reps", type=int, default=10)
+    ap.add_argument("--no-two-calls", action="store_true",
+                    help="skip the comparison timing of the step as two launches per layer")
     ap.add_argument("--decode-workload", default="70b",
                     choices=["70b", "8b", "ragged", "70b-fp8", "mistral-window", "70b-block32"],
                     help="decode workload timed (the reported line uses 70b)")
@@ -531,13 +588,14 @@ def main():
         return
     probe = bw_probe()
     log("bw probe: %.1f GB/s" % probe)
-    dec, _ = run_decode(args.steps, args.warmup, args.decode_workload)
+    two = not args.no_two_calls
+    dec, _ = run_decode(args.steps, args.warmup, args.decode_workload, two_calls=two)
     fp8 = None
     if not args.no_fp8 and args.decode_workload == "70b":
-        fp8, _ = run_decode(args.steps, args.warmup, "70b-fp8")
+        fp8, _ = run_decode(args.steps, args.warmup, "70b-fp8", two_calls=two)
     win = None
     if not args.no_window and args.decode_workload == "70b":
-        win, _ = run_decode(args.steps, args.warmup, "mistral-window")
+        win, _ = run_decode(args.steps, args.warmup, "mistral-window", two_calls=two)
     inj = None if args.no_inject else run_inject(args.inject_reps)
     cow = None if args.no_cow else run_cow(args.cow_reps)
     inj_host = None if args.no_host_store else run_inject_host(max(2, args.inject_reps // 3))
@@ -559,22 +617,27 @@ def main():
         "config": {"workload": dec["workload"], "batch": dec["batch"], "context": dec["context"],
                    "layers": dec["layers"], "part_tokens": dec["part_tokens"],
                    "work_items": dec["n_items"], "waves_per_workgroup": dec["waves"],
-                   "pool_layout": POOL_LAYOUT},
+                   "pool_layout": POOL_LAYOUT,
+                   "step": "per layer: pkv_append_decode_attention (the step's token "
+                           "appended at position len-1 with RoPE, then attention over len "
+                           "tokens, one launch)"},
         "roofline": {"bound": "hbm", "achieved": round(dec["launch_gbps"], 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(dec["launch_gbps"] / PEAK_HBM_GBPS, 4),
                      "traffic": recorded_traffic(),
-                     "kernel": "decode_mfma_kernel (pkv_decode_attention, one layer)",
+                     "kernel": "decode_mfma_kernel (pkv_append_decode_attention, one layer)",
                      "bytes_per_launch": dec["bytes_per_launch"],
                      "launch_us_avg": round(dec["launch_ms_avg"] * 1e3, 2),
                      "launch_us_p10_p50_p90": [round(dec["launch_ms_p10"] * 1e3, 2),
                                                round(dec["launch_ms_p50"] * 1e3, 2),
                                                round(dec["launch_ms_p90"] * 1e3, 2)],
                      "frac_of_bw_probe": round(dec["launch_gbps"] / probe, 4),
+                     "append_bytes_per_launch": dec["append_bytes_per_launch"],
                      "launch_timing": "HIP events around each of %d launches in an instrumented "
                                       "pass of %d steps after the timed steps (%.3f ms/step)"
                                       % (dec["launches_timed"], dec["launches_timed"] // dec["layers"],
                                          dec["instrumented_ms_per_step"])},
+        "two_calls_ms_per_step": _r4(dec["two_calls_ms_per_step"]),
         "bw_probe_gbps": round(probe, 1),
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", "?"),
                    "compute_units": props.multi_processor_count},
@@ -588,6 +651,7 @@ def main():
             "ms_per_step": round(fp8["ms_per_step"], 4), "gbps": round(fp8["value"], 1),
             "pct_of_peak": round(100 * fp8["value"] / PEAK_HBM_GBPS, 2),
             "launch_us_avg": round(fp8["launch_ms_avg"] * 1e3, 2),
+            "two_calls_ms_per_step": _r4(fp8["two_calls_ms_per_step"]),
             "step_speedup_vs_bf16": round(dec["ms_per_step"] / fp8["ms_per_step"], 3)}
     if win is not None:
         line["decode_window"] = {
@@ -595,6 +659,7 @@ def main():
             "gbps": round(win["value"], 1), "pct_of_peak": round(100 * win["value"] / PEAK_HBM_GBPS, 2),
             "launch_us_avg": round(win["launch_ms_avg"] * 1e3, 2),
             "launch_gbps": round(win["launch_gbps"], 1), "layers": win["layers"],
+            "two_calls_ms_per_step": _r4(win["two_calls_ms_per_step"]),
             "bytes_per_launch": win["bytes_per_launch"]}
     if inj is not None:
         line["inject"] = {"tokens_per_s": round(inj["tokens_per_s"], 1), "unit": "tokens/s",

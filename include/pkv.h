@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 6
+#define PKV_ABI_VERSION 7
 /* Tokens per physical block ([InferScale] §2; [KV essay] "Paged attention"). */
 #define PKV_BLOCK_TOKENS 16
 
@@ -432,6 +432,37 @@ pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int3
                                 const int32_t* d_tables,
                                 int32_t table_stride, float* d_out, float* d_lse, void* d_ws,
                                 size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * One decode step's append and attention in one launch ([KV essay] "The
+ * fix": each generated token's K/V entry is appended and the step attends
+ * over the cache including it; [InferScale] §2: the key is stored rotated at
+ * its own position).  Equal, byte for byte in the pool and in d_out/d_lse, to
+ *   pkv_append_kv(pool, layer, d_tables, table_stride, first_pos = lens - 1,
+ *                 n_seqs, 1, d_k_new, d_v_new, q_dtype, rope_mode, d_cos,
+ *                 d_sin, max_pos)
+ * followed by pkv_decode_attention with the same plan: every sequence b of
+ * the plan with lens[b] >= 1 gets its newest token, at position lens[b] - 1,
+ * written (K rotated by R_p, V as given) and attended to.  Sequences of
+ * length 0 get no write.
+ * k_new, v_new: device [n_seqs][n_kv_heads][head_dim] in q_dtype, 16-byte
+ * aligned, unrotated.  The slot of position lens[b] - 1 must be reserved
+ * (pkv_extend); a block id out of range in its table entry skips the write,
+ * as pkv_append_kv does.  The block holding that slot may be written back
+ * whole (its other slots with the bytes they held), so, as for any write, it must
+ * belong to this sequence alone: pkv_extend copies a shared block first.
+ * Errors, all before anything is enqueued: those of
+ * pkv_decode_attention; PKV_E_INVALID for null or misaligned k_new/v_new or
+ * bad rotary arguments; PKV_E_RANGE when a newest position has no rotary row
+ * (>= max_pos, rope_mode other than PKV_ROPE_NONE).
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_append_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int32_t layer,
+                                       const void* d_q, int32_t q_dtype, float scale,
+                                       const int32_t* d_tables, int32_t table_stride,
+                                       const void* d_k_new, const void* d_v_new,
+                                       int32_t rope_mode, const float* d_cos,
+                                       const float* d_sin, int32_t max_pos, float* d_out,
+                                       float* d_lse, void* d_ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Measurement helper: a streaming 16-byte-per-lane read of n_bytes (a

@@ -115,6 +115,9 @@ SIGNATURES = {
     "pkv_decode_plan_upload": (_I32, [_P, _P, _SZ, _P]),
     "pkv_decode_attention": (_I32, [_P, ctypes.POINTER(pkv_pool), _I32, _P, _I32,
                                     ctypes.c_float, _P, _I32, _P, _P, _P, _SZ, _P]),
+    "pkv_append_decode_attention": (_I32, [_P, ctypes.POINTER(pkv_pool), _I32, _P, _I32,
+                                           ctypes.c_float, _P, _I32, _P, _P, _I32, _P, _P, _I32,
+                                           _P, _P, _P, _SZ, _P]),
     "pkv_bw_probe": (_I32, [_P, _SZ, _P, _P]),
 }
 
@@ -446,6 +449,19 @@ def pkv_decode_attention(plan, pool: pkv_pool, layer, q, tables, out, lse, works
                                                _ptr(out), _ptr(lse), _ptr(workspace),
                                                workspace.numel() * workspace.element_size(),
                                                _stream(stream)))
+
+
+def pkv_append_decode_attention(plan, pool: pkv_pool, layer, q, tables, k_new, v_new, rope_mode,
+                                cos, sin, max_pos, out, lse, workspace, scale=0.0, stream=None,
+                                q_dtype=None):
+    """k_new, v_new: [n_seqs][n_kv_heads][head_dim] in q's format (q_dtype
+    defaults to the torch dtype of q)."""
+    qd = DTYPE_CODES[q_dtype] if isinstance(q_dtype, str) else _dtype_of(q, pool.dtype)
+    _check(load_library().pkv_append_decode_attention(
+        plan, ctypes.byref(pool), layer, _ptr(q), qd, float(scale), _ptr(tables), tables.shape[1],
+        _ptr(k_new), _ptr(v_new), ROPE_CODES.get(rope_mode, rope_mode), _ptr(cos), _ptr(sin),
+        max_pos, _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def pkv_bw_probe(src, sink, stream=None):

@@ -1015,13 +1015,14 @@ pkv_status pkv_decode_plan_create(const int64_t* lens, int32_t n_seqs, int32_t n
     if (n_items <= 1) {
       // whole range in one item (an empty one included): final output
       plan->items.push_back(
-          DecodeItem{b, int32_t(start), int32_t(lens[b] - start), -1, int32_t(lo)});
+          DecodeItem{b, int32_t(start), int32_t(lens[b] - start), -1, int32_t(lo), 1});
     } else {
       plan->merges.push_back(MergeSeq{b, slots, int32_t(n_items), 0});
       for (int64_t i = 0; i < n_items; ++i) {
         const int64_t t0 = start + i * part;
         const int64_t n = std::min<int64_t>(part, lens[b] - t0);
-        plan->items.push_back(DecodeItem{b, int32_t(t0), int32_t(n), slots++, int32_t(lo)});
+        plan->items.push_back(DecodeItem{b, int32_t(t0), int32_t(n), slots++, int32_t(lo),
+                                         int32_t(i == n_items - 1)});
       }
     }
   }
@@ -1079,10 +1080,24 @@ pkv_status pkv_decode_plan_upload(pkv_plan* plan, void* d_ws, size_t ws_bytes, v
   return ok();
 }
 
-pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int32_t layer,
-                                const void* d_q, int32_t q_dtype, float scale,
-                                const int32_t* d_tables, int32_t table_stride, float* d_out,
-                                float* d_lse, void* d_ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Fused append of each sequence's newest token (null new_k: none).
+struct NewToken {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  int32_t rope_mode = PKV_ROPE_NONE;
+  const float* cos = nullptr;
+  const float* sin = nullptr;
+  int32_t max_pos = 0;
+};
+
+pkv_status decode_common(const pkv_plan* plan, const pkv_pool* pool, int32_t layer,
+                         const void* d_q, int32_t q_dtype, float scale, const int32_t* d_tables,
+                         int32_t table_stride, const NewToken& nt, float* d_out, float* d_lse,
+                         void* d_ws, size_t ws_bytes, void* stream) {
   if (!plan) return fail(PKV_E_INVALID, "null plan");
   if (pkv_status st = check_pool(pool)) return st;
   if (pkv_status st = check_input_dtype(pool, q_dtype, "q")) return st;
@@ -1091,6 +1106,17 @@ pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int3
     return fail(PKV_E_INVALID, "plan and pool disagree on KV heads or head_dim");
   if (pool->dtype == PKV_FP8E4M3 && plan->n_q_heads / plan->n_kv_heads > 16)
     return fail(PKV_E_UNSUPPORTED, "FP8E4M3 decode supports up to 16 query heads per KV head");
+  if (nt.k) {
+    if (pkv_status st = check_rope(nt.rope_mode, nt.cos, nt.sin, nt.max_pos)) return st;
+    if (!nt.v) return fail(PKV_E_INVALID, "null v_new");
+    if ((reinterpret_cast<uintptr_t>(nt.k) | reinterpret_cast<uintptr_t>(nt.v)) & 15)
+      return fail(PKV_E_INVALID, "k_new / v_new must be 16-byte aligned");
+    if (nt.rope_mode != PKV_ROPE_NONE)
+      for (const DecodeItem& it : plan->items)
+        if (it.last && it.n_tokens > 0 && int64_t(it.t_begin) + it.n_tokens > nt.max_pos)
+          return fail(PKV_E_RANGE, "position %lld of sequence %d has no rotary row (max_pos %d)",
+                      (long long)(int64_t(it.t_begin) + it.n_tokens - 1), it.seq, nt.max_pos);
+  }
   if (plan->n_seqs == 0) return ok();
   if (!d_q || !d_out || !d_tables) return fail(PKV_E_INVALID, "null device argument");
   if (reinterpret_cast<uintptr_t>(d_q) & 15) return fail(PKV_E_INVALID, "q must be 16-byte aligned");
@@ -1109,7 +1135,7 @@ pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int3
     return fail(PKV_E_UNSUPPORTED, "%zu work items x %d KV heads exceed one launch",
                 plan->items.size(), pool->n_kv_heads);
   char* ws = static_cast<char*>(d_ws);
-  pkv::DecodeArgs a;
+  pkv::DecodeArgs a{};
   a.q = d_q;
   a.q_dtype = q_dtype;
   a.n_q_heads = plan->n_q_heads;
@@ -1125,11 +1151,48 @@ pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int3
   a.part_ml = reinterpret_cast<float*>(ws + plan->off_part_ml);
   a.out = d_out;
   a.lse = d_lse;
+  a.new_k = nt.k;
+  a.new_v = nt.v;
+  a.rope_mode = nt.rope_mode;
+  a.cos_t = nt.cos;
+  a.sin_t = nt.sin;
+  a.max_pos = nt.max_pos;
   int variant = 0;
   if (const char* env = std::getenv("PKV_DECODE_KERNEL")) variant = std::atoi(env);
   hipError_t e = pkv::launch_decode(*pool, layer, a, variant, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int32_t layer,
+                                const void* d_q, int32_t q_dtype, float scale,
+                                const int32_t* d_tables, int32_t table_stride, float* d_out,
+                                float* d_lse, void* d_ws, size_t ws_bytes, void* stream) {
+  return decode_common(plan, pool, layer, d_q, q_dtype, scale, d_tables, table_stride,
+                       NewToken{}, d_out, d_lse, d_ws, ws_bytes, stream);
+}
+
+pkv_status pkv_append_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int32_t layer,
+                                       const void* d_q, int32_t q_dtype, float scale,
+                                       const int32_t* d_tables, int32_t table_stride,
+                                       const void* d_k_new, const void* d_v_new,
+                                       int32_t rope_mode, const float* d_cos,
+                                       const float* d_sin, int32_t max_pos, float* d_out,
+                                       float* d_lse, void* d_ws, size_t ws_bytes, void* stream) {
+  if (!d_k_new || !d_v_new) return fail(PKV_E_INVALID, "null k_new or v_new");
+  NewToken nt;
+  nt.k = d_k_new;
+  nt.v = d_v_new;
+  nt.rope_mode = rope_mode;
+  nt.cos = d_cos;
+  nt.sin = d_sin;
+  nt.max_pos = max_pos;
+  return decode_common(plan, pool, layer, d_q, q_dtype, scale, d_tables, table_stride, nt, d_out,
+                       d_lse, d_ws, ws_bytes, stream);
 }
 
 pkv_status pkv_bw_probe(const void* d_src, size_t n_bytes, void* d_sink, void* stream) {

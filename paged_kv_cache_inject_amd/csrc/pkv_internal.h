@@ -31,6 +31,7 @@ struct DecodeItem {
   int32_t n_tokens;  // positions t_begin .. t_begin + n_tokens - 1
   int32_t slot;      // partial-result slot, or -1 for a final result
   int32_t lo;        // first position attended (a sliding window's start)
+  int32_t last;      // 1 if the range ends at the sequence's last position
 };
 
 // Merge work: sequence seq owns partial slots [first, first + count).
@@ -68,6 +69,15 @@ struct DecodeArgs {
   float* part_ml;  // [n_slots][n_q_heads][2]
   float* out;
   float* lse;      // may be null
+  // Fused append of each sequence's newest token (position len - 1) before
+  // it is attended: rows [n_seqs][n_kv_heads][head_dim] in the query's
+  // format, unrotated; null when no token is appended.
+  const void* new_k;
+  const void* new_v;
+  int rope_mode;
+  const float* cos_t;
+  const float* sin_t;
+  int max_pos;
 };
 
 // kernel_variant: 0 = automatic, 1 = force the generic VALU kernel.

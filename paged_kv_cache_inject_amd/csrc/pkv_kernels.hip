@@ -141,6 +141,9 @@ __device__ inline void st8_stream(void* p, uint2 v) {
   const u32x2_t w = {v.x, v.y};
   __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
 }
+__device__ inline void st4_stream(void* p, uint32_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
 __device__ inline uint32_t ld4_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
 }
@@ -457,13 +460,52 @@ struct AppendParams {
   int max_pos;
 };
 
+// One token's K row of one head: rotate source chunk pair (c0, c0 + CS/2) at
+// the position whose rotary rows are cr/sr (mode PAIRS, HALVES or NONE) and
+// store both chunks at slot `tin` of the K plane (chunk-major: [chunk][slot]).
 template <int SDT, int PDT, int D>
-__global__ __launch_bounds__(256) void append_kv_kernel(AppendParams p) {
-  typedef typename Fmt<SDT>::T TS;
-  typedef typename Fmt<PDT>::T TP;
+__device__ inline void put_k_pair(const char* kin, char* kplane, int tin, int c0, int mode,
+                                  const float* cr, const float* sr, float ksc) {
   constexpr int ES = Fmt<SDT>::kBytes, EP = Fmt<PDT>::kBytes;
   constexpr int XS = 16 / ES, XP = 16 / EP;
   constexpr int CS = D / XS;
+  const int j0 = c0 * XS, j1 = (c0 + CS / 2) * XS;
+  float kl[XS], kh[XS];
+  unpack16<SDT>(ld16(kin + j0 * ES), kl);
+  unpack16<SDT>(ld16(kin + j1 * ES), kh);
+  if (mode == PKV_ROPE_PAIRS) {
+    rot_pairs_f<XS>(kl, j0, cr, sr);
+    rot_pairs_f<XS>(kh, j1, cr, sr);
+  } else if (mode == PKV_ROPE_HALVES) {
+    rot_halves_f<XS>(kl, kh, j0, cr, sr);
+  }
+  Packed<PDT, XS> pk;
+  pk.set(kl, ksc);
+  store_packed(kplane + (((j0 / XP) * kBlock + tin) * XP + j0 % XP) * EP, pk);
+  pk.set(kh, ksc);
+  store_packed(kplane + (((j1 / XP) * kBlock + tin) * XP + j1 % XP) * EP, pk);
+}
+
+// One token's V element j of one head, stored at slot `tin` of the V plane
+// (dimension-major: [dim][slot]); a quantised pool stores e4m3(v / vsc).
+template <int SDT, int PDT>
+__device__ inline void put_v_elem(const char* vin, char* vplane, int tin, int j, float vsc) {
+  typedef typename Fmt<SDT>::T TS;
+  typedef typename Fmt<PDT>::T TP;
+  const TS v = reinterpret_cast<const TS*>(vin)[j];
+  TP out;
+  if constexpr (SDT == PDT) {
+    out = v;
+  } else {
+    out = Fmt<PDT>::from_f32(Fmt<SDT>::to_f32(v) / vsc);
+  }
+  reinterpret_cast<TP*>(vplane)[j * kBlock + tin] = out;
+}
+
+template <int SDT, int PDT, int D>
+__global__ __launch_bounds__(256) void append_kv_kernel(AppendParams p) {
+  constexpr int ES = Fmt<SDT>::kBytes;
+  constexpr int CS = D / (16 / ES);
   const int b = blockIdx.x / p.n_new;
   const int t = blockIdx.x - b * p.n_new;
   const int pos = p.first_pos[b] + t;
@@ -484,35 +526,15 @@ __global__ __launch_bounds__(256) void append_kv_kernel(AppendParams p) {
   for (int w = threadIdx.x; w < p.n_kv_heads * (CS / 2); w += blockDim.x) {
     const int h = w / (CS / 2);
     const int c0 = w - h * (CS / 2);
-    const int j0 = c0 * XS, j1 = (c0 + CS / 2) * XS;
-    float kl[XS], kh[XS];
-    unpack16<SDT>(ld16(kin + int64_t(h) * D * ES + j0 * ES), kl);
-    unpack16<SDT>(ld16(kin + int64_t(h) * D * ES + j1 * ES), kh);
-    if (p.rope_mode == PKV_ROPE_PAIRS) {
-      rot_pairs_f<XS>(kl, j0, cr, sr);
-      rot_pairs_f<XS>(kh, j1, cr, sr);
-    } else if (p.rope_mode == PKV_ROPE_HALVES) {
-      rot_halves_f<XS>(kl, kh, j0, cr, sr);
-    }
     const float ksc = PDT == PKV_FP8E4M3 ? p.k_scale[p.layer * p.n_kv_heads + h] : 1.f;
-    char* kplane = kplane0 + int64_t(h) * p.p_head;
-    Packed<PDT, XS> pk;
-    pk.set(kl, ksc);
-    store_packed(kplane + (((j0 / XP) * kBlock + tin) * XP + j0 % XP) * EP, pk);
-    pk.set(kh, ksc);
-    store_packed(kplane + (((j1 / XP) * kBlock + tin) * XP + j1 % XP) * EP, pk);
+    put_k_pair<SDT, PDT, D>(kin + int64_t(h) * D * ES, kplane0 + int64_t(h) * p.p_head, tin, c0,
+                            p.rope_mode, cr, sr, ksc);
   }
   for (int w = threadIdx.x; w < p.n_kv_heads * D; w += blockDim.x) {
     const int h = w / D;
     const int j = w - h * D;
-    const TS v = reinterpret_cast<const TS*>(vin + int64_t(h) * D * ES)[j];
-    TP out;
-    if constexpr (SDT == PDT) {
-      out = v;
-    } else {
-      out = Fmt<PDT>::from_f32(Fmt<SDT>::to_f32(v) / p.v_scale[p.layer * p.n_kv_heads + h]);
-    }
-    reinterpret_cast<TP*>(vplane0 + int64_t(h) * p.p_head)[j * kBlock + tin] = out;
+    const float vsc = PDT == PKV_FP8E4M3 ? p.v_scale[p.layer * p.n_kv_heads + h] : 1.f;
+    put_v_elem<SDT, PDT>(vin + int64_t(h) * D * ES, vplane0 + int64_t(h) * p.p_head, tin, j, vsc);
   }
 }
 
@@ -540,6 +562,14 @@ struct DecodeParams {
   float* lse;
   const float* k_scale;              // this layer's [heads] scales, quantised pools only
   const float* v_scale;
+  // Fused append (new_k null: none): rows [seq][n_kv_heads][D] in the
+  // query's format; each sequence's token goes to position len - 1.
+  const char* new_k;
+  const char* new_v;
+  int rope_mode;
+  const float* cos_t;
+  const float* sin_t;
+  int max_pos;
 };
 
 // Launch order of the decode kernels: workgroups walk the (longest-first)
@@ -554,6 +584,121 @@ __device__ inline void decode_work(const DecodeParams& p, int x, int& item, int&
   head = r / cc;
   item = c0 + r % cc;
 }
+
+// Fused append of an item's newest token (the item ends at its sequence's
+// last position, pos = t_begin + n_tokens - 1) for KV head g: where its K
+// and V rows go and what they are made from.  ok is false (no write) when
+// the slot's block id is out of range or the position has no rotary row,
+// as in the append kernel.
+// A rotary pairing as a type, to instantiate code per pairing.
+template <int M>
+struct RopeTag {
+  static constexpr int value = M;
+};
+
+struct NewSlot {
+  char* k;          // K head plane of the slot's block
+  char* v;          // V head plane
+  const char* kin;  // source rows, unrotated
+  const char* vin;
+  const float* cr;  // rotary rows of the position
+  const float* sr;
+  float ksc, vsc;   // quantised pools: this head's scales
+  int tin;          // slot within the block
+  bool ok;
+};
+
+template <int SDT, int PDT, int D>
+__device__ inline NewSlot new_slot(const DecodeParams& p, const DecodeItem& it, int g) {
+  NewSlot ns;
+  const int pos = it.t_begin + it.n_tokens - 1;
+  ns.tin = pos % kBlock;
+  const int64_t row = (int64_t(it.seq) * p.n_kv_heads + g) * D * Fmt<SDT>::kBytes;
+  ns.kin = p.new_k + row;
+  ns.vin = p.new_v + row;
+  // (the host has checked that the position has a rotary row; the clamp
+  // only keeps the address in range)
+  const int rpos = min(pos, max(p.max_pos - 1, 0));
+  ns.cr = p.cos_t + size_t(rpos) * (D / 2);
+  ns.sr = p.sin_t + size_t(rpos) * (D / 2);
+  ns.ksc = PDT == PKV_FP8E4M3 ? p.k_scale[g] : 1.f;
+  ns.vsc = PDT == PKV_FP8E4M3 ? p.v_scale[g] : 1.f;
+  ns.ok = p.rope_mode == PKV_ROPE_NONE || pos < p.max_pos;
+  ns.k = ns.v = nullptr;
+  return ns;
+}
+
+// The slot's K and V head planes once its block id is known; ok drops when
+// the id is out of range.
+__device__ inline void set_slot_planes(NewSlot& ns, const DecodeParams& p, int blk, int g) {
+  ns.ok = ns.ok && blk >= 0 && blk < p.num_blocks;
+  const int b = ns.ok ? blk : 0;
+  ns.k = const_cast<char*>(p.pool_k) + int64_t(b) * p.p_block + int64_t(g) * p.p_head;
+  ns.v = const_cast<char*>(p.pool_v) + int64_t(b) * p.p_block + int64_t(g) * p.p_head;
+}
+
+// Pool chunk c (dims c*XP .. c*XP + XP - 1) of the new token's K row: the
+// source dims rotated as put_k_pair rotates them (the halves pairing reads
+// the partner dims D/2 away as well), stored at the token's slot.  load()
+// reads everything the chunk needs and store() computes and writes it, so
+// that a caller can issue all its loads before its first store.  The decode
+// kernels call them from the lane that later loads this chunk, so the lane's
+// own program order makes that load see the store.
+template <int SDT, int PDT, int D, int MODE>
+struct KChunkPut {
+  static constexpr int ES = Fmt<SDT>::kBytes;
+  static constexpr int XS = 16 / ES, XP = 16 / Fmt<PDT>::kBytes;
+  static constexpr int NS = XP / XS;  // 16-byte source pieces per pool chunk (1 or 2)
+  static constexpr int NR = MODE == PKV_ROPE_PAIRS ? XP / 2 : MODE == PKV_ROPE_HALVES ? XP : 0;
+  uint4 x[NS], y[NS];                 // the chunk's source dims and (halves) the partner's
+  float c[NR > 0 ? NR : 1], s[NR > 0 ? NR : 1];  // rotary rows at the chunk's pair indices
+
+  __device__ void load(const NewSlot& ns, int ch) {
+    const int j0 = ch * XP;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) x[i] = ld16(ns.kin + (j0 + i * XS) * ES);
+    if constexpr (MODE == PKV_ROPE_PAIRS) {
+#pragma unroll
+      for (int e = 0; e < NR; ++e) {
+        c[e] = ns.cr[j0 / 2 + e];
+        s[e] = ns.sr[j0 / 2 + e];
+      }
+    } else if constexpr (MODE == PKV_ROPE_HALVES) {
+      const int jp = j0 < D / 2 ? j0 + D / 2 : j0 - D / 2;
+      const int i0 = j0 < D / 2 ? j0 : jp;  // pair index of the chunk's first dim
+#pragma unroll
+      for (int i = 0; i < NS; ++i) y[i] = ld16(ns.kin + (jp + i * XS) * ES);
+#pragma unroll
+      for (int e = 0; e < NR; ++e) {
+        c[e] = ns.cr[i0 + e];
+        s[e] = ns.sr[i0 + e];
+      }
+    }
+  }
+
+  // The chunk's 16 bytes in the pool format.
+  __device__ uint4 pack(const NewSlot& ns, int ch) const {
+    float f[XP];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) unpack16<SDT>(x[i], f + i * XS);
+    if constexpr (MODE == PKV_ROPE_PAIRS) {
+      rot_pairs_f<XP>(f, 0, c, s);
+    } else if constexpr (MODE == PKV_ROPE_HALVES) {
+      float g[XP];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) unpack16<SDT>(y[i], g + i * XS);
+      if (ch * XP < D / 2) rot_halves_f<XP>(f, g, 0, c, s);
+      else rot_halves_f<XP>(g, f, 0, c, s);
+    }
+    Packed<PDT, XP> pk;
+    pk.set(f, ns.ksc);
+    return *reinterpret_cast<const uint4*>(pk.v);
+  }
+
+  __device__ void store(const NewSlot& ns, int ch) const {
+    st16_stream(ns.k + (ch * kBlock + ns.tin) * 16, pack(ns, ch));
+  }
+};
 
 // Stores one head's result: final (single-range sequence) or partial state.
 // m is in the log2-scaled domain; l is the sum of 2^(s - m).
@@ -645,7 +790,11 @@ __device__ inline uint2 e4m3x4_to_f16x4(uint32_t w) {
 // format (equal to KVDT, or BF16/F16 for an fp8 pool whose MFMA operands are
 // float16), head dim D, prefetch depth, waves per workgroup NW.
 template <int KVDT, int QDT, int D, int DEPTH, int NW>
-__global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
+// `tables` is p.tables again as a restrict-qualified argument: the kernel's
+// only stores (the fused append) go to the pool, and with the table known
+// not to alias them its entries keep coming through scalar loads.
+__global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
+                                                              const int32_t* __restrict__ tables) {
   constexpr bool FP8 = KVDT == PKV_FP8E4M3;
   constexpr int OT = FP8 ? PKV_F16 : KVDT;  // MFMA operand format
   constexpr int S = D / 32;   // QK MFMA steps of 32 dims
@@ -694,12 +843,23 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   }
   const float score_mul = p.scale_log2 * kmul;
 
-  const int32_t* tab = p.tables + int64_t(it.seq) * p.table_stride + it.t_begin / kBlock;
+  const int32_t* tab = tables + int64_t(it.seq) * p.table_stride + it.t_begin / kBlock;
   const char* kbase = p.pool_k + int64_t(g) * p.p_head;
   const char* vbase = p.pool_v + int64_t(g) * p.p_head;
   const int nblk = (it.n_tokens + kBlock - 1) / kBlock;
   // This wave takes blocks wave, wave + NW, wave + 2 NW, ...
   const int nj = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;
+  // Fused append: the wave that takes the newest token's block (its j-th,
+  // put_j) makes the token's K chunks and V elements in the pool format
+  // before its loop, each lane those it holds when it loads that block (K
+  // chunks 4s + grp and V dims 16n + row of the slot); when it takes that
+  // block it puts them into its registers in place of the loaded ones and
+  // writes the block's planes back.  Other waves: put_j = -1.
+  int put_j = -1;
+  if (p.new_k != nullptr && it.last && it.n_tokens > 0) {
+    const int lb = (it.n_tokens - 1) / kBlock;
+    if (lb % NW == wave) put_j = lb / NW;
+  }
 
   f32x4_t acc[NT];
 #pragma unroll
@@ -711,8 +871,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
   uint2 vbuf[DEPTH][NT];   // fp8: only .x holds the 4 codes
   bool okbuf[DEPTH];
 
+  int put_blk = -1;  // block id read for the newest token's block
   auto issue = [&](int j, int d) {
     int blk = tab[wave + j * NW];
+    if (j == put_j) put_blk = blk;
     const bool ok = unsigned(blk) < unsigned(p.num_blocks);
     okbuf[d] = ok;
     blk = ok ? blk : 0;
@@ -727,15 +889,105 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
     }
   };
 
+  NewSlot ns{};
+  uint4 knew[SL];     // lanes with row == slot: the token's K chunks 4s + grp
+  uint32_t vnew[NT];  // lanes with grp == slot / 4: its V dims 16n + row (pool bits)
+  // The token's K and V rows in the pool format, made by the whole wave
+  // (lane i < D/2 rotates pair i; lanes take V dims lane, lane + 64) and
+  // read back by the lanes that hold them.
+  typedef typename Fmt<KVDT>::T TP;
+  __shared__ __align__(16) TP new_row[2][D];
+  auto make_new = [&](auto mode_tag) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    typedef typename Fmt<QDT>::T TQ;
+    const TQ* kin = reinterpret_cast<const TQ*>(ns.kin);
+    const TQ* vin = reinterpret_cast<const TQ*>(ns.vin);
+    if (lane < D / 2) {
+      const int i = lane;
+      const int j0 = MODE == PKV_ROPE_HALVES ? i : 2 * i;
+      const int j1 = MODE == PKV_ROPE_HALVES ? i + D / 2 : 2 * i + 1;
+      float x0 = Fmt<QDT>::to_f32(kin[j0]), x1 = Fmt<QDT>::to_f32(kin[j1]);
+      if constexpr (MODE != PKV_ROPE_NONE) {
+        const float c = ns.cr[i], sn = ns.sr[i];
+        const float y0 = x0 * c - x1 * sn;
+        const float y1 = x0 * sn + x1 * c;
+        x0 = y0;
+        x1 = y1;
+      }
+      new_row[0][j0] = Fmt<KVDT>::from_f32(FP8 ? x0 / ns.ksc : x0);
+      new_row[0][j1] = Fmt<KVDT>::from_f32(FP8 ? x1 / ns.ksc : x1);
+    }
+#pragma unroll
+    for (int j = lane; j < D; j += 64) {
+      if constexpr (QDT == KVDT) new_row[1][j] = vin[j];
+      else new_row[1][j] = Fmt<KVDT>::from_f32(Fmt<QDT>::to_f32(vin[j]) / ns.vsc);
+    }
+    // the row is written and read by lanes of this one wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int s = 0; s < SL; ++s)
+      knew[s] = *reinterpret_cast<const uint4*>(&new_row[0][(4 * s + grp) * (16 / sizeof(TP))]);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) vnew[n] = uint32_t(new_row[1][16 * n + row]);
+  };
+
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d)
     if (d < nj) issue(d, d);
+  if (put_j >= 0) {
+    ns = new_slot<QDT, KVDT, D>(p, it, g);
+    if (p.rope_mode == PKV_ROPE_PAIRS) make_new(RopeTag<PKV_ROPE_PAIRS>{});
+    else if (p.rope_mode == PKV_ROPE_HALVES) make_new(RopeTag<PKV_ROPE_HALVES>{});
+    else make_new(RopeTag<PKV_ROPE_NONE>{});
+    if (!ns.ok) put_j = -1;  // no write, and the block is read as stored
+  }
 
   for (int j0 = 0; j0 < nj; j0 += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int j = j0 + d;
       if (j < nj) {
+        if (j == put_j) {
+          // the newest token's slot: the values made above, not the pool's
+          if (row == ns.tin) {
+#pragma unroll
+            for (int s = 0; s < SL; ++s) kbuf[d][s] = knew[s];
+          }
+          if (grp == ns.tin / 4) {
+            const int e = ns.tin & 3;  // token 4 grp + e of the lane's V registers
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+              if constexpr (FP8) {
+                const uint32_t mask = 0xFFu << (8 * e);
+                vbuf[d][n].x = (vbuf[d][n].x & ~mask) | (vnew[n] << (8 * e));
+              } else {
+                const uint32_t mask = 0xFFFFu << (16 * (e & 1));
+                const uint32_t bits = vnew[n] << (16 * (e & 1));
+                uint32_t x = vbuf[d][n].x, y = vbuf[d][n].y;
+                if (e < 2) x = (x & ~mask) | bits;
+                else y = (y & ~mask) | bits;
+                vbuf[d][n] = make_uint2(x, y);
+              }
+            }
+          }
+          // The block's K and V planes go back to the pool whole, with the
+          // token in place: full lines, where the token's own elements would
+          // be partial writes to every line of the V plane.  (The slot's
+          // block id was read when this block was issued.)
+          if (unsigned(put_blk) < unsigned(p.num_blocks)) {
+            char* kp = const_cast<char*>(kbase) + int64_t(put_blk) * p.p_block;
+            char* vp = const_cast<char*>(vbase) + int64_t(put_blk) * p.p_block;
+#pragma unroll
+            for (int s = 0; s < SL; ++s) st16_stream(kp + (64 * s + lane) * 16, kbuf[d][s]);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+              if constexpr (FP8) st4_stream(vp + (16 * n + row) * 16 + grp * 4, vbuf[d][n].x);
+              else st8_stream(vp + (16 * n + row) * 32 + grp * 8, vbuf[d][n]);
+            }
+          }
+        }
         f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
         if constexpr (FP8) {
 #pragma unroll
@@ -885,7 +1137,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p) {
 constexpr int kValuHeads = 4;
 
 template <int DT, int D>
-__global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p,
+                                                         const int32_t* __restrict__ tables) {
   typedef typename Fmt<DT>::T T;
   constexpr int E = Fmt<DT>::kBytes;
   constexpr int X = 16 / E;
@@ -899,10 +1152,32 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   int item_i, g;
   decode_work(p, blockIdx.x, item_i, g);
   const DecodeItem it = p.items[item_i];
-  const int32_t* tab = p.tables + int64_t(it.seq) * p.table_stride + it.t_begin / kBlock;
+  const int32_t* tab = tables + int64_t(it.seq) * p.table_stride + it.t_begin / kBlock;
   const char* kbase = p.pool_k + int64_t(g) * p.p_head;
   const char* vbase = p.pool_v + int64_t(g) * p.p_head;
   const int nblk = (it.n_tokens + kBlock - 1) / kBlock;
+  // Fused append: the newest token is written first, each lane storing the
+  // K chunks (quarter * QC + c of the slot) and V dims (lane + 64k) that it
+  // loads itself below.
+  if (p.new_k != nullptr && it.last && it.n_tokens > 0) {
+    NewSlot ns = new_slot<DT, DT, D>(p, it, g);
+    set_slot_planes(ns, p, tab[(it.n_tokens - 1) / kBlock], g);
+    if (ns.ok) {
+      if (tok == ns.tin) {
+        auto put_k = [&](auto mode_tag) {
+          for (int c = 0; c < QC; ++c) {
+            KChunkPut<DT, DT, D, decltype(mode_tag)::value> kc;
+            kc.load(ns, quarter * QC + c);
+            kc.store(ns, quarter * QC + c);
+          }
+        };
+        if (p.rope_mode == PKV_ROPE_PAIRS) put_k(RopeTag<PKV_ROPE_PAIRS>{});
+        else if (p.rope_mode == PKV_ROPE_HALVES) put_k(RopeTag<PKV_ROPE_HALVES>{});
+        else put_k(RopeTag<PKV_ROPE_NONE>{});
+      }
+      for (int k = 0; k < DL; ++k) put_v_elem<DT, DT>(ns.vin, ns.v, ns.tin, lane + 64 * k, ns.vsc);
+    }
+  }
 
   for (int h0 = 0; h0 < p.group; h0 += kValuHeads) {
     const int nh = min(kValuHeads, p.group - h0);
@@ -1214,6 +1489,12 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
   p.lse = a.lse;
   p.k_scale = pool.k_scale ? pool.k_scale + int64_t(layer) * pool.n_kv_heads : nullptr;
   p.v_scale = pool.v_scale ? pool.v_scale + int64_t(layer) * pool.n_kv_heads : nullptr;
+  p.new_k = static_cast<const char*>(a.new_k);
+  p.new_v = static_cast<const char*>(a.new_v);
+  p.rope_mode = a.rope_mode;
+  p.cos_t = a.cos_t;
+  p.sin_t = a.sin_t;
+  p.max_pos = a.max_pos;
   hipError_t e = hipSuccess;
   if (a.n_items > 0) {
     dim3 grid(unsigned(a.n_items) * unsigned(pool.n_kv_heads));
@@ -1228,7 +1509,9 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
 #define PKV_DEC_MFMA(KV, Q, DD, DEP, W)                                                      \
     if (!launched && mfma && pool.dtype == KV && a.q_dtype == Q && pool.head_dim == DD &&    \
         depth == DEP && nw == W) {                                                           \
-      e = launch(decode_mfma_kernel<KV, Q, DD, DEP, W>, grid, dim3(64 * W), stream, p);      \
+      hipLaunchKernelGGL((decode_mfma_kernel<KV, Q, DD, DEP, W>), grid, dim3(64 * W), 0,       \
+                         stream, p, p.tables);                                               \
+      e = hipGetLastError();                                                                 \
       launched = true;                                                                       \
     }
 #define PKV_DEC_MFMA_W(KV, Q, DD, DEP) \
@@ -1239,7 +1522,8 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
     PKV_DEC_MFMA_W(KV, Q, 128, 1) PKV_DEC_MFMA_W(KV, Q, 128, 2)
 #define PKV_DEC_VALU(DT, DD)                                                                 \
     if (!launched && pool.dtype == DT && pool.head_dim == DD) {                              \
-      e = launch(decode_valu_kernel<DT, DD>, grid, dim3(64), stream, p);                     \
+      hipLaunchKernelGGL((decode_valu_kernel<DT, DD>), grid, dim3(64), 0, stream, p, p.tables); \
+      e = hipGetLastError();                                                                 \
       launched = true;                                                                       \
     }
     PKV_DEC_MFMA_ALL(PKV_BF16, PKV_BF16) PKV_DEC_MFMA_ALL(PKV_F16, PKV_F16)

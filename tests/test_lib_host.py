@@ -309,6 +309,31 @@ def test_decode_plan_splits():
                                        bad.get("d", 64), bad.get("part", 0))
 
 
+def test_append_decode_host_validation_errors():
+    """The one-launch append and decode checks its new-token arguments on
+    the host before any device work (fake device pointers, never read)."""
+    import torch
+    fake = 1 << 20
+    pool = pkv.pkv_pool(1, 8, 2, 64, pkv.PKV_BF16, 0, fake, fake + 4096, 8 * 4096, 4096, 1024)
+    plan = pkv.pkv_decode_plan_create([10, 60], 4, 2, 64, 0)
+    tables = np.zeros((2, 8), dtype=np.int32)
+    ws = torch.empty(pkv.pkv_decode_workspace_bytes(plan), dtype=torch.uint8)
+
+    def call(k_new=fake, v_new=fake, mode="pairs", max_pos=100, q_dtype="bf16"):
+        pkv.pkv_append_decode_attention(plan, pool, 0, fake, tables, k_new, v_new, mode, fake, fake,
+                                        max_pos, fake, fake, ws, stream=0, q_dtype=q_dtype)
+
+    cases = [(dict(k_new=None), "INVALID"), (dict(v_new=None), "INVALID"),
+             (dict(k_new=fake + 2), "INVALID"), (dict(mode=7), "INVALID"),
+             (dict(max_pos=59), "RANGE"), (dict(max_pos=-1), "INVALID"),
+             (dict(q_dtype="f16"), "UNSUPPORTED")]
+    for kw, code in cases:
+        with pytest.raises(pkv.PkvError) as e:
+            call(**kw)
+        assert e.value.code == code, (kw, e.value.code)
+    pkv.pkv_decode_plan_destroy(plan)
+
+
 def test_inject_host_validation_errors():
     """Argument errors are found on the host before any device work (the
     fake device pointers below are never dereferenced)."""
