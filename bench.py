@@ -213,16 +213,12 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None, two_calls=True)
     cos_h, sin_h = pkv.pkv_rope_table(cfg.head_dim, cfg.rope_base, max_pos)
     dcos, dsin = torch.from_numpy(cos_h).cuda(), torch.from_numpy(sin_h).cuda()
 
-    def step(events=None):
+    def step():
         pkv.pkv_decode_plan_upload(plan, ws)
         for layer in range(cfg.n_layers):
-            if events is not None:
-                events[layer][0].record()
             pkv.pkv_append_decode_attention(plan, pool, layer, q, tables, k_new[layer],
                                             v_new[layer], "pairs", dcos, dsin, max_pos, out, lse,
                                             ws, q_dtype=new_dt)
-            if events is not None:
-                events[layer][1].record()
 
     def step_two_calls():
         pkv.pkv_decode_plan_upload(plan, ws)
@@ -259,20 +255,21 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None, two_calls=True)
         u_e.record()
         torch.cuda.synchronize()
         two_calls_ms = u_s.elapsed_time(u_e) / steps
-    # Instrumented pass: the same number of steps again, with a HIP event
-    # pair around every launch on the stream the kernels run on, for the
-    # per-launch kernel duration (the markers themselves add a few us per
-    # launch, which is why they stay out of the timed region).
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(cfg.n_layers)]
-          for _ in range(launch_steps)]
+    # Instrumented pass: the same number of steps again, each launch carrying
+    # a start/stop event pair attached to its own dispatch (the kernel's
+    # execution, as a profiler's kernel trace measures it).
     i_s, i_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    i_s.record()
-    for k in range(launch_steps):
-        step(ev[k])
-    i_e.record()
-    torch.cuda.synchronize()
-    launch_ms = [ev[k][l][0].elapsed_time(ev[k][l][1]) for k in range(launch_steps)
-                 for l in range(cfg.n_layers)]
+    pkv.pkv_kernel_timing(True)
+    try:
+        i_s.record()
+        for _ in range(launch_steps):
+            step()
+        i_e.record()
+        torch.cuda.synchronize()
+    finally:
+        pkv.pkv_kernel_timing(False)
+    launch_ms = [float(x) for x in pkv.pkv_kernel_times()]
+    assert len(launch_ms) == launch_steps * cfg.n_layers, len(launch_ms)
     # attended tokens: the last `window` positions under a sliding window
     attended = np.minimum(lens, window) if window > 0 else lens
     per_decode = decode_bytes(attended, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads, 2,
@@ -633,8 +630,9 @@ def main():
                                                round(dec["launch_ms_p90"] * 1e3, 2)],
                      "frac_of_bw_probe": round(dec["launch_gbps"] / probe, 4),
                      "append_bytes_per_launch": dec["append_bytes_per_launch"],
-                     "launch_timing": "HIP events around each of %d launches in an instrumented "
-                                      "pass of %d steps after the timed steps (%.3f ms/step)"
+                     "launch_timing": "start/stop events attached to each of %d dispatches "
+                                      "(hipExtLaunchKernel, via pkv_kernel_timing) in a pass of "
+                                      "%d steps after the timed steps (%.3f ms/step)"
                                       % (dec["launches_timed"], dec["launches_timed"] // dec["layers"],
                                          dec["instrumented_ms_per_step"])},
         "two_calls_ms_per_step": _r4(dec["two_calls_ms_per_step"]),

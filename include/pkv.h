@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 7
+#define PKV_ABI_VERSION 8
 /* Tokens per physical block ([InferScale] §2; [KV essay] "Paged attention"). */
 #define PKV_BLOCK_TOKENS 16
 
@@ -463,6 +463,21 @@ pkv_status pkv_append_decode_attention(const pkv_plan* plan, const pkv_pool* poo
                                        int32_t rope_mode, const float* d_cos,
                                        const float* d_sin, int32_t max_pos, float* d_out,
                                        float* d_lse, void* d_ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Measurement helper: kernel durations from the dispatches themselves.
+ * pkv_kernel_timing(1) makes every following decode launch on the calling
+ * thread (pkv_decode_attention, pkv_append_decode_attention; the attention
+ * kernel, not a split sequence's merge kernel) carry a start/stop event pair
+ * attached to its own dispatch, so that the pair spans exactly the kernel's
+ * execution; pkv_kernel_timing(0) stops that.  pkv_kernel_times waits for
+ * the recorded launches, writes up to max_n durations in milliseconds
+ * (host float array) in launch order, releases every recorded pair and
+ * returns the number recorded (PKV_E_INVALID for a bad buffer, PKV_E_HIP if
+ * an event failed).
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_kernel_timing(int32_t enable);
+int32_t pkv_kernel_times(float* ms_out, int32_t max_n);
 
 /* ---------------------------------------------------------------------------
  * Measurement helper: a streaming 16-byte-per-lane read of n_bytes (a

@@ -119,6 +119,8 @@ SIGNATURES = {
                                            ctypes.c_float, _P, _I32, _P, _P, _I32, _P, _P, _I32,
                                            _P, _P, _P, _SZ, _P]),
     "pkv_bw_probe": (_I32, [_P, _SZ, _P, _P]),
+    "pkv_kernel_timing": (_I32, [_I32]),
+    "pkv_kernel_times": (_I32, [_P, _I32]),
 }
 
 _lib = None
@@ -462,6 +464,19 @@ def pkv_append_decode_attention(plan, pool: pkv_pool, layer, q, tables, k_new, v
         _ptr(k_new), _ptr(v_new), ROPE_CODES.get(rope_mode, rope_mode), _ptr(cos), _ptr(sin),
         max_pos, _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def pkv_kernel_timing(enable: bool):
+    _check(load_library().pkv_kernel_timing(1 if enable else 0))
+
+
+def pkv_kernel_times(max_n=1 << 20):
+    """Durations (ms, numpy float32) of the decode launches recorded since
+    timing was switched on; releases them."""
+    import numpy as np
+    buf = np.empty(max_n, dtype=np.float32)
+    n = _check(load_library().pkv_kernel_times(buf.ctypes.data, max_n))
+    return buf[:min(n, max_n)].copy()
 
 
 def pkv_bw_probe(src, sink, stream=None):

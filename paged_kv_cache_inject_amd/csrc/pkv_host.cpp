@@ -1195,6 +1195,19 @@ pkv_status pkv_append_decode_attention(const pkv_plan* plan, const pkv_pool* poo
                        d_lse, d_ws, ws_bytes, stream);
 }
 
+pkv_status pkv_kernel_timing(int32_t enable) {
+  pkv::set_kernel_timing(enable != 0);
+  return ok();
+}
+
+int32_t pkv_kernel_times(float* ms_out, int32_t max_n) {
+  if (max_n < 0 || (max_n > 0 && !ms_out)) return fail(PKV_E_INVALID, "bad output buffer");
+  hipError_t e = hipSuccess;
+  const int n = pkv::collect_kernel_times(ms_out, max_n, &e);
+  if (e != hipSuccess) return hip_fail(e, "kernel timing events");
+  return n;
+}
+
 pkv_status pkv_bw_probe(const void* d_src, size_t n_bytes, void* d_sink, void* stream) {
   if (!d_src || !d_sink || n_bytes % 16 || (reinterpret_cast<uintptr_t>(d_src) & 15))
     return fail(PKV_E_INVALID, "bad probe arguments");

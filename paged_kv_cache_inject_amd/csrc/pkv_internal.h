@@ -86,6 +86,13 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
 
 hipError_t launch_bw_probe(const void* src, size_t n_bytes, void* sink, hipStream_t stream);
 
+// Measurement: dispatch-attached timing of this thread's decode launches.
+void set_kernel_timing(bool on);
+// Waits for the recorded launches, writes up to max_n durations (ms) in launch
+// order, drops them all and returns how many there were; *err holds the
+// first HIP error met.
+int collect_kernel_times(float* ms_out, int max_n, hipError_t* err);
+
 // Copy-on-write copies handed to one launch (a kernel argument, no device
 // staging): pairs i < n copy every layer's K and V planes of block src[i]
 // into block dst[i].  No two pairs of a batch may touch a common block as

@@ -30,12 +30,15 @@
 // keys are reproducible bit for bit.  Where a fused multiply-add is wanted it
 // is written as fmaf().
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 
 #include <algorithm>
+#include <utility>
+#include <vector>
 
 #include "pkv_internal.h"
 
@@ -1355,6 +1358,34 @@ hipError_t launch(K kernel, dim3 grid, dim3 block, hipStream_t stream, const P& 
   return hipGetLastError();
 }
 
+// Kernel timing for measurement (this thread's decode launches): when on,
+// each launch carries a start/stop event pair attached to its own dispatch,
+// so the pair spans exactly the kernel's execution.
+struct KernelTiming {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pairs;
+};
+thread_local KernelTiming g_timing;
+
+template <typename K, typename... A>
+hipError_t launch_decode_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, A... args) {
+  if (!g_timing.on) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+    return hipGetLastError();
+  }
+  hipEvent_t a = nullptr, b = nullptr;
+  hipError_t e = hipEventCreate(&a);
+  if (e == hipSuccess) e = hipEventCreate(&b);
+  if (e != hipSuccess) {
+    if (a) (void)hipEventDestroy(a);
+    return e;
+  }
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, a, b, 0, args...);
+  e = hipGetLastError();
+  g_timing.pairs.emplace_back(a, b);
+  return e;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1509,9 +1540,8 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
 #define PKV_DEC_MFMA(KV, Q, DD, DEP, W)                                                      \
     if (!launched && mfma && pool.dtype == KV && a.q_dtype == Q && pool.head_dim == DD &&    \
         depth == DEP && nw == W) {                                                           \
-      hipLaunchKernelGGL((decode_mfma_kernel<KV, Q, DD, DEP, W>), grid, dim3(64 * W), 0,       \
-                         stream, p, p.tables);                                               \
-      e = hipGetLastError();                                                                 \
+      e = launch_decode_kernel(decode_mfma_kernel<KV, Q, DD, DEP, W>, grid, dim3(64 * W),    \
+                               stream, p, p.tables);                                         \
       launched = true;                                                                       \
     }
 #define PKV_DEC_MFMA_W(KV, Q, DD, DEP) \
@@ -1522,8 +1552,8 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
     PKV_DEC_MFMA_W(KV, Q, 128, 1) PKV_DEC_MFMA_W(KV, Q, 128, 2)
 #define PKV_DEC_VALU(DT, DD)                                                                 \
     if (!launched && pool.dtype == DT && pool.head_dim == DD) {                              \
-      hipLaunchKernelGGL((decode_valu_kernel<DT, DD>), grid, dim3(64), 0, stream, p, p.tables); \
-      e = hipGetLastError();                                                                 \
+      e = launch_decode_kernel(decode_valu_kernel<DT, DD>, grid, dim3(64), stream, p,        \
+                               p.tables);                                                    \
       launched = true;                                                                       \
     }
     PKV_DEC_MFMA_ALL(PKV_BF16, PKV_BF16) PKV_DEC_MFMA_ALL(PKV_F16, PKV_F16)
@@ -1564,6 +1594,25 @@ hipError_t launch_copy_blocks(const pkv_pool& pool, const CopyBatch& batch, hipS
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(batch.n, pool.n_layers, 2), dim3(256), 0, stream,
                      p, batch);
   return hipGetLastError();
+}
+
+void set_kernel_timing(bool on) { g_timing.on = on; }
+
+int collect_kernel_times(float* ms_out, int max_n, hipError_t* err) {
+  int n = 0;
+  *err = hipSuccess;
+  for (auto& pr : g_timing.pairs) {
+    float ms = -1.f;
+    hipError_t e = hipEventSynchronize(pr.second);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess && *err == hipSuccess) *err = e;
+    if (ms_out && n < max_n) ms_out[n] = ms;
+    ++n;
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+  }
+  g_timing.pairs.clear();
+  return n;
 }
 
 hipError_t launch_bw_probe(const void* src, size_t n_bytes, void* sink, hipStream_t stream) {
