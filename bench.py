@@ -371,8 +371,93 @@ def run_inject(reps):
                bytes_per_call=bytes_call, requests=cfg.batch, layers=L)
     log("inject: %.3f ms/call, %.3g tok/s, %.1f GB/s" % (ms, res["tokens_per_s"], res["gbps"]))
     pkv.pkv_cache_destroy(cache)
+    res["request_path"] = run_request_path(cfg, st, pool, src, runs, dcos, dsin, max_pos, ws,
+                                           reps=max(2, reps // 3))
     del store_k, store_v, buf, ws
     torch.cuda.empty_cache()
+    return res
+
+
+def run_request_path(cfg, st, pool, src, runs, dcos, dsin, max_pos, inject_ws, reps):
+    """Every step of the path for one batch of requests, from an empty cache:
+    reserve each request's blocks, inject the composed memory (all layers),
+    extend by the 32-token suffix, export and upload the tables, append the
+    suffix in every layer, extend by the decode token, export the tables
+    again, plan, and run the decode step (the token appended at len - 1 and
+    attended over) in every layer.  Timed from the host's first call to the
+    end of the last kernel; the GPU time of each phase comes from events."""
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    from workloads.configs import device_normal
+    L, H, d, B = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim, cfg.batch
+    HQ, suffix = cfg.n_q_heads, cfg.extra["suffix"]
+    row = H * d
+    seqs = list(range(B))
+    suf_k = [device_normal(B * suffix * row, "bf16", cfg.seed * 31 + 4 * l) for l in range(L)]
+    suf_v = [device_normal(B * suffix * row, "bf16", cfg.seed * 31 + 4 * l + 1) for l in range(L)]
+    tok_k = [device_normal(B * row, "bf16", cfg.seed * 31 + 4 * l + 2) for l in range(L)]
+    tok_v = [device_normal(B * row, "bf16", cfg.seed * 31 + 4 * l + 3) for l in range(L)]
+    q = device_normal(B * HQ * d, "bf16", cfg.seed * 37).view(B, HQ, d)
+    out = torch.empty(B, HQ, d, device="cuda")
+    lse = torch.empty(B, HQ, device="cuda")
+    tdev = torch.empty(B, st["max_blocks"], dtype=torch.int32, device="cuda")
+    fdev = torch.empty(B, dtype=torch.int32, device="cuda")
+    lens_end = np.asarray(st["mem_lens"]) + suffix + 1
+    probe = pkv.pkv_decode_plan_create(lens_end, HQ, H, d, 0)
+    dws = torch.empty(pkv.pkv_decode_workspace_bytes(probe), dtype=torch.uint8, device="cuda")
+    pkv.pkv_decode_plan_destroy(probe)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def batch():
+        c = pkv.pkv_cache_create(st["num_blocks"], B, st["max_blocks"], st["free_list_seed"])
+        for b, m in enumerate(st["mem_lens"]):
+            pkv.pkv_alloc_blocks(c, b, int(m))
+        ev[0].record()
+        pkv.pkv_inject(c, pool, src, runs, 0, L, "pairs", dcos, dsin, max_pos, inject_ws)
+        ev[1].record()
+        first = pkv.pkv_extend(c, seqs, suffix)
+        table, _ = pkv.pkv_block_table(c, seqs, st["max_blocks"])
+        tdev.copy_(torch.from_numpy(table))
+        fdev.copy_(torch.from_numpy(first.astype(np.int32)))
+        for layer in range(L):
+            pkv.pkv_append_kv(pool, layer, tdev, fdev, suffix, suf_k[layer], suf_v[layer],
+                              "pairs", dcos, dsin, max_pos)
+        ev[2].record()
+        pkv.pkv_extend(c, seqs, 1)
+        table, lens = pkv.pkv_block_table(c, seqs, st["max_blocks"])
+        tdev.copy_(torch.from_numpy(table))
+        plan = pkv.pkv_decode_plan_create(lens, HQ, H, d, 0)
+        pkv.pkv_decode_plan_upload(plan, dws)
+        for layer in range(L):
+            pkv.pkv_append_decode_attention(plan, pool, layer, q, tdev, tok_k[layer], tok_v[layer],
+                                            "pairs", dcos, dsin, max_pos, out, lse, dws)
+        ev[3].record()
+        return c, plan
+
+    c, plan = batch()                      # warm-up
+    torch.cuda.synchronize()
+    pkv.pkv_decode_plan_destroy(plan)
+    pkv.pkv_cache_destroy(c)
+    wall, phases = [], []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        c, plan = batch()
+        torch.cuda.synchronize()
+        wall.append((time.perf_counter() - t0) * 1e3)
+        phases.append([ev[i].elapsed_time(ev[i + 1]) for i in range(3)])
+        pkv.pkv_decode_plan_destroy(plan)
+        pkv.pkv_cache_destroy(c)
+    ms = float(np.median(wall))
+    ph = np.median(np.array(phases), axis=0)
+    n_tok = int(sum(r[1] for r in st["runs"]))
+    res = dict(ms_per_batch=ms, requests=B, layers=L, injected_tokens=n_tok,
+               requests_per_s=B / (ms * 1e-3), injected_tokens_per_s=n_tok / (ms * 1e-3),
+               gpu_ms_inject=float(ph[0]), gpu_ms_suffix_append=float(ph[1]),
+               gpu_ms_decode_step=float(ph[2]))
+    log("request path: %.3f ms per batch of %d requests (inject %.3f, suffix append %.3f, "
+        "decode step %.3f ms on the GPU)" % (ms, B, ph[0], ph[1], ph[2]))
+    del suf_k, suf_v, tok_k, tok_v, q, out, lse, tdev, fdev, dws
     return res
 
 
@@ -667,6 +752,17 @@ def main():
                           "layers": inj["layers"],
                           "workload": "top-8 of 10k chunks (64..256 tokens), 32 layers x 8 x 128 "
                                       "bf16, 64 requests, gaps of 1..15 positions"}
+        rp = inj["request_path"]
+        line["request_path"] = {
+            "workload": "the same 64 requests from an empty cache: reserve blocks, inject, "
+                        "32-token suffix append, decode step (token appended at len-1 and "
+                        "attended) over 32 layers; host planning and table uploads included",
+            "ms_per_batch": round(rp["ms_per_batch"], 3),
+            "requests_per_s": round(rp["requests_per_s"], 1),
+            "injected_tokens_per_s": round(rp["injected_tokens_per_s"], 1),
+            "gpu_ms": {"inject": round(rp["gpu_ms_inject"], 3),
+                       "suffix_append": round(rp["gpu_ms_suffix_append"], 3),
+                       "decode_step": round(rp["gpu_ms_decode_step"], 3)}}
     if inj_host is not None:
         line["inject_host_store"] = {
             "workload": "top-8 of 250 chunks (64..256 tokens) + prefix, 16 requests, 32 layers x "
