@@ -1,17 +1,20 @@
 // HIP kernels of libpkv for MI355X (gfx950, CDNA4, wave64).
 //
 //   inject_rope_kernel     write side: one workgroup per (destination block,
-//                          layer); rotates stored pre-RoPE keys to their
+//                          layers); rotates stored pre-RoPE keys to their
 //                          destination positions and scatters K/V into the
 //                          block's planes ("InferScale" §3 scatter copy through
-//                          the slot mapping, §3.3 and §5.1 chunked RoPE).
-//   append_kv_kernel       one workgroup per new token (the per-step append of
-//                          "InferScale" §2 / "LLM Inference: KV Caching",
-//                          "The fix").
+//                          the slot mapping, §3.3 and §5.1 chunked RoPE).  In
+//                          append mode it writes new tokens (the per-step
+//                          append of "InferScale" §2 / "LLM Inference: KV
+//                          Caching", "The fix"), one workgroup per (sequence,
+//                          block touched, group of KV heads).
 //   decode_mfma_kernel     read side: one workgroup per (token range, KV head),
 //                          its waves taking interleaved blocks; QK^T and PV of
 //                          the whole GQA group on MFMA tiles, online softmax
-//                          in registers, the waves' states merged in LDS.
+//                          in registers, the waves' states merged in LDS.  It
+//                          can also append each sequence's newest token first
+//                          (one launch per decode step and layer).
 //   decode_valu_kernel     generic read side for any dtype / group size.
 //   decode_merge_kernel    log-sum-exp merge of ranges of one sequence that
 //                          ran on different workgroups.
@@ -293,6 +296,18 @@ struct InjectParams {
   int rope_mode;
   const float* cos_t;
   const float* sin_t;
+  // Append mode (app_first non-null): workgroup x = (sequence b, i) makes its
+  // own descriptor, block i of the blocks holding positions
+  // [first_pos[b], first_pos[b] + app_n_new), whose tokens are source rows
+  // b * app_n_new + (position - first_pos[b]); workgroup y takes KV heads
+  // y * HG ... of the single layer layer_begin.
+  const int32_t* app_first;
+  const int32_t* app_tables;
+  int app_stride;
+  int app_n_new;
+  int app_blocks;                    // blocks one sequence's new tokens can touch
+  int num_blocks;
+  int max_pos;
 };
 
 constexpr int kInjectThreads = 256;
@@ -325,10 +340,42 @@ __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParam
   __shared__ float cs[kBlock][D];
   __shared__ InjectDesc desc;
 
-  if (threadIdx.x < sizeof(InjectDesc) / 4)
-    reinterpret_cast<int32_t*>(&desc)[threadIdx.x] =
-        reinterpret_cast<const int32_t*>(&p.descs[blockIdx.x])[threadIdx.x];
+  int h_begin = 0, h_end = p.n_kv_heads;
+  int l0 = p.layer_begin + blockIdx.y * p.layers_per_wg;
+  int l1 = min(l0 + p.layers_per_wg, p.layer_end);
+  if (p.app_first == nullptr) {
+    if (threadIdx.x < sizeof(InjectDesc) / 4)
+      reinterpret_cast<int32_t*>(&desc)[threadIdx.x] =
+          reinterpret_cast<const int32_t*>(&p.descs[blockIdx.x])[threadIdx.x];
+  } else {
+    const int b = blockIdx.x / p.app_blocks;
+    const int first = p.app_first[b];
+    const int lo = max(first, 0), hi = first + p.app_n_new;  // positions written
+    const int lb = lo / kBlock + (blockIdx.x - b * p.app_blocks);
+    if (threadIdx.x < kBlock) {
+      const int pos = lb * kBlock + threadIdx.x;
+      const bool in = pos >= lo && pos < hi && (p.rope_mode == PKV_ROPE_NONE || pos < p.max_pos);
+      desc.src[threadIdx.x] = in ? b * p.app_n_new + (pos - first) : -1;
+    } else if (threadIdx.x == kBlock) {
+      int blk = -1;
+      if (lo < hi && lb * kBlock < hi && lb < p.app_stride)
+        blk = p.app_tables[int64_t(b) * p.app_stride + lb];
+      desc.phys_block = blk >= 0 && blk < p.num_blocks ? blk : -1;
+      desc.pos_base = lb * kBlock;
+    }
+    h_begin = blockIdx.y * HG;
+    h_end = min(h_begin + HG, p.n_kv_heads);
+    l0 = p.layer_begin;
+    l1 = l0 + 1;
+  }
   __syncthreads();
+  if (p.app_first != nullptr) {
+    bool any = desc.phys_block >= 0;
+    bool some = false;
+#pragma unroll
+    for (int t = 0; t < kBlock; ++t) some |= desc.src[t] >= 0;
+    if (!(any && some)) return;  // the same for every thread: nothing to write here
+  }
   if (p.rope_mode != PKV_ROPE_NONE) {
     for (int w = threadIdx.x; w < kBlock * (D / 2); w += kInjectThreads) {
       const int t = w / (D / 2), i = w - t * (D / 2);
@@ -343,15 +390,13 @@ __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParam
   for (int t = 0; t < kBlock; ++t) full &= desc.src[t] >= 0;
   __syncthreads();
 
-  const int l0 = p.layer_begin + blockIdx.y * p.layers_per_wg;
-  const int l1 = min(l0 + p.layers_per_wg, p.layer_end);
   for (int layer = l0; layer < l1; ++layer) {
     char* kplane0 = p.pool_k + layer * p.p_layer + int64_t(desc.phys_block) * p.p_block;
     char* vplane0 = p.pool_v + layer * p.p_layer + int64_t(desc.phys_block) * p.p_block;
     const char* sk = p.src_k + layer * p.s_layer;
     const char* sv = p.src_v + layer * p.s_layer;
-    for (int h0 = 0; h0 < p.n_kv_heads; h0 += HG) {
-      const int nh = min(HG, p.n_kv_heads - h0);
+    for (int h0 = h_begin; h0 < h_end; h0 += HG) {
+      const int nh = min(HG, h_end - h0);
       uint4 k0[UPT], k1[UPT], v0[UPT], v1[UPT];
 #pragma unroll
       for (int u = 0; u < UPT; ++u) {
@@ -423,11 +468,15 @@ __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParam
         const int t0 = (r % (kBlock / XP)) * XP;
         char* dst = vplane0 + int64_t(h0 + hl) * p.p_head + (int64_t(j) * kBlock + t0) * EP;
         TP out[XP];
-        bool need_old = false;
+        bool need_old = false, any = full;
         if (!full) {
 #pragma unroll
-          for (int e = 0; e < XP; ++e) need_old |= desc.src[t0 + e] < 0;
+          for (int e = 0; e < XP; ++e) {
+            need_old |= desc.src[t0 + e] < 0;
+            any |= desc.src[t0 + e] >= 0;
+          }
         }
+        if (!any) continue;  // no slot of this piece is written
         if (need_old) *reinterpret_cast<uint4*>(out) = ld16(dst);
 #pragma unroll
         for (int e = 0; e < XP; ++e)
@@ -437,56 +486,6 @@ __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParam
       __syncthreads();
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Append: one workgroup per (sequence, new token)
-// ---------------------------------------------------------------------------
-struct AppendParams {
-  char* pool_k;
-  char* pool_v;
-  int64_t p_layer, p_block, p_head;  // bytes
-  int n_kv_heads;
-  const float* k_scale;              // [layers][heads], quantised pools only
-  const float* v_scale;
-  int num_blocks;
-  int layer;
-  const int32_t* tables;
-  int table_stride;
-  const int32_t* first_pos;
-  int n_new;
-  const char* k_new;
-  const char* v_new;
-  int rope_mode;
-  const float* cos_t;
-  const float* sin_t;
-  int max_pos;
-};
-
-// One token's K row of one head: rotate source chunk pair (c0, c0 + CS/2) at
-// the position whose rotary rows are cr/sr (mode PAIRS, HALVES or NONE) and
-// store both chunks at slot `tin` of the K plane (chunk-major: [chunk][slot]).
-template <int SDT, int PDT, int D>
-__device__ inline void put_k_pair(const char* kin, char* kplane, int tin, int c0, int mode,
-                                  const float* cr, const float* sr, float ksc) {
-  constexpr int ES = Fmt<SDT>::kBytes, EP = Fmt<PDT>::kBytes;
-  constexpr int XS = 16 / ES, XP = 16 / EP;
-  constexpr int CS = D / XS;
-  const int j0 = c0 * XS, j1 = (c0 + CS / 2) * XS;
-  float kl[XS], kh[XS];
-  unpack16<SDT>(ld16(kin + j0 * ES), kl);
-  unpack16<SDT>(ld16(kin + j1 * ES), kh);
-  if (mode == PKV_ROPE_PAIRS) {
-    rot_pairs_f<XS>(kl, j0, cr, sr);
-    rot_pairs_f<XS>(kh, j1, cr, sr);
-  } else if (mode == PKV_ROPE_HALVES) {
-    rot_halves_f<XS>(kl, kh, j0, cr, sr);
-  }
-  Packed<PDT, XS> pk;
-  pk.set(kl, ksc);
-  store_packed(kplane + (((j0 / XP) * kBlock + tin) * XP + j0 % XP) * EP, pk);
-  pk.set(kh, ksc);
-  store_packed(kplane + (((j1 / XP) * kBlock + tin) * XP + j1 % XP) * EP, pk);
 }
 
 // One token's V element j of one head, stored at slot `tin` of the V plane
@@ -503,42 +502,6 @@ __device__ inline void put_v_elem(const char* vin, char* vplane, int tin, int j,
     out = Fmt<PDT>::from_f32(Fmt<SDT>::to_f32(v) / vsc);
   }
   reinterpret_cast<TP*>(vplane)[j * kBlock + tin] = out;
-}
-
-template <int SDT, int PDT, int D>
-__global__ __launch_bounds__(256) void append_kv_kernel(AppendParams p) {
-  constexpr int ES = Fmt<SDT>::kBytes;
-  constexpr int CS = D / (16 / ES);
-  const int b = blockIdx.x / p.n_new;
-  const int t = blockIdx.x - b * p.n_new;
-  const int pos = p.first_pos[b] + t;
-  if (pos < 0) return;
-  if (p.rope_mode != PKV_ROPE_NONE && pos >= p.max_pos) return;
-  const int lb = pos / kBlock;
-  if (lb >= p.table_stride) return;
-  const int blk = p.tables[int64_t(b) * p.table_stride + lb];
-  if (blk < 0 || blk >= p.num_blocks) return;
-  const int tin = pos % kBlock;
-  char* kplane0 = p.pool_k + p.layer * p.p_layer + int64_t(blk) * p.p_block;
-  char* vplane0 = p.pool_v + p.layer * p.p_layer + int64_t(blk) * p.p_block;
-  const int64_t row0 = (int64_t(b) * p.n_new + t) * p.n_kv_heads * D * ES;
-  const char* kin = p.k_new + row0;
-  const char* vin = p.v_new + row0;
-  const float* cr = p.cos_t + size_t(pos) * (D / 2);
-  const float* sr = p.sin_t + size_t(pos) * (D / 2);
-  for (int w = threadIdx.x; w < p.n_kv_heads * (CS / 2); w += blockDim.x) {
-    const int h = w / (CS / 2);
-    const int c0 = w - h * (CS / 2);
-    const float ksc = PDT == PKV_FP8E4M3 ? p.k_scale[p.layer * p.n_kv_heads + h] : 1.f;
-    put_k_pair<SDT, PDT, D>(kin + int64_t(h) * D * ES, kplane0 + int64_t(h) * p.p_head, tin, c0,
-                            p.rope_mode, cr, sr, ksc);
-  }
-  for (int w = threadIdx.x; w < p.n_kv_heads * D; w += blockDim.x) {
-    const int h = w / D;
-    const int j = w - h * D;
-    const float vsc = PDT == PKV_FP8E4M3 ? p.v_scale[p.layer * p.n_kv_heads + h] : 1.f;
-    put_v_elem<SDT, PDT>(vin + int64_t(h) * D * ES, vplane0 + int64_t(h) * p.p_head, tin, j, vsc);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -641,8 +604,8 @@ __device__ inline void set_slot_planes(NewSlot& ns, const DecodeParams& p, int b
 }
 
 // Pool chunk c (dims c*XP .. c*XP + XP - 1) of the new token's K row: the
-// source dims rotated as put_k_pair rotates them (the halves pairing reads
-// the partner dims D/2 away as well), stored at the token's slot.  load()
+// source dims rotated as the inject kernel rotates them (the halves pairing
+// reads the partner dims D/2 away as well), stored at the token's slot.  load()
 // reads everything the chunk needs and store() computes and writes it, so
 // that a caller can issue all its loads before its first store.  The decode
 // kernels call them from the lane that later loads this chunk, so the lane's
@@ -1397,7 +1360,7 @@ hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, bool src_in_h
                          hipStream_t stream) {
   const int eb = elem_size(pool.dtype);
   const int sb = elem_size(src.dtype);
-  InjectParams p;
+  InjectParams p{};
   p.pool_k = static_cast<char*>(pool.k);
   p.pool_v = static_cast<char*>(pool.v);
   p.p_layer = pool.layer_stride * eb;
@@ -1451,8 +1414,13 @@ hipError_t launch_append(const pkv_pool& pool, int layer, const int32_t* d_table
                          const void* d_k, const void* d_v, int new_dtype, int rope_mode,
                          const float* d_cos, const float* d_sin, int max_pos,
                          hipStream_t stream) {
+  // The inject kernel in append mode: one workgroup per (sequence, block the
+  // new tokens can touch, group of 4 KV heads), its descriptor made on the
+  // device from the sequence's first position and table row.
   const int eb = elem_size(pool.dtype);
-  AppendParams p;
+  const int sb = elem_size(new_dtype);
+  constexpr int HG = 4;
+  InjectParams p{};
   p.pool_k = static_cast<char*>(pool.k);
   p.pool_v = static_cast<char*>(pool.v);
   p.p_layer = pool.layer_stride * eb;
@@ -1461,23 +1429,29 @@ hipError_t launch_append(const pkv_pool& pool, int layer, const int32_t* d_table
   p.n_kv_heads = pool.n_kv_heads;
   p.k_scale = pool.k_scale;
   p.v_scale = pool.v_scale;
-  p.num_blocks = pool.num_blocks;
-  p.layer = layer;
-  p.tables = d_tables;
-  p.table_stride = table_stride;
-  p.first_pos = d_first_pos;
-  p.n_new = n_new;
-  p.k_new = static_cast<const char*>(d_k);
-  p.v_new = static_cast<const char*>(d_v);
+  p.src_k = static_cast<const char*>(d_k);
+  p.src_v = static_cast<const char*>(d_v);
+  p.s_layer = 0;
+  p.s_token = int64_t(pool.n_kv_heads) * pool.head_dim * sb;
+  p.layer_begin = layer;
+  p.layer_end = layer + 1;
+  p.layers_per_wg = 1;
   p.rope_mode = rope_mode;
   p.cos_t = d_cos;
   p.sin_t = d_sin;
+  p.app_first = d_first_pos;
+  p.app_tables = d_tables;
+  p.app_stride = table_stride;
+  p.app_n_new = n_new;
+  p.app_blocks = (n_new + 2 * kBlock - 2) / kBlock;  // ceil((n_new + 15) / 16)
+  p.num_blocks = pool.num_blocks;
   p.max_pos = max_pos;
-  dim3 grid(int64_t(n_seqs) * n_new);
-  dim3 block(256);
+  if (int64_t(n_seqs) * p.app_blocks > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid(unsigned(n_seqs * p.app_blocks), unsigned((pool.n_kv_heads + HG - 1) / HG));
+  dim3 block(kInjectThreads);
 #define PKV_APP(SDT, PDT, DD) \
   if (new_dtype == SDT && pool.dtype == PDT && pool.head_dim == DD) \
-    return launch(append_kv_kernel<SDT, PDT, DD>, grid, block, stream, p);
+    return launch(inject_rope_kernel<SDT, PDT, DD, HG, false>, grid, block, stream, p);
 #define PKV_APP_D(SDT, PDT) PKV_APP(SDT, PDT, 64) PKV_APP(SDT, PDT, 128)
   PKV_APP_D(PKV_F32, PKV_F32) PKV_APP_D(PKV_BF16, PKV_BF16) PKV_APP_D(PKV_F16, PKV_F16)
   PKV_APP_D(PKV_BF16, PKV_FP8E4M3) PKV_APP_D(PKV_F16, PKV_FP8E4M3)
