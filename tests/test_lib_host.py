@@ -414,3 +414,13 @@ def test_cache_facade_is_the_handle_calls():
         assert [c.block_refcount(b) for b in range(16)] == m.ref
         assert c.table_width() == 8
     assert c.handle is None
+
+
+def test_kernel_timing_helper_without_launches():
+    """The timing helper returns nothing recorded when nothing was launched,
+    and rejects a missing output buffer."""
+    assert len(pkv.pkv_kernel_times()) == 0
+    pkv.pkv_kernel_timing(True)
+    pkv.pkv_kernel_timing(False)
+    assert len(pkv.pkv_kernel_times()) == 0
+    assert pkv.load_library().pkv_kernel_times(None, 4) == pkv.PKV_E_INVALID
