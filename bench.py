@@ -152,9 +152,11 @@ def bw_probe(n_bytes=8 << 30, reps=5):
 
 
 def decode_workload(name):
-    from workloads.configs import (LLAMA8B_1LAYER, LLAMA70B_80LAYER, MISTRAL_WINDOW, RAGGED_MHA,
-                                   llama70b_structure, llama8b_structure, ragged_mha_structure,
-                                   window_structure)
+    from workloads.configs import (LLAMA8B_1LAYER, LLAMA70B_80LAYER, MISTRAL_WINDOW, MQA_64,
+                                   RAGGED_MHA, llama70b_structure, llama8b_structure,
+                                   ragged_mha_structure, window_structure)
+    if name == "mqa":
+        return MQA_64, llama70b_structure(MQA_64)
     if name == "mistral-window":
         return MISTRAL_WINDOW, window_structure()
     if name in ("70b", "70b-fp8"):
@@ -649,7 +651,8 @@ def main():
     ap.add_argument("--no-two-calls", action="store_true",
                     help="skip the comparison timing of the step as two launches per layer")
     ap.add_argument("--decode-workload", default="70b",
-                    choices=["70b", "8b", "ragged", "70b-fp8", "mistral-window", "70b-block32"],
+                    choices=["70b", "8b", "ragged", "70b-fp8", "mistral-window", "70b-block32",
+                             "mqa"],
                     help="decode workload timed (the reported line uses 70b)")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -401,7 +401,8 @@ pkv_status pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* d_t
  * scaled scores).  A sequence of length 0 gets out = 0, lse = -inf.
  * q: device [n_seqs][n_q_heads][head_dim] in q_dtype (the pool's; PKV_BF16 or
  * PKV_F16 for an FP8E4M3 pool), already rotated to its own position.
- * scale <= 0 selects 1/sqrt(head_dim).
+ * scale <= 0 selects 1/sqrt(head_dim).  An FP8E4M3 pool takes up to 64 query
+ * heads per KV head (PKV_E_UNSUPPORTED beyond); other pools take any group.
  * ------------------------------------------------------------------------- */
 pkv_status pkv_decode_plan_create(const int64_t* lens, int32_t n_seqs, int32_t n_q_heads,
                                   int32_t n_kv_heads, int32_t head_dim, int32_t part_tokens,

@@ -1104,8 +1104,8 @@ pkv_status decode_common(const pkv_plan* plan, const pkv_pool* pool, int32_t lay
   if (layer < 0 || layer >= pool->n_layers) return fail(PKV_E_INVALID, "layer %d", layer);
   if (pool->n_kv_heads != plan->n_kv_heads || pool->head_dim != plan->head_dim)
     return fail(PKV_E_INVALID, "plan and pool disagree on KV heads or head_dim");
-  if (pool->dtype == PKV_FP8E4M3 && plan->n_q_heads / plan->n_kv_heads > 16)
-    return fail(PKV_E_UNSUPPORTED, "FP8E4M3 decode supports up to 16 query heads per KV head");
+  if (pool->dtype == PKV_FP8E4M3 && plan->n_q_heads / plan->n_kv_heads > 64)
+    return fail(PKV_E_UNSUPPORTED, "FP8E4M3 decode supports up to 64 query heads per KV head");
   if (nt.k) {
     if (pkv_status st = check_rope(nt.rope_mode, nt.cos, nt.sin, nt.max_pos)) return st;
     if (!nt.v) return fail(PKV_E_INVALID, "null v_new");

@@ -754,8 +754,10 @@ __device__ inline uint2 e4m3x4_to_f16x4(uint32_t w) {
 
 // Decode kernel template parameters: KVDT the pool format, QDT the query
 // format (equal to KVDT, or BF16/F16 for an fp8 pool whose MFMA operands are
-// float16), head dim D, prefetch depth, waves per workgroup NW.
-template <int KVDT, int QDT, int D, int DEPTH, int NW>
+// float16), head dim D, prefetch depth, waves per workgroup NW, and NG tiles
+// of 16 query heads (a KV head's group of up to 16 NG query heads: every
+// block's K and V, loaded once, serve all NG tiles).
+template <int KVDT, int QDT, int D, int DEPTH, int NW, int NG>
 // `tables` is p.tables again as a restrict-qualified argument: the kernel's
 // only stores (the fused append) go to the pool, and with the table known
 // not to alias them its entries keep coming through scalar loads.
@@ -776,17 +778,19 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
   int item_i, g;
   decode_work(p, blockIdx.x, item_i, g);
   const DecodeItem it = p.items[item_i];
-  const int hq = g * p.group + row;
-  const bool head_ok = row < p.group;
+  // Tile t covers query heads g G + 16 t + row (G = p.group).
+  auto head_of = [&](int t) { return g * p.group + 16 * t + row; };
+  auto head_ok = [&](int t) { return 16 * t + row < p.group; };
 
-  // q operand (B of QK) for head `row`: the dims whose K this lane loads in
-  // the same step (16-bit pools: chunk 4s + grp of 8 dims; fp8 pools: half
-  // `st % 2` of chunk 4(st/2) + grp of 16 dims).
-  uint4 qreg[S];
-  {
+  // q operand (B of QK) for head `row` of each tile: the dims whose K this
+  // lane loads in the same step (16-bit pools: chunk 4s + grp of 8 dims; fp8
+  // pools: half `st % 2` of chunk 4(st/2) + grp of 16 dims).
+  uint4 qreg[NG][S];
+#pragma unroll
+  for (int t = 0; t < NG; ++t) {
     typedef typename Fmt<QDT>::T TQ;
     const TQ* qh = reinterpret_cast<const TQ*>(p.q) +
-                   (int64_t(it.seq) * p.n_q_heads + (head_ok ? hq : g * p.group)) * D;
+                   (int64_t(it.seq) * p.n_q_heads + (head_ok(t) ? head_of(t) : g * p.group)) * D;
 #pragma unroll
     for (int st = 0; st < S; ++st) {
       const int dim0 = FP8 ? (4 * (st / 2) + grp) * 16 + 8 * (st % 2) : (4 * st + grp) * 8;
@@ -799,7 +803,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
         for (int e = 0; e < 8; ++e) hv[e] = static_cast<_Float16>(f[e]);
         raw = *reinterpret_cast<const uint4*>(hv);
       }
-      qreg[st] = head_ok ? raw : make_uint4(0, 0, 0, 0);
+      qreg[t][st] = head_ok(t) ? raw : make_uint4(0, 0, 0, 0);
     }
   }
   float kmul = 1.f, vmul = 1.f;
@@ -827,11 +831,16 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
     if (lb % NW == wave) put_j = lb / NW;
   }
 
-  f32x4_t acc[NT];
+  f32x4_t acc[NG][NT];
+  float m[NG];  // running max (log2 domain), uniform over the head's lanes
+  float l[NG];  // this lane's share of the running sum
 #pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;  // running max (log2 domain), uniform over the head's lanes
-  float l = 0.f;        // this lane's share of the running sum
+  for (int t = 0; t < NG; ++t) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m[t] = -INFINITY;
+    l[t] = 0.f;
+  }
 
   uint4 kbuf[DEPTH][SL];
   uint2 vbuf[DEPTH][NT];   // fp8: only .x holds the 4 codes
@@ -954,19 +963,29 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
             }
           }
         }
-        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+        // every tile's scores before the next block's loads reuse kbuf[d]
+        f32x4_t sc[NG];
+#pragma unroll
+        for (int t = 0; t < NG; ++t) sc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if constexpr (FP8) {
 #pragma unroll
           for (int s = 0; s < SL; ++s) {
             const uint4 w = kbuf[d][s];
             const uint2 a0 = e4m3x4_to_f16x4(w.x), a1 = e4m3x4_to_f16x4(w.y);
             const uint2 a2 = e4m3x4_to_f16x4(w.z), a3 = e4m3x4_to_f16x4(w.w);
-            sc = Mfma<OT>::qk(make_uint4(a0.x, a0.y, a1.x, a1.y), qreg[2 * s], sc);
-            sc = Mfma<OT>::qk(make_uint4(a2.x, a2.y, a3.x, a3.y), qreg[2 * s + 1], sc);
+            const uint4 k0 = make_uint4(a0.x, a0.y, a1.x, a1.y);
+            const uint4 k1 = make_uint4(a2.x, a2.y, a3.x, a3.y);
+#pragma unroll
+            for (int t = 0; t < NG; ++t) {
+              sc[t] = Mfma<OT>::qk(k0, qreg[t][2 * s], sc[t]);
+              sc[t] = Mfma<OT>::qk(k1, qreg[t][2 * s + 1], sc[t]);
+            }
           }
         } else {
 #pragma unroll
-          for (int s = 0; s < S; ++s) sc = Mfma<OT>::qk(kbuf[d][s], qreg[s], sc);
+          for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int t = 0; t < NG; ++t) sc[t] = Mfma<OT>::qk(kbuf[d][s], qreg[t][s], sc[t]);
         }
         uint2 vcur[NT];
 #pragma unroll
@@ -995,101 +1014,119 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
             vcur[n].y &= mx1;
           }
         }
-        float s4[4];
-        float mx = -INFINITY;
+        bool live[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool live = blk_ok && (4 * grp + r) < valid && (4 * grp + r) >= skip;
-          s4[r] = live ? sc[r] * score_mul : -INFINITY;
-          mx = fmaxf(mx, s4[r]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // Rescale the running state only when some head's maximum grows (a
-        // wave-uniform test): otherwise the factor would be exactly 1, and
-        // after the first blocks of a long range it rarely grows.
-        const bool grow = mx > m;  // false while both are -inf
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-          const float alpha = grow ? exp2f(m - mx) : 1.f;  // 0 when m was -inf
-          l *= alpha;
+        for (int r = 0; r < 4; ++r)
+          live[r] = blk_ok && (4 * grp + r) < valid && (4 * grp + r) >= skip;
 #pragma unroll
-          for (int n = 0; n < NT; ++n) acc[n] *= alpha;
-          m = fmaxf(m, mx);
-        }
-        // m is -inf only while every score seen so far is masked; then every
-        // s4 is -inf too and its weight must be 0.
-        const float m_ref = m == -INFINITY ? 0.f : m;
-        float pr[4];
+        for (int t = 0; t < NG; ++t) {
+          float s4[4];
+          float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pr[r] = exp2f(s4[r] - m_ref);
-          l += pr[r];
-        }
-        uint16_t ph[4], pl[4];
+          for (int r = 0; r < 4; ++r) {
+            s4[r] = live[r] ? sc[t][r] * score_mul : -INFINITY;
+            mx = fmaxf(mx, s4[r]);
+          }
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          // Rescale the running state only when some head's maximum grows (a
+          // wave-uniform test): otherwise the factor would be exactly 1, and
+          // after the first blocks of a long range it rarely grows.
+          const bool grow = mx > m[t];  // false while both are -inf
+          if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float alpha = grow ? exp2f(m[t] - mx) : 1.f;  // 0 when m was -inf
+            l[t] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Mfma<OT>::split(pr[r], ph[r], pl[r]);
-        const uint2 bh = make_uint2(uint32_t(ph[0]) | (uint32_t(ph[1]) << 16),
-                                    uint32_t(ph[2]) | (uint32_t(ph[3]) << 16));
-        const uint2 bl = make_uint2(uint32_t(pl[0]) | (uint32_t(pl[1]) << 16),
-                                    uint32_t(pl[2]) | (uint32_t(pl[3]) << 16));
+            for (int n = 0; n < NT; ++n) acc[t][n] *= alpha;
+            m[t] = fmaxf(m[t], mx);
+          }
+          // m is -inf only while every score seen so far is masked; then every
+          // s4 is -inf too and its weight must be 0.
+          const float m_ref = m[t] == -INFINITY ? 0.f : m[t];
+          float pr[4];
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          acc[n] = Mfma<OT>::pv(vcur[n], bh, acc[n]);
-          acc[n] = Mfma<OT>::pv(vcur[n], bl, acc[n]);
+          for (int r = 0; r < 4; ++r) {
+            pr[r] = exp2f(s4[r] - m_ref);
+            l[t] += pr[r];
+          }
+          uint16_t ph[4], pl[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Mfma<OT>::split(pr[r], ph[r], pl[r]);
+          const uint2 bh = make_uint2(uint32_t(ph[0]) | (uint32_t(ph[1]) << 16),
+                                      uint32_t(ph[2]) | (uint32_t(ph[3]) << 16));
+          const uint2 bl = make_uint2(uint32_t(pl[0]) | (uint32_t(pl[1]) << 16),
+                                      uint32_t(pl[2]) | (uint32_t(pl[3]) << 16));
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            acc[t][n] = Mfma<OT>::pv(vcur[n], bh, acc[t][n]);
+            acc[t][n] = Mfma<OT>::pv(vcur[n], bl, acc[t][n]);
+          }
         }
       }
     }
   }
 
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+#pragma unroll
+  for (int t = 0; t < NG; ++t) {
+    l[t] += __shfl_xor(l[t], 16);
+    l[t] += __shfl_xor(l[t], 32);
+  }
 
   if constexpr (NW > 1) {
-    // Merge the waves' softmax states.  Every wave scales its partial output
-    // to the common maximum and parks it in LDS; wave w then sums output
-    // tiles w, w + NW, ... over all waves in fixed order (wave 0, 1, ...).
+    // Merge the waves' softmax states, one tile of heads at a time.  Every
+    // wave scales its partial output to the common maximum and parks it in
+    // LDS; wave w then sums output tiles w, w + NW, ... over all waves in
+    // fixed order (wave 0, 1, ...).
     __shared__ float sm_m[NW][16], sm_l[NW][16];
     __shared__ float sm_o[NW][16][D + 4];
-    if (grp == 0) {
-      sm_m[wave][row] = m;
-      sm_l[wave][row] = l;
-    }
-    __syncthreads();
-    float big_m = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) big_m = fmaxf(big_m, sm_m[w][row]);
-    float big_l = 0.f;
+    for (int t = 0; t < NG; ++t) {
+      if (t > 0) __syncthreads();  // the previous tile's reads of LDS are done
+      if (grp == 0) {
+        sm_m[wave][row] = m[t];
+        sm_l[wave][row] = l[t];
+      }
+      __syncthreads();
+      float big_m = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = sm_m[w][row];
-      big_l += (mw == -INFINITY ? 0.f : exp2f(mw - big_m)) * sm_l[w][row];
-    }
-    const float own = m == -INFINITY ? 0.f : exp2f(m - big_m);
+      for (int w = 0; w < NW; ++w) big_m = fmaxf(big_m, sm_m[w][row]);
+      float big_l = 0.f;
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      *reinterpret_cast<f32x4_t*>(&sm_o[wave][row][16 * n + 4 * grp]) = acc[n] * own;
-    __syncthreads();
-    if (!head_ok) return;
-    for (int n = wave; n < NT; n += NW) {
-      f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+      for (int w = 0; w < NW; ++w) {
+        const float mw = sm_m[w][row];
+        big_l += (mw == -INFINITY ? 0.f : exp2f(mw - big_m)) * sm_l[w][row];
+      }
+      const float own = m[t] == -INFINITY ? 0.f : exp2f(m[t] - big_m);
 #pragma unroll
-      for (int w = 0; w < NW; ++w)
-        a += *reinterpret_cast<const f32x4_t*>(&sm_o[w][row][16 * n + 4 * grp]);
+      for (int n = 0; n < NT; ++n)
+        *reinterpret_cast<f32x4_t*>(&sm_o[wave][row][16 * n + 4 * grp]) = acc[t][n] * own;
+      __syncthreads();
+      if (head_ok(t)) {
+        for (int n = wave; n < NT; n += NW) {
+          f32x4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        store_head_result(p, it, hq, 16 * n + 4 * grp + r, a[r] * vmul, big_m, big_l,
-                          n == 0 && r == 0 && grp == 0, D);
+          for (int w = 0; w < NW; ++w)
+            a += *reinterpret_cast<const f32x4_t*>(&sm_o[w][row][16 * n + 4 * grp]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            store_head_result(p, it, head_of(t), 16 * n + 4 * grp + r, a[r] * vmul, big_m,
+                              big_l, n == 0 && r == 0 && grp == 0, D);
+        }
+      }
     }
     return;
   }
 
-  if (!head_ok) return;
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
+  for (int t = 0; t < NG; ++t) {
+    if (!head_ok(t)) continue;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      store_head_result(p, it, hq, 16 * n + 4 * grp + r, acc[n][r] * vmul, m, l,
-                        n == 0 && r == 0 && grp == 0, D);
+    for (int n = 0; n < NT; ++n) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        store_head_result(p, it, head_of(t), 16 * n + 4 * grp + r, acc[t][n][r] * vmul, m[t],
+                          l[t], n == 0 && r == 0 && grp == 0, D);
+    }
   }
 }
 
@@ -1505,25 +1542,35 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
     dim3 grid(unsigned(a.n_items) * unsigned(pool.n_kv_heads));
     // variant: 0 automatic, 1 generic VALU kernel (not for fp8 pools), 10 + k
     // MFMA kernel with a prefetch depth of k blocks (k = 1, 2).
+    // Tiles of 16 query heads per KV head: groups up to 64 run on MFMA.
+    const int ng = p.group <= 16 ? 1 : p.group <= 32 ? 2 : p.group <= 64 ? 4 : 0;
     const bool mfma = (kernel_variant != 1 || pool.dtype == PKV_FP8E4M3) &&
-                      pool.dtype != PKV_F32 && p.group <= 16;
+                      pool.dtype != PKV_F32 && ng > 0;
     // One block in flight per wave measured fastest with 8 waves per workgroup.
     const int depth = kernel_variant == 12 ? 2 : 1;
-    const int nw = a.waves;
+    // More tiles hold more accumulators: 2 tiles fit 8 waves per workgroup
+    // (two per SIMD), 4 tiles one wave per SIMD.
+    int nw = a.waves;
+    if (ng == 2) nw = nw >= 8 ? 8 : 4;
+    if (ng == 4) nw = 4;
     bool launched = false;
-#define PKV_DEC_MFMA(KV, Q, DD, DEP, W)                                                      \
+#define PKV_DEC_MFMA(KV, Q, DD, DEP, W, G)                                                   \
     if (!launched && mfma && pool.dtype == KV && a.q_dtype == Q && pool.head_dim == DD &&    \
-        depth == DEP && nw == W) {                                                           \
-      e = launch_decode_kernel(decode_mfma_kernel<KV, Q, DD, DEP, W>, grid, dim3(64 * W),    \
+        depth == DEP && nw == W && ng == G) {                                                \
+      e = launch_decode_kernel(decode_mfma_kernel<KV, Q, DD, DEP, W, G>, grid, dim3(64 * W), \
                                stream, p, p.tables);                                         \
       launched = true;                                                                       \
     }
 #define PKV_DEC_MFMA_W(KV, Q, DD, DEP) \
-    PKV_DEC_MFMA(KV, Q, DD, DEP, 1) PKV_DEC_MFMA(KV, Q, DD, DEP, 2) \
-    PKV_DEC_MFMA(KV, Q, DD, DEP, 4) PKV_DEC_MFMA(KV, Q, DD, DEP, 8)
+    PKV_DEC_MFMA(KV, Q, DD, DEP, 1, 1) PKV_DEC_MFMA(KV, Q, DD, DEP, 2, 1) \
+    PKV_DEC_MFMA(KV, Q, DD, DEP, 4, 1) PKV_DEC_MFMA(KV, Q, DD, DEP, 8, 1)
+#define PKV_DEC_MFMA_G(KV, Q, DD) \
+    PKV_DEC_MFMA(KV, Q, DD, 1, 4, 2) PKV_DEC_MFMA(KV, Q, DD, 1, 8, 2) \
+    PKV_DEC_MFMA(KV, Q, DD, 1, 4, 4)
 #define PKV_DEC_MFMA_ALL(KV, Q) \
     PKV_DEC_MFMA_W(KV, Q, 64, 1) PKV_DEC_MFMA_W(KV, Q, 64, 2) \
-    PKV_DEC_MFMA_W(KV, Q, 128, 1) PKV_DEC_MFMA_W(KV, Q, 128, 2)
+    PKV_DEC_MFMA_W(KV, Q, 128, 1) PKV_DEC_MFMA_W(KV, Q, 128, 2) \
+    PKV_DEC_MFMA_G(KV, Q, 64) PKV_DEC_MFMA_G(KV, Q, 128)
 #define PKV_DEC_VALU(DT, DD)                                                                 \
     if (!launched && pool.dtype == DT && pool.head_dim == DD) {                              \
       e = launch_decode_kernel(decode_valu_kernel<DT, DD>, grid, dim3(64), stream, p,        \
@@ -1536,6 +1583,7 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
     PKV_DEC_VALU(PKV_BF16, 128) PKV_DEC_VALU(PKV_F16, 64) PKV_DEC_VALU(PKV_F16, 128)
 #undef PKV_DEC_MFMA
 #undef PKV_DEC_MFMA_W
+#undef PKV_DEC_MFMA_G
 #undef PKV_DEC_MFMA_ALL
 #undef PKV_DEC_VALU
     if (!launched) return hipErrorInvalidValue;

@@ -5,10 +5,10 @@ The call must leave the pool and produce out/lse byte for byte as
 pkv_append_kv (first position len - 1, one token) followed by
 pkv_decode_attention does, and match the oracle's append and decode: pool
 bytes exactly, attention within tolerance.  Cases cover the MFMA kernel
-(bf16, f16, fp8 pools; head dims 64 and 128), the generic kernel (float32
-pools, 32 query heads per KV head), split ranges (only the last range
-writes), a sliding window, the three rotary pairings, and lengths 0, 1 and
-block edges."""
+(bf16, f16, fp8 pools; head dims 64 and 128; 1, 2 and 4 tiles of 16 query
+heads per KV head), the generic kernel (float32 pools), split ranges (only
+the last range writes), a sliding window, the three rotary pairings, and
+lengths 0, 1 and block edges."""
 
 import numpy as np
 import pytest
@@ -28,6 +28,8 @@ CASES = [
     ("fp8", 4, 4, 64, "pairs", 0, 0),
     ("f32", 4, 2, 64, "pairs", 0, 0),
     ("bf16", 64, 2, 128, "halves", 0, 0),
+    ("fp8", 64, 2, 128, "pairs", 16, 0),
+    ("bf16", 64, 1, 64, "halves", 0, 0),
     ("bf16", 32, 8, 128, "pairs", 0, 100),
 ]
 

@@ -64,6 +64,8 @@ def test_llama8b_layer_full():
 @pytest.mark.parametrize("dtype,hq,hkv,d", [
     ("bf16", 64, 8, 128), ("bf16", 32, 8, 128), ("f16", 8, 8, 128), ("bf16", 16, 1, 64),
     ("f16", 32, 2, 64), ("f32", 4, 2, 64), ("bf16", 6, 2, 128),
+    # more than 16 query heads per KV head: 2 or 4 tiles of 16, the last one partial
+    ("bf16", 32, 1, 128), ("f16", 48, 2, 64), ("bf16", 64, 1, 128), ("f16", 40, 1, 64),
 ])
 def test_edge_lengths_and_splits(dtype, hq, hkv, d):
     from tests import gpu_util as gu

@@ -107,7 +107,8 @@ def test_fp8_append_matches_oracle(sdt, n_new):
 
 
 @pytest.mark.parametrize("qdt,hq,hkv,d", [("bf16", 64, 8, 128), ("f16", 32, 8, 128),
-                                          ("bf16", 8, 8, 128), ("bf16", 16, 2, 64)])
+                                          ("bf16", 8, 8, 128), ("bf16", 16, 2, 64),
+                                          ("bf16", 64, 2, 128), ("f16", 64, 1, 64)])
 def test_fp8_decode_matches_oracle(qdt, hq, hkv, d):
     import torch
     from oracle import attention as o_att

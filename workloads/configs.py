@@ -68,8 +68,13 @@ MISTRAL_WINDOW = Config(
     "blocks only",
     1006, 32, 32, 32, 8, 128, "bf16", extra=dict(length=32768, window=4096))
 
+MQA_64 = Config(
+    "mqa-64-heads", "multi-query decode: 8 layers, Hq=64 Hkv=1 d=128 bf16, B=128 x 8192 tokens, "
+    "shuffled tables (64 query heads share each KV head)",
+    1007, 8, 128, 64, 1, 128, "bf16", extra=dict(length=8192, num_blocks=65536))
+
 CONFIGS = {c.name: c for c in (TINY, LLAMA8B_1LAYER, LLAMA70B_80LAYER, INJECT_TOP8, RAGGED_MHA,
-                                MISTRAL_WINDOW)}
+                                MISTRAL_WINDOW, MQA_64)}
 
 
 def get_config(name: str) -> Config:
