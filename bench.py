@@ -410,25 +410,42 @@ def run_request_path(cfg, st, pool, src, runs, dcos, dsin, max_pos, inject_ws, r
     pkv.pkv_decode_plan_destroy(probe)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
 
-    def batch():
+    host = {}
+
+    def timed(key, fn, *a):
+        t0 = time.perf_counter()
+        r = fn(*a)
+        host[key] = host.get(key, 0.0) + (time.perf_counter() - t0) * 1e3
+        return r
+
+    def reserve():
         c = pkv.pkv_cache_create(st["num_blocks"], B, st["max_blocks"], st["free_list_seed"])
         for b, m in enumerate(st["mem_lens"]):
             pkv.pkv_alloc_blocks(c, b, int(m))
+        return c
+
+    def tables_for(c, n_new):
+        first = pkv.pkv_extend(c, seqs, n_new)
+        table, lens = pkv.pkv_block_table(c, seqs, st["max_blocks"])
+        return first, table, lens
+
+    def batch():
+        host.clear()
+        c = timed("reserve", reserve)
         ev[0].record()
-        pkv.pkv_inject(c, pool, src, runs, 0, L, "pairs", dcos, dsin, max_pos, inject_ws)
+        timed("inject_call", pkv.pkv_inject, c, pool, src, runs, 0, L, "pairs", dcos, dsin,
+              max_pos, inject_ws)
         ev[1].record()
-        first = pkv.pkv_extend(c, seqs, suffix)
-        table, _ = pkv.pkv_block_table(c, seqs, st["max_blocks"])
+        first, table, _ = timed("extend_and_tables", tables_for, c, suffix)
         tdev.copy_(torch.from_numpy(table))
         fdev.copy_(torch.from_numpy(first.astype(np.int32)))
         for layer in range(L):
             pkv.pkv_append_kv(pool, layer, tdev, fdev, suffix, suf_k[layer], suf_v[layer],
                               "pairs", dcos, dsin, max_pos)
         ev[2].record()
-        pkv.pkv_extend(c, seqs, 1)
-        table, lens = pkv.pkv_block_table(c, seqs, st["max_blocks"])
+        _, table, lens = timed("extend_and_tables", tables_for, c, 1)
         tdev.copy_(torch.from_numpy(table))
-        plan = pkv.pkv_decode_plan_create(lens, HQ, H, d, 0)
+        plan = timed("decode_plan", pkv.pkv_decode_plan_create, lens, HQ, H, d, 0)
         pkv.pkv_decode_plan_upload(plan, dws)
         for layer in range(L):
             pkv.pkv_append_decode_attention(plan, pool, layer, q, tdev, tok_k[layer], tok_v[layer],
@@ -440,7 +457,7 @@ def run_request_path(cfg, st, pool, src, runs, dcos, dsin, max_pos, inject_ws, r
     torch.cuda.synchronize()
     pkv.pkv_decode_plan_destroy(plan)
     pkv.pkv_cache_destroy(c)
-    wall, phases = [], []
+    wall, phases, hosts = [], [], []
     for _ in range(reps):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -448,6 +465,7 @@ def run_request_path(cfg, st, pool, src, runs, dcos, dsin, max_pos, inject_ws, r
         torch.cuda.synchronize()
         wall.append((time.perf_counter() - t0) * 1e3)
         phases.append([ev[i].elapsed_time(ev[i + 1]) for i in range(3)])
+        hosts.append(dict(host))
         pkv.pkv_decode_plan_destroy(plan)
         pkv.pkv_cache_destroy(c)
     ms = float(np.median(wall))
@@ -456,9 +474,11 @@ def run_request_path(cfg, st, pool, src, runs, dcos, dsin, max_pos, inject_ws, r
     res = dict(ms_per_batch=ms, requests=B, layers=L, injected_tokens=n_tok,
                requests_per_s=B / (ms * 1e-3), injected_tokens_per_s=n_tok / (ms * 1e-3),
                gpu_ms_inject=float(ph[0]), gpu_ms_suffix_append=float(ph[1]),
-               gpu_ms_decode_step=float(ph[2]))
+               gpu_ms_decode_step=float(ph[2]),
+               host_ms={k: float(np.median([h[k] for h in hosts])) for k in hosts[0]})
     log("request path: %.3f ms per batch of %d requests (inject %.3f, suffix append %.3f, "
-        "decode step %.3f ms on the GPU)" % (ms, B, ph[0], ph[1], ph[2]))
+        "decode step %.3f ms on the GPU; host %s)" % (ms, B, ph[0], ph[1], ph[2],
+                                                      res["host_ms"]))
     del suf_k, suf_v, tok_k, tok_v, q, out, lse, tdev, fdev, dws
     return res
 
@@ -765,7 +785,12 @@ def main():
             "injected_tokens_per_s": round(rp["injected_tokens_per_s"], 1),
             "gpu_ms": {"inject": round(rp["gpu_ms_inject"], 3),
                        "suffix_append": round(rp["gpu_ms_suffix_append"], 3),
-                       "decode_step": round(rp["gpu_ms_decode_step"], 3)}}
+                       "decode_step": round(rp["gpu_ms_decode_step"], 3)},
+            "host_ms": {k: round(v, 3) for k, v in rp["host_ms"].items()},
+            "host_ms_meaning": "reserve: cache create + 64 block reservations; inject_call: "
+                               "the inject call (host planning, descriptor upload, launch); "
+                               "extend_and_tables: two extends with table exports; "
+                               "decode_plan: planning the decode step"}
     if inj_host is not None:
         line["inject_host_store"] = {
             "workload": "top-8 of 250 chunks (64..256 tokens) + prefix, 16 requests, 32 layers x "
