@@ -470,8 +470,10 @@ pkv_status pkv_append_decode_attention(const pkv_plan* plan, const pkv_pool* poo
  * pkv_kernel_timing(1) makes every following decode launch on the calling
  * thread (pkv_decode_attention, pkv_append_decode_attention; the attention
  * kernel, not a split sequence's merge kernel) carry a start/stop event pair
- * attached to its own dispatch, so that the pair spans exactly the kernel's
- * execution; pkv_kernel_timing(0) stops that.  pkv_kernel_times waits for
+ * attached to its own dispatch, so that the pair spans that dispatch and the
+ * kernel's execution, not the neighbouring work on the stream (on MI355X
+ * about 4 us more than the kernel's own start and end timestamps);
+ * pkv_kernel_timing(0) stops that.  pkv_kernel_times waits for
  * the recorded launches, writes up to max_n durations in milliseconds
  * (host float array) in launch order, releases every recorded pair and
  * returns the number recorded (PKV_E_INVALID for a bad buffer, PKV_E_HIP if

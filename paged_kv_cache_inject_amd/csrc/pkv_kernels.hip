@@ -124,7 +124,6 @@ template <> struct Fmt<PKV_FP8E4M3> {
 
 // 16-byte global access helpers.
 __device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ inline void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // Streaming (non-temporal) loads for data read exactly once: the cached K/V
 // of a decode step.  The hint keeps them from displacing reusable lines.
@@ -211,69 +210,6 @@ __device__ inline void store_packed(void* dst, const Packed<PDT, N>& pk) {
   static_assert(B == 16 || B == 8, "16- or 8-byte pieces");
   if constexpr (B == 16) st16_stream(dst, *reinterpret_cast<const uint4*>(pk.v));
   else st8_stream(dst, *reinterpret_cast<const uint2*>(pk.v));
-}
-
-// Rotate the X elements of one 16-byte chunk.  PAIRS: element e pairs with
-// e^1 inside the chunk (pair index = (first_dim + e) / 2).  HALVES: element e
-// of chunk `a` (first half) pairs with element e of chunk `b` (second half),
-// pair index first_dim + e.  y0 = x0*c - x1*s, y1 = x0*s + x1*c in float32.
-template <int DT>
-__device__ inline void rotate_pairs(uint4& chunk, int first_dim, const float* cos_row,
-                                    const float* sin_row) {
-  typedef typename Fmt<DT>::T T;
-  constexpr int X = 16 / Fmt<DT>::kBytes;
-  T v[X];
-  *reinterpret_cast<uint4*>(v) = chunk;
-#pragma unroll
-  for (int e = 0; e < X; e += 2) {
-    const int i = (first_dim + e) >> 1;
-    const float c = cos_row[i], s = sin_row[i];
-    const float x0 = Fmt<DT>::to_f32(v[e]), x1 = Fmt<DT>::to_f32(v[e + 1]);
-    const float y0 = x0 * c - x1 * s;
-    const float y1 = x0 * s + x1 * c;
-    v[e] = Fmt<DT>::from_f32(y0);
-    v[e + 1] = Fmt<DT>::from_f32(y1);
-  }
-  chunk = *reinterpret_cast<uint4*>(v);
-}
-
-template <int DT>
-__device__ inline void rotate_halves(uint4& a, uint4& b, int first_dim, const float* cos_row,
-                                     const float* sin_row) {
-  typedef typename Fmt<DT>::T T;
-  constexpr int X = 16 / Fmt<DT>::kBytes;
-  T va[X], vb[X];
-  *reinterpret_cast<uint4*>(va) = a;
-  *reinterpret_cast<uint4*>(vb) = b;
-#pragma unroll
-  for (int e = 0; e < X; ++e) {
-    const int i = first_dim + e;
-    const float c = cos_row[i], s = sin_row[i];
-    const float x0 = Fmt<DT>::to_f32(va[e]), x1 = Fmt<DT>::to_f32(vb[e]);
-    const float y0 = x0 * c - x1 * s;
-    const float y1 = x0 * s + x1 * c;
-    va[e] = Fmt<DT>::from_f32(y0);
-    vb[e] = Fmt<DT>::from_f32(y1);
-  }
-  a = *reinterpret_cast<uint4*>(va);
-  b = *reinterpret_cast<uint4*>(vb);
-}
-
-// Rotates the chunk pair (c0, c0 + C/2) of one token at position pos.
-template <int DT, int D>
-__device__ inline void rotate_chunk_pair(uint4& lo, uint4& hi, int c0, int pos, int mode,
-                                         const float* cos_t, const float* sin_t) {
-  constexpr int X = 16 / Fmt<DT>::kBytes;
-  constexpr int C = D / X;
-  if (mode == PKV_ROPE_NONE) return;
-  const float* cr = cos_t + size_t(pos) * (D / 2);
-  const float* sr = sin_t + size_t(pos) * (D / 2);
-  if (mode == PKV_ROPE_PAIRS) {
-    rotate_pairs<DT>(lo, c0 * X, cr, sr);
-    rotate_pairs<DT>(hi, (c0 + C / 2) * X, cr, sr);
-  } else {
-    rotate_halves<DT>(lo, hi, c0 * X, cr, sr);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -585,8 +521,9 @@ __device__ inline NewSlot new_slot(const DecodeParams& p, const DecodeItem& it, 
   // (the host has checked that the position has a rotary row; the clamp
   // only keeps the address in range)
   const int rpos = min(pos, max(p.max_pos - 1, 0));
-  ns.cr = p.cos_t + size_t(rpos) * (D / 2);
-  ns.sr = p.sin_t + size_t(rpos) * (D / 2);
+  const bool rot = p.rope_mode != PKV_ROPE_NONE;  // the tables may be null otherwise
+  ns.cr = rot ? p.cos_t + size_t(rpos) * (D / 2) : nullptr;
+  ns.sr = rot ? p.sin_t + size_t(rpos) * (D / 2) : nullptr;
   ns.ksc = PDT == PKV_FP8E4M3 ? p.k_scale[g] : 1.f;
   ns.vsc = PDT == PKV_FP8E4M3 ? p.v_scale[g] : 1.f;
   ns.ok = p.rope_mode == PKV_ROPE_NONE || pos < p.max_pos;
@@ -1360,7 +1297,8 @@ hipError_t launch(K kernel, dim3 grid, dim3 block, hipStream_t stream, const P& 
 
 // Kernel timing for measurement (this thread's decode launches): when on,
 // each launch carries a start/stop event pair attached to its own dispatch,
-// so the pair spans exactly the kernel's execution.
+// so the pair spans the dispatch and the kernel's execution (a few
+// microseconds more than a profiler's kernel timestamps).
 struct KernelTiming {
   bool on = false;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pairs;
