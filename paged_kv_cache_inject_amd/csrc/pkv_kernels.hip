@@ -40,6 +40,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -151,6 +152,29 @@ __device__ inline void st4_stream(void* p, uint32_t v) {
 }
 __device__ inline uint32_t ld4_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+// A 16x16 MFMA result holds each column in lanes c, c + 16, c + 32 and
+// c + 48.  These combine a value over those four lanes, leaving the result in
+// all four, with CDNA4's lane swaps between 16-lane rows and 32-lane halves
+// (register to register: no LDS traffic and no wait on it).  Each step adds
+// or compares the same two values in every lane of a pair, so all four lanes
+// get bit-identical results.
+__device__ inline float cols_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float cols_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // The X elements of a 16-byte chunk as float32.
@@ -784,8 +808,13 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
   bool okbuf[DEPTH];
 
   int put_blk = -1;  // block id read for the newest token's block
+  // Block ids are read one issue ahead (issues come in order j = 0, 1, ...),
+  // so the scalar load's latency does not sit between a block's arrival and
+  // the next block's loads.
+  int blk_next = nj > 0 ? tab[wave] : 0;
   auto issue = [&](int j, int d) {
-    int blk = tab[wave + j * NW];
+    int blk = blk_next;
+    if (j + 1 < nj) blk_next = tab[wave + (j + 1) * NW];
     if (j == put_j) put_blk = blk;
     const bool ok = unsigned(blk) < unsigned(p.num_blocks);
     okbuf[d] = ok;
@@ -802,11 +831,11 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
   };
 
   NewSlot ns{};
-  uint4 knew[SL];     // lanes with row == slot: the token's K chunks 4s + grp
-  uint32_t vnew[NT];  // lanes with grp == slot / 4: its V dims 16n + row (pool bits)
   // The token's K and V rows in the pool format, made by the whole wave
   // (lane i < D/2 rotates pair i; lanes take V dims lane, lane + 64) and
-  // read back by the lanes that hold them.
+  // read back, when the wave takes the token's block, by the lanes that hold
+  // the slot (K chunks 4s + grp in lanes with row == slot, V dims 16n + row
+  // in lanes with grp == slot / 4): kept in LDS meanwhile, not in registers.
   typedef typename Fmt<KVDT>::T TP;
   __shared__ __align__(16) TP new_row[2][D];
   auto make_new = [&](auto mode_tag) {
@@ -838,11 +867,6 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int s = 0; s < SL; ++s)
-      knew[s] = *reinterpret_cast<const uint4*>(&new_row[0][(4 * s + grp) * (16 / sizeof(TP))]);
-#pragma unroll
-    for (int n = 0; n < NT; ++n) vnew[n] = uint32_t(new_row[1][16 * n + row]);
   };
 
 #pragma unroll
@@ -865,18 +889,21 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
           // the newest token's slot: the values made above, not the pool's
           if (row == ns.tin) {
 #pragma unroll
-            for (int s = 0; s < SL; ++s) kbuf[d][s] = knew[s];
+            for (int s = 0; s < SL; ++s)
+              kbuf[d][s] = *reinterpret_cast<const uint4*>(
+                  &new_row[0][(4 * s + grp) * (16 / sizeof(TP))]);
           }
           if (grp == ns.tin / 4) {
             const int e = ns.tin & 3;  // token 4 grp + e of the lane's V registers
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
+              const uint32_t vnew = uint32_t(new_row[1][16 * n + row]);
               if constexpr (FP8) {
                 const uint32_t mask = 0xFFu << (8 * e);
-                vbuf[d][n].x = (vbuf[d][n].x & ~mask) | (vnew[n] << (8 * e));
+                vbuf[d][n].x = (vbuf[d][n].x & ~mask) | (vnew << (8 * e));
               } else {
                 const uint32_t mask = 0xFFFFu << (16 * (e & 1));
-                const uint32_t bits = vnew[n] << (16 * (e & 1));
+                const uint32_t bits = vnew << (16 * (e & 1));
                 uint32_t x = vbuf[d][n].x, y = vbuf[d][n].y;
                 if (e < 2) x = (x & ~mask) | bits;
                 else y = (y & ~mask) | bits;
@@ -935,10 +962,18 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
         // Slots of this block before a sliding window's start (positive only
         // in the window's first block).
         const int skip = it.lo - (it.t_begin + (wave + j * NW) * kBlock);
-        if (valid < kBlock || skip > 0 || !blk_ok) {
-          // Slots outside [lo, end) (or of a rejected block id) may hold
-          // anything, NaN included: zero their V so that 0-weight * V stays 0.
-          // Lane holds tokens 4*grp + e, e = 0..3, as 16-bit halves of x, y.
+        // Scaled scores; slots outside [lo, end) or of a rejected block id
+        // get -inf.  A whole block (the common case; wave-uniform) needs no
+        // masks, and the masked case rewrites the values in place.
+        float s4[NG][4];
+#pragma unroll
+        for (int t = 0; t < NG; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s4[t][r] = sc[t][r] * score_mul;
+        if (!(blk_ok && valid >= kBlock && skip <= 0)) {
+          // The masked slots may hold anything, NaN included: zero their V
+          // so that 0-weight * V stays 0.  Lane holds tokens 4*grp + e,
+          // e = 0..3, as 16-bit halves of x, y.
           const int lim = blk_ok ? valid : 0;
           auto in = [&](int e) { return e < lim && e >= skip; };
           const uint32_t mx0 = (in(4 * grp + 0) ? 0x0000ffffu : 0u) |
@@ -950,28 +985,25 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
             vcur[n].x &= mx0;
             vcur[n].y &= mx1;
           }
-        }
-        bool live[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          live[r] = blk_ok && (4 * grp + r) < valid && (4 * grp + r) >= skip;
+          for (int t = 0; t < NG; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (!in(4 * grp + r)) s4[t][r] = -INFINITY;
+        }
 #pragma unroll
         for (int t = 0; t < NG; ++t) {
-          float s4[4];
           float mx = -INFINITY;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            s4[r] = live[r] ? sc[t][r] * score_mul : -INFINITY;
-            mx = fmaxf(mx, s4[r]);
-          }
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s4[t][r]);
+          mx = cols_max(mx);
           // Rescale the running state only when some head's maximum grows (a
           // wave-uniform test): otherwise the factor would be exactly 1, and
           // after the first blocks of a long range it rarely grows.
           const bool grow = mx > m[t];  // false while both are -inf
           if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            const float alpha = grow ? exp2f(m[t] - mx) : 1.f;  // 0 when m was -inf
+            // 0 when m was -inf
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m[t] - mx) : 1.f;
             l[t] *= alpha;
 #pragma unroll
             for (int n = 0; n < NT; ++n) acc[t][n] *= alpha;
@@ -980,10 +1012,13 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
           // m is -inf only while every score seen so far is masked; then every
           // s4 is -inf too and its weight must be 0.
           const float m_ref = m[t] == -INFINITY ? 0.f : m[t];
+          // The hardware 2^x (about one ulp over the normal range): the
+          // arguments are <= 0, and weights below 2^-126, which it may flush
+          // to 0, are far below one ulp of the sum (at least 1).
           float pr[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            pr[r] = exp2f(s4[r] - m_ref);
+            pr[r] = __builtin_amdgcn_exp2f(s4[t][r] - m_ref);
             l[t] += pr[r];
           }
           uint16_t ph[4], pl[4];
@@ -1005,8 +1040,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
 
 #pragma unroll
   for (int t = 0; t < NG; ++t) {
-    l[t] += __shfl_xor(l[t], 16);
-    l[t] += __shfl_xor(l[t], 32);
+    l[t] = cols_sum(l[t]);
   }
 
   if constexpr (NW > 1) {
