@@ -3,9 +3,10 @@
 One step = one decode pass over all 80 layers of the Llama-3-70B-shaped
 workload (batch 32 x 8,192 tokens, 64 query / 8 KV heads of 128, bf16, 16-token
 blocks under a shuffled table): the per-step split plan is uploaded, then
-paged decode attention runs layer after layer.  The reported value is the
-whole step's algorithmic HBM bytes (every cached K/V byte, q, out, lse and the
-block-table entries) divided by its time, in GB/s.
+each layer runs as one launch that appends the step's token at position
+len - 1 (RoPE there) and attends over the layer's cache.  The reported value
+is the whole step's algorithmic HBM bytes (every cached K/V byte, q, out, lse,
+the block-table entries and the appended token) divided by its time, in GB/s.
 
 The injection workload runs after it: top-8 memory chunks of 64..256 tokens
 from a 10,000-chunk store of unrotated bf16 K/V (32 layers x 8 KV heads x 128)
@@ -36,19 +37,21 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def recorded_traffic(kernel="decode_mfma_kernel"):
-    """HBM bytes per launch of `kernel` from the rocprofv3 counter summary in
-    profiles/, if it was taken on the current kernel sources (else None)."""
+def recorded_traffic(kernel="decode_mfma_kernel", workload="70b", root=ROOT):
+    """HBM bytes per launch of `kernel` on decode workload `workload` from the
+    rocprofv3 counter summaries in profiles/, if one was taken on that
+    workload with the current kernel sources (else None)."""
     import glob
     import hashlib
-    src = os.path.join(ROOT, "paged_kv_cache_inject_amd", "csrc", "pkv_kernels.hip")
+    src = os.path.join(root, "paged_kv_cache_inject_amd", "csrc", "pkv_kernels.hip")
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+    for path in sorted(glob.glob(os.path.join(root, "profiles", "*.md"))):
         for line in open(path):
             if not line.startswith("traffic-record:"):
                 continue
             fields = dict(kv.split("=", 1) for kv in line.split()[1:])
-            if fields.get("kernel") == kernel and fields.get("sources_sha256") == sha:
+            if (fields.get("kernel") == kernel and fields.get("workload") == workload
+                    and fields.get("sources_sha256") == sha):
                 return int(fields["bytes_per_launch"])
     return None
 
@@ -732,7 +735,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(dec["launch_gbps"], 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(dec["launch_gbps"] / PEAK_HBM_GBPS, 4),
-                     "traffic": recorded_traffic(),
+                     "traffic": recorded_traffic(workload=args.decode_workload),
                      "kernel": "decode_mfma_kernel (pkv_append_decode_attention, one layer)",
                      "bytes_per_launch": dec["bytes_per_launch"],
                      "launch_us_avg": round(dec["launch_ms_avg"] * 1e3, 2),
