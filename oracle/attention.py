@@ -23,7 +23,11 @@ Readings taken:
   attends to positions max(0, n - W) .. n-1 only;
 * besides ``out`` the log-sum-exp ``lse = m + ln(sum exp(s - m))`` of the
   scaled scores is returned; a sequence of length 0 gives out = 0 and
-  lse = -inf.
+  lse = -inf;
+* (a reading about malformed input, not from the pages) a block-table entry
+  outside [0, num_blocks) inside a sequence's length names no block: its
+  positions are left out of the softmax, as if absent, and a sequence left
+  with no position gives out = 0 and lse = -inf.
 
 The split-K merge (partial softmax states over disjoint token ranges combined
 by their log-sum-exp) is stated in ``lse_merge``; the tests check it equals
@@ -34,7 +38,7 @@ import math
 
 import numpy as np
 
-from .layout import PoolSpec, gather_sequence, gather_sequence_planes
+from .layout import PoolSpec, block_in_range, gather_sequence, gather_sequence_planes
 from .numerics import to_f64
 
 
@@ -76,13 +80,16 @@ def decode_contiguous(q, k_seqs, v_seqs, dtype: str, n_q_heads: int, scale=None)
 
 def decode_paged(q, k_pool, v_pool, spec: PoolSpec, layer: int, tables, lens,
                  n_q_heads: int, scale=None, seqs=None, heads=None, by_plane=False,
-                 q_dtype=None, k_scale=None, v_scale=None, window=None):
+                 q_dtype=None, k_scale=None, v_scale=None, window=None, num_blocks=None):
     """Decode attention reading K/V through the block tables.
 
     ``seqs`` / ``heads`` restrict which (sequence, query head) outputs are
     computed (sampling at large sizes); the rest stay 0 / -inf.  ``by_plane``
     gathers a whole plane at a time (same values, faster).  ``window`` (a
     positive int) limits each query to the last ``window`` positions.
+    ``num_blocks``, when given, makes positions whose table entry is outside
+    [0, num_blocks) drop out of the attention (the tables may then hold such
+    entries; without it every entry inside a length must name a block).
     """
     q64 = to_f64(q, spec.dtype if q_dtype is None else q_dtype)
     b_n, hq, d = q64.shape
@@ -96,8 +103,14 @@ def decode_paged(q, k_pool, v_pool, spec: PoolSpec, layer: int, tables, lens,
         kv_heads = sorted({h // g for h in qh})
         gather = gather_sequence_planes if by_plane else gather_sequence
         start = max(0, int(lens[b]) - int(window)) if window else 0
-        k_raw, v_raw = gather(k_pool, v_pool, spec, layer, tables[b], int(lens[b]), heads=kv_heads,
-                              start=start)
+        if num_blocks is None:
+            k_raw, v_raw = gather(k_pool, v_pool, spec, layer, tables[b], int(lens[b]),
+                                  heads=kv_heads, start=start)
+        else:
+            kept = [p for p in range(start, int(lens[b]))
+                    if block_in_range(tables[b], p, num_blocks)]
+            k_raw, v_raw = gather_sequence(k_pool, v_pool, spec, layer, tables[b], int(lens[b]),
+                                           heads=kv_heads, positions=kept)
         k64 = to_f64(k_raw, spec.dtype)
         v64 = to_f64(v_raw, spec.dtype)
         if spec.dtype == "fp8":
@@ -107,7 +120,7 @@ def decode_paged(q, k_pool, v_pool, spec: PoolSpec, layer: int, tables, lens,
             v64 = v64 * vs[None, :, None]
         for h in qh:
             i = kv_heads.index(h // g)
-            if lens[b] == 0:
+            if lens[b] == 0 or k64.shape[0] == 0:
                 continue
             out[b, h], lse[b, h] = softmax_attend(q64[b, h], k64[:, i, :], v64[:, i, :], sc)
     return out, lse

@@ -32,7 +32,8 @@ contiguous.
 
 import numpy as np
 
-from .layout import BLOCK_TOKENS, PoolSpec, k_element_offsets, v_element_offsets, slot
+from .layout import (BLOCK_TOKENS, PoolSpec, block_in_range, k_element_offsets, v_element_offsets,
+                     slot)
 from .numerics import from_f32, to_f32, f32_to_e4m3_rne_sat
 from .rope import rotate_f32
 
@@ -122,14 +123,20 @@ def inject(k_pool, v_pool, spec: PoolSpec, tables, lens, runs, src_k, src_v,
 
 
 def append(k_pool, v_pool, spec: PoolSpec, layer: int, tables, lens_after, seqs, n_new: int,
-           k_new, v_new, mode: str, cos_t, sin_t, src_dtype=None, k_scale=None, v_scale=None):
+           k_new, v_new, mode: str, cos_t, sin_t, src_dtype=None, k_scale=None, v_scale=None,
+           num_blocks=None):
     """Write n_new tokens per sequence at its last n_new positions.
 
-    k_new, v_new: raw arrays [len(seqs)][n_new][n_kv_heads][d].
+    k_new, v_new: raw arrays [len(seqs)][n_new][n_kv_heads][d].  With
+    ``num_blocks`` given, a token whose table entry is outside
+    [0, num_blocks) is not written (the tables live on the device there and
+    are not trusted).
     """
     for i, seq in enumerate(seqs):
         first = lens_after[seq] - n_new
         for t in range(n_new):
+            if num_blocks is not None and not block_in_range(tables[seq], first + t, num_blocks):
+                continue
             write_token(k_pool, v_pool, spec, layer, tables[seq], first + t,
                         k_new[i, t], v_new[i, t], mode, cos_t, sin_t, src_dtype, k_scale,
                         v_scale)

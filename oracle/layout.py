@@ -113,20 +113,30 @@ def read_token(k_pool, v_pool, spec: PoolSpec, layer: int, block: int, t: int):
     return k, v
 
 
+def block_in_range(table_row, p: int, num_blocks: int) -> bool:
+    """Whether logical position ``p``'s table entry names a block of the pool
+    (0 <= id < num_blocks).  Index data that lives on the device is not
+    trusted: a position whose entry is out of range is never read or written
+    (its element is skipped)."""
+    b = int(table_row[p // BLOCK_TOKENS])
+    return 0 <= b < num_blocks
+
+
 def gather_sequence(k_pool, v_pool, spec: PoolSpec, layer: int, table_row, length: int,
-                    heads=None, start: int = 0):
+                    heads=None, start: int = 0, positions=None):
     """Raw K, V of positions start..length-1 of one sequence:
-    [length - start][H][d] each.
+    [length - start][H][d] each (or of the listed ``positions``, in order).
 
     Walks the block table one position at a time (the definition of paged
     reading); ``heads`` restricts the KV heads returned.
     """
     heads = list(range(spec.n_kv_heads)) if heads is None else list(heads)
     sdt = spec.storage_dtype()
-    n = max(0, length - start)
+    positions = list(range(start, length)) if positions is None else list(positions)
+    n = len(positions)
     k = np.empty((n, len(heads), spec.head_dim), dtype=sdt)
     v = np.empty((n, len(heads), spec.head_dim), dtype=sdt)
-    for i_p, p in enumerate(range(start, length)):
+    for i_p, p in enumerate(positions):
         s = slot(table_row, p)
         blk, t = divmod(s, BLOCK_TOKENS)
         for i, h in enumerate(heads):

@@ -125,6 +125,77 @@ def test_zero_length_sequence():
     assert np.all(out == 0) and np.all(np.isneginf(lse))
 
 
+def test_out_of_range_block_ids_drop_out_of_attention():
+    """Positions whose table entry names no block (negative, or >= num_blocks)
+    are left out: the result equals contiguous attention over the remaining
+    positions; a sequence with none left gives 0 / -inf."""
+    from oracle.layout import k_element_offsets, v_element_offsets
+    rng = np.random.default_rng(77)
+    nb_pool, hkv, hq, d = 16, 2, 4, 32
+    spec = PoolSpec(1, nb_pool, hkv, d, "bf16").resolved()
+    lens = [40, 33, 16, 20]
+    k_seq = [small_bf16_values(rng, (n, hkv, d)) for n in lens]
+    v_seq = [small_bf16_values(rng, (n, hkv, d)) for n in lens]
+    q = small_bf16_values(rng, (len(lens), hq, d))
+    kp, vp = empty_pool(spec)
+    tables, at = [], 0
+    for b, n in enumerate(lens):
+        nb = -(-n // 16)
+        tables.append(list(range(at, at + nb)) + [-1] * (3 - nb))
+        at += nb
+        for p in range(n):
+            blk, t = divmod(slot(tables[b], p), 16)
+            for h in range(hkv):
+                kp[k_element_offsets(spec, 0, blk, h, t)] = k_seq[b][p, h]
+                vp[v_element_offsets(spec, 0, blk, h, t)] = v_seq[b][p, h]
+    # seq 0: middle block gone; seq 1: last (partial) block names block 16 =
+    # num_blocks; seq 2: its only block is gone; seq 3: first block far out
+    tables[0][1] = -1
+    tables[1][2] = nb_pool
+    tables[2][0] = -(2 ** 31)
+    tables[3][0] = 10 ** 6
+    kept = [list(range(0, 16)) + list(range(32, 40)), list(range(0, 32)), [],
+            list(range(16, 20))]
+    ref, ref_lse = att.decode_contiguous(
+        q, [k_seq[b][kept[b]] for b in range(4)], [v_seq[b][kept[b]] for b in range(4)],
+        "bf16", hq)
+    out, lse = att.decode_paged(q, kp, vp, spec, 0, tables, lens, hq, num_blocks=nb_pool)
+    assert np.array_equal(out, ref) and np.array_equal(lse, ref_lse)
+    assert np.all(out[2] == 0) and np.all(np.isneginf(lse[2]))
+    # under a window the same positions drop out of the window's range
+    out_w, lse_w = att.decode_paged(q, kp, vp, spec, 0, tables, lens, hq, num_blocks=nb_pool,
+                                    window=20)
+    kept_w = [[p for p in kept[b] if p >= lens[b] - 20] for b in range(4)]
+    ref_w, ref_lse_w = att.decode_contiguous(
+        q, [k_seq[b][kept_w[b]] for b in range(4)], [v_seq[b][kept_w[b]] for b in range(4)],
+        "bf16", hq)
+    assert np.array_equal(out_w, ref_w) and np.array_equal(lse_w, ref_lse_w)
+
+
+def test_append_skips_out_of_range_block_ids():
+    """A token whose table entry names no block is not written; the others are."""
+    spec = PoolSpec(1, 6, 2, 64, "bf16").resolved()
+    cos_t, sin_t = rope_table(64, 10000.0, 64)
+    rng = np.random.default_rng(8)
+    k_new = small_bf16_values(rng, (3, 2, 2, 64))
+    v_new = small_bf16_values(rng, (3, 2, 2, 64))
+    good = [[4, 1, -1], [0, -1, -1], [2, 3, -1]]
+    lens_after = [18, 2, 17]          # seq 2's two tokens straddle blocks 2 and 3
+    bad = [list(r) for r in good]
+    bad[1][0] = 6                      # num_blocks: seq 1 writes nothing
+    bad[2][1] = -5                     # seq 2: only its token in block 2 is written
+    a_k, a_v = empty_pool(spec)
+    append(a_k, a_v, spec, 0, bad, lens_after, [0, 1, 2], 2, k_new, v_new, "pairs", cos_t,
+           sin_t, num_blocks=6)
+    r_k, r_v = empty_pool(spec)
+    append(r_k, r_v, spec, 0, good, lens_after, [0], 2, k_new[0:1], v_new[0:1], "pairs", cos_t,
+           sin_t)
+    # seq 2, token 0 only (position 15): as an append of one token at length 16
+    append(r_k, r_v, spec, 0, good, [0, 0, 16], [2], 1, k_new[2:3, 0:1], v_new[2:3, 0:1],
+           "pairs", cos_t, sin_t)
+    assert np.array_equal(a_k, r_k) and np.array_equal(a_v, r_v)
+
+
 # -- inject ------------------------------------------------------------------------------
 def test_inject_at_position_zero_is_a_bit_copy():
     spec = PoolSpec(1, 2, 2, 64, "bf16").resolved()
