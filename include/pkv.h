@@ -368,8 +368,13 @@ pkv_status pkv_inject(pkv_cache* cache, const pkv_pool* pool, const pkv_src* src
  *   K[slot] = round(R_p * k_new[b][t]),  V[slot] = v_new[b][t]
  * k_new, v_new: device, [n_seqs][n_new][n_kv_heads][head_dim] in new_dtype
  * (the pool's, or PKV_BF16 / PKV_F16 for an FP8E4M3 pool).
- * d_first_pos: device int32[n_seqs] (the first_pos_out of pkv_extend).
- * Rows of tokens at positions >= max_pos or beyond the table are skipped.
+ * d_first_pos: device int32[n_seqs] (the first_pos_out of pkv_extend), with
+ * d_first_pos[b] + n_new <= INT32_MAX.  The table and the first positions are
+ * device data and are range-checked: a token is skipped (not written) when
+ * its position is negative, lies past the table row (p / 16 >= table_stride),
+ * has no rotary row under a rotary pairing (p >= max_pos, rope_mode other
+ * than PKV_ROPE_NONE), or when its table entry is not a block id in
+ * [0, num_blocks).
  * ------------------------------------------------------------------------- */
 pkv_status pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* d_tables,
                          int32_t table_stride, const int32_t* d_first_pos, int32_t n_seqs,

@@ -128,14 +128,21 @@ def append(k_pool, v_pool, spec: PoolSpec, layer: int, tables, lens_after, seqs,
     """Write n_new tokens per sequence at its last n_new positions.
 
     k_new, v_new: raw arrays [len(seqs)][n_new][n_kv_heads][d].  With
-    ``num_blocks`` given, a token whose table entry is outside
-    [0, num_blocks) is not written (the tables live on the device there and
-    are not trusted).
+    ``num_blocks`` given, the tables and first positions are device data and
+    not trusted: a token is not written when its position is negative, past
+    the table row, under a rotary pairing at or past the rotary table
+    (max_pos = its row count), or when its table entry is outside
+    [0, num_blocks).
     """
+    max_pos = cos_t.shape[0]
     for i, seq in enumerate(seqs):
         first = lens_after[seq] - n_new
         for t in range(n_new):
-            if num_blocks is not None and not block_in_range(tables[seq], first + t, num_blocks):
+            p = first + t
+            if num_blocks is not None and (
+                    p < 0 or p // BLOCK_TOKENS >= len(tables[seq])
+                    or (mode != "none" and p >= max_pos)
+                    or not block_in_range(tables[seq], p, num_blocks)):
                 continue
             write_token(k_pool, v_pool, spec, layer, tables[seq], first + t,
                         k_new[i, t], v_new[i, t], mode, cos_t, sin_t, src_dtype, k_scale,

@@ -7,12 +7,14 @@ import pytest
 
 pytestmark = pytest.mark.gpu
 
-CANARY = {"f32": 0x7FC0DEAD, "bf16": 0x7FAB, "f16": 0x7DAB}
+CANARY = {"f32": 0x7FC0DEAD, "bf16": 0x7FAB, "f16": 0x7DAB, "fp8": 0x5A}
 
 
 def canary_buffer(dp, dtype):
     if dtype == "f32":
         return np.full(dp.total, np.uint32(CANARY[dtype]).view(np.float32), dtype=np.float32)
+    if dtype == "fp8":
+        return np.full(dp.total, CANARY[dtype], dtype=np.uint8)
     return np.full(dp.total, CANARY[dtype], dtype=np.uint16)
 
 
@@ -143,3 +145,61 @@ def test_append_matches_oracle(dtype, d, mode, n_new):
                         k_new, v_new, mode, o_cos, o_sin)
     torch.cuda.synchronize()
     gu.assert_bytes_equal(dp.host_copy(), ref, "pool after append")
+
+
+@pytest.mark.parametrize("dtype,mode", [("bf16", "pairs"), ("bf16", "none"), ("f16", "halves"),
+                                        ("fp8", "pairs")])
+def test_append_skips_positions_the_device_data_does_not_cover(dtype, mode):
+    """First positions and tables on the device are range-checked: tokens at
+    negative positions, past the table row, past the rotary table (under a
+    rotary pairing) or in a block whose id is out of range are not written;
+    the other tokens of the same call are.  Pool byte-exact against the
+    oracle's append over the same device data."""
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    from oracle import inject as o_inject
+    from oracle.rope import rope_table
+    from tests import gpu_util as gu
+    from workloads.configs import host_normal
+
+    gu.say("append, out-of-range device data", dtype, mode)
+    rng = np.random.default_rng(404)
+    L, H, d, NB, W, max_pos, n_new = 2, 4, 128, 40, 4, 50, 8
+    dp = gu.DevicePool(L, NB, H, d, dtype, fill_bits=CANARY[dtype])
+    ks = vs = None
+    if dtype == "fp8":
+        ks = rng.uniform(0.01, 0.03, size=(L, H)).astype(np.float32)
+        vs = rng.uniform(0.01, 0.03, size=(L, H)).astype(np.float32)
+        dp.set_scales(ks, vs)
+    # each row: W = 4 blocks of 16 positions (64 positions), distinct blocks
+    ids = rng.permutation(NB)[:7 * W].astype(np.int32).reshape(7, W)
+    table = ids.copy()
+    table[5, 1] = NB + 3            # positions 16..31 of row 5 name no block
+    table[6, 0] = -1
+    # first positions: straddling 0; straddling max_pos; straddling the end of
+    # the row; far past it; straddling a bad entry; inside; inside a bad entry
+    first = np.array([-3, 46, 60, 2 ** 30, 12, 30, 4], dtype=np.int32)
+    src_dt = "bf16" if dtype == "fp8" else dtype
+    o_cos, o_sin = rope_table(d, 10000.0, max_pos)
+    _, _, dcos, dsin = gu.rope_tables(d, max_pos)
+    ref = canary_buffer(dp, dtype)
+    kp, vp = dp.oracle_arrays(ref)
+    tdev = torch.from_numpy(table).cuda()
+    fdev = torch.from_numpy(first).cuda()
+    rows = [list(r) for r in table]
+    lens_after = [int(f) + n_new for f in first]
+    for layer in range(L):
+        k_new = host_normal(rng, (7, n_new, H, d), src_dt)
+        v_new = host_normal(rng, (7, n_new, H, d), src_dt)
+        pkv.pkv_append_kv(dp.desc(), layer, tdev, fdev, n_new,
+                          gu.to_device_raw(k_new.reshape(-1), src_dt),
+                          gu.to_device_raw(v_new.reshape(-1), src_dt), mode, dcos, dsin, max_pos,
+                          new_dtype=src_dt)
+        o_inject.append(kp, vp, dp.spec(), layer, rows, lens_after, list(range(7)), n_new, k_new,
+                        v_new, mode, o_cos, o_sin, src_dtype=src_dt, k_scale=ks, v_scale=vs,
+                        num_blocks=NB)
+    torch.cuda.synchronize()
+    got = dp.host_copy()
+    gu.assert_bytes_equal(got, ref, "pool after append with out-of-range device data")
+    # something was written, and the canary survives where nothing may be
+    assert (got != canary_buffer(dp, dtype)).any()

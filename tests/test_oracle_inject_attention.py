@@ -196,6 +196,36 @@ def test_append_skips_out_of_range_block_ids():
     assert np.array_equal(a_k, r_k) and np.array_equal(a_v, r_v)
 
 
+def test_append_skips_positions_outside_the_row_and_the_rotary_table():
+    """With device-side tables (num_blocks given): tokens at negative
+    positions, past the table row or (rotating) at or past max_pos are not
+    written; the rest equal a plain append of just those tokens."""
+    spec = PoolSpec(1, 8, 1, 32, "bf16").resolved()
+    cos_t, sin_t = rope_table(32, 10000.0, 20)            # max_pos 20
+    rng = np.random.default_rng(12)
+    k_new = small_bf16_values(rng, (3, 4, 1, 32))
+    v_new = small_bf16_values(rng, (3, 4, 1, 32))
+    tables = [[3, 5], [1, 6], [2, 7]]                    # 32 positions per row
+    firsts = [-2, 18, 30]                                # 4 tokens each
+    for mode in ("pairs", "none"):
+        a_k, a_v = empty_pool(spec)
+        append(a_k, a_v, spec, 0, tables, [f + 4 for f in firsts], [0, 1, 2], 4, k_new, v_new,
+               mode, cos_t, sin_t, num_blocks=8)
+        r_k, r_v = empty_pool(spec)
+        # row 0: positions 0, 1 (tokens 2, 3)
+        append(r_k, r_v, spec, 0, tables, [2, 0, 0], [0], 2, k_new[0:1, 2:], v_new[0:1, 2:],
+               mode, cos_t, sin_t)
+        # row 1: 18, 19 rotating; 18..21 without rotation
+        n1 = 2 if mode == "pairs" else 4
+        append(r_k, r_v, spec, 0, tables, [0, 18 + n1, 0], [1], n1, k_new[1:2, :n1],
+               v_new[1:2, :n1], mode, cos_t, sin_t)
+        # row 2: 30, 31 without rotation (32, 33 are past the row); none rotating
+        if mode == "none":
+            append(r_k, r_v, spec, 0, tables, [0, 0, 32], [2], 2, k_new[2:3, :2], v_new[2:3, :2],
+                   mode, cos_t, sin_t)
+        assert np.array_equal(a_k, r_k) and np.array_equal(a_v, r_v), mode
+
+
 # -- inject ------------------------------------------------------------------------------
 def test_inject_at_position_zero_is_a_bit_copy():
     spec = PoolSpec(1, 2, 2, 64, "bf16").resolved()
