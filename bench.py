@@ -136,6 +136,48 @@ def append_bytes(n_seqs, n_kv_heads, head_dim, elem, kv_elem=None):
     return rows * 2 * (elem + kv_elem) + n_seqs * head_dim * 4 + n_seqs * 8
 
 
+def item_balance(lens, part_tokens, n_kv_heads, n_cus=256):
+    """Work items of a decode plan and how evenly they load the CUs.
+
+    Items are the plan's token ranges (a sequence longer than part_tokens is
+    split into ranges of that many tokens, the last shorter), launched
+    longest first, every KV head of an item in turn.  The load model: one
+    workgroup per CU at a time, time proportional to tokens, each workgroup
+    starting on the CU that frees first.  `lpt_makespan_over_mean` is the
+    model's finishing time over the perfectly even share (1.0 = balanced)."""
+    import heapq
+    items = []
+    for n in lens:
+        n = int(n)
+        t = 0
+        while t < n:
+            items.append(min(part_tokens, n - t))
+            t += part_tokens
+    items.sort(reverse=True)
+    free = [(0, c) for c in range(n_cus)]
+    heapq.heapify(free)
+    for x in items:
+        for _ in range(n_kv_heads):
+            t, c = heapq.heappop(free)
+            heapq.heappush(free, (t + x, c))
+    makespan = max(t for t, _ in free)
+    mean = sum(items) * n_kv_heads / n_cus
+    a = np.asarray(items)
+    edges = [0] + [1 << k for k in range(4, 16)] + [1 << 30]
+    hist = {}
+    for lo, hi in zip(edges[:-1], edges[1:]):
+        c = int(((a > lo) & (a <= hi)).sum())
+        if c:
+            hist["%d-%d" % (lo + 1, min(hi, int(a.max())))] = c
+    return {"items": len(items), "workgroups": len(items) * n_kv_heads,
+            "tokens_per_item_p0_p50_p90_p100": [int(a.min()), int(np.median(a)),
+                                                int(np.percentile(a, 90)), int(a.max())],
+            "tokens_per_item_histogram": hist,
+            "lpt_makespan_over_mean": round(makespan / mean, 4),
+            "model": "one workgroup per CU at a time, time proportional to tokens, "
+                     "longest first, %d CUs" % n_cus}
+
+
 def bw_probe(n_bytes=8 << 30, reps=5):
     import torch
     import paged_kv_cache_inject_amd as pkv
@@ -674,6 +716,8 @@ def main():
     ap.add_argument("--host-store-only", action="store_true",
                     help="time only the pinned-host-store inject (no JSON line)")
     ap.add_argument("--cow-reps", type=int, default=10)
+    ap.add_argument("--no-shapes", action="store_true",
+                    help="skip the 8B-shaped and ragged-MHA decode figures")
     ap.add_argument("--no-two-calls", action="store_true",
                     help="skip the comparison timing of the step as two launches per layer")
     ap.add_argument("--decode-workload", default="70b",
@@ -710,6 +754,12 @@ def main():
     inj = None if args.no_inject else run_inject(args.inject_reps)
     cow = None if args.no_cow else run_cow(args.cow_reps)
     inj_host = None if args.no_host_store else run_inject_host(max(2, args.inject_reps // 3))
+    shapes = {}
+    if not args.no_shapes and args.decode_workload == "70b":
+        # the other decode shapes (one layer each; also timed with the last-level
+        # cache flushed between steps)
+        for name in ("8b", "ragged"):
+            shapes[name] = run_decode(args.steps, args.warmup, name, two_calls=False)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     line = {
         "metric": "paged decode attention achieved HBM GB/s (% of peak) + injected tokens/s",
@@ -817,6 +867,27 @@ def main():
                        "us": round(cow["us_per_round"], 1), "gbps": round(cow["gbps"], 1),
                        "pct_of_peak": round(100 * cow["gbps"] / PEAK_HBM_GBPS, 2),
                        "kernel": "copy_blocks_kernel (pkv_copy_blocks)"}
+    for name, key in (("8b", "decode_8b"), ("ragged", "decode_ragged")):
+        if name not in shapes:
+            continue
+        r, st = shapes[name]
+        line[key] = {
+            "workload": r["workload"], "dtype": r["dtype"],
+            "ms_per_step": round(r["ms_per_step"], 4), "gbps": round(r["value"], 1),
+            "pct_of_peak": round(100 * r["value"] / PEAK_HBM_GBPS, 2),
+            "cold_ms_per_step": round(r["cold_ms_per_step"], 4),
+            "cold_gbps": round(r["cold_gbps"], 1),
+            "launch_us_p10_p50_p90": [round(r["event_ms_p10"] * 1e3, 2),
+                                      round(r["event_ms_p50"] * 1e3, 2),
+                                      round(r["event_ms_p90"] * 1e3, 2)],
+            "bytes_per_step": r["bytes_per_step"], "work_items": r["n_items"],
+            "part_tokens": r["part_tokens"], "waves_per_workgroup": r["waves"],
+            "seed": r["seed"], "tables_sha256": r["tables_sha256"],
+            "cold_meaning": "each step timed after writing a 1 GiB buffer, so the 256 MB "
+                            "last-level cache holds none of the layer"}
+        if name == "ragged":
+            line[key]["balance"] = item_balance(st["lens"], r["part_tokens"],
+                                                decode_workload(name)[0].n_kv_heads)
     print(json.dumps(line), flush=True)
 
 
