@@ -715,10 +715,13 @@ __device__ inline uint2 e4m3x4_to_f16x4(uint32_t w) {
 
 // Decode kernel template parameters: KVDT the pool format, QDT the query
 // format (equal to KVDT, or BF16/F16 for an fp8 pool whose MFMA operands are
-// float16), head dim D, prefetch depth, waves per workgroup NW, and NG tiles
-// of 16 query heads (a KV head's group of up to 16 NG query heads: every
-// block's K and V, loaded once, serve all NG tiles).
-template <int KVDT, int QDT, int D, int DEPTH, int NW, int NG>
+// float16), head dim D, prefetch depth, waves per workgroup NW, NG tiles of
+// 16 query heads (a KV head's group of up to 16 NG query heads: every
+// block's K and V, loaded once, serve all NG tiles), and PUT: whether the
+// kernel carries the decode step's append of the newest token (attention
+// alone runs an instance without that code, which it would otherwise pay for
+// in registers and scheduling even when no token is appended).
+template <int KVDT, int QDT, int D, int DEPTH, int NW, int NG, bool PUT>
 // `tables` is p.tables again as a restrict-qualified argument: the kernel's
 // only stores (the fused append) go to the pool, and with the table known
 // not to alias them its entries keep coming through scalar loads.
@@ -787,9 +790,11 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
   // block it puts them into its registers in place of the loaded ones and
   // writes the block's planes back.  Other waves: put_j = -1.
   int put_j = -1;
-  if (p.new_k != nullptr && it.last && it.n_tokens > 0) {
-    const int lb = (it.n_tokens - 1) / kBlock;
-    if (lb % NW == wave) put_j = lb / NW;
+  if constexpr (PUT) {
+    if (p.new_k != nullptr && it.last && it.n_tokens > 0) {
+      const int lb = (it.n_tokens - 1) / kBlock;
+      if (lb % NW == wave) put_j = lb / NW;
+    }
   }
 
   f32x4_t acc[NG][NT];
@@ -872,12 +877,14 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d)
     if (d < nj) issue(d, d);
-  if (put_j >= 0) {
-    ns = new_slot<QDT, KVDT, D>(p, it, g);
-    if (p.rope_mode == PKV_ROPE_PAIRS) make_new(RopeTag<PKV_ROPE_PAIRS>{});
-    else if (p.rope_mode == PKV_ROPE_HALVES) make_new(RopeTag<PKV_ROPE_HALVES>{});
-    else make_new(RopeTag<PKV_ROPE_NONE>{});
-    if (!ns.ok) put_j = -1;  // no write, and the block is read as stored
+  if constexpr (PUT) {
+    if (put_j >= 0) {
+      ns = new_slot<QDT, KVDT, D>(p, it, g);
+      if (p.rope_mode == PKV_ROPE_PAIRS) make_new(RopeTag<PKV_ROPE_PAIRS>{});
+      else if (p.rope_mode == PKV_ROPE_HALVES) make_new(RopeTag<PKV_ROPE_HALVES>{});
+      else make_new(RopeTag<PKV_ROPE_NONE>{});
+      if (!ns.ok) put_j = -1;  // no write, and the block is read as stored
+    }
   }
 
   for (int j0 = 0; j0 < nj; j0 += DEPTH) {
@@ -885,7 +892,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
     for (int d = 0; d < DEPTH; ++d) {
       const int j = j0 + d;
       if (j < nj) {
-        if (j == put_j) {
+        if (PUT && j == put_j) {
           // the newest token's slot: the values made above, not the pool's
           if (row == ns.tin) {
 #pragma unroll
@@ -1340,9 +1347,10 @@ struct KernelTiming {
 thread_local KernelTiming g_timing;
 
 template <typename K, typename... A>
-hipError_t launch_decode_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, A... args) {
+hipError_t launch_decode_kernel(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                                A... args) {
   if (!g_timing.on) {
-    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
     return hipGetLastError();
   }
   hipEvent_t a = nullptr, b = nullptr;
@@ -1352,10 +1360,55 @@ hipError_t launch_decode_kernel(K kernel, dim3 grid, dim3 block, hipStream_t str
     if (a) (void)hipEventDestroy(a);
     return e;
   }
-  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, a, b, 0, args...);
+  hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, a, b, 0, args...);
   e = hipGetLastError();
   g_timing.pairs.emplace_back(a, b);
   return e;
+}
+
+// Dynamic LDS that keeps kernel F at one workgroup per CU: enough that two
+// workgroups' LDS do not fit in one CU (160 KiB on gfx950).  The one-tile,
+// 8-wave decode kernel without the append code fits in 128 VGPRs, so two of
+// its workgroups could share a CU; when a launch has only a few workgroups
+// per CU, that pins pairs of workgroups together from the start instead of
+// handing each CU the next workgroup as it frees (the 8B-shaped layer, 512
+// workgroups, measured 8 % slower that way).  Computed once per kernel.
+template <auto F>
+size_t one_per_cu_lds() {
+  static const size_t pad = [] {
+    int dev = 0, per_cu = 0;
+    hipFuncAttributes fa{};
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                              dev) != hipSuccess ||
+        hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(F)) != hipSuccess) {
+      (void)hipGetLastError();
+      return size_t(0);
+    }
+    const size_t half = size_t(per_cu) / 2 + 1;
+    return fa.sharedSizeBytes < half ? half - fa.sharedSizeBytes : size_t(0);
+  }();
+  return pad;
+}
+
+// CUs of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0) {
+      (void)hipGetLastError();
+      v = 256;
+    }
+    cus[dev] = v;
+  }
+  return cus[dev];
 }
 
 }  // namespace
@@ -1518,19 +1571,35 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
     const int ng = p.group <= 16 ? 1 : p.group <= 32 ? 2 : p.group <= 64 ? 4 : 0;
     const bool mfma = (kernel_variant != 1 || pool.dtype == PKV_FP8E4M3) &&
                       pool.dtype != PKV_F32 && ng > 0;
-    // One block in flight per wave measured fastest with 8 waves per workgroup.
-    const int depth = kernel_variant == 12 ? 2 : 1;
+    // The decode step's append (new token rows given) runs the PUT instance.
+    const bool put = a.new_k != nullptr;
+    // One block in flight per wave measured fastest with 8 waves per workgroup
+    // (depth 2 is instantiated for attention alone only).
+    const int depth = kernel_variant == 12 && !put ? 2 : 1;
     // More tiles hold more accumulators: 2 tiles fit 8 waves per workgroup
     // (two per SIMD), 4 tiles one wave per SIMD.
     int nw = a.waves;
     if (ng == 2) nw = nw >= 8 ? 8 : 4;
     if (ng == 4) nw = 4;
+    // 8-wave launches with fewer than 16 workgroups per CU run one workgroup
+    // per CU (see one_per_cu_lds); many-workgroup launches (ragged batches)
+    // may run two, which hides each workgroup's start-up behind another's
+    // loads.  Launches of fewer waves per workgroup are left alone: they need
+    // several workgroups per CU to fill it.
+    const bool one_per_cu = nw == 8 && grid.x < 16u * unsigned(device_cus());
     bool launched = false;
 #define PKV_DEC_MFMA(KV, Q, DD, DEP, W, G)                                                   \
     if (!launched && mfma && pool.dtype == KV && a.q_dtype == Q && pool.head_dim == DD &&    \
         depth == DEP && nw == W && ng == G) {                                                \
-      e = launch_decode_kernel(decode_mfma_kernel<KV, Q, DD, DEP, W, G>, grid, dim3(64 * W), \
-                               stream, p, p.tables);                                         \
+      if (put) {                                                                             \
+        constexpr auto k = decode_mfma_kernel<KV, Q, DD, DEP, W, G, DEP == 1>;               \
+        e = launch_decode_kernel(k, grid, dim3(64 * W), one_per_cu ? one_per_cu_lds<k>() : 0, \
+                                 stream, p, p.tables);                                       \
+      } else {                                                                               \
+        constexpr auto k = decode_mfma_kernel<KV, Q, DD, DEP, W, G, false>;                  \
+        e = launch_decode_kernel(k, grid, dim3(64 * W), one_per_cu ? one_per_cu_lds<k>() : 0, \
+                                 stream, p, p.tables);                                       \
+      }                                                                                      \
       launched = true;                                                                       \
     }
 #define PKV_DEC_MFMA_W(KV, Q, DD, DEP) \
@@ -1545,7 +1614,7 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
     PKV_DEC_MFMA_G(KV, Q, 64) PKV_DEC_MFMA_G(KV, Q, 128)
 #define PKV_DEC_VALU(DT, DD)                                                                 \
     if (!launched && pool.dtype == DT && pool.head_dim == DD) {                              \
-      e = launch_decode_kernel(decode_valu_kernel<DT, DD>, grid, dim3(64), stream, p,        \
+      e = launch_decode_kernel(decode_valu_kernel<DT, DD>, grid, dim3(64), 0, stream, p,     \
                                p.tables);                                                    \
       launched = true;                                                                       \
     }
