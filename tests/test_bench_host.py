@@ -66,3 +66,19 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_item_balance_load_model():
+    """The balance figure of the ragged batch: items follow the plan's split
+    rule, and the longest-first load model's finish over the even share is
+    1 for equal items and the largest item's share for one dominant item."""
+    even = bench.item_balance([32] * 256, 1 << 20, 1, n_cus=256)
+    assert even["items"] == 256 and even["lpt_makespan_over_mean"] == 1.0
+    one = bench.item_balance([1000] + [10] * 255, 1 << 20, 1, n_cus=256)
+    assert abs(one["lpt_makespan_over_mean"] - 1000 / (3550 / 256)) < 1e-3
+    split = bench.item_balance([1000] + [10] * 255, 100, 1, n_cus=256)
+    assert split["items"] == 10 + 255
+    assert abs(split["lpt_makespan_over_mean"] - 100 / (3550 / 256)) < 1e-3
+    assert sum(split["tokens_per_item_histogram"].values()) == split["items"]
+    # every KV head of an item is one workgroup
+    assert bench.item_balance([64] * 4, 1 << 20, 8, n_cus=256)["workgroups"] == 32
