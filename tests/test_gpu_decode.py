@@ -256,3 +256,21 @@ def test_nan_in_unused_slots_does_not_leak(dtype, hq, hkv, d):
     dp.buf.copy_(gu.to_device_raw(host, dtype))
     q = host_normal(rng, (len(lens), hq, d), dtype)
     check_decode_all(dp, 0, q, table, lens, hq, parts=(0, 16, 64), variants=("auto", "valu"))
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 64, 8, 64), ("bf16", 32, 1, 64),
+                                             ("f16", 16, 2, 128), ("bf16", 16, 8, 128)])
+def test_eight_wave_launches_with_one_workgroup_per_cu(dtype, hq, hkv, d):
+    """Sequences long enough for 8-wave workgroups, few workgroups per CU:
+    these launches ask for extra dynamic LDS (one workgroup per CU), up to
+    ~47 KB of it at d = 64.  One and two tiles of query heads."""
+    from workloads.configs import host_normal, deal_tables
+    from tests import gpu_util as gu
+    rng = np.random.default_rng(hq + hkv + d)
+    lens = np.array([600, 1500, 2047, 900, 3000], dtype=np.int64)
+    need = int(sum(-(-x // 16) for x in lens))
+    table = deal_tables(rng.permutation(need + 3)[:need].astype(np.int32), lens, 256)
+    dp = gu.DevicePool(1, need + 3, hkv, d, dtype)
+    fill_random_pool(dp, 29)
+    q = host_normal(rng, (len(lens), hq, d), dtype)
+    check_decode_all(dp, 0, q, table, lens, hq, parts=(0, 512))
