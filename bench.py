@@ -59,9 +59,11 @@ def recorded_traffic(kernel="decode_mfma_kernel", workload="70b", root=ROOT):
 POOL_LAYOUT = os.environ.get("PKV_BENCH_LAYOUT", "block")
 
 
-def device_pool_fp8(n_layers, num_blocks, n_kv_heads, head_dim, seed, scale=0.01, layout=None):
+def device_pool_fp8(n_layers, num_blocks, n_kv_heads, head_dim, seed, scale=0.01, layout=None,
+                    per_block=False):
     """fp8 (E4M3) pool of random finite codes with one K and one V scale per
-    (layer, KV head); layouts as in device_pool."""
+    (layer, KV head), or per (layer, block, KV head) (values in [scale,
+    2 scale)); layouts as in device_pool."""
     import torch
     import paged_kv_cache_inject_amd as pkv
     layout = layout or POOL_LAYOUT
@@ -79,11 +81,17 @@ def device_pool_fp8(n_layers, num_blocks, n_kv_heads, head_dim, seed, scale=0.01
                                  generator=g))
         part |= torch.randint(0, 2, (layer_stride,), dtype=torch.uint8, device="cuda",
                               generator=g) << 7
-    ks = torch.full((n_layers, n_kv_heads), scale, dtype=torch.float32, device="cuda")
-    vs = torch.full((n_layers, n_kv_heads), scale, dtype=torch.float32, device="cuda")
-    desc = pkv.pkv_pool(n_layers, num_blocks, n_kv_heads, head_dim, pkv.PKV_FP8E4M3, 0,
-                        buf.data_ptr(), buf.data_ptr() + v_off, layer_stride,
-                        block_stride, head_stride, ks.data_ptr(), vs.data_ptr())
+    if per_block:
+        g.manual_seed(seed * 1000 + 999)
+        shape = (n_layers, num_blocks, n_kv_heads)
+        ks = scale * (1 + torch.rand(shape, dtype=torch.float32, device="cuda", generator=g))
+        vs = scale * (1 + torch.rand(shape, dtype=torch.float32, device="cuda", generator=g))
+    else:
+        ks = torch.full((n_layers, n_kv_heads), scale, dtype=torch.float32, device="cuda")
+        vs = torch.full((n_layers, n_kv_heads), scale, dtype=torch.float32, device="cuda")
+    desc = pkv.pkv_pool(n_layers, num_blocks, n_kv_heads, head_dim, pkv.PKV_FP8E4M3,
+                        1 if per_block else 0, buf.data_ptr(), buf.data_ptr() + v_off,
+                        layer_stride, block_stride, head_stride, ks.data_ptr(), vs.data_ptr())
     return (buf, ks, vs), desc
 
 
@@ -204,7 +212,7 @@ def decode_workload(name):
         return MQA_64, llama70b_structure(MQA_64)
     if name == "mistral-window":
         return MISTRAL_WINDOW, window_structure()
-    if name in ("70b", "70b-fp8"):
+    if name in ("70b", "70b-fp8", "70b-fp8b"):
         return LLAMA70B_80LAYER, llama70b_structure(LLAMA70B_80LAYER)
     if name == "70b-block32":
         return LLAMA70B_80LAYER, llama70b_structure(LLAMA70B_80LAYER, block_tokens=32)
@@ -222,12 +230,13 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None, two_calls=True)
     cfg, st = decode_workload(workload)
     lens = st["lens"]
     launch_steps = steps if launch_steps is None else launch_steps
-    fp8 = workload.endswith("-fp8")
+    per_block = workload.endswith("-fp8b")     # fp8 with scales per (layer, block, head)
+    fp8 = workload.endswith("-fp8") or per_block
     log("decode: allocating and filling %d layers x %d blocks%s"
         % (cfg.n_layers, st["num_blocks"], " (fp8)" if fp8 else ""))
     if fp8:
         buf, pool = device_pool_fp8(cfg.n_layers, st["num_blocks"], cfg.n_kv_heads,
-                                    cfg.head_dim, cfg.seed)
+                                    cfg.head_dim, cfg.seed, per_block=per_block)
     else:
         buf, pool = device_pool(cfg.n_layers, st["num_blocks"], cfg.n_kv_heads, cfg.head_dim,
                                 cfg.dtype, cfg.seed)
@@ -340,7 +349,8 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None, two_calls=True)
                tables_sha256=hashlib.sha256(np.ascontiguousarray(st["tables"]).tobytes()).hexdigest(),
                launches_timed=len(launch_ms),
                n_items=n_items, part_tokens=part_tokens, waves=waves,
-               workload=cfg.workload + (" (fp8 E4M3 cache)" if fp8 else ""),
+               workload=cfg.workload + ((" (fp8 E4M3 cache, scales per block)" if per_block
+                                         else " (fp8 E4M3 cache)") if fp8 else ""),
                dtype="fp8e4m3" if fp8 else cfg.dtype,
                batch=cfg.batch, context=int(lens.max()), layers=cfg.n_layers)
     res["value"] = res["bytes_per_step"] / (ms_step * 1e-3) / 1e9
@@ -721,8 +731,8 @@ def main():
     ap.add_argument("--no-two-calls", action="store_true",
                     help="skip the comparison timing of the step as two launches per layer")
     ap.add_argument("--decode-workload", default="70b",
-                    choices=["70b", "8b", "ragged", "70b-fp8", "mistral-window", "70b-block32",
-                             "mqa"],
+                    choices=["70b", "8b", "ragged", "70b-fp8", "70b-fp8b", "mistral-window",
+                             "70b-block32", "mqa"],
                     help="decode workload timed (the reported line uses 70b)")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 8
+#define PKV_ABI_VERSION 9
 /* Tokens per physical block ([InferScale] §2; [KV essay] "Paged attention"). */
 #define PKV_BLOCK_TOKENS 16
 
@@ -90,16 +90,25 @@ typedef struct pkv_plan pkv_plan;   /* host decode split plan (opaque)    */
  * aligned (base pointers and every stride times the element size a multiple
  * of 16).  dtype is PKV_F32, PKV_BF16, PKV_F16 or PKV_FP8E4M3; head_dim is 64
  * or 128.  An FP8E4M3 pool stores code = e4m3(x / scale) (round to nearest
- * even, saturating at 448) with one float scale per (layer, KV head) for K
- * and one for V: k_scale, v_scale are device float [n_layers][n_kv_heads]
- * (NULL for the other formats). */
+ * even, saturating at 448) with float scales for K and for V ("Latency
+ * Optimization > KV Cache Management": a quantised cache keeps a scale
+ * beside its codes), chosen by scale_mode:
+ *   0: one per (layer, KV head); k_scale, v_scale are device
+ *      float [n_layers][n_kv_heads];
+ *   1: one per (layer, block, KV head); k_scale, v_scale are device
+ *      float [n_layers][num_blocks][n_kv_heads].  A block's entries must hold
+ *      its scales before anything is written to it (the caller sets them,
+ *      e.g. from the magnitudes the block will hold); pkv_copy_blocks copies
+ *      a block's entries along with its planes, so in this mode it writes
+ *      through k_scale and v_scale.
+ * The scale pointers are NULL and scale_mode 0 for the other formats. */
 typedef struct {
   int32_t n_layers;
   int32_t num_blocks;
   int32_t n_kv_heads;
   int32_t head_dim;
   int32_t dtype;
-  int32_t _reserved;
+  int32_t scale_mode;   /* FP8E4M3 pools: 0 per (layer, head), 1 per (layer, block, head) */
   void* k;              /* device */
   void* v;              /* device */
   int64_t layer_stride; /* elements */

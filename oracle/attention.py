@@ -17,7 +17,8 @@ Readings taken:
 * scale = 1/sqrt(d); everything is evaluated in float64 from the exactly
   widened stored values;
 * an fp8 cache holds codes whose values are e4m3(code) times the float32
-  scale of their (layer, KV head); the query then comes in a 16-bit format;
+  scale of their (layer, KV head), or of their (layer, block, KV head) when
+  the scales are given per block; the query then comes in a 16-bit format;
 * with a sliding window W ([KV essay] "Capping the window": a token
   attends only to the last W tokens), the query of a sequence of length n
   attends to positions max(0, n - W) .. n-1 only;
@@ -38,7 +39,8 @@ import math
 
 import numpy as np
 
-from .layout import PoolSpec, block_in_range, gather_sequence, gather_sequence_planes
+from .layout import (BLOCK_TOKENS, PoolSpec, block_in_range, gather_sequence,
+                     gather_sequence_planes)
 from .numerics import to_f64
 
 
@@ -103,21 +105,26 @@ def decode_paged(q, k_pool, v_pool, spec: PoolSpec, layer: int, tables, lens,
         kv_heads = sorted({h // g for h in qh})
         gather = gather_sequence_planes if by_plane else gather_sequence
         start = max(0, int(lens[b]) - int(window)) if window else 0
+        kept = list(range(start, int(lens[b])))
         if num_blocks is None:
             k_raw, v_raw = gather(k_pool, v_pool, spec, layer, tables[b], int(lens[b]),
                                   heads=kv_heads, start=start)
         else:
-            kept = [p for p in range(start, int(lens[b]))
-                    if block_in_range(tables[b], p, num_blocks)]
+            kept = [p for p in kept if block_in_range(tables[b], p, num_blocks)]
             k_raw, v_raw = gather_sequence(k_pool, v_pool, spec, layer, tables[b], int(lens[b]),
                                            heads=kv_heads, positions=kept)
         k64 = to_f64(k_raw, spec.dtype)
         v64 = to_f64(v_raw, spec.dtype)
         if spec.dtype == "fp8":
-            ks = np.array([float(k_scale[layer][h]) for h in kv_heads])
-            vs = np.array([float(v_scale[layer][h]) for h in kv_heads])
-            k64 = k64 * ks[None, :, None]
-            v64 = v64 * vs[None, :, None]
+            # each position's values times the scale of its block and head
+            blocks = np.array([int(tables[b][p // BLOCK_TOKENS]) for p in kept], dtype=np.int64)
+            for arr, scales in ((k64, k_scale), (v64, v_scale)):
+                sa = np.asarray(scales, dtype=np.float64)
+                if sa.ndim == 3:
+                    per = sa[layer][blocks][:, kv_heads]               # [positions][heads]
+                else:
+                    per = np.broadcast_to(sa[layer][kv_heads], (len(kept), len(kv_heads)))
+                arr *= per[:, :, None]
         for h in qh:
             i = kv_heads.index(h // g)
             if lens[b] == 0 or k64.shape[0] == 0:

@@ -32,8 +32,8 @@ contiguous.
 
 import numpy as np
 
-from .layout import (BLOCK_TOKENS, PoolSpec, block_in_range, k_element_offsets, v_element_offsets,
-                     slot)
+from .layout import (BLOCK_TOKENS, PoolSpec, block_in_range, k_element_offsets, scale_at,
+                     v_element_offsets, slot)
 from .numerics import from_f32, to_f32, f32_to_e4m3_rne_sat
 from .rope import rotate_f32
 
@@ -82,7 +82,9 @@ def write_token(k_pool, v_pool, spec: PoolSpec, layer: int, table_row, pos: int,
     """Store one token (all KV heads) of one layer at position ``pos``.
 
     k_raw, v_raw: [n_kv_heads][d] in ``src_dtype`` (default: the cache's).
-    k_scale, v_scale: [n_layers][n_kv_heads] float32 (fp8 caches only).
+    k_scale, v_scale: float32 [n_layers][n_kv_heads], or per block
+    [n_layers][num_blocks][n_kv_heads] (fp8 caches only): the code stored is
+    e4m3(x / scale) with the scale of the destination's layer, block and head.
     """
     src_dtype = spec.dtype if src_dtype is None else src_dtype
     s = slot(table_row, pos)
@@ -90,8 +92,8 @@ def write_token(k_pool, v_pool, spec: PoolSpec, layer: int, table_row, pos: int,
     k32 = to_f32(k_raw, src_dtype)
     k_rot = rotate_f32(k32, np.full(k32.shape[:-1], pos), cos_t, sin_t, mode)
     for h in range(spec.n_kv_heads):
-        ks = None if k_scale is None else k_scale[layer][h]
-        vs = None if v_scale is None else v_scale[layer][h]
+        ks = None if k_scale is None else scale_at(k_scale, layer, blk, h)
+        vs = None if v_scale is None else scale_at(v_scale, layer, blk, h)
         k_pool[k_element_offsets(spec, layer, blk, h, t)] = _store(k_rot[h], spec.dtype, ks)
         if src_dtype == spec.dtype:
             v_pool[v_element_offsets(spec, layer, blk, h, t)] = v_raw[h]
@@ -149,11 +151,13 @@ def append(k_pool, v_pool, spec: PoolSpec, layer: int, tables, lens_after, seqs,
                         v_scale)
 
 
-def copy_blocks(k_pool, v_pool, spec: PoolSpec, pairs):
+def copy_blocks(k_pool, v_pool, spec: PoolSpec, pairs, k_scale=None, v_scale=None):
     """Carry out queued copy-on-write copies, one after another in order:
     for each (src, dst) every layer's and KV head's K and V plane of block
     ``src`` is copied into block ``dst`` (a block holds all layers, since one
-    table serves every layer)."""
+    table serves every layer).  Per-block fp8 scales (numpy arrays
+    [n_layers][num_blocks][n_kv_heads]) travel with their planes; they are
+    updated in place."""
     plane = BLOCK_TOKENS * spec.head_dim
     for src, dst in pairs:
         for layer in range(spec.n_layers):
@@ -162,3 +166,6 @@ def copy_blocks(k_pool, v_pool, spec: PoolSpec, pairs):
                 b = spec.plane_base(layer, int(dst), h)
                 k_pool[b:b + plane] = k_pool[a:a + plane].copy()
                 v_pool[b:b + plane] = v_pool[a:a + plane].copy()
+        for sc in (k_scale, v_scale):
+            if sc is not None and np.ndim(sc) == 3:
+                sc[:, int(dst), :] = sc[:, int(src), :]

@@ -113,6 +113,14 @@ def read_token(k_pool, v_pool, spec: PoolSpec, layer: int, block: int, t: int):
     return k, v
 
 
+def scale_at(scales, layer: int, blk: int, h: int) -> float:
+    """The float32 scale of an fp8 pool for (layer, block, KV head): scales
+    are [n_layers][n_kv_heads] (one per layer and head) or
+    [n_layers][num_blocks][n_kv_heads] (one per block as well)."""
+    s = np.asarray(scales)
+    return float(s[layer, blk, h]) if s.ndim == 3 else float(s[layer, h])
+
+
 def block_in_range(table_row, p: int, num_blocks: int) -> bool:
     """Whether logical position ``p``'s table entry names a block of the pool
     (0 <= id < num_blocks).  Index data that lives on the device is not

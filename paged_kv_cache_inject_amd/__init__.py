@@ -43,7 +43,7 @@ class PkvError(RuntimeError):
 class pkv_pool(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("_reserved", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
                 ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("layer_stride", ctypes.c_int64), ("block_stride", ctypes.c_int64),
                 ("head_stride", ctypes.c_int64), ("k_scale", ctypes.c_void_p),
@@ -328,8 +328,11 @@ def pkv_rope_table(head_dim, base, max_pos):
 # Descriptors
 # ---------------------------------------------------------------------------
 def make_pool(k, v, n_layers, num_blocks, n_kv_heads, head_dim, dtype,
-              layer_stride, block_stride, head_stride, k_scale=None, v_scale=None) -> pkv_pool:
-    return pkv_pool(n_layers, num_blocks, n_kv_heads, head_dim, DTYPE_CODES[dtype], 0,
+              layer_stride, block_stride, head_stride, k_scale=None, v_scale=None,
+              scale_mode=0) -> pkv_pool:
+    """scale_mode (fp8 pools): 0 scales per (layer, KV head), 1 per (layer,
+    block, KV head)."""
+    return pkv_pool(n_layers, num_blocks, n_kv_heads, head_dim, DTYPE_CODES[dtype], scale_mode,
                     _ptr(k), _ptr(v), layer_stride, block_stride, head_stride, _ptr(k_scale),
                     _ptr(v_scale))
 

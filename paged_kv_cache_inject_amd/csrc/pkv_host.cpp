@@ -280,6 +280,8 @@ pkv_status check_pool(const pkv_pool* p) {
     return fail(PKV_E_INVALID, "block_stride smaller than a plane");
   if (p->dtype == PKV_FP8E4M3 && (!p->k_scale || !p->v_scale))
     return fail(PKV_E_INVALID, "an FP8E4M3 pool needs k_scale and v_scale");
+  if (p->scale_mode != 0 && !(p->scale_mode == 1 && p->dtype == PKV_FP8E4M3))
+    return fail(PKV_E_INVALID, "scale_mode %d (0, or 1 for an FP8E4M3 pool)", p->scale_mode);
   return PKV_OK;
 }
 

@@ -244,8 +244,9 @@ struct InjectParams {
   char* pool_v;
   int64_t p_layer, p_block, p_head;  // bytes
   int n_kv_heads;
-  const float* k_scale;              // [layers][heads], quantised pools only
-  const float* v_scale;
+  const float* k_scale;              // quantised pools only: [layers][heads], or
+  const float* v_scale;              // [layers][num_blocks][heads] (scale_mode 1)
+  int scale_mode;
   const char* src_k;
   const char* src_v;
   int64_t s_layer, s_token;          // bytes
@@ -393,7 +394,11 @@ __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParam
         } else if (p.rope_mode == PKV_ROPE_HALVES) {
           rot_halves_f<XS>(kl, kh, j0, cs[t], cs[t] + D / 2);
         }
-        const float ksc = PDT == PKV_FP8E4M3 ? p.k_scale[layer * p.n_kv_heads + h] : 1.f;
+        // the scales of this (layer, head), or of this (layer, block, head)
+        const int64_t si = p.scale_mode == 1
+                               ? (int64_t(layer) * p.num_blocks + desc.phys_block) * p.n_kv_heads + h
+                               : int64_t(layer) * p.n_kv_heads + h;
+        const float ksc = PDT == PKV_FP8E4M3 ? p.k_scale[si] : 1.f;
         Packed<PDT, XS> pk;
         char* kplane = kplane0 + int64_t(h) * p.p_head;
         pk.set(kl, ksc);
@@ -404,7 +409,7 @@ __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParam
           *reinterpret_cast<uint4*>(&vtile[hl][t][j0]) = v0[u];
           *reinterpret_cast<uint4*>(&vtile[hl][t][j1]) = v1[u];
         } else {
-          const float vsc = p.v_scale[layer * p.n_kv_heads + h];
+          const float vsc = p.v_scale[si];
           float vf[XS];
           Packed<PDT, XS> pv;
           unpack16<SDT>(v0[u], vf);
@@ -486,8 +491,9 @@ struct DecodeParams {
   float* part_ml;
   float* out;
   float* lse;
-  const float* k_scale;              // this layer's [heads] scales, quantised pools only
-  const float* v_scale;
+  const float* k_scale;              // quantised pools only: this layer's [heads]
+  const float* v_scale;              // scales, or its [num_blocks][heads] (scale_mode 1)
+  int scale_mode;
   // Fused append (new_k null: none): rows [seq][n_kv_heads][D] in the
   // query's format; each sequence's token goes to position len - 1.
   const char* new_k;
@@ -717,11 +723,13 @@ __device__ inline uint2 e4m3x4_to_f16x4(uint32_t w) {
 // format (equal to KVDT, or BF16/F16 for an fp8 pool whose MFMA operands are
 // float16), head dim D, prefetch depth, waves per workgroup NW, NG tiles of
 // 16 query heads (a KV head's group of up to 16 NG query heads: every
-// block's K and V, loaded once, serve all NG tiles), and PUT: whether the
+// block's K and V, loaded once, serve all NG tiles), PUT: whether the
 // kernel carries the decode step's append of the newest token (attention
 // alone runs an instance without that code, which it would otherwise pay for
-// in registers and scheduling even when no token is appended).
-template <int KVDT, int QDT, int D, int DEPTH, int NW, int NG, bool PUT>
+// in registers and scheduling even when no token is appended), and BLK: an
+// fp8 pool whose scales are per (layer, block, KV head) (its own instance,
+// for the same reason).
+template <int KVDT, int QDT, int D, int DEPTH, int NW, int NG, bool PUT, bool BLK>
 // `tables` is p.tables again as a restrict-qualified argument: the kernel's
 // only stores (the fused append) go to the pool, and with the table known
 // not to alias them its entries keep coming through scalar loads.
@@ -770,8 +778,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
       qreg[t][st] = head_ok(t) ? raw : make_uint4(0, 0, 0, 0);
     }
   }
+  // fp8 scales: per (layer, KV head), folded into the score multiplier and
+  // the final output; or per (layer, block, KV head) (blockwise), read with
+  // each block's id and applied to its scores and to its P·V product.
+  constexpr bool blockwise = FP8 && BLK;
   float kmul = 1.f, vmul = 1.f;
-  if constexpr (FP8) {
+  if constexpr (FP8 && !blockwise) {
     kmul = p.k_scale[g];
     vmul = p.v_scale[g];
   }
@@ -811,6 +823,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
   uint4 kbuf[DEPTH][SL];
   uint2 vbuf[DEPTH][NT];   // fp8: only .x holds the 4 codes
   bool okbuf[DEPTH];
+  float kscb[DEPTH], vscb[DEPTH];  // blockwise fp8 scales of the blocks in flight
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) kscb[d] = vscb[d] = 1.f;
 
   int put_blk = -1;  // block id read for the newest token's block
   // Block ids are read one issue ahead (issues come in order j = 0, 1, ...),
@@ -824,6 +839,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
     const bool ok = unsigned(blk) < unsigned(p.num_blocks);
     okbuf[d] = ok;
     blk = ok ? blk : 0;
+    if constexpr (blockwise) {
+      kscb[d] = p.k_scale[int64_t(blk) * p.n_kv_heads + g];
+      vscb[d] = p.v_scale[int64_t(blk) * p.n_kv_heads + g];
+    }
     const char* kp = kbase + int64_t(blk) * p.p_block;
     const char* vp = vbase + int64_t(blk) * p.p_block;
 #pragma unroll
@@ -880,6 +899,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
   if constexpr (PUT) {
     if (put_j >= 0) {
       ns = new_slot<QDT, KVDT, D>(p, it, g);
+      if constexpr (blockwise) {  // the scales of the block the token goes to
+        const int pb = tab[wave + put_j * NW];
+        const int64_t pi = int64_t(unsigned(pb) < unsigned(p.num_blocks) ? pb : 0) * p.n_kv_heads + g;
+        ns.ksc = p.k_scale[pi];
+        ns.vsc = p.v_scale[pi];
+      }
       if (p.rope_mode == PKV_ROPE_PAIRS) make_new(RopeTag<PKV_ROPE_PAIRS>{});
       else if (p.rope_mode == PKV_ROPE_HALVES) make_new(RopeTag<PKV_ROPE_HALVES>{});
       else make_new(RopeTag<PKV_ROPE_NONE>{});
@@ -963,6 +988,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
         for (int n = 0; n < NT; ++n)
           vcur[n] = FP8 ? e4m3x4_to_f16x4(vbuf[d][n].x) : vbuf[d][n];
         const bool blk_ok = okbuf[d];
+        // this block's scales, before the next issue reuses the slot
+        const float ksb = kscb[d], vsb = vscb[d];
         if (j + DEPTH < nj) issue(j + DEPTH, d);
 
         const int valid = it.n_tokens - (wave + j * NW) * kBlock;  // tokens in range
@@ -973,10 +1000,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
         // get -inf.  A whole block (the common case; wave-uniform) needs no
         // masks, and the masked case rewrites the values in place.
         float s4[NG][4];
+        float smul = score_mul;
+        if constexpr (blockwise) smul = p.scale_log2 * ksb;
 #pragma unroll
         for (int t = 0; t < NG; ++t)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) s4[t][r] = sc[t][r] * score_mul;
+          for (int r = 0; r < 4; ++r) s4[t][r] = sc[t][r] * smul;
         if (!(blk_ok && valid >= kBlock && skip <= 0)) {
           // The masked slots may hold anything, NaN included: zero their V
           // so that 0-weight * V stays 0.  Lane holds tokens 4*grp + e,
@@ -1035,10 +1064,21 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
                                       uint32_t(ph[2]) | (uint32_t(ph[3]) << 16));
           const uint2 bl = make_uint2(uint32_t(pl[0]) | (uint32_t(pl[1]) << 16),
                                       uint32_t(pl[2]) | (uint32_t(pl[3]) << 16));
+          if constexpr (blockwise) {
+            // this block's P·V on its own, then scaled by its V scale
 #pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            acc[t][n] = Mfma<OT>::pv(vcur[n], bh, acc[t][n]);
-            acc[t][n] = Mfma<OT>::pv(vcur[n], bl, acc[t][n]);
+            for (int n = 0; n < NT; ++n) {
+              f32x4_t b = Mfma<OT>::pv(vcur[n], bh, f32x4_t{0.f, 0.f, 0.f, 0.f});
+              b = Mfma<OT>::pv(vcur[n], bl, b);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[t][n][r] = fmaf(vsb, b[r], acc[t][n][r]);
+            }
+          } else {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+              acc[t][n] = Mfma<OT>::pv(vcur[n], bh, acc[t][n]);
+              acc[t][n] = Mfma<OT>::pv(vcur[n], bl, acc[t][n]);
+            }
           }
         }
       }
@@ -1310,6 +1350,11 @@ struct CopyParams {
   int64_t p_layer, p_block, p_head;  // byte strides
   int n_kv_heads;
   int plane_units;    // 16-byte units per plane
+  // Per-(layer, block, head) scales of a quantised pool (null otherwise):
+  // the copy carries a block's scales with its planes.
+  float* k_scale;
+  float* v_scale;
+  int num_blocks;
 };
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p, CopyBatch b) {
@@ -1323,6 +1368,12 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p, CopyBatc
     const int h = u / p.plane_units;
     const int64_t off = int64_t(h) * p.p_head + int64_t(u - h * p.plane_units) * 16;
     st16_stream(dst + off, ld16_stream(src + off));
+  }
+  float* sc = blockIdx.z == 0 ? p.k_scale : p.v_scale;
+  if (sc != nullptr && threadIdx.x < p.n_kv_heads) {
+    const int64_t l = int64_t(blockIdx.y) * p.num_blocks;
+    sc[(l + b.dst[pair]) * p.n_kv_heads + threadIdx.x] =
+        sc[(l + b.src[pair]) * p.n_kv_heads + threadIdx.x];
   }
 }
 
@@ -1431,6 +1482,8 @@ hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, bool src_in_h
   p.n_kv_heads = pool.n_kv_heads;
   p.k_scale = pool.k_scale;
   p.v_scale = pool.v_scale;
+  p.scale_mode = pool.scale_mode;
+  p.num_blocks = pool.num_blocks;
   p.src_k = static_cast<const char*>(src.k);
   p.src_v = static_cast<const char*>(src.v);
   p.s_layer = src.layer_stride * sb;
@@ -1491,6 +1544,7 @@ hipError_t launch_append(const pkv_pool& pool, int layer, const int32_t* d_table
   p.n_kv_heads = pool.n_kv_heads;
   p.k_scale = pool.k_scale;
   p.v_scale = pool.v_scale;
+  p.scale_mode = pool.scale_mode;
   p.src_k = static_cast<const char*>(d_k);
   p.src_v = static_cast<const char*>(d_v);
   p.s_layer = 0;
@@ -1554,8 +1608,11 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
   p.part_ml = a.part_ml;
   p.out = a.out;
   p.lse = a.lse;
-  p.k_scale = pool.k_scale ? pool.k_scale + int64_t(layer) * pool.n_kv_heads : nullptr;
-  p.v_scale = pool.v_scale ? pool.v_scale + int64_t(layer) * pool.n_kv_heads : nullptr;
+  // this layer's scales: [heads], or [num_blocks][heads] per block
+  const int64_t per_layer = int64_t(pool.scale_mode == 1 ? pool.num_blocks : 1) * pool.n_kv_heads;
+  p.k_scale = pool.k_scale ? pool.k_scale + int64_t(layer) * per_layer : nullptr;
+  p.v_scale = pool.v_scale ? pool.v_scale + int64_t(layer) * per_layer : nullptr;
+  p.scale_mode = pool.scale_mode;
   p.new_k = static_cast<const char*>(a.new_k);
   p.new_v = static_cast<const char*>(a.new_v);
   p.rope_mode = a.rope_mode;
@@ -1571,8 +1628,10 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
     const int ng = p.group <= 16 ? 1 : p.group <= 32 ? 2 : p.group <= 64 ? 4 : 0;
     const bool mfma = (kernel_variant != 1 || pool.dtype == PKV_FP8E4M3) &&
                       pool.dtype != PKV_F32 && ng > 0;
-    // The decode step's append (new token rows given) runs the PUT instance.
+    // The decode step's append (new token rows given) runs the PUT instance,
+    // an fp8 pool with per-block scales the BLK one.
     const bool put = a.new_k != nullptr;
+    const bool blk = pool.dtype == PKV_FP8E4M3 && pool.scale_mode == 1;
     // One block in flight per wave measured fastest with 8 waves per workgroup
     // (depth 2 is instantiated for attention alone only).
     const int depth = kernel_variant == 12 && !put ? 2 : 1;
@@ -1591,12 +1650,21 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
 #define PKV_DEC_MFMA(KV, Q, DD, DEP, W, G)                                                   \
     if (!launched && mfma && pool.dtype == KV && a.q_dtype == Q && pool.head_dim == DD &&    \
         depth == DEP && nw == W && ng == G) {                                                \
-      if (put) {                                                                             \
-        constexpr auto k = decode_mfma_kernel<KV, Q, DD, DEP, W, G, DEP == 1>;               \
+      constexpr bool B8 = KV == PKV_FP8E4M3; /* per-block scales exist for fp8 only */       \
+      if (put && blk) {                                                                      \
+        constexpr auto k = decode_mfma_kernel<KV, Q, DD, DEP, W, G, DEP == 1, B8>;           \
+        e = launch_decode_kernel(k, grid, dim3(64 * W), one_per_cu ? one_per_cu_lds<k>() : 0, \
+                                 stream, p, p.tables);                                       \
+      } else if (put) {                                                                      \
+        constexpr auto k = decode_mfma_kernel<KV, Q, DD, DEP, W, G, DEP == 1, false>;        \
+        e = launch_decode_kernel(k, grid, dim3(64 * W), one_per_cu ? one_per_cu_lds<k>() : 0, \
+                                 stream, p, p.tables);                                       \
+      } else if (blk) {                                                                      \
+        constexpr auto k = decode_mfma_kernel<KV, Q, DD, DEP, W, G, false, B8>;              \
         e = launch_decode_kernel(k, grid, dim3(64 * W), one_per_cu ? one_per_cu_lds<k>() : 0, \
                                  stream, p, p.tables);                                       \
       } else {                                                                               \
-        constexpr auto k = decode_mfma_kernel<KV, Q, DD, DEP, W, G, false>;                  \
+        constexpr auto k = decode_mfma_kernel<KV, Q, DD, DEP, W, G, false, false>;           \
         e = launch_decode_kernel(k, grid, dim3(64 * W), one_per_cu ? one_per_cu_lds<k>() : 0, \
                                  stream, p, p.tables);                                       \
       }                                                                                      \
@@ -1654,6 +1722,10 @@ hipError_t launch_copy_blocks(const pkv_pool& pool, const CopyBatch& batch, hipS
   p.p_head = pool.head_stride * eb;
   p.n_kv_heads = pool.n_kv_heads;
   p.plane_units = kBlock * pool.head_dim * eb / 16;
+  const bool blockwise = pool.dtype == PKV_FP8E4M3 && pool.scale_mode == 1;
+  p.k_scale = blockwise ? const_cast<float*>(pool.k_scale) : nullptr;
+  p.v_scale = blockwise ? const_cast<float*>(pool.v_scale) : nullptr;
+  p.num_blocks = pool.num_blocks;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(batch.n, pool.n_layers, 2), dim3(256), 0, stream,
                      p, batch);
   return hipGetLastError();

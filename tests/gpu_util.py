@@ -62,6 +62,7 @@ class DevicePool:
         self.total = n_layers * self.layer_stride
         self.buf = torch.empty(self.total, dtype=torch_dtype(dtype), device=device)
         self.k_scale = self.v_scale = None        # float32 [layers][heads] (fp8 pools)
+        self.scale_mode = 0                       # 1: scales [layers][blocks][heads]
         if fill_bits is not None:
             if dtype == "fp8":
                 self.buf.fill_(int(fill_bits) & 0xFF)
@@ -74,11 +75,16 @@ class DevicePool:
         e = ELEM[self.dtype]
         base = self.buf.data_ptr() + layer_offset * self.layer_stride * e
         return pkv.pkv_pool(self.n_layers - layer_offset, self.num_blocks, self.n_kv_heads,
-                            self.head_dim, pkv.DTYPE_CODES[self.dtype], 0, base,
+                            self.head_dim, pkv.DTYPE_CODES[self.dtype], self.scale_mode, base,
                             base + self.v_off * e, self.layer_stride, self.block_stride,
                             self.head_stride,
-                            None if self.k_scale is None else self.k_scale.data_ptr(),
-                            None if self.v_scale is None else self.v_scale.data_ptr())
+                            None if self.k_scale is None else self._scale_ptr(self.k_scale, layer_offset),
+                            None if self.v_scale is None else self._scale_ptr(self.v_scale, layer_offset))
+
+    def _scale_ptr(self, t, layer_offset):
+        """Address of layer `layer_offset`'s scales (the pool view starts there)."""
+        per_layer = t[0].numel()
+        return t.data_ptr() + layer_offset * per_layer * 4
 
     def spec(self):
         return PoolSpec(self.n_layers, self.num_blocks, self.n_kv_heads, self.head_dim,
@@ -89,8 +95,10 @@ class DevicePool:
         return raw_view(self.buf.cpu()).copy()
 
     def set_scales(self, k_scale, v_scale):
-        """Per-(layer, KV head) float32 scales of an fp8 pool (host arrays)."""
+        """float32 scales of an fp8 pool (host arrays): [layers][heads], or
+        [layers][blocks][heads] for per-block scales."""
         import torch
+        self.scale_mode = 1 if np.ndim(k_scale) == 3 else 0
         self.k_scale = torch.from_numpy(np.ascontiguousarray(k_scale, np.float32)).cuda()
         self.v_scale = torch.from_numpy(np.ascontiguousarray(v_scale, np.float32)).cuda()
 

@@ -31,6 +31,8 @@ CASES = [
     ("fp8", 64, 2, 128, "pairs", 16, 0),
     ("bf16", 64, 1, 64, "halves", 0, 0),
     ("bf16", 32, 8, 128, "pairs", 0, 100),
+    # fp8 with scales per (layer, block, KV head)
+    ("fp8b", 16, 2, 128, "pairs", 0, 0), ("fp8b", 64, 1, 64, "halves", 16, 0),
 ]
 
 
@@ -57,7 +59,9 @@ def test_append_decode_matches_two_calls_and_oracle(dtype, hq, hkv, d, mode, par
     from workloads.configs import host_normal, deal_tables
 
     gu.say("append+decode", dtype, hq, hkv, d, mode, part, window)
-    rng = np.random.default_rng(hq * 1009 + hkv * 31 + d + part + window)
+    rng = np.random.default_rng(hq * 1009 + hkv * 31 + d + part + window + (dtype == "fp8b"))
+    blockwise = dtype == "fp8b"
+    dtype = "fp8" if blockwise else dtype
     L, layer = 2, 1
     lens = np.array(LENS, dtype=np.int64)
     B = len(lens)
@@ -68,8 +72,9 @@ def test_append_decode_matches_two_calls_and_oracle(dtype, hq, hkv, d, mode, par
     pools = [gu.DevicePool(L, nb, hkv, d, dtype) for _ in range(2)]
     ks = vs = None
     if dtype == "fp8":
-        ks = rng.uniform(0.01, 0.03, size=(L, hkv)).astype(np.float32)
-        vs = rng.uniform(0.01, 0.03, size=(L, hkv)).astype(np.float32)
+        shape = (L, nb, hkv) if blockwise else (L, hkv)
+        ks = rng.uniform(0.01, 0.03, size=shape).astype(np.float32)
+        vs = rng.uniform(0.01, 0.03, size=shape).astype(np.float32)
         for dp in pools:
             dp.set_scales(ks, vs)
     raw = _fill(pools[0], rng, dtype)

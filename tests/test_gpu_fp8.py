@@ -9,15 +9,19 @@ import pytest
 pytestmark = pytest.mark.gpu
 
 
-def scales(rng, L, H):
-    k = rng.uniform(0.004, 0.03, size=(L, H)).astype(np.float32)
-    v = rng.uniform(0.004, 0.03, size=(L, H)).astype(np.float32)
+def scales(rng, L, H, nb=None):
+    """Scales per (layer, KV head), or per (layer, block, KV head) when nb is
+    given (pool scale_mode 1)."""
+    shape = (L, H) if nb is None else (L, nb, H)
+    k = rng.uniform(0.004, 0.03, size=shape).astype(np.float32)
+    v = rng.uniform(0.004, 0.03, size=shape).astype(np.float32)
     return k, v
 
 
-@pytest.mark.parametrize("sdt,d,mode", [("bf16", 128, "pairs"), ("bf16", 128, "halves"),
-                                        ("f16", 64, "pairs"), ("bf16", 64, "none")])
-def test_fp8_inject_matches_oracle(sdt, d, mode):
+@pytest.mark.parametrize("sdt,d,mode,blockwise", [
+    ("bf16", 128, "pairs", False), ("bf16", 128, "halves", False), ("f16", 64, "pairs", False),
+    ("bf16", 64, "none", False), ("bf16", 128, "pairs", True), ("f16", 64, "halves", True)])
+def test_fp8_inject_matches_oracle(sdt, d, mode, blockwise):
     import torch
     import paged_kv_cache_inject_amd as pkv
     from oracle import inject as o_inject
@@ -26,11 +30,11 @@ def test_fp8_inject_matches_oracle(sdt, d, mode):
     from tests import gpu_util as gu
     from workloads.configs import host_normal
 
-    gu.say("fp8 inject", sdt, d, mode)
-    rng = np.random.default_rng(hash((sdt, d, mode)) % 2 ** 32)
+    gu.say("fp8 inject", sdt, d, mode, "per block" if blockwise else "per head")
+    rng = np.random.default_rng(hash((sdt, d, mode, blockwise)) % 2 ** 32)
     L, H, NB, max_pos = 3, 4, 48, 300
     dp = gu.DevicePool(L, NB, H, d, "fp8", fill_bits=0x5A)
-    ks, vs = scales(rng, L, H)
+    ks, vs = scales(rng, L, H, NB if blockwise else None)
     dp.set_scales(ks, vs)
     cache = pkv.pkv_cache_create(NB, 4, 16, free_list_seed=21)
     model = AllocatorModel(NB, 4, 16, seed=21)
@@ -60,8 +64,9 @@ def test_fp8_inject_matches_oracle(sdt, d, mode):
         gu.assert_bytes_equal(dp.host_copy(), ref, "fp8 pool after inject call %d" % i)
 
 
-@pytest.mark.parametrize("sdt,n_new", [("bf16", 1), ("bf16", 17), ("f16", 32)])
-def test_fp8_append_matches_oracle(sdt, n_new):
+@pytest.mark.parametrize("sdt,n_new,blockwise", [("bf16", 1, False), ("bf16", 17, False),
+                                                 ("f16", 32, False), ("bf16", 17, True)])
+def test_fp8_append_matches_oracle(sdt, n_new, blockwise):
     import torch
     import paged_kv_cache_inject_amd as pkv
     from oracle import inject as o_inject
@@ -70,10 +75,10 @@ def test_fp8_append_matches_oracle(sdt, n_new):
     from tests import gpu_util as gu
     from workloads.configs import host_normal
 
-    rng = np.random.default_rng(n_new + 100)
+    rng = np.random.default_rng(n_new + 100 + blockwise)
     L, H, NB, B, d, max_pos = 2, 8, 64, 6, 128, 512
     dp = gu.DevicePool(L, NB, H, d, "fp8", fill_bits=0x33)
-    ks, vs = scales(rng, L, H)
+    ks, vs = scales(rng, L, H, NB if blockwise else None)
     dp.set_scales(ks, vs)
     cache = pkv.pkv_cache_create(NB, B, 32, free_list_seed=5)
     model = AllocatorModel(NB, B, 32, seed=5)
@@ -106,10 +111,11 @@ def test_fp8_append_matches_oracle(sdt, n_new):
     gu.assert_bytes_equal(dp.host_copy(), ref, "fp8 pool after append")
 
 
-@pytest.mark.parametrize("qdt,hq,hkv,d", [("bf16", 64, 8, 128), ("f16", 32, 8, 128),
-                                          ("bf16", 8, 8, 128), ("bf16", 16, 2, 64),
-                                          ("bf16", 64, 2, 128), ("f16", 64, 1, 64)])
-def test_fp8_decode_matches_oracle(qdt, hq, hkv, d):
+@pytest.mark.parametrize("qdt,hq,hkv,d,blockwise", [
+    ("bf16", 64, 8, 128, False), ("f16", 32, 8, 128, False), ("bf16", 8, 8, 128, False),
+    ("bf16", 16, 2, 64, False), ("bf16", 64, 2, 128, False), ("f16", 64, 1, 64, False),
+    ("bf16", 64, 8, 128, True), ("f16", 64, 1, 64, True), ("bf16", 32, 2, 128, True)])
+def test_fp8_decode_matches_oracle(qdt, hq, hkv, d, blockwise):
     import torch
     from oracle import attention as o_att
     from tests import gpu_util as gu
@@ -121,7 +127,7 @@ def test_fp8_decode_matches_oracle(qdt, hq, hkv, d):
     nb = need + 5
     table = deal_tables(rng.permutation(nb)[:need].astype(np.int32), lens, 128)
     dp = gu.DevicePool(1, nb, hkv, d, "fp8")
-    ks, vs = scales(rng, 1, hkv)
+    ks, vs = scales(rng, 1, hkv, nb if blockwise else None)
     dp.set_scales(ks, vs)
     # codes of magnitude up to ~448 times scales ~0.01: values of order 1
     codes = rng.integers(0, 0x7F, size=dp.total, dtype=np.uint8)
@@ -220,3 +226,39 @@ def test_fp8_nan_codes_in_unused_slots_do_not_leak():
         out, lse = gu.decode(dp, 0, q_dev, tdev, lens, hq, part, q_dtype="bf16")
         gu.assert_close(out.cpu().numpy(), ref, "fp8 NaN-canary out part=%d" % part)
         gu.assert_close(lse.cpu().numpy(), ref_lse, "fp8 NaN-canary lse part=%d" % part)
+
+
+def test_fp8_block_copy_carries_per_block_scales():
+    """Copy-on-write of a block of an fp8 pool with scales per (layer, block,
+    KV head): pkv_copy_blocks copies the planes and the block's scale
+    entries, as the oracle's copy does; other entries keep their values."""
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    from oracle import inject as o_inject
+    from tests import gpu_util as gu
+
+    rng = np.random.default_rng(808)
+    L, H, NB, d = 3, 4, 12, 128
+    dp = gu.DevicePool(L, NB, H, d, "fp8")
+    ks, vs = scales(rng, L, H, NB)
+    dp.set_scales(ks, vs)
+    codes = rng.integers(0, 0x7E, size=dp.total, dtype=np.uint8)
+    dp.buf.copy_(gu.to_device_raw(codes, "fp8"))
+    cache = pkv.pkv_cache_create(NB, 2, 8, free_list_seed=4)
+    pkv.pkv_extend(cache, [0], 20)                  # two blocks
+    pkv.pkv_fork(cache, 0, 1)
+    pkv.pkv_extend(cache, [1], 1)                   # position 20 lies in the shared block
+    pairs = [tuple(int(x) for x in pr) for pr in pkv.pkv_pending_copies(cache)]
+    assert len(pairs) == 1
+    pkv.pkv_copy_blocks(cache, dp.desc())
+    torch.cuda.synchronize()
+    ref = codes.copy()
+    kp, vp = dp.oracle_arrays(ref)
+    k_ref, v_ref = ks.copy(), vs.copy()
+    o_inject.copy_blocks(kp, vp, dp.spec(), pairs, k_scale=k_ref, v_scale=v_ref)
+    gu.assert_bytes_equal(dp.host_copy(), ref, "fp8 pool after the copy")
+    assert np.array_equal(dp.k_scale.cpu().numpy(), k_ref)
+    assert np.array_equal(dp.v_scale.cpu().numpy(), v_ref)
+    src, dst = pairs[0]
+    assert np.array_equal(k_ref[:, dst], ks[:, src]) and not np.array_equal(ks[:, dst], ks[:, src])
+    pkv.pkv_cache_destroy(cache)

@@ -121,3 +121,79 @@ def test_fp8_decode_equals_dequantised_contiguous():
             v64 = e4m3_to_f64(codes_v[b][:, g]) * float(v_scale[0, g])
             o, l = att.softmax_attend(q64[b, h], k64, v64, d ** -0.5)
             assert np.allclose(out[b, h], o, rtol=1e-13, atol=1e-15) and abs(lse[b, h] - l) < 1e-12
+
+
+def test_fp8_per_block_scales():
+    """Scales per (layer, block, KV head): decode dequantises each position
+    with the scale of the block it lies in (checked against softmax over
+    values dequantised position by position); equal scales in every block
+    reproduce the per-head result exactly; the stored code of a value is
+    e4m3(v / the scale of its destination block); a block copy carries its
+    scales."""
+    from oracle.inject import append, copy_blocks
+    d, H, HQ, NB = 64, 2, 4, 10
+    spec = PoolSpec(1, NB, H, d, "fp8").resolved()
+    rng = np.random.default_rng(19)
+    lens = [5, 33, 70]
+    kb = rng.uniform(0.01, 0.05, size=(1, NB, H)).astype(np.float32)
+    vb = rng.uniform(0.01, 0.05, size=(1, NB, H)).astype(np.float32)
+    codes_k = [rng.integers(0, 0x7E, size=(n, H, d)).astype(np.uint8) for n in lens]
+    codes_v = [rng.integers(0, 0x7E, size=(n, H, d)).astype(np.uint8) for n in lens]
+    kp = np.zeros(spec.elements(), np.uint8)
+    vp = np.zeros(spec.elements(), np.uint8)
+    perm = rng.permutation(NB)
+    tables, at = [], 0
+    for b, n in enumerate(lens):
+        nb = -(-n // 16)
+        tables.append(list(perm[at:at + nb]))
+        at += nb
+        for p in range(n):
+            blk, t = divmod(slot(tables[b], p), 16)
+            for h in range(H):
+                kp[k_element_offsets(spec, 0, blk, h, t)] = codes_k[b][p, h]
+                vp[v_element_offsets(spec, 0, blk, h, t)] = codes_v[b][p, h]
+    q = f32_to_bf16_rne(rng.standard_normal((3, HQ, d)).astype(np.float32))
+    out, lse = att.decode_paged(q, kp, vp, spec, 0, tables, lens, HQ, q_dtype="bf16",
+                                k_scale=kb, v_scale=vb)
+    q64 = to_f64(q, "bf16")
+    for b, n in enumerate(lens):
+        blk_of = [int(tables[b][p // 16]) for p in range(n)]
+        for h in range(HQ):
+            g = h // 2
+            k64 = np.stack([e4m3_to_f64(codes_k[b][p, g]) * float(kb[0, blk_of[p], g])
+                            for p in range(n)])
+            v64 = np.stack([e4m3_to_f64(codes_v[b][p, g]) * float(vb[0, blk_of[p], g])
+                            for p in range(n)])
+            o, l = att.softmax_attend(q64[b, h], k64, v64, d ** -0.5)
+            assert np.allclose(out[b, h], o, rtol=1e-13, atol=1e-15) and abs(lse[b, h] - l) < 1e-12
+    # the same scale in every block equals the per-(layer, head) form
+    kh = np.array([[0.02, 0.04]], np.float32)
+    vh = np.array([[0.03, 0.05]], np.float32)
+    o1, l1 = att.decode_paged(q, kp, vp, spec, 0, tables, lens, HQ, q_dtype="bf16",
+                              k_scale=kh, v_scale=vh)
+    o2, l2 = att.decode_paged(q, kp, vp, spec, 0, tables, lens, HQ, q_dtype="bf16",
+                              k_scale=np.repeat(kh[:, None, :], NB, axis=1),
+                              v_scale=np.repeat(vh[:, None, :], NB, axis=1))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # stored codes use the destination block's scale (no rotation: mode none)
+    cos_t, sin_t = rope_table(d, 10000.0, 64)
+    ak = np.zeros(spec.elements(), np.uint8)
+    av = np.zeros(spec.elements(), np.uint8)
+    k_new = f32_to_bf16_rne(rng.standard_normal((1, 2, H, d)).astype(np.float32))
+    v_new = f32_to_bf16_rne(rng.standard_normal((1, 2, H, d)).astype(np.float32))
+    row = [3, 7]                        # positions 15 and 16: blocks 3 and 7
+    append(ak, av, spec, 0, [row], [17], [0], 2, k_new, v_new, "none", cos_t, sin_t,
+           src_dtype="bf16", k_scale=kb, v_scale=vb)
+    for t, (blk, slot_t) in enumerate([(3, 15), (7, 0)]):
+        for h in range(H):
+            want_k = f32_to_e4m3_rne_sat(np.divide(to_f64(k_new[0, t, h], "bf16").astype(np.float32),
+                                                   kb[0, blk, h], dtype=np.float32))
+            want_v = f32_to_e4m3_rne_sat(np.divide(to_f64(v_new[0, t, h], "bf16").astype(np.float32),
+                                                   vb[0, blk, h], dtype=np.float32))
+            assert np.array_equal(ak[k_element_offsets(spec, 0, blk, h, slot_t)], want_k)
+            assert np.array_equal(av[v_element_offsets(spec, 0, blk, h, slot_t)], want_v)
+    # a block copy carries the block's scales
+    kc, vc = kb.copy(), vb.copy()
+    copy_blocks(ak, av, spec, [(3, 9)], k_scale=kc, v_scale=vc)
+    assert np.array_equal(kc[:, 9], kb[:, 3]) and np.array_equal(vc[:, 9], vb[:, 3])
+    assert np.array_equal(np.delete(kc, 9, axis=1), np.delete(kb, 9, axis=1))
