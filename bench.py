@@ -755,9 +755,10 @@ def main():
     log("bw probe: %.1f GB/s" % probe)
     two = not args.no_two_calls
     dec, _ = run_decode(args.steps, args.warmup, args.decode_workload, two_calls=two)
-    fp8 = None
+    fp8 = fp8b = None
     if not args.no_fp8 and args.decode_workload == "70b":
         fp8, _ = run_decode(args.steps, args.warmup, "70b-fp8", two_calls=two)
+        fp8b, _ = run_decode(args.steps, args.warmup, "70b-fp8b", two_calls=False)
     win = None
     if not args.no_window and args.decode_workload == "70b":
         win, _ = run_decode(args.steps, args.warmup, "mistral-window", two_calls=two)
@@ -827,6 +828,14 @@ def main():
             "launch_us_avg": round(fp8["launch_ms_avg"] * 1e3, 2),
             "two_calls_ms_per_step": _r4(fp8["two_calls_ms_per_step"]),
             "step_speedup_vs_bf16": round(dec["ms_per_step"] / fp8["ms_per_step"], 3)}
+    if fp8b is not None:
+        line["decode_fp8_block_scales"] = {
+            "workload": "the same decode workload with an fp8 (E4M3) cache whose scales are "
+                        "per (layer, block, KV head), bf16 queries",
+            "ms_per_step": round(fp8b["ms_per_step"], 4), "gbps": round(fp8b["value"], 1),
+            "pct_of_peak": round(100 * fp8b["value"] / PEAK_HBM_GBPS, 2),
+            "launch_us_avg": round(fp8b["launch_ms_avg"] * 1e3, 2),
+            "vs_per_head_scales": round(fp8b["ms_per_step"] / fp8["ms_per_step"], 3)}
     if win is not None:
         line["decode_window"] = {
             "workload": win["workload"], "ms_per_step": round(win["ms_per_step"], 4),
