@@ -275,7 +275,9 @@ int32_t pkv_pending_copies(const pkv_cache* cache, int32_t* pairs_out, int32_t c
 
 /* Carry out the queued copies on `stream` and empty the queue: for each pair,
  * every layer's K and V planes (all KV heads) of block src are copied into
- * block dst.  The result equals doing them one after another in queue order.
+ * block dst; for an FP8E4M3 pool with scale_mode 1, block dst's scale
+ * entries (every layer and KV head, K and V) are set to block src's.  The
+ * result equals doing them one after another in queue order.
  * The pool's blocks must include every queued id.  Device work only; the
  * pool must not be written by other work until the copies finish (stream
  * order suffices).  Errors: INVALID, RANGE (an id outside the pool), HIP. */
