@@ -15,15 +15,19 @@ LENS = [0, 1, 15, 16, 17, 40, 100, 333, 700, 2000]
 
 
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 32, 4, 128), ("f16", 8, 8, 64),
-                                            ("f32", 4, 2, 64), ("fp8", 16, 2, 128)])
+                                            ("f32", 4, 2, 64), ("fp8", 16, 2, 128),
+                                            ("fp8b", 16, 2, 128)])
 def test_window_decode_matches_oracle(dtype, hq, hkv, d):
+    """("fp8b": an fp8 pool with scales per (layer, block, KV head).)"""
     import torch
     from oracle import attention as o_att
     from tests import gpu_util as gu
     from workloads.configs import host_normal, deal_tables
 
     gu.say("window decode", dtype, hq, hkv, d)
-    rng = np.random.default_rng(hq * 3 + d)
+    rng = np.random.default_rng(hq * 3 + d + (dtype == "fp8b"))
+    blockwise = dtype == "fp8b"
+    dtype = "fp8" if blockwise else dtype
     lens = np.array(LENS, dtype=np.int64)
     need = int(sum(-(-x // 16) for x in lens))
     nb = need + 4
@@ -31,8 +35,9 @@ def test_window_decode_matches_oracle(dtype, hq, hkv, d):
     dp = gu.DevicePool(1, nb, hkv, d, dtype)
     ks = vs = None
     if dtype == "fp8":
-        ks = rng.uniform(0.01, 0.03, size=(1, hkv)).astype(np.float32)
-        vs = rng.uniform(0.01, 0.03, size=(1, hkv)).astype(np.float32)
+        shape = (1, nb, hkv) if blockwise else (1, hkv)
+        ks = rng.uniform(0.01, 0.03, size=shape).astype(np.float32)
+        vs = rng.uniform(0.01, 0.03, size=shape).astype(np.float32)
         dp.set_scales(ks, vs)
         codes = rng.integers(0, 0x60, size=dp.total, dtype=np.uint8)
         codes |= (rng.integers(0, 2, size=dp.total, dtype=np.uint8) << 7).astype(np.uint8)
