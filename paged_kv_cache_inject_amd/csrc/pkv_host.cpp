@@ -178,6 +178,7 @@ struct pkv_cache {
   std::vector<std::vector<int32_t>> tables;
   std::vector<int64_t> lens;
   std::vector<int32_t> desc_of_block;  // inject planner scratch, -1 when idle
+  std::vector<uint8_t> touched_flag;   // inject planner scratch per (seq, block index), 0 when idle
   Staging staging;
 
   void fl_push_back(int32_t b) {
@@ -813,15 +814,17 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
       reset_scratch();
       return st;
     }
-    for (int32_t t = 0; t < run.n_tokens; ++t) {
-      const int32_t p = run.dst_pos + t;
-      const int32_t cb = table[p / c->bt];
+    // One 16-token plane at a time: look its descriptor up once, then fill
+    // the run's slots in it.
+    for (int32_t t0 = 0; t0 < run.n_tokens;) {
+      const int32_t p0 = run.dst_pos + t0;
+      const int32_t cb = table[p0 / c->bt];
       if (cb < 0) {
         reset_scratch();
         return fail(PKV_E_RANGE, "seq %d position %d lies in a block a window trim dropped",
-                    run.seq, p);
+                    run.seq, p0);
       }
-      const int64_t plane = int64_t(cb) * c->sub + (p % c->bt) / kBlock;
+      const int64_t plane = int64_t(cb) * c->sub + (p0 % c->bt) / kBlock;
       if (plane >= pool->num_blocks) {
         reset_scratch();
         return fail(PKV_E_RANGE, "block %d outside the pool", cb);
@@ -833,7 +836,7 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
         di = int32_t(descs.size());
         InjectDesc d;
         d.phys_block = blk;
-        d.pos_base = p - p % kBlock;
+        d.pos_base = p0 - p0 % kBlock;
         for (int k = 0; k < kBlock; ++k) d.src[k] = -1;
         descs.push_back(d);
         dseq.push_back(run.seq);
@@ -841,13 +844,17 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
         dnext.push_back(desc_of_block[blk]);
         desc_of_block[blk] = di;
       }
-      int32_t& slot_src = descs[di].src[p % kBlock];
-      if (slot_src >= 0) {
-        reset_scratch();
-        return fail(PKV_E_OVERLAP, "two tokens of this call target seq %d position %d",
-                    run.seq, p);
+      const int32_t n_here = std::min(run.n_tokens - t0, kBlock - p0 % kBlock);
+      int32_t* slots = descs[di].src + p0 % kBlock;
+      for (int32_t k = 0; k < n_here; ++k) {
+        if (slots[k] >= 0) {
+          reset_scratch();
+          return fail(PKV_E_OVERLAP, "two tokens of this call target seq %d position %d",
+                      run.seq, p0 + k);
+        }
+        slots[k] = int32_t(run.src_token + t0 + k);
       }
-      slot_src = int32_t(run.src_token + t);
+      t0 += n_here;
     }
   }
   reset_scratch();
@@ -871,17 +878,26 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
   {
     std::vector<std::pair<int32_t, int64_t>> touched;  // (seq, block index)
     {
-      std::unordered_map<int64_t, char> seen;
+      const int64_t n_flags = int64_t(c->max_seqs) * c->max_blocks_per_seq;
+      if (int64_t(c->touched_flag.size()) < n_flags) c->touched_flag.assign(n_flags, 0);
       for (size_t i = 0; i < descs.size(); ++i) {
         const int64_t idx = descs[i].pos_base / c->bt;
-        if (seen.emplace(int64_t(dseq[i]) * c->max_blocks_per_seq + idx, 1).second)
+        uint8_t& f = c->touched_flag[int64_t(dseq[i]) * c->max_blocks_per_seq + idx];
+        if (!f) {
+          f = 1;
           touched.emplace_back(dseq[i], idx);
+        }
       }
+      for (const auto& si : touched)
+        c->touched_flag[int64_t(si.first) * c->max_blocks_per_seq + si.second] = 0;
     }
+    // Reference counts as they will be when each touched block is reached
+    // (only shared blocks, ref > 1, need a copy or are tracked).
     std::unordered_map<int32_t, int32_t> refs_then;
     int64_t need = 0;
     for (const auto& si : touched) {
       const int32_t b = c->tables[si.first][si.second];
+      if (c->ref[b] <= 1) continue;
       auto it = refs_then.find(b);
       const int32_t rc = it == refs_then.end() ? c->ref[b] : it->second;
       if (rc > 1) {
