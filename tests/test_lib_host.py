@@ -424,3 +424,38 @@ def test_kernel_timing_helper_without_launches():
     pkv.pkv_kernel_timing(False)
     assert len(pkv.pkv_kernel_times()) == 0
     assert pkv.load_library().pkv_kernel_times(None, 4) == pkv.PKV_E_INVALID
+
+
+def test_inject_overlap_found_in_any_plane_and_scale_mode_checked():
+    """The planner walks each run a 16-token plane at a time: a second write
+    to a slot is found wherever it falls (first plane, a later plane, the
+    second plane of a 32-token block); a pool's scale_mode is 0, or 1 for an
+    fp8 pool only."""
+    fake = 1 << 20
+    pool = pkv.pkv_pool(1, 16, 2, 64, pkv.PKV_BF16, 0, fake, fake + 4096, 16 * 4096, 4096, 1024)
+    src = pkv.pkv_src(fake, fake, 0, 128, 256, pkv.PKV_BF16)
+    for bt in (16, 32):
+        c = pkv.pkv_cache_create(8, 2, 8, block_tokens=bt)   # 8 blocks = up to 16 planes
+        pkv.pkv_alloc_blocks(c, 0, 100)
+        for runs in ([(0, 10, 12, 0), (0, 3, 18, 50)],      # second plane of the first run
+                     [(0, 40, 3, 0), (0, 1, 42, 90)],       # third plane
+                     [(0, 20, 20, 0), (0, 2, 38, 90)],      # 32-token block, its second plane
+                     [(0, 5, 0, 0), (0, 1, 4, 90)]):        # first plane
+            with pytest.raises(pkv.PkvError) as e:
+                pkv.pkv_inject(c, pool, src, runs, 0, 1, "pairs", fake, fake, 200, None, stream=0)
+            assert e.value.code == "OVERLAP", (bt, runs)
+        # nothing was planned or kept: the sequence is still empty
+        _, lens = pkv.pkv_block_table(c, [0], pkv.pkv_table_width(c))
+        assert list(lens) == [0]
+        pkv.pkv_cache_destroy(c)
+    c = pkv.pkv_cache_create(8, 2, 4)
+    pkv.pkv_alloc_blocks(c, 0, 40)
+    for dtype, mode, scales in ((pkv.PKV_BF16, 1, None), (pkv.PKV_FP8E4M3, 2, fake),
+                                (pkv.PKV_BF16, -1, None)):
+        bad = pkv.pkv_pool(1, 8, 2, 64, dtype, mode, fake, fake + 4096, 8 * 4096, 4096, 1024,
+                           scales, scales)
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_inject(c, bad, src, [(0, 1, 0, 0)], 0, 1, "pairs", fake, fake, 100, None,
+                           stream=0)
+        assert e.value.code == "INVALID" and "scale_mode" in str(e.value)
+    pkv.pkv_cache_destroy(c)
