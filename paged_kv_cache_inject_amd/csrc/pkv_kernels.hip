@@ -104,22 +104,15 @@ template <> struct Fmt<PKV_FP8E4M3> {
     return (b & 0x80) ? -v : v;
   }
   // Round to nearest, ties to even; magnitudes that would round beyond 448
-  // saturate to 448; NaN stays NaN.
+  // saturate to 448; NaN stays NaN (0x7F with its sign).  CDNA4's packed
+  // f32 -> E4M3 conversion rounds to nearest even but turns out-of-range
+  // values into the NaN code, so the value is clamped to +-448 first; a check
+  // on the GPU over every float32 bit pattern found this equal to the
+  // rounding rule above for every non-NaN input.
   __device__ static uint8_t from_f32(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7fffffffu;
-    if (a > 0x7f800000u) return uint8_t(sign | 0x7Fu);
-    if (a >= 0x43e00000u) return uint8_t(sign | 0x7Eu);          // >= 448
-    if (a < 0x3c800000u) {                                         // < 2^-6: step 2^-9
-      const uint32_t q = uint32_t(rintf(__uint_as_float(a) * 512.0f));
-      return uint8_t(sign | q);                                    // q = 8 is 2^-6
-    }
-    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);                  // keep 3 mantissa bits
-    r &= 0xFFF00000u;
-    uint32_t code = ((((r >> 23) & 0xFFu) - 120u) << 3) | ((r >> 20) & 7u);
-    if (code > 0x7Eu) code = 0x7Eu;
-    return uint8_t(sign | code);
+    if (x != x) return uint8_t(((__float_as_uint(x) >> 24) & 0x80u) | 0x7Fu);
+    const float c = fminf(fmaxf(x, -448.0f), 448.0f);
+    return uint8_t(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFF);
   }
 };
 
