@@ -541,7 +541,7 @@ def run_request_path(cfg, st, pool, src, runs, dcos, dsin, max_pos, inject_ws, r
     return res
 
 
-def run_inject_host(reps, n_chunks=250, batch=16):
+def run_inject_host(reps, n_chunks=250, batch=16, dma_compare=False):
     """The injection workload with the chunk store in pinned host memory
     ([InferScale] §6): 16 requests compose the prefix and top-8 of 250 chunks;
     the inject kernel reads only the runs' rows, over PCIe, while it writes the
@@ -605,7 +605,9 @@ def run_inject_host(reps, n_chunks=250, batch=16):
         # The alternative: a copy engine moves each run's rows (one
         # host-to-device copy per run, layer and K/V) into a device staging
         # buffer for the kernel to scatter from.  Only the copies are timed.
-        staging = torch.empty(n_tok * row * 2, dtype=torch.uint8, device="cuda")
+        dma_runs_ms = None
+        staging = torch.empty(n_tok * row * 2 if dma_compare else 16, dtype=torch.uint8,
+                              device="cuda")
         hk_view = torch.from_numpy(pkv.host_view(hk, nbytes))
         hv_view = torch.from_numpy(pkv.host_view(hv, nbytes))
 
@@ -619,12 +621,13 @@ def run_inject_host(reps, n_chunks=250, batch=16):
                             hview[a:a + n * row * 2], non_blocking=True)
                     at += n
 
-        copies()
-        torch.cuda.synchronize()
-        w0 = time.perf_counter()
-        copies()
-        torch.cuda.synchronize()
-        dma_runs_ms = (time.perf_counter() - w0) * 1e3
+        if dma_compare:
+            copies()
+            torch.cuda.synchronize()
+            w0 = time.perf_counter()
+            copies()
+            torch.cuda.synchronize()
+            dma_runs_ms = (time.perf_counter() - w0) * 1e3
         del staging
         res = dict(ms_per_call=ms, tokens=n_tok, requests=batch, layers=L,
                    tokens_per_s=n_tok / (ms * 1e-3), pcie_gbps=src_bytes / (ms * 1e-3) / 1e9,
@@ -751,6 +754,10 @@ def main():
     ap.add_argument("--host-store-only", action="store_true",
                     help="time only the pinned-host-store inject (no JSON line)")
     ap.add_argument("--cow-reps", type=int, default=10)
+    ap.add_argument("--dma-compare", action="store_true",
+                    help="also time moving the host store's run rows by one copy per run "
+                         "(off by default: it ended in a host segfault under counter "
+                         "collection, cause not shown)")
     ap.add_argument("--no-shapes", action="store_true",
                     help="skip the 8B-shaped and ragged-MHA decode figures")
     ap.add_argument("--no-two-calls", action="store_true",
@@ -789,7 +796,8 @@ def main():
         win, _ = run_decode(args.steps, args.warmup, "mistral-window", two_calls=two)
     inj = None if args.no_inject else run_inject(args.inject_reps)
     cow = None if args.no_cow else run_cow(args.cow_reps)
-    inj_host = None if args.no_host_store else run_inject_host(max(2, args.inject_reps // 3))
+    inj_host = None if args.no_host_store else run_inject_host(
+        max(2, args.inject_reps // 3), dma_compare=args.dma_compare)
     shapes = {}
     if not args.no_shapes and args.decode_workload == "70b":
         # the other decode shapes (one layer each; also timed with the last-level
@@ -905,7 +913,7 @@ def main():
             "dma_h2d_ceiling_gbps": round(inj_host["dma_gbps"], 2),
             "frac_of_dma_ceiling": round(inj_host["pcie_gbps"] / inj_host["dma_gbps"], 3),
             "store_gb": round(inj_host["store_gb"], 2),
-            "dma_per_run_ms": round(inj_host["dma_per_run_ms"], 2),
+            "dma_per_run_ms": _r4(inj_host["dma_per_run_ms"]),
             "dma_per_run_copies": inj_host["dma_per_run_copies"],
             "dma_per_run_meaning": "the same rows moved by the copy engine instead, one "
                                    "host-to-device copy per run, layer and K/V into a device "

@@ -262,3 +262,47 @@ def test_fp8_block_copy_carries_per_block_scales():
     src, dst = pairs[0]
     assert np.array_equal(k_ref[:, dst], ks[:, src]) and not np.array_equal(ks[:, dst], ks[:, src])
     pkv.pkv_cache_destroy(cache)
+
+
+@pytest.mark.parametrize("sdt", ["bf16", "f16"])
+def test_fp8_encoding_of_every_16bit_value(sdt):
+    """Every bf16 (or f16) bit pattern -- zeros, subnormals, values around
+    the E4M3 ties and the 448 saturation point, infinities, NaNs -- injected
+    unrotated into an fp8 pool with unit scales: the stored codes equal the
+    oracle's round-to-nearest-even, saturating encoding byte for byte."""
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    from oracle import inject as o_inject
+    from oracle.allocator import AllocatorModel
+    from oracle.rope import rope_table
+    from tests import gpu_util as gu
+
+    L, H, d = 1, 1, 64
+    n_tok = 65536 // (H * d)                      # 1,024 tokens hold every pattern once
+    NB = n_tok // 16
+    dp = gu.DevicePool(L, NB, H, d, "fp8", fill_bits=0x11)
+    ks = np.ones((L, H), np.float32)
+    dp.set_scales(ks, ks)
+    pat = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    src_k = pat.reshape(L, n_tok, H, d)
+    src_v = pat[::-1].copy().reshape(L, n_tok, H, d)
+    cache = pkv.pkv_cache_create(NB, 1, NB, free_list_seed=2)
+    model = AllocatorModel(NB, 1, NB, seed=2)
+    pkv.pkv_alloc_blocks(cache, 0, n_tok)
+    model.alloc_blocks(0, n_tok)
+    dk = gu.to_device_raw(src_k.reshape(-1), sdt)
+    dv = gu.to_device_raw(src_v.reshape(-1), sdt)
+    src = pkv.make_src(dk, dv, n_tok * H * d, H * d, n_tok, dtype=sdt)
+    runs = [(0, n_tok, 0, 0)]
+    ws = gu.workspace(pkv.pkv_inject_workspace_bytes(runs))
+    o_cos, o_sin = rope_table(d, 10000.0, n_tok)
+    _, _, dcos, dsin = gu.rope_tables(d, n_tok)
+    pkv.pkv_inject(cache, dp.desc(), src, runs, 0, L, "none", dcos, dsin, n_tok, ws)
+    torch.cuda.synchronize()
+    ref = np.full(dp.total, 0x11, dtype=np.uint8)
+    kp, vp = dp.oracle_arrays(ref)
+    o_inject.inject(kp, vp, dp.spec(), model.tables, [0], runs, src_k.reshape(-1),
+                    src_v.reshape(-1), n_tok * H * d, H * d, 0, L, "none", o_cos, o_sin,
+                    src_dtype=sdt, k_scale=ks, v_scale=ks)
+    gu.assert_bytes_equal(dp.host_copy(), ref, "fp8 codes of every %s value" % sdt)
+    pkv.pkv_cache_destroy(cache)
