@@ -82,3 +82,14 @@ def test_item_balance_load_model():
     assert sum(split["tokens_per_item_histogram"].values()) == split["items"]
     # every KV head of an item is one workgroup
     assert bench.item_balance([64] * 4, 1 << 20, 8, n_cus=256)["workgroups"] == 32
+
+
+def test_host_store_dma_comparison_is_opt_in():
+    """The per-run DMA comparison of the host-store workload runs only when
+    asked for (--dma-compare): the default bench run and the profiled runs
+    leave it out."""
+    import inspect
+    assert inspect.signature(bench.run_inject_host).parameters["dma_compare"].default is False
+    src = inspect.getsource(bench.main)
+    assert "dma_compare=args.dma_compare" in src
+    assert '"--dma-compare", action="store_true"' in src
