@@ -229,10 +229,13 @@ pkv_status pkv_set_blocks(pkv_cache* cache, int32_t seq, const int32_t* ids,
                           int32_t n_ids, int64_t len);
 
 /* Append n_new positions to each of seqs[n_seqs] (host, distinct), reserving
- * a block whenever a sequence crosses a 16-token boundary.  When the new
- * positions start inside a block the sequence shares, that block is copied
- * first (queued; see pkv_copy_blocks), sequences handled in list order.
- * All-or-nothing over the whole list (the copies count as reservations).
+ * a block whenever a sequence crosses a 16-token boundary.  Every block
+ * already in a sequence's table that will hold one of its new positions (the
+ * partly filled block at its length, and reserved blocks past it, which a
+ * fork shares as well) and that other sequences share is copied first
+ * (queued; see pkv_copy_blocks), sequences in list order, blocks in table
+ * order.  All-or-nothing over the whole list (the copies count as
+ * reservations).
  * first_pos_out (host, may be NULL) receives each sequence's first new
  * position (its old length).  Errors: INVALID, RANGE, OOM. */
 pkv_status pkv_extend(pkv_cache* cache, const int32_t* seqs, int32_t n_seqs,

@@ -33,7 +33,9 @@ exact match from position 0.  Readings taken:
 * ``fork(src, dst)`` gives an empty sequence the table and length of another
   (every block's count + 1), as beams and parallel samples share a prompt;
 * copy-on-write: before positions of a block whose count exceeds 1 are
-  written (by ``extend`` for the new positions, or by an inject), the writer
+  written (by ``extend`` for every block already in the table that holds one
+  of the new positions -- reserved blocks past the length included, since a
+  fork shares them too -- or by an inject), the writer
   takes a fresh block from the free list's head, the pair (old, new) is
   queued, the writer's table entry is replaced and the old block's count
   drops by one; queued copies take effect, in queue order, before any write;
@@ -214,8 +216,8 @@ class AllocatorModel:
             if want > self.max_blocks_per_seq:
                 raise AllocError("RANGE", "more blocks than a table row holds")
             total += max(0, want - len(self.tables[s]))
-            if n_new > 0 and self.lens[s] % self.bt:
-                b = self.tables[s][self.lens[s] // self.bt]
+            for i in self._written_entries(s, n_new):
+                b = self.tables[s][i]
                 r = refs.get(b, self.ref[b])     # count as it will be when s is reached
                 if r > 1:
                     total += 1
@@ -224,19 +226,26 @@ class AllocatorModel:
             raise AllocError("OOM", "pool exhausted")
         first = []
         for s in seqs:
-            if self._partial_shared(s, n_new):
-                self._cow(s, self.lens[s] // self.bt)
+            for i in self._written_entries(s, n_new):
+                if self.ref[self.tables[s][i]] > 1:
+                    self._cow(s, i)
             self.alloc_blocks(s, self.lens[s] + n_new)
             first.append(self.lens[s])
             self.lens[s] += n_new
         return first
 
-    def _partial_shared(self, s: int, n_new: int) -> bool:
-        """Will appending to ``s`` write into a block other sequences share?"""
-        ln = self.lens[s]
-        if n_new <= 0 or ln % self.bt == 0:
-            return False
-        return self.ref[self.tables[s][ln // self.bt]] > 1
+    def _written_entries(self, s: int, n_new: int):
+        """Table indices of the blocks ``s`` already holds that will receive
+        some of its next ``n_new`` positions: the block holding position len
+        (if the length is inside it) and any reserved blocks beyond it.  A
+        fork shares reserved blocks as well, so each of them may need a copy
+        before the write."""
+        if n_new <= 0:
+            return range(0)
+        t = self.tables[s]
+        lo = self.lens[s] // self.bt
+        hi = min(len(t), blocks_for(self.lens[s] + n_new, self.bt))
+        return [i for i in range(lo, hi) if t[i] >= 0]
 
     def set_len(self, seq: int, length: int):
         self._check_seq(seq)

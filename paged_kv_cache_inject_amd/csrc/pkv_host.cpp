@@ -233,6 +233,12 @@ struct pkv_cache {
     tables[seq][idx] = fresh;
     --ref[old];
   }
+  // One past the last table index, among the blocks seq already holds, that
+  // its next n_new positions reach (the first is lens[seq] / bt).
+  int64_t written_end(int32_t seq, int32_t n_new) const {
+    if (n_new <= 0) return 0;
+    return std::min<int64_t>(int64_t(tables[seq].size()), blocks_for(lens[seq] + n_new));
+  }
   // Drops one reference to each block of a table, in table order.
   void release(const std::vector<int32_t>& t) {
     for (int32_t b : t)
@@ -513,8 +519,10 @@ pkv_status pkv_extend(pkv_cache* c, const int32_t* seqs, int32_t n_seqs, int32_t
     if (want > c->max_blocks_per_seq)
       return fail(PKV_E_RANGE, "sequence %d would need %lld blocks", s, (long long)want);
     total += std::max<int64_t>(0, want - int64_t(c->tables[s].size()));
-    if (n_new > 0 && c->lens[s] % c->bt) {
-      const int32_t b = c->tables[s][c->lens[s] / c->bt];
+    const int64_t hi = c->written_end(s, n_new);
+    for (int64_t j = c->lens[s] / c->bt; j < hi; ++j) {
+      const int32_t b = c->tables[s][j];
+      if (b < 0) continue;
       auto it = refs_then.find(b);
       const int32_t r = it == refs_then.end() ? c->ref[b] : it->second;
       if (r > 1) {
@@ -527,9 +535,14 @@ pkv_status pkv_extend(pkv_cache* c, const int32_t* seqs, int32_t n_seqs, int32_t
     return fail(PKV_E_OOM, "need %lld blocks, %d free", (long long)total, c->fl_size);
   for (int32_t i = 0; i < n_seqs; ++i) {
     const int32_t s = seqs[i];
-    // The new positions start inside a block other sequences share: copy it.
-    if (n_new > 0 && c->lens[s] % c->bt && c->ref[c->tables[s][c->lens[s] / c->bt]] > 1)
-      c->cow(s, c->lens[s] / c->bt);
+    // Blocks already in the table that will receive new positions and that
+    // other sequences share (a fork shares reserved blocks past the length
+    // too): each is copied before the write.
+    const int64_t hi = c->written_end(s, n_new);
+    for (int64_t j = c->lens[s] / c->bt; j < hi; ++j) {
+      const int32_t b = c->tables[s][j];
+      if (b >= 0 && c->ref[b] > 1) c->cow(s, j);
+    }
     pkv_alloc_blocks(c, s, c->lens[s] + n_new);
     if (first_pos_out) first_pos_out[i] = c->lens[s];
     c->lens[s] += n_new;

@@ -171,9 +171,15 @@ def test_sharing_and_prefix_cache_match_oracle_on_random_operations(seed, bt):
     history = []                                   # key lists committed so far
     counts = dict(fork=0, cow=0, hit=0)
     for step in range(600):
-        op = int(rng.integers(0, 7))
+        op = int(rng.integers(0, 8))
         s = int(rng.integers(0, ns))
-        if op == 6:
+        if op == 7:
+            # capacity past the length, which a later fork shares
+            n = m.lens[s] + int(rng.choice([1, 16, 40]))
+            ec, em, _, _ = _both(lambda: pkv.pkv_alloc_blocks(c, s, n),
+                                 lambda: m.alloc_blocks(s, n))
+            counts["reserve"] = counts.get("reserve", 0) + (ec is None)
+        elif op == 6:
             w = int(rng.choice([1, 10, 40]))
             ec, em, rc, rm = _both(lambda: pkv.pkv_trim_window(c, [s], w),
                                    lambda: m.trim_window([s], w))
@@ -225,8 +231,31 @@ def test_sharing_and_prefix_cache_match_oracle_on_random_operations(seed, bt):
         assert pkv.pkv_prefix_cached_blocks(c) == len(m.entries), step
         m.check_invariants()
     counts["cow"] = len(m.pending)
-    assert counts["fork"] > 30 and counts["hit"] > (4 if bt == 16 else 1) and counts["cow"] > 8, counts
-    assert counts.get("trim", 0) > 10, counts
+    assert counts["fork"] > 30 and counts["hit"] > (2 if bt == 16 else 1) and counts["cow"] > 8, counts
+    assert counts.get("reserve", 0) > 30, counts
+    assert counts.get("trim", 0) > 5, counts
+    pkv.pkv_cache_destroy(c)
+
+
+@pytest.mark.parametrize("length,n_new", [(32, 1), (30, 5), (48, 20)])
+def test_extend_copies_reserved_shared_blocks_through_the_abi(length, n_new):
+    """After a fork the sharers' reserved blocks past the length are shared
+    too; extending both must leave each new position in a block of its own
+    sequence (entries differ, count 1), as the oracle model says."""
+    c = pkv.pkv_cache_create(16, 4, 8)
+    m = AllocatorModel(16, 4, 8)
+    for f in (lambda: pkv.pkv_set_blocks(c, 0, [3, 5, 7, 9], length),
+              lambda: m.set_blocks(0, [3, 5, 7, 9], length)):
+        f()
+    pkv.pkv_fork(c, 0, 1)
+    m.fork(0, 1)
+    assert list(pkv.pkv_extend(c, [0, 1], n_new)) == m.extend([0, 1], n_new)
+    table, _ = pkv.pkv_block_table(c, [0, 1])
+    for i in range(length // 16, -(-(length + n_new) // 16)):
+        a, b = int(table[0][i]), int(table[1][i])
+        assert a != b and pkv.pkv_block_refcount(c, a) == 1 and pkv.pkv_block_refcount(c, b) == 1
+    assert pkv.pkv_pending_copies(c) == m.pending
+    assert _unpad(table[0]) == m.tables[0] and _unpad(table[1]) == m.tables[1]
     pkv.pkv_cache_destroy(c)
 
 

@@ -258,6 +258,42 @@ def test_extend_by_all_sharers_needs_one_copy_fewer():
     sh.check()
 
 
+@pytest.mark.parametrize("length,n_new", [(32, 1), (30, 5), (48, 20)])
+def test_extend_copies_reserved_blocks_a_fork_shares(length, n_new):
+    """A fork shares every block of the table, reserved blocks past the
+    length included.  When both sharers then extend, every shared block that
+    receives new positions is copied for the first of them, so that after
+    the extend each sequence writes only blocks it alone names ([KV essay]
+    "Paged attention": a shared block is duplicated before a write)."""
+    m = AllocatorModel(16, 4, 8)
+    m.set_blocks(0, [3, 5, 7, 9], length)
+    m.fork(0, 1)
+    m.extend([0, 1], n_new)
+    touched = range(length // 16, -(-(length + n_new) // 16))
+    for i in touched:
+        assert m.tables[0][i] != m.tables[1][i], (i, m.tables)
+        assert m.ref[m.tables[0][i]] == 1 and m.ref[m.tables[1][i]] == 1, (i, m.ref)
+    # only the touched blocks that existed were copied, oldest first, all by seq 0
+    existing = [i for i in touched if i < 4]
+    assert [src for src, _ in m.pending] == [[3, 5, 7, 9][i] for i in existing]
+    for i in range(length // 16):               # untouched blocks stay shared
+        assert m.tables[0][i] == m.tables[1][i] and m.ref[m.tables[0][i]] == 2
+
+
+def test_extend_shared_reserved_block_needs_a_free_block_or_fails_whole():
+    """The copies of reserved shared blocks count toward the all-or-nothing
+    reservation: with no free block left, the extend fails and changes
+    nothing."""
+    m = AllocatorModel(4, 2, 4)
+    m.set_blocks(0, [0, 1, 2, 3], 32)
+    m.fork(0, 1)
+    before = ([list(t) for t in m.tables], list(m.lens), list(m.ref))
+    with pytest.raises(AllocError) as e:
+        m.extend([0], 1)
+    assert e.value.code == "OOM"
+    assert ([list(t) for t in m.tables], list(m.lens), list(m.ref)) == before
+
+
 def test_errors_leave_the_state_unchanged():
     m = AllocatorModel(4, 3, 4)
     m.extend([0], 40)
@@ -337,7 +373,7 @@ def test_queued_copies_act_one_after_another():
 @pytest.mark.parametrize("bt", [16, 32])
 def test_brute_force_random_operations_against_slot_contents(bt):
     rng = random.Random(2024 + bt)
-    hits = copies = 0
+    hits = copies = reserved = 0
     for trial in range(600):
         nb, ns = rng.choice([(6, 3), (10, 4), (24, 5)])
         m = AllocatorModel(nb, ns, 6, seed=rng.choice([0, 7, 99]), block_tokens=bt)
@@ -347,7 +383,7 @@ def test_brute_force_random_operations_against_slot_contents(bt):
         for _ in range(30):
             tag += 1
             op = rng.choice(["extend", "extend", "fork", "free", "inject", "match", "match",
-                             "commit", "commit"])
+                             "commit", "commit", "reserve"])
             s = rng.randrange(ns)
             try:
                 if op == "extend":
@@ -356,6 +392,11 @@ def test_brute_force_random_operations_against_slot_contents(bt):
                     sh.extend(seqs, [keys_of(tag * 8 + i, n) for i in range(len(seqs))])
                 elif op == "fork":
                     sh.fork(s, rng.randrange(ns))
+                elif op == "reserve":
+                    # capacity beyond the length: a later fork shares these
+                    # blocks before anything is written to them
+                    m.alloc_blocks(s, m.lens[s] + rng.choice([1, 16, 40]))
+                    reserved += 1
                 elif op == "free":
                     sh.free(s)
                 elif op == "inject" and m.lens[s] > 0:
@@ -377,4 +418,4 @@ def test_brute_force_random_operations_against_slot_contents(bt):
                 pass
             sh.check()
         copies += sh.copies
-    assert hits > 120 and copies > 150, (hits, copies)
+    assert hits > 60 and copies > 150 and reserved > 500, (hits, copies, reserved)
