@@ -286,9 +286,9 @@ int32_t pkv_pending_copies(const pkv_cache* cache, int32_t* pairs_out, int32_t c
  * order suffices).  Errors: INVALID, RANGE (an id outside the pool), HIP. */
 pkv_status pkv_copy_blocks(pkv_cache* cache, const pkv_pool* pool, void* stream);
 
-/* Prefix cache ([KV essay] "Prefix caching"; [KV management]: serving systems
- * hash the prefix to find matching entries, and a match must be exact from
- * position 0).  The caller names what each position holds by a 64-bit key
+/* Prefix cache ([KV essay] "Prefix caching"; [KV management]: engines look
+ * prefixes up by a hash, and reuse needs identical tokens from position 0
+ * on).  The caller names what each position holds by a 64-bit key
  * (a token id of a prompt, or the store row of injected memory).  A full
  * block is registered under (the block registered for the preceding 16
  * positions, or -1 at position 0; its 16 keys), compared exactly.  An entry
@@ -316,8 +316,8 @@ pkv_status pkv_prefix_commit(pkv_cache* cache, int32_t seq, const uint64_t* keys
 int32_t pkv_prefix_cached_blocks(const pkv_cache* cache);
 
 /* Sliding window ([KV essay] "Capping the window instead of shrinking the
- * rows": older entries fall out of the cache, which stops growing once the
- * window fills).  For each of seqs[n_seqs] (host), drop the references to
+ * rows": entries older than the window can be discarded, so the cache's size
+ * is bounded by the window).  For each of seqs[n_seqs] (host), drop the references to
  * the blocks lying wholly before its last `window` positions, in table order
  * (blocks reaching count 0 join the free list's tail); their table entries
  * become -1.  Lengths and positions are unchanged; writing a dropped position
@@ -403,7 +403,7 @@ pkv_status pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* d_t
  * reads KV head h / (n_q_heads / n_kv_heads)).  Sequence b attends to its
  * lens[b] cached tokens (positions 0 .. lens[b]-1, no mask), or, under a
  * sliding window (window > 0; [KV essay] "Capping the window instead of
- * shrinking the rows": a token attends only to the last W tokens), to
+ * shrinking the rows": attention covers a trailing span of W positions), to
  * positions max(0, lens[b] - window) .. lens[b]-1; blocks before those
  * positions are never read, so a table trimmed by pkv_trim_window with a
  * window >= this one decodes the same.

@@ -3,8 +3,8 @@
 [KV essay] "Paged attention" gives the structure: a shared pool of fixed
 blocks, a free list, a per-sequence block table, and a new block handed out
 only when a sequence reaches it (so only the last block is partly empty).
-[Inside engines] "PagedAttention" repeats on-demand allocation when the
-current 16-token block fills; "Continuous Batching" returns a finished
+[Inside engines] "PagedAttention" likewise allocates a further block only
+once the sequence has filled the 16 tokens of its last one; "Continuous Batching" returns a finished
 sequence's blocks to the pool at once.
 
 The pages print a free list but not the order in which it is consumed.  The
@@ -51,8 +51,9 @@ exact match from position 0.  Readings taken:
   together with every entry registered under it.
 
 Sliding window ([KV essay] "Capping the window instead of shrinking the
-rows": a token attends only to the last W tokens, older entries fall out of
-the cache, which stops growing once the window fills): ``trim_window``
+rows": attention is limited to a trailing span of W positions, so entries
+older than that span can be discarded and the cache's size is bounded by W
+rather than by the conversation): ``trim_window``
 drops a sequence's references to the blocks that lie wholly before its last
 W positions (table order), leaving -1 in their table entries; positions and
 capacity keep counting from 0.

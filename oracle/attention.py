@@ -19,8 +19,8 @@ Readings taken:
 * an fp8 cache holds codes whose values are e4m3(code) times the float32
   scale of their (layer, KV head), or of their (layer, block, KV head) when
   the scales are given per block; the query then comes in a 16-bit format;
-* with a sliding window W ([KV essay] "Capping the window": a token
-  attends only to the last W tokens), the query of a sequence of length n
+* with a sliding window W ([KV essay] "Capping the window": attention
+  covers a trailing span of W positions), the query of a sequence of length n
   attends to positions max(0, n - W) .. n-1 only;
 * besides ``out`` the log-sum-exp ``lse = m + ln(sum exp(s - m))`` of the
   scaled scores is returned; a sequence of length 0 gives out = 0 and

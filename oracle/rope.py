@@ -1,11 +1,11 @@
 """Rotary position embedding at a destination position (oracle; test infra).
 
-[InferScale] §2 (background on positional encoding): RoPE rotates a query or
-key at position p by a fixed block-diagonal rotation R_p, and because
+[InferScale] §2 (background on positional encoding): RoPE multiplies a query
+or key at position p by R_p, a rotation made of 2x2 blocks, and because
 R_a^T R_b = R_{b-a} the score of a key rotated to b against a query rotated
-to a depends only on b - a.  [InferScale] §3.3 and §5.1: keys are stored
-before rotation and rotated, with the model's own rotary tables, at whatever
-position the request assigns.
+to a depends only on b - a.  [InferScale] §3.3 and §5.1: the stored keys
+carry no rotation; they are rotated only when composition gives them a
+position, with the same cos/sin tables the model uses.
 
 The pages name RoFormer (Su et al.) and nothing more precise.  Readings taken:
 

@@ -142,6 +142,44 @@ def test_plane_offsets_are_bijections(dtype, d):
     assert np.all(np.diff(v_plane_offset(np.arange(16), 5)) == 1)
 
 
+def _plane_cases():
+    import json
+    import os
+    from tests.conftest import GOLDEN
+    with open(os.path.join(GOLDEN, "plane_offsets.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _plane_cases(), ids=lambda c: "%s-t%d-j%d" % (c["dtype"], c["t"], c["j"]))
+def test_plane_offsets_equal_hand_worked_values(case):
+    """The oracle's in-plane offsets against values worked by hand from the
+    layout the C header states (tests/golden/plane_offsets.json)."""
+    assert int(k_plane_offset(case["t"], case["j"], case["dtype"])) == case["k"], case["work"]
+    assert int(v_plane_offset(case["t"], case["j"])) == case["v"], case["work"]
+
+
+def test_plane_offset_pins_reject_plausible_other_layouts():
+    """Each plausible misreading of the layout disagrees with some hand-worked
+    value: a token-major K plane (all dims of token t together), chunks of the
+    wrong width, or a token-major V plane."""
+    cases = _plane_cases()
+    x = {"f32": 4, "bf16": 8, "f16": 8, "fp8": 16}
+    d_of = {"f32": 64, "bf16": 128, "f16": 64, "fp8": 128}
+
+    def token_major_k(t, j, dt):
+        return t * d_of[dt] + j
+
+    def wrong_chunk_k(t, j, dt):               # chunks of 8 dims whatever the element size
+        return ((j // 8) * 16 + t) * 8 + j % 8
+
+    def token_major_v(t, j, dt):
+        return t * d_of[dt] + j
+
+    for name, fk in (("token-major K", token_major_k), ("8-dim chunks", wrong_chunk_k)):
+        assert any(fk(c["t"], c["j"], c["dtype"]) != c["k"] for c in cases), name
+    assert any(token_major_v(c["t"], c["j"], c["dtype"]) != c["v"] for c in cases)
+
+
 def test_paged_gather_equals_contiguous_under_any_permutation():
     spec = PoolSpec(2, 12, 2, 64, "bf16").resolved()
     rng = np.random.default_rng(3)

@@ -6,10 +6,12 @@ Worked cases come from the pages' own descriptions:
   block is duplicated only when one of them writes;
 * [KV management]: beams share the prompt's pages until they diverge, and
   only pages holding positions where they differ are copied;
-* [KV essay] "Prefix caching": a cached prefix needs an exact match from
-  position 0 (a timestamp at the start defeats it, at the end it does not),
-  and reuse reaches up to the first point of divergence; an entry lasts until
-  the allocator needs the space.
+* [KV essay] "Prefix caching": reuse requires the new request to agree with
+  the cached tokens from position 0 on (a value that changes at the very
+  start, such as a timestamp, leaves nothing reusable, while the same value
+  at the end keeps everything before it reusable); reuse covers the positions
+  before the first difference, and an entry survives until its space is
+  reallocated.
 A brute-force test runs random operation sequences against a shadow model
 that tracks what every physical slot holds, so a missing or misplaced copy
 shows up as a sequence reading something it never wrote.
@@ -162,7 +164,7 @@ def test_prefix_match_needs_an_exact_match_from_position_zero():
     sh.check()
 
 
-def test_cached_entry_lasts_until_the_allocator_needs_the_space():
+def test_cached_entry_survives_until_its_block_is_reallocated():
     m = AllocatorModel(8, 4, 8)
     sh = Shadow(m)
     prompt = keys_of(7, 48)

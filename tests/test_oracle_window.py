@@ -1,7 +1,7 @@
 """Pins the oracle's sliding window ([KV essay] "Capping the window instead
-of shrinking the rows"): a token attends only to the last W tokens, older
-entries fall out of the cache, the cache stops growing once the window
-fills, and a 32K context with a 4096-token window needs an eighth of the
+of shrinking the rows"): attention covers a trailing span of W positions,
+entries older than the span can be dropped, the cache's size is then
+bounded by W, and a 32K context with a 4096-token window needs an eighth of the
 memory (0.5 GB instead of 4 GB for the Mistral-7B shape the page prices)."""
 import math
 
@@ -97,7 +97,7 @@ def test_trim_keeps_exactly_the_window_mistral_numbers():
     m.check_invariants()
 
 
-def test_cache_stops_growing_once_the_window_fills():
+def test_cache_size_is_bounded_by_the_window():
     W = 50
     m = AllocatorModel(64, 2, 64)
     held = []
