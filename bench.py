@@ -545,7 +545,12 @@ def run_inject_host(reps, n_chunks=250, batch=16, dma_compare=False):
     """The injection workload with the chunk store in pinned host memory
     ([InferScale] §6): 16 requests compose the prefix and top-8 of 250 chunks;
     the inject kernel reads only the runs' rows, over PCIe, while it writes the
-    pool.  Reported against the same run's host-to-device DMA ceiling."""
+    pool.  Reported against the same run's host-to-device DMA ceiling.
+
+    The K and V stores are torch tensors allocated with pin_memory=True, so
+    every torch copy into or out of them goes through torch's own
+    pinned-memory path; the inject call reads them through their pinned
+    addresses."""
     import torch
     import paged_kv_cache_inject_amd as pkv
     from workloads.configs import INJECT_TOP8, inject_structure, device_normal
@@ -553,18 +558,21 @@ def run_inject_host(reps, n_chunks=250, batch=16, dma_compare=False):
     st = inject_structure(cfg, n_chunks=n_chunks, batch=batch)
     L, H, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
     n_src, row = st["n_src"], H * d
-    nbytes = L * n_src * row * 2
+    nbytes = L * n_src * row * 2                       # one of K, V
     log("inject (host store): %d tokens x %d layers in pinned host memory (%.1f GB)"
         % (n_src, L, 2 * nbytes / 1e9))
-    hk, hv = pkv.pkv_host_alloc(nbytes), pkv.pkv_host_alloc(nbytes)
+    stores = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+    assert all(t.is_pinned() and t.numel() == nbytes for t in stores)
     try:
-        for base, salt in ((hk, 0), (hv, 1)):
-            view = pkv.host_view(base, nbytes)
+        for salt, store in enumerate(stores):
             for layer in range(L):
-                a, b = layer * n_src * row * 2, (layer + 1) * n_src * row * 2
+                a = layer * n_src * row * 2
+                b = a + n_src * row * 2
+                assert 0 <= a < b <= store.numel()
                 t = device_normal(n_src * row, "bf16", cfg.seed * 1000 + 2 * layer + salt)
-                torch.from_numpy(view[a:b]).copy_(t.view(torch.uint8))
+                store[a:b].copy_(t.view(torch.uint8))
                 del t
+        log("inject (host store): store filled")
         # DMA ceiling: 1 GiB pinned -> device
         pin = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
         dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -585,10 +593,13 @@ def run_inject_host(reps, n_chunks=250, batch=16, dma_compare=False):
         max_pos = 4096
         cos, sin = pkv.pkv_rope_table(d, cfg.rope_base, max_pos)
         dcos, dsin = torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda()
-        src = pkv.make_src(hk, hv, n_src * row, row, n_src, dtype="bf16")
+        src = pkv.make_src(stores[0].data_ptr(), stores[1].data_ptr(), n_src * row, row, n_src,
+                           dtype="bf16")
         runs = pkv.make_runs(st["runs"])
         ws = torch.empty(pkv.pkv_inject_workspace_bytes(runs), dtype=torch.uint8, device="cuda")
         n_tok = int(sum(r[1] for r in st["runs"]))
+        for (_seq, n, _dst, src_tok) in st["runs"]:
+            assert 0 <= src_tok and src_tok + n <= n_src
 
         def once():
             pkv.pkv_inject(cache, pool, src, runs, 0, L, "pairs", dcos, dsin, max_pos, ws)
@@ -603,32 +614,33 @@ def run_inject_host(reps, n_chunks=250, batch=16, dma_compare=False):
         ms = s.elapsed_time(e) / reps
         src_bytes = n_tok * L * row * 2 * 2            # K and V rows read over PCIe
         # The alternative: a copy engine moves each run's rows (one
-        # host-to-device copy per run, layer and K/V) into a device staging
-        # buffer for the kernel to scatter from.  Only the copies are timed.
+        # host-to-device copy per run, layer and K/V) from the same pinned
+        # store into a device staging buffer for the kernel to scatter from.
+        # Only the copies are timed.
         dma_runs_ms = None
-        staging = torch.empty(n_tok * row * 2 if dma_compare else 16, dtype=torch.uint8,
-                              device="cuda")
-        hk_view = torch.from_numpy(pkv.host_view(hk, nbytes))
-        hv_view = torch.from_numpy(pkv.host_view(hv, nbytes))
-
-        def copies():
-            for layer in range(L):
-                at = 0
-                for (_seq, n, _dst, src_tok) in st["runs"]:
-                    a = (layer * n_src + src_tok) * row * 2
-                    for hview in (hk_view, hv_view):
-                        staging[at * row * 2:(at + n) * row * 2].copy_(
-                            hview[a:a + n * row * 2], non_blocking=True)
-                    at += n
-
         if dma_compare:
+            staging = torch.empty(n_tok * row * 2, dtype=torch.uint8, device="cuda")
+
+            def copies():
+                for layer in range(L):
+                    at = 0
+                    for (_seq, n, _dst, src_tok) in st["runs"]:
+                        nb_ = n * row * 2
+                        assert (at + n) * row * 2 <= staging.numel()
+                        for store in stores:
+                            a = (layer * n_src + src_tok) * row * 2
+                            assert a + nb_ <= nbytes
+                            staging[at * row * 2:at * row * 2 + nb_].copy_(store[a:a + nb_],
+                                                                           non_blocking=True)
+                        at += n
+
             copies()
             torch.cuda.synchronize()
             w0 = time.perf_counter()
             copies()
             torch.cuda.synchronize()
             dma_runs_ms = (time.perf_counter() - w0) * 1e3
-        del staging
+            del staging
         res = dict(ms_per_call=ms, tokens=n_tok, requests=batch, layers=L,
                    tokens_per_s=n_tok / (ms * 1e-3), pcie_gbps=src_bytes / (ms * 1e-3) / 1e9,
                    dma_gbps=dma_gbps, src_bytes=src_bytes, store_gb=2 * nbytes / 1e9,
@@ -639,8 +651,7 @@ def run_inject_host(reps, n_chunks=250, batch=16, dma_compare=False):
         del buf, ws
     finally:
         torch.cuda.synchronize()
-        pkv.pkv_host_free(hk)
-        pkv.pkv_host_free(hv)
+        del stores
     torch.cuda.empty_cache()
     return res
 
@@ -756,8 +767,7 @@ def main():
     ap.add_argument("--cow-reps", type=int, default=10)
     ap.add_argument("--dma-compare", action="store_true",
                     help="also time moving the host store's run rows by one copy per run "
-                         "(off by default: it ended in a host segfault under counter "
-                         "collection, cause not shown)")
+                         "(17,408 copies; off by default to keep the run short)")
     ap.add_argument("--no-shapes", action="store_true",
                     help="skip the 8B-shaped and ragged-MHA decode figures")
     ap.add_argument("--no-two-calls", action="store_true",

@@ -101,8 +101,14 @@ def test_reduced_workload_host_store_equals_device_store():
     nbytes = dev_k.numel() * 2
     hk, hv = pkv.pkv_host_alloc(nbytes), pkv.pkv_host_alloc(nbytes)
     try:
-        torch.from_numpy(pkv.host_view(hk, nbytes)).copy_(dev_k.view(torch.uint8))
-        torch.from_numpy(pkv.host_view(hv, nbytes)).copy_(dev_v.view(torch.uint8))
+        # device -> torch-owned host tensor, then a plain host copy into the
+        # library's pinned buffers (torch never copies into memory it did not
+        # allocate)
+        for addr, t in ((hk, dev_k), (hv, dev_v)):
+            host = t.view(torch.uint8).cpu().numpy()
+            assert host.nbytes == nbytes
+            pkv.host_view(addr, nbytes)[:] = host
+            del host
         max_pos = 4096
         _, _, dcos, dsin = gu.rope_tables(d, max_pos)
         pools = []
