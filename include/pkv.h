@@ -485,6 +485,36 @@ pkv_status pkv_append_decode_attention(const pkv_plan* plan, const pkv_pool* poo
                                        float* d_lse, void* d_ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The decode step without any allocation, for callers that cannot allocate
+ * device or pinned memory at the call: code being captured into a HIP graph,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * checks, results and stream behaviour as pkv_append_decode_attention, except
+ * that there is no workspace argument and no separate plan upload: the
+ * plan's work list (24 bytes per item, 16 per split sequence) is copied from
+ * the plan's host memory into a static device scratch buffer on `stream`,
+ * and the kernels use that buffer for the work list and the partial states
+ * of split sequences.  The scratch holds PKV_NOALLOC_SCRATCH_BYTES (16 MiB)
+ * per device, reserved on each device the library runs on until the process
+ * ends; a plan whose pkv_decode_workspace_bytes exceeds it is refused with
+ * PKV_E_WORKSPACE before anything is enqueued.  The call makes no device or
+ * pinned-host allocation and no library allocation (pkv_kernel_timing does
+ * not apply to it).  Every call on one device shares that device's scratch:
+ * calls on one device that overlap in time (different streams, or host
+ * threads) race on it, so order them on one stream.  Nothing in the scratch
+ * needs clearing between calls: each call rewrites the work list, and every
+ * partial state is written before it is read.
+ * ------------------------------------------------------------------------- */
+#define PKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+pkv_status pkv_append_decode_attention_noalloc(const pkv_plan* plan, const pkv_pool* pool,
+                                               int32_t layer, const void* d_q, int32_t q_dtype,
+                                               float scale, const int32_t* d_tables,
+                                               int32_t table_stride, const void* d_k_new,
+                                               const void* d_v_new, int32_t rope_mode,
+                                               const float* d_cos, const float* d_sin,
+                                               int32_t max_pos, float* d_out, float* d_lse,
+                                               void* stream);
+
+/* ---------------------------------------------------------------------------
  * Measurement helper: kernel durations from the dispatches themselves.
  * pkv_kernel_timing(1) makes every following decode launch on the calling
  * thread (pkv_decode_attention, pkv_append_decode_attention; the attention

@@ -31,6 +31,7 @@ DTYPE_CODES = {"f32": PKV_F32, "bf16": PKV_BF16, "f16": PKV_F16, "fp8": PKV_FP8E
 PKV_ROPE_PAIRS, PKV_ROPE_HALVES, PKV_ROPE_NONE = 0, 1, 2
 ROPE_CODES = {"pairs": PKV_ROPE_PAIRS, "halves": PKV_ROPE_HALVES, "none": PKV_ROPE_NONE}
 BLOCK_TOKENS = 16
+PKV_NOALLOC_SCRATCH_BYTES = 16 << 20     # static scratch of the allocation-free step
 
 
 class PkvError(RuntimeError):
@@ -118,6 +119,9 @@ SIGNATURES = {
     "pkv_append_decode_attention": (_I32, [_P, ctypes.POINTER(pkv_pool), _I32, _P, _I32,
                                            ctypes.c_float, _P, _I32, _P, _P, _I32, _P, _P, _I32,
                                            _P, _P, _P, _SZ, _P]),
+    "pkv_append_decode_attention_noalloc": (_I32, [_P, ctypes.POINTER(pkv_pool), _I32, _P, _I32,
+                                                   ctypes.c_float, _P, _I32, _P, _P, _I32, _P, _P,
+                                                   _I32, _P, _P, _P]),
     "pkv_bw_probe": (_I32, [_P, _SZ, _P, _P]),
     "pkv_kernel_timing": (_I32, [_I32]),
     "pkv_kernel_times": (_I32, [_P, _I32]),
@@ -467,6 +471,18 @@ def pkv_append_decode_attention(plan, pool: pkv_pool, layer, q, tables, k_new, v
         _ptr(k_new), _ptr(v_new), ROPE_CODES.get(rope_mode, rope_mode), _ptr(cos), _ptr(sin),
         max_pos, _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def pkv_append_decode_attention_noalloc(plan, pool: pkv_pool, layer, q, tables, k_new, v_new,
+                                        rope_mode, cos, sin, max_pos, out, lse, scale=0.0,
+                                        stream=None, q_dtype=None):
+    """The decode step with the library's static device scratch as its
+    workspace (no workspace argument, no plan upload)."""
+    qd = DTYPE_CODES[q_dtype] if isinstance(q_dtype, str) else _dtype_of(q, pool.dtype)
+    _check(load_library().pkv_append_decode_attention_noalloc(
+        plan, ctypes.byref(pool), layer, _ptr(q), qd, float(scale), _ptr(tables), tables.shape[1],
+        _ptr(k_new), _ptr(v_new), ROPE_CODES.get(rope_mode, rope_mode), _ptr(cos), _ptr(sin),
+        max_pos, _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def pkv_kernel_timing(enable: bool):

@@ -1125,10 +1125,13 @@ struct NewToken {
   int32_t max_pos = 0;
 };
 
+// upload_plan: the workspace is the library's static scratch, and the plan's
+// work list is copied into it on `stream` before the launch (the
+// allocation-free entry point); otherwise the caller uploaded the plan.
 pkv_status decode_common(const pkv_plan* plan, const pkv_pool* pool, int32_t layer,
                          const void* d_q, int32_t q_dtype, float scale, const int32_t* d_tables,
                          int32_t table_stride, const NewToken& nt, float* d_out, float* d_lse,
-                         void* d_ws, size_t ws_bytes, void* stream) {
+                         void* d_ws, size_t ws_bytes, void* stream, bool upload_plan = false) {
   if (!plan) return fail(PKV_E_INVALID, "null plan");
   if (pkv_status st = check_pool(pool)) return st;
   if (pkv_status st = check_input_dtype(pool, q_dtype, "q")) return st;
@@ -1188,9 +1191,22 @@ pkv_status decode_common(const pkv_plan* plan, const pkv_pool* pool, int32_t lay
   a.cos_t = nt.cos;
   a.sin_t = nt.sin;
   a.max_pos = nt.max_pos;
+  a.timed = !upload_plan;
   int variant = 0;
   if (const char* env = std::getenv("PKV_DECODE_KERNEL")) variant = std::atoi(env);
-  hipError_t e = pkv::launch_decode(*pool, layer, a, variant, static_cast<hipStream_t>(stream));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (upload_plan) {
+    // from the plan's own host memory: the runtime stages these small copies
+    hipError_t e = hipSuccess;
+    if (!plan->items.empty())
+      e = hipMemcpyAsync(ws + plan->off_items, plan->items.data(),
+                         plan->items.size() * sizeof(DecodeItem), hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess && !plan->merges.empty())
+      e = hipMemcpyAsync(ws + plan->off_merges, plan->merges.data(),
+                         plan->merges.size() * sizeof(MergeSeq), hipMemcpyHostToDevice, hs);
+    if (e != hipSuccess) return hip_fail(e, "work list copy into the static scratch");
+  }
+  hipError_t e = pkv::launch_decode(*pool, layer, a, variant, hs);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
 }
@@ -1224,6 +1240,35 @@ pkv_status pkv_append_decode_attention(const pkv_plan* plan, const pkv_pool* poo
   nt.max_pos = max_pos;
   return decode_common(plan, pool, layer, d_q, q_dtype, scale, d_tables, table_stride, nt, d_out,
                        d_lse, d_ws, ws_bytes, stream);
+}
+
+pkv_status pkv_append_decode_attention_noalloc(const pkv_plan* plan, const pkv_pool* pool,
+                                               int32_t layer, const void* d_q, int32_t q_dtype,
+                                               float scale, const int32_t* d_tables,
+                                               int32_t table_stride, const void* d_k_new,
+                                               const void* d_v_new, int32_t rope_mode,
+                                               const float* d_cos, const float* d_sin,
+                                               int32_t max_pos, float* d_out, float* d_lse,
+                                               void* stream) {
+  if (!plan) return fail(PKV_E_INVALID, "null plan");
+  if (plan->ws_bytes > pkv::kScratchBytes)
+    return fail(PKV_E_WORKSPACE,
+                "the plan needs %zu bytes of workspace, more than the %zu-byte static scratch "
+                "of the allocation-free call; use pkv_append_decode_attention with a workspace",
+                plan->ws_bytes, pkv::kScratchBytes);
+  if (!d_k_new || !d_v_new) return fail(PKV_E_INVALID, "null k_new or v_new");
+  void* ws = nullptr;
+  const hipError_t e = pkv::scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e, "address of the static scratch");
+  NewToken nt;
+  nt.k = d_k_new;
+  nt.v = d_v_new;
+  nt.rope_mode = rope_mode;
+  nt.cos = d_cos;
+  nt.sin = d_sin;
+  nt.max_pos = max_pos;
+  return decode_common(plan, pool, layer, d_q, q_dtype, scale, d_tables, table_stride, nt, d_out,
+                       d_lse, ws, pkv::kScratchBytes, stream, true);
 }
 
 pkv_status pkv_kernel_timing(int32_t enable) {

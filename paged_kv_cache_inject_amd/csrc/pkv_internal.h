@@ -78,6 +78,8 @@ struct DecodeArgs {
   const float* cos_t;
   const float* sin_t;
   int max_pos;
+  // false: never attach timing events (the allocation-free entry point)
+  bool timed;
 };
 
 // kernel_variant: 0 = automatic, 1 = force the generic VALU kernel.
@@ -85,6 +87,14 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
                          int kernel_variant, hipStream_t stream);
 
 hipError_t launch_bw_probe(const void* src, size_t n_bytes, void* sink, hipStream_t stream);
+
+// Workspace of the allocation-free decode step: a file-scope device array of
+// kScratchBytes in pkv_kernels.hip, one copy per device.
+constexpr size_t kScratchBytes = size_t(PKV_NOALLOC_SCRATCH_BYTES);
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+// Device address of the current device's copy, looked up (hipGetSymbolAddress)
+// on the first call per device and kept; never the array's host-side name.
+hipError_t scratch_address(void** out);
 
 // Measurement: dispatch-attached timing of this thread's decode launches.
 void set_kernel_timing(bool on);

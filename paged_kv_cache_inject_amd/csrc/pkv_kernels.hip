@@ -40,11 +40,18 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 #include <vector>
 
 #include "pkv_internal.h"
+
+// Workspace of pkv_append_decode_attention_noalloc (work list, merge list,
+// partial softmax states of split sequences).  Each device the library runs
+// on holds its own copy until the process ends.  Host code never uses this
+// name as an address: pkv::scratch_address() gives the device address.
+static __device__ __align__(256) unsigned char scratch[pkv::kScratchBytes];
 
 namespace pkv {
 namespace {
@@ -1392,8 +1399,8 @@ thread_local KernelTiming g_timing;
 
 template <typename K, typename... A>
 hipError_t launch_decode_kernel(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
-                                A... args) {
-  if (!g_timing.on) {
+                                bool timed, A... args) {
+  if (!g_timing.on || !timed) {
     hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
     return hipGetLastError();
   }
@@ -1647,19 +1654,19 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
       if (put && blk) {                                                                      \
         constexpr auto k = decode_mfma_kernel<KV, Q, DD, DEP, W, G, DEP == 1, B8>;           \
         e = launch_decode_kernel(k, grid, dim3(64 * W), one_per_cu ? one_per_cu_lds<k>() : 0, \
-                                 stream, p, p.tables);                                       \
+                                 stream, a.timed, p, p.tables);                              \
       } else if (put) {                                                                      \
         constexpr auto k = decode_mfma_kernel<KV, Q, DD, DEP, W, G, DEP == 1, false>;        \
         e = launch_decode_kernel(k, grid, dim3(64 * W), one_per_cu ? one_per_cu_lds<k>() : 0, \
-                                 stream, p, p.tables);                                       \
+                                 stream, a.timed, p, p.tables);                              \
       } else if (blk) {                                                                      \
         constexpr auto k = decode_mfma_kernel<KV, Q, DD, DEP, W, G, false, B8>;              \
         e = launch_decode_kernel(k, grid, dim3(64 * W), one_per_cu ? one_per_cu_lds<k>() : 0, \
-                                 stream, p, p.tables);                                       \
+                                 stream, a.timed, p, p.tables);                              \
       } else {                                                                               \
         constexpr auto k = decode_mfma_kernel<KV, Q, DD, DEP, W, G, false, false>;           \
         e = launch_decode_kernel(k, grid, dim3(64 * W), one_per_cu ? one_per_cu_lds<k>() : 0, \
-                                 stream, p, p.tables);                                       \
+                                 stream, a.timed, p, p.tables);                              \
       }                                                                                      \
       launched = true;                                                                       \
     }
@@ -1675,8 +1682,8 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
     PKV_DEC_MFMA_G(KV, Q, 64) PKV_DEC_MFMA_G(KV, Q, 128)
 #define PKV_DEC_VALU(DT, DD)                                                                 \
     if (!launched && pool.dtype == DT && pool.head_dim == DD) {                              \
-      e = launch_decode_kernel(decode_valu_kernel<DT, DD>, grid, dim3(64), 0, stream, p,     \
-                               p.tables);                                                    \
+      e = launch_decode_kernel(decode_valu_kernel<DT, DD>, grid, dim3(64), 0, stream,        \
+                               a.timed, p, p.tables);                                        \
       launched = true;                                                                       \
     }
     PKV_DEC_MFMA_ALL(PKV_BF16, PKV_BF16) PKV_DEC_MFMA_ALL(PKV_F16, PKV_F16)
@@ -1741,6 +1748,26 @@ int collect_kernel_times(float* ms_out, int max_n, hipError_t* err) {
   }
   g_timing.pairs.clear();
   return n;
+}
+
+hipError_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));  // with this device current
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_bw_probe(const void* src, size_t n_bytes, void* sink, hipStream_t stream) {
