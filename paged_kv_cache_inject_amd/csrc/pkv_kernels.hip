@@ -273,19 +273,23 @@ struct InjectParams {
 
 constexpr int kInjectThreads = 256;
 
-// One workgroup per (destination block, group of layers).  The block's 16
-// rotary rows are staged in LDS once; then for every layer and group of HG
-// KV heads: each (token, source chunk pair) unit reads its two 16-byte K and
-// V chunks of the source row (format SDT), rotates K in float32 and stores it
-// into the K plane in the pool format PDT; V goes through LDS (already in
-// PDT) to be written dimension-major.  Source chunk pairs are (c0, c0 + C/2)
-// so that the halves pairing finds both partners in one unit.
-// ROW picks the lanes' walk over a head's (token, chunk pair) units: token
-// fastest (each load instruction takes 64 bytes of 16 token rows; the K
-// stores of a chunk are contiguous) for sources in HBM, or chunk fastest
-// (each load instruction takes 128-byte pieces of 8 token rows) for sources
-// in pinned host memory, whose PCIe reads want whole, aligned lines.
-template <int SDT, int PDT, int D, int HG, bool ROW>
+// One workgroup of 4 waves per (destination block, group of layers).  The
+// block's 16 rotary rows are staged in LDS once.  Each wave then takes whole
+// KV heads (heads wave, wave + 4, ... of every layer of the group): for each
+// (layer, head) every lane reads UPH (token, source chunk pair) units -- the
+// two 16-byte K and V chunks of a source row (format SDT) -- rotates K in
+// float32 and stores it into the K plane in the pool format PDT; V goes
+// through the wave's own LDS tile (already in PDT) to be written
+// dimension-major.  A wave touches only its own tile, so only the wave's own
+// ordering is needed there, no workgroup barrier.  Source chunk pairs are
+// (c0, c0 + C/2) so that the halves pairing finds both partners in one unit.
+// The lanes walk a head's units chunk fastest: each load instruction takes
+// whole 128-byte lines of 8 token rows (bf16 d = 128: the first or second
+// half of each row), which measured 1.28x faster than token fastest (64 bytes
+// of 16 rows per instruction) on the top-8 injection, and suits PCIe reads
+// from a pinned host store as well.  PF: the next (layer, head)'s loads are
+// issued before the current one is processed.
+template <int SDT, int PDT, int D, int HG, bool PF>
 __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParams p) {
   typedef typename Fmt<PDT>::T TP;
   constexpr int ES = Fmt<SDT>::kBytes, EP = Fmt<PDT>::kBytes;
@@ -294,12 +298,16 @@ __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParam
   constexpr int CS = D / XS;                  // source chunks per row
   constexpr int UNITS = kBlock * (CS / 2);    // (token, chunk pair) units per head
   constexpr int VPIECES = D * (kBlock / XP);  // 16-byte pieces of a V plane
-  constexpr int UPT = (HG * UNITS + kInjectThreads - 1) / kInjectThreads;
-  constexpr int VPT = (HG * VPIECES + kInjectThreads - 1) / kInjectThreads;
+  constexpr int NWAVE = kInjectThreads / 64;
+  constexpr int UPH = UNITS / 64;             // units per lane and head
+  constexpr int VPH = VPIECES / 64;           // V pieces per lane and head
   static_assert(XP % XS == 0, "a source chunk lands inside one pool chunk");
-  __shared__ TP vtile[HG][kBlock][D];
+  static_assert(UNITS % 64 == 0 && VPIECES % 64 == 0, "whole waves per head");
+  __shared__ TP vtile[NWAVE][kBlock][D];
   __shared__ float cs[kBlock][D];
   __shared__ InjectDesc desc;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   int h_begin = 0, h_end = p.n_kv_heads;
   int l0 = p.layer_begin + blockIdx.y * p.layers_per_wg;
@@ -351,104 +359,130 @@ __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParam
   for (int t = 0; t < kBlock; ++t) full &= desc.src[t] >= 0;
   __syncthreads();
 
-  for (int layer = l0; layer < l1; ++layer) {
-    char* kplane0 = p.pool_k + layer * p.p_layer + int64_t(desc.phys_block) * p.p_block;
-    char* vplane0 = p.pool_v + layer * p.p_layer + int64_t(desc.phys_block) * p.p_block;
+  // this wave's heads h_begin + wave + NWAVE k, for every layer of the group
+  const int span = h_end - h_begin;
+  const int heads_here = span > wave ? (span - wave + NWAVE - 1) / NWAVE : 0;
+  const int n_iter = (l1 - l0) * heads_here;
+  auto unit_tc = [&](int u, int& t, int& c0) {
+    const int r = lane + 64 * u;
+    t = r / (CS / 2);
+    c0 = r % (CS / 2);
+  };
+  // loads of iteration `it`: per unit, K chunks c0 and c0 + C/2, then V's
+  auto issue = [&](int it, uint4 (&b)[UPH][4]) {
+    const int layer = l0 + it / heads_here;
+    const int h = h_begin + wave + NWAVE * (it % heads_here);
     const char* sk = p.src_k + layer * p.s_layer;
     const char* sv = p.src_v + layer * p.s_layer;
-    for (int h0 = h_begin; h0 < h_end; h0 += HG) {
-      const int nh = min(HG, h_end - h0);
-      uint4 k0[UPT], k1[UPT], v0[UPT], v1[UPT];
 #pragma unroll
-      for (int u = 0; u < UPT; ++u) {
-        const int w = threadIdx.x + u * kInjectThreads;
-        const int hl = w / UNITS;
-        const int r = w - hl * UNITS;
-        const int t = ROW ? r / (CS / 2) : r % kBlock;
-        const int c0 = ROW ? r % (CS / 2) : r / kBlock;
-        const int src = (w < nh * UNITS) ? desc.src[t] : -1;
-        if (src >= 0) {
-          const int64_t row = int64_t(src) * p.s_token + int64_t(h0 + hl) * D * ES;
-          k0[u] = ld16_stream(sk + row + c0 * 16);
-          k1[u] = ld16_stream(sk + row + (c0 + CS / 2) * 16);
-          v0[u] = ld16_stream(sv + row + c0 * 16);
-          v1[u] = ld16_stream(sv + row + (c0 + CS / 2) * 16);
+    for (int u = 0; u < UPH; ++u) {
+      int t, c0;
+      unit_tc(u, t, c0);
+      const int src = desc.src[t];
+      if (src >= 0) {
+        const int64_t row = int64_t(src) * p.s_token + int64_t(h) * D * ES;
+        b[u][0] = ld16_stream(sk + row + c0 * 16);
+        b[u][1] = ld16_stream(sk + row + (c0 + CS / 2) * 16);
+        b[u][2] = ld16_stream(sv + row + c0 * 16);
+        b[u][3] = ld16_stream(sv + row + (c0 + CS / 2) * 16);
+      }
+    }
+  };
+  auto process = [&](int it, const uint4 (&b)[UPH][4]) {
+    const int layer = l0 + it / heads_here;
+    const int h = h_begin + wave + NWAVE * (it % heads_here);
+    char* kplane = p.pool_k + layer * p.p_layer + int64_t(desc.phys_block) * p.p_block +
+                   int64_t(h) * p.p_head;
+    char* vplane = p.pool_v + layer * p.p_layer + int64_t(desc.phys_block) * p.p_block +
+                   int64_t(h) * p.p_head;
+    // the scales of this (layer, head), or of this (layer, block, head)
+    const int64_t si = p.scale_mode == 1
+                           ? (int64_t(layer) * p.num_blocks + desc.phys_block) * p.n_kv_heads + h
+                           : int64_t(layer) * p.n_kv_heads + h;
+#pragma unroll
+    for (int u = 0; u < UPH; ++u) {
+      int t, c0;
+      unit_tc(u, t, c0);
+      if (desc.src[t] < 0) continue;
+      const int j0 = c0 * XS, j1 = (c0 + CS / 2) * XS;  // first dims of the two chunks
+      float kl[XS], kh[XS];
+      unpack16<SDT>(b[u][0], kl);
+      unpack16<SDT>(b[u][1], kh);
+      if (p.rope_mode == PKV_ROPE_PAIRS) {
+        rot_pairs_f<XS>(kl, j0, cs[t], cs[t] + D / 2);
+        rot_pairs_f<XS>(kh, j1, cs[t], cs[t] + D / 2);
+      } else if (p.rope_mode == PKV_ROPE_HALVES) {
+        rot_halves_f<XS>(kl, kh, j0, cs[t], cs[t] + D / 2);
+      }
+      const float ksc = PDT == PKV_FP8E4M3 ? p.k_scale[si] : 1.f;
+      Packed<PDT, XS> pk;
+      pk.set(kl, ksc);
+      store_packed(kplane + (((j0 / XP) * kBlock + t) * XP + j0 % XP) * EP, pk);
+      pk.set(kh, ksc);
+      store_packed(kplane + (((j1 / XP) * kBlock + t) * XP + j1 % XP) * EP, pk);
+      if constexpr (SDT == PDT) {
+        *reinterpret_cast<uint4*>(&vtile[wave][t][j0]) = b[u][2];
+        *reinterpret_cast<uint4*>(&vtile[wave][t][j1]) = b[u][3];
+      } else {
+        const float vsc = p.v_scale[si];
+        float vf[XS];
+        Packed<PDT, XS> pv;
+        unpack16<SDT>(b[u][2], vf);
+        pv.set(vf, vsc);
+        *reinterpret_cast<uint2*>(&vtile[wave][t][j0]) = *reinterpret_cast<const uint2*>(pv.v);
+        unpack16<SDT>(b[u][3], vf);
+        pv.set(vf, vsc);
+        *reinterpret_cast<uint2*>(&vtile[wave][t][j1]) = *reinterpret_cast<const uint2*>(pv.v);
+      }
+    }
+    // the tile is written and read by lanes of this wave only
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // V plane dimension-major, XP tokens per 16-byte piece; a piece with
+    // slots this call does not write keeps their old contents.
+#pragma unroll
+    for (int v = 0; v < VPH; ++v) {
+      const int r = lane + 64 * v;
+      const int j = r / (kBlock / XP);
+      const int t0 = (r % (kBlock / XP)) * XP;
+      char* dst = vplane + (int64_t(j) * kBlock + t0) * EP;
+      TP out[XP];
+      bool need_old = false, any = full;
+      if (!full) {
+#pragma unroll
+        for (int e = 0; e < XP; ++e) {
+          need_old |= desc.src[t0 + e] < 0;
+          any |= desc.src[t0 + e] >= 0;
         }
       }
+      if (!any) continue;  // no slot of this piece is written
+      if (need_old) *reinterpret_cast<uint4*>(out) = ld16(dst);
 #pragma unroll
-      for (int u = 0; u < UPT; ++u) {
-        const int w = threadIdx.x + u * kInjectThreads;
-        const int hl = w / UNITS;
-        const int r = w - hl * UNITS;
-        const int t = ROW ? r / (CS / 2) : r % kBlock;
-        const int c0 = ROW ? r % (CS / 2) : r / kBlock;
-        if (w >= nh * UNITS || desc.src[t] < 0) continue;
-        const int h = h0 + hl;
-        const int j0 = c0 * XS, j1 = (c0 + CS / 2) * XS;  // first dims of the two chunks
-        float kl[XS], kh[XS];
-        unpack16<SDT>(k0[u], kl);
-        unpack16<SDT>(k1[u], kh);
-        if (p.rope_mode == PKV_ROPE_PAIRS) {
-          rot_pairs_f<XS>(kl, j0, cs[t], cs[t] + D / 2);
-          rot_pairs_f<XS>(kh, j1, cs[t], cs[t] + D / 2);
-        } else if (p.rope_mode == PKV_ROPE_HALVES) {
-          rot_halves_f<XS>(kl, kh, j0, cs[t], cs[t] + D / 2);
-        }
-        // the scales of this (layer, head), or of this (layer, block, head)
-        const int64_t si = p.scale_mode == 1
-                               ? (int64_t(layer) * p.num_blocks + desc.phys_block) * p.n_kv_heads + h
-                               : int64_t(layer) * p.n_kv_heads + h;
-        const float ksc = PDT == PKV_FP8E4M3 ? p.k_scale[si] : 1.f;
-        Packed<PDT, XS> pk;
-        char* kplane = kplane0 + int64_t(h) * p.p_head;
-        pk.set(kl, ksc);
-        store_packed(kplane + (((j0 / XP) * kBlock + t) * XP + j0 % XP) * EP, pk);
-        pk.set(kh, ksc);
-        store_packed(kplane + (((j1 / XP) * kBlock + t) * XP + j1 % XP) * EP, pk);
-        if constexpr (SDT == PDT) {
-          *reinterpret_cast<uint4*>(&vtile[hl][t][j0]) = v0[u];
-          *reinterpret_cast<uint4*>(&vtile[hl][t][j1]) = v1[u];
-        } else {
-          const float vsc = p.v_scale[si];
-          float vf[XS];
-          Packed<PDT, XS> pv;
-          unpack16<SDT>(v0[u], vf);
-          pv.set(vf, vsc);
-          *reinterpret_cast<uint2*>(&vtile[hl][t][j0]) = *reinterpret_cast<const uint2*>(pv.v);
-          unpack16<SDT>(v1[u], vf);
-          pv.set(vf, vsc);
-          *reinterpret_cast<uint2*>(&vtile[hl][t][j1]) = *reinterpret_cast<const uint2*>(pv.v);
-        }
+      for (int e = 0; e < XP; ++e)
+        if (desc.src[t0 + e] >= 0) out[e] = vtile[wave][t0 + e][j];
+      st16_stream(dst, *reinterpret_cast<uint4*>(out));
+    }
+    // the tile's reads are done before the next iteration writes it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  uint4 b0[UPH][4], b1[UPH][4];
+  if constexpr (PF) {
+    if (n_iter > 0) issue(0, b0);
+    for (int it = 0; it < n_iter; it += 2) {
+      if (it + 1 < n_iter) issue(it + 1, b1);
+      process(it, b0);
+      if (it + 1 < n_iter) {
+        if (it + 2 < n_iter) issue(it + 2, b0);
+        process(it + 1, b1);
       }
-      __syncthreads();
-      // V planes dimension-major, XP tokens per 16-byte piece; a piece with
-      // slots this call does not write keeps their old contents.
-#pragma unroll
-      for (int u = 0; u < VPT; ++u) {
-        const int w = threadIdx.x + u * kInjectThreads;
-        if (w >= nh * VPIECES) break;
-        const int hl = w / VPIECES;
-        const int r = w - hl * VPIECES;
-        const int j = r / (kBlock / XP);
-        const int t0 = (r % (kBlock / XP)) * XP;
-        char* dst = vplane0 + int64_t(h0 + hl) * p.p_head + (int64_t(j) * kBlock + t0) * EP;
-        TP out[XP];
-        bool need_old = false, any = full;
-        if (!full) {
-#pragma unroll
-          for (int e = 0; e < XP; ++e) {
-            need_old |= desc.src[t0 + e] < 0;
-            any |= desc.src[t0 + e] >= 0;
-          }
-        }
-        if (!any) continue;  // no slot of this piece is written
-        if (need_old) *reinterpret_cast<uint4*>(out) = ld16(dst);
-#pragma unroll
-        for (int e = 0; e < XP; ++e)
-          if (desc.src[t0 + e] >= 0) out[e] = vtile[hl][t0 + e][j];
-        st16_stream(dst, *reinterpret_cast<uint4*>(out));
-      }
-      __syncthreads();
+    }
+  } else {
+    for (int it = 0; it < n_iter; ++it) {
+      issue(it, b0);
+      process(it, b0);
     }
   }
 }
@@ -793,20 +827,26 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
   const char* kbase = p.pool_k + int64_t(g) * p.p_head;
   const char* vbase = p.pool_v + int64_t(g) * p.p_head;
   const int nblk = (it.n_tokens + kBlock - 1) / kBlock;
-  // This wave takes blocks wave, wave + NW, wave + 2 NW, ...
+  // This wave takes blocks wave, wave + NW, wave + 2 NW, ...; the wave that
+  // owns the range's last block takes that one first and the rest in order.
+  // (The fused append writes the last block back; taken first, the write's
+  // latency passes while the wave streams its other blocks instead of
+  // holding the workgroup at its end.  Attention alone takes the same order,
+  // so the two compute bit-identical results.)
   const int nj = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;
-  // Fused append: the wave that takes the newest token's block (its j-th,
-  // put_j) makes the token's K chunks and V elements in the pool format
-  // before its loop, each lane those it holds when it loads that block (K
-  // chunks 4s + grp and V dims 16n + row of the slot); when it takes that
-  // block it puts them into its registers in place of the loaded ones and
-  // writes the block's planes back.  Other waves: put_j = -1.
+  const bool last_first = nblk > 0 && (nblk - 1) % NW == wave;
+  auto block_of = [&](int j) {  // block index within the range of the j-th block taken
+    return wave + NW * (last_first ? (j == 0 ? nj - 1 : j - 1) : j);
+  };
+  // Fused append: the wave that takes the newest token's block (its first,
+  // put_j = 0) makes the token's K chunks and V elements in the pool format
+  // when it takes that block, each lane those it holds (K chunks 4s + grp and
+  // V dims 16n + row of the slot), puts them into its registers in place of
+  // the loaded ones and writes the block's planes back.  Other waves:
+  // put_j = -1.
   int put_j = -1;
   if constexpr (PUT) {
-    if (p.new_k != nullptr && it.last && it.n_tokens > 0) {
-      const int lb = (it.n_tokens - 1) / kBlock;
-      if (lb % NW == wave) put_j = lb / NW;
-    }
+    if (p.new_k != nullptr && it.last && it.n_tokens > 0 && last_first) put_j = 0;
   }
 
   f32x4_t acc[NG][NT];
@@ -831,10 +871,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
   // Block ids are read one issue ahead (issues come in order j = 0, 1, ...),
   // so the scalar load's latency does not sit between a block's arrival and
   // the next block's loads.
-  int blk_next = nj > 0 ? tab[wave] : 0;
+  int blk_next = nj > 0 ? tab[block_of(0)] : 0;
   auto issue = [&](int j, int d) {
     int blk = blk_next;
-    if (j + 1 < nj) blk_next = tab[wave + (j + 1) * NW];
+    if (j + 1 < nj) blk_next = tab[block_of(j + 1)];
     if (j == put_j) put_blk = blk;
     const bool ok = unsigned(blk) < unsigned(p.num_blocks);
     okbuf[d] = ok;
@@ -856,26 +896,50 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
 
   NewSlot ns{};
   // The token's K and V rows in the pool format, made by the whole wave
-  // (lane i < D/2 rotates pair i; lanes take V dims lane, lane + 64) and
-  // read back, when the wave takes the token's block, by the lanes that hold
+  // (lane i < D/2 rotates pair i; lanes take V dims lane, lane + 64) when it
+  // reaches the token's block, and read back at once by the lanes that hold
   // the slot (K chunks 4s + grp in lanes with row == slot, V dims 16n + row
-  // in lanes with grp == slot / 4): kept in LDS meanwhile, not in registers.
+  // in lanes with grp == slot / 4), through LDS.  Their inputs (the pair's
+  // two source dims, its rotary entries, the lane's V dims) are loaded
+  // before the loop: their latency then hides behind the block loads instead
+  // of holding this wave back at the start, which would make the whole
+  // workgroup finish a memory round trip late.
   typedef typename Fmt<KVDT>::T TP;
+  typedef typename Fmt<QDT>::T TQ;
   __shared__ __align__(16) TP new_row[2][D];
-  auto make_new = [&](auto mode_tag) {
-    constexpr int MODE = decltype(mode_tag)::value;
-    typedef typename Fmt<QDT>::T TQ;
+  constexpr int NV = (D + 63) / 64;  // V dims per lane
+  TQ nk0 = 0, nk1 = 0;               // the pair's source dims (lanes < D/2)
+  float ncs = 1.f, nsn = 0.f;        // its rotary entries
+  TQ nv[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) nv[k] = 0;
+  const bool halves = p.rope_mode == PKV_ROPE_HALVES;
+  const bool rotate = p.rope_mode != PKV_ROPE_NONE;
+  auto load_new = [&]() {
     const TQ* kin = reinterpret_cast<const TQ*>(ns.kin);
     const TQ* vin = reinterpret_cast<const TQ*>(ns.vin);
     if (lane < D / 2) {
       const int i = lane;
-      const int j0 = MODE == PKV_ROPE_HALVES ? i : 2 * i;
-      const int j1 = MODE == PKV_ROPE_HALVES ? i + D / 2 : 2 * i + 1;
-      float x0 = Fmt<QDT>::to_f32(kin[j0]), x1 = Fmt<QDT>::to_f32(kin[j1]);
-      if constexpr (MODE != PKV_ROPE_NONE) {
-        const float c = ns.cr[i], sn = ns.sr[i];
-        const float y0 = x0 * c - x1 * sn;
-        const float y1 = x0 * sn + x1 * c;
+      nk0 = kin[halves ? i : 2 * i];
+      nk1 = kin[halves ? i + D / 2 : 2 * i + 1];
+      if (rotate) {
+        ncs = ns.cr[i];
+        nsn = ns.sr[i];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+      if (lane + 64 * k < D) nv[k] = vin[lane + 64 * k];
+  };
+  auto make_new = [&]() {
+    if (lane < D / 2) {
+      const int i = lane;
+      const int j0 = halves ? i : 2 * i;
+      const int j1 = halves ? i + D / 2 : 2 * i + 1;
+      float x0 = Fmt<QDT>::to_f32(nk0), x1 = Fmt<QDT>::to_f32(nk1);
+      if (rotate) {
+        const float y0 = x0 * ncs - x1 * nsn;
+        const float y1 = x0 * nsn + x1 * ncs;
         x0 = y0;
         x1 = y1;
       }
@@ -883,9 +947,11 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
       new_row[0][j1] = Fmt<KVDT>::from_f32(FP8 ? x1 / ns.ksc : x1);
     }
 #pragma unroll
-    for (int j = lane; j < D; j += 64) {
-      if constexpr (QDT == KVDT) new_row[1][j] = vin[j];
-      else new_row[1][j] = Fmt<KVDT>::from_f32(Fmt<QDT>::to_f32(vin[j]) / ns.vsc);
+    for (int k = 0; k < NV; ++k) {
+      const int j = lane + 64 * k;
+      if (j >= D) continue;
+      if constexpr (QDT == KVDT) new_row[1][j] = nv[k];
+      else new_row[1][j] = Fmt<KVDT>::from_f32(Fmt<QDT>::to_f32(nv[k]) / ns.vsc);
     }
     // the row is written and read by lanes of this one wave
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -900,15 +966,13 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
     if (put_j >= 0) {
       ns = new_slot<QDT, KVDT, D>(p, it, g);
       if constexpr (blockwise) {  // the scales of the block the token goes to
-        const int pb = tab[wave + put_j * NW];
+        const int pb = tab[block_of(put_j)];
         const int64_t pi = int64_t(unsigned(pb) < unsigned(p.num_blocks) ? pb : 0) * p.n_kv_heads + g;
         ns.ksc = p.k_scale[pi];
         ns.vsc = p.v_scale[pi];
       }
-      if (p.rope_mode == PKV_ROPE_PAIRS) make_new(RopeTag<PKV_ROPE_PAIRS>{});
-      else if (p.rope_mode == PKV_ROPE_HALVES) make_new(RopeTag<PKV_ROPE_HALVES>{});
-      else make_new(RopeTag<PKV_ROPE_NONE>{});
       if (!ns.ok) put_j = -1;  // no write, and the block is read as stored
+      else load_new();
     }
   }
 
@@ -918,7 +982,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
       const int j = j0 + d;
       if (j < nj) {
         if (PUT && j == put_j) {
-          // the newest token's slot: the values made above, not the pool's
+          // the newest token's slot: the values made now, not the pool's
+          make_new();
           if (row == ns.tin) {
 #pragma unroll
             for (int s = 0; s < SL; ++s)
@@ -992,10 +1057,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
         const float ksb = kscb[d], vsb = vscb[d];
         if (j + DEPTH < nj) issue(j + DEPTH, d);
 
-        const int valid = it.n_tokens - (wave + j * NW) * kBlock;  // tokens in range
+        const int valid = it.n_tokens - block_of(j) * kBlock;  // tokens in range
         // Slots of this block before a sliding window's start (positive only
         // in the window's first block).
-        const int skip = it.lo - (it.t_begin + (wave + j * NW) * kBlock);
+        const int skip = it.lo - (it.t_begin + block_of(j) * kBlock);
         // Scaled scores; slots outside [lo, end) or of a rejected block id
         // get -inf.  A whole block (the common case; wave-uniform) needs no
         // masks, and the masked case rewrites the values in place.
@@ -1145,6 +1210,238 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
         store_head_result(p, it, head_of(t), 16 * n + 4 * grp + r, acc[t][n][r] * vmul, m[t],
                           l[t], n == 0 && r == 0 && grp == 0, D);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode, packed dot products on the VALU (bf16/f16 pools, G <= 4 query heads
+// per KV head, attention alone): the workgroup shape, block order, loads and
+// online softmax of decode_mfma_kernel, with the two contractions done by
+// v_dot2_f32_{bf16,f16} instead of matrix instructions.  Kept as a measured
+// alternative for small query groups.
+//
+// Per 16-token block, lane (row, grp) = (lane % 16, lane / 16):
+//   scores:  the lane holds K chunks 4s + grp of token `row` (the MFMA
+//            kernel's loads) and the same dims of each query head; its
+//            partial dot products are summed over the four lanes of a token
+//            (lane swaps), so every lane of row t holds s[t][h];
+//   softmax: maximum and weights per head over the 16 tokens of a row (DPP
+//            row operations); the running sum is kept per token row;
+//   PV:      the lane holds V dims 16n + row for tokens 4 grp .. 4 grp + 3
+//            (the MFMA kernel's loads) and fetches those tokens' weights
+//            from the lanes of their rows (ds_bpermute); the weights go to
+//            16-bit as a hi part plus a lo residual, as in the MFMA kernel,
+//            and each (dim, head) takes four dot2 steps.  The partial outputs
+//            are summed over the four token groups at the end.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ inline float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Maximum / sum over the 16 lanes of each row, result in every lane of the
+// row (quad swaps, then half-row and row mirrors); each step combines the
+// same two values in both lanes of a pair, so the row's lanes agree bit for
+// bit.
+__device__ inline float row_max16(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm 1,0,3,2
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm 2,3,0,1
+  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+  return fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+}
+__device__ inline float row_sum16(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  return x + dpp_f<0x140>(x);
+}
+
+template <int DT> struct Dot2;
+template <> struct Dot2<PKV_BF16> {
+  typedef __attribute__((ext_vector_type(2))) __bf16 V2;
+  __device__ static float dot(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(V2, a), __builtin_bit_cast(V2, b),
+                                           c, false);
+  }
+};
+template <> struct Dot2<PKV_F16> {
+  typedef __attribute__((ext_vector_type(2))) _Float16 V2;
+  __device__ static float dot(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(V2, a), __builtin_bit_cast(V2, b), c, false);
+  }
+};
+
+template <int KVDT, int D, int NW, int GM>
+__global__ __launch_bounds__(64 * NW) void decode_dot2_kernel(DecodeParams p,
+                                                              const int32_t* __restrict__ tables) {
+  constexpr int S = D / 32;   // 16-byte K loads per lane and block (chunks 4s + grp)
+  constexpr int NT = D / 16;  // 8-byte V loads per lane and block (dims 16n + row)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = lane & 15;
+  const int grp = lane >> 4;
+  int item_i, g;
+  decode_work(p, blockIdx.x, item_i, g);
+  const DecodeItem it = p.items[item_i];
+  const int group = p.group;
+
+  // query dims matching this lane's K chunks, every head of the group
+  uint4 qreg[GM][S];
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    const int hh = h < group ? h : 0;
+    const uint16_t* qh = reinterpret_cast<const uint16_t*>(p.q) +
+                         (int64_t(it.seq) * p.n_q_heads + g * group + hh) * D;
+#pragma unroll
+    for (int st = 0; st < S; ++st) qreg[h][st] = ld16(qh + (4 * st + grp) * 8);
+  }
+  const int32_t* tab = tables + int64_t(it.seq) * p.table_stride + it.t_begin / kBlock;
+  const char* kbase = p.pool_k + int64_t(g) * p.p_head;
+  const char* vbase = p.pool_v + int64_t(g) * p.p_head;
+  const int nblk = (it.n_tokens + kBlock - 1) / kBlock;
+  const int nj = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;
+
+  float acc[GM][NT];
+  float m[GM], l[GM];
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[h][n] = 0.f;
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+  }
+  uint4 kbuf[S];
+  uint2 vbuf[NT];
+  bool okb = false;
+  int blk_next = nj > 0 ? tab[wave] : 0;
+  auto issue = [&](int j) {
+    int blk = blk_next;
+    if (j + 1 < nj) blk_next = tab[wave + (j + 1) * NW];
+    okb = unsigned(blk) < unsigned(p.num_blocks);
+    blk = okb ? blk : 0;
+    const char* kp = kbase + int64_t(blk) * p.p_block;
+    const char* vp = vbase + int64_t(blk) * p.p_block;
+#pragma unroll
+    for (int st = 0; st < S; ++st) kbuf[st] = ld16_stream(kp + (64 * st + lane) * 16);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) vbuf[n] = ld8_stream(vp + (16 * n + row) * 32 + grp * 8);
+  };
+  if (nj > 0) issue(0);
+  for (int j = 0; j < nj; ++j) {
+    float part[GM];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      float a = 0.f;
+#pragma unroll
+      for (int st = 0; st < S; ++st) {
+        a = Dot2<KVDT>::dot(kbuf[st].x, qreg[h][st].x, a);
+        a = Dot2<KVDT>::dot(kbuf[st].y, qreg[h][st].y, a);
+        a = Dot2<KVDT>::dot(kbuf[st].z, qreg[h][st].z, a);
+        a = Dot2<KVDT>::dot(kbuf[st].w, qreg[h][st].w, a);
+      }
+      part[h] = a;
+    }
+    uint2 vcur[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) vcur[n] = vbuf[n];
+    const bool blk_ok = okb;
+    if (j + 1 < nj) issue(j + 1);
+
+    const int valid = it.n_tokens - (wave + j * NW) * kBlock;
+    const int skip = it.lo - (it.t_begin + (wave + j * NW) * kBlock);
+    const int lim = blk_ok ? valid : 0;
+    const bool masked = !(blk_ok && valid >= kBlock && skip <= 0);
+    const bool row_in = row < lim && row >= skip;
+    if (masked) {
+      auto in = [&](int e) { return e < lim && e >= skip; };
+      const uint32_t mx0 = (in(4 * grp + 0) ? 0x0000ffffu : 0u) | (in(4 * grp + 1) ? 0xffff0000u : 0u);
+      const uint32_t mx1 = (in(4 * grp + 2) ? 0x0000ffffu : 0u) | (in(4 * grp + 3) ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        vcur[n].x &= mx0;
+        vcur[n].y &= mx1;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      float sc = cols_sum(part[h]) * p.scale_log2;   // s[row][h], same in the row's 4 lanes
+      if (masked && !row_in) sc = -INFINITY;
+      const float mx = row_max16(sc);                // wave-uniform
+      if (mx > m[h]) {
+        const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);  // 0 when m was -inf
+        l[h] *= alpha;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[h][n] *= alpha;
+        m[h] = mx;
+      }
+      const float m_ref = m[h] == -INFINITY ? 0.f : m[h];
+      const float pr = __builtin_amdgcn_exp2f(sc - m_ref);
+      l[h] += pr;
+      // weights of tokens 4 grp + r from the lanes of those rows (same grp)
+      uint16_t ph[4], pl[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int src = (grp * 16 + 4 * grp + r) * 4;
+        const float w = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(pr)));
+        Mfma<KVDT>::split(w, ph[r], pl[r]);
+      }
+      const uint32_t h01 = uint32_t(ph[0]) | (uint32_t(ph[1]) << 16);
+      const uint32_t h23 = uint32_t(ph[2]) | (uint32_t(ph[3]) << 16);
+      const uint32_t l01 = uint32_t(pl[0]) | (uint32_t(pl[1]) << 16);
+      const uint32_t l23 = uint32_t(pl[2]) | (uint32_t(pl[3]) << 16);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        float a = acc[h][n];
+        a = Dot2<KVDT>::dot(vcur[n].x, h01, a);
+        a = Dot2<KVDT>::dot(vcur[n].y, h23, a);
+        a = Dot2<KVDT>::dot(vcur[n].x, l01, a);
+        a = Dot2<KVDT>::dot(vcur[n].y, l23, a);
+        acc[h][n] = a;
+      }
+    }
+  }
+  // full sums: tokens over the row, outputs over the four token groups
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    l[h] = row_sum16(l[h]);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[h][n] = cols_sum(acc[h][n]);
+  }
+  __shared__ float sm_m[NW][GM], sm_l[NW][GM];
+  __shared__ float sm_o[NW][GM][D];
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      sm_m[wave][h] = m[h];
+      sm_l[wave][h] = l[h];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    float big_m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) big_m = fmaxf(big_m, sm_m[w][h]);
+    const float own = m[h] == -INFINITY ? 0.f : exp2f(m[h] - big_m);
+    if (grp == 0) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) sm_o[wave][h][16 * n + row] = acc[h][n] * own;
+    }
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < GM * D; o += 64 * NW) {
+    const int h = o / D, dim = o - h * D;
+    if (h >= group) continue;
+    float big_m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) big_m = fmaxf(big_m, sm_m[w][h]);
+    float big_l = 0.f, a = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = sm_m[w][h];
+      big_l += (mw == -INFINITY ? 0.f : exp2f(mw - big_m)) * sm_l[w][h];
+      a += sm_o[w][h][dim];
+    }
+    store_head_result(p, it, g * group + h, dim, a, big_m, big_l, dim == 0, D);
   }
 }
 
@@ -1505,16 +1802,15 @@ hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, bool src_in_h
   p.layers_per_wg = lpw;
   dim3 grid(n_desc, (n_layers + lpw - 1) / lpw);
   dim3 block(kInjectThreads);
-  // KV heads per pass: V tiles of 16 KiB (4 heads of d=128 bf16) by default.
-  int hg = 4;
-  if (const char* env = std::getenv("PKV_INJECT_HEADS")) hg = std::atoi(env) == 8 ? 8 : 4;
-  const bool row = src_in_host_memory;
-  if (row) hg = 4;
-#define PKV_INJ(SDT, PDT, DD, H, R) \
-  if (src.dtype == SDT && pool.dtype == PDT && pool.head_dim == DD && hg == H && row == R) \
-    return launch(inject_rope_kernel<SDT, PDT, DD, H, R>, grid, block, stream, p);
-#define PKV_INJ_H(SDT, PDT, DD) \
-  PKV_INJ(SDT, PDT, DD, 4, false) PKV_INJ(SDT, PDT, DD, 8, false) PKV_INJ(SDT, PDT, DD, 4, true)
+  (void)src_in_host_memory;  // one walk serves device and pinned host stores
+  // The next (layer, head)'s loads issued before the current one is processed
+  // (PKV_INJECT_PREFETCH=0: not).
+  bool pf = true;
+  if (const char* env = std::getenv("PKV_INJECT_PREFETCH")) pf = std::atoi(env) != 0;
+#define PKV_INJ(SDT, PDT, DD, F) \
+  if (src.dtype == SDT && pool.dtype == PDT && pool.head_dim == DD && pf == F) \
+    return launch(inject_rope_kernel<SDT, PDT, DD, 4, F>, grid, block, stream, p);
+#define PKV_INJ_H(SDT, PDT, DD) PKV_INJ(SDT, PDT, DD, false) PKV_INJ(SDT, PDT, DD, true)
 #define PKV_INJ_D(SDT, PDT) PKV_INJ_H(SDT, PDT, 64) PKV_INJ_H(SDT, PDT, 128)
   PKV_INJ_D(PKV_F32, PKV_F32) PKV_INJ_D(PKV_BF16, PKV_BF16) PKV_INJ_D(PKV_F16, PKV_F16)
   PKV_INJ_D(PKV_BF16, PKV_FP8E4M3) PKV_INJ_D(PKV_F16, PKV_FP8E4M3)
@@ -1622,7 +1918,8 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
   hipError_t e = hipSuccess;
   if (a.n_items > 0) {
     dim3 grid(unsigned(a.n_items) * unsigned(pool.n_kv_heads));
-    // variant: 0 automatic, 1 generic VALU kernel (not for fp8 pools), 10 + k
+    // variant: 0 automatic, 1 generic VALU kernel (not for fp8 pools), 2 packed
+    // dot products on the VALU where they apply (decode_dot2_kernel), 10 + k
     // MFMA kernel with a prefetch depth of k blocks (k = 1, 2).
     // Tiles of 16 query heads per KV head: groups up to 64 run on MFMA.
     const int ng = p.group <= 16 ? 1 : p.group <= 32 ? 2 : p.group <= 64 ? 4 : 0;
@@ -1686,6 +1983,23 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
                                a.timed, p, p.tables);                                        \
       launched = true;                                                                       \
     }
+    // variant 2: packed dot products on the VALU for small query groups
+    // (attention alone, 8-wave workgroups)
+    const bool dot2 = kernel_variant == 2 && !put && p.group <= 4 && nw == 8 &&
+                      (pool.dtype == PKV_BF16 || pool.dtype == PKV_F16) && a.q_dtype == pool.dtype;
+#define PKV_DEC_DOT2(KV, DD, GG)                                                             \
+    if (!launched && dot2 && pool.dtype == KV && pool.head_dim == DD &&                      \
+        (GG == 4 ? p.group > 2 : GG == 2 ? p.group == 2 : p.group == 1)) {                   \
+      constexpr auto k = decode_dot2_kernel<KV, DD, 8, GG>;                                  \
+      e = launch_decode_kernel(k, grid, dim3(512), one_per_cu ? one_per_cu_lds<k>() : 0,      \
+                               stream, a.timed, p, p.tables);                                \
+      launched = true;                                                                       \
+    }
+#define PKV_DEC_DOT2_G(KV, DD) PKV_DEC_DOT2(KV, DD, 1) PKV_DEC_DOT2(KV, DD, 2) PKV_DEC_DOT2(KV, DD, 4)
+    PKV_DEC_DOT2_G(PKV_BF16, 64) PKV_DEC_DOT2_G(PKV_BF16, 128)
+    PKV_DEC_DOT2_G(PKV_F16, 64) PKV_DEC_DOT2_G(PKV_F16, 128)
+#undef PKV_DEC_DOT2
+#undef PKV_DEC_DOT2_G
     PKV_DEC_MFMA_ALL(PKV_BF16, PKV_BF16) PKV_DEC_MFMA_ALL(PKV_F16, PKV_F16)
     PKV_DEC_MFMA_ALL(PKV_FP8E4M3, PKV_BF16) PKV_DEC_MFMA_ALL(PKV_FP8E4M3, PKV_F16)
     PKV_DEC_VALU(PKV_F32, 64) PKV_DEC_VALU(PKV_F32, 128) PKV_DEC_VALU(PKV_BF16, 64)

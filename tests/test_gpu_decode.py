@@ -36,6 +36,8 @@ def check_decode_all(dp, layer, q_raw, table, lens, hq, parts=(0,), variants=("a
     for variant in variants:
         if variant == "valu":
             os.environ["PKV_DECODE_KERNEL"] = "1"
+        elif variant == "dot2":
+            os.environ["PKV_DECODE_KERNEL"] = "2"
         try:
             for part in parts:
                 out, lse = gu.decode(dp, layer, q_dev, tables_dev, lens, hq, part)
@@ -274,3 +276,33 @@ def test_eight_wave_launches_with_one_workgroup_per_cu(dtype, hq, hkv, d):
     fill_random_pool(dp, 29)
     q = host_normal(rng, (len(lens), hq, d), dtype)
     check_decode_all(dp, 0, q, table, lens, hq, parts=(0, 512))
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("f16", 8, 8, 128),
+                                             ("bf16", 6, 2, 64), ("f16", 12, 4, 64),
+                                             ("bf16", 8, 4, 128)])
+def test_dot2_kernel_small_groups(dtype, hq, hkv, d):
+    """The packed-dot-product kernel (query groups of 1 to 4, 8-wave
+    workgroups) against the oracle: partial last blocks, an empty sequence,
+    split ranges; and it is a different kernel from the matrix one (its
+    rounding differs somewhere)."""
+    import torch
+    from tests import gpu_util as gu
+    from workloads.configs import host_normal, deal_tables
+    rng = np.random.default_rng(hq * 17 + hkv + d)
+    lens = np.array([600, 1500, 2047, 900, 3000, 17, 0, 700], dtype=np.int64)
+    need = int(sum(-(-x // 16) for x in lens))
+    table = deal_tables(rng.permutation(need + 5)[:need].astype(np.int32), lens, 256)
+    dp = gu.DevicePool(1, need + 5, hkv, d, dtype)
+    fill_random_pool(dp, 31)
+    q = host_normal(rng, (len(lens), hq, d), dtype)
+    check_decode_all(dp, 0, q, table, lens, hq, parts=(0, 512), variants=("dot2",))
+    q_dev = gu.to_device_raw(q.reshape(-1), dtype).view(q.shape)
+    tdev = torch.from_numpy(table).cuda()
+    os.environ["PKV_DECODE_KERNEL"] = "2"
+    try:
+        out2, _ = gu.decode(dp, 0, q_dev, tdev, lens, hq, 0)
+    finally:
+        os.environ.pop("PKV_DECODE_KERNEL", None)
+    out0, _ = gu.decode(dp, 0, q_dev, tdev, lens, hq, 0)
+    assert not torch.equal(out2, out0), "the packed-dot-product kernel did not run"
