@@ -223,7 +223,12 @@ def decode_workload(name):
     raise ValueError(name)
 
 
-def run_decode(steps, warmup, workload="70b", launch_steps=None, two_calls=True):
+def run_decode(steps, warmup, workload="70b", launch_steps=None, two_calls=True,
+               attention_only=False):
+    """One decode step per layer of `workload`: the one-launch append and
+    attention (pkv_append_decode_attention), or with attention_only the
+    attention call alone over the same cache (pkv_decode_attention), for
+    comparing kernels."""
     import torch
     import paged_kv_cache_inject_amd as pkv
     from workloads.configs import host_normal, device_normal
@@ -272,9 +277,13 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None, two_calls=True)
     def step():
         pkv.pkv_decode_plan_upload(plan, ws)
         for layer in range(cfg.n_layers):
-            pkv.pkv_append_decode_attention(plan, pool, layer, q, tables, k_new[layer],
-                                            v_new[layer], "pairs", dcos, dsin, max_pos, out, lse,
-                                            ws, q_dtype=new_dt)
+            if attention_only:
+                pkv.pkv_decode_attention(plan, pool, layer, q, tables, out, lse, ws,
+                                         q_dtype=new_dt)
+            else:
+                pkv.pkv_append_decode_attention(plan, pool, layer, q, tables, k_new[layer],
+                                                v_new[layer], "pairs", dcos, dsin, max_pos, out,
+                                                lse, ws, q_dtype=new_dt)
 
     def step_two_calls():
         pkv.pkv_decode_plan_upload(plan, ws)
@@ -330,8 +339,8 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None, two_calls=True)
     attended = np.minimum(lens, window) if window > 0 else lens
     per_decode = decode_bytes(attended, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads, 2,
                               kv_elem=1 if fp8 else 2)
-    per_append = append_bytes(cfg.batch, cfg.n_kv_heads, cfg.head_dim, 2,
-                              kv_elem=1 if fp8 else 2)
+    per_append = 0 if attention_only else append_bytes(cfg.batch, cfg.n_kv_heads, cfg.head_dim,
+                                                       2, kv_elem=1 if fp8 else 2)
     per_launch = per_decode + per_append
     ms_step = total_ms / steps
     res = dict(ms_per_step=ms_step, wall_ms_per_step=wall * 1e3 / steps,
@@ -703,43 +712,302 @@ def run_cow(reps):
     return res
 
 
-def cpu_baseline(budget_s=12.0):
-    """The oracle's decode on whole sequences of the decode workload (all 64
-    query heads per sequence, layer after layer), one thread, until the
-    budget is spent."""
+def run_tiny(reps=200):
+    """The tiny fp32 workload (1 layer, 2 sequences of 37 and 100 tokens, 4
+    query / 2 KV heads, d 64, 16-block pool under a permuted table): latency
+    of injecting its 24-token unrotated chunk at positions 40..63 of
+    sequence 1 (pkv_inject, one layer) and of one decode over both sequences
+    (pkv_decode_attention).  Each call is timed from the host call to its
+    completion (median) and by events around it on the stream."""
     import torch
-    from threadpoolctl import threadpool_limits
+    import paged_kv_cache_inject_amd as pkv
+    from workloads.configs import TINY, tiny_inputs
+    cfg = TINY
+    w = tiny_inputs(cfg)
+    L, H, d, hq = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads
+    buf, pool = device_pool(L, w["num_blocks"], H, d, "f32", None)
+    buf.zero_()
+    cache = pkv.pkv_cache_create(w["num_blocks"], 2, w["max_blocks"])
+    for sq in range(2):
+        pkv.pkv_set_blocks(cache, sq, [b for b in w["tables"][sq] if b >= 0], 0)
+    n_src = w["src_k"].shape[1]
+    sk = torch.from_numpy(np.ascontiguousarray(w["src_k"]).reshape(-1)).cuda()
+    sv = torch.from_numpy(np.ascontiguousarray(w["src_v"]).reshape(-1)).cuda()
+    src = pkv.make_src(sk, sv, n_src * H * d, H * d, n_src)
+    max_pos = 128
+    cos, sin = pkv.pkv_rope_table(d, cfg.rope_base, max_pos)
+    dcos, dsin = torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda()
+    ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    pkv.pkv_inject(cache, pool, src, w["prefill_runs"], 0, L, "pairs", dcos, dsin, max_pos, ws)
+    table, lens = pkv.pkv_block_table(cache, [0, 1], w["max_blocks"])
+    tdev = torch.from_numpy(table).cuda()
+    q = torch.from_numpy(np.ascontiguousarray(w["q"]).reshape(-1)).cuda().view(2, hq, d)
+    out = torch.empty(2, hq, d, device="cuda")
+    lse = torch.empty(2, hq, device="cuda")
+    plan = pkv.pkv_decode_plan_create(lens, hq, H, d, 0)
+    dws = torch.empty(pkv.pkv_decode_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
+    pkv.pkv_decode_plan_upload(plan, dws)
+    runs = pkv.make_runs(w["chunk_runs"])
+
+    def inject():
+        pkv.pkv_inject(cache, pool, src, runs, 0, L, "pairs", dcos, dsin, max_pos, ws)
+
+    def decode():
+        pkv.pkv_decode_attention(plan, pool, 0, q, tdev, out, lse, dws)
+
+    res = {}
+    for name, fn in (("inject_chunk", inject), ("decode", decode)):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        host, ev = [], []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            host.append((time.perf_counter() - t0) * 1e6)
+            ev.append(a.elapsed_time(b) * 1e3)
+        res[name] = {"host_call_to_done_us_p50": round(float(np.median(host)), 2),
+                     "events_us_p50": round(float(np.median(ev)), 2)}
+    pkv.pkv_decode_plan_destroy(plan)
+    pkv.pkv_cache_destroy(cache)
+    del buf, sk, sv, ws, dws
+    log("tiny: inject %s, decode %s" % (res["inject_chunk"], res["decode"]))
+    return res
+
+
+def _oracle_tiny(reps):
+    """The oracle on the tiny workload: prefill and chunk inject, then decode
+    of both sequences; returns (ms for the chunk inject, ms for the decode,
+    pid)."""
+    from oracle import attention as o_att, inject as o_inject
+    from oracle.allocator import AllocatorModel
+    from oracle.layout import PoolSpec
+    from oracle.rope import rope_table
+    from workloads.configs import TINY, tiny_inputs
+    cfg = TINY
+    w = tiny_inputs(cfg)
+    L, H, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+    nb = w["num_blocks"]
+    plane = 16 * d
+    spec = PoolSpec(L, nb, H, d, "f32", nb * 2 * H * plane, 2 * H * plane, plane)
+    pool = np.zeros(L * nb * 2 * H * plane, dtype=np.float32)
+    model = AllocatorModel(nb, 2, w["max_blocks"])
+    for sq in range(2):
+        model.set_blocks(sq, [b for b in w["tables"][sq] if b >= 0], 0)
+    cos, sin = rope_table(d, cfg.rope_base, 128)
+    n_src = w["src_k"].shape[1]
+    args = (w["src_k"].reshape(-1), w["src_v"].reshape(-1), n_src * H * d, H * d, 0, L, "pairs",
+            cos, sin)
+    lens = o_inject.inject(pool, pool[H * plane:], spec, model.tables, [0, 0], w["prefill_runs"],
+                           *args)
+    t_inj = t_dec = 0.0
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        o_inject.inject(pool, pool[H * plane:], spec, model.tables, lens, w["chunk_runs"], *args)
+        t1 = time.perf_counter()
+        o_att.decode_paged(w["q"], pool, pool[H * plane:], spec, 0, model.tables, lens,
+                           cfg.n_q_heads)
+        t_dec += time.perf_counter() - t1
+        t_inj += t1 - t0
+    return t_inj / reps * 1e3, t_dec / reps * 1e3, os.getpid()
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle timed on the host's cores (a reported baseline, not
+# a target).  Worker processes are spawned at the start of main(), before this
+# process touches the GPU, and never import torch; each runs numpy with one
+# BLAS thread.  Every unit builds fresh synthetic inputs of the workload's
+# shape (not timed) and times only the oracle call.
+# ---------------------------------------------------------------------------
+CPU_SHARE = 16            # host cores one GPU's job may use on the GPU box
+
+
+def _worker_init():
+    os.environ["OMP_NUM_THREADS"] = "1"
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except ImportError:
+        pass
+
+
+def _worker_ready(pause):
+    time.sleep(pause)          # keeps every worker busy so that each submit spawns one
+    return os.getpid()
+
+
+def start_cpu_pool():
+    """Spawn one worker per host core (at most CPU_SHARE); returns (pool, n)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    n = max(1, min(CPU_SHARE, len(os.sched_getaffinity(0))))
+    ex = ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn"),
+                             initializer=_worker_init)
+    pids = list(ex.map(_worker_ready, [1.0] * n))
+    return ex, len(set(pids))
+
+
+def host_info():
+    model, ram = "?", None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                ram = round(int(line.split()[1]) / 2 ** 20, 1)
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_ram_gib": ram}
+
+
+def _oracle_decode_units(hq, hkv, d, dtype, lens, seed):
+    """Oracle decode of one synthetic sequence per length (one layer each):
+    a pool holding only that sequence's blocks under a shuffled table, N(0,1)
+    values, and a query; times decode_paged alone.  Returns (kv bytes, s)."""
     from oracle import attention as o_att
     from oracle.layout import PoolSpec
-    from workloads.configs import LLAMA70B_80LAYER, llama70b_structure, host_normal, device_normal
-    cfg = LLAMA70B_80LAYER
-    st = llama70b_structure(cfg)
-    nb = st["num_blocks"]
-    plane = 16 * cfg.head_dim
-    bs = 2 * cfg.n_kv_heads * plane
-    q = host_normal(st["rng"], (cfg.batch, cfg.n_q_heads, cfg.head_dim), cfg.dtype)
-    spec = PoolSpec(1, nb, cfg.n_kv_heads, cfg.head_dim, "bf16", nb * bs, bs, plane)
-    rows = [list(r) for r in st["tables"]]
-    seqs_done, layers, dt = 0, 0, 0.0
-    while dt < budget_s and layers < cfg.n_layers:
-        layer = device_normal(nb * bs, "bf16", cfg.seed * 1000 + layers)
-        flat = layer.view(torch.int16).cpu().numpy().view(np.uint16)
-        del layer
-        kp, vp = flat, flat[cfg.n_kv_heads * plane:]
+    from workloads.configs import host_normal
+    rng = np.random.default_rng(seed)
+    plane = 16 * d
+    bs = 2 * hkv * plane
+    elem = 1 if dtype == "fp8" else (4 if dtype == "f32" else 2)
+    by = secs = 0.0
+    for ln in lens:
+        nb = -(-int(ln) // 16)
+        pool = host_normal(rng, (nb * bs,), dtype)
+        table = [rng.permutation(nb).tolist()]
+        q = host_normal(rng, (1, hq, d), dtype)
+        spec = PoolSpec(1, nb, hkv, d, dtype, nb * bs, bs, plane)
         t0 = time.perf_counter()
-        with threadpool_limits(limits=1):
-            for b in range(cfg.batch):
-                o_att.decode_paged(q, kp, vp, spec, 0, rows, st["lens"], cfg.n_q_heads,
-                                   seqs=[b], by_plane=True)
-                seqs_done += 1
-                if dt + time.perf_counter() - t0 > budget_s:
-                    break
-        dt += time.perf_counter() - t0
-        layers += 1
-    by = seqs_done * decode_bytes(st["lens"][:1], cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads, 2)
-    return dict(value=by / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample="%d (sequence, layer) pairs of the decode workload: 8192 tokens, all 64 "
-                       "query heads each; float64 numpy, one thread, %.1f s" % (seqs_done, dt))
+        o_att.decode_paged(q, pool, pool[hkv * plane:], spec, 0, table, [int(ln)], hq, seqs=[0],
+                           by_plane=True)
+        secs += time.perf_counter() - t0
+        by += int(ln) * hkv * d * elem * 2
+    return by, secs, os.getpid()
+
+
+def _oracle_inject_request(L, hkv, d, runs, seed):
+    """Oracle inject of one request's runs (prefix, chunks, separators) over
+    L layers from a store holding only the rows the runs name.  Returns
+    (injected tokens x layers, s)."""
+    from oracle import inject as o_inject
+    from oracle.allocator import AllocatorModel
+    from oracle.layout import PoolSpec
+    from oracle.rope import rope_table
+    from workloads.configs import host_normal
+    rng = np.random.default_rng(seed)
+    n_tok = sum(n for (_s, n, _p, _src) in runs)
+    m = max(p + n for (_s, n, p, _src) in runs)
+    local, at = [], 0
+    for (_s, n, p, _src) in runs:                 # store rows renumbered 0..n_tok-1
+        local.append((0, n, p, at))
+        at += n
+    row = hkv * d
+    src_k = host_normal(rng, (L * n_tok * row,), "bf16")
+    src_v = host_normal(rng, (L * n_tok * row,), "bf16")
+    nb = -(-m // 16)
+    model = AllocatorModel(nb, 1, nb)
+    model.alloc_blocks(0, m)
+    plane = 16 * d
+    bs = 2 * hkv * plane
+    spec = PoolSpec(L, nb, hkv, d, "bf16", nb * bs, bs, plane)
+    pool = np.zeros(L * nb * bs, dtype=np.uint16)
+    cos, sin = rope_table(d, 10000.0, m)
+    t0 = time.perf_counter()
+    o_inject.inject(pool, pool[hkv * plane:], spec, model.tables, [0], local, src_k, src_v,
+                    n_tok * row, row, 0, L, "pairs", cos, sin)
+    return n_tok * L, time.perf_counter() - t0, os.getpid()
+
+
+def _parallel(ex, fn, jobs):
+    """Run jobs on the pool; returns (total work, the busiest worker's summed
+    oracle time, all workers' summed oracle time)."""
+    futs = [ex.submit(fn, *j) for j in jobs]
+    res = [f.result() for f in futs]
+    per_pid = {}
+    for work, secs, pid in res:
+        per_pid[pid] = per_pid.get(pid, 0.0) + secs
+    return sum(r[0] for r in res), max(per_pid.values()), sum(per_pid.values())
+
+
+def cpu_baselines(ex, n_workers, units_70b=8):
+    """The oracle on the host's cores, per workload: the 70B decode (a
+    sample of (sequence, layer) units), the 8B-shaped layer (in full), the
+    ragged MHA batch (a sample of its sequences) and the top-8 injection (a
+    sample of requests over 8 of 32 layers).  Each reports the all-core
+    rate (total work over the busiest worker's oracle time) and the rate of
+    one worker running alone."""
+    from workloads.configs import (INJECT_TOP8, LLAMA70B_80LAYER, LLAMA8B_1LAYER, RAGGED_MHA,
+                                   inject_structure, llama8b_structure, ragged_mha_structure)
+    info = host_info()
+    out = {}
+    # 70B-shaped decode: units of one (sequence, layer), 8,192 tokens, 64/8 heads
+    c = LLAMA70B_80LAYER
+    alone = ex.submit(_oracle_decode_units, c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype,
+                      [8192] * 2, 7).result()
+    per_job = units_70b
+    by, span, busy = _parallel(ex, _oracle_decode_units,
+                               [(c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype, [8192] * per_job,
+                                 100 + i) for i in range(n_workers)])
+    out["decode_70b"] = dict(
+        value=by / span / 1e9, unit="GB/s", cores=n_workers, kind="oracle",
+        single_core_value=alone[0] / alone[1] / 1e9,
+        sample="%d (sequence, layer) units of the 70B-shaped decode (8,192 tokens, 64 query / "
+               "8 KV heads, d 128, bf16) out of %d, %d per worker; float64 numpy, one BLAS "
+               "thread per worker; value = KV bytes / the busiest worker's oracle time; "
+               "single_core_value = one worker alone on 2 units" % (per_job * n_workers,
+                                                                     c.batch * c.n_layers, per_job),
+        **info)
+    # 8B-shaped layer, all 64 sequences
+    c = LLAMA8B_1LAYER
+    lens = [int(x) for x in llama8b_structure(c)["lens"]]
+    by, span, busy = _parallel(ex, _oracle_decode_units,
+                               [(c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype,
+                                 lens[i::n_workers], 200 + i) for i in range(n_workers)])
+    out["decode_8b"] = dict(value=by / span / 1e9, unit="GB/s", cores=n_workers, kind="oracle",
+                            single_core_value=by / busy / 1e9,
+                            sample="all 64 sequences of the 8B-shaped layer (lengths 512..4096), "
+                                   "dealt over the workers; single_core_value = KV bytes over "
+                                   "the summed per-worker times", **info)
+    # ragged MHA: a seeded sample of 4 sequences per worker (lognormal lengths)
+    c = RAGGED_MHA
+    lens = [int(x) for x in ragged_mha_structure(c)["lens"]]
+    pick = np.random.default_rng(5).choice(len(lens), min(len(lens), 4 * n_workers),
+                                           replace=False)
+    sample = [lens[i] for i in pick]
+    by, span, busy = _parallel(ex, _oracle_decode_units,
+                               [(c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype,
+                                 sample[i::n_workers], 300 + i) for i in range(n_workers)])
+    out["decode_ragged"] = dict(
+        value=by / span / 1e9, unit="GB/s", cores=n_workers, kind="oracle",
+        single_core_value=by / busy / 1e9,
+        sample="%d of the 256 ragged MHA sequences (seeded draw, %d tokens), 64 heads, d 128, "
+               "f16; single_core_value = KV bytes over the summed per-worker times"
+               % (len(sample), sum(sample)), **info)
+    # injection: one request per worker, 8 of its 32 layers
+    c = INJECT_TOP8
+    st = inject_structure(c)
+    by_req = {}
+    for r in st["runs"]:
+        by_req.setdefault(r[0], []).append(r)
+    reqs = sorted(by_req)[:n_workers]
+    tl, span, busy = _parallel(ex, _oracle_inject_request,
+                               [(8, c.n_kv_heads, c.head_dim,
+                                 sorted(by_req[b], key=lambda r: r[2]), 400 + b) for b in reqs])
+    out["inject"] = dict(
+        value=tl / c.n_layers / span, unit="tokens/s", cores=n_workers, kind="oracle",
+        single_core_value=tl / c.n_layers / busy,
+        sample="%d requests of the top-8 injection (prefix, 8 chunks and their separators), 8 "
+               "of 32 layers each, rows of the retrieved chunks only; tokens/s counts a token "
+               "once for all 32 layers (token-layers / 32)" % len(reqs), **info)
+    return out
 
 
 def _r4(x):
@@ -772,6 +1040,11 @@ def main():
                     help="skip the 8B-shaped and ragged-MHA decode figures")
     ap.add_argument("--no-two-calls", action="store_true",
                     help="skip the comparison timing of the step as two launches per layer")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="time the attention call alone (no fused append) in the decode step")
+    ap.add_argument("--decode-kernel", default="auto", choices=["auto", "dot2"],
+                    help="dot2: packed dot products on the VALU where they apply (query groups "
+                         "of at most 4, 8-wave workgroups, attention alone)")
     ap.add_argument("--decode-workload", default="70b",
                     choices=["70b", "8b", "ragged", "70b-fp8", "70b-fp8b", "mistral-window",
                              "70b-block32", "mqa"],
@@ -781,6 +1054,11 @@ def main():
         print("bench.py measures one GPU: the hot path here runs on a single MI355X; "
               "multi-GPU sharding is design-only. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    cpu_pool = n_cpu = None
+    if not args.no_cpu_baseline and not (args.inject_only or args.host_store_only):
+        # the oracle's worker processes start before this process touches the GPU
+        cpu_pool, n_cpu = start_cpu_pool()
+        log("cpu baseline: %d worker processes" % n_cpu)
     import torch
     import paged_kv_cache_inject_amd as pkv
     pkv.load_library()
@@ -796,7 +1074,11 @@ def main():
     probe = bw_probe()
     log("bw probe: %.1f GB/s" % probe)
     two = not args.no_two_calls
-    dec, _ = run_decode(args.steps, args.warmup, args.decode_workload, two_calls=two)
+    if args.decode_kernel == "dot2":
+        os.environ["PKV_DECODE_KERNEL"] = "2"
+    dec, _ = run_decode(args.steps, args.warmup, args.decode_workload,
+                        two_calls=two and not args.attention_only,
+                        attention_only=args.attention_only)
     fp8 = fp8b = None
     if not args.no_fp8 and args.decode_workload == "70b":
         fp8, _ = run_decode(args.steps, args.warmup, "70b-fp8", two_calls=two)
@@ -814,7 +1096,17 @@ def main():
         # cache flushed between steps)
         for name in ("8b", "ragged"):
             shapes[name] = run_decode(args.steps, args.warmup, name, two_calls=False)
-    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    tiny = run_tiny() if args.decode_workload == "70b" else None
+    cpu = {}
+    if cpu_pool is not None:
+        log("cpu baseline: the oracle on %d cores" % n_cpu)
+        cpu = cpu_baselines(cpu_pool, n_cpu)
+        if tiny is not None:
+            ti, td, _ = cpu_pool.submit(_oracle_tiny, 20).result()
+            tiny["oracle_ms"] = {"inject_chunk": round(ti, 3), "decode": round(td, 3),
+                                 "cores": 1}
+        cpu_pool.shutdown()
+        log("cpu baseline: %s" % {k: round(v["value"], 3) for k, v in cpu.items()})
     line = {
         "metric": "paged decode attention achieved HBM GB/s (% of peak) + injected tokens/s",
         "value": round(dec["value"], 1),
@@ -833,7 +1125,9 @@ def main():
                    "layers": dec["layers"], "part_tokens": dec["part_tokens"],
                    "work_items": dec["n_items"], "waves_per_workgroup": dec["waves"],
                    "pool_layout": POOL_LAYOUT,
-                   "step": "per layer: pkv_append_decode_attention (the step's token "
+                   "step": ("per layer: pkv_decode_attention alone (%s kernel)"
+                            % args.decode_kernel) if args.attention_only else
+                           "per layer: pkv_append_decode_attention (the step's token "
                            "appended at position len-1 with RoPE, then attention over len "
                            "tokens, one launch)"},
         "roofline": {"bound": "hbm", "achieved": round(dec["launch_gbps"], 1),
@@ -860,8 +1154,13 @@ def main():
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", "?"),
                    "compute_units": props.multi_processor_count},
         "inputs": {"seed": dec["seed"], "tables_sha256": dec["tables_sha256"]},
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu.get("decode_70b"),
     }
+    if tiny is not None:
+        line["tiny"] = dict(workload="tiny fp32 reference: 1 layer, 2 sequences (37 and 100 "
+                                     "tokens), 4 query / 2 KV heads, d 64, 16-block pool; a "
+                                     "24-token chunk injected at 40..63 of sequence 1",
+                            latency_only=True, **tiny)
     if fp8 is not None:
         line["decode_fp8"] = {
             "workload": "the same decode workload with an fp8 (E4M3) cache, per-(layer, KV head) "
@@ -894,7 +1193,8 @@ def main():
                           "tokens_per_call": inj["tokens"], "requests": inj["requests"],
                           "layers": inj["layers"],
                           "workload": "top-8 of 10k chunks (64..256 tokens), 32 layers x 8 x 128 "
-                                      "bf16, 64 requests, gaps of 1..15 positions"}
+                                      "bf16, 64 requests, gaps of 1..15 positions",
+                          "cpu_baseline": cpu.get("inject")}
         rp = inj["request_path"]
         line["request_path"] = {
             "workload": "the same 64 requests from an empty cache: reserve blocks, inject, "
@@ -951,7 +1251,8 @@ def main():
             "part_tokens": r["part_tokens"], "waves_per_workgroup": r["waves"],
             "seed": r["seed"], "tables_sha256": r["tables_sha256"],
             "cold_meaning": "each step timed after writing a 1 GiB buffer, so the 256 MB "
-                            "last-level cache holds none of the layer"}
+                            "last-level cache holds none of the layer",
+            "cpu_baseline": cpu.get(key)}
         if name == "ragged":
             line[key]["balance"] = item_balance(st["lens"], r["part_tokens"],
                                                 decode_workload(name)[0].n_kv_heads)
