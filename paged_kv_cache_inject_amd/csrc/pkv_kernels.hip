@@ -827,26 +827,20 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
   const char* kbase = p.pool_k + int64_t(g) * p.p_head;
   const char* vbase = p.pool_v + int64_t(g) * p.p_head;
   const int nblk = (it.n_tokens + kBlock - 1) / kBlock;
-  // This wave takes blocks wave, wave + NW, wave + 2 NW, ...; the wave that
-  // owns the range's last block takes that one first and the rest in order.
-  // (The fused append writes the last block back; taken first, the write's
-  // latency passes while the wave streams its other blocks instead of
-  // holding the workgroup at its end.  Attention alone takes the same order,
-  // so the two compute bit-identical results.)
+  // This wave takes blocks wave, wave + NW, wave + 2 NW, ...
   const int nj = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;
-  const bool last_first = nblk > 0 && (nblk - 1) % NW == wave;
-  auto block_of = [&](int j) {  // block index within the range of the j-th block taken
-    return wave + NW * (last_first ? (j == 0 ? nj - 1 : j - 1) : j);
-  };
-  // Fused append: the wave that takes the newest token's block (its first,
-  // put_j = 0) makes the token's K chunks and V elements in the pool format
-  // when it takes that block, each lane those it holds (K chunks 4s + grp and
-  // V dims 16n + row of the slot), puts them into its registers in place of
-  // the loaded ones and writes the block's planes back.  Other waves:
-  // put_j = -1.
+  // Fused append: the wave that takes the newest token's block (its j-th,
+  // put_j) makes the token's K chunks and V elements in the pool format
+  // before its loop, each lane those it holds when it loads that block (K
+  // chunks 4s + grp and V dims 16n + row of the slot); when it takes that
+  // block it puts them into its registers in place of the loaded ones and
+  // writes the block's planes back.  Other waves: put_j = -1.
   int put_j = -1;
   if constexpr (PUT) {
-    if (p.new_k != nullptr && it.last && it.n_tokens > 0 && last_first) put_j = 0;
+    if (p.new_k != nullptr && it.last && it.n_tokens > 0) {
+      const int lb = (it.n_tokens - 1) / kBlock;
+      if (lb % NW == wave) put_j = lb / NW;
+    }
   }
 
   f32x4_t acc[NG][NT];
@@ -871,10 +865,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
   // Block ids are read one issue ahead (issues come in order j = 0, 1, ...),
   // so the scalar load's latency does not sit between a block's arrival and
   // the next block's loads.
-  int blk_next = nj > 0 ? tab[block_of(0)] : 0;
+  int blk_next = nj > 0 ? tab[wave] : 0;
   auto issue = [&](int j, int d) {
     int blk = blk_next;
-    if (j + 1 < nj) blk_next = tab[block_of(j + 1)];
+    if (j + 1 < nj) blk_next = tab[wave + (j + 1) * NW];
     if (j == put_j) put_blk = blk;
     const bool ok = unsigned(blk) < unsigned(p.num_blocks);
     okbuf[d] = ok;
@@ -896,50 +890,26 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
 
   NewSlot ns{};
   // The token's K and V rows in the pool format, made by the whole wave
-  // (lane i < D/2 rotates pair i; lanes take V dims lane, lane + 64) when it
-  // reaches the token's block, and read back at once by the lanes that hold
+  // (lane i < D/2 rotates pair i; lanes take V dims lane, lane + 64) and
+  // read back, when the wave takes the token's block, by the lanes that hold
   // the slot (K chunks 4s + grp in lanes with row == slot, V dims 16n + row
-  // in lanes with grp == slot / 4), through LDS.  Their inputs (the pair's
-  // two source dims, its rotary entries, the lane's V dims) are loaded
-  // before the loop: their latency then hides behind the block loads instead
-  // of holding this wave back at the start, which would make the whole
-  // workgroup finish a memory round trip late.
+  // in lanes with grp == slot / 4): kept in LDS meanwhile, not in registers.
   typedef typename Fmt<KVDT>::T TP;
-  typedef typename Fmt<QDT>::T TQ;
   __shared__ __align__(16) TP new_row[2][D];
-  constexpr int NV = (D + 63) / 64;  // V dims per lane
-  TQ nk0 = 0, nk1 = 0;               // the pair's source dims (lanes < D/2)
-  float ncs = 1.f, nsn = 0.f;        // its rotary entries
-  TQ nv[NV];
-#pragma unroll
-  for (int k = 0; k < NV; ++k) nv[k] = 0;
-  const bool halves = p.rope_mode == PKV_ROPE_HALVES;
-  const bool rotate = p.rope_mode != PKV_ROPE_NONE;
-  auto load_new = [&]() {
+  auto make_new = [&](auto mode_tag) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    typedef typename Fmt<QDT>::T TQ;
     const TQ* kin = reinterpret_cast<const TQ*>(ns.kin);
     const TQ* vin = reinterpret_cast<const TQ*>(ns.vin);
     if (lane < D / 2) {
       const int i = lane;
-      nk0 = kin[halves ? i : 2 * i];
-      nk1 = kin[halves ? i + D / 2 : 2 * i + 1];
-      if (rotate) {
-        ncs = ns.cr[i];
-        nsn = ns.sr[i];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < NV; ++k)
-      if (lane + 64 * k < D) nv[k] = vin[lane + 64 * k];
-  };
-  auto make_new = [&]() {
-    if (lane < D / 2) {
-      const int i = lane;
-      const int j0 = halves ? i : 2 * i;
-      const int j1 = halves ? i + D / 2 : 2 * i + 1;
-      float x0 = Fmt<QDT>::to_f32(nk0), x1 = Fmt<QDT>::to_f32(nk1);
-      if (rotate) {
-        const float y0 = x0 * ncs - x1 * nsn;
-        const float y1 = x0 * nsn + x1 * ncs;
+      const int j0 = MODE == PKV_ROPE_HALVES ? i : 2 * i;
+      const int j1 = MODE == PKV_ROPE_HALVES ? i + D / 2 : 2 * i + 1;
+      float x0 = Fmt<QDT>::to_f32(kin[j0]), x1 = Fmt<QDT>::to_f32(kin[j1]);
+      if constexpr (MODE != PKV_ROPE_NONE) {
+        const float c = ns.cr[i], sn = ns.sr[i];
+        const float y0 = x0 * c - x1 * sn;
+        const float y1 = x0 * sn + x1 * c;
         x0 = y0;
         x1 = y1;
       }
@@ -947,11 +917,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
       new_row[0][j1] = Fmt<KVDT>::from_f32(FP8 ? x1 / ns.ksc : x1);
     }
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int j = lane + 64 * k;
-      if (j >= D) continue;
-      if constexpr (QDT == KVDT) new_row[1][j] = nv[k];
-      else new_row[1][j] = Fmt<KVDT>::from_f32(Fmt<QDT>::to_f32(nv[k]) / ns.vsc);
+    for (int j = lane; j < D; j += 64) {
+      if constexpr (QDT == KVDT) new_row[1][j] = vin[j];
+      else new_row[1][j] = Fmt<KVDT>::from_f32(Fmt<QDT>::to_f32(vin[j]) / ns.vsc);
     }
     // the row is written and read by lanes of this one wave
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -966,13 +934,15 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
     if (put_j >= 0) {
       ns = new_slot<QDT, KVDT, D>(p, it, g);
       if constexpr (blockwise) {  // the scales of the block the token goes to
-        const int pb = tab[block_of(put_j)];
+        const int pb = tab[wave + put_j * NW];
         const int64_t pi = int64_t(unsigned(pb) < unsigned(p.num_blocks) ? pb : 0) * p.n_kv_heads + g;
         ns.ksc = p.k_scale[pi];
         ns.vsc = p.v_scale[pi];
       }
+      if (p.rope_mode == PKV_ROPE_PAIRS) make_new(RopeTag<PKV_ROPE_PAIRS>{});
+      else if (p.rope_mode == PKV_ROPE_HALVES) make_new(RopeTag<PKV_ROPE_HALVES>{});
+      else make_new(RopeTag<PKV_ROPE_NONE>{});
       if (!ns.ok) put_j = -1;  // no write, and the block is read as stored
-      else load_new();
     }
   }
 
@@ -982,8 +952,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
       const int j = j0 + d;
       if (j < nj) {
         if (PUT && j == put_j) {
-          // the newest token's slot: the values made now, not the pool's
-          make_new();
+          // the newest token's slot: the values made above, not the pool's
           if (row == ns.tin) {
 #pragma unroll
             for (int s = 0; s < SL; ++s)
@@ -1057,10 +1026,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
         const float ksb = kscb[d], vsb = vscb[d];
         if (j + DEPTH < nj) issue(j + DEPTH, d);
 
-        const int valid = it.n_tokens - block_of(j) * kBlock;  // tokens in range
+        const int valid = it.n_tokens - (wave + j * NW) * kBlock;  // tokens in range
         // Slots of this block before a sliding window's start (positive only
         // in the window's first block).
-        const int skip = it.lo - (it.t_begin + block_of(j) * kBlock);
+        const int skip = it.lo - (it.t_begin + (wave + j * NW) * kBlock);
         // Scaled scores; slots outside [lo, end) or of a rejected block id
         // get -inf.  A whole block (the common case; wave-uniform) needs no
         // masks, and the masked case rewrites the values in place.
