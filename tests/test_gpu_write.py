@@ -203,3 +203,63 @@ def test_append_skips_positions_the_device_data_does_not_cover(dtype, mode):
     gu.assert_bytes_equal(got, ref, "pool after append with out-of-range device data")
     # something was written, and the canary survives where nothing may be
     assert (got != canary_buffer(dp, dtype)).any()
+
+
+@pytest.mark.parametrize("pf", ["0", "1"])
+@pytest.mark.parametrize("dtype,src_dtype,d,mode", [
+    ("bf16", "bf16", 128, "pairs"), ("fp8", "bf16", 128, "halves"), ("f32", "f32", 64, "none"),
+    ("f16", "f16", 64, "pairs"),
+])
+def test_inject_layer_groups_with_and_without_prefetch(pf, dtype, src_dtype, d, mode):
+    """Workgroups that walk several layers and heads: 8 KV heads (two per
+    wave) and 5 layers per workgroup give each wave 10 (layer, head) steps,
+    so the one-deep prefetch alternates its buffers and ends on an odd step;
+    the same call without prefetch gives the same bytes.  Pool byte-exact
+    against the oracle."""
+    import os
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    from oracle import inject as o_inject
+    from oracle.allocator import AllocatorModel
+    from oracle.rope import rope_table
+    from tests import gpu_util as gu
+    from workloads.configs import host_normal
+
+    gu.say("inject layer groups", pf, dtype, src_dtype, d, mode)
+    rng = np.random.default_rng(len(dtype) * 31 + d + len(mode) + int(pf))
+    L, H, NB, max_pos = 5, 8, 40, 400
+    dp = gu.DevicePool(L, NB, H, d, dtype, fill_bits=CANARY[dtype])
+    ks = vs = None
+    if dtype == "fp8":
+        ks = rng.uniform(0.005, 0.03, size=(L, H)).astype(np.float32)
+        vs = rng.uniform(0.005, 0.03, size=(L, H)).astype(np.float32)
+        dp.set_scales(ks, vs)
+    cache = pkv.pkv_cache_create(NB, 3, 16, free_list_seed=5)
+    model = AllocatorModel(NB, 3, 16, seed=5)
+    for s, n in enumerate((130, 61, 200)):
+        pkv.pkv_alloc_blocks(cache, s, n)
+        model.alloc_blocks(s, n)
+    n_src = 500
+    src_k = host_normal(rng, (L, n_src, H, d), src_dtype)
+    src_v = host_normal(rng, (L, n_src, H, d), src_dtype)
+    runs = [(0, 130, 0, 0), (1, 61, 0, 130), (2, 7, 0, 300), (2, 150, 7, 191), (2, 43, 157, 400)]
+    o_cos, o_sin = rope_table(d, 10000.0, max_pos)
+    _, _, dcos, dsin = gu.rope_tables(d, max_pos)
+    dk = gu.to_device_raw(src_k.reshape(-1), src_dtype)
+    dv = gu.to_device_raw(src_v.reshape(-1), src_dtype)
+    src = pkv.make_src(dk, dv, n_src * H * d, H * d, n_src, dtype=src_dtype)
+    ws = gu.workspace(pkv.pkv_inject_workspace_bytes(runs))
+    os.environ["PKV_INJECT_LAYERS_PER_WG"] = "5"
+    os.environ["PKV_INJECT_PREFETCH"] = pf
+    try:
+        pkv.pkv_inject(cache, dp.desc(), src, runs, 0, L, mode, dcos, dsin, max_pos, ws)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("PKV_INJECT_LAYERS_PER_WG", None)
+        os.environ.pop("PKV_INJECT_PREFETCH", None)
+    ref = canary_buffer(dp, dtype)
+    kp, vp = dp.oracle_arrays(ref)
+    o_inject.inject(kp, vp, dp.spec(), model.tables, [0, 0, 0], runs, src_k.reshape(-1),
+                    src_v.reshape(-1), n_src * H * d, H * d, 0, L, mode, o_cos, o_sin,
+                    src_dtype=src_dtype, k_scale=ks, v_scale=vs)
+    gu.assert_bytes_equal(dp.host_copy(), ref, "pool after a layer-group inject")
