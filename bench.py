@@ -1253,9 +1253,8 @@ def main():
             "cold_meaning": "each step timed after writing a 1 GiB buffer, so the 256 MB "
                             "last-level cache holds none of the layer",
             "cpu_baseline": cpu.get(key)}
-        if name == "ragged":
-            line[key]["balance"] = item_balance(st["lens"], r["part_tokens"],
-                                                decode_workload(name)[0].n_kv_heads)
+        line[key]["balance"] = item_balance(st["lens"], r["part_tokens"],
+                                            decode_workload(name)[0].n_kv_heads)
     print(json.dumps(line), flush=True)
 
 

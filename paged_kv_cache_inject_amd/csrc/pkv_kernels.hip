@@ -946,178 +946,216 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
     }
   }
 
-  for (int j0 = 0; j0 < nj; j0 += DEPTH) {
+  // One block of the wave's range (j its index among the wave's blocks, d
+  // its prefetch buffer; AT_PUT: the newest token's block, put_j).  A macro,
+  // not a lambda: the lambda form measured ~1 % slower on the 16-bit decode
+  // steps (its code differs in register allocation and waits).
+#define PKV_DECODE_BLOCK(j, d, AT_PUT) \
+  do {                                 \
+          if (AT_PUT) {                                                                          \
+            /* the newest token's slot: the values made above, not the pool's */                 \
+            if (row == ns.tin) {                                                                 \
+  _Pragma("unroll")                                                                              \
+              for (int s = 0; s < SL; ++s)                                                       \
+                kbuf[d][s] = *reinterpret_cast<const uint4*>(                                    \
+                    &new_row[0][(4 * s + grp) * (16 / sizeof(TP))]);                             \
+            }                                                                                    \
+            if (grp == ns.tin / 4) {                                                             \
+              const int e = ns.tin & 3;  /* token 4 grp + e of the lane's V registers */         \
+  _Pragma("unroll")                                                                              \
+              for (int n = 0; n < NT; ++n) {                                                     \
+                const uint32_t vnew = uint32_t(new_row[1][16 * n + row]);                        \
+                if constexpr (FP8) {                                                             \
+                  const uint32_t mask = 0xFFu << (8 * e);                                        \
+                  vbuf[d][n].x = (vbuf[d][n].x & ~mask) | (vnew << (8 * e));                     \
+                } else {                                                                         \
+                  const uint32_t mask = 0xFFFFu << (16 * (e & 1));                               \
+                  const uint32_t bits = vnew << (16 * (e & 1));                                  \
+                  uint32_t x = vbuf[d][n].x, y = vbuf[d][n].y;                                   \
+                  if (e < 2) x = (x & ~mask) | bits;                                             \
+                  else y = (y & ~mask) | bits;                                                   \
+                  vbuf[d][n] = make_uint2(x, y);                                                 \
+                }                                                                                \
+              }                                                                                  \
+            }                                                                                    \
+            /* The block's K and V planes go back to the pool whole, with the */                 \
+            /* token in place: full lines, where the token's own elements would */               \
+            /* be partial writes to every line of the V plane.  (The slot's */                   \
+            /* block id was read when this block was issued.) */                                 \
+            if (unsigned(put_blk) < unsigned(p.num_blocks)) {                                    \
+              char* kp = const_cast<char*>(kbase) + int64_t(put_blk) * p.p_block;                \
+              char* vp = const_cast<char*>(vbase) + int64_t(put_blk) * p.p_block;                \
+  _Pragma("unroll")                                                                              \
+              for (int s = 0; s < SL; ++s) st16_stream(kp + (64 * s + lane) * 16, kbuf[d][s]);   \
+  _Pragma("unroll")                                                                              \
+              for (int n = 0; n < NT; ++n) {                                                     \
+                if constexpr (FP8) st4_stream(vp + (16 * n + row) * 16 + grp * 4, vbuf[d][n].x); \
+                else st8_stream(vp + (16 * n + row) * 32 + grp * 8, vbuf[d][n]);                 \
+              }                                                                                  \
+            }                                                                                    \
+          }                                                                                      \
+          /* every tile's scores before the next block's loads reuse kbuf[d] */                  \
+          f32x4_t sc[NG];                                                                        \
+  _Pragma("unroll")                                                                              \
+          for (int t = 0; t < NG; ++t) sc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};                      \
+          if constexpr (FP8) {                                                                   \
+  _Pragma("unroll")                                                                              \
+            for (int s = 0; s < SL; ++s) {                                                       \
+              const uint4 w = kbuf[d][s];                                                        \
+              const uint2 a0 = e4m3x4_to_f16x4(w.x), a1 = e4m3x4_to_f16x4(w.y);                  \
+              const uint2 a2 = e4m3x4_to_f16x4(w.z), a3 = e4m3x4_to_f16x4(w.w);                  \
+              const uint4 k0 = make_uint4(a0.x, a0.y, a1.x, a1.y);                               \
+              const uint4 k1 = make_uint4(a2.x, a2.y, a3.x, a3.y);                               \
+  _Pragma("unroll")                                                                              \
+              for (int t = 0; t < NG; ++t) {                                                     \
+                sc[t] = Mfma<OT>::qk(k0, qreg[t][2 * s], sc[t]);                                 \
+                sc[t] = Mfma<OT>::qk(k1, qreg[t][2 * s + 1], sc[t]);                             \
+              }                                                                                  \
+            }                                                                                    \
+          } else {                                                                               \
+  _Pragma("unroll")                                                                              \
+            for (int s = 0; s < S; ++s)                                                          \
+  _Pragma("unroll")                                                                              \
+              for (int t = 0; t < NG; ++t) sc[t] = Mfma<OT>::qk(kbuf[d][s], qreg[t][s], sc[t]);  \
+          }                                                                                      \
+          uint2 vcur[NT];                                                                        \
+  _Pragma("unroll")                                                                              \
+          for (int n = 0; n < NT; ++n)                                                           \
+            vcur[n] = FP8 ? e4m3x4_to_f16x4(vbuf[d][n].x) : vbuf[d][n];                          \
+          const bool blk_ok = okbuf[d];                                                          \
+          /* this block's scales, before the next issue reuses the slot */                       \
+          const float ksb = kscb[d], vsb = vscb[d];                                              \
+          if (j + DEPTH < nj) issue(j + DEPTH, d);                                               \
+                                                                                                 \
+          const int valid = it.n_tokens - (wave + j * NW) * kBlock;  /* tokens in range */       \
+          /* Slots of this block before a sliding window's start (positive only */               \
+          /* in the window's first block). */                                                    \
+          const int skip = it.lo - (it.t_begin + (wave + j * NW) * kBlock);                      \
+          /* Scaled scores; slots outside [lo, end) or of a rejected block id */                 \
+          /* get -inf.  A whole block (the common case; wave-uniform) needs no */                \
+          /* masks, and the masked case rewrites the values in place. */                         \
+          float s4[NG][4];                                                                       \
+          float smul = score_mul;                                                                \
+          if constexpr (blockwise) smul = p.scale_log2 * ksb;                                    \
+  _Pragma("unroll")                                                                              \
+          for (int t = 0; t < NG; ++t)                                                           \
+  _Pragma("unroll")                                                                              \
+            for (int r = 0; r < 4; ++r) s4[t][r] = sc[t][r] * smul;                              \
+          if (!(blk_ok && valid >= kBlock && skip <= 0)) {                                       \
+            /* The masked slots may hold anything, NaN included: zero their V */                 \
+            /* so that 0-weight * V stays 0.  Lane holds tokens 4*grp + e, */                    \
+            /* e = 0..3, as 16-bit halves of x, y. */                                            \
+            const int lim = blk_ok ? valid : 0;                                                  \
+            auto in = [&](int e) { return e < lim && e >= skip; };                               \
+            const uint32_t mx0 = (in(4 * grp + 0) ? 0x0000ffffu : 0u) |                          \
+                                 (in(4 * grp + 1) ? 0xffff0000u : 0u);                           \
+            const uint32_t mx1 = (in(4 * grp + 2) ? 0x0000ffffu : 0u) |                          \
+                                 (in(4 * grp + 3) ? 0xffff0000u : 0u);                           \
+  _Pragma("unroll")                                                                              \
+            for (int n = 0; n < NT; ++n) {                                                       \
+              vcur[n].x &= mx0;                                                                  \
+              vcur[n].y &= mx1;                                                                  \
+            }                                                                                    \
+  _Pragma("unroll")                                                                              \
+            for (int t = 0; t < NG; ++t)                                                         \
+  _Pragma("unroll")                                                                              \
+              for (int r = 0; r < 4; ++r)                                                        \
+                if (!in(4 * grp + r)) s4[t][r] = -INFINITY;                                      \
+          }                                                                                      \
+  _Pragma("unroll")                                                                              \
+          for (int t = 0; t < NG; ++t) {                                                         \
+            float mx = -INFINITY;                                                                \
+  _Pragma("unroll")                                                                              \
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s4[t][r]);                                \
+            mx = cols_max(mx);                                                                   \
+            /* Rescale the running state only when some head's maximum grows (a */               \
+            /* wave-uniform test): otherwise the factor would be exactly 1, and */               \
+            /* after the first blocks of a long range it rarely grows. */                        \
+            const bool grow = mx > m[t];  /* false while both are -inf */                        \
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {                                        \
+              /* 0 when m was -inf */                                                            \
+              const float alpha = grow ? __builtin_amdgcn_exp2f(m[t] - mx) : 1.f;                \
+              l[t] *= alpha;                                                                     \
+  _Pragma("unroll")                                                                              \
+              for (int n = 0; n < NT; ++n) acc[t][n] *= alpha;                                   \
+              m[t] = fmaxf(m[t], mx);                                                            \
+            }                                                                                    \
+            /* m is -inf only while every score seen so far is masked; then every */             \
+            /* s4 is -inf too and its weight must be 0. */                                       \
+            const float m_ref = m[t] == -INFINITY ? 0.f : m[t];                                  \
+            /* The hardware 2^x (about one ulp over the normal range): the */                    \
+            /* arguments are <= 0, and weights below 2^-126, which it may flush */               \
+            /* to 0, are far below one ulp of the sum (at least 1). */                           \
+            float pr[4];                                                                         \
+  _Pragma("unroll")                                                                              \
+            for (int r = 0; r < 4; ++r) {                                                        \
+              pr[r] = __builtin_amdgcn_exp2f(s4[t][r] - m_ref);                                  \
+              l[t] += pr[r];                                                                     \
+            }                                                                                    \
+            /* 16-bit pools: P as a 16-bit high part plus a 16-bit residual, */                  \
+            /* two MFMAs (a single bf16 P could exceed the tolerance).  fp8 */                   \
+            /* pools: P rounded once to float16 (relative error at most 2^-12, */                \
+            /* far inside the tolerance), one MFMA. */                                           \
+            constexpr bool LO = !FP8;                                                            \
+            uint16_t ph[4], pl[4];                                                               \
+  _Pragma("unroll")                                                                              \
+            for (int r = 0; r < 4; ++r) {                                                        \
+              if constexpr (LO) Mfma<OT>::split(pr[r], ph[r], pl[r]);                            \
+              else ph[r] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(pr[r]));           \
+            }                                                                                    \
+            const uint2 bh = make_uint2(uint32_t(ph[0]) | (uint32_t(ph[1]) << 16),               \
+                                        uint32_t(ph[2]) | (uint32_t(ph[3]) << 16));              \
+            uint2 bl = make_uint2(0, 0);                                                         \
+            if constexpr (LO)                                                                    \
+              bl = make_uint2(uint32_t(pl[0]) | (uint32_t(pl[1]) << 16),                         \
+                              uint32_t(pl[2]) | (uint32_t(pl[3]) << 16));                        \
+            if constexpr (blockwise) {                                                           \
+              /* this block's P·V on its own, then scaled by its V scale */                      \
+  _Pragma("unroll")                                                                              \
+              for (int n = 0; n < NT; ++n) {                                                     \
+                f32x4_t b = Mfma<OT>::pv(vcur[n], bh, f32x4_t{0.f, 0.f, 0.f, 0.f});              \
+                if constexpr (LO) b = Mfma<OT>::pv(vcur[n], bl, b);                              \
+  _Pragma("unroll")                                                                              \
+                for (int r = 0; r < 4; ++r) acc[t][n][r] = fmaf(vsb, b[r], acc[t][n][r]);        \
+              }                                                                                  \
+            } else {                                                                             \
+  _Pragma("unroll")                                                                              \
+              for (int n = 0; n < NT; ++n) {                                                     \
+                acc[t][n] = Mfma<OT>::pv(vcur[n], bh, acc[t][n]);                                \
+                if constexpr (LO) acc[t][n] = Mfma<OT>::pv(vcur[n], bl, acc[t][n]);              \
+              }                                                                                  \
+            }                                                                                    \
+          } \
+  } while (0)
+  // fp8 pools run the newest token's block, the wave's last (put_j ==
+  // nj - 1), after the loop, so the loop carries none of the append's values
+  // and tests (their decode step measured 2-3 % faster that way); 16-bit pools
+  // test for it in the loop (the separate block measured ~1 % slower there).
+  if constexpr (FP8) {
+    const int nmain = put_j >= 0 ? put_j : nj;
+    for (int j0 = 0; j0 < nmain; j0 += DEPTH) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int j = j0 + d;
-      if (j < nj) {
-        if (PUT && j == put_j) {
-          // the newest token's slot: the values made above, not the pool's
-          if (row == ns.tin) {
+      for (int d = 0; d < DEPTH; ++d) {
+        const int j = j0 + d;
+        if (j < nmain) PKV_DECODE_BLOCK(j, d, false);
+      }
+    }
+    if constexpr (PUT) {
+      if (put_j >= 0) {
+        const int j = put_j, d = put_j % DEPTH;
+        PKV_DECODE_BLOCK(j, d, true);
+      }
+    }
+  } else {
+    for (int j0 = 0; j0 < nj; j0 += DEPTH) {
 #pragma unroll
-            for (int s = 0; s < SL; ++s)
-              kbuf[d][s] = *reinterpret_cast<const uint4*>(
-                  &new_row[0][(4 * s + grp) * (16 / sizeof(TP))]);
-          }
-          if (grp == ns.tin / 4) {
-            const int e = ns.tin & 3;  // token 4 grp + e of the lane's V registers
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-              const uint32_t vnew = uint32_t(new_row[1][16 * n + row]);
-              if constexpr (FP8) {
-                const uint32_t mask = 0xFFu << (8 * e);
-                vbuf[d][n].x = (vbuf[d][n].x & ~mask) | (vnew << (8 * e));
-              } else {
-                const uint32_t mask = 0xFFFFu << (16 * (e & 1));
-                const uint32_t bits = vnew << (16 * (e & 1));
-                uint32_t x = vbuf[d][n].x, y = vbuf[d][n].y;
-                if (e < 2) x = (x & ~mask) | bits;
-                else y = (y & ~mask) | bits;
-                vbuf[d][n] = make_uint2(x, y);
-              }
-            }
-          }
-          // The block's K and V planes go back to the pool whole, with the
-          // token in place: full lines, where the token's own elements would
-          // be partial writes to every line of the V plane.  (The slot's
-          // block id was read when this block was issued.)
-          if (unsigned(put_blk) < unsigned(p.num_blocks)) {
-            char* kp = const_cast<char*>(kbase) + int64_t(put_blk) * p.p_block;
-            char* vp = const_cast<char*>(vbase) + int64_t(put_blk) * p.p_block;
-#pragma unroll
-            for (int s = 0; s < SL; ++s) st16_stream(kp + (64 * s + lane) * 16, kbuf[d][s]);
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-              if constexpr (FP8) st4_stream(vp + (16 * n + row) * 16 + grp * 4, vbuf[d][n].x);
-              else st8_stream(vp + (16 * n + row) * 32 + grp * 8, vbuf[d][n]);
-            }
-          }
-        }
-        // every tile's scores before the next block's loads reuse kbuf[d]
-        f32x4_t sc[NG];
-#pragma unroll
-        for (int t = 0; t < NG; ++t) sc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if constexpr (FP8) {
-#pragma unroll
-          for (int s = 0; s < SL; ++s) {
-            const uint4 w = kbuf[d][s];
-            const uint2 a0 = e4m3x4_to_f16x4(w.x), a1 = e4m3x4_to_f16x4(w.y);
-            const uint2 a2 = e4m3x4_to_f16x4(w.z), a3 = e4m3x4_to_f16x4(w.w);
-            const uint4 k0 = make_uint4(a0.x, a0.y, a1.x, a1.y);
-            const uint4 k1 = make_uint4(a2.x, a2.y, a3.x, a3.y);
-#pragma unroll
-            for (int t = 0; t < NG; ++t) {
-              sc[t] = Mfma<OT>::qk(k0, qreg[t][2 * s], sc[t]);
-              sc[t] = Mfma<OT>::qk(k1, qreg[t][2 * s + 1], sc[t]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int s = 0; s < S; ++s)
-#pragma unroll
-            for (int t = 0; t < NG; ++t) sc[t] = Mfma<OT>::qk(kbuf[d][s], qreg[t][s], sc[t]);
-        }
-        uint2 vcur[NT];
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-          vcur[n] = FP8 ? e4m3x4_to_f16x4(vbuf[d][n].x) : vbuf[d][n];
-        const bool blk_ok = okbuf[d];
-        // this block's scales, before the next issue reuses the slot
-        const float ksb = kscb[d], vsb = vscb[d];
-        if (j + DEPTH < nj) issue(j + DEPTH, d);
-
-        const int valid = it.n_tokens - (wave + j * NW) * kBlock;  // tokens in range
-        // Slots of this block before a sliding window's start (positive only
-        // in the window's first block).
-        const int skip = it.lo - (it.t_begin + (wave + j * NW) * kBlock);
-        // Scaled scores; slots outside [lo, end) or of a rejected block id
-        // get -inf.  A whole block (the common case; wave-uniform) needs no
-        // masks, and the masked case rewrites the values in place.
-        float s4[NG][4];
-        float smul = score_mul;
-        if constexpr (blockwise) smul = p.scale_log2 * ksb;
-#pragma unroll
-        for (int t = 0; t < NG; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) s4[t][r] = sc[t][r] * smul;
-        if (!(blk_ok && valid >= kBlock && skip <= 0)) {
-          // The masked slots may hold anything, NaN included: zero their V
-          // so that 0-weight * V stays 0.  Lane holds tokens 4*grp + e,
-          // e = 0..3, as 16-bit halves of x, y.
-          const int lim = blk_ok ? valid : 0;
-          auto in = [&](int e) { return e < lim && e >= skip; };
-          const uint32_t mx0 = (in(4 * grp + 0) ? 0x0000ffffu : 0u) |
-                               (in(4 * grp + 1) ? 0xffff0000u : 0u);
-          const uint32_t mx1 = (in(4 * grp + 2) ? 0x0000ffffu : 0u) |
-                               (in(4 * grp + 3) ? 0xffff0000u : 0u);
-#pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            vcur[n].x &= mx0;
-            vcur[n].y &= mx1;
-          }
-#pragma unroll
-          for (int t = 0; t < NG; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (!in(4 * grp + r)) s4[t][r] = -INFINITY;
-        }
-#pragma unroll
-        for (int t = 0; t < NG; ++t) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s4[t][r]);
-          mx = cols_max(mx);
-          // Rescale the running state only when some head's maximum grows (a
-          // wave-uniform test): otherwise the factor would be exactly 1, and
-          // after the first blocks of a long range it rarely grows.
-          const bool grow = mx > m[t];  // false while both are -inf
-          if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            // 0 when m was -inf
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m[t] - mx) : 1.f;
-            l[t] *= alpha;
-#pragma unroll
-            for (int n = 0; n < NT; ++n) acc[t][n] *= alpha;
-            m[t] = fmaxf(m[t], mx);
-          }
-          // m is -inf only while every score seen so far is masked; then every
-          // s4 is -inf too and its weight must be 0.
-          const float m_ref = m[t] == -INFINITY ? 0.f : m[t];
-          // The hardware 2^x (about one ulp over the normal range): the
-          // arguments are <= 0, and weights below 2^-126, which it may flush
-          // to 0, are far below one ulp of the sum (at least 1).
-          float pr[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            pr[r] = __builtin_amdgcn_exp2f(s4[t][r] - m_ref);
-            l[t] += pr[r];
-          }
-          uint16_t ph[4], pl[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) Mfma<OT>::split(pr[r], ph[r], pl[r]);
-          const uint2 bh = make_uint2(uint32_t(ph[0]) | (uint32_t(ph[1]) << 16),
-                                      uint32_t(ph[2]) | (uint32_t(ph[3]) << 16));
-          const uint2 bl = make_uint2(uint32_t(pl[0]) | (uint32_t(pl[1]) << 16),
-                                      uint32_t(pl[2]) | (uint32_t(pl[3]) << 16));
-          if constexpr (blockwise) {
-            // this block's P·V on its own, then scaled by its V scale
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-              f32x4_t b = Mfma<OT>::pv(vcur[n], bh, f32x4_t{0.f, 0.f, 0.f, 0.f});
-              b = Mfma<OT>::pv(vcur[n], bl, b);
-#pragma unroll
-              for (int r = 0; r < 4; ++r) acc[t][n][r] = fmaf(vsb, b[r], acc[t][n][r]);
-            }
-          } else {
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-              acc[t][n] = Mfma<OT>::pv(vcur[n], bh, acc[t][n]);
-              acc[t][n] = Mfma<OT>::pv(vcur[n], bl, acc[t][n]);
-            }
-          }
-        }
+      for (int d = 0; d < DEPTH; ++d) {
+        const int j = j0 + d;
+        if (j < nj) PKV_DECODE_BLOCK(j, d, PUT && j == put_j);
       }
     }
   }
+#undef PKV_DECODE_BLOCK
 
 #pragma unroll
   for (int t = 0; t < NG; ++t) {
