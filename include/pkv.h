@@ -454,10 +454,13 @@ pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int3
                                 size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
- * One decode step's append and attention in one launch ([KV essay] "The
+ * One decode step's append and attention, in one launch ([KV essay] "The
  * fix": each generated token's K/V entry is appended and the step attends
  * over the cache including it; [InferScale] §2: the key is stored rotated at
- * its own position).  Equal, byte for byte in the pool and in d_out/d_lse, to
+ * its own position).  Launches of many workgroups on 16-bit pools (at least
+ * 16 per CU, e.g. ragged batches of short sequences) run it as two launches,
+ * the append and then attention alone, which measured faster there; the
+ * results are the same.  Equal, byte for byte in the pool and in d_out/d_lse, to
  *   pkv_append_kv(pool, layer, d_tables, table_stride, first_pos = lens - 1,
  *                 n_seqs, 1, d_k_new, d_v_new, q_dtype, rope_mode, d_cos,
  *                 d_sin, max_pos)
@@ -490,7 +493,8 @@ pkv_status pkv_append_decode_attention(const pkv_plan* plan, const pkv_pool* poo
  * tight serving loops, harnesses that forbid allocation.  Same arguments,
  * checks, results and stream behaviour as pkv_append_decode_attention, except
  * that there is no workspace argument and no separate plan upload: the
- * plan's work list (24 bytes per item, 16 per split sequence) is copied from
+ * plan's work list (24 bytes per item, 16 per split sequence, 4 per
+ * sequence for its newest position) is copied from
  * the plan's host memory into a static device scratch buffer on `stream`,
  * and the kernels use that buffer for the work list and the partial states
  * of split sequences.  The scratch holds PKV_NOALLOC_SCRATCH_BYTES (16 MiB)

@@ -251,7 +251,9 @@ struct pkv_plan {
   int32_t n_slots = 0, waves = 1;
   std::vector<DecodeItem> items;
   std::vector<MergeSeq> merges;
-  size_t off_items = 0, off_merges = 0, off_part_o = 0, off_part_ml = 0, ws_bytes = 0;
+  std::vector<int32_t> newest;  // per sequence: lens - 1 (-1: empty)
+  size_t off_items = 0, off_merges = 0, off_pos = 0, off_part_o = 0, off_part_ml = 0,
+         ws_bytes = 0;
   Staging staging;
 };
 
@@ -1062,11 +1064,15 @@ pkv_status pkv_decode_plan_create(const int64_t* lens, int32_t n_seqs, int32_t n
   std::stable_sort(plan->items.begin(), plan->items.end(),
                    [](const DecodeItem& x, const DecodeItem& y) { return x.n_tokens > y.n_tokens; });
   plan->n_slots = slots;
+  plan->newest.resize(size_t(n_seqs));
+  for (int32_t b = 0; b < n_seqs; ++b) plan->newest[b] = int32_t(lens[b] - 1);
   size_t off = 0;
   plan->off_items = off;
   off = align_up(off + plan->items.size() * sizeof(DecodeItem), 256);
   plan->off_merges = off;
   off = align_up(off + plan->merges.size() * sizeof(MergeSeq), 256);
+  plan->off_pos = off;
+  off = align_up(off + plan->newest.size() * sizeof(int32_t), 256);
   plan->off_part_o = off;
   off = align_up(off + size_t(slots) * n_q_heads * head_dim * sizeof(float), 256);
   plan->off_part_ml = off;
@@ -1106,6 +1112,8 @@ pkv_status pkv_decode_plan_upload(pkv_plan* plan, void* d_ws, size_t ws_bytes, v
               plan->items.size() * sizeof(DecodeItem));
   std::memcpy(static_cast<char*>(host) + plan->off_merges, plan->merges.data(),
               plan->merges.size() * sizeof(MergeSeq));
+  std::memcpy(static_cast<char*>(host) + plan->off_pos, plan->newest.data(),
+              plan->newest.size() * sizeof(int32_t));
   if (pkv_status st = plan->staging.upload(d_ws, bytes, static_cast<hipStream_t>(stream)))
     return st;
   return ok();
@@ -1191,6 +1199,8 @@ pkv_status decode_common(const pkv_plan* plan, const pkv_pool* pool, int32_t lay
   a.cos_t = nt.cos;
   a.sin_t = nt.sin;
   a.max_pos = nt.max_pos;
+  a.put_pos = reinterpret_cast<const int32_t*>(ws + plan->off_pos);
+  a.n_seqs = plan->n_seqs;
   a.timed = !upload_plan;
   int variant = 0;
   if (const char* env = std::getenv("PKV_DECODE_KERNEL")) variant = std::atoi(env);
@@ -1204,6 +1214,9 @@ pkv_status decode_common(const pkv_plan* plan, const pkv_pool* pool, int32_t lay
     if (e == hipSuccess && !plan->merges.empty())
       e = hipMemcpyAsync(ws + plan->off_merges, plan->merges.data(),
                          plan->merges.size() * sizeof(MergeSeq), hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess && !plan->newest.empty())
+      e = hipMemcpyAsync(ws + plan->off_pos, plan->newest.data(),
+                         plan->newest.size() * sizeof(int32_t), hipMemcpyHostToDevice, hs);
     if (e != hipSuccess) return hip_fail(e, "work list copy into the static scratch");
   }
   hipError_t e = pkv::launch_decode(*pool, layer, a, variant, hs);

@@ -78,6 +78,11 @@ struct DecodeArgs {
   const float* cos_t;
   const float* sin_t;
   int max_pos;
+  // Each sequence's newest position (lens - 1, -1 for an empty sequence),
+  // device int32[n_seqs] in the workspace: for launches that append in a
+  // launch of their own before attention alone.
+  const int32_t* put_pos;
+  int n_seqs;
   // false: never attach timing events (the allocation-free entry point)
   bool timed;
 };

@@ -1932,18 +1932,35 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
     const int ng = p.group <= 16 ? 1 : p.group <= 32 ? 2 : p.group <= 64 ? 4 : 0;
     const bool mfma = (kernel_variant != 1 || pool.dtype == PKV_FP8E4M3) &&
                       pool.dtype != PKV_F32 && ng > 0;
-    // The decode step's append (new token rows given) runs the PUT instance,
-    // an fp8 pool with per-block scales the BLK one.
-    const bool put = a.new_k != nullptr;
-    const bool blk = pool.dtype == PKV_FP8E4M3 && pool.scale_mode == 1;
-    // One block in flight per wave measured fastest with 8 waves per workgroup
-    // (depth 2 is instantiated for attention alone only).
-    const int depth = kernel_variant == 12 && !put ? 2 : 1;
     // More tiles hold more accumulators: 2 tiles fit 8 waves per workgroup
     // (two per SIMD), 4 tiles one wave per SIMD.
     int nw = a.waves;
     if (ng == 2) nw = nw >= 8 ? 8 : 4;
     if (ng == 4) nw = 4;
+    // The decode step's append (new token rows given) runs the PUT instance,
+    // an fp8 pool with per-block scales the BLK one.  Exception: a 16-bit
+    // pool's one-tile, 8-wave launch of at least 16 workgroups per CU (ragged
+    // batches of short sequences) appends in a launch of its own first and
+    // then runs attention alone, which gives the same bytes and outputs.
+    // That PUT instance needs more than 128 VGPRs, so one of its workgroups
+    // fits per CU, where attention alone runs two and hides each one's
+    // start-up behind the other's loads; on ragged MHA (16,384 workgroups)
+    // the two launches measured 2.14 ms against 2.22 ms for one (on the
+    // 8B-shaped layer, 512 workgroups, one launch is the faster: 100 against
+    // 106 us).
+    bool put = a.new_k != nullptr;
+    if (put && mfma && ng == 1 && nw == 8 && pool.dtype != PKV_FP8E4M3 && a.put_pos &&
+        grid.x >= 16u * unsigned(device_cus())) {
+      e = launch_append(pool, layer, a.tables, a.table_stride, a.put_pos, a.n_seqs, 1, a.new_k,
+                        a.new_v, a.q_dtype, a.rope_mode, a.cos_t, a.sin_t, a.max_pos, stream);
+      if (e != hipSuccess) return e;
+      put = false;
+      p.new_k = p.new_v = nullptr;
+    }
+    const bool blk = pool.dtype == PKV_FP8E4M3 && pool.scale_mode == 1;
+    // One block in flight per wave measured fastest with 8 waves per workgroup
+    // (depth 2 is instantiated for attention alone only).
+    const int depth = kernel_variant == 12 && !put ? 2 : 1;
     // 8-wave launches with fewer than 16 workgroups per CU run one workgroup
     // per CU (see one_per_cu_lds); many-workgroup launches (ragged batches)
     // may run two, which hides each workgroup's start-up behind another's

@@ -194,6 +194,38 @@ def test_llama8b_step_full():
              q, k, v, st["tables"])
 
 
+def test_many_workgroups_step_appends_in_its_own_launch():
+    """A launch of at least 16 workgroups per CU (128 sequences x 32 KV heads
+    of 520..700 tokens, f16 and bf16, one sequence empty): the step appends in
+    a launch of its own and then runs attention alone.  Pool, out and lse
+    byte for byte those of the two calls; every live sequence against the
+    oracle; the empty sequence gets no write."""
+    import torch
+    from tests import gpu_util as gu
+    from workloads.configs import deal_tables, host_normal
+    for dtype, seed in (("f16", 31), ("bf16", 32)):
+        rng = np.random.default_rng(seed)
+        B, hkv, hq, d = 128, 32, 32, 128
+        lens = rng.integers(520, 700, size=B).astype(np.int64)
+        lens[7] = 0
+        need = int(sum(-(-int(x) // 16) for x in lens))
+        nb = need + 8
+        table = deal_tables(rng.permutation(nb)[:need].astype(np.int32), lens, 64)
+        gu.say("many-workgroup step", dtype, "pool", nb, "blocks")
+        dp = gu.DevicePool(1, nb, hkv, d, dtype)
+        _fill_normal(dp, seed)
+        max_pos = int(lens.max())
+        _attach_rope(dp, max_pos)
+        q = host_normal(rng, (B, hq, d), dtype)
+        q_dev = gu.to_device_raw(q.reshape(-1), dtype).view(q.shape)
+        tdev = torch.from_numpy(table).cuda()
+        k, v, kd, vd = _new_rows(rng, B, hkv, d, dtype)
+        run_step(dp, 0, lens, hq, q_dev, tdev, kd, vd, "pairs", dtype, max_pos, None, q, k, v,
+                 table)
+        del dp
+        torch.cuda.empty_cache()
+
+
 def test_ragged_mha_step_sampled():
     """The ragged MHA batch (256 sequences, lognormal lengths, 64 KV heads,
     f16): 24 sequences (shortest, longest, random) against the oracle, all of

@@ -1,6 +1,6 @@
 """The allocation-free decode step (pkv_append_decode_attention_noalloc,
-for callers that cannot allocate): on two calls in a row, the second with a
-smaller input, its pool writes, out and lse equal those of
+for callers that cannot allocate): on calls in a row, each with a smaller
+input than the one before, its pool writes, out and lse equal those of
 pkv_append_decode_attention with a caller workspace, byte for byte; a plan
 whose workspace exceeds the static scratch is refused before anything is
 enqueued."""
@@ -82,7 +82,13 @@ def _one_call_pair(dtype, hq, hkv, d, lens, part, mode, seed):
 
 @pytest.mark.gpu
 def test_noalloc_step_equals_workspace_step_on_two_calls():
-    # first call: split sequences (partial states and the merge use the scratch)
+    # a launch of 16 workgroups per CU or more (128 sequences x 32 KV heads,
+    # one empty): the step appends in a launch of its own, from the newest
+    # positions the call copies into the scratch
+    lens = np.random.default_rng(13).integers(520, 700, size=128)
+    lens[5] = 0
+    _one_call_pair("f16", 32, 32, 128, lens.tolist(), 0, "pairs", 13)
+    # split sequences (partial states and the merge use the scratch)
     _one_call_pair("bf16", 32, 8, 128, [3000, 17, 1, 0, 900, 2048, 5000, 600], 512, "pairs", 11)
     # second call, smaller: fewer, shorter sequences, another format; the scratch
     # still holds the first call's work list and partials
