@@ -753,6 +753,12 @@ __device__ inline uint2 e4m3x4_to_f16x4(uint32_t w) {
   return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8): wait until at most n vector-memory operations are
+// outstanding; wait for every LDS/scalar operation.
+constexpr int wait_vm_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int wait_lgkm0_imm() { return 15 | (3 << 14) | (7 << 4); }
+
 // Decode kernel template parameters: KVDT the pool format, QDT the query
 // format (equal to KVDT, or BF16/F16 for an fp8 pool whose MFMA operands are
 // float16), head dim D, prefetch depth, waves per workgroup NW, NG tiles of
@@ -865,6 +871,19 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
   // Block ids are read one issue ahead (issues come in order j = 0, 1, ...),
   // so the scalar load's latency does not sit between a block's arrival and
   // the next block's loads.
+  // Staged instance (attention alone, one tile, 8 waves, 16-bit pools, two
+  // blocks in flight per wave: kernel variant 12): each block's K and V
+  // planes go to the wave's LDS buffer d by direct loads (global_load_lds,
+  // 1 KiB per instruction, no VGPRs while in flight) and are read from there
+  // when the block is taken.  The compiler does not track direct loads
+  // against LDS reads, so the waits are explicit: before block j the wave
+  // waits until only block j + 1's loads are outstanding (loads complete in
+  // order), and before refilling buffer d it waits for its LDS reads.  Same
+  // values and order as the register path, so the results are bit-identical.
+  constexpr bool STAGE = !PUT && NG == 1 && NW == 8 && !FP8 && DEPTH == 2;
+  constexpr int PLANE = kBlock * D * 2;           // bytes of a K or a V plane
+  constexpr int NDL = 2 * PLANE / 1024;           // direct loads per block
+  __shared__ __align__(16) char stage[STAGE ? NW : 1][2][STAGE ? 2 * PLANE : 16];
   int blk_next = nj > 0 ? tab[wave] : 0;
   auto issue = [&](int j, int d) {
     int blk = blk_next;
@@ -879,6 +898,20 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
     }
     const char* kp = kbase + int64_t(blk) * p.p_block;
     const char* vp = vbase + int64_t(blk) * p.p_block;
+    if constexpr (STAGE) {
+      typedef __attribute__((address_space(3))) void* lds_ptr;
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int c = 0; c < PLANE / 1024; ++c)  // aux 2: non-temporal, as ld16_stream
+        __builtin_amdgcn_global_load_lds(kp + c * 1024 + lane * 16,
+                                         (lds_ptr)&stage[wave][d][c * 1024], 16, 0, 2);
+#pragma unroll
+      for (int c = 0; c < PLANE / 1024; ++c)
+        __builtin_amdgcn_global_load_lds(vp + c * 1024 + lane * 16,
+                                         (lds_ptr)&stage[wave][d][PLANE + c * 1024], 16, 0, 2);
+      asm volatile("" ::: "memory");
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < SL; ++s) kbuf[d][s] = ld16_stream(kp + (64 * s + lane) * 16);
 #pragma unroll
@@ -994,6 +1027,18 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
               }                                                                                  \
             }                                                                                    \
           }                                                                                      \
+          if constexpr (STAGE) {                                                                 \
+            asm volatile("" ::: "memory");                                                       \
+            if (j + 1 < nj) __builtin_amdgcn_s_waitcnt(wait_vm_imm(NDL));                        \
+            else __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));                                     \
+            asm volatile("" ::: "memory");                                                       \
+            _Pragma("unroll")                                                                    \
+            for (int s2 = 0; s2 < SL; ++s2)                                                      \
+              kbuf[d][s2] = *(const uint4*)&stage[wave][d][(64 * s2 + lane) * 16];              \
+            _Pragma("unroll")                                                                    \
+            for (int n = 0; n < NT; ++n)                                                         \
+              vbuf[d][n] = *(const uint2*)&stage[wave][d][PLANE + (16 * n + row) * 32 + grp * 8]; \
+          }                                                                                      \
           /* every tile's scores before the next block's loads reuse kbuf[d] */                  \
           f32x4_t sc[NG];                                                                        \
   _Pragma("unroll")                                                                              \
@@ -1025,6 +1070,11 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
           const bool blk_ok = okbuf[d];                                                          \
           /* this block's scales, before the next issue reuses the slot */                       \
           const float ksb = kscb[d], vsb = vscb[d];                                              \
+          if constexpr (STAGE) {  /* this block's LDS reads are done before buffer d refills */ \
+            asm volatile("" ::: "memory");                                                       \
+            __builtin_amdgcn_s_waitcnt(wait_lgkm0_imm());                                        \
+            asm volatile("" ::: "memory");                                                       \
+          }                                                                                      \
           if (j + DEPTH < nj) issue(j + DEPTH, d);                                               \
                                                                                                  \
           const int valid = it.n_tokens - (wave + j * NW) * kBlock;  /* tokens in range */       \
@@ -1168,7 +1218,17 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
     // LDS; wave w then sums output tiles w, w + NW, ... over all waves in
     // fixed order (wave 0, 1, ...).
     __shared__ float sm_m[NW][16], sm_l[NW][16];
-    __shared__ float sm_o[NW][16][D + 4];
+    // (the staged instance parks the partial outputs in its staging buffers,
+    // which every wave has finished with by the first barrier below)
+    typedef float SmO[16][D + 4];
+    SmO* sm_o;
+    if constexpr (STAGE) {
+      static_assert(sizeof(SmO) * NW <= sizeof(stage), "merge buffers fit the staging area");
+      sm_o = reinterpret_cast<SmO*>(&stage[0][0][0]);
+    } else {
+      __shared__ float sm_o_arr[NW][16][D + 4];
+      sm_o = sm_o_arr;
+    }
 #pragma unroll
     for (int t = 0; t < NG; ++t) {
       if (t > 0) __syncthreads();  // the previous tile's reads of LDS are done
@@ -1927,7 +1987,9 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
     dim3 grid(unsigned(a.n_items) * unsigned(pool.n_kv_heads));
     // variant: 0 automatic, 1 generic VALU kernel (not for fp8 pools), 2 packed
     // dot products on the VALU where they apply (decode_dot2_kernel), 10 + k
-    // MFMA kernel with a prefetch depth of k blocks (k = 1, 2).
+    // MFMA kernel with a prefetch depth of k blocks (k = 1, 2; for attention
+    // alone with one tile, 8 waves and a 16-bit pool, depth 2 stages K and V
+    // through LDS by direct loads).
     // Tiles of 16 query heads per KV head: groups up to 64 run on MFMA.
     const int ng = p.group <= 16 ? 1 : p.group <= 32 ? 2 : p.group <= 64 ? 4 : 0;
     const bool mfma = (kernel_variant != 1 || pool.dtype == PKV_FP8E4M3) &&

@@ -38,6 +38,8 @@ def check_decode_all(dp, layer, q_raw, table, lens, hq, parts=(0,), variants=("a
             os.environ["PKV_DECODE_KERNEL"] = "1"
         elif variant == "dot2":
             os.environ["PKV_DECODE_KERNEL"] = "2"
+        elif variant == "staged":
+            os.environ["PKV_DECODE_KERNEL"] = "12"
         try:
             for part in parts:
                 out, lse = gu.decode(dp, layer, q_dev, tables_dev, lens, hq, part)
@@ -306,3 +308,34 @@ def test_dot2_kernel_small_groups(dtype, hq, hkv, d):
         os.environ.pop("PKV_DECODE_KERNEL", None)
     out0, _ = gu.decode(dp, 0, q_dev, tdev, lens, hq, 0)
     assert not torch.equal(out2, out0), "the packed-dot-product kernel did not run"
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("f16", 64, 64, 128),
+                                           ("bf16", 8, 8, 64), ("f16", 16, 4, 64)])
+def test_lds_staged_variant(dtype, hq, hkv, d):
+    """Attention alone with K and V staged through LDS by direct loads (kernel
+    variant 12: one tile, 8-wave workgroups, two blocks in flight per wave)
+    against the oracle, with partial last blocks, an empty sequence and split
+    ranges; and bit for bit equal to the default kernel, which takes the same
+    values in the same order from registers."""
+    import torch
+    from tests import gpu_util as gu
+    from workloads.configs import host_normal, deal_tables
+    rng = np.random.default_rng(hq * 13 + hkv + d)
+    lens = np.array([600, 1500, 2047, 900, 3000, 17, 0, 700, 1024, 515], dtype=np.int64)
+    need = int(sum(-(-x // 16) for x in lens))
+    table = deal_tables(rng.permutation(need + 5)[:need].astype(np.int32), lens, 256)
+    dp = gu.DevicePool(1, need + 5, hkv, d, dtype)
+    fill_random_pool(dp, 37)
+    q = host_normal(rng, (len(lens), hq, d), dtype)
+    check_decode_all(dp, 0, q, table, lens, hq, parts=(0, 512), variants=("staged",))
+    q_dev = gu.to_device_raw(q.reshape(-1), dtype).view(q.shape)
+    tdev = torch.from_numpy(table).cuda()
+    for part in (0, 512):
+        os.environ["PKV_DECODE_KERNEL"] = "12"
+        try:
+            out12, lse12 = gu.decode(dp, 0, q_dev, tdev, lens, hq, part)
+        finally:
+            os.environ.pop("PKV_DECODE_KERNEL", None)
+        out0, lse0 = gu.decode(dp, 0, q_dev, tdev, lens, hq, part)
+        assert torch.equal(out12, out0) and torch.equal(lse12, lse0), "staged vs register path"
