@@ -440,7 +440,8 @@ int32_t pkv_decode_plan_part_tokens(const pkv_plan* plan);
  * softmax states in LDS; -1 for NULL. */
 int32_t pkv_decode_plan_waves(const pkv_plan* plan);
 
-/* Device workspace a plan needs (work list + float partials). */
+/* Device workspace a plan needs (work list, each sequence's newest position,
+ * float partials). */
 size_t pkv_decode_workspace_bytes(const pkv_plan* plan);
 
 /* Copy the plan's work list into the workspace (asynchronous on stream; the
