@@ -1566,7 +1566,10 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p,
 
   for (int h0 = 0; h0 < p.group; h0 += kValuHeads) {
     const int nh = min(kValuHeads, p.group - h0);
+    // (head loops run to kValuHeads, unrolled, with a uniform i < nh test, so
+    // the per-head arrays stay in registers)
     float qv[kValuHeads][QC * X];
+#pragma unroll
     for (int i = 0; i < kValuHeads; ++i) {
       const int hq = g * p.group + h0 + min(i, nh - 1);
       const T* qh = reinterpret_cast<const T*>(p.q + (int64_t(it.seq) * p.n_q_heads + hq) * D * E);
@@ -1576,6 +1579,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p,
         for (int e = 0; e < X; ++e) qv[i][c * X + e] = Fmt<DT>::to_f32(qh[(quarter * QC + c) * X + e]);
     }
     float m[kValuHeads], l[kValuHeads], acc[kValuHeads][DL];
+#pragma unroll
     for (int i = 0; i < kValuHeads; ++i) {
       m[i] = -INFINITY;
       l[i] = 0.f;
@@ -1596,7 +1600,9 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p,
 #pragma unroll
         for (int e = 0; e < X; ++e) kv[c * X + e] = Fmt<DT>::to_f32(chunk[e]);
       }
-      for (int i = 0; i < nh; ++i) {
+#pragma unroll
+      for (int i = 0; i < kValuHeads; ++i) {
+        if (i >= nh) continue;
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < QC * X; ++e) s = fmaf(qv[i][e], kv[e], s);
@@ -1636,7 +1642,9 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p,
 #pragma unroll
         for (int t = 0; t < kBlock; ++t)
           vv[t] = t < lim && t >= skip ? Fmt<DT>::to_f32(vrow[t]) : 0.f;
-        for (int i = 0; i < nh; ++i) {
+#pragma unroll
+        for (int i = 0; i < kValuHeads; ++i) {
+          if (i >= nh) continue;
           float a = acc[i][k];
 #pragma unroll
           for (int t = 0; t < kBlock; ++t) a = fmaf(ps[i][t], vv[t], a);
@@ -1645,7 +1653,9 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p,
       }
       __syncthreads();
     }
-    for (int i = 0; i < nh; ++i) {
+#pragma unroll
+    for (int i = 0; i < kValuHeads; ++i) {
+      if (i >= nh) continue;
       const int hq = g * p.group + h0 + i;
 #pragma unroll
       for (int k = 0; k < DL; ++k)
