@@ -1586,19 +1586,51 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p,
 #pragma unroll
       for (int k = 0; k < DL; ++k) acc[i][k] = 0.f;
     }
-    for (int bi = 0; bi < nblk; ++bi) {
-      const int blk = tab[bi];
-      const bool ok = unsigned(blk) < unsigned(p.num_blocks);
-      const bool live = ok && (bi * kBlock + tok) < it.n_tokens &&
-                        it.t_begin + bi * kBlock + tok >= it.lo;
-      const char* kp = kbase + int64_t(ok ? blk : 0) * p.p_block;
-      const char* vp = vbase + int64_t(ok ? blk : 0) * p.p_block;
-      float kv[QC * X];
+    // Each block's K chunk elements and V row elements are loaded one block
+    // ahead (with its table entry), so their latency overlaps the previous
+    // block's arithmetic; rows of more than 256 bytes load in turn.
+    constexpr bool PF = D * E <= 256;
+    T kraw[QC * X];
+    T vraw[DL][kBlock];
+    auto load_block = [&](int blk) {
+      const bool okb = unsigned(blk) < unsigned(p.num_blocks);
+      const char* kp = kbase + int64_t(okb ? blk : 0) * p.p_block;
+      const char* vp = vbase + int64_t(okb ? blk : 0) * p.p_block;
 #pragma unroll
       for (int c = 0; c < QC; ++c) {
         const T* chunk = reinterpret_cast<const T*>(kp + ((quarter * QC + c) * kBlock + tok) * 16);
 #pragma unroll
-        for (int e = 0; e < X; ++e) kv[c * X + e] = Fmt<DT>::to_f32(chunk[e]);
+        for (int e = 0; e < X; ++e) kraw[c * X + e] = chunk[e];
+      }
+#pragma unroll
+      for (int k = 0; k < DL; ++k) {
+        const T* vrow = reinterpret_cast<const T*>(vp + int64_t(lane + 64 * k) * kBlock * E);
+#pragma unroll
+        for (int t = 0; t < kBlock; ++t) vraw[k][t] = vrow[t];
+      }
+    };
+    int blk_next = nblk > 0 ? tab[0] : 0;
+    if (PF && nblk > 0) load_block(blk_next);
+    for (int bi = 0; bi < nblk; ++bi) {
+      const int blk = blk_next;
+      if (!PF) load_block(blk);
+      const bool ok = unsigned(blk) < unsigned(p.num_blocks);
+      const bool live = ok && (bi * kBlock + tok) < it.n_tokens &&
+                        it.t_begin + bi * kBlock + tok >= it.lo;
+      float kv[QC * X];
+#pragma unroll
+      for (int e = 0; e < QC * X; ++e) kv[e] = Fmt<DT>::to_f32(kraw[e]);
+      float vv[DL][kBlock];
+      const int lim = ok ? it.n_tokens - bi * kBlock : 0;  // live tokens of the block
+      const int skip = it.lo - (it.t_begin + bi * kBlock);  // before a window's start
+#pragma unroll
+      for (int k = 0; k < DL; ++k)
+#pragma unroll
+        for (int t = 0; t < kBlock; ++t)
+          vv[k][t] = t < lim && t >= skip ? Fmt<DT>::to_f32(vraw[k][t]) : 0.f;
+      if (bi + 1 < nblk) {
+        blk_next = tab[bi + 1];
+        if (PF) load_block(blk_next);
       }
 #pragma unroll
       for (int i = 0; i < kValuHeads; ++i) {
@@ -1634,20 +1666,12 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p,
       __syncthreads();
 #pragma unroll
       for (int k = 0; k < DL; ++k) {
-        const int j = lane + 64 * k;
-        const T* vrow = reinterpret_cast<const T*>(vp + int64_t(j) * kBlock * E);
-        float vv[kBlock];
-        const int lim = ok ? it.n_tokens - bi * kBlock : 0;  // live tokens of the block
-        const int skip = it.lo - (it.t_begin + bi * kBlock);  // before a window's start
-#pragma unroll
-        for (int t = 0; t < kBlock; ++t)
-          vv[t] = t < lim && t >= skip ? Fmt<DT>::to_f32(vrow[t]) : 0.f;
 #pragma unroll
         for (int i = 0; i < kValuHeads; ++i) {
           if (i >= nh) continue;
           float a = acc[i][k];
 #pragma unroll
-          for (int t = 0; t < kBlock; ++t) a = fmaf(ps[i][t], vv[t], a);
+          for (int t = 0; t < kBlock; ++t) a = fmaf(ps[i][t], vv[k][t], a);
           acc[i][k] = a;
         }
       }
