@@ -941,14 +941,20 @@ pkv_status pkv_inject(pkv_cache* c, const pkv_pool* pool, const pkv_src* src,
   if (!c->pending.empty())
     if (pkv_status st = flush_copies(c, *pool, s)) return st;
   if (launch) {
-    void* host = nullptr;
-    if (pkv_status st = c->staging.acquire(bytes, &host)) return st;
-    std::memcpy(host, descs.data(), bytes);
-    if (pkv_status st = c->staging.upload(d_ws, bytes, s)) return st;
-    hipError_t e = pkv::launch_inject(*pool, src_dev, k_host || v_host,
-                                      static_cast<const InjectDesc*>(d_ws),
-                                      int(descs.size()), layer_begin, layer_end, rope_mode,
-                                      d_cos, d_sin, s);
+    // A few descriptors travel in the kernel arguments; more go through the
+    // workspace by one copy.
+    const bool inline_descs = descs.size() <= size_t(pkv::kInlineDescs);
+    if (!inline_descs) {
+      void* host = nullptr;
+      if (pkv_status st = c->staging.acquire(bytes, &host)) return st;
+      std::memcpy(host, descs.data(), bytes);
+      if (pkv_status st = c->staging.upload(d_ws, bytes, s)) return st;
+    }
+    hipError_t e = pkv::launch_inject(
+        *pool, src_dev, k_host || v_host,
+        inline_descs ? nullptr : static_cast<const InjectDesc*>(d_ws),
+        inline_descs ? descs.data() : nullptr, int(descs.size()), layer_begin, layer_end,
+        rope_mode, d_cos, d_sin, s);
     if (e != hipSuccess) return hip_fail(e, "inject launch");
   }
   for (int32_t r = 0; r < n_runs; ++r) {

@@ -42,10 +42,14 @@ struct MergeSeq {
   int32_t _pad;
 };
 
+// Calls of at most kInlineDescs descriptors pass them in the kernel
+// arguments (h_desc: host memory, read at the launch) instead of a device copy
+// (d_desc); exactly one of the two is used.
+constexpr int kInlineDescs = 4;
 hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, bool src_in_host_memory,
-                         const InjectDesc* d_desc, int n_desc, int layer_begin, int layer_end,
-                         int rope_mode, const float* d_cos, const float* d_sin,
-                         hipStream_t stream);
+                         const InjectDesc* d_desc, const InjectDesc* h_desc, int n_desc,
+                         int layer_begin, int layer_end, int rope_mode, const float* d_cos,
+                         const float* d_sin, hipStream_t stream);
 
 hipError_t launch_append(const pkv_pool& pool, int layer, const int32_t* d_tables,
                          int table_stride, const int32_t* d_first_pos, int n_seqs, int n_new,

@@ -269,6 +269,10 @@ struct InjectParams {
   int app_blocks;                    // blocks one sequence's new tokens can touch
   int num_blocks;
   int max_pos;
+  // Calls of at most kInlineDescs descriptors carry them here, in the kernel
+  // arguments, instead of a device copy (n_inline > 0; descs unused).
+  int n_inline;
+  InjectDesc inline_descs[kInlineDescs];
 };
 
 constexpr int kInjectThreads = 256;
@@ -315,7 +319,8 @@ __global__ __launch_bounds__(kInjectThreads) void inject_rope_kernel(InjectParam
   if (p.app_first == nullptr) {
     if (threadIdx.x < sizeof(InjectDesc) / 4)
       reinterpret_cast<int32_t*>(&desc)[threadIdx.x] =
-          reinterpret_cast<const int32_t*>(&p.descs[blockIdx.x])[threadIdx.x];
+          reinterpret_cast<const int32_t*>(p.n_inline > 0 ? &p.inline_descs[blockIdx.x]
+                                                          : &p.descs[blockIdx.x])[threadIdx.x];
   } else {
     const int b = blockIdx.x / p.app_blocks;
     const int first = p.app_first[b];
@@ -1866,9 +1871,9 @@ int device_cus() {
 // Launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, bool src_in_host_memory,
-                         const InjectDesc* d_desc, int n_desc, int layer_begin, int layer_end,
-                         int rope_mode, const float* d_cos, const float* d_sin,
-                         hipStream_t stream) {
+                         const InjectDesc* d_desc, const InjectDesc* h_desc, int n_desc,
+                         int layer_begin, int layer_end, int rope_mode, const float* d_cos,
+                         const float* d_sin, hipStream_t stream) {
   const int eb = elem_size(pool.dtype);
   const int sb = elem_size(src.dtype);
   InjectParams p{};
@@ -1887,6 +1892,13 @@ hipError_t launch_inject(const pkv_pool& pool, const pkv_src& src, bool src_in_h
   p.s_layer = src.layer_stride * sb;
   p.s_token = src.token_stride * sb;
   p.descs = d_desc;
+  if (h_desc != nullptr) {
+    if (n_desc > kInlineDescs) return hipErrorInvalidValue;
+    p.n_inline = n_desc;
+    for (int i = 0; i < n_desc; ++i) p.inline_descs[i] = h_desc[i];
+  } else if (d_desc == nullptr) {
+    return hipErrorInvalidValue;
+  }
   p.layer_begin = layer_begin;
   p.layer_end = layer_end;
   p.rope_mode = rope_mode;
