@@ -51,6 +51,8 @@ def test_inject_matches_oracle(dtype, d, mode):
         [(2, 5, 3, 200), (2, 40, 9, 153), (2, 1, 250 - 1, 399),             # unaligned, partial
          (2, 100, 60, 210), (0, 24, 40, 300), (1, 2, 35, 330)],              # overwrites
         [(2, 0, 0, 0), (1, 1, 0, 398)],                                      # empty run, one token
+        [(0, 64, 0, 5)],       # 4 destination blocks: descriptors in the kernel arguments
+        [(0, 65, 0, 6)],       # 5 destination blocks: descriptors through the workspace
     ]
     o_cos, o_sin = rope_table(d, 10000.0, max_pos)
     cos, sin, dcos, dsin = gu.rope_tables(d, max_pos)
