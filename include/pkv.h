@@ -445,7 +445,11 @@ int32_t pkv_decode_plan_waves(const pkv_plan* plan);
 size_t pkv_decode_workspace_bytes(const pkv_plan* plan);
 
 /* Copy the plan's work list into the workspace (asynchronous on stream; the
- * host copy is kept in library-owned pinned memory until it has landed). */
+ * host copy is kept in library-owned pinned memory until it has landed).
+ * A plan of at most 128 work items that splits no sequence, and whose
+ * launches have fewer than 16 workgroups (items x KV heads) per compute unit
+ * of the current device, travels in each decode launch's kernel arguments
+ * instead: for it this call validates the workspace and enqueues nothing. */
 pkv_status pkv_decode_plan_upload(pkv_plan* plan, void* d_ws, size_t ws_bytes, void* stream);
 
 pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int32_t layer,

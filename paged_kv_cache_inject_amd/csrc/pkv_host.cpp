@@ -1102,6 +1102,24 @@ int32_t pkv_decode_plan_waves(const pkv_plan* plan) { return plan ? plan->waves 
 
 size_t pkv_decode_workspace_bytes(const pkv_plan* plan) { return plan ? plan->ws_bytes : 0; }
 
+}  // extern "C"
+
+namespace {
+
+// Whether the plan's work list travels in the decode kernel's arguments
+// instead of the workspace: at most kInlineItems items, no split sequence
+// (the merge reads the workspace), and too few workgroups for the launch
+// that appends in a launch of its own (it reads the newest positions from
+// the workspace).  Its launches then need no upload.
+bool plan_inline(const pkv_plan* plan) {
+  return plan->items.size() <= size_t(pkv::kInlineItems) && plan->merges.empty() &&
+         int64_t(plan->items.size()) * plan->n_kv_heads < int64_t(16) * pkv::device_cus();
+}
+
+}  // namespace
+
+extern "C" {
+
 pkv_status pkv_decode_plan_upload(pkv_plan* plan, void* d_ws, size_t ws_bytes, void* stream) {
   if (!plan) return fail(PKV_E_INVALID, "null plan");
   if (!d_ws || ws_bytes < plan->ws_bytes)
@@ -1110,7 +1128,7 @@ pkv_status pkv_decode_plan_upload(pkv_plan* plan, void* d_ws, size_t ws_bytes, v
   if (reinterpret_cast<uintptr_t>(d_ws) & 255)
     return fail(PKV_E_WORKSPACE, "workspace must be 256-byte aligned");
   const size_t bytes = plan->off_part_o;
-  if (bytes == 0) return ok();
+  if (bytes == 0 || plan_inline(plan)) return ok();
   void* host = nullptr;
   if (pkv_status st = plan->staging.acquire(bytes, &host)) return st;
   std::memset(host, 0, bytes);
@@ -1191,6 +1209,8 @@ pkv_status decode_common(const pkv_plan* plan, const pkv_pool* pool, int32_t lay
   a.tables = d_tables;
   a.table_stride = table_stride;
   a.items = reinterpret_cast<const DecodeItem*>(ws + plan->off_items);
+  const bool inline_items = plan_inline(plan);
+  a.h_items = inline_items ? plan->items.data() : nullptr;
   a.n_items = int(plan->items.size());
   a.merges = reinterpret_cast<const MergeSeq*>(ws + plan->off_merges);
   a.n_merges = int(plan->merges.size());
@@ -1211,7 +1231,7 @@ pkv_status decode_common(const pkv_plan* plan, const pkv_pool* pool, int32_t lay
   int variant = 0;
   if (const char* env = std::getenv("PKV_DECODE_KERNEL")) variant = std::atoi(env);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (upload_plan) {
+  if (upload_plan && !inline_items) {
     // from the plan's own host memory: the runtime stages these small copies
     hipError_t e = hipSuccess;
     if (!plan->items.empty())

@@ -34,6 +34,11 @@ struct DecodeItem {
   int32_t last;      // 1 if the range ends at the sequence's last position
 };
 
+// Plans of at most kInlineItems work items with no split sequence (and not
+// run as an append launch plus attention) travel in the decode kernel's
+// arguments: no device copy of the work list is made for them.
+constexpr int kInlineItems = 128;
+
 // Merge work: sequence seq owns partial slots [first, first + count).
 struct MergeSeq {
   int32_t seq;
@@ -65,6 +70,9 @@ struct DecodeArgs {
   const int32_t* tables;
   int table_stride;
   const DecodeItem* items;
+  // Host copy of the work list when the plan travels in the kernel
+  // arguments (then items is unused); null otherwise.
+  const DecodeItem* h_items;
   int n_items;
   const MergeSeq* merges;
   int n_merges;
@@ -94,6 +102,10 @@ struct DecodeArgs {
 // kernel_variant: 0 = automatic, 1 = force the generic VALU kernel.
 hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
                          int kernel_variant, hipStream_t stream);
+
+// Compute units of the current device (cached per device; 256 when no device
+// answers).
+int device_cus();
 
 hipError_t launch_bw_probe(const void* src, size_t n_bytes, void* sink, hipStream_t stream);
 

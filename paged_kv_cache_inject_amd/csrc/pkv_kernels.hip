@@ -541,7 +541,26 @@ struct DecodeParams {
   const float* cos_t;
   const float* sin_t;
   int max_pos;
+  // The work list itself when it travels in the kernel arguments (items
+  // null): plans of at most kInlineItems items.
+  DecodeItem inline_items[kInlineItems];
 };
+
+// Work item i of the launch: from the device work list, or from the kernel
+// arguments.  Both are read through the constant address space, so that the
+// (wave-uniform) item comes in by scalar loads and its fields stay scalar:
+// the work list is not written during the launch, and the kernel's first
+// argument, DecodeParams, starts at offset 0 of the kernel-argument segment.
+__device__ inline DecodeItem decode_item(const DecodeParams& p, int i) {
+  typedef const __attribute__((address_space(4))) char* ConstBytes;
+  typedef const __attribute__((address_space(4))) int32_t* ConstWords;
+  const ConstBytes list = p.items ? (ConstBytes)p.items
+                                  : (ConstBytes)__builtin_amdgcn_kernarg_segment_ptr() +
+                                        offsetof(DecodeParams, inline_items);
+  const ConstWords w = (ConstWords)(list + int64_t(i) * sizeof(DecodeItem));
+  static_assert(sizeof(DecodeItem) == 6 * sizeof(int32_t), "six 32-bit fields");
+  return DecodeItem{w[0], w[1], w[2], w[3], w[4], w[5]};
+}
 
 // Launch order of the decode kernels: workgroups walk the (longest-first)
 // items in chunks of `chunk` items; inside a chunk, head by head.  All heads
@@ -794,7 +813,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
   const int grp = lane >> 4;
   int item_i, g;
   decode_work(p, blockIdx.x, item_i, g);
-  const DecodeItem it = p.items[item_i];
+  const DecodeItem it = decode_item(p, item_i);
   // Tile t covers query heads g G + 16 t + row (G = p.group).
   auto head_of = [&](int t) { return g * p.group + 16 * t + row; };
   auto head_ok = [&](int t) { return 16 * t + row < p.group; };
@@ -1353,7 +1372,7 @@ __global__ __launch_bounds__(64 * NW) void decode_dot2_kernel(DecodeParams p,
   const int grp = lane >> 4;
   int item_i, g;
   decode_work(p, blockIdx.x, item_i, g);
-  const DecodeItem it = p.items[item_i];
+  const DecodeItem it = decode_item(p, item_i);
   const int group = p.group;
 
   // query dims matching this lane's K chunks, every head of the group
@@ -1541,7 +1560,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p,
   const int quarter = lane >> 4;
   int item_i, g;
   decode_work(p, blockIdx.x, item_i, g);
-  const DecodeItem it = p.items[item_i];
+  const DecodeItem it = decode_item(p, item_i);
   const int32_t* tab = tables + int64_t(it.seq) * p.table_stride + it.t_begin / kBlock;
   const char* kbase = p.pool_k + int64_t(g) * p.p_head;
   const char* vbase = p.pool_v + int64_t(g) * p.p_head;
@@ -1845,6 +1864,8 @@ size_t one_per_cu_lds() {
   return pad;
 }
 
+}  // namespace
+
 // CUs of the current device (cached per device).
 int device_cus() {
   static int cus[64] = {};
@@ -1864,8 +1885,6 @@ int device_cus() {
   }
   return cus[dev];
 }
-
-}  // namespace
 
 // ---------------------------------------------------------------------------
 // Launchers
@@ -2004,6 +2023,11 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
   p.table_stride = a.table_stride;
   p.items = a.items;
   p.n_items = a.n_items;
+  if (a.h_items) {
+    if (a.n_items > kInlineItems || a.n_merges > 0) return hipErrorInvalidValue;
+    p.items = nullptr;
+    for (int i = 0; i < a.n_items; ++i) p.inline_items[i] = a.h_items[i];
+  }
   // Items per chunk of the launch order.  One (all heads of an item, then
   // the next item) measured best on ragged and uneven batches: 8B-shaped
   // 5.4 -> 6.2 TB/s, ragged MHA 5.8 -> 6.1 TB/s against head-major order.

@@ -339,3 +339,46 @@ def test_lds_staged_variant(dtype, hq, hkv, d):
             os.environ.pop("PKV_DECODE_KERNEL", None)
         out0, lse0 = gu.decode(dp, 0, q_dev, tdev, lens, hq, part)
         assert torch.equal(out12, out0) and torch.equal(lse12, lse0), "staged vs register path"
+
+
+@pytest.mark.parametrize("n_seqs,inline", [(128, True), (129, False)])
+def test_plan_in_kernel_arguments(n_seqs, inline):
+    """Plans of at most 128 items with no split travel in the kernel
+    arguments: their upload leaves the workspace untouched, and decode is
+    still right; one item more goes through the workspace."""
+    import torch
+    import paged_kv_cache_inject_amd as pkv
+    from oracle import attention as o_att
+    from tests import gpu_util as gu
+    from workloads.configs import host_normal, deal_tables
+    rng = np.random.default_rng(n_seqs)
+    hq, hkv, d, dtype = 8, 2, 64, "bf16"
+    lens = rng.integers(0, 90, size=n_seqs).astype(np.int64)
+    need = int(sum(-(-x // 16) for x in lens))
+    nb = need + 5
+    table = deal_tables(rng.permutation(nb)[:need].astype(np.int32), lens, 8)
+    dp = gu.DevicePool(1, nb, hkv, d, dtype)
+    fill_random_pool(dp, 23)
+    q = host_normal(rng, (n_seqs, hq, d), dtype)
+    plan = pkv.pkv_decode_plan_create(lens, hq, hkv, d, 128)
+    try:
+        assert pkv.pkv_decode_plan_items(plan) == n_seqs      # no sequence split
+        n_ws = pkv.pkv_decode_workspace_bytes(plan)
+        ws = torch.full((n_ws,), 0x5A, dtype=torch.uint8, device="cuda")
+        pkv.pkv_decode_plan_upload(plan, ws)
+        torch.cuda.synchronize()
+        untouched = bool((ws == 0x5A).all())
+        assert untouched == inline, (n_seqs, untouched)
+        q_dev = gu.to_device_raw(q.reshape(-1), dtype).view(q.shape)
+        tables_dev = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).cuda()
+        out = torch.full((n_seqs, hq, d), float("nan"), device="cuda")
+        lse = torch.full((n_seqs, hq), float("nan"), device="cuda")
+        pkv.pkv_decode_attention(plan, dp.desc(), 0, q_dev, tables_dev, out, lse, ws)
+        torch.cuda.synchronize()
+    finally:
+        pkv.pkv_decode_plan_destroy(plan)
+    kp, vp = dp.oracle_arrays(dp.host_copy())
+    ref, ref_lse = o_att.decode_paged(q, kp, vp, dp.spec(), 0, [list(r) for r in table], lens,
+                                      hq, by_plane=True)
+    gu.assert_close(out.cpu().numpy(), ref, "out")
+    gu.assert_close(lse.cpu().numpy(), ref_lse, "lse")

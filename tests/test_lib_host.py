@@ -338,6 +338,24 @@ def test_decode_plan_splits():
                                        bad.get("d", 64), bad.get("part", 0))
 
 
+def test_small_plan_upload_enqueues_nothing():
+    """A plan of at most 128 items that splits no sequence travels in the
+    decode launch's kernel arguments: its upload only validates the
+    workspace (a fake, aligned device address is never touched)."""
+    fake = 1 << 20
+    plan = pkv.pkv_decode_plan_create([40] * 128, 8, 2, 64, 0)
+    try:
+        assert pkv.pkv_decode_plan_items(plan) == 128
+        n = pkv.pkv_decode_workspace_bytes(plan)
+        lib = pkv.load_library()
+        assert lib.pkv_decode_plan_upload(plan, fake, n, None) == 0
+        # the workspace is still checked
+        assert lib.pkv_decode_plan_upload(plan, fake, n - 1, None) < 0
+        assert lib.pkv_decode_plan_upload(plan, fake + 16, n, None) < 0
+    finally:
+        pkv.pkv_decode_plan_destroy(plan)
+
+
 def test_append_decode_host_validation_errors():
     """The one-launch append and decode checks its new-token arguments on
     the host before any device work (fake device pointers, never read)."""
