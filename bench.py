@@ -366,22 +366,36 @@ def run_decode(steps, warmup, workload="70b", launch_steps=None, two_calls=True,
     res["launch_gbps"] = per_launch / (res["launch_ms_avg"] * 1e-3) / 1e9
     if cfg.n_layers == 1:
         # A single layer re-reads the same bytes every step, part of which the
-        # 256 MB last-level cache can hold: also time each step after writing
-        # a 1 GiB scratch buffer (outside the events), median of the steps.
+        # 256 MB last-level cache can hold: also time each step after reading
+        # through a 1 GiB buffer (outside the events), which leaves none of the
+        # layer in that cache and no dirty lines in it, median of the steps.
+        # The same after writing the buffer instead: that step also carries
+        # some of the write's aftermath.
+        flush = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        pkv.pkv_bw_probe(flush, sink)
         scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        cold = []
-        for k in range(steps):
-            scratch.fill_(k & 0xFF)
-            c_s, c_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            c_s.record()
-            step()
-            c_e.record()
-            torch.cuda.synchronize()
-            cold.append(c_s.elapsed_time(c_e))
-        del scratch
-        res["cold_ms_per_step"] = float(np.median(cold))
+
+        def after(prep):
+            times = []
+            for k in range(steps):
+                prep(k)
+                c_s, c_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                c_s.record()
+                step()
+                c_e.record()
+                torch.cuda.synchronize()
+                times.append(c_s.elapsed_time(c_e))
+            return float(np.median(times))
+
+        res["cold_ms_per_step"] = after(lambda k: pkv.pkv_bw_probe(flush, sink))
+        res["cold_after_write_ms_per_step"] = after(lambda k: scratch.fill_(k & 0xFF))
+        del flush, scratch, sink
         res["cold_gbps"] = res["bytes_per_step"] / (res["cold_ms_per_step"] * 1e-3) / 1e9
-        log("decode: cold caches %.4f ms/step, %.1f GB/s" % (res["cold_ms_per_step"], res["cold_gbps"]))
+        res["cold_after_write_gbps"] = (res["bytes_per_step"] /
+                                        (res["cold_after_write_ms_per_step"] * 1e-3) / 1e9)
+        log("decode: cold caches %.4f ms/step, %.1f GB/s (after a 1 GiB write %.4f ms/step)"
+            % (res["cold_ms_per_step"], res["cold_gbps"], res["cold_after_write_ms_per_step"]))
     log("decode: %.3f ms/step, %.1f GB/s; per launch %.1f us -> %.1f GB/s; as two calls "
         "per layer %s ms/step" % (ms_step, res["value"], res["launch_ms_avg"] * 1e3,
                                   res["launch_gbps"],
@@ -1244,14 +1258,18 @@ def main():
             "pct_of_peak": round(100 * r["value"] / PEAK_HBM_GBPS, 2),
             "cold_ms_per_step": round(r["cold_ms_per_step"], 4),
             "cold_gbps": round(r["cold_gbps"], 1),
+            "cold_after_write_ms_per_step": round(r["cold_after_write_ms_per_step"], 4),
+            "cold_after_write_gbps": round(r["cold_after_write_gbps"], 1),
             "launch_us_p10_p50_p90": [round(r["event_ms_p10"] * 1e3, 2),
                                       round(r["event_ms_p50"] * 1e3, 2),
                                       round(r["event_ms_p90"] * 1e3, 2)],
             "bytes_per_step": r["bytes_per_step"], "work_items": r["n_items"],
             "part_tokens": r["part_tokens"], "waves_per_workgroup": r["waves"],
             "seed": r["seed"], "tables_sha256": r["tables_sha256"],
-            "cold_meaning": "each step timed after writing a 1 GiB buffer, so the 256 MB "
-                            "last-level cache holds none of the layer",
+            "cold_meaning": "each step timed after reading through a 1 GiB buffer, so the "
+                            "256 MB last-level cache holds none of the layer (and no dirty "
+                            "lines); cold_after_write: after writing that buffer instead, "
+                            "which leaves some of the write's aftermath in the timed step",
             "cpu_baseline": cpu.get(key)}
         line[key]["balance"] = item_balance(st["lens"], r["part_tokens"],
                                             decode_workload(name)[0].n_kv_heads)
