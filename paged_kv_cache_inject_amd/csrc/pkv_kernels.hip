@@ -951,32 +951,47 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
   // read back, when the wave takes the token's block, by the lanes that hold
   // the slot (K chunks 4s + grp in lanes with row == slot, V dims 16n + row
   // in lanes with grp == slot / 4): kept in LDS meanwhile, not in registers.
+  // The source values are all read before the wave's first block is issued:
+  // loads complete in order, so waiting for them does not wait for that
+  // block, and no load waits behind the arithmetic of another.
   typedef typename Fmt<KVDT>::T TP;
+  typedef typename Fmt<QDT>::T TQ;
   __shared__ __align__(16) TP new_row[2][D];
-  auto make_new = [&](auto mode_tag) {
-    constexpr int MODE = decltype(mode_tag)::value;
-    typedef typename Fmt<QDT>::T TQ;
+  TQ nk[2], nv[D / 64];
+  float nrc = 1.f, nrs = 0.f;  // rotary row at the lane's pair
+  const bool halves = p.rope_mode == PKV_ROPE_HALVES;
+  const int nj0 = halves ? lane : 2 * lane;           // the lane's pair (lane < D/2)
+  const int nj1 = halves ? lane + D / 2 : 2 * lane + 1;
+  auto load_new = [&]() {
     const TQ* kin = reinterpret_cast<const TQ*>(ns.kin);
     const TQ* vin = reinterpret_cast<const TQ*>(ns.vin);
     if (lane < D / 2) {
-      const int i = lane;
-      const int j0 = MODE == PKV_ROPE_HALVES ? i : 2 * i;
-      const int j1 = MODE == PKV_ROPE_HALVES ? i + D / 2 : 2 * i + 1;
-      float x0 = Fmt<QDT>::to_f32(kin[j0]), x1 = Fmt<QDT>::to_f32(kin[j1]);
-      if constexpr (MODE != PKV_ROPE_NONE) {
-        const float c = ns.cr[i], sn = ns.sr[i];
-        const float y0 = x0 * c - x1 * sn;
-        const float y1 = x0 * sn + x1 * c;
+      nk[0] = kin[nj0];
+      nk[1] = kin[nj1];
+      if (p.rope_mode != PKV_ROPE_NONE) {
+        nrc = ns.cr[lane];
+        nrs = ns.sr[lane];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) nv[e] = vin[lane + 64 * e];
+  };
+  auto make_new = [&]() {
+    if (lane < D / 2) {
+      float x0 = Fmt<QDT>::to_f32(nk[0]), x1 = Fmt<QDT>::to_f32(nk[1]);
+      if (p.rope_mode != PKV_ROPE_NONE) {
+        const float y0 = x0 * nrc - x1 * nrs;
+        const float y1 = x0 * nrs + x1 * nrc;
         x0 = y0;
         x1 = y1;
       }
-      new_row[0][j0] = Fmt<KVDT>::from_f32(FP8 ? x0 / ns.ksc : x0);
-      new_row[0][j1] = Fmt<KVDT>::from_f32(FP8 ? x1 / ns.ksc : x1);
+      new_row[0][nj0] = Fmt<KVDT>::from_f32(FP8 ? x0 / ns.ksc : x0);
+      new_row[0][nj1] = Fmt<KVDT>::from_f32(FP8 ? x1 / ns.ksc : x1);
     }
 #pragma unroll
-    for (int j = lane; j < D; j += 64) {
-      if constexpr (QDT == KVDT) new_row[1][j] = vin[j];
-      else new_row[1][j] = Fmt<KVDT>::from_f32(Fmt<QDT>::to_f32(vin[j]) / ns.vsc);
+    for (int e = 0; e < D / 64; ++e) {
+      if constexpr (QDT == KVDT) new_row[1][lane + 64 * e] = nv[e];
+      else new_row[1][lane + 64 * e] = Fmt<KVDT>::from_f32(Fmt<QDT>::to_f32(nv[e]) / ns.vsc);
     }
     // the row is written and read by lanes of this one wave
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -984,11 +999,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (d < nj) issue(d, d);
   if constexpr (PUT) {
+    static_assert(DEPTH == 1, "the fused append runs with one block in flight");
     if (put_j >= 0) {
+      // The token's loads, then the wave's first block (it has one: put_j
+      // is among its blocks), then the row: all in one path, so that the row
+      // waits for the token's loads only.
       ns = new_slot<QDT, KVDT, D>(p, it, g);
       if constexpr (blockwise) {  // the scales of the block the token goes to
         const int pb = tab[wave + put_j * NW];
@@ -996,11 +1012,17 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams p,
         ns.ksc = p.k_scale[pi];
         ns.vsc = p.v_scale[pi];
       }
-      if (p.rope_mode == PKV_ROPE_PAIRS) make_new(RopeTag<PKV_ROPE_PAIRS>{});
-      else if (p.rope_mode == PKV_ROPE_HALVES) make_new(RopeTag<PKV_ROPE_HALVES>{});
-      else make_new(RopeTag<PKV_ROPE_NONE>{});
+      load_new();
+      issue(0, 0);
+      make_new();
       if (!ns.ok) put_j = -1;  // no write, and the block is read as stored
+    } else if (nj > 0) {
+      issue(0, 0);
     }
+  } else {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+      if (d < nj) issue(d, d);
   }
 
   // One block of the wave's range (j its index among the wave's blocks, d
