@@ -350,7 +350,9 @@ pkv_status pkv_rope_table(int32_t head_dim, double base, int32_t max_pos,
  * in order of first touch: runs in order, positions ascending; OOM when the
  * free list cannot cover the copies), a written block loses its prefix-cache
  * entry, and every queued copy is carried out on `stream` before the write.
- * Afterwards each sequence's length is max(length, dst_pos + n_tokens).  Runs are host memory.  The device
+ * Afterwards each sequence's length is max(length, dst_pos + n_tokens) over its
+ * non-empty runs.  An empty run (n_tokens = 0) writes nothing: past the sequence
+ * and sign checks it is neither range-checked nor counted.  Runs are host memory.  The device
  * workspace (d_ws, ws_bytes >= pkv_inject_workspace_bytes(runs, n_runs)) holds
  * the per-block write plan; it must not be reused by other work until this
  * call's kernels finish (stream order suffices).
@@ -417,7 +419,9 @@ pkv_status pkv_append_kv(const pkv_pool* pool, int32_t layer, const int32_t* d_t
  *
  * Outputs: d_out (device float [n_seqs][n_q_heads][head_dim]) and, if not
  * NULL, d_lse (device float [n_seqs][n_q_heads], ln of the sum of exp of the
- * scaled scores).  A sequence of length 0 gets out = 0, lse = -inf.
+ * scaled scores).  A sequence of length 0 gets out = 0, lse = -inf.  A plan
+ * of no sequences (n_seqs = 0) is valid: decode calls with it check the pool
+ * and layer, enqueue nothing and read none of their device pointers.
  * q: device [n_seqs][n_q_heads][head_dim] in q_dtype (the pool's; PKV_BF16 or
  * PKV_F16 for an FP8E4M3 pool), already rotated to its own position.
  * scale <= 0 selects 1/sqrt(head_dim).  An FP8E4M3 pool takes up to 64 query
@@ -480,8 +484,8 @@ pkv_status pkv_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int3
  * whole (its other slots with the bytes they held), so, as for any write, it must
  * belong to this sequence alone: pkv_extend copies a shared block first.
  * Errors, all before anything is enqueued: those of
- * pkv_decode_attention; PKV_E_INVALID for null or misaligned k_new/v_new or
- * bad rotary arguments; PKV_E_RANGE when a newest position has no rotary row
+ * pkv_decode_attention; PKV_E_INVALID for misaligned k_new/v_new, for null
+ * ones when the plan has a sequence, or for bad rotary arguments; PKV_E_RANGE when a newest position has no rotary row
  * (>= max_pos, rope_mode other than PKV_ROPE_NONE).
  * ------------------------------------------------------------------------- */
 pkv_status pkv_append_decode_attention(const pkv_plan* plan, const pkv_pool* pool, int32_t layer,

@@ -53,6 +53,8 @@ def validate_runs(tables, lens, runs, max_pos: int):
             raise InjectError("INVALID", "unknown sequence %d" % seq)
         if n < 0 or p0 < 0 or src < 0:
             raise InjectError("INVALID", "negative run field")
+        if n == 0:
+            continue  # an empty run names no position: nothing to check or write
         row = tables[seq]
         if p0 + n > len(row) * BLOCK_TOKENS:
             raise InjectError("RANGE", "run past reserved capacity")
@@ -120,7 +122,8 @@ def inject(k_pool, v_pool, spec: PoolSpec, tables, lens, runs, src_k, src_v,
                         mode, cos_t, sin_t, src_dtype, k_scale, v_scale)
     new_lens = list(lens)
     for (seq, n, p0, _src) in runs:
-        new_lens[seq] = max(new_lens[seq], p0 + n)
+        if n > 0:  # the length covers the positions written
+            new_lens[seq] = max(new_lens[seq], p0 + n)
     return new_lens
 
 

@@ -1269,7 +1269,9 @@ pkv_status pkv_append_decode_attention(const pkv_plan* plan, const pkv_pool* poo
                                        int32_t rope_mode, const float* d_cos,
                                        const float* d_sin, int32_t max_pos, float* d_out,
                                        float* d_lse, void* d_ws, size_t ws_bytes, void* stream) {
-  if (!d_k_new || !d_v_new) return fail(PKV_E_INVALID, "null k_new or v_new");
+  // (a plan of no sequences has no rows to read: its device arguments may be null)
+  if (plan && plan->n_seqs > 0 && (!d_k_new || !d_v_new))
+    return fail(PKV_E_INVALID, "null k_new or v_new");
   NewToken nt;
   nt.k = d_k_new;
   nt.v = d_v_new;
@@ -1295,7 +1297,8 @@ pkv_status pkv_append_decode_attention_noalloc(const pkv_plan* plan, const pkv_p
                 "the plan needs %zu bytes of workspace, more than the %zu-byte static scratch "
                 "of the allocation-free call; use pkv_append_decode_attention with a workspace",
                 plan->ws_bytes, pkv::kScratchBytes);
-  if (!d_k_new || !d_v_new) return fail(PKV_E_INVALID, "null k_new or v_new");
+  if (plan->n_seqs > 0 && (!d_k_new || !d_v_new))
+    return fail(PKV_E_INVALID, "null k_new or v_new");
   void* ws = nullptr;
   const hipError_t e = pkv::scratch_address(&ws);
   if (e != hipSuccess) return hip_fail(e, "address of the static scratch");

@@ -381,6 +381,43 @@ def test_append_decode_host_validation_errors():
     pkv.pkv_decode_plan_destroy(plan)
 
 
+def test_empty_batch_calls_need_no_device_arguments():
+    """Calls with nothing to do return success on the host and enqueue
+    nothing, whatever their device pointers: decode and the fused step over a
+    plan of no sequences, an append for no sequences or of no tokens, an
+    inject call with no runs or only empty runs (null device pointers, never
+    dereferenced; no device is needed)."""
+    import ctypes
+    lib = pkv.load_library()
+    fake = 1 << 20
+    pool = pkv.pkv_pool(1, 8, 2, 64, pkv.PKV_BF16, 0, fake, fake + 4096, 8 * 4096, 4096, 1024)
+    none = pkv.ROPE_CODES["none"]
+    plan = pkv.pkv_decode_plan_create(np.zeros(0, np.int64), 4, 2, 64, 0)
+    try:
+        assert lib.pkv_decode_attention(plan, ctypes.byref(pool), 0, None, pkv.PKV_BF16, 0.0,
+                                        None, 8, None, None, None, 0, None) == 0
+        assert lib.pkv_append_decode_attention(plan, ctypes.byref(pool), 0, None, pkv.PKV_BF16,
+                                               0.0, None, 8, None, None, none, None, None, 0,
+                                               None, None, None, 0, None) == 0
+    finally:
+        pkv.pkv_decode_plan_destroy(plan)
+    for n_seqs, n_new in ((0, 1), (3, 0)):
+        assert lib.pkv_append_kv(ctypes.byref(pool), 0, None, 8, None, n_seqs, n_new, None, None,
+                                 pkv.PKV_BF16, none, None, None, 0, None) == 0
+    src = pkv.pkv_src(fake, fake, 0, 128, 64, pkv.PKV_BF16)
+    c = pkv.pkv_cache_create(8, 2, 4)
+    try:
+        pkv.pkv_alloc_blocks(c, 0, 20)
+        for runs in ([], [(0, 0, 0, 0), (0, 0, 500, 0), (1, 0, 7, 9)]):
+            arr = pkv.make_runs(runs) if runs else None
+            assert lib.pkv_inject(c, ctypes.byref(pool), ctypes.byref(src), arr, len(runs), 0, 1,
+                                  none, None, None, 0, None, 0, None) == 0, pkv.pkv_last_error()
+        _, lens = pkv.pkv_block_table(c, range(2))
+        assert list(lens) == [0, 0]
+    finally:
+        pkv.pkv_cache_destroy(c)
+
+
 def test_inject_host_validation_errors():
     """Argument errors are found on the host before any device work (the
     fake device pointers below are never dereferenced)."""

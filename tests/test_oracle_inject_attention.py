@@ -290,6 +290,32 @@ def test_inject_validation():
     assert validate_runs(tables, [0, 0], [(0, 0, 31, 0)], 40) == []
 
 
+def test_inject_empty_runs_write_nothing_and_keep_lengths():
+    """An empty run names no position: it writes nothing, is not checked
+    against capacity, the rotary table or the store, and leaves the length as
+    it is; an unknown sequence or a negative field is still refused."""
+    spec = PoolSpec(1, 4, 1, 16, "f32").resolved()
+    kp, vp = empty_pool(spec)
+    cos_t, sin_t = rope_table(16, 10000.0, 40)
+    src = np.arange(16 * 4, dtype=np.float32) + 1.0
+    tables = [[0, 1, -1], [2, -1, -1]]
+    runs = [(0, 0, 100, 0), (1, 0, 50, 0), (0, 0, 5, 10 ** 6)]
+    lens = inject(kp, vp, spec, tables, [3, 0], runs, src, src, 0, 16, 0, 1, "pairs",
+                  cos_t, sin_t)
+    assert lens == [3, 0]
+    assert not kp.any() and not vp.any()
+    # beside a run that writes, the length is that run's end alone
+    lens = inject(kp, vp, spec, tables, [3, 0], [(0, 2, 4, 0), (0, 0, 30, 0)], src, src, 0,
+                  16, 0, 1, "pairs", cos_t, sin_t)
+    assert lens == [6, 0]
+    for runs, code in (([(2, 0, 0, 0)], "INVALID"), ([(0, 0, -1, 0)], "INVALID"),
+                       ([(0, 0, 0, -1)], "INVALID")):
+        with pytest.raises(InjectError) as e:
+            inject(kp, vp, spec, tables, [0, 0], runs, src, src, 0, 16, 0, 1, "pairs", cos_t,
+                   sin_t)
+        assert e.value.code == code
+
+
 def test_append_matches_inject_of_the_same_tokens():
     spec = PoolSpec(1, 6, 2, 64, "bf16").resolved()
     cos_t, sin_t = rope_table(64, 10000.0, 64)
