@@ -2050,10 +2050,19 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
     p.items = nullptr;
     for (int i = 0; i < a.n_items; ++i) p.inline_items[i] = a.h_items[i];
   }
-  // Items per chunk of the launch order.  One (all heads of an item, then
-  // the next item) measured best on ragged and uneven batches: 8B-shaped
-  // 5.4 -> 6.2 TB/s, ragged MHA 5.8 -> 6.1 TB/s against head-major order.
-  p.chunk = 1;
+  // Items per chunk of the launch order: the longest-first item order is
+  // kept from chunk to chunk, and inside a chunk consecutive workgroups take
+  // one KV head of consecutive items.  The dispatcher hands consecutive
+  // workgroups to the 8 XCDs in turn, so with item-major order (all heads of
+  // an item, then the next item) and a KV-head count that is a multiple of 8
+  // each XCD would take the same heads of every item; in chunks of 8 items
+  // each takes its own items instead.  Ragged MHA (64 KV heads, 64
+  // workgroups per CU): 2.13-2.19 against 2.20-2.25 ms per step with
+  // item-major order, chunks of 4 in between, 16 and more slower (32: 2.39);
+  // the 70B-, fp8- and 8B-shaped launches (a few workgroups per CU) measured
+  // the same either way.  Fully head-major order was the slowest
+  // (8B-shaped 5.4 against 6.2 TB/s).
+  p.chunk = 8;
   if (const char* env = std::getenv("PKV_DECODE_CHUNK")) {
     const int v = std::atoi(env);
     if (v > 0) p.chunk = v;
