@@ -2053,16 +2053,21 @@ hipError_t launch_decode(const pkv_pool& pool, int layer, const DecodeArgs& a,
   // Items per chunk of the launch order: the longest-first item order is
   // kept from chunk to chunk, and inside a chunk consecutive workgroups take
   // one KV head of consecutive items.  The dispatcher hands consecutive
-  // workgroups to the 8 XCDs in turn, so with item-major order (all heads of
-  // an item, then the next item) and a KV-head count that is a multiple of 8
-  // each XCD would take the same heads of every item; in chunks of 8 items
-  // each takes its own items instead.  Ragged MHA (64 KV heads, 64
-  // workgroups per CU): 2.13-2.19 against 2.20-2.25 ms per step with
-  // item-major order, chunks of 4 in between, 16 and more slower (32: 2.39);
-  // the 70B-, fp8- and 8B-shaped launches (a few workgroups per CU) measured
-  // the same either way.  Fully head-major order was the slowest
-  // (8B-shaped 5.4 against 6.2 TB/s).
-  p.chunk = 8;
+  // workgroups to the 8 XCDs in turn.  In item-major order (chunks of 1: all
+  // heads of an item, then the next item), with a KV-head count that is a
+  // multiple of 8, each XCD takes the same heads of every item; in chunks of
+  // 8 items each XCD takes all heads of its own items.  Launches of many
+  // rounds of workgroups per CU (ragged batches) measured faster in chunks
+  // of 8: ragged MHA (64 KV heads, 64 workgroups per CU) 2.13-2.19 against
+  // 2.20-2.25 ms per step, chunks of 4 in between, 16 and more slower (32:
+  // 2.39).  Launches of one or two rounds keep item-major order, which gives
+  // every XCD one head of every item: in chunks of 8 the XCD that takes the
+  // first item of each chunk gets the longest items, and the 8B-shaped layer
+  // (two rounds) measured 92.4-92.7 against 90.7-91.6 us.  Fully head-major
+  // order was the slowest (8B-shaped 5.4 against 6.2 TB/s).
+  const bool many_rounds =
+      int64_t(a.n_items) * pool.n_kv_heads >= int64_t(16) * device_cus();
+  p.chunk = many_rounds ? 8 : 1;
   if (const char* env = std::getenv("PKV_DECODE_CHUNK")) {
     const int v = std::atoi(env);
     if (v > 0) p.chunk = v;

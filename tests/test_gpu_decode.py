@@ -341,6 +341,42 @@ def test_lds_staged_variant(dtype, hq, hkv, d):
         assert torch.equal(out12, out0) and torch.equal(lse12, lse0), "staged vs register path"
 
 
+def test_launch_order_chunks_cover_every_item():
+    """A launch of many rounds of workgroups per CU takes its items in chunks
+    of 8 (each XCD takes whole items); with a partial last chunk every
+    (item, KV head) is still served once: the result equals the oracle, and
+    it is bit for bit the same in item-major order and in chunks of 3 and 5
+    (the order changes no arithmetic)."""
+    import torch
+    from tests import gpu_util as gu
+    from workloads.configs import host_normal, deal_tables
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    hkv, hq, d = 32, 32, 64
+    n = -(-16 * cus // hkv) + 3          # at least 16 workgroups per CU, n % 8 != 0
+    if n % 8 == 0:
+        n += 1
+    rng = np.random.default_rng(2024)
+    lens = rng.integers(1, 200, size=n).astype(np.int64)
+    lens[:4] = [0, 1, 16, 17]
+    need = int(sum(-(-x // 16) for x in lens))
+    table = deal_tables(rng.permutation(need + 3)[:need].astype(np.int32), lens, 16)
+    dp = gu.DevicePool(1, need + 3, hkv, d, "f16")
+    fill_random_pool(dp, 41)
+    q = host_normal(rng, (n, hq, d), "f16")
+    gu.say("launch order: %d sequences x %d KV heads on %d CUs" % (n, hkv, cus))
+    check_decode_all(dp, 0, q, table, lens, hq)
+    q_dev = gu.to_device_raw(q.reshape(-1), "f16").view(q.shape)
+    tdev = torch.from_numpy(table).cuda()
+    out8, lse8 = gu.decode(dp, 0, q_dev, tdev, lens, hq, 0)
+    for chunk in ("1", "3", "5"):
+        os.environ["PKV_DECODE_CHUNK"] = chunk
+        try:
+            out, lse = gu.decode(dp, 0, q_dev, tdev, lens, hq, 0)
+        finally:
+            os.environ.pop("PKV_DECODE_CHUNK", None)
+        assert torch.equal(out, out8) and torch.equal(lse, lse8), "chunks of %s" % chunk
+
+
 @pytest.mark.parametrize("n_seqs,inline", [(128, True), (129, False)])
 def test_plan_in_kernel_arguments(n_seqs, inline):
     """Plans of at most 128 items with no split travel in the kernel
