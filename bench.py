@@ -59,6 +59,22 @@ def recorded_traffic(kernel="decode_mfma_kernel", workload="70b", root=ROOT):
 POOL_LAYOUT = os.environ.get("PKV_BENCH_LAYOUT", "block")
 
 
+def layout_strides(layout, num_blocks, n_kv_heads, plane):
+    """(layer, block, head strides, V offset) in elements of a pool layout:
+    "block": [layer][block][K planes of all heads | V planes of all heads];
+    "head": [layer][block][head][K plane | V plane];
+    "plane": [layer][K | V][head][block], so that one head's planes of
+    consecutive blocks are adjacent (a 32-token allocation block's two
+    16-token planes form one contiguous run per head)."""
+    if layout == "plane":
+        head_stride = num_blocks * plane
+        return 2 * n_kv_heads * head_stride, plane, head_stride, n_kv_heads * head_stride
+    block_stride = 2 * n_kv_heads * plane
+    if layout == "head":
+        return num_blocks * block_stride, block_stride, 2 * plane, plane
+    return num_blocks * block_stride, block_stride, plane, n_kv_heads * plane
+
+
 def device_pool_fp8(n_layers, num_blocks, n_kv_heads, head_dim, seed, scale=0.01, layout=None,
                     per_block=False):
     """fp8 (E4M3) pool of random finite codes with one K and one V scale per
@@ -67,11 +83,8 @@ def device_pool_fp8(n_layers, num_blocks, n_kv_heads, head_dim, seed, scale=0.01
     import torch
     import paged_kv_cache_inject_amd as pkv
     layout = layout or POOL_LAYOUT
-    plane = 16 * head_dim
-    block_stride = 2 * n_kv_heads * plane
-    layer_stride = num_blocks * block_stride
-    head_stride = 2 * plane if layout == "head" else plane
-    v_off = plane if layout == "head" else n_kv_heads * plane
+    layer_stride, block_stride, head_stride, v_off = layout_strides(
+        layout, num_blocks, n_kv_heads, 16 * head_dim)
     buf = torch.empty(n_layers * layer_stride, dtype=torch.uint8, device="cuda")
     g = torch.Generator(device="cuda")
     for layer in range(n_layers):
@@ -96,18 +109,14 @@ def device_pool_fp8(n_layers, num_blocks, n_kv_heads, head_dim, seed, scale=0.01
 
 
 def device_pool(n_layers, num_blocks, n_kv_heads, head_dim, dtype, seed, layout=None):
-    """Pool buffer filled with N(0,1) per layer.  layout "head":
-    [layer][block][head][K plane | V plane] (one (block, head) = K and V
-    adjacent); layout "block": [layer][block][K planes | V planes]."""
+    """Pool buffer filled with N(0,1) per layer, in one of the layouts of
+    layout_strides."""
     import torch
     import paged_kv_cache_inject_amd as pkv
     from workloads.configs import device_normal
     layout = layout or POOL_LAYOUT
-    plane = 16 * head_dim
-    block_stride = 2 * n_kv_heads * plane
-    layer_stride = num_blocks * block_stride
-    head_stride = 2 * plane if layout == "head" else plane
-    v_off = plane if layout == "head" else n_kv_heads * plane
+    layer_stride, block_stride, head_stride, v_off = layout_strides(
+        layout, num_blocks, n_kv_heads, 16 * head_dim)
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
     buf = torch.empty(n_layers * layer_stride, dtype=tdt, device="cuda")
     if seed is not None:
@@ -214,7 +223,7 @@ def decode_workload(name):
         return MISTRAL_WINDOW, window_structure()
     if name in ("70b", "70b-fp8", "70b-fp8b"):
         return LLAMA70B_80LAYER, llama70b_structure(LLAMA70B_80LAYER)
-    if name == "70b-block32":
+    if name in ("70b-block32", "70b-block32-fp8"):
         return LLAMA70B_80LAYER, llama70b_structure(LLAMA70B_80LAYER, block_tokens=32)
     if name == "8b":
         return LLAMA8B_1LAYER, llama8b_structure(LLAMA8B_1LAYER)
@@ -1061,7 +1070,7 @@ def main():
                          "of at most 4, 8-wave workgroups, attention alone)")
     ap.add_argument("--decode-workload", default="70b",
                     choices=["70b", "8b", "ragged", "70b-fp8", "70b-fp8b", "mistral-window",
-                             "70b-block32", "mqa"],
+                             "70b-block32", "70b-block32-fp8", "mqa"],
                     help="decode workload timed (the reported line uses 70b)")
     args = ap.parse_args()
     if args.gpus != 1:
