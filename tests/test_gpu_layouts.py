@@ -11,8 +11,12 @@ import pytest
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
-def test_padded_split_pool_inject_append_decode(dtype, d):
+@pytest.mark.parametrize("dtype,d,layout", [("bf16", 128, "padded"), ("f16", 64, "padded"),
+                                            ("bf16", 128, "plane"), ("f16", 64, "plane")])
+def test_padded_split_pool_inject_append_decode(dtype, d, layout):
+    """layout "padded": head planes and blocks padded apart; "plane": one
+    head's planes of consecutive blocks adjacent ([head][block] per layer,
+    block stride one plane), as bench.py's plane layout."""
     import torch
     import paged_kv_cache_inject_amd as pkv
     from oracle import attention as o_att, inject as o_inject
@@ -25,9 +29,13 @@ def test_padded_split_pool_inject_append_decode(dtype, d):
     rng = np.random.default_rng(d)
     L, H, NB, HQ, max_pos = 3, 2, 20, 8, 512
     plane = 16 * d
-    hs = plane + 64                      # 128 bytes of padding after every head plane
-    bs = H * hs + 128
-    ls = NB * bs + 256
+    if layout == "plane":
+        bs, hs = plane, NB * plane
+        ls = H * hs
+    else:
+        hs = plane + 64                  # 128 bytes of padding after every head plane
+        bs = H * hs + 128
+        ls = NB * bs + 256
     total = L * ls
     fill = 0x7FAB
     k_buf = torch.full((total,), 0, dtype=torch.int16, device="cuda").fill_(fill).view(
