@@ -563,9 +563,10 @@ __device__ inline DecodeItem decode_item(const DecodeParams& p, int i) {
 }
 
 // Launch order of the decode kernels: workgroups walk the (longest-first)
-// items in chunks of `chunk` items; inside a chunk, head by head.  All heads
-// of the longest items start first, and workgroups running together serve
-// different sequences.  Returns (item, kv head) of workgroup x.
+// items in chunks of `chunk` items; inside a chunk, head by head, so that
+// consecutive workgroups serve consecutive items of the chunk (chunks of 1:
+// all heads of an item, then the next item).  All heads of the longest items
+// start first either way.  Returns (item, kv head) of workgroup x.
 __device__ inline void decode_work(const DecodeParams& p, int x, int& item, int& head) {
   const int per_chunk = p.chunk * p.n_kv_heads;
   const int c0 = (x / per_chunk) * p.chunk;       // first item of this chunk
