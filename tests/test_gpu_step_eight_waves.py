@@ -226,6 +226,48 @@ def test_many_workgroups_step_appends_in_its_own_launch():
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("blockwise", [False, True])
+def test_many_workgroups_fp8_step_in_one_launch(blockwise):
+    """fp8 pools keep the one-launch step on launches of many rounds of
+    workgroups per CU: the items are taken in chunks of 8 (here with a
+    partial last chunk) and two of the fused instance's workgroups share a
+    CU.  131+ sequences x 32 KV heads of 520..700 tokens, scales per head or
+    per block, one sequence empty: pool, out and lse byte for byte those of
+    the two calls; every live sequence against the oracle."""
+    import torch
+    from tests import gpu_util as gu
+    from workloads.configs import deal_tables, host_normal
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    hkv, hq, d = 32, 32, 128
+    B = -(-16 * cus // hkv) + 3           # at least 16 workgroups per CU, B % 8 != 0
+    if B % 8 == 0:
+        B += 1
+    rng = np.random.default_rng(77 + blockwise)
+    lens = rng.integers(520, 700, size=B).astype(np.int64)
+    lens[5] = 0
+    need = int(sum(-(-int(x) // 16) for x in lens))
+    nb = need + 8
+    table = deal_tables(rng.permutation(nb)[:need].astype(np.int32), lens, 64)
+    gu.say("many-workgroup fp8 step: %d sequences, pool %d blocks, per-block scales %s"
+           % (B, nb, blockwise))
+    dp = gu.DevicePool(1, nb, hkv, d, "fp8")
+    shape = (1, nb, hkv) if blockwise else (1, hkv)
+    ks = rng.uniform(0.01, 0.03, size=shape).astype(np.float32)
+    vs = rng.uniform(0.01, 0.03, size=shape).astype(np.float32)
+    dp.set_scales(ks, vs)
+    _fill_fp8(dp, rng)
+    max_pos = int(lens.max())
+    _attach_rope(dp, max_pos)
+    q = host_normal(rng, (B, hq, d), "bf16")
+    q_dev = gu.to_device_raw(q.reshape(-1), "bf16").view(q.shape)
+    tdev = torch.from_numpy(table).cuda()
+    k, v, kd, vd = _new_rows(rng, B, hkv, d, "bf16")
+    run_step(dp, 0, lens, hq, q_dev, tdev, kd, vd, "pairs", "bf16", max_pos, None, q, k, v,
+             table, ks=ks, vs=vs)
+    del dp
+    torch.cuda.empty_cache()
+
+
 def test_ragged_mha_step_sampled():
     """The ragged MHA batch (256 sequences, lognormal lengths, 64 KV heads,
     f16): 24 sequences (shortest, longest, random) against the oracle, all of
