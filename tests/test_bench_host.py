@@ -93,3 +93,25 @@ def test_host_store_dma_comparison_is_opt_in():
     src = inspect.getsource(bench.main)
     assert "dma_compare=args.dma_compare" in src
     assert '"--dma-compare", action="store_true"' in src
+
+
+def test_pool_layouts_tile_the_buffer():
+    """Every layout bench.py offers places the K and V planes of every
+    (layer, block, KV head) inside the pool buffer without overlap, and
+    together they cover it exactly."""
+    import numpy as np
+    plane, nl, nb, h = 64, 2, 5, 3
+    for layout in ("block", "head", "plane"):
+        ls, bs, hs, v_off = bench.layout_strides(layout, nb, h, plane)
+        used = np.zeros(nl * ls, dtype=np.int32)
+        for layer in range(nl):
+            for b in range(nb):
+                for hh in range(h):
+                    for base in (0, v_off):
+                        at = base + layer * ls + b * bs + hh * hs
+                        assert 0 <= at and at + plane <= used.size, (layout, layer, b, hh)
+                        used[at:at + plane] += 1
+        assert np.all(used == 1), layout
+    # the plane layout keeps one head's planes of consecutive blocks adjacent
+    ls, bs, hs, v_off = bench.layout_strides("plane", nb, h, plane)
+    assert bs == plane and hs == nb * plane
